@@ -1,0 +1,208 @@
+"""Thin ctypes binding of libhypic.so (include/hypic.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, their device pointers and the current HIP stream are passed to the
+C ABI, and a non-OK status raises.  Every step of the computation runs in the
+library's HIP kernels; there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhypic.so")
+
+HYPIC_OK, HYPIC_E_INVALID, HYPIC_E_UNSUPPORTED, HYPIC_E_DEVICE = 0, 1, 2, 3
+GATE_HEAD, GATE_TOKEN, GATE_DIAG = 0, 1, 2
+F32, BF16 = 0, 1
+T_DENSE, T_SCALAR = 0, 1
+
+EXPORTED = ("hypic_segment_build", "hypic_compose", "hypic_seam_advance", "hypic_seam_workspace_bytes",
+            "hypic_last_error", "hypic_abi_version", "hypic_selftest_layouts")
+
+
+class HypicError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"hypic status {status}: {msg}")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("n_heads", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("gate", ctypes.c_int32), ("delta", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
+                ("t_layout", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libhypic.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m hybrid_attention_prefill_amd.build_lib`")
+    lib = ctypes.CDLL(path)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    D = ctypes.POINTER(Dims)
+    lib.hypic_segment_build.argtypes = [D, I32, P, P, I64, P, P, P, P, P, P, P]
+    lib.hypic_segment_build.restype = ctypes.c_int
+    lib.hypic_compose.argtypes = [D, I32, I32, P, I32, P, P, P, P]
+    lib.hypic_compose.restype = ctypes.c_int
+    lib.hypic_seam_advance.argtypes = [D, I32, I32, I32, P, I64, P, P, P, P, P, ctypes.c_float, P, I32,
+                                       P, P, P, P, P, ctypes.c_size_t, P]
+    lib.hypic_seam_advance.restype = ctypes.c_int
+    lib.hypic_seam_workspace_bytes.argtypes = [D, I32, I32, I32]
+    lib.hypic_seam_workspace_bytes.restype = ctypes.c_size_t
+    lib.hypic_last_error.restype = ctypes.c_char_p
+    lib.hypic_abi_version.restype = ctypes.c_int32
+    lib.hypic_selftest_layouts.argtypes = [P, P]
+    lib.hypic_selftest_layouts.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != HYPIC_OK:
+        raise HypicError(status, load_library().hypic_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, name, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _in_dtype(t):
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise ValueError(f"inputs must be bfloat16 or float32, got {t.dtype}")
+
+
+def make_dims(H, dk, dv, *, gate, delta, in_dtype, t_layout=T_DENSE):
+    return Dims(int(H), int(dk), int(dv), int(gate), int(bool(delta)), int(in_dtype), int(t_layout))
+
+
+def abi_version() -> int:
+    return int(load_library().hypic_abi_version())
+
+
+def segment_build(k, v, g, beta, seg_begin, seg_end, *, gate, delta, t_layout=T_DENSE,
+                  want_T=True, T_out=None, S_out=None, stream=None):
+    """(T_C, S(C|0)) for every (segment, head) -- hypic_segment_build."""
+    lib = load_library()
+    _dev(k, "k")
+    n_tok, H, dk = k.shape
+    dv = v.shape[2]
+    dt = _in_dtype(k)
+    _dev(v, "v", k.dtype, (n_tok, H, dv))
+    if gate == GATE_HEAD:
+        _dev(g, "g", torch.float32, (H,))
+    elif gate == GATE_TOKEN:
+        _dev(g, "g", k.dtype, (n_tok, H))
+    else:
+        _dev(g, "g", k.dtype, (n_tok, H, dk))
+    if delta:
+        _dev(beta, "beta", k.dtype, (n_tok, H))
+    _dev(seg_begin, "seg_begin", torch.int64)
+    n_seg = seg_begin.shape[0]
+    _dev(seg_end, "seg_end", torch.int64, (n_seg,))
+    if S_out is None:
+        S_out = torch.empty((n_seg, H, dk, dv), device=k.device, dtype=torch.float32)
+    _dev(S_out, "S_out", torch.float32, (n_seg, H, dk, dv))
+    if want_T and T_out is None:
+        shape = (n_seg, H) if t_layout == T_SCALAR else (n_seg, H, dk, dk)
+        T_out = torch.empty(shape, device=k.device, dtype=torch.float32)
+    if T_out is not None:
+        _dev(T_out, "T_out", torch.float32)
+    d = make_dims(H, dk, dv, gate=gate, delta=delta, in_dtype=dt, t_layout=t_layout)
+    _check(lib.hypic_segment_build(ctypes.byref(d), n_seg, _ptr(seg_begin), _ptr(seg_end), n_tok, _ptr(k),
+                                   _ptr(v), _ptr(g), _ptr(beta) if delta else None, _ptr(T_out),
+                                   _ptr(S_out), _stream(stream)))
+    return T_out, S_out
+
+
+def compose(T_cache, S_cache, pair_id, S_run, *, t_layout=T_DENSE, stream=None):
+    """In place: S_run[c] <- T[id] S_run[c] + S[id] along each chain -- hypic_compose."""
+    lib = load_library()
+    _dev(S_cache, "S_cache", torch.float32)
+    n_pair, H, dk, dv = S_cache.shape
+    if t_layout == T_SCALAR:
+        _dev(T_cache, "T_cache", torch.float32, (n_pair, H))
+    else:
+        _dev(T_cache, "T_cache", torch.float32, (n_pair, H, dk, dk))
+    _dev(pair_id, "pair_id", torch.int32)
+    n_chain, n_step = pair_id.shape
+    _dev(S_run, "S_run", torch.float32, (n_chain, H, dk, dv))
+    d = make_dims(H, dk, dv, gate=GATE_HEAD if t_layout == T_SCALAR else GATE_TOKEN, delta=0,
+                  in_dtype=F32, t_layout=t_layout)
+    _check(lib.hypic_compose(ctypes.byref(d), n_chain, n_step, _ptr(pair_id), n_pair, _ptr(T_cache),
+                             _ptr(S_cache), _ptr(S_run), _stream(stream)))
+    return S_run
+
+
+def seam_workspace_bytes(H, dk, dv, n_chain, n_step, w, *, gate=GATE_TOKEN, delta=True, in_dtype=BF16):
+    d = make_dims(H, dk, dv, gate=gate, delta=delta, in_dtype=in_dtype)
+    return int(load_library().hypic_seam_workspace_bytes(ctypes.byref(d), n_chain, n_step, w))
+
+
+def seam_advance(q, k, v, g, beta, seam_start, S_run, out, *, gate, delta, w, scale, pair_id=None,
+                 T_cache=None, S_cache=None, workspace=None, stream=None):
+    """Seam windows then composition along each chain -- hypic_seam_advance (in place on S_run, out)."""
+    lib = load_library()
+    _dev(k, "k")
+    n_tok, H, dk = k.shape
+    dv = v.shape[2]
+    dt = _in_dtype(k)
+    _dev(q, "q", k.dtype, (n_tok, H, dk))
+    _dev(v, "v", k.dtype, (n_tok, H, dv))
+    _dev(seam_start, "seam_start", torch.int64)
+    n_chain, n_step = seam_start.shape
+    _dev(S_run, "S_run", torch.float32, (n_chain, H, dk, dv))
+    _dev(out, "out", torch.float32, (n_chain, n_step, w, H, dv))
+    n_pair = 0
+    if pair_id is not None:
+        _dev(pair_id, "pair_id", torch.int32, (n_chain, n_step))
+        _dev(S_cache, "S_cache", torch.float32)
+        n_pair = S_cache.shape[0]
+        _dev(T_cache, "T_cache", torch.float32, (n_pair, H, dk, dk))
+    need = seam_workspace_bytes(H, dk, dv, n_chain, n_step, w, gate=gate, delta=delta, in_dtype=dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, device=k.device, dtype=torch.uint8)
+    d = make_dims(H, dk, dv, gate=gate, delta=delta, in_dtype=dt)
+    _check(lib.hypic_seam_advance(ctypes.byref(d), n_chain, n_step, w, _ptr(seam_start), n_tok, _ptr(q),
+                                  _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(pair_id), n_pair,
+                                  _ptr(T_cache), _ptr(S_cache), _ptr(S_run), _ptr(out), _ptr(workspace),
+                                  0 if workspace is None else workspace.numel(), _stream(stream)))
+    return S_run, out
+
+
+def selftest_layouts(device="cuda"):
+    """Run the lane-layout self-test kernel; returns its 1280 raw floats (host)."""
+    lib = load_library()
+    out = torch.full((1280,), float("nan"), device=device, dtype=torch.float32)
+    _check(lib.hypic_selftest_layouts(_ptr(out), _stream(None)))
+    torch.cuda.synchronize()
+    return out.cpu().numpy()

@@ -1,0 +1,150 @@
+// api.cpp -- the C ABI of libhypic (declared in include/hypic.h): argument
+// validation, kernel selection and launch on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/hypic.h"
+#include "hypic_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hypic_status fail(hypic_status st, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+hypic_status ok()
+{
+    return HYPIC_OK;
+}
+
+hypic_status from_hip(hipError_t e, const char* what)
+{
+    if (e == hipSuccess) return ok();
+    if (e == hipErrorNotSupported) return fail(HYPIC_E_UNSUPPORTED, "%s: no kernel for this shape/dtype", what);
+    return fail(HYPIC_E_DEVICE, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool valid_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+hypic_status check_dims(const hypic_dims* d)
+{
+    if (!d) return fail(HYPIC_E_INVALID, "dims is NULL");
+    if (d->n_heads < 1) return fail(HYPIC_E_INVALID, "n_heads must be >= 1 (got %d)", d->n_heads);
+    if (!valid_d(d->d_k) || !valid_d(d->d_v))
+        return fail(HYPIC_E_INVALID, "d_k and d_v must be 16, 32, 64 or 128 (got %d, %d)", d->d_k, d->d_v);
+    if (d->gate < HYPIC_GATE_HEAD || d->gate > HYPIC_GATE_DIAG)
+        return fail(HYPIC_E_INVALID, "gate must be 0, 1 or 2 (got %d)", d->gate);
+    if (d->delta != 0 && d->delta != 1) return fail(HYPIC_E_INVALID, "delta must be 0 or 1 (got %d)", d->delta);
+    if (d->in_dtype != HYPIC_F32 && d->in_dtype != HYPIC_BF16)
+        return fail(HYPIC_E_INVALID, "in_dtype must be 0 (f32) or 1 (bf16) (got %d)", d->in_dtype);
+    if (d->t_layout != HYPIC_T_DENSE && d->t_layout != HYPIC_T_SCALAR)
+        return fail(HYPIC_E_INVALID, "t_layout must be 0 (dense) or 1 (scalar) (got %d)", d->t_layout);
+    if (d->t_layout == HYPIC_T_SCALAR && (d->delta || d->gate == HYPIC_GATE_DIAG))
+        return fail(HYPIC_E_INVALID, "a scalar T exists only for scalar gates without the delta rule");
+    return ok();
+}
+
+constexpr long long kMaxGrid = 0x7fffffffLL;
+
+}  // namespace
+
+extern "C" {
+
+int32_t hypic_abi_version(void) { return HYPIC_ABI_VERSION; }
+
+const char* hypic_last_error(void) { return g_last_error.c_str(); }
+
+hypic_status hypic_segment_build(const hypic_dims* dims, int32_t n_seg, const int64_t* seg_begin,
+                                 const int64_t* seg_end, int64_t n_tokens, const void* k, const void* v,
+                                 const void* g, const void* beta, float* T_out, float* S_out, void* stream)
+{
+    if (hypic_status s = check_dims(dims)) return s;
+    if (n_seg < 0) return fail(HYPIC_E_INVALID, "n_seg must be >= 0 (got %d)", n_seg);
+    if (n_tokens < 0) return fail(HYPIC_E_INVALID, "n_tokens must be >= 0");
+    if (n_seg == 0) return ok();
+    if (!seg_begin || !seg_end) return fail(HYPIC_E_INVALID, "seg_begin / seg_end is NULL");
+    if (!S_out) return fail(HYPIC_E_INVALID, "S_out is NULL");
+    if (n_tokens > 0 && (!k || !v || !g)) return fail(HYPIC_E_INVALID, "k, v or g is NULL");
+    if (dims->delta && n_tokens > 0 && !beta) return fail(HYPIC_E_INVALID, "beta is NULL with delta = 1");
+    if ((long long)n_seg * dims->n_heads > kMaxGrid) return fail(HYPIC_E_INVALID, "n_seg * n_heads too large");
+    if (dims->d_k != dims->d_v) return fail(HYPIC_E_UNSUPPORTED, "d_k != d_v is not implemented");
+    const bool bf16 = dims->in_dtype == HYPIC_BF16;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (!dims->delta && dims->gate != HYPIC_GATE_DIAG) {
+        return from_hip(hypic::build_decay(dims->d_k, bf16, dims->gate == HYPIC_GATE_HEAD, n_seg,
+                                           dims->n_heads, seg_begin, seg_end, n_tokens, k, v, g, T_out,
+                                           dims->t_layout == HYPIC_T_SCALAR, S_out, st),
+                        "hypic_segment_build");
+    }
+    if (dims->delta && dims->gate == HYPIC_GATE_TOKEN) {
+        return from_hip(hypic::build_gdn(dims->d_k, bf16, n_seg, dims->n_heads, seg_begin, seg_end,
+                                         n_tokens, k, v, g, beta, T_out, S_out, st),
+                        "hypic_segment_build");
+    }
+    return fail(HYPIC_E_UNSUPPORTED, "hypic_segment_build: gate %d with delta %d is not implemented",
+                dims->gate, dims->delta);
+}
+
+hypic_status hypic_compose(const hypic_dims* dims, int32_t n_chain, int32_t n_step, const int32_t* pair_id,
+                           int32_t n_pair, const float* T_cache, const float* S_cache, float* S_run,
+                           void* stream)
+{
+    if (hypic_status s = check_dims(dims)) return s;
+    if (n_chain < 0 || n_step < 0 || n_pair < 0)
+        return fail(HYPIC_E_INVALID, "n_chain, n_step and n_pair must be >= 0");
+    if (n_chain == 0 || n_step == 0) return ok();
+    if (!pair_id || !S_run) return fail(HYPIC_E_INVALID, "pair_id or S_run is NULL");
+    if (n_pair > 0 && (!T_cache || !S_cache)) return fail(HYPIC_E_INVALID, "T_cache or S_cache is NULL");
+    if ((long long)n_chain * dims->n_heads * 8 > kMaxGrid) return fail(HYPIC_E_INVALID, "too many chains");
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (dims->t_layout == HYPIC_T_SCALAR)
+        return from_hip(hypic::compose_scalar(dims->d_k, dims->d_v, n_chain, dims->n_heads, n_step, pair_id,
+                                              n_pair, T_cache, S_cache, S_run, st),
+                        "hypic_compose");
+    if (dims->d_k != dims->d_v) return fail(HYPIC_E_UNSUPPORTED, "d_k != d_v is not implemented");
+    return from_hip(hypic::compose_dense(dims->d_k, n_chain, dims->n_heads, n_step, pair_id, n_pair, T_cache,
+                                         S_cache, S_run, st),
+                    "hypic_compose");
+}
+
+size_t hypic_seam_workspace_bytes(const hypic_dims* dims, int32_t n_chain, int32_t n_step, int32_t w)
+{
+    (void)dims; (void)n_chain; (void)n_step; (void)w;
+    return 0;
+}
+
+hypic_status hypic_seam_advance(const hypic_dims* dims, int32_t n_chain, int32_t n_step, int32_t w,
+                                const int64_t* seam_start, int64_t n_tokens, const void* q, const void* k,
+                                const void* v, const void* g, const void* beta, float scale,
+                                const int32_t* pair_id, int32_t n_pair, const float* T_cache,
+                                const float* S_cache, float* S_run, float* out, void* workspace,
+                                size_t workspace_bytes, void* stream)
+{
+    (void)n_chain; (void)n_step; (void)w; (void)seam_start; (void)n_tokens; (void)q; (void)k; (void)v;
+    (void)g; (void)beta; (void)scale; (void)pair_id; (void)n_pair; (void)T_cache; (void)S_cache;
+    (void)S_run; (void)out; (void)workspace; (void)workspace_bytes; (void)stream;
+    if (hypic_status s = check_dims(dims)) return s;
+    return fail(HYPIC_E_UNSUPPORTED, "hypic_seam_advance is not implemented yet");
+}
+
+// Diagnostic: runs the lane-layout self-test kernel into a device buffer of
+// 1280 floats (see selftest.hip).  Not part of the method.
+hypic_status hypic_selftest_layouts(float* out, void* stream)
+{
+    if (!out) return fail(HYPIC_E_INVALID, "out is NULL");
+    return from_hip(hypic::selftest_layouts(out, reinterpret_cast<hipStream_t>(stream)), "hypic_selftest_layouts");
+}
+
+}  // extern "C"

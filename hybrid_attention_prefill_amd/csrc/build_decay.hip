@@ -1,0 +1,170 @@
+// build_decay.hip -- segment build for transitions without the delta-rule erase:
+// M_t = e^{g_t} I (g_t = log gamma_h for RetNet-style constant decay, or a
+// per-token scalar log-gate), write k_t v_t^T.  Here T_C = e^{sum g} I and
+//     S(C|0) = sum_t e^{sum_{s>t} g_s} k_t v_t^T = K^T diag(w) V
+// ([ZH] = the Chinese HYPIC page, section 2.1, which names RetNet among the
+// decayed families whose segments need T_C).  For a constant decay gamma this
+// is w_t = gamma^(L-1-t), the closed form.
+//
+// Chunks of 64 tokens, in order: S <- e^{b_C} S + K^T diag(e^{b_C - b}) V with
+// b the in-chunk cumulative log-gate, so every exponent is <= 0.  One
+// workgroup (4 waves) per (segment, head); S tiles are dealt to waves and stay
+// in fp32 MFMA accumulators.  The product runs on v_mfma_f32_16x16x32_bf16:
+// the weighted V is split into bf16 hi + lo (bf16 keys are exact; fp32 keys
+// are split too), keeping the fp32 exponent range for the tiny weights of
+// fast-decaying heads.
+#include "hypic_device.h"
+#include "hypic_kernels.h"
+
+namespace hypic {
+
+namespace {
+constexpr int CH = 64;
+constexpr int LDT = CH + 8;
+
+template <bool BF16>
+__device__ __forceinline__ float ld1(const void* base, size_t e) {
+    if constexpr (BF16) return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[e]);
+    else return reinterpret_cast<const float*>(base)[e];
+}
+}  // namespace
+
+template <int D, bool BF16, bool HEAD_GATE>
+__global__ __launch_bounds__(256) void build_decay_kernel(
+    int n_seg, int H, const int64_t* __restrict__ seg_begin, const int64_t* __restrict__ seg_end,
+    int64_t n_tokens, const void* __restrict__ k, const void* __restrict__ v,
+    const void* __restrict__ gl, float* __restrict__ T_out, int t_scalar, float* __restrict__ S_out)
+{
+    constexpr int RT = D / 16;
+    constexpr int NT = RT * RT;            // output tiles
+    constexpr int TW = (NT + 3) / 4;       // tiles per wave
+    constexpr bool KSPLIT = !BF16;         // fp32 keys need a lo plane
+    __shared__ __attribute__((aligned(16))) uint16_t Kt[2][D][LDT];   // K^T (hi, lo)
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D][LDT];   // (w V)^T (hi, lo)
+    __shared__ float gsh[CH], wsh[CH];
+    __shared__ float bCs;
+
+    const int unit = blockIdx.x, seg = unit / H, h = unit % H;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g4 = lane >> 4, n16 = lane & 15;
+    int64_t beg = seg_begin[seg], end = seg_end[seg];
+    beg = beg < 0 ? 0 : (beg > n_tokens ? n_tokens : beg);
+    end = end < beg ? beg : (end > n_tokens ? n_tokens : end);
+
+    f32x4 acc[TW];
+#pragma unroll
+    for (int i = 0; i < TW; ++i) acc[i] = zero4();
+    float log_t = 0.f;
+    const float ghead = HEAD_GATE ? reinterpret_cast<const float*>(gl)[h] : 0.f;
+    const size_t stride = (size_t)H * D;
+
+    for (int64_t c0 = beg; c0 < end; c0 += CH) {
+        const int n = (int)((end - c0) < CH ? (end - c0) : CH);
+        if (tid < CH) {
+            float gv = 0.f;
+            if (tid < n) gv = HEAD_GATE ? ghead : ld1<BF16>(gl, (size_t)(c0 + tid) * H + h);
+            gsh[tid] = gv;
+        }
+        __syncthreads();
+        if (wave == 0) {  // in-chunk inclusive cumsum; weight e^{b_C - b_t}
+            float x = gsh[lane];
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(x, off, 64);
+                if (lane >= off) x += y;
+            }
+            const float bc = __shfl(x, 63, 64);
+            wsh[lane] = lane < n ? expf(bc - x) : 0.f;
+            if (lane == 0) bCs = bc;
+        }
+        __syncthreads();
+        for (int it = tid; it < CH * D; it += 256) {
+            const int t = it / D, ch = it % D;  // consecutive threads: consecutive channels
+            float kx = 0.f, vx = 0.f;
+            if (t < n) {
+                const size_t e = (size_t)(c0 + t) * stride + (size_t)h * D + ch;
+                kx = ld1<BF16>(k, e);
+                vx = ld1<BF16>(v, e) * wsh[t];
+            }
+            __bf16 kh, kl, vh, vl;
+            split_bf16(kx, kh, kl);
+            split_bf16(vx, vh, vl);
+            Kt[0][ch][t] = bf16_bits(kh);
+            Kt[1][ch][t] = bf16_bits(kl);
+            Vt[0][ch][t] = bf16_bits(vh);
+            Vt[1][ch][t] = bf16_bits(vl);
+        }
+        __syncthreads();
+        const float ebc = expf(bCs);
+#pragma unroll
+        for (int i = 0; i < TW; ++i) {
+            const int tile = wave + 4 * i;
+            if (tile >= NT) continue;
+            const int mt = tile / RT, nt = tile % RT;  // key-channel tile, value-channel tile
+            f32x4 a = acc[i] * ebc;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const bf16x8 kh = *reinterpret_cast<const bf16x8*>(&Kt[0][mt * 16 + n16][ks * 32 + 8 * g4]);
+                const bf16x8 vh = *reinterpret_cast<const bf16x8*>(&Vt[0][nt * 16 + n16][ks * 32 + 8 * g4]);
+                const bf16x8 vl = *reinterpret_cast<const bf16x8*>(&Vt[1][nt * 16 + n16][ks * 32 + 8 * g4]);
+                a = mma_bf16(kh, vh, a);
+                a = mma_bf16(kh, vl, a);
+                if constexpr (KSPLIT) {
+                    const bf16x8 kl = *reinterpret_cast<const bf16x8*>(&Kt[1][mt * 16 + n16][ks * 32 + 8 * g4]);
+                    a = mma_bf16(kl, vh, a);
+                }
+            }
+            acc[i] = a;
+        }
+        log_t += bCs;
+        __syncthreads();
+    }
+
+    const size_t pair = (size_t)seg * H + h;
+    float* S = S_out + pair * D * D;
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+        const int tile = wave + 4 * i;
+        if (tile >= NT) continue;
+        const int mt = tile / RT, nt = tile % RT;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) S[(size_t)(mt * 16 + 4 * g4 + e) * D + nt * 16 + n16] = acc[i][e];
+    }
+    if (T_out) {
+        const float tval = expf(log_t);
+        if (t_scalar) {
+            if (tid == 0) T_out[pair] = tval;
+        } else {
+            float* T = T_out + pair * D * D;
+            for (int it = tid; it < D * D; it += 256) T[it] = (it / D == it % D) ? tval : 0.f;
+        }
+    }
+}
+
+template <int D, bool BF16, bool HEAD>
+static hipError_t launch_decay(int n_seg, int H, const int64_t* sb, const int64_t* se, int64_t n_tok,
+                               const void* k, const void* v, const void* g, float* T_out, int t_scalar,
+                               float* S_out, hipStream_t st)
+{
+    hipLaunchKernelGGL((build_decay_kernel<D, BF16, HEAD>), dim3(n_seg * H), dim3(256), 0, st, n_seg, H,
+                       sb, se, n_tok, k, v, g, T_out, t_scalar, S_out);
+    return hipGetLastError();
+}
+
+hipError_t build_decay(int d, bool in_bf16, bool head_gate, int n_seg, int H, const int64_t* sb,
+                       const int64_t* se, int64_t n_tok, const void* k, const void* v, const void* g,
+                       float* T_out, int t_scalar, float* S_out, hipStream_t st)
+{
+#define HYPIC_CASE(D_)                                                                                  \
+    if (d == D_) {                                                                                      \
+        if (in_bf16 && head_gate) return launch_decay<D_, true, true>(n_seg, H, sb, se, n_tok, k, v, g, T_out, t_scalar, S_out, st);   \
+        if (in_bf16 && !head_gate) return launch_decay<D_, true, false>(n_seg, H, sb, se, n_tok, k, v, g, T_out, t_scalar, S_out, st); \
+        if (!in_bf16 && head_gate) return launch_decay<D_, false, true>(n_seg, H, sb, se, n_tok, k, v, g, T_out, t_scalar, S_out, st); \
+        return launch_decay<D_, false, false>(n_seg, H, sb, se, n_tok, k, v, g, T_out, t_scalar, S_out, st);                          \
+    }
+    HYPIC_CASE(16) HYPIC_CASE(32) HYPIC_CASE(64) HYPIC_CASE(128)
+#undef HYPIC_CASE
+    return hipErrorNotSupported;
+}
+
+}  // namespace hypic

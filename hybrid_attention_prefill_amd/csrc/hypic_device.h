@@ -1,0 +1,115 @@
+// hypic_device.h -- device helpers shared by the gfx950 kernels of libhypic.
+//
+// MFMA shapes used (CDNA4, wave64):
+//   v_mfma_f32_16x16x32_f16 / _bf16 : D(16x16,f32) += A(16x32) B(32x16)
+//     A: lane l holds A[l%16][8*(l/16) + j], j = 0..7
+//     B: lane l holds B[8*(l/16) + j][l%16], j = 0..7
+//     D: lane l holds D[4*(l/16) + i][l%16], i = 0..3
+//   v_mfma_f32_16x16x4_f32 : D(16x16) += A(16x4) B(4x16)
+//     A: lane l holds A[l%16][l/16];  B: lane l holds B[l/16][l%16]
+// These lane layouts are checked on the device by the test-suite.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hypic {
+
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+
+__device__ __forceinline__ f32x4 mma_f16(const f16x8& a, const f16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_f32(float a, float b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// ---- scalar conversions -------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float(((unsigned)b) << 16);
+}
+__device__ __forceinline__ uint16_t f16_bits(_Float16 h) { return __builtin_bit_cast(uint16_t, h); }
+__device__ __forceinline__ uint16_t bf16_bits(__bf16 h) { return __builtin_bit_cast(uint16_t, h); }
+
+// Round x to the operand type; `lo` receives the rounded remainder (3-term split).
+__device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
+    hi = (_Float16)x;
+    lo = (_Float16)(x - (float)hi);
+}
+__device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
+    hi = (__bf16)x;
+    lo = (__bf16)(x - (float)hi);
+}
+
+// Pack two 16-bit values (low = a) into a dword.
+__device__ __forceinline__ unsigned pack2(uint16_t a, uint16_t b) {
+    return (unsigned)a | ((unsigned)b << 16);
+}
+
+// ---- accumulator tiles -> B operand (k = accumulator rows) -----------------------
+// Two D tiles d0 (rows 0..15) and d1 (rows 16..31) of the same 16 columns, each
+// already packed to 16-bit pairs per lane (p0 = rows 4g,4g+1; p1 = rows 4g+2,4g+3
+// of tile 0; q0, q1 the same for tile 1), become the B fragment of the 32-row
+// k-block: lane (g, n) receives rows 8g .. 8g+7 of column n.  Two cross-lane
+// swaps: lanes 32..63 of the tile-0 words trade with lanes 0..31 of the tile-1
+// words, then odd 16-lane rows of the first word trade with even rows of the
+// second.
+__device__ __forceinline__ u32x4 dtiles_to_bfrag(unsigned p0, unsigned p1, unsigned q0, unsigned q1) {
+    auto s0 = __builtin_amdgcn_permlane32_swap(p0, q0, false, false);
+    auto s1 = __builtin_amdgcn_permlane32_swap(p1, q1, false, false);
+    // s0[0] = new p0 (tile0 rows 0-7 in lanes 0-31, tile1 rows 0-7 in lanes 32-63)
+    // s0[1] = new q0 (tile0 rows 8-15 in lanes 0-31, tile1 rows 8-15 in lanes 32-63)
+    auto t0 = __builtin_amdgcn_permlane16_swap(s0[0], s0[1], false, false);
+    auto t1 = __builtin_amdgcn_permlane16_swap(s1[0], s1[1], false, false);
+    return u32x4{t0[0], t1[0], t0[1], t1[1]};
+}
+
+template <typename T8>
+__device__ __forceinline__ T8 as_frag(const u32x4& u) { return __builtin_bit_cast(T8, u); }
+
+// Pack the 4 floats of a D tile lane into two 16-bit pairs of the operand type.
+__device__ __forceinline__ void pack_f16(const f32x4& d, unsigned& w0, unsigned& w1) {
+    w0 = pack2(f16_bits((_Float16)d[0]), f16_bits((_Float16)d[1]));
+    w1 = pack2(f16_bits((_Float16)d[2]), f16_bits((_Float16)d[3]));
+}
+__device__ __forceinline__ void pack_f16_split(const f32x4& d, unsigned& h0, unsigned& h1,
+                                               unsigned& l0, unsigned& l1) {
+    _Float16 h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) split_f16(d[i], h[i], l[i]);
+    h0 = pack2(f16_bits(h[0]), f16_bits(h[1]));
+    h1 = pack2(f16_bits(h[2]), f16_bits(h[3]));
+    l0 = pack2(f16_bits(l[0]), f16_bits(l[1]));
+    l1 = pack2(f16_bits(l[2]), f16_bits(l[3]));
+}
+__device__ __forceinline__ void pack_bf16_split(const f32x4& d, unsigned& h0, unsigned& h1,
+                                                unsigned& l0, unsigned& l1) {
+    __bf16 h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) split_bf16(d[i], h[i], l[i]);
+    h0 = pack2(bf16_bits(h[0]), bf16_bits(h[1]));
+    h1 = pack2(bf16_bits(h[2]), bf16_bits(h[3]));
+    l0 = pack2(bf16_bits(l[0]), bf16_bits(l[1]));
+    l1 = pack2(bf16_bits(l[2]), bf16_bits(l[3]));
+}
+
+// ---- grid -> XCD-aware unit mapping --------------------------------------------
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup x runs on XCD
+// x % 8).  Units are dealt to XCDs round-robin and the `nsub` workgroups of one
+// unit are kept on the same XCD, so they share that XCD's L2.
+struct UnitSlot { int unit, sub; };
+__device__ __forceinline__ UnitSlot xcd_unit_slot(int x, int nsub) {
+    const int xcd = x & 7, li = x >> 3;
+    return UnitSlot{(li / nsub) * 8 + xcd, li % nsub};
+}
+static inline int xcd_grid_size(int n_units, int nsub) { return ((n_units + 7) / 8) * 8 * nsub; }
+
+}  // namespace hypic

@@ -1,0 +1,62 @@
+// selftest.hip -- device check of the lane layouts the kernels rely on: the
+// operand / result layouts of the three MFMA shapes and the accumulator-to-
+// operand cross-lane shuffle.  Every access is inside the 64-lane wave and the
+// fixed-size output buffer.
+#include "hypic_device.h"
+#include "hypic_kernels.h"
+
+namespace hypic {
+
+// out layout (floats), 1280 entries:
+//   [0,256)    D (16x16, row-major) of mfma_f32_16x16x32_f16
+//   [256,512)  D of mfma_f32_16x16x32_bf16
+//   [512,768)  D of mfma_f32_16x16x4f32
+//   [768,1280) B fragments made by dtiles_to_bfrag (64 lanes x 8 values)
+// Operands are filled assuming the documented lane layouts with small integer
+// matrices (exact in every type); the host recomputes D = A B and the expected
+// shuffle result and compares.
+__global__ void selftest_layout_kernel(float* out)
+{
+    const int l = threadIdx.x;
+    const int g4 = l >> 4, n16 = l & 15;
+    // A[i][k] = (3i + k) % 7 - 3,  B[k][j] = (5k + 2j) % 5 - 2
+    f16x8 ah, bh;
+    bf16x8 ab, bb;
+    for (int j = 0; j < 8; ++j) {
+        const int k = 8 * g4 + j;
+        const float a = (float)((n16 * 3 + k) % 7 - 3);
+        const float b = (float)((k * 5 + n16 * 2) % 5 - 2);
+        ah[j] = (_Float16)a; bh[j] = (_Float16)b;
+        ab[j] = (__bf16)a; bb[j] = (__bf16)b;
+    }
+    f32x4 d = mma_f16(ah, bh, zero4());
+    for (int i = 0; i < 4; ++i) out[(4 * g4 + i) * 16 + n16] = d[i];
+    d = mma_bf16(ab, bb, zero4());
+    for (int i = 0; i < 4; ++i) out[256 + (4 * g4 + i) * 16 + n16] = d[i];
+    // f32 16x16x4: A[i][k] with k = l/16 ; B[k][j] with k = l/16
+    {
+        const float a = (float)((n16 * 3 + g4) % 7 - 3);
+        const float b = (float)((g4 * 5 + n16 * 2) % 5 - 2);
+        d = mma_f32(a, b, zero4());
+        for (int i = 0; i < 4; ++i) out[512 + (4 * g4 + i) * 16 + n16] = d[i];
+    }
+    // shuffle input: tile0[r][c] = 16 r + c, tile1[r][c] = 256 + 16 r + c (exact in fp16)
+    f32x4 t0, t1;
+    for (int i = 0; i < 4; ++i) {
+        t0[i] = (float)((4 * g4 + i) * 16 + n16);
+        t1[i] = (float)(256 + (4 * g4 + i) * 16 + n16);
+    }
+    unsigned p0, p1, q0, q1;
+    pack_f16(t0, p0, p1);
+    pack_f16(t1, q0, q1);
+    const f16x8 f = as_frag<f16x8>(dtiles_to_bfrag(p0, p1, q0, q1));
+    for (int j = 0; j < 8; ++j) out[768 + l * 8 + j] = (float)f[j];
+}
+
+hipError_t selftest_layouts(float* out, hipStream_t st)
+{
+    hipLaunchKernelGGL(selftest_layout_kernel, dim3(1), dim3(64), 0, st, out);
+    return hipGetLastError();
+}
+
+}  // namespace hypic

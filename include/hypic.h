@@ -1,0 +1,172 @@
+/*
+ * hypic.h -- C ABI of libhypic.so: the data-parallel hot path of HYPIC's
+ * position-independent caching for linear-attention layers, on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Sources (web pages retelling the HYPIC work; cited by short key):
+ *   [ZH] "首 token 延迟降 3.25 倍！小红书联合北大、上交提出 HYPIC，让混合注意力
+ *        大模型用上「位置无关缓存」" (nav.aitube.vip): section 2.1 (linear
+ *        layers cache the segment transition operator), section 2.2 (seam
+ *        windows), section 2.3 (segment parallelism).
+ *   [ES] "Xiaohongshu, la Universidad de Pekín y la Universidad de Jiao Tong
+ *        de Shanghai presentan HYPIC ..." (xix.ai): the paragraphs on the
+ *        linear layers and on the seam windows.
+ *
+ * The method ([ZH] 2.1): a linear-attention head keeps a state S (d_k x d_v);
+ * every token t applies its transition M_t (d_k x d_k) and adds a write term:
+ *     S_t = M_t S_{t-1} + c_t k_t v_t^T.
+ * For a segment C of tokens 1..L the cached pair is
+ *     T_C    = M_L ... M_1                      (ordered product, later left)
+ *     S(C|0) = state after C started from S = 0,
+ * and any prefix composes exactly:  S(C1 C2) = T(C2) S(C1) + S(C2).
+ *
+ * Transition families (gate x delta):
+ *     gate HEAD,  delta 0 : M_t = gamma_h I,                  c_t = 1   (RetNet-style)
+ *     gate TOKEN, delta 1 : M_t = alpha_t (I - b_t k_t k_t^T), c_t = b_t (gated DeltaNet)
+ *     gate DIAG,  delta 1 : M_t = diag(a_t)(I - b_t k_t k_t^T), c_t = b_t (KDA-style)
+ * Gates are passed as log-gates g <= 0 (gamma = exp(g), alpha_t = exp(g_t),
+ * a_t = exp(g_t) per key channel).
+ *
+ * Conventions for every entry point
+ *   - All array arguments are DEVICE pointers owned by the caller; nothing is
+ *     copied, retained or freed.  The library allocates no device memory.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream) and returns once the kernels are enqueued.
+ *   - Argument errors return HYPIC_E_INVALID before anything is launched;
+ *     valid but unimplemented combinations return HYPIC_E_UNSUPPORTED; a failed
+ *     launch returns HYPIC_E_DEVICE.  Faults while kernels run surface when the
+ *     caller synchronises.  The library never aborts and never prints;
+ *     hypic_last_error() gives a message for the last non-OK status of the
+ *     calling thread.
+ *   - Values the host cannot check are made safe on the device: token ranges
+ *     are clamped to [0, n_tokens), pair ids outside [0, n_pair) skip their
+ *     step, seam windows that do not fit in [0, n_tokens) are skipped.
+ *   - Layouts are row-major.  Token arrays are packed over the prompt:
+ *     k, q [n_tokens][H][d_k], v [n_tokens][H][d_v], beta [n_tokens][H],
+ *     g [H] (HEAD, always fp32) | [n_tokens][H] (TOKEN) | [n_tokens][H][d_k] (DIAG).
+ *     q, k, v, beta and token gates have dtype `in_dtype`.
+ *     Pairs: T [n_pair][H][d_k][d_k] fp32 (or [n_pair][H] with HYPIC_T_SCALAR),
+ *            S [n_pair][H][d_k][d_v] fp32.
+ *   - Outputs of concurrent calls must not alias each other.
+ */
+#ifndef HYPIC_H
+#define HYPIC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HYPIC_ABI_VERSION 1
+
+typedef enum {
+    HYPIC_OK = 0,
+    HYPIC_E_INVALID = 1,     /* bad argument; nothing was launched              */
+    HYPIC_E_UNSUPPORTED = 2, /* valid combination this build does not implement  */
+    HYPIC_E_DEVICE = 3       /* HIP error while launching                       */
+} hypic_status;
+
+typedef enum { HYPIC_GATE_HEAD = 0, HYPIC_GATE_TOKEN = 1, HYPIC_GATE_DIAG = 2 } hypic_gate;
+typedef enum { HYPIC_F32 = 0, HYPIC_BF16 = 1 } hypic_dtype;
+typedef enum { HYPIC_T_DENSE = 0, HYPIC_T_SCALAR = 1 } hypic_t_layout;
+
+typedef struct {
+    int32_t n_heads;  /* H >= 1                                                  */
+    int32_t d_k;      /* key dim: 16, 32, 64 or 128                             */
+    int32_t d_v;      /* value dim: 16, 32, 64 or 128                           */
+    int32_t gate;     /* hypic_gate                                             */
+    int32_t delta;    /* 1: delta-rule erase + beta-weighted write; 0: plain     */
+    int32_t in_dtype; /* hypic_dtype of q, k, v, beta and token gates            */
+    int32_t t_layout; /* hypic_t_layout of T (SCALAR only for gate HEAD, delta 0) */
+} hypic_dims;
+
+/*
+ * hypic_segment_build -- the one-time cost at a segment's first prefill
+ * ([ZH] 2.1 and the overhead paragraph of the evaluation): for every segment i
+ * and head h, start from T = I, S = 0 and apply the tokens
+ * [seg_begin[i], seg_end[i]) in order, writing
+ *     T_out[i][h] = T_C  and  S_out[i][h] = S(C|0).
+ * Segments are independent and may overlap or leave gaps (e.g. seam windows
+ * excluded from the cache); an empty range yields the identity pair (I, 0).
+ *   seg_begin, seg_end : int64 [n_seg] token offsets into the packed arrays
+ *   n_tokens           : length of the packed token arrays (ranges are clamped)
+ *   beta               : ignored (may be NULL) when delta == 0
+ *   T_out              : may be NULL to skip T (S only)
+ * Implemented: (HEAD, delta 0) any d in {16,32,64,128} with d_k == d_v;
+ * (TOKEN, delta 1) and (DIAG, delta 1) for d_k == d_v in {16, 128}.
+ */
+hypic_status hypic_segment_build(const hypic_dims* dims, int32_t n_seg,
+                                 const int64_t* seg_begin, const int64_t* seg_end,
+                                 int64_t n_tokens, const void* k, const void* v,
+                                 const void* g, const void* beta,
+                                 float* T_out, float* S_out, void* stream);
+
+/*
+ * hypic_compose -- reuse of cached pairs ([ZH] 2.1: left-multiply by T_C,
+ * then add): for every chain c, head h and step j = 0..n_step-1 in order,
+ * with id = pair_id[c][j],
+ *     S_run[c][h] <- T[id][h] S_run[c][h] + S[id][h]      (0 <= id < n_pair)
+ * and nothing for other ids.  A chain is one request's running state in one
+ * linear layer; several layers go in one call as separate chains whose ids
+ * index that layer's part of the caches.
+ *   pair_id : int32 [n_chain][n_step]
+ *   S_run   : fp32 [n_chain][H][d_k][d_v], read and written in place
+ */
+hypic_status hypic_compose(const hypic_dims* dims, int32_t n_chain, int32_t n_step,
+                           const int32_t* pair_id, int32_t n_pair,
+                           const float* T_cache, const float* S_cache,
+                           float* S_run, void* stream);
+
+/*
+ * hypic_seam_advance -- reuse with seam windows ([ZH] 2.2): for every chain c,
+ * head h and step j in order:
+ *   1. if s = seam_start[c][j] >= 0 (and s + w <= n_tokens), step the w tokens
+ *      s .. s+w-1 from the running state with their own transitions and
+ *      writes, and emit each token's output
+ *          out[c][j][i][h][:] = S_after_token^T (scale * q_{s+i})
+ *      (output rows of steps without a seam are not written);
+ *   2. if pair_id is not NULL and 0 <= pair_id[c][j] < n_pair, compose with
+ *      that cached pair as in hypic_compose.
+ * Internal segments cache tokens [start + w, end) and pass their first w
+ * tokens here as the seam window; the final state equals the full recurrence.
+ *   seam_start : int64 [n_chain][n_step], -1 = no seam at this step
+ *   w          : 1..16 (the pages' default is 8)
+ *   out        : fp32 [n_chain][n_step][w][H][d_v]
+ *   workspace  : device scratch of hypic_seam_workspace_bytes(...) bytes,
+ *                owned by the caller, 256-byte aligned; contents are
+ *                overwritten; concurrent calls need distinct workspaces.
+ * Implemented: (TOKEN, delta 1) with d_k == d_v == 128 or 16.
+ */
+hypic_status hypic_seam_advance(const hypic_dims* dims, int32_t n_chain, int32_t n_step,
+                                int32_t w, const int64_t* seam_start, int64_t n_tokens,
+                                const void* q, const void* k, const void* v,
+                                const void* g, const void* beta, float scale,
+                                const int32_t* pair_id, int32_t n_pair,
+                                const float* T_cache, const float* S_cache,
+                                float* S_run, float* out,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace hypic_seam_advance needs (0 on invalid dims). */
+size_t hypic_seam_workspace_bytes(const hypic_dims* dims, int32_t n_chain, int32_t n_step,
+                                  int32_t w);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char* hypic_last_error(void);
+
+/* HYPIC_ABI_VERSION of the loaded library. */
+int32_t hypic_abi_version(void);
+
+/*
+ * Diagnostic, not part of the method: runs one wave that exercises the MFMA
+ * lane layouts and the accumulator-to-operand lane shuffle the kernels rely
+ * on, writing 1280 floats to the device buffer `out` (layout documented in the
+ * library source).  The test-suite recomputes the expected values on the host.
+ */
+hypic_status hypic_selftest_layouts(float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HYPIC_H */

@@ -1,0 +1,30 @@
+"""Device check of the MFMA lane layouts and the accumulator->operand lane
+shuffle that every kernel relies on (expected values recomputed on the host)."""
+import numpy as np
+import pytest
+
+from hybrid_attention_prefill_amd import binding as hb
+
+
+@pytest.mark.gpu
+def test_mfma_layouts_and_shuffle():
+    print("selftest_layouts", flush=True)
+    out = hb.selftest_layouts()
+    i = np.arange(16)[:, None]
+    k32 = np.arange(32)[None, :]
+    A = ((3 * i + k32) % 7 - 3).astype(np.float64)                       # 16 x 32
+    B = ((5 * np.arange(32)[:, None] + 2 * np.arange(16)[None, :]) % 5 - 2).astype(np.float64)
+    D = A @ B
+    np.testing.assert_array_equal(out[0:256].reshape(16, 16), D)          # f16
+    np.testing.assert_array_equal(out[256:512].reshape(16, 16), D)        # bf16
+    A4 = ((3 * i + np.arange(4)[None, :]) % 7 - 3).astype(np.float64)
+    B4 = ((5 * np.arange(4)[:, None] + 2 * np.arange(16)[None, :]) % 5 - 2).astype(np.float64)
+    np.testing.assert_array_equal(out[512:768].reshape(16, 16), A4 @ B4)  # f32
+    frag = out[768:1280].reshape(64, 8)
+    exp = np.empty((64, 8))
+    for lane in range(64):
+        g, n = lane // 16, lane % 16
+        for j in range(8):
+            row = 8 * g + j
+            exp[lane, j] = row * 16 + n if row < 16 else 256 + (row - 16) * 16 + n
+    np.testing.assert_array_equal(frag, exp)

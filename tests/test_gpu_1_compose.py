@@ -1,0 +1,79 @@
+"""hypic_compose parity with the fp64 oracle (bf16 hi/lo split MFMA)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from hybrid_attention_prefill_amd import binding as hb
+from _util import dev, rel_f
+
+pytestmark = pytest.mark.gpu
+
+
+def _pairs(seed, n_pair, H, d, t_norm=0.9):
+    rng = np.random.default_rng(seed)
+    T = rng.standard_normal((n_pair, H, d, d)) / np.sqrt(d)
+    T *= t_norm / np.linalg.norm(T, ord=2, axis=(-2, -1))[..., None, None]   # contraction
+    S = rng.standard_normal((n_pair, H, d, d))
+    return T.astype(np.float32), S.astype(np.float32)
+
+
+@pytest.mark.parametrize("d,H,n_chain,n_step", [(16, 1, 1, 2), (16, 3, 2, 9), (64, 8, 1, 16),
+                                                (128, 16, 1, 32), (128, 4, 3, 7), (32, 2, 2, 5)])
+def test_compose_matches_oracle(d, H, n_chain, n_step):
+    print(f"compose d={d} H={H} chains={n_chain} steps={n_step}", flush=True)
+    n_pair = 11
+    T, S = _pairs(d * 7 + H, n_pair, H, d)
+    rng = np.random.default_rng(5)
+    ids = rng.integers(-1, n_pair, size=(n_chain, n_step)).astype(np.int32)
+    ids[0, 0] = n_pair + 3          # out of range: skipped
+    R0 = rng.standard_normal((n_chain, H, d, d)).astype(np.float32)
+    ref = oracle.compose(T, S, np.where(ids >= n_pair, -1, ids), R0)   # the ABI skips such ids
+    Rg = dev(R0, torch.float32)
+    hb.compose(dev(T, torch.float32), dev(S, torch.float32), dev(ids, torch.int32), Rg)
+    torch.cuda.synchronize()
+    err = rel_f(Rg.cpu().numpy(), ref)
+    assert err.max() < 1e-4, err.max()
+
+
+def test_compose_many_chains_full_width():
+    """Enough (chain, head) units for the full-width column block (the batched path)."""
+    d, H, n_chain, n_step, n_pair = 128, 16, 64, 3, 5
+    print("compose many chains", flush=True)
+    T, S = _pairs(3, n_pair, H, d)
+    rng = np.random.default_rng(6)
+    ids = rng.integers(0, n_pair, size=(n_chain, n_step)).astype(np.int32)
+    R0 = np.zeros((n_chain, H, d, d), dtype=np.float32)
+    Rg = dev(R0, torch.float32)
+    hb.compose(dev(T, torch.float32), dev(S, torch.float32), dev(ids, torch.int32), Rg)
+    torch.cuda.synchronize()
+    got = Rg.cpu().numpy()
+    sample = [0, 17, 63]
+    ref = oracle.compose(T, S, ids[sample], R0[sample])
+    assert rel_f(got[sample], ref).max() < 1e-4
+
+
+def test_compose_identity_T_is_plain_sum():
+    d, H = 64, 2
+    rng = np.random.default_rng(8)
+    T = np.broadcast_to(np.eye(d, dtype=np.float32), (3, H, d, d)).copy()
+    S = rng.standard_normal((3, H, d, d)).astype(np.float32)
+    R0 = rng.standard_normal((1, H, d, d)).astype(np.float32)
+    Rg = dev(R0, torch.float32)
+    hb.compose(dev(T, torch.float32), dev(S, torch.float32), dev(np.array([[0, 1, 2]], np.int32), torch.int32), Rg)
+    torch.cuda.synchronize()
+    ref = R0[0].astype(np.float64) + S.astype(np.float64).sum(axis=0)
+    assert rel_f(Rg.cpu().numpy()[0], ref).max() < 1e-5
+
+
+def test_compose_scalar_T():
+    d, H = 64, 8
+    rng = np.random.default_rng(9)
+    t = rng.uniform(0.5, 1.0, size=(6, H)).astype(np.float32)
+    S = rng.standard_normal((6, H, d, d)).astype(np.float32)
+    ids = np.array([[0, 1, -1, 5, 2]], np.int32)
+    ref = oracle.compose(t, S, ids, t_scalar=True)
+    Rg = torch.zeros((1, H, d, d), device="cuda")
+    hb.compose(dev(t, torch.float32), dev(S, torch.float32), dev(ids, torch.int32), Rg, t_layout=hb.T_SCALAR)
+    torch.cuda.synchronize()
+    assert rel_f(Rg.cpu().numpy(), ref).max() < 1e-6
