@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <string>
 
@@ -115,14 +116,15 @@ hypic_status hypic_compose(const hypic_dims* dims, int32_t n_chain, int32_t n_st
                         "hypic_compose");
     if (dims->d_k != dims->d_v) return fail(HYPIC_E_UNSUPPORTED, "d_k != d_v is not implemented");
     return from_hip(hypic::compose_dense(dims->d_k, n_chain, dims->n_heads, n_step, pair_id, n_pair, T_cache,
-                                         S_cache, S_run, st),
+                                         S_cache, S_run, nullptr, st),
                     "hypic_compose");
 }
 
 size_t hypic_seam_workspace_bytes(const hypic_dims* dims, int32_t n_chain, int32_t n_step, int32_t w)
 {
-    (void)dims; (void)n_chain; (void)n_step; (void)w;
-    return 0;
+    if (!dims || dims->n_heads < 1 || !valid_d(dims->d_k) || dims->d_k != dims->d_v) return 0;
+    if (n_chain < 0 || n_step < 0 || w < 1 || w > 16) return 0;
+    return (size_t)n_chain * n_step * dims->n_heads * hypic::seam_record_floats(dims->d_k) * sizeof(float);
 }
 
 hypic_status hypic_seam_advance(const hypic_dims* dims, int32_t n_chain, int32_t n_step, int32_t w,
@@ -132,11 +134,34 @@ hypic_status hypic_seam_advance(const hypic_dims* dims, int32_t n_chain, int32_t
                                 const float* S_cache, float* S_run, float* out, void* workspace,
                                 size_t workspace_bytes, void* stream)
 {
-    (void)n_chain; (void)n_step; (void)w; (void)seam_start; (void)n_tokens; (void)q; (void)k; (void)v;
-    (void)g; (void)beta; (void)scale; (void)pair_id; (void)n_pair; (void)T_cache; (void)S_cache;
-    (void)S_run; (void)out; (void)workspace; (void)workspace_bytes; (void)stream;
     if (hypic_status s = check_dims(dims)) return s;
-    return fail(HYPIC_E_UNSUPPORTED, "hypic_seam_advance is not implemented yet");
+    if (n_chain < 0 || n_step < 0 || n_pair < 0 || n_tokens < 0)
+        return fail(HYPIC_E_INVALID, "n_chain, n_step, n_pair and n_tokens must be >= 0");
+    if (w < 1 || w > 16) return fail(HYPIC_E_INVALID, "w must be in 1..16 (got %d)", w);
+    if (n_chain == 0 || n_step == 0) return ok();
+    if (!seam_start || !S_run || !out) return fail(HYPIC_E_INVALID, "seam_start, S_run or out is NULL");
+    if (n_tokens > 0 && (!q || !k || !v || !g || !beta)) return fail(HYPIC_E_INVALID, "q, k, v, g or beta is NULL");
+    if (pair_id && n_pair > 0 && (!T_cache || !S_cache)) return fail(HYPIC_E_INVALID, "T_cache or S_cache is NULL");
+    if (dims->gate != HYPIC_GATE_TOKEN || !dims->delta)
+        return fail(HYPIC_E_UNSUPPORTED, "hypic_seam_advance: only the scalar-gated delta rule is implemented");
+    if (dims->t_layout != HYPIC_T_DENSE) return fail(HYPIC_E_UNSUPPORTED, "hypic_seam_advance needs dense T");
+    if (dims->d_k != dims->d_v) return fail(HYPIC_E_UNSUPPORTED, "d_k != d_v is not implemented");
+    if ((long long)n_chain * n_step * dims->n_heads > kMaxGrid || (long long)n_chain * dims->n_heads * 8 > kMaxGrid)
+        return fail(HYPIC_E_INVALID, "too many chains or steps");
+    const size_t need = hypic_seam_workspace_bytes(dims, n_chain, n_step, w);
+    if (!workspace || workspace_bytes < need)
+        return fail(HYPIC_E_INVALID, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(HYPIC_E_INVALID, "workspace must be 256-byte aligned");
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const bool bf16 = dims->in_dtype == HYPIC_BF16;
+    float* ws = static_cast<float*>(workspace);
+    hipError_t e = hypic::seam_prep(dims->d_k, n_chain, n_step, dims->n_heads, seam_start, n_tokens, w, q, k, v,
+                                    g, beta, bf16, scale, ws, st);
+    if (e != hipSuccess) return from_hip(e, "hypic_seam_advance (window preparation)");
+    hypic::SeamArgs sa{seam_start, n_tokens, w, (int)bf16, scale, q, k, ws, out};
+    return from_hip(hypic::compose_dense(dims->d_k, n_chain, dims->n_heads, n_step, pair_id,
+                                         pair_id ? n_pair : 0, T_cache, S_cache, S_run, &sa, st),
+                    "hypic_seam_advance");
 }
 
 // Diagnostic: runs the lane-layout self-test kernel into a device buffer of

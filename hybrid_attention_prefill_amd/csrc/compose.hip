@@ -14,15 +14,23 @@
 // split the same way in registers (the A operand), and the product is taken as
 // hi*hi + hi*lo + lo*hi on v_mfma_f32_16x16x32_bf16 (relative error ~2^-16,
 // with fp32's exponent range, so tiny T entries are not flushed).
+//
+// With SEAM (hypic_seam_advance, [ZH] section 2.2) a step may first advance the
+// state through its seam window using the state-independent window factors
+// prepared by seam.hip: Y = Wt R and Z = scale Q R on MFMA, then the window
+// outputs O = diag(e^b) Z + Mo U' and the rank-16 update
+// R <- e^{b_w} R + K^T diag(e^{b_w-b}) U', U' = U - diag(e^b) Y.
 #include "hypic_device.h"
 #include "hypic_kernels.h"
+#include "seam_layout.h"
 
 namespace hypic {
 
-template <int DK, int DV, int NB>
+template <int DK, int DV, int NB, bool SEAM>
 __global__ __launch_bounds__(256) void compose_dense_kernel(
     int n_units, int H, int n_step, const int32_t* __restrict__ pair_id, int n_pair,
-    const float* __restrict__ Tc, const float* __restrict__ Sc, float* __restrict__ Srun)
+    const float* __restrict__ Tc, const float* __restrict__ Sc, float* __restrict__ Srun,
+    SeamArgs sa)
 {
     constexpr int NCB = DV / NB;
     constexpr int KP = DK < 32 ? 32 : DK;   // contraction length padded to the MFMA K
@@ -33,6 +41,13 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(
     constexpr int LDB = KP + 8;             // LDS row length (16-bit units), padded
     __shared__ __attribute__((aligned(16))) uint16_t Rh[2][NB][LDB];
     __shared__ __attribute__((aligned(16))) uint16_t Rl[2][NB][LDB];
+    // seam window: K^T (hi, lo; k = window token), U'' (hi, lo; k = window token),
+    // Y and Z = scale Q R (fp32)
+    constexpr int LDW = 32 + 8;
+    constexpr int SW = SEAM ? 1 : 0;
+    __shared__ __attribute__((aligned(16))) uint16_t Kw[2][SW ? DK : 1][LDW];
+    __shared__ __attribute__((aligned(16))) uint16_t Uw[2][SW ? NB : 1][LDW];
+    __shared__ float Ysh[SW ? kSeamMaxW : 1][NB + 1], Zsh[SW ? kSeamMaxW : 1][NB + 1];
 
     const UnitSlot us = xcd_unit_slot(blockIdx.x, NCB);
     if (us.unit >= n_units) return;
@@ -45,8 +60,12 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(
             (&Rh[0][0][0])[i] = 0;
             (&Rl[0][0][0])[i] = 0;
         }
-        __syncthreads();
     }
+    if constexpr (SEAM) {  // window tokens 16..31 of the k = token operands stay zero
+        for (int i = threadIdx.x; i < 2 * DK * LDW; i += blockDim.x) (&Kw[0][0][0])[i] = 0;
+        for (int i = threadIdx.x; i < 2 * NB * LDW; i += blockDim.x) (&Uw[0][0][0])[i] = 0;
+    }
+    __syncthreads();
 
     float* Rg = Srun + ((size_t)c * H + h) * DK * DV + cb * NB;
     f32x4 acc[RTW][CT];
@@ -82,10 +101,122 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(
     store_split(0);
     __syncthreads();
 
+    // ---- one seam window (SEAM only): reads R from planes `buf`, leaves the
+    // advanced state in the accumulators and in planes buf ^ 1.
+    auto seam_step = [&](size_t cj, int64_t s0, int buf) {
+        const float* rec = sa.ws + (cj * H + h) * SeamRec<DK>::kFloats;
+        const size_t tok_base = (size_t)s0 * H * DK + (size_t)h * DK;
+        auto ldin = [&](const void* base, size_t e) -> float {
+            return sa.in_bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[e])
+                              : reinterpret_cast<const float*>(base)[e];
+        };
+        // stage K^T of the window (k = token), split into bf16 hi + lo
+        for (int it = threadIdx.x; it < kSeamMaxW * DK; it += blockDim.x) {
+            const int t = it / DK, ch = it % DK;
+            const float x = t < sa.w ? ldin(sa.k, tok_base + (size_t)t * H * DK + ch) : 0.f;
+            __bf16 hi, lo;
+            split_bf16(x, hi, lo);
+            Kw[0][ch][t] = bf16_bits(hi);
+            Kw[1][ch][t] = bf16_bits(lo);
+        }
+        // Y = Wt R (tile x < CT) and Z = scale Q R (tile x >= CT), 16 x NB each
+        for (int x = wave; x < 2 * CT; x += 4) {
+            const bool isz = x >= CT;
+            const int ct = isz ? x - CT : x;
+            f32x4 p = zero4();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int k0 = ks * 32 + 8 * g4;
+                float a[8];
+                if (k0 < DK) {
+                    if (!isz) {
+                        const f32x4* src = reinterpret_cast<const f32x4*>(rec + SeamRec<DK>::kWt + n16 * DK + k0);
+                        const f32x4 x0 = src[0], x1 = src[1];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) { a[e] = x0[e]; a[4 + e] = x1[e]; }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            a[e] = n16 < sa.w ? sa.scale * ldin(sa.q, tok_base + (size_t)n16 * H * DK + k0 + e) : 0.f;
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) a[e] = 0.f;
+                }
+                bf16x8 ah, al;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    __bf16 hi, lo;
+                    split_bf16(a[e], hi, lo);
+                    ah[e] = hi;
+                    al[e] = lo;
+                }
+                const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&Rh[buf][ct * 16 + n16][ks * 32 + 8 * g4]);
+                const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&Rl[buf][ct * 16 + n16][ks * 32 + 8 * g4]);
+                p = mma_bf16(ah, bh, p);
+                p = mma_bf16(ah, bl, p);
+                p = mma_bf16(al, bh, p);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (isz) Zsh[4 * g4 + e][ct * 16 + n16] = p[e];
+                else Ysh[4 * g4 + e][ct * 16 + n16] = p[e];
+            }
+        }
+        __syncthreads();
+        // window outputs and U'' = diag(e^{b_w - b}) U'  (k = token operand)
+        const float* eb = rec + SeamRec<DK>::kEb;
+        const float* ebw = rec + SeamRec<DK>::kEbw;
+        const float* Mo = rec + SeamRec<DK>::kMo;
+        const float* Ur = rec + SeamRec<DK>::kU;
+        for (int it = threadIdx.x; it < kSeamMaxW * NB; it += blockDim.x) {
+            const int t = it / NB, n = it % NB;
+            const int col = cb * NB + n;
+            float o = eb[t] * Zsh[t][n];
+            for (int s = 0; s <= t; ++s) o += Mo[t * kSeamMaxW + s] * (Ur[s * DV + col] - eb[s] * Ysh[s][n]);
+            if (t < sa.w) sa.out[((cj * sa.w + t) * H + h) * DV + col] = o;
+            const float u2 = ebw[t] * (Ur[t * DV + col] - eb[t] * Ysh[t][n]);
+            __bf16 hi, lo;
+            split_bf16(u2, hi, lo);
+            Uw[0][n][t] = bf16_bits(hi);
+            Uw[1][n][t] = bf16_bits(lo);
+        }
+        __syncthreads();
+        // R <- e^{b_w} R + K^T U''
+        const float ebW = rec[SeamRec<DK>::kEbW];
+#pragma unroll
+        for (int i = 0; i < RTW; ++i) {
+            const int rt = wave + 4 * i;
+            if (rt >= RT) continue;
+            const bf16x8 kh = *reinterpret_cast<const bf16x8*>(&Kw[0][rt * 16 + n16][8 * g4]);
+            const bf16x8 kl = *reinterpret_cast<const bf16x8*>(&Kw[1][rt * 16 + n16][8 * g4]);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                const bf16x8 uh = *reinterpret_cast<const bf16x8*>(&Uw[0][ct * 16 + n16][8 * g4]);
+                const bf16x8 ul = *reinterpret_cast<const bf16x8*>(&Uw[1][ct * 16 + n16][8 * g4]);
+                f32x4 a = acc[i][ct] * ebW;
+                a = mma_bf16(kh, uh, a);
+                a = mma_bf16(kh, ul, a);
+                a = mma_bf16(kl, uh, a);
+                acc[i][ct] = a;
+            }
+        }
+        store_split(buf ^ 1);
+        __syncthreads();
+    };
+
     int cur = 0;
-    const int32_t* ids = pair_id + (size_t)c * n_step;
+    const int32_t* ids = pair_id ? pair_id + (size_t)c * n_step : nullptr;
     for (int j = 0; j < n_step; ++j) {
-        const int id = ids[j];
+        if constexpr (SEAM) {
+            const size_t cj = (size_t)c * n_step + j;
+            const int64_t s0 = sa.seam_start[cj];
+            if (s0 >= 0 && s0 + sa.w <= sa.n_tokens) {  // uniform over the workgroup
+                seam_step(cj, s0, cur);
+                cur ^= 1;
+            }
+        }
+        const int id = ids ? ids[j] : -1;
         if ((unsigned)id >= (unsigned)n_pair) continue;  // uniform over the workgroup
         const float* T = Tc + ((size_t)id * H + h) * DK * DK;
         const float* S = Sc + ((size_t)id * H + h) * DK * DV + cb * NB;
@@ -189,14 +320,25 @@ __global__ __launch_bounds__(256) void compose_scalar_kernel(
 }
 
 // ---------------------------------------------------------------- launchers
+static constexpr int KP_OF(int dk) { return dk < 32 ? 32 : dk; }
+
 template <int DK, int DV, int NB>
 static hipError_t launch_dense(int n_chain, int H, int n_step, const int32_t* pair_id, int n_pair,
-                               const float* Tc, const float* Sc, float* Srun, hipStream_t st)
+                               const float* Tc, const float* Sc, float* Srun, const SeamArgs* sa,
+                               hipStream_t st)
 {
     const int n_units = n_chain * H;
     const int grid = xcd_grid_size(n_units, DV / NB);
-    hipLaunchKernelGGL((compose_dense_kernel<DK, DV, NB>), dim3(grid), dim3(256), 0, st,
-                       n_units, H, n_step, pair_id, n_pair, Tc, Sc, Srun);
+    if (sa) {
+        // the seam path's extra LDS does not fit beside a full-width 128-column block
+        if constexpr (NB * KP_OF(DK) <= 64 * 128)
+            hipLaunchKernelGGL((compose_dense_kernel<DK, DV, NB, true>), dim3(grid), dim3(256), 0, st,
+                               n_units, H, n_step, pair_id, n_pair, Tc, Sc, Srun, *sa);
+        else
+            return hipErrorInvalidValue;
+    } else
+        hipLaunchKernelGGL((compose_dense_kernel<DK, DV, NB, false>), dim3(grid), dim3(256), 0, st,
+                           n_units, H, n_step, pair_id, n_pair, Tc, Sc, Srun, SeamArgs{});
     return hipGetLastError();
 }
 
@@ -210,11 +352,12 @@ static int pick_nb(long long n_units, int dv)
 }
 
 hipError_t compose_dense(int d, int n_chain, int H, int n_step, const int32_t* pair_id, int n_pair,
-                         const float* Tc, const float* Sc, float* Srun, hipStream_t st)
+                         const float* Tc, const float* Sc, float* Srun, const SeamArgs* sa, hipStream_t st)
 {
-    const int nb = pick_nb((long long)n_chain * H, d);
+    int nb = pick_nb((long long)n_chain * H, d);
+    if (sa && nb > 64) nb = 64;
 #define HYPIC_CASE(D_, NB_) \
-    if (d == D_ && nb == NB_) return launch_dense<D_, D_, NB_>(n_chain, H, n_step, pair_id, n_pair, Tc, Sc, Srun, st);
+    if (d == D_ && nb == NB_) return launch_dense<D_, D_, NB_>(n_chain, H, n_step, pair_id, n_pair, Tc, Sc, Srun, sa, st);
     HYPIC_CASE(16, 16)
     HYPIC_CASE(32, 32) HYPIC_CASE(32, 16)
     HYPIC_CASE(64, 64) HYPIC_CASE(64, 32) HYPIC_CASE(64, 16)

@@ -5,9 +5,22 @@
 
 namespace hypic {
 
-// compose.hip
+// Seam-window arguments of the chain kernel (hypic_seam_advance).
+struct SeamArgs {
+    const int64_t* seam_start;  // [n_chain][n_step], -1 = none
+    int64_t n_tokens;
+    int w;
+    int in_bf16;
+    float scale;
+    const void* q;
+    const void* k;
+    const float* ws;            // records of seam_prep
+    float* out;                 // [n_chain][n_step][w][H][d_v]
+};
+
+// compose.hip (sa == nullptr: plain composition)
 hipError_t compose_dense(int d, int n_chain, int H, int n_step, const int32_t* pair_id, int n_pair,
-                         const float* Tc, const float* Sc, float* Srun, hipStream_t st);
+                         const float* Tc, const float* Sc, float* Srun, const SeamArgs* sa, hipStream_t st);
 hipError_t compose_scalar(int dk, int dv, int n_chain, int H, int n_step, const int32_t* pair_id,
                           int n_pair, const float* Tc, const float* Sc, float* Srun, hipStream_t st);
 
@@ -20,6 +33,12 @@ hipError_t build_gdn(int d, bool in_bf16, int n_seg, int H, const int64_t* sb, c
 hipError_t build_decay(int d, bool in_bf16, bool head_gate, int n_seg, int H, const int64_t* sb,
                        const int64_t* se, int64_t n_tok, const void* k, const void* v, const void* g,
                        float* T_out, int t_scalar, float* S_out, hipStream_t st);
+
+// seam.hip
+hipError_t seam_prep(int d, int n_chain, int n_step, int H, const int64_t* seam_start, int64_t n_tokens,
+                     int w, const void* q, const void* k, const void* v, const void* g, const void* beta,
+                     bool in_bf16, float scale, float* ws, hipStream_t st);
+size_t seam_record_floats(int d);
 
 // selftest.hip
 hipError_t selftest_layouts(float* out, hipStream_t st);
