@@ -94,6 +94,11 @@ hypic_status hypic_segment_build(const hypic_dims* dims, int32_t n_seg, const in
                                          n_tokens, k, v, g, beta, T_out, S_out, st),
                         "hypic_segment_build");
     }
+    if (dims->delta && dims->gate == HYPIC_GATE_DIAG) {
+        return from_hip(hypic::build_kda(dims->d_k, bf16, n_seg, dims->n_heads, seg_begin, seg_end, n_tokens, k,
+                                         v, g, beta, T_out, S_out, st),
+                        "hypic_segment_build");
+    }
     return fail(HYPIC_E_UNSUPPORTED, "hypic_segment_build: gate %d with delta %d is not implemented",
                 dims->gate, dims->delta);
 }

@@ -26,10 +26,12 @@
 // bf16 inputs, or fp16 hi + lo with three products (NSPLIT = 2) for fp32 inputs.
 #include "hypic_device.h"
 #include "hypic_kernels.h"
+#include "build_common.h"
 
 namespace hypic {
 
 namespace {
+using namespace bld;
 
 constexpr int CH = 64;       // chunk length
 constexpr int LDT = CH + 8;  // padded LDS row for token-indexed rows (16-bit units)
@@ -51,21 +53,6 @@ struct alignas(16) GdnSmem {
     float gate[CH], beta[CH], b[CH], eb[CH], ebr[CH];
     float bC;
 };
-
-// fp32 16x16 block product on MFMA: returns A(16x16) B(16x16), D layout.
-__device__ __forceinline__ f32x4 mm16_f32(const float* A, int lda, const float* B, int ldb, int lane) {
-    const int g4 = lane >> 4, n16 = lane & 15;
-    f32x4 acc = zero4();
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-        acc = mma_f32(A[n16 * lda + kb * 4 + g4], B[(kb * 4 + g4) * ldb + n16], acc);
-    return acc;
-}
-__device__ __forceinline__ void st16_f32(float* dst, int ld, const f32x4& v, int lane, float sgn) {
-    const int g4 = lane >> 4, n16 = lane & 15;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dst[(4 * g4 + i) * ld + n16] = sgn * v[i];
-}
 
 // Inverse of I + Lt (64x64 unit lower triangular, Lt in F1) into F2.
 template <typename SM>
@@ -120,90 +107,6 @@ __device__ void tri_inverse(SM& sm, int wave, int lane) {
         st16_f32(&sm.F2[r * 16][cc * 16], LDF, q, lane, -1.f);
     }
     __syncthreads();
-}
-
-template <int NSPLIT>
-struct Frag;
-template <>
-struct Frag<1> {
-    f16x8 h;
-};
-template <>
-struct Frag<2> {
-    f16x8 h, l;
-};
-
-// Load an operand fragment: 8 consecutive 16-bit values at row `row`, column `col`
-// of each plane of a [NSPLIT][rows][LD] LDS array.
-template <int NSPLIT, typename Arr>
-__device__ __forceinline__ Frag<NSPLIT> frag_at(const Arr& a, int row, int col) {
-    Frag<NSPLIT> f;
-    f.h = *reinterpret_cast<const f16x8*>(&a[0][row][col]);
-    if constexpr (NSPLIT == 2) f.l = *reinterpret_cast<const f16x8*>(&a[1][row][col]);
-    return f;
-}
-
-template <int NSPLIT>
-__device__ __forceinline__ f32x4 mma(const Frag<NSPLIT>& a, const Frag<NSPLIT>& b, f32x4 c) {
-    c = mma_f16(a.h, b.h, c);
-    if constexpr (NSPLIT == 2) {
-        c = mma_f16(a.h, b.l, c);
-        c = mma_f16(a.l, b.h, c);
-    }
-    return c;
-}
-
-// Two accumulator tiles (rows 0..15, 16..31 of a 32-row k-block) -> B fragment.
-template <int NSPLIT>
-__device__ __forceinline__ Frag<NSPLIT> dpair_to_frag(const f32x4& d0, const f32x4& d1) {
-    Frag<NSPLIT> f;
-    if constexpr (NSPLIT == 1) {
-        unsigned p0, p1, q0, q1;
-        pack_f16(d0, p0, p1);
-        pack_f16(d1, q0, q1);
-        f.h = as_frag<f16x8>(dtiles_to_bfrag(p0, p1, q0, q1));
-    } else {
-        unsigned p0, p1, pl0, pl1, q0, q1, ql0, ql1;
-        pack_f16_split(d0, p0, p1, pl0, pl1);
-        pack_f16_split(d1, q0, q1, ql0, ql1);
-        f.h = as_frag<f16x8>(dtiles_to_bfrag(p0, p1, q0, q1));
-        f.l = as_frag<f16x8>(dtiles_to_bfrag(pl0, pl1, ql0, ql1));
-    }
-    return f;
-}
-
-template <int NSPLIT>
-__device__ __forceinline__ void put16(uint16_t* hi, uint16_t* lo, float x) {
-    if constexpr (NSPLIT == 1) {
-        *hi = f16_bits((_Float16)x);
-    } else {
-        _Float16 a, b;
-        split_f16(x, a, b);
-        *hi = f16_bits(a);
-        *lo = f16_bits(b);
-    }
-}
-
-template <bool BF16>
-__device__ __forceinline__ void load8(const void* base, size_t elem, float out[8]) {
-    if constexpr (BF16) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + elem);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            out[2 * e] = __uint_as_float(w[e] << 16);
-            out[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
-        }
-    } else {
-        const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + elem);
-        const f32x4 a = p[0], b = p[1];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { out[e] = a[e]; out[4 + e] = b[e]; }
-    }
-}
-template <bool BF16>
-__device__ __forceinline__ float load1(const void* base, size_t elem) {
-    if constexpr (BF16) return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[elem]);
-    else return reinterpret_cast<const float*>(base)[elem];
 }
 
 }  // namespace

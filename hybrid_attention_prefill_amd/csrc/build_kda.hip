@@ -1,0 +1,429 @@
+// build_kda.hip -- segment build (T_C, S(C|0)) for the per-channel (diagonal)
+// gate with the delta rule, gate applied after the erase:
+//     M_t = diag(a_t) (I - b_t k_t k_t^T),   S_t = M_t S_{t-1} + b_t k_t v_t^T,
+// a_t = e^{g_t} per key channel.  The cached pair is T_C = M_L..M_1 and S(C|0)
+// ([ZH] = the Chinese HYPIC page, section 2.1, which names KDA among the
+// families the transition operator covers; the gate-left-of-erase order is the
+// reading documented with the oracle).
+//
+// Chunked form (C = 32; derivation in the design notes).  Per key channel let
+// a_t be the exclusive in-chunk cumulative log-gate (a_0 = 0, a_C = b_C).  With
+//     Lp[t][s] = b_t sum_c k_t k_s e^{a_t - a_s},  L'[t][s] = sum_c k_t k_s e^{a_t - a_{s+1}}  (s < t)
+//     A = (I + Lp)^-1,  W = A diag(b) (e^{a} o K),  U = A diag(b) L' diag(b) V
+//     Kh = e^{b_C - a} o K,  Kh' = e^{b_C - a_{+1}} o K
+// the augmented state X = [T | S] advances as
+//     X <- diag(e^{b_C}) X - Kh^T (W X) + [0 | Kh'^T diag(b) V - Kh^T U].
+// Every exponential has a non-positive exponent except inside the decay-weighted
+// Gram matrices, which are factored per 16-token row block I around
+// rho_I = a_{16 I}: left e^{a_t - rho_I} <= 1 and right e^{rho_I - a_s}, which is
+// <= 1 off the diagonal block and bounded by one 16-token block's decay on it.
+// Those two Gram matrices, W and every product of the T columns use bf16 hi + lo
+// operands (three products on v_mfma_f32_16x16x32_bf16, fp32 range): with strong
+// per-channel decay the decayed rows of W and Kh leave fp16's range while T is
+// still far above the floor.  The S columns use fp16 operands with fp32
+// accumulation on v_mfma_f32_16x16x32_f16 (their small entries are negligible
+// next to the fresh writes).  The T columns are renormalised by a power of two
+// each chunk (a per-channel decay cannot be factored out as one scalar), and
+// once every T entry is below 2^-120 they are dropped: T_C = 0 is then within
+// the comparison floor and stays so, since the transitions do not expand
+// (log-gates <= 0, 0 <= b ||k||^2 <= 2).
+//
+// One workgroup (8 waves) per (segment, head); X in MFMA accumulators, two
+// 16-column tiles per wave (one of T, one of S at d = 128).  bf16 inputs.
+#include "hypic_device.h"
+#include "hypic_kernels.h"
+#include "build_common.h"
+
+namespace hypic {
+
+namespace {
+using namespace bld;
+
+constexpr int CK = 32;        // chunk length
+constexpr int LDT = CK + 8;   // token-indexed 16-bit rows
+constexpr int LDF = CK + 1;   // fp32 32x32 matrices
+
+template <int D>
+struct alignas(16) KdaSmem {
+    uint16_t Kb[CK][D + 8];        // K (bf16 bits), token-major
+    float Ag[CK + 1][D + 4];       // exclusive cumulative log-gate per channel; row CK = b_C
+    float beta[CK];
+    float F1[CK][LDF];             // Lp (strictly lower, beta folded)
+    float F1p[CK][LDF];            // L'
+    float F2[CK][LDF];             // A = (I + Lp)^-1
+    float F3[16][17];
+    uint16_t RmT[2][D][LDT];       // (e^{a} o K)^T, bf16 hi / lo
+    uint16_t KhTb[2][D][LDT];      // Kh^T, bf16 hi / lo (T columns)
+    uint16_t ApB[2][CK][LDT];      // A diag(b), bf16 hi / lo
+    uint16_t WpB[2][CK][D + 8];    // W, token-major, bf16 hi / lo (T columns)
+    uint16_t KhT[D][LDT];          // Kh^T
+    uint16_t KhpT[D][LDT];         // Kh'^T
+    uint16_t bVT[D][LDT];          // (diag(b) V)^T
+    uint16_t Ap[CK][LDT];          // A diag(b)
+    uint16_t Lpb[CK][LDT];         // L' (fp16)
+    uint16_t Z1T[D][LDT];          // (L' diag(b) V)^T
+    uint16_t Wp[CK][D + 8];        // W, token-major (S columns)
+    float red[8];
+};
+
+__device__ __forceinline__ float bf(uint16_t b) { return bf16_bits_to_f32(b); }
+
+// fp16 operand fragment: 8 consecutive values at (row, col) of a row-major LDS matrix.
+__device__ __forceinline__ Frag<1> f16frag(const uint16_t* base, int ld, int row, int col) {
+    Frag<1> f;
+    f.h = *reinterpret_cast<const f16x8*>(base + row * ld + col);
+    return f;
+}
+
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(512) void build_kda_kernel(
+    int n_seg, int H, const int64_t* __restrict__ seg_begin, const int64_t* __restrict__ seg_end,
+    int64_t n_tokens, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ gl, const uint16_t* __restrict__ beta, float* __restrict__ T_out,
+    float* __restrict__ S_out)
+{
+    using SM = KdaSmem<D>;
+    constexpr int RT = D / 16;
+    constexpr int NCT = 2 * RT;
+    constexpr int CTW = (NCT + 7) / 8;
+    constexpr int KSD = D / 32;
+    static_assert(D % 32 == 0, "d must be a multiple of 32");
+    __shared__ SM sm;
+
+    const int unit = blockIdx.x;
+    const int seg = unit / H, h = unit % H;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g4 = lane >> 4, n16 = lane & 15;
+    int64_t beg = seg_begin[seg], end = seg_end[seg];
+    beg = beg < 0 ? 0 : (beg > n_tokens ? n_tokens : beg);
+    end = end < beg ? beg : (end > n_tokens ? n_tokens : end);
+
+    f32x4 X[RT][CTW];
+#pragma unroll
+    for (int c = 0; c < CTW; ++c) {
+        const int ct = wave + 8 * c;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            X[rt][c] = zero4();
+            if (ct < RT) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    X[rt][c][e] = (rt * 16 + 4 * g4 + e == ct * 16 + n16) ? 1.f : 0.f;
+            }
+        }
+    }
+    int log2s = 0;       // T = 2^log2s * X_T
+    bool t_live = true;  // false once every T entry is below 2^-120
+
+    const size_t tok_stride = (size_t)H * D;
+    for (int64_t c0 = beg; c0 < end; c0 += CK) {
+        const int n = (int)((end - c0) < CK ? (end - c0) : CK);
+        // ---- 1. stage K (bf16), V (registers), beta, gates; per-channel cumsum
+        float vx[8];
+        int vt = -1, vcg = 0;
+        for (int it = tid; it < CK * (D / 8); it += 512) {
+            const int t = it / (D / 8), cg = it % (D / 8);
+            u32x4 kw = u32x4{0, 0, 0, 0}, vw = u32x4{0, 0, 0, 0}, gw = u32x4{0, 0, 0, 0};
+            if (t < n) {
+                const size_t e = (size_t)(c0 + t) * tok_stride + (size_t)h * D + cg * 8;
+                kw = *reinterpret_cast<const u32x4*>(k + e);
+                vw = *reinterpret_cast<const u32x4*>(v + e);
+                gw = *reinterpret_cast<const u32x4*>(gl + e);
+            }
+            *reinterpret_cast<u32x4*>(&sm.Kb[t][cg * 8]) = kw;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sm.Ag[t + 1][cg * 8 + 2 * e] = __uint_as_float(gw[e] << 16);       // g_t, scanned below
+                sm.Ag[t + 1][cg * 8 + 2 * e + 1] = __uint_as_float(gw[e] & 0xFFFF0000u);
+                vx[2 * e] = __uint_as_float(vw[e] << 16);
+                vx[2 * e + 1] = __uint_as_float(vw[e] & 0xFFFF0000u);
+            }
+            vt = t;
+            vcg = cg;
+        }
+        if (tid < CK) sm.beta[tid] = tid < n ? bf(beta[(size_t)(c0 + tid) * H + h]) : 0.f;
+        __syncthreads();
+        if (tid < D) {  // exclusive cumulative log-gate of channel tid, in place
+            float acc = 0.f;
+            sm.Ag[0][tid] = 0.f;
+#pragma unroll 8
+            for (int t = 0; t < CK; ++t) {
+                acc += sm.Ag[t + 1][tid];
+                sm.Ag[t + 1][tid] = acc;
+            }
+        }
+        if (vt >= 0) {   // (diag(b) V)^T, fp16
+            const float bt = sm.beta[vt];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sm.bVT[vcg * 8 + e][vt] = f16_bits((_Float16)(bt * vx[e]));
+        }
+        __syncthreads();
+
+        // ---- 2. decay-weighted Gram matrices Lp (waves 0-2) and L' (waves 3-5), bf16 hi+lo
+        if (wave < 6) {
+            const bool lp = wave < 3;
+            const int tile = lp ? wave : wave - 3;
+            const int I = tile == 0 ? 0 : 1, J = tile == 2 ? 1 : 0;
+            const int t = 16 * I + n16, s = 16 * J + n16;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks) {
+                bf16x8 ah, al, bh, bl;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int c = ks * 32 + 8 * g4 + e;
+                    const float rho = sm.Ag[16 * I][c];
+                    const float a = bf(sm.Kb[t][c]) * __expf(sm.Ag[t][c] - rho);
+                    const float b = bf(sm.Kb[s][c]) * __expf(rho - sm.Ag[lp ? s : s + 1][c]);
+                    __bf16 x, y;
+                    split_bf16(a, x, y);
+                    ah[e] = x; al[e] = y;
+                    split_bf16(b, x, y);
+                    bh[e] = x; bl[e] = y;
+                }
+                acc = mma_bf16(ah, bh, acc);
+                acc = mma_bf16(ah, bl, acc);
+                acc = mma_bf16(al, bh, acc);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int tt = 16 * I + 4 * g4 + e, ss = 16 * J + n16;
+                if (lp) sm.F1[tt][ss] = ss < tt ? sm.beta[tt] * acc[e] : 0.f;
+                else sm.F1p[tt][ss] = ss < tt ? acc[e] : 0.f;
+            }
+        } else {
+            // waves 6-7: decay-scaled key operands (channel-major, token-contiguous), fp16
+            for (int it = tid - 384; it < D * CK; it += 128) {
+                const int c = it / CK, t = it % CK;
+                const float kx = bf(sm.Kb[t][c]);
+                const float at = sm.Ag[t][c], at1 = sm.Ag[t + 1][c], bc = sm.Ag[CK][c];
+                put_bf16_split(&sm.RmT[0][c][t], &sm.RmT[1][c][t], kx * __expf(at));
+                const float kh = kx * __expf(bc - at);
+                sm.KhT[c][t] = f16_bits((_Float16)kh);
+                put_bf16_split(&sm.KhTb[0][c][t], &sm.KhTb[1][c][t], kh);
+                sm.KhpT[c][t] = f16_bits((_Float16)(kx * __expf(bc - at1)));
+            }
+        }
+        __syncthreads();
+
+        // ---- 3. A = (I + Lp)^-1: diagonal 16x16 blocks, then A10 = -D1 L10 D0
+        if (wave < 2 && lane < 16) {
+            const int o = wave * 16, j = lane;
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float s = (r == j) ? 1.f : 0.f;
+#pragma unroll
+                for (int q = 0; q < r; ++q) s -= sm.F1[o + r][o + q] * x[q];
+                x[r] = s;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sm.F2[o + r][o + j] = x[r];
+        }
+        for (int it = tid; it < CK * CK; it += 512) {  // L' to fp16 (row-major); the block above
+            const int t = it / CK, s = it % CK;          // the diagonal is never computed
+            sm.Lpb[t][s] = f16_bits((_Float16)(s < t ? sm.F1p[t][s] : 0.f));
+        }
+        __syncthreads();
+        if (wave == 0) {
+            const f32x4 p = mm16_f32(&sm.F1[16][0], LDF, &sm.F2[0][0], LDF, lane);
+            st16_f32(&sm.F3[0][0], 17, p, lane, 1.f);
+        }
+        __syncthreads();
+        if (wave == 0) {
+            const f32x4 q = mm16_f32(&sm.F2[16][16], LDF, &sm.F3[0][0], 17, lane);
+            st16_f32(&sm.F2[16][0], LDF, q, lane, -1.f);
+        }
+        __syncthreads();
+        for (int it = tid; it < CK * CK; it += 512) {
+            const int t = it / CK, s = it % CK;
+            const float ap = s <= t ? sm.F2[t][s] * sm.beta[s] : 0.f;
+            sm.Ap[t][s] = f16_bits((_Float16)ap);
+            put_bf16_split(&sm.ApB[0][t][s], &sm.ApB[1][t][s], ap);
+        }
+        __syncthreads();
+
+        // ---- 4. W^T = Rm^T Ap^T (-> W token-major) and Z1^T = (bV)^T L'^T
+        for (int tile = wave; tile < 2 * RT * 2; tile += 8) {
+            const bool isw = tile < RT * 2;
+            const int tl = isw ? tile : tile - RT * 2;
+            const int mt = tl / 2, nt = tl % 2;   // channel tile, token tile
+            f32x4 acc = zero4();
+            if (isw) {
+                const FragB a = fragb_at(&sm.RmT[0][0][0], &sm.RmT[1][0][0], LDT, mt * 16 + n16, 8 * g4);
+                const FragB b = fragb_at(&sm.ApB[0][0][0], &sm.ApB[1][0][0], LDT, nt * 16 + n16, 8 * g4);
+                acc = mma3(a, b, acc);
+                uint16_t hh[4], bh[4], bl[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    hh[e] = f16_bits((_Float16)acc[e]);
+                    put_bf16_split(&bh[e], &bl[e], acc[e]);
+                }
+                const int row = nt * 16 + n16, col = mt * 16 + 4 * g4;
+                *reinterpret_cast<u32x2*>(&sm.Wp[row][col]) = u32x2{pack2(hh[0], hh[1]), pack2(hh[2], hh[3])};
+                *reinterpret_cast<u32x2*>(&sm.WpB[0][row][col]) = u32x2{pack2(bh[0], bh[1]), pack2(bh[2], bh[3])};
+                *reinterpret_cast<u32x2*>(&sm.WpB[1][row][col]) = u32x2{pack2(bl[0], bl[1]), pack2(bl[2], bl[3])};
+            } else {
+                const Frag<1> a = f16frag(&sm.bVT[0][0], LDT, mt * 16 + n16, 8 * g4);
+                const Frag<1> b = f16frag(&sm.Lpb[0][0], LDT, nt * 16 + n16, 8 * g4);
+                acc = mma<1>(a, b, acc);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sm.Z1T[mt * 16 + 4 * g4 + e][nt * 16 + n16] = f16_bits((_Float16)acc[e]);
+            }
+        }
+        __syncthreads();
+
+        // ---- 5. per owned column tile: Y = W X, R = -(Y [+ U]), X <- e^{b_C} X + Kh^T R [+ Kh'^T bV]
+#pragma unroll
+        for (int c = 0; c < CTW; ++c) {
+            const int ct = wave + 8 * c;
+            if (ct >= NCT) continue;
+            const bool is_s = ct >= RT;
+            const int vt16 = ct - RT;
+            if (!is_s) {  // T columns: bf16 hi + lo products
+                if (!t_live) continue;
+                FragB xb[KSD];
+#pragma unroll
+                for (int kb = 0; kb < KSD; ++kb) xb[kb] = dpair_to_fragb(X[2 * kb][c], X[2 * kb + 1][c]);
+                f32x4 R[2];
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+                    f32x4 y = zero4();
+#pragma unroll
+                    for (int kb = 0; kb < KSD; ++kb)
+                        y = mma3(fragb_at(&sm.WpB[0][0][0], &sm.WpB[1][0][0], D + 8, tt * 16 + n16, kb * 32 + 8 * g4),
+                                 xb[kb], y);
+                    R[tt] = -y;
+                }
+                const FragB rb = dpair_to_fragb(R[0], R[1]);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    f32x4 acc;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[e] = X[rt][c][e] * __expf(sm.Ag[CK][rt * 16 + 4 * g4 + e]);
+                    X[rt][c] = mma3(fragb_at(&sm.KhTb[0][0][0], &sm.KhTb[1][0][0], LDT, rt * 16 + n16, 8 * g4), rb, acc);
+                }
+                continue;
+            }
+            f32x4 U[2] = {zero4(), zero4()};
+            if (is_s) {  // U = Ap Z1 for this value tile
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+                    const Frag<1> a = f16frag(&sm.Ap[0][0], LDT, tt * 16 + n16, 8 * g4);
+                    const Frag<1> b = f16frag(&sm.Z1T[0][0], LDT, vt16 * 16 + n16, 8 * g4);
+                    U[tt] = mma<1>(a, b, U[tt]);
+                }
+            }
+            Frag<1> xb[KSD];
+#pragma unroll
+            for (int kb = 0; kb < KSD; ++kb) xb[kb] = dpair_to_frag<1>(X[2 * kb][c], X[2 * kb + 1][c]);
+            f32x4 R[2];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                f32x4 y = zero4();
+#pragma unroll
+                for (int kb = 0; kb < KSD; ++kb) {
+                    const Frag<1> a = f16frag(&sm.Wp[0][0], D + 8, tt * 16 + n16, kb * 32 + 8 * g4);
+                    y = mma<1>(a, xb[kb], y);
+                }
+                R[tt] = -(y + U[tt]);
+            }
+            const Frag<1> rb = dpair_to_frag<1>(R[0], R[1]);
+            Frag<1> vb;
+            if (is_s) vb = f16frag(&sm.bVT[0][0], LDT, vt16 * 16 + n16, 8 * g4);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                f32x4 acc;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = X[rt][c][e] * __expf(sm.Ag[CK][rt * 16 + 4 * g4 + e]);
+                const Frag<1> a = f16frag(&sm.KhT[0][0], LDT, rt * 16 + n16, 8 * g4);
+                acc = mma<1>(a, rb, acc);
+                if (is_s) {
+                    const Frag<1> a2 = f16frag(&sm.KhpT[0][0], LDT, rt * 16 + n16, 8 * g4);
+                    acc = mma<1>(a2, vb, acc);
+                }
+                X[rt][c] = acc;
+            }
+        }
+        // ---- 6. renormalise the T columns by a power of two when they get small
+        float m = 0.f;
+#pragma unroll
+        for (int c = 0; c < CTW; ++c) {
+            const int ct = wave + 8 * c;
+            if (ct < RT) {
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(X[rt][c][e]));
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+        if (lane == 0) sm.red[wave] = m;
+        __syncthreads();
+        float mm = 0.f;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) mm = fmaxf(mm, sm.red[w]);
+        int em = 0;
+        if (mm > 0.f) frexpf(mm, &em);
+        if (t_live && (mm == 0.f || log2s + em < -120)) {  // T is below the floor for good
+            t_live = false;
+#pragma unroll
+            for (int c = 0; c < CTW; ++c)
+                if (wave + 8 * c < RT)
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) X[rt][c] = zero4();
+        } else if (mm < 0x1p-16f) {
+            const int e = em;
+            const float sc = ldexpf(1.f, -e);
+#pragma unroll
+            for (int c = 0; c < CTW; ++c) {
+                if (wave + 8 * c < RT) {
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) X[rt][c] *= sc;
+                }
+            }
+            log2s += e;
+        }
+        __syncthreads();
+    }
+
+    const size_t pair = (size_t)seg * H + h;
+#pragma unroll
+    for (int c = 0; c < CTW; ++c) {
+        const int ct = wave + 8 * c;
+        if (ct >= NCT) continue;
+        const bool is_s = ct >= RT;
+        if (!is_s && T_out == nullptr) continue;
+        float* dst = is_s ? S_out + pair * D * D + (ct - RT) * 16 : T_out + pair * D * D + ct * 16;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                dst[(size_t)(rt * 16 + 4 * g4 + e) * D + n16] = is_s ? X[rt][c][e] : ldexpf(X[rt][c][e], log2s);
+    }
+}
+
+hipError_t build_kda(int d, bool in_bf16, int n_seg, int H, const int64_t* sb, const int64_t* se, int64_t n_tok,
+                     const void* k, const void* v, const void* g, const void* beta, float* T_out, float* S_out,
+                     hipStream_t st)
+{
+    if (!in_bf16) return hipErrorNotSupported;
+    const uint16_t *k16 = static_cast<const uint16_t*>(k), *v16 = static_cast<const uint16_t*>(v),
+                   *g16 = static_cast<const uint16_t*>(g), *b16 = static_cast<const uint16_t*>(beta);
+    if (d == 128) {
+        hipLaunchKernelGGL(build_kda_kernel<128>, dim3(n_seg * H), dim3(512), 0, st, n_seg, H, sb, se, n_tok, k16,
+                           v16, g16, b16, T_out, S_out);
+        return hipGetLastError();
+    }
+    if (d == 64) {
+        hipLaunchKernelGGL(build_kda_kernel<64>, dim3(n_seg * H), dim3(512), 0, st, n_seg, H, sb, se, n_tok, k16,
+                           v16, g16, b16, T_out, S_out);
+        return hipGetLastError();
+    }
+    return hipErrorNotSupported;
+}
+
+}  // namespace hypic

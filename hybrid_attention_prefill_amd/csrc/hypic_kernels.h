@@ -29,6 +29,11 @@ hipError_t build_gdn(int d, bool in_bf16, int n_seg, int H, const int64_t* sb, c
                      int64_t n_tok, const void* k, const void* v, const void* g, const void* beta,
                      float* T_out, float* S_out, hipStream_t st);
 
+// build_kda.hip (per-channel gate, delta rule; bf16 inputs)
+hipError_t build_kda(int d, bool in_bf16, int n_seg, int H, const int64_t* sb, const int64_t* se, int64_t n_tok,
+                     const void* k, const void* v, const void* g, const void* beta, float* T_out, float* S_out,
+                     hipStream_t st);
+
 // build_decay.hip (scalar gate or head-constant decay, no erase)
 hipError_t build_decay(int d, bool in_bf16, bool head_gate, int n_seg, int H, const int64_t* sb,
                        const int64_t* se, int64_t n_tok, const void* k, const void* v, const void* g,

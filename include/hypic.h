@@ -94,8 +94,12 @@ typedef struct {
  *   n_tokens           : length of the packed token arrays (ranges are clamped)
  *   beta               : ignored (may be NULL) when delta == 0
  *   T_out              : may be NULL to skip T (S only)
- * Implemented: (HEAD, delta 0) any d in {16,32,64,128} with d_k == d_v;
- * (TOKEN, delta 1) and (DIAG, delta 1) for d_k == d_v in {16, 128}.
+ * Implemented (d_k == d_v = d):
+ *   gate HEAD or TOKEN, delta 0 : d in {16, 32, 64, 128}, fp32 or bf16 inputs;
+ *   gate TOKEN, delta 1         : d = 16 (fp32 or bf16), 64 or 128 (bf16);
+ *   gate DIAG,  delta 1         : d = 64 or 128, bf16 inputs.
+ * Other combinations return HYPIC_E_UNSUPPORTED.  For the delta-rule kernels
+ * the state and values must stay within fp16 range (|entries| < 6e4).
  */
 hypic_status hypic_segment_build(const hypic_dims* dims, int32_t n_seg,
                                  const int64_t* seg_begin, const int64_t* seg_end,
@@ -137,7 +141,7 @@ hypic_status hypic_compose(const hypic_dims* dims, int32_t n_chain, int32_t n_st
  *   workspace  : device scratch of hypic_seam_workspace_bytes(...) bytes,
  *                owned by the caller, 256-byte aligned; contents are
  *                overwritten; concurrent calls need distinct workspaces.
- * Implemented: (TOKEN, delta 1) with d_k == d_v == 128 or 16.
+ * Implemented: gate TOKEN, delta 1, d_k == d_v in {16, 32, 64, 128}, dense T.
  */
 hypic_status hypic_seam_advance(const hypic_dims* dims, int32_t n_chain, int32_t n_step,
                                 int32_t w, const int64_t* seam_start, int64_t n_tokens,

@@ -134,3 +134,39 @@ def test_cfg3_full_size_sampled():
         T0, S0 = oracle.segment_build(W.k[b:e, h:h + 1], W.v[b:e, h:h + 1], W.g[b:e, h:h + 1],
                                       W.beta[b:e, h:h + 1], [0], [e - b], gate=W.gate, delta=True)
         assert_pairs_close(T[s:s + 1, h:h + 1], S[s:s + 1, h:h + 1], T0, S0, TOL["bf16"], f"seg {s} head {h}")
+
+
+@pytest.mark.parametrize("stress", [False, True])
+def test_cfg5_kda_ragged(stress):
+    """KDA-style per-channel gate, d=128, bf16: several chunks, ragged tails, one token."""
+    W = wl.make(5, stress=stress, n_heads=2, lengths=[256, 100, 33, 1], n_req=1, n_step=1, n_layers=1)
+    print(W.name, "ragged", flush=True)
+    T, S = _gpu_build(W)
+    T0, S0 = _oracle_build(W)
+    eS, eT = assert_pairs_close(T, S, T0, S0, TOL["bf16"], W.name)
+    print(f"{W.name}: S {eS:.2e} T {eT}")
+
+
+def test_cfg5_kda_stress_compose_matches_full():
+    W = wl.make(5, stress=True, n_heads=2, n_seg=4, seg_len=300, n_req=1, n_step=1, n_layers=1)
+    T, S = _gpu_build(W)
+    Rg = torch.zeros((1, 2, 128, 128), device="cuda")
+    hb.compose(dev(T, torch.float32), dev(S, torch.float32), dev(np.arange(4, dtype=np.int32)[None, :], torch.int32), Rg)
+    torch.cuda.synchronize()
+    full, _ = oracle.run(W.k, W.v, W.g, W.beta, gate=W.gate, delta=True)
+    assert rel_f(Rg.cpu().numpy()[0], full).max() <= TOL["bf16"]
+    naive = oracle.naive_sum(S, np.arange(4)[None, :])[0]
+    assert rel_f(naive, full).min() > 20 * TOL["bf16"]
+
+
+def test_cfg5_segment_shape_all_heads_sampled():
+    """32 heads x 2048-token segments (the KDA workload's segment shape), sampled checks."""
+    W = wl.make(5, n_seg=3, n_req=1, n_step=1, n_layers=1)
+    print(W.name, "32 heads x 3 x 2048", flush=True)
+    T, S = _gpu_build(W)
+    assert np.all(np.isfinite(S)) and np.all(np.isfinite(T))
+    for s, h in [(0, 0), (1, 17), (2, 31)]:
+        b, e = W.cache_begin[s], W.cache_end[s]
+        T0, S0 = oracle.segment_build(W.k[b:e, h:h + 1], W.v[b:e, h:h + 1], W.g[b:e, h:h + 1],
+                                      W.beta[b:e, h:h + 1], [0], [e - b], gate=W.gate, delta=True)
+        assert_pairs_close(T[s:s + 1, h:h + 1], S[s:s + 1, h:h + 1], T0, S0, TOL["bf16"], f"seg {s} head {h}")
