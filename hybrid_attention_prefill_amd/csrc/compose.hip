@@ -23,8 +23,11 @@
 #include "hypic_device.h"
 #include "hypic_kernels.h"
 #include "seam_layout.h"
+#include "build_common.h"
 
 namespace hypic {
+using bld::FragB;
+using bld::dpair_to_fragb;
 
 template <int DK, int DV, int NB, bool SEAM>
 __global__ __launch_bounds__(256) void compose_dense_kernel(
@@ -39,15 +42,14 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(
     constexpr int CT = NB / 16;             // 16-column tiles of the block
     constexpr int RTW = (RT + 3) / 4;       // row tiles per wave
     constexpr int LDB = KP + 8;             // LDS row length (16-bit units), padded
-    __shared__ __attribute__((aligned(16))) uint16_t Rh[2][NB][LDB];
-    __shared__ __attribute__((aligned(16))) uint16_t Rl[2][NB][LDB];
-    // seam window: K^T (hi, lo; k = window token), U'' (hi, lo; k = window token),
-    // Y and Z = scale Q R (fp32)
     constexpr int LDW = 32 + 8;
     constexpr int SW = SEAM ? 1 : 0;
-    __shared__ __attribute__((aligned(16))) uint16_t Kw[2][SW ? DK : 1][LDW];
-    __shared__ __attribute__((aligned(16))) uint16_t Uw[2][SW ? NB : 1][LDW];
-    __shared__ float Ysh[SW ? kSeamMaxW : 1][NB + 1], Zsh[SW ? kSeamMaxW : 1][NB + 1];
+    constexpr int W16 = kSeamMaxW;
+    static_assert(!SEAM || CT <= 4, "seam epilogue: one wave per column tile");
+    __shared__ __attribute__((aligned(16))) uint16_t Rh[2][NB][LDB];   // R, bf16 hi, [column][row]
+    __shared__ __attribute__((aligned(16))) uint16_t Rl[2][NB][LDB];   // R, bf16 lo
+    __shared__ __attribute__((aligned(16))) uint16_t Uh[SW ? NB : 1][LDW];   // U'' hi, [column][token]
+    __shared__ __attribute__((aligned(16))) uint16_t Ul[SW ? NB : 1][LDW];
 
     const UnitSlot us = xcd_unit_slot(blockIdx.x, NCB);
     if (us.unit >= n_units) return;
@@ -61,9 +63,11 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(
             (&Rl[0][0][0])[i] = 0;
         }
     }
-    if constexpr (SEAM) {  // window tokens 16..31 of the k = token operands stay zero
-        for (int i = threadIdx.x; i < 2 * DK * LDW; i += blockDim.x) (&Kw[0][0][0])[i] = 0;
-        for (int i = threadIdx.x; i < 2 * NB * LDW; i += blockDim.x) (&Uw[0][0][0])[i] = 0;
+    if constexpr (SEAM) {  // window tokens 16..31 of the k = token operand stay zero
+        for (int i = threadIdx.x; i < NB * LDW; i += blockDim.x) {
+            (&Uh[0][0])[i] = 0;
+            (&Ul[0][0])[i] = 0;
+        }
     }
     __syncthreads();
 
@@ -101,99 +105,212 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(
     store_split(0);
     __syncthreads();
 
-    // ---- one seam window (SEAM only): reads R from planes `buf`, leaves the
-    // advanced state in the accumulators and in planes buf ^ 1.
-    auto seam_step = [&](size_t cj, int64_t s0, int buf) {
-        const float* rec = sa.ws + (cj * H + h) * SeamRec<DK>::kFloats;
-        const size_t tok_base = (size_t)s0 * H * DK + (size_t)h * DK;
-        auto ldin = [&](const void* base, size_t e) -> float {
-            return sa.in_bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[e])
-                              : reinterpret_cast<const float*>(base)[e];
-        };
-        // stage K^T of the window (k = token), split into bf16 hi + lo
-        for (int it = threadIdx.x; it < kSeamMaxW * DK; it += blockDim.x) {
-            const int t = it / DK, ch = it % DK;
-            const float x = t < sa.w ? ldin(sa.k, tok_base + (size_t)t * H * DK + ch) : 0.f;
-            __bf16 hi, lo;
-            split_bf16(x, hi, lo);
-            Kw[0][ch][t] = bf16_bits(hi);
-            Kw[1][ch][t] = bf16_bits(lo);
+    auto ldin8 = [&](const void* base, size_t e, float* out) {
+        if (sa.in_bf16) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + e);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                out[2 * x] = __uint_as_float(w[x] << 16);
+                out[2 * x + 1] = __uint_as_float(w[x] & 0xFFFF0000u);
+            }
+        } else {
+            const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + e);
+            const f32x4 a = p[0], b = p[1];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) { out[x] = a[x]; out[4 + x] = b[x]; }
         }
-        // Y = Wt R (tile x < CT) and Z = scale Q R (tile x >= CT), 16 x NB each
-        for (int x = wave; x < 2 * CT; x += 4) {
-            const bool isz = x >= CT;
-            const int ct = isz ? x - CT : x;
-            f32x4 p = zero4();
+    };
+    auto ld8f = [&](const float* p, float* out) {
+        const f32x4 a = reinterpret_cast<const f32x4*>(p)[0], b = reinterpret_cast<const f32x4*>(p)[1];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int k0 = ks * 32 + 8 * g4;
-                float a[8];
-                if (k0 < DK) {
-                    if (!isz) {
-                        const f32x4* src = reinterpret_cast<const f32x4*>(rec + SeamRec<DK>::kWt + n16 * DK + k0);
-                        const f32x4 x0 = src[0], x1 = src[1];
+        for (int x = 0; x < 4; ++x) { out[x] = a[x]; out[4 + x] = b[x]; }
+    };
+    auto split8 = [&](const float* a, bf16x8& hi, bf16x8& lo) {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) { a[e] = x0[e]; a[4 + e] = x1[e]; }
+        for (int e = 0; e < 8; ++e) {
+            __bf16 x, y;
+            split_bf16(a[e], x, y);
+            hi[e] = x;
+            lo[e] = y;
+        }
+    };
+
+    // ---- what a step's first products read (T rows, window Wt and q rows): loaded one step ahead.
+    // The rest of a step's inputs (S block, window factors and keys) is loaded when the step
+    // starts; its latency overlaps the step's MFMAs.
+    struct Step {
+        int id;          // pair index, or -1
+        int64_t s0;      // seam window start, or -1
+        float ta[RTW][KS][8];      // T rows of this wave (A operand)
+        float wt[SW ? KS : 1][8];  // Wt row (A operand), waves < CT
+        float qa[SW ? KS : 1][8];  // scale * q row (A operand), waves < CT
+    };
+    const int32_t* ids = pair_id ? pair_id + (size_t)c * n_step : nullptr;
+    auto load_step = [&](int j, Step& st) {
+        st.id = ids ? ids[j] : -1;
+        if ((unsigned)st.id >= (unsigned)n_pair) st.id = -1;
+        st.s0 = -1;
+        if constexpr (SEAM) {
+            const int64_t s0 = sa.seam_start[(size_t)c * n_step + j];
+            if (s0 >= 0 && s0 + sa.w <= sa.n_tokens) st.s0 = s0;
+        }
+        if (st.id >= 0) {
+            const float* T = Tc + ((size_t)st.id * H + h) * DK * DK;
+#pragma unroll
+            for (int i = 0; i < RTW; ++i) {
+                const int rt = wave + 4 * i;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int k0 = ks * 32 + 8 * g4;
+                    if (rt < RT && k0 < DK) ld8f(T + (size_t)(rt * 16 + n16) * DK + k0, st.ta[i][ks]);
+                    else
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) st.ta[i][ks][e] = 0.f;
+                }
+            }
+        }
+        if constexpr (SEAM) {
+            if (st.s0 >= 0 && wave < CT) {
+                const size_t cj = (size_t)c * n_step + j;
+                const float* rec = sa.ws + (cj * H + h) * SeamRec<DK>::kFloats;
+                const size_t tok = (size_t)(st.s0 + n16) * H * DK + (size_t)h * DK;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int k0 = ks * 32 + 8 * g4;
+                    if (k0 < DK) {
+                        ld8f(rec + SeamRec<DK>::kWt + n16 * DK + k0, st.wt[ks]);
+                        if (n16 < sa.w) {
+                            ldin8(sa.q, tok + k0, st.qa[ks]);
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) st.qa[ks][e] *= sa.scale;
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) st.qa[ks][e] = 0.f;
+                        }
                     } else {
 #pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            a[e] = n16 < sa.w ? sa.scale * ldin(sa.q, tok_base + (size_t)n16 * H * DK + k0 + e) : 0.f;
+                        for (int e = 0; e < 8; ++e) { st.wt[ks][e] = 0.f; st.qa[ks][e] = 0.f; }
                     }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) a[e] = 0.f;
                 }
-                bf16x8 ah, al;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    __bf16 hi, lo;
-                    split_bf16(a[e], hi, lo);
-                    ah[e] = hi;
-                    al[e] = lo;
-                }
-                const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&Rh[buf][ct * 16 + n16][ks * 32 + 8 * g4]);
-                const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&Rl[buf][ct * 16 + n16][ks * 32 + 8 * g4]);
-                p = mma_bf16(ah, bh, p);
-                p = mma_bf16(ah, bl, p);
-                p = mma_bf16(al, bh, p);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (isz) Zsh[4 * g4 + e][ct * 16 + n16] = p[e];
-                else Ysh[4 * g4 + e][ct * 16 + n16] = p[e];
             }
         }
-        __syncthreads();
-        // window outputs and U'' = diag(e^{b_w - b}) U'  (k = token operand)
-        const float* eb = rec + SeamRec<DK>::kEb;
-        const float* ebw = rec + SeamRec<DK>::kEbw;
-        const float* Mo = rec + SeamRec<DK>::kMo;
-        const float* Ur = rec + SeamRec<DK>::kU;
-        for (int it = threadIdx.x; it < kSeamMaxW * NB; it += blockDim.x) {
-            const int t = it / NB, n = it % NB;
-            const int col = cb * NB + n;
-            float o = eb[t] * Zsh[t][n];
-            for (int s = 0; s <= t; ++s) o += Mo[t * kSeamMaxW + s] * (Ur[s * DV + col] - eb[s] * Ysh[s][n]);
-            if (t < sa.w) sa.out[((cj * sa.w + t) * H + h) * DV + col] = o;
-            const float u2 = ebw[t] * (Ur[t * DV + col] - eb[t] * Ysh[t][n]);
-            __bf16 hi, lo;
-            split_bf16(u2, hi, lo);
-            Uw[0][n][t] = bf16_bits(hi);
-            Uw[1][n][t] = bf16_bits(lo);
-        }
-        __syncthreads();
-        // R <- e^{b_w} R + K^T U''
-        const float ebW = rec[SeamRec<DK>::kEbW];
+    };
+
+    // ---- R <- T R + S on the planes `buf` (result in the accumulators)
+    auto compose_step = [&](const Step& st, int buf) {
+        const float* S = Sc + ((size_t)st.id * H + h) * DK * DV + cb * NB;
 #pragma unroll
         for (int i = 0; i < RTW; ++i) {
             const int rt = wave + 4 * i;
             if (rt >= RT) continue;
-            const bf16x8 kh = *reinterpret_cast<const bf16x8*>(&Kw[0][rt * 16 + n16][8 * g4]);
-            const bf16x8 kl = *reinterpret_cast<const bf16x8*>(&Kw[1][rt * 16 + n16][8 * g4]);
+            float sv[CT][4];
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sv[ct][e] = S[(size_t)(rt * 16 + 4 * g4 + e) * DV + ct * 16 + n16];
+            f32x4 p[CT];
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) p[ct] = zero4();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                bf16x8 ah, al;
+                split8(st.ta[i][ks], ah, al);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&Rh[buf][ct * 16 + n16][ks * 32 + 8 * g4]);
+                    const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&Rl[buf][ct * 16 + n16][ks * 32 + 8 * g4]);
+                    p[ct] = mma_bf16(ah, bh, p[ct]);
+                    p[ct] = mma_bf16(ah, bl, p[ct]);
+                    p[ct] = mma_bf16(al, bh, p[ct]);
+                }
+            }
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i][ct][e] = p[ct][e] + sv[ct][e];
+        }
+    };
+
+    // ---- one seam window on the planes `buf`: outputs, then R <- e^{b_w} R + K^T U''
+    auto seam_step = [&](const Step& st, int buf, size_t cj) {
+        const float* rec = sa.ws + (cj * H + h) * SeamRec<DK>::kFloats;
+        const float ebW = rec[SeamRec<DK>::kEbW];
+        float kt[RTW][8];   // window K^T rows of this wave (A operand, k = token)
+#pragma unroll
+        for (int i = 0; i < RTW; ++i) {
+            const int rt = wave + 4 * i;
+            if (rt < RT && g4 < 2) ld8f(rec + SeamRec<DK>::kKt + (rt * 16 + n16) * W16 + 8 * g4, kt[i]);
+            else
+#pragma unroll
+                for (int e = 0; e < 8; ++e) kt[i][e] = 0.f;
+        }
+        if (wave < CT) {
+            const int ct = wave;
+            float mo[8], ur[4], eb[4], ebw[4];
+            if (g4 < 2) ld8f(rec + SeamRec<DK>::kMo + n16 * W16 + 8 * g4, mo);
+            else
+#pragma unroll
+                for (int e = 0; e < 8; ++e) mo[e] = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 4 * g4 + e;
+                ur[e] = rec[SeamRec<DK>::kU + t * DV + cb * NB + ct * 16 + n16];
+                eb[e] = rec[SeamRec<DK>::kEb + t];
+                ebw[e] = rec[SeamRec<DK>::kEbw + t];
+            }
+            f32x4 y = zero4(), z = zero4();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&Rh[buf][ct * 16 + n16][ks * 32 + 8 * g4]);
+                const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&Rl[buf][ct * 16 + n16][ks * 32 + 8 * g4]);
+                bf16x8 ah, al;
+                split8(st.wt[ks], ah, al);
+                y = mma_bf16(ah, bh, y);
+                y = mma_bf16(ah, bl, y);
+                y = mma_bf16(al, bh, y);
+                split8(st.qa[ks], ah, al);
+                z = mma_bf16(ah, bh, z);
+                z = mma_bf16(ah, bl, z);
+                z = mma_bf16(al, bh, z);
+            }
+            f32x4 u;   // U' = U - diag(e^b) Y, rows t = 4 g4 + e
+#pragma unroll
+            for (int e = 0; e < 4; ++e) u[e] = ur[e] - eb[e] * y[e];
+            // O = diag(e^b) Z + Mo U'  (U' as the B operand, tokens 16..31 zero)
+            const FragB ub = dpair_to_fragb(u, zero4());
+            bf16x8 mh, ml;
+            split8(mo, mh, ml);
+            f32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = eb[e] * z[e];
+            o = mma_bf16(mh, ub.h, o);
+            o = mma_bf16(mh, ub.l, o);
+            o = mma_bf16(ml, ub.h, o);
+            const int col = cb * NB + ct * 16 + n16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 4 * g4 + e;
+                if (t < sa.w) sa.out[((cj * sa.w + t) * H + h) * DV + col] = o[e];
+            }
+            f32x4 u2;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) u2[e] = ebw[e] * u[e];
+            unsigned h0, h1, l0, l1;
+            pack_bf16_split(u2, h0, h1, l0, l1);
+            *reinterpret_cast<u32x2*>(&Uh[ct * 16 + n16][4 * g4]) = u32x2{h0, h1};
+            *reinterpret_cast<u32x2*>(&Ul[ct * 16 + n16][4 * g4]) = u32x2{l0, l1};
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < RTW; ++i) {
+            const int rt = wave + 4 * i;
+            if (rt >= RT) continue;
+            bf16x8 kh, kl;
+            split8(kt[i], kh, kl);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
-                const bf16x8 uh = *reinterpret_cast<const bf16x8*>(&Uw[0][ct * 16 + n16][8 * g4]);
-                const bf16x8 ul = *reinterpret_cast<const bf16x8*>(&Uw[1][ct * 16 + n16][8 * g4]);
+                const bf16x8 uh = *reinterpret_cast<const bf16x8*>(&Uh[ct * 16 + n16][8 * g4]);
+                const bf16x8 ul = *reinterpret_cast<const bf16x8*>(&Ul[ct * 16 + n16][8 * g4]);
                 f32x4 a = acc[i][ct] * ebW;
                 a = mma_bf16(kh, uh, a);
                 a = mma_bf16(kh, ul, a);
@@ -201,84 +318,29 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(
                 acc[i][ct] = a;
             }
         }
-        store_split(buf ^ 1);
-        __syncthreads();
     };
 
     int cur = 0;
-    const int32_t* ids = pair_id ? pair_id + (size_t)c * n_step : nullptr;
+    Step st_cur;
+    if (n_step > 0) load_step(0, st_cur);
     for (int j = 0; j < n_step; ++j) {
+        Step st_nxt;
+        if (j + 1 < n_step) load_step(j + 1, st_nxt);
         if constexpr (SEAM) {
-            const size_t cj = (size_t)c * n_step + j;
-            const int64_t s0 = sa.seam_start[cj];
-            if (s0 >= 0 && s0 + sa.w <= sa.n_tokens) {  // uniform over the workgroup
-                seam_step(cj, s0, cur);
+            if (st_cur.s0 >= 0) {  // uniform over the workgroup
+                seam_step(st_cur, cur, (size_t)c * n_step + j);
+                store_split(cur ^ 1);
+                __syncthreads();
                 cur ^= 1;
             }
         }
-        const int id = ids ? ids[j] : -1;
-        if ((unsigned)id >= (unsigned)n_pair) continue;  // uniform over the workgroup
-        const float* T = Tc + ((size_t)id * H + h) * DK * DK;
-        const float* S = Sc + ((size_t)id * H + h) * DK * DV + cb * NB;
-
-        f32x4 p[RTW][CT];
-#pragma unroll
-        for (int i = 0; i < RTW; ++i)
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) p[i][ct] = zero4();
-
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            bf16x8 bh[CT], bl[CT];
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                bh[ct] = *reinterpret_cast<const bf16x8*>(&Rh[cur][ct * 16 + n16][ks * 32 + 8 * g4]);
-                bl[ct] = *reinterpret_cast<const bf16x8*>(&Rl[cur][ct * 16 + n16][ks * 32 + 8 * g4]);
-            }
-#pragma unroll
-            for (int i = 0; i < RTW; ++i) {
-                const int rt = wave + 4 * i;
-                if (rt >= RT) continue;
-                const int k0 = ks * 32 + 8 * g4;
-                float a[8];
-                if (k0 < DK) {
-                    const f32x4* src = reinterpret_cast<const f32x4*>(T + (size_t)(rt * 16 + n16) * DK + k0);
-                    const f32x4 x0 = src[0], x1 = src[1];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) { a[e] = x0[e]; a[4 + e] = x1[e]; }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) a[e] = 0.f;
-                }
-                bf16x8 ah, al;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    __bf16 hi, lo;
-                    split_bf16(a[e], hi, lo);
-                    ah[e] = hi;
-                    al[e] = lo;
-                }
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) {
-                    p[i][ct] = mma_bf16(ah, bh[ct], p[i][ct]);
-                    p[i][ct] = mma_bf16(ah, bl[ct], p[i][ct]);
-                    p[i][ct] = mma_bf16(al, bh[ct], p[i][ct]);
-                }
-            }
+        if (st_cur.id >= 0) {  // uniform over the workgroup
+            compose_step(st_cur, cur);
+            store_split(cur ^ 1);
+            __syncthreads();
+            cur ^= 1;
         }
-#pragma unroll
-        for (int i = 0; i < RTW; ++i) {
-            const int rt = wave + 4 * i;
-            if (rt >= RT) continue;
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    acc[i][ct][e] = p[i][ct][e] + S[(size_t)(rt * 16 + 4 * g4 + e) * DV + ct * 16 + n16];
-        }
-        store_split(cur ^ 1);
-        __syncthreads();
-        cur ^= 1;
+        if (j + 1 < n_step) st_cur = st_nxt;
     }
 
 #pragma unroll

@@ -94,6 +94,10 @@ __global__ __launch_bounds__(256) void seam_prep_kernel(
         for (int r = 0; r < W; ++r) At[r][tid] = x[r];
     }
     __syncthreads();
+    for (int it = tid; it < W * D; it += 256) {  // window keys, channel-major, for the state update
+        const int ch = it / W, t = it % W;
+        rp[SeamRec<D>::kKt + ch * W + t] = Ks[t][ch];
+    }
     for (int it = tid; it < W * D; it += 256) {
         const int t = it / D, ch = it % D;
         float wk = 0.f, uv = 0.f;

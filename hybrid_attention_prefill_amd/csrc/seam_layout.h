@@ -13,7 +13,8 @@ struct SeamRec {
     static constexpr int kEb = kMo + kSeamMaxW * kSeamMaxW;  // [16] e^{b_t}
     static constexpr int kEbw = kEb + kSeamMaxW;        // [16] e^{b_w - b_t}
     static constexpr int kEbW = kEbw + kSeamMaxW;       // [1]  e^{b_w}
-    static constexpr int kFloats = (kEbW + 1 + 63) / 64 * 64;  // 256-byte records
+    static constexpr int kKt = kEbW + 4;                // [D][16] window keys, channel-major (K^T)
+    static constexpr int kFloats = (kKt + D * kSeamMaxW + 63) / 64 * 64;  // 256-byte records
 };
 
 }  // namespace hypic
