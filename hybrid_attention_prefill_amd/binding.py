@@ -60,7 +60,7 @@ def load_library(path: str = LIB_PATH):
     lib.hypic_seam_workspace_bytes.restype = ctypes.c_size_t
     lib.hypic_last_error.restype = ctypes.c_char_p
     lib.hypic_abi_version.restype = ctypes.c_int32
-    lib.hypic_selftest_layouts.argtypes = [P, P]
+    lib.hypic_selftest_layouts.argtypes = [P, P, P]
     lib.hypic_selftest_layouts.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -200,9 +200,10 @@ def seam_advance(q, k, v, g, beta, seam_start, S_run, out, *, gate, delta, w, sc
 
 
 def selftest_layouts(device="cuda"):
-    """Run the lane-layout self-test kernel; returns its 1280 raw floats (host)."""
+    """Run the lane-layout self-test kernel on in = [0, 1, ..., 255]; returns its 1600 raw floats (host)."""
     lib = load_library()
-    out = torch.full((1280,), float("nan"), device=device, dtype=torch.float32)
-    _check(lib.hypic_selftest_layouts(_ptr(out), _stream(None)))
+    inp = torch.arange(256, device=device, dtype=torch.float32)
+    out = torch.full((1600,), float("nan"), device=device, dtype=torch.float32)
+    _check(lib.hypic_selftest_layouts(_ptr(inp), _ptr(out), _stream(None)))
     torch.cuda.synchronize()
     return out.cpu().numpy()

@@ -170,11 +170,11 @@ hypic_status hypic_seam_advance(const hypic_dims* dims, int32_t n_chain, int32_t
 }
 
 // Diagnostic: runs the lane-layout self-test kernel into a device buffer of
-// 1280 floats (see selftest.hip).  Not part of the method.
-hypic_status hypic_selftest_layouts(float* out, void* stream)
+// 1600 floats from 256 input floats (see selftest.hip).  Not part of the method.
+hypic_status hypic_selftest_layouts(const float* in, float* out, void* stream)
 {
-    if (!out) return fail(HYPIC_E_INVALID, "out is NULL");
-    return from_hip(hypic::selftest_layouts(out, reinterpret_cast<hipStream_t>(stream)), "hypic_selftest_layouts");
+    if (!in || !out) return fail(HYPIC_E_INVALID, "in or out is NULL");
+    return from_hip(hypic::selftest_layouts(in, out, reinterpret_cast<hipStream_t>(stream)), "hypic_selftest_layouts");
 }
 
 }  // extern "C"

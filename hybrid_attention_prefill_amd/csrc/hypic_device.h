@@ -101,6 +101,20 @@ __device__ __forceinline__ void pack_bf16_split(const f32x4& d, unsigned& h0, un
     l1 = pack2(bf16_bits(l[2]), bf16_bits(l[3]));
 }
 
+// ---- workgroup barrier for LDS traffic only ------------------------------------
+// Waits for this wave's LDS operations (lgkmcnt = 0), then s_barrier.  Unlike
+// __syncthreads() it does not wait for outstanding vector-memory loads, so loads
+// issued ahead of time (into registers, or global->LDS direct loads that only the
+// issuing wave reads back) stay in flight across it.  The empty asm statements
+// keep the compiler from moving memory accesses across the barrier.
+// s_waitcnt immediate: vmcnt = 63 (unconstrained), expcnt = 7, lgkmcnt = 0.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // ---- grid -> XCD-aware unit mapping --------------------------------------------
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup x runs on XCD
 // x % 8).  Units are dealt to XCDs round-robin and the `nsub` workgroups of one

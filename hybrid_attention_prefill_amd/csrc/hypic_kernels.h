@@ -46,6 +46,6 @@ hipError_t seam_prep(int d, int n_chain, int n_step, int H, const int64_t* seam_
 size_t seam_record_floats(int d);
 
 // selftest.hip
-hipError_t selftest_layouts(float* out, hipStream_t st);
+hipError_t selftest_layouts(const float* in, float* out, hipStream_t st);
 
 }  // namespace hypic

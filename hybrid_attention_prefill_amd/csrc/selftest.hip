@@ -12,11 +12,16 @@ namespace hypic {
 //   [256,512)  D of mfma_f32_16x16x32_bf16
 //   [512,768)  D of mfma_f32_16x16x4f32
 //   [768,1280) B fragments made by dtiles_to_bfrag (64 lanes x 8 values)
+//   [1280,1536) 16-byte global->LDS loads: lane l fetches in[4 g .. 4 g + 3] with
+//              g = (7 l) % 64 and reads back LDS bytes [16 l, 16 l + 16)
+//   [1536,1600) 4-byte global->LDS loads: lane l fetches in[(5 l) % 256], reads back [4 l, 4 l + 4)
 // Operands are filled assuming the documented lane layouts with small integer
 // matrices (exact in every type); the host recomputes D = A B and the expected
 // shuffle result and compares.
-__global__ void selftest_layout_kernel(float* out)
+__global__ void selftest_layout_kernel(const float* in, float* out)
 {
+    __shared__ __attribute__((aligned(16))) float lds16[64 * 4];
+    __shared__ __attribute__((aligned(16))) float lds4[64];
     const int l = threadIdx.x;
     const int g4 = l >> 4, n16 = l & 15;
     // A[i][k] = (3i + k) % 7 - 3,  B[k][j] = (5k + 2j) % 5 - 2
@@ -51,11 +56,18 @@ __global__ void selftest_layout_kernel(float* out)
     pack_f16(t1, q0, q1);
     const f16x8 f = as_frag<f16x8>(dtiles_to_bfrag(p0, p1, q0, q1));
     for (int j = 0; j < 8; ++j) out[768 + l * 8 + j] = (float)f[j];
+    // global -> LDS direct loads (each lane's destination is implied by its lane id)
+    __builtin_amdgcn_global_load_lds(in + ((7 * l) % 64) * 4, (__attribute__((address_space(3))) void*)lds16, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(in + (5 * l) % 256, (__attribute__((address_space(3))) void*)lds4, 4, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    for (int j = 0; j < 4; ++j) out[1280 + l * 4 + j] = lds16[l * 4 + j];
+    out[1536 + l] = lds4[l];
 }
 
-hipError_t selftest_layouts(float* out, hipStream_t st)
+hipError_t selftest_layouts(const float* in, float* out, hipStream_t st)
 {
-    hipLaunchKernelGGL(selftest_layout_kernel, dim3(1), dim3(64), 0, st, out);
+    hipLaunchKernelGGL(selftest_layout_kernel, dim3(1), dim3(64), 0, st, in, out);
     return hipGetLastError();
 }
 

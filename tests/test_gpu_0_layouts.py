@@ -28,3 +28,8 @@ def test_mfma_layouts_and_shuffle():
             row = 8 * g + j
             exp[lane, j] = row * 16 + n if row < 16 else 256 + (row - 16) * 16 + n
     np.testing.assert_array_equal(frag, exp)
+    # global -> LDS direct loads: lane l's bytes land at LDS offset (size * l)
+    lane = np.arange(64)
+    g = (7 * lane) % 64
+    np.testing.assert_array_equal(out[1280:1536].reshape(64, 4), (4 * g)[:, None] + np.arange(4)[None, :])
+    np.testing.assert_array_equal(out[1536:1600], (5 * lane) % 256)
