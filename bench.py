@@ -101,8 +101,12 @@ def main():
     q = T(W.q, dt) if W.q is not None else None
     in_bytes = 2 if W.in_dtype == "bf16" else 4
     gate_elems = {0: 0, 1: 1, 2: d}[W.gate]
-    t_layout = hb.T_SCALAR if args.config == 2 else hb.T_DENSE
+    # constant decay caches T as one number; dense T is cached in the composition kernels'
+    # operand format (bf16 hi/lo planes, 4 bytes per entry like fp32)
+    t_layout = hb.T_SCALAR if args.config == 2 else hb.T_SPLIT
     tsz = 1 if t_layout == hb.T_SCALAR else d * d
+    tdt = torch.bfloat16 if t_layout == hb.T_SPLIT else torch.float32
+    tshape = lambda n: (n, H) if t_layout == hb.T_SCALAR else (n, H, 2, d * d)
     timer = Timer(torch)
     info = {}
 
@@ -112,10 +116,11 @@ def main():
         order = np.concatenate([warm, cold])           # cache slots: warm pairs first, cold last
         slot = np.empty(W.n_seg, dtype=np.int32)
         slot[order] = np.arange(W.n_seg, dtype=np.int32)
-        Tc = torch.empty((W.n_seg, H, d, d), device=dev)
+        Tc = torch.empty(tshape(W.n_seg), device=dev, dtype=tdt)
         Sc = torch.empty((W.n_seg, H, d, d), device=dev)
         sb_all, se_all = T(W.cache_begin[order], torch.int64), T(W.cache_end[order], torch.int64)
-        hb.segment_build(k, v, g, beta, sb_all, se_all, gate=W.gate, delta=W.delta, T_out=Tc, S_out=Sc)
+        hb.segment_build(k, v, g, beta, sb_all, se_all, gate=W.gate, delta=W.delta, t_layout=t_layout,
+                         T_out=Tc, S_out=Sc)
         n_warm = len(warm)
         sb_c, se_c = T(W.cache_begin[cold], torch.int64), T(W.cache_end[cold], torch.int64)
         Tcold, Scold = Tc[n_warm:], Sc[n_warm:]
@@ -128,7 +133,8 @@ def main():
 
         def step():
             timer.run("segment_build", lambda: hb.segment_build(k, v, g, beta, sb_c, se_c, gate=W.gate,
-                                                                delta=W.delta, T_out=Tcold, S_out=Scold))
+                                                                delta=W.delta, t_layout=t_layout,
+                                                                T_out=Tcold, S_out=Scold))
             R.zero_()
             timer.run("seam_advance", lambda: hb.seam_advance(q, k, v, g, beta, seam, R, out, gate=W.gate,
                                                               delta=W.delta, w=W.w, scale=W.scale, pair_id=ids,
@@ -148,11 +154,11 @@ def main():
         info.update(cold_segments=int(len(cold)), cold_tokens=cold_tokens, seam_windows=n_windows, w=W.w)
     else:
         sb, se = T(W.cache_begin, torch.int64), T(W.cache_end, torch.int64)
-        Tb = torch.empty((W.n_seg, H) if t_layout == hb.T_SCALAR else (W.n_seg, H, d, d), device=dev)
+        Tb = torch.empty(tshape(W.n_seg), device=dev, dtype=tdt)
         Sb = torch.empty((W.n_seg, H, d, d), device=dev)
         if args.config == 5:
             # one distinct cache copy per layer, so re-reads are not served from the 256 MB MALL
-            Tc = torch.empty((W.n_layers * W.n_seg, H, d, d), device=dev)
+            Tc = torch.empty(tshape(W.n_layers * W.n_seg), device=dev, dtype=tdt)
             Sc = torch.empty((W.n_layers * W.n_seg, H, d, d), device=dev)
         else:
             Tc, Sc = Tb, Sb
@@ -163,7 +169,8 @@ def main():
 
         if args.config == 5:
             # the 30 per-layer caches: copies of one untimed earlier build
-            hb.segment_build(k, v, g, beta, sb, se, gate=W.gate, delta=W.delta, T_out=Tb, S_out=Sb)
+            hb.segment_build(k, v, g, beta, sb, se, gate=W.gate, delta=W.delta, t_layout=t_layout,
+                             T_out=Tb, S_out=Sb)
             for l in range(W.n_layers):
                 Tc[l * W.n_seg:(l + 1) * W.n_seg].copy_(Tb)
                 Sc[l * W.n_seg:(l + 1) * W.n_seg].copy_(Sb)
@@ -228,7 +235,8 @@ def main():
         "vs_baseline": None,
         "dtype": W.in_dtype,
         "data": "synthetic",
-        "config": {"workload": W.name, "heads": H, "d_k": d, "d_v": d, **info},
+        "config": {"workload": W.name, "heads": H, "d_k": d, "d_v": d,
+                   "t_cache": {hb.T_SCALAR: "scalar f32", hb.T_SPLIT: "bf16 hi/lo planes"}[t_layout], **info},
         "compose_us_per_segment": round(chain_avg / (n_segments_composed) * 1e6, 4),
         "build_us": round(build_avg * 1e6, 2),
         "kernels": kern,

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libhypic.so")
 HYPIC_OK, HYPIC_E_INVALID, HYPIC_E_UNSUPPORTED, HYPIC_E_DEVICE = 0, 1, 2, 3
 GATE_HEAD, GATE_TOKEN, GATE_DIAG = 0, 1, 2
 F32, BF16 = 0, 1
-T_DENSE, T_SCALAR = 0, 1
+T_DENSE, T_SCALAR, T_SPLIT = 0, 1, 2
 
 EXPORTED = ("hypic_segment_build", "hypic_compose", "hypic_seam_advance", "hypic_seam_workspace_bytes",
             "hypic_last_error", "hypic_abi_version", "hypic_selftest_layouts")
@@ -101,6 +101,25 @@ def _in_dtype(t):
     raise ValueError(f"inputs must be bfloat16 or float32, got {t.dtype}")
 
 
+def _t_shape(t_layout, n, H, dk):
+    return {T_DENSE: (n, H, dk, dk), T_SCALAR: (n, H), T_SPLIT: (n, H, 2, dk * dk)}[t_layout]
+
+
+def _t_dtype(t_layout):
+    return torch.bfloat16 if t_layout == T_SPLIT else torch.float32
+
+
+def t_layout_of(T):
+    """Layout of a T cache tensor: bf16 [n,H,2,d*d] SPLIT, fp32 [n,H] SCALAR, fp32 [n,H,d,d] DENSE."""
+    if T.dtype == torch.bfloat16 and T.dim() == 4:
+        return T_SPLIT
+    if T.dtype == torch.float32 and T.dim() == 2:
+        return T_SCALAR
+    if T.dtype == torch.float32 and T.dim() == 4:
+        return T_DENSE
+    raise ValueError(f"T cache of dtype {T.dtype} and shape {tuple(T.shape)} matches no T layout")
+
+
 def make_dims(H, dk, dv, *, gate, delta, in_dtype, t_layout=T_DENSE):
     return Dims(int(H), int(dk), int(dv), int(gate), int(bool(delta)), int(in_dtype), int(t_layout))
 
@@ -133,10 +152,9 @@ def segment_build(k, v, g, beta, seg_begin, seg_end, *, gate, delta, t_layout=T_
         S_out = torch.empty((n_seg, H, dk, dv), device=k.device, dtype=torch.float32)
     _dev(S_out, "S_out", torch.float32, (n_seg, H, dk, dv))
     if want_T and T_out is None:
-        shape = (n_seg, H) if t_layout == T_SCALAR else (n_seg, H, dk, dk)
-        T_out = torch.empty(shape, device=k.device, dtype=torch.float32)
+        T_out = torch.empty(_t_shape(t_layout, n_seg, H, dk), device=k.device, dtype=_t_dtype(t_layout))
     if T_out is not None:
-        _dev(T_out, "T_out", torch.float32)
+        _dev(T_out, "T_out", _t_dtype(t_layout), _t_shape(t_layout, n_seg, H, dk))
     d = make_dims(H, dk, dv, gate=gate, delta=delta, in_dtype=dt, t_layout=t_layout)
     _check(lib.hypic_segment_build(ctypes.byref(d), n_seg, _ptr(seg_begin), _ptr(seg_end), n_tok, _ptr(k),
                                    _ptr(v), _ptr(g), _ptr(beta) if delta else None, _ptr(T_out),
@@ -144,15 +162,15 @@ def segment_build(k, v, g, beta, seg_begin, seg_end, *, gate, delta, t_layout=T_
     return T_out, S_out
 
 
-def compose(T_cache, S_cache, pair_id, S_run, *, t_layout=T_DENSE, stream=None):
-    """In place: S_run[c] <- T[id] S_run[c] + S[id] along each chain -- hypic_compose."""
+def compose(T_cache, S_cache, pair_id, S_run, *, t_layout=None, stream=None):
+    """In place: S_run[c] <- T[id] S_run[c] + S[id] along each chain -- hypic_compose.
+    The T layout is taken from T_cache's dtype and rank unless given."""
     lib = load_library()
     _dev(S_cache, "S_cache", torch.float32)
     n_pair, H, dk, dv = S_cache.shape
-    if t_layout == T_SCALAR:
-        _dev(T_cache, "T_cache", torch.float32, (n_pair, H))
-    else:
-        _dev(T_cache, "T_cache", torch.float32, (n_pair, H, dk, dk))
+    if t_layout is None:
+        t_layout = t_layout_of(T_cache)
+    _dev(T_cache, "T_cache", _t_dtype(t_layout), _t_shape(t_layout, n_pair, H, dk))
     _dev(pair_id, "pair_id", torch.int32)
     n_chain, n_step = pair_id.shape
     _dev(S_run, "S_run", torch.float32, (n_chain, H, dk, dv))
@@ -182,16 +200,19 @@ def seam_advance(q, k, v, g, beta, seam_start, S_run, out, *, gate, delta, w, sc
     n_chain, n_step = seam_start.shape
     _dev(S_run, "S_run", torch.float32, (n_chain, H, dk, dv))
     _dev(out, "out", torch.float32, (n_chain, n_step, w, H, dv))
-    n_pair = 0
+    n_pair, t_layout = 0, T_DENSE
     if pair_id is not None:
         _dev(pair_id, "pair_id", torch.int32, (n_chain, n_step))
         _dev(S_cache, "S_cache", torch.float32)
         n_pair = S_cache.shape[0]
-        _dev(T_cache, "T_cache", torch.float32, (n_pair, H, dk, dk))
+        t_layout = t_layout_of(T_cache)
+        if t_layout == T_SCALAR:
+            raise ValueError("seam_advance needs a dense T cache (DENSE or SPLIT layout)")
+        _dev(T_cache, "T_cache", _t_dtype(t_layout), _t_shape(t_layout, n_pair, H, dk))
     need = seam_workspace_bytes(H, dk, dv, n_chain, n_step, w, gate=gate, delta=delta, in_dtype=dt)
     if workspace is None and need > 0:
         workspace = torch.empty(need, device=k.device, dtype=torch.uint8)
-    d = make_dims(H, dk, dv, gate=gate, delta=delta, in_dtype=dt)
+    d = make_dims(H, dk, dv, gate=gate, delta=delta, in_dtype=dt, t_layout=t_layout)
     _check(lib.hypic_seam_advance(ctypes.byref(d), n_chain, n_step, w, _ptr(seam_start), n_tok, _ptr(q),
                                   _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(pair_id), n_pair,
                                   _ptr(T_cache), _ptr(S_cache), _ptr(S_run), _ptr(out), _ptr(workspace),

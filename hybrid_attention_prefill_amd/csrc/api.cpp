@@ -50,8 +50,8 @@ hypic_status check_dims(const hypic_dims* d)
     if (d->delta != 0 && d->delta != 1) return fail(HYPIC_E_INVALID, "delta must be 0 or 1 (got %d)", d->delta);
     if (d->in_dtype != HYPIC_F32 && d->in_dtype != HYPIC_BF16)
         return fail(HYPIC_E_INVALID, "in_dtype must be 0 (f32) or 1 (bf16) (got %d)", d->in_dtype);
-    if (d->t_layout != HYPIC_T_DENSE && d->t_layout != HYPIC_T_SCALAR)
-        return fail(HYPIC_E_INVALID, "t_layout must be 0 (dense) or 1 (scalar) (got %d)", d->t_layout);
+    if (d->t_layout != HYPIC_T_DENSE && d->t_layout != HYPIC_T_SCALAR && d->t_layout != HYPIC_T_SPLIT)
+        return fail(HYPIC_E_INVALID, "t_layout must be 0 (dense), 1 (scalar) or 2 (split) (got %d)", d->t_layout);
     if (d->t_layout == HYPIC_T_SCALAR && (d->delta || d->gate == HYPIC_GATE_DIAG))
         return fail(HYPIC_E_INVALID, "a scalar T exists only for scalar gates without the delta rule");
     return ok();
@@ -69,7 +69,7 @@ const char* hypic_last_error(void) { return g_last_error.c_str(); }
 
 hypic_status hypic_segment_build(const hypic_dims* dims, int32_t n_seg, const int64_t* seg_begin,
                                  const int64_t* seg_end, int64_t n_tokens, const void* k, const void* v,
-                                 const void* g, const void* beta, float* T_out, float* S_out, void* stream)
+                                 const void* g, const void* beta, void* T_out, float* S_out, void* stream)
 {
     if (hypic_status s = check_dims(dims)) return s;
     if (n_seg < 0) return fail(HYPIC_E_INVALID, "n_seg must be >= 0 (got %d)", n_seg);
@@ -86,17 +86,18 @@ hypic_status hypic_segment_build(const hypic_dims* dims, int32_t n_seg, const in
     if (!dims->delta && dims->gate != HYPIC_GATE_DIAG) {
         return from_hip(hypic::build_decay(dims->d_k, bf16, dims->gate == HYPIC_GATE_HEAD, n_seg,
                                            dims->n_heads, seg_begin, seg_end, n_tokens, k, v, g, T_out,
-                                           dims->t_layout == HYPIC_T_SCALAR, S_out, st),
+                                           dims->t_layout, S_out, st),
                         "hypic_segment_build");
     }
     if (dims->delta && dims->gate == HYPIC_GATE_TOKEN) {
         return from_hip(hypic::build_gdn(dims->d_k, bf16, n_seg, dims->n_heads, seg_begin, seg_end,
-                                         n_tokens, k, v, g, beta, T_out, S_out, st),
+                                         n_tokens, k, v, g, beta, T_out,
+                                         dims->t_layout == HYPIC_T_SPLIT, S_out, st),
                         "hypic_segment_build");
     }
     if (dims->delta && dims->gate == HYPIC_GATE_DIAG) {
         return from_hip(hypic::build_kda(dims->d_k, bf16, n_seg, dims->n_heads, seg_begin, seg_end, n_tokens, k,
-                                         v, g, beta, T_out, S_out, st),
+                                         v, g, beta, T_out, dims->t_layout == HYPIC_T_SPLIT, S_out, st),
                         "hypic_segment_build");
     }
     return fail(HYPIC_E_UNSUPPORTED, "hypic_segment_build: gate %d with delta %d is not implemented",
@@ -104,7 +105,7 @@ hypic_status hypic_segment_build(const hypic_dims* dims, int32_t n_seg, const in
 }
 
 hypic_status hypic_compose(const hypic_dims* dims, int32_t n_chain, int32_t n_step, const int32_t* pair_id,
-                           int32_t n_pair, const float* T_cache, const float* S_cache, float* S_run,
+                           int32_t n_pair, const void* T_cache, const float* S_cache, float* S_run,
                            void* stream)
 {
     if (hypic_status s = check_dims(dims)) return s;
@@ -117,11 +118,11 @@ hypic_status hypic_compose(const hypic_dims* dims, int32_t n_chain, int32_t n_st
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (dims->t_layout == HYPIC_T_SCALAR)
         return from_hip(hypic::compose_scalar(dims->d_k, dims->d_v, n_chain, dims->n_heads, n_step, pair_id,
-                                              n_pair, T_cache, S_cache, S_run, st),
+                                              n_pair, static_cast<const float*>(T_cache), S_cache, S_run, st),
                         "hypic_compose");
     if (dims->d_k != dims->d_v) return fail(HYPIC_E_UNSUPPORTED, "d_k != d_v is not implemented");
     return from_hip(hypic::compose_dense(dims->d_k, n_chain, dims->n_heads, n_step, pair_id, n_pair, T_cache,
-                                         S_cache, S_run, nullptr, st),
+                                         dims->t_layout == HYPIC_T_SPLIT, S_cache, S_run, nullptr, st),
                     "hypic_compose");
 }
 
@@ -129,13 +130,13 @@ size_t hypic_seam_workspace_bytes(const hypic_dims* dims, int32_t n_chain, int32
 {
     if (!dims || dims->n_heads < 1 || !valid_d(dims->d_k) || dims->d_k != dims->d_v) return 0;
     if (n_chain < 0 || n_step < 0 || w < 1 || w > 16) return 0;
-    return (size_t)n_chain * n_step * dims->n_heads * hypic::seam_record_floats(dims->d_k) * sizeof(float);
+    return (size_t)n_chain * n_step * dims->n_heads * hypic::seam_record_bytes(dims->d_k);
 }
 
 hypic_status hypic_seam_advance(const hypic_dims* dims, int32_t n_chain, int32_t n_step, int32_t w,
                                 const int64_t* seam_start, int64_t n_tokens, const void* q, const void* k,
                                 const void* v, const void* g, const void* beta, float scale,
-                                const int32_t* pair_id, int32_t n_pair, const float* T_cache,
+                                const int32_t* pair_id, int32_t n_pair, const void* T_cache,
                                 const float* S_cache, float* S_run, float* out, void* workspace,
                                 size_t workspace_bytes, void* stream)
 {
@@ -149,7 +150,8 @@ hypic_status hypic_seam_advance(const hypic_dims* dims, int32_t n_chain, int32_t
     if (pair_id && n_pair > 0 && (!T_cache || !S_cache)) return fail(HYPIC_E_INVALID, "T_cache or S_cache is NULL");
     if (dims->gate != HYPIC_GATE_TOKEN || !dims->delta)
         return fail(HYPIC_E_UNSUPPORTED, "hypic_seam_advance: only the scalar-gated delta rule is implemented");
-    if (dims->t_layout != HYPIC_T_DENSE) return fail(HYPIC_E_UNSUPPORTED, "hypic_seam_advance needs dense T");
+    if (dims->t_layout == HYPIC_T_SCALAR)
+        return fail(HYPIC_E_UNSUPPORTED, "hypic_seam_advance needs a dense T (layout DENSE or SPLIT)");
     if (dims->d_k != dims->d_v) return fail(HYPIC_E_UNSUPPORTED, "d_k != d_v is not implemented");
     if ((long long)n_chain * n_step * dims->n_heads > kMaxGrid || (long long)n_chain * dims->n_heads * 8 > kMaxGrid)
         return fail(HYPIC_E_INVALID, "too many chains or steps");
@@ -159,13 +161,14 @@ hypic_status hypic_seam_advance(const hypic_dims* dims, int32_t n_chain, int32_t
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(HYPIC_E_INVALID, "workspace must be 256-byte aligned");
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const bool bf16 = dims->in_dtype == HYPIC_BF16;
-    float* ws = static_cast<float*>(workspace);
+    void* ws = workspace;
     hipError_t e = hypic::seam_prep(dims->d_k, n_chain, n_step, dims->n_heads, seam_start, n_tokens, w, q, k, v,
                                     g, beta, bf16, scale, ws, st);
     if (e != hipSuccess) return from_hip(e, "hypic_seam_advance (window preparation)");
     hypic::SeamArgs sa{seam_start, n_tokens, w, (int)bf16, scale, q, k, ws, out};
     return from_hip(hypic::compose_dense(dims->d_k, n_chain, dims->n_heads, n_step, pair_id,
-                                         pair_id ? n_pair : 0, T_cache, S_cache, S_run, &sa, st),
+                                         pair_id ? n_pair : 0, T_cache, dims->t_layout == HYPIC_T_SPLIT, S_cache,
+                                         S_run, &sa, st),
                     "hypic_seam_advance");
 }
 

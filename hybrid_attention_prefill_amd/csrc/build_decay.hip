@@ -33,7 +33,7 @@ template <int D, bool BF16, bool HEAD_GATE>
 __global__ __launch_bounds__(256) void build_decay_kernel(
     int n_seg, int H, const int64_t* __restrict__ seg_begin, const int64_t* __restrict__ seg_end,
     int64_t n_tokens, const void* __restrict__ k, const void* __restrict__ v,
-    const void* __restrict__ gl, float* __restrict__ T_out, int t_scalar, float* __restrict__ S_out)
+    const void* __restrict__ gl, void* __restrict__ T_out, int t_layout, float* __restrict__ S_out)
 {
     constexpr int RT = D / 16;
     constexpr int NT = RT * RT;            // output tiles
@@ -132,35 +132,34 @@ __global__ __launch_bounds__(256) void build_decay_kernel(
     }
     if (T_out) {
         const float tval = expf(log_t);
-        if (t_scalar) {
-            if (tid == 0) T_out[pair] = tval;
-        } else {
-            float* T = T_out + pair * D * D;
-            for (int it = tid; it < D * D; it += 256) T[it] = (it / D == it % D) ? tval : 0.f;
+        if (t_layout == 1) {   // scalar
+            if (tid == 0) reinterpret_cast<float*>(T_out)[pair] = tval;
+        } else {               // dense gamma^L I, fp32 or bf16 hi/lo planes
+            for (int it = tid; it < D * D; it += 256) put_t(T_out, t_layout == 2, pair, D, it / D, it % D, (it / D == it % D) ? tval : 0.f);
         }
     }
 }
 
 template <int D, bool BF16, bool HEAD>
 static hipError_t launch_decay(int n_seg, int H, const int64_t* sb, const int64_t* se, int64_t n_tok,
-                               const void* k, const void* v, const void* g, float* T_out, int t_scalar,
+                               const void* k, const void* v, const void* g, void* T_out, int t_layout,
                                float* S_out, hipStream_t st)
 {
     hipLaunchKernelGGL((build_decay_kernel<D, BF16, HEAD>), dim3(n_seg * H), dim3(256), 0, st, n_seg, H,
-                       sb, se, n_tok, k, v, g, T_out, t_scalar, S_out);
+                       sb, se, n_tok, k, v, g, T_out, t_layout, S_out);
     return hipGetLastError();
 }
 
 hipError_t build_decay(int d, bool in_bf16, bool head_gate, int n_seg, int H, const int64_t* sb,
                        const int64_t* se, int64_t n_tok, const void* k, const void* v, const void* g,
-                       float* T_out, int t_scalar, float* S_out, hipStream_t st)
+                       void* T_out, int t_layout, float* S_out, hipStream_t st)
 {
 #define HYPIC_CASE(D_)                                                                                  \
     if (d == D_) {                                                                                      \
-        if (in_bf16 && head_gate) return launch_decay<D_, true, true>(n_seg, H, sb, se, n_tok, k, v, g, T_out, t_scalar, S_out, st);   \
-        if (in_bf16 && !head_gate) return launch_decay<D_, true, false>(n_seg, H, sb, se, n_tok, k, v, g, T_out, t_scalar, S_out, st); \
-        if (!in_bf16 && head_gate) return launch_decay<D_, false, true>(n_seg, H, sb, se, n_tok, k, v, g, T_out, t_scalar, S_out, st); \
-        return launch_decay<D_, false, false>(n_seg, H, sb, se, n_tok, k, v, g, T_out, t_scalar, S_out, st);                          \
+        if (in_bf16 && head_gate) return launch_decay<D_, true, true>(n_seg, H, sb, se, n_tok, k, v, g, T_out, t_layout, S_out, st);   \
+        if (in_bf16 && !head_gate) return launch_decay<D_, true, false>(n_seg, H, sb, se, n_tok, k, v, g, T_out, t_layout, S_out, st); \
+        if (!in_bf16 && head_gate) return launch_decay<D_, false, true>(n_seg, H, sb, se, n_tok, k, v, g, T_out, t_layout, S_out, st); \
+        return launch_decay<D_, false, false>(n_seg, H, sb, se, n_tok, k, v, g, T_out, t_layout, S_out, st);                          \
     }
     HYPIC_CASE(16) HYPIC_CASE(32) HYPIC_CASE(64) HYPIC_CASE(128)
 #undef HYPIC_CASE

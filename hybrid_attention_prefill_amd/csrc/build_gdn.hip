@@ -115,7 +115,7 @@ template <int D, int NSPLIT, bool BF16>
 __global__ __launch_bounds__(512) void build_gdn_kernel(
     int n_seg, int H, const int64_t* __restrict__ seg_begin, const int64_t* __restrict__ seg_end,
     int64_t n_tokens, const void* __restrict__ k, const void* __restrict__ v,
-    const void* __restrict__ gl, const void* __restrict__ beta, float* __restrict__ T_out,
+    const void* __restrict__ gl, const void* __restrict__ beta, void* __restrict__ T_out, int t_split,
     float* __restrict__ S_out)
 {
     using SM = GdnSmem<D, NSPLIT>;
@@ -352,34 +352,35 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
         if (ct >= NCT) continue;
         const bool is_s = ct >= RT;
         if (!is_s && T_out == nullptr) continue;
-        float* dst = is_s ? S_out + pair * D * D + (ct - RT) * 16 : T_out + pair * D * D + ct * 16;
-        const float sc = is_s ? 1.f : tscale;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                dst[(size_t)(rt * 16 + 4 * g4 + e) * D + n16] = sc * X[rt][c][e];
+            for (int e = 0; e < 4; ++e) {
+                const int row = rt * 16 + 4 * g4 + e;
+                if (is_s) S_out[pair * D * D + (size_t)row * D + (ct - RT) * 16 + n16] = X[rt][c][e];
+                else put_t(T_out, t_split, pair, D, row, ct * 16 + n16, tscale * X[rt][c][e]);
+            }
     }
 }
 
 template <int D, int NSPLIT, bool BF16>
 static hipError_t launch_gdn(int n_seg, int H, const int64_t* sb, const int64_t* se, int64_t n_tok,
                              const void* k, const void* v, const void* g, const void* beta,
-                             float* T_out, float* S_out, hipStream_t st)
+                             void* T_out, bool t_split, float* S_out, hipStream_t st)
 {
     hipLaunchKernelGGL((build_gdn_kernel<D, NSPLIT, BF16>), dim3(n_seg * H), dim3(512), 0, st, n_seg,
-                       H, sb, se, n_tok, k, v, g, beta, T_out, S_out);
+                       H, sb, se, n_tok, k, v, g, beta, T_out, (int)t_split, S_out);
     return hipGetLastError();
 }
 
 hipError_t build_gdn(int d, bool in_bf16, int n_seg, int H, const int64_t* sb, const int64_t* se,
                      int64_t n_tok, const void* k, const void* v, const void* g, const void* beta,
-                     float* T_out, float* S_out, hipStream_t st)
+                     void* T_out, bool t_split, float* S_out, hipStream_t st)
 {
-    if (d == 128 && in_bf16) return launch_gdn<128, 1, true>(n_seg, H, sb, se, n_tok, k, v, g, beta, T_out, S_out, st);
-    if (d == 64 && in_bf16) return launch_gdn<64, 1, true>(n_seg, H, sb, se, n_tok, k, v, g, beta, T_out, S_out, st);
-    if (d == 16 && !in_bf16) return launch_gdn<16, 2, false>(n_seg, H, sb, se, n_tok, k, v, g, beta, T_out, S_out, st);
-    if (d == 16 && in_bf16) return launch_gdn<16, 1, true>(n_seg, H, sb, se, n_tok, k, v, g, beta, T_out, S_out, st);
+    if (d == 128 && in_bf16) return launch_gdn<128, 1, true>(n_seg, H, sb, se, n_tok, k, v, g, beta, T_out, t_split, S_out, st);
+    if (d == 64 && in_bf16) return launch_gdn<64, 1, true>(n_seg, H, sb, se, n_tok, k, v, g, beta, T_out, t_split, S_out, st);
+    if (d == 16 && !in_bf16) return launch_gdn<16, 2, false>(n_seg, H, sb, se, n_tok, k, v, g, beta, T_out, t_split, S_out, st);
+    if (d == 16 && in_bf16) return launch_gdn<16, 1, true>(n_seg, H, sb, se, n_tok, k, v, g, beta, T_out, t_split, S_out, st);
     return hipErrorNotSupported;
 }
 

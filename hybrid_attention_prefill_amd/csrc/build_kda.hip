@@ -81,8 +81,8 @@ template <int D>
 __global__ __launch_bounds__(512) void build_kda_kernel(
     int n_seg, int H, const int64_t* __restrict__ seg_begin, const int64_t* __restrict__ seg_end,
     int64_t n_tokens, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ gl, const uint16_t* __restrict__ beta, float* __restrict__ T_out,
-    float* __restrict__ S_out)
+    const uint16_t* __restrict__ gl, const uint16_t* __restrict__ beta, void* __restrict__ T_out,
+    int t_split, float* __restrict__ S_out)
 {
     using SM = KdaSmem<D>;
     constexpr int RT = D / 16;
@@ -397,30 +397,32 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
         if (ct >= NCT) continue;
         const bool is_s = ct >= RT;
         if (!is_s && T_out == nullptr) continue;
-        float* dst = is_s ? S_out + pair * D * D + (ct - RT) * 16 : T_out + pair * D * D + ct * 16;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                dst[(size_t)(rt * 16 + 4 * g4 + e) * D + n16] = is_s ? X[rt][c][e] : ldexpf(X[rt][c][e], log2s);
+            for (int e = 0; e < 4; ++e) {
+                const int row = rt * 16 + 4 * g4 + e;
+                if (is_s) S_out[pair * D * D + (size_t)row * D + (ct - RT) * 16 + n16] = X[rt][c][e];
+                else put_t(T_out, t_split, pair, D, row, ct * 16 + n16, ldexpf(X[rt][c][e], log2s));
+            }
     }
 }
 
 hipError_t build_kda(int d, bool in_bf16, int n_seg, int H, const int64_t* sb, const int64_t* se, int64_t n_tok,
-                     const void* k, const void* v, const void* g, const void* beta, float* T_out, float* S_out,
-                     hipStream_t st)
+                     const void* k, const void* v, const void* g, const void* beta, void* T_out, bool t_split,
+                     float* S_out, hipStream_t st)
 {
     if (!in_bf16) return hipErrorNotSupported;
     const uint16_t *k16 = static_cast<const uint16_t*>(k), *v16 = static_cast<const uint16_t*>(v),
                    *g16 = static_cast<const uint16_t*>(g), *b16 = static_cast<const uint16_t*>(beta);
     if (d == 128) {
         hipLaunchKernelGGL(build_kda_kernel<128>, dim3(n_seg * H), dim3(512), 0, st, n_seg, H, sb, se, n_tok, k16,
-                           v16, g16, b16, T_out, S_out);
+                           v16, g16, b16, T_out, (int)t_split, S_out);
         return hipGetLastError();
     }
     if (d == 64) {
         hipLaunchKernelGGL(build_kda_kernel<64>, dim3(n_seg * H), dim3(512), 0, st, n_seg, H, sb, se, n_tok, k16,
-                           v16, g16, b16, T_out, S_out);
+                           v16, g16, b16, T_out, (int)t_split, S_out);
         return hipGetLastError();
     }
     return hipErrorNotSupported;

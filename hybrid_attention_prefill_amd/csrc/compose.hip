@@ -10,39 +10,38 @@
 // block needs all of T; the blocks of one (chain, head) are placed on the same
 // XCD so T is fetched from HBM once and served to the others from L2.
 // The running state stays in fp32 MFMA accumulators for the whole chain; each
-// step it is re-split into bf16 hi + lo planes in LDS (the B operand), T is
-// split the same way in registers (the A operand), and the product is taken as
-// hi*hi + hi*lo + lo*hi on v_mfma_f32_16x16x32_bf16 (relative error ~2^-16,
-// with fp32's exponent range, so tiny T entries are not flushed).
+// step it is re-split into bf16 hi + lo planes in LDS (the B operand).  T is the
+// A operand, as bf16 hi + lo planes: cached that way by the build kernels (T layout
+// SPLIT, loaded as is) or split in registers from fp32.  The product is taken as
+// hi*hi + hi*lo + lo*hi on v_mfma_f32_16x16x32_bf16 (relative error ~2^-16, with
+// fp32's exponent range, so tiny T entries are not flushed).
 //
 // With SEAM (hypic_seam_advance, [ZH] section 2.2) a step may first advance the
 // state through its seam window using the state-independent window factors
-// prepared by seam.hip: Y = Wt R and Z = scale Q R on MFMA, then the window
-// outputs O = diag(e^b) Z + Mo U' and the rank-16 update
+// prepared by seam.hip: Y = Wt R and Z = Q R on MFMA, then the window outputs
+// O = scale diag(e^b) Z + Mo U' and the rank-16 update
 // R <- e^{b_w} R + K^T diag(e^{b_w-b}) U', U' = U - diag(e^b) Y.
 #include "hypic_device.h"
 #include "hypic_kernels.h"
 #include "seam_layout.h"
-#include "build_common.h"
 
 namespace hypic {
-using bld::FragB;
 
 // s_waitcnt immediate (gfx9 encoding) that waits for every outstanding vector-memory
-// load (including global->LDS direct loads) and every LDS access: vmcnt = 0,
-// expcnt = 7 (unconstrained), lgkmcnt = 0.
-constexpr unsigned kWaitVmcnt0 = 0x0070;   // also lgkmcnt = 0: LDS reads of the stage being refilled are done
+// operation (loads, stores and global->LDS direct loads) and every LDS access:
+// vmcnt = 0, expcnt = 7 (unconstrained), lgkmcnt = 0.
+constexpr unsigned kWaitVmcnt0 = 0x0070;
 constexpr int kRing = 512, kRingFill = 256;   // LDS ring of per-step pair ids / seam starts
-using bld::dpair_to_fragb;
 
-// waves per workgroup: one 16-row tile of the state per wave for plain composition at
-// d_k = 128; the seam variant keeps four (its window factors need the register room)
-constexpr int chain_waves(int dk, bool seam) { return (dk >= 128 && !seam) ? 8 : 4; }
+// waves per workgroup: one 16-row tile of the state per wave at d_k = 128
+constexpr int chain_waves(int dk) { return dk >= 128 ? 8 : 4; }
 
-template <int DK, int DV, int NB, bool SEAM>
-__global__ __launch_bounds__(64 * chain_waves(DK, SEAM)) void compose_dense_kernel(
+// TS: T cached as bf16 hi/lo planes ([n_pair][H][2][DK][DK], hypic_t_layout SPLIT),
+// fed to the MFMA units as loaded; otherwise fp32 T, split in registers.
+template <int DK, int DV, int NB, bool SEAM, bool TS>
+__global__ __launch_bounds__(64 * chain_waves(DK)) void compose_dense_kernel(
     int n_units, int H, int n_step, const int32_t* __restrict__ pair_id, int n_pair,
-    const float* __restrict__ Tc, const float* __restrict__ Sc, float* __restrict__ Srun,
+    const void* __restrict__ Tc, const float* __restrict__ Sc, float* __restrict__ Srun,
     SeamArgs sa)
 {
     constexpr int NCB = DV / NB;
@@ -50,15 +49,13 @@ __global__ __launch_bounds__(64 * chain_waves(DK, SEAM)) void compose_dense_kern
     constexpr int KS = KP / 32;
     constexpr int RT = DK / 16;             // 16-row tiles of the state
     constexpr int CT = NB / 16;             // 16-column tiles of the block
-    constexpr int NW = chain_waves(DK, SEAM);
+    constexpr int NW = chain_waves(DK);
     constexpr int RTW = (RT + NW - 1) / NW; // row tiles per wave
     constexpr int LDB = KP + 8;             // LDS row length (16-bit units), padded
     constexpr int LDW = 32 + 8;
     constexpr int SW = SEAM ? 1 : 0;
-    constexpr int W16 = kSeamMaxW;
+    using Rec = SeamRec<DK>;
     static_assert(!SEAM || CT == 1, "seam path: one 16-column tile per workgroup");
-    constexpr bool PF_S = RTW * CT * 4 <= 16;   // prefetch the S block too when it is small
-    // tile ct's Y = Wt R (state path) runs on wave ct, its Z = scale Q R (outputs) on wave CT + ct
     __shared__ __attribute__((aligned(16))) uint16_t Rh[2][NB][LDB];   // R, bf16 hi, [column][row]
     __shared__ __attribute__((aligned(16))) uint16_t Rl[2][NB][LDB];   // R, bf16 lo
     __shared__ __attribute__((aligned(16))) uint16_t Uh[SW ? 2 : 1][SW ? NB : 1][LDW];  // [U'' | U'] hi, [col][token]
@@ -66,16 +63,17 @@ __global__ __launch_bounds__(64 * chain_waves(DK, SEAM)) void compose_dense_kern
     __shared__ int ring_id[kRing];
     __shared__ int64_t ring_s0[SW ? kRing : 1];
     // Seam window factors of the next step, fetched by global->LDS direct loads into
-    // wave-private regions (two stages).  Each lane reads back exactly the bytes it
-    // fetched (lane l's 16 or 4 bytes land at offset 16 l or 4 l of a 1 KiB or 256 B slot).
-    //   per wave: Kt slots [RTW][2] (all waves), ebW slot
-    //   wave 0 (Y): Wt slots [KS][2], U and e^{b_w-b} dword slots [8], e^b dword slots [4]
-    //   wave 1 (Z): q slots [KS][2], Mo slots [2], e^b dword slots [4]
-    constexpr int KT_SLOTS = SW ? RTW * 2 : 1;
-    __shared__ __attribute__((aligned(16))) f32x4 st_kt[SW ? 2 : 1][SW ? NW : 1][KT_SLOTS][64];
-    __shared__ __attribute__((aligned(16))) f32x4 st_xa[SW ? 2 : 1][SW ? 2 : 1][SW ? KS * 2 : 1][64];
-    __shared__ __attribute__((aligned(16))) float st_yz[SW ? 2 : 1][SW ? 2 : 1][SW ? 8 : 1][64];
-    __shared__ __attribute__((aligned(16))) float st_eb[SW ? 2 : 1][SW ? 2 : 1][SW ? 4 : 1][64];
+    // wave-private slots (two stages).  Lane l's 16 (or 4) bytes land at byte 16 l (4 l)
+    // of a slot, and each lane reads back exactly what it fetched.
+    //   every wave: K^T hi/lo of its row tiles, e^{b_w}
+    //   wave 0 (Y = Wt R): Wt hi/lo, U block and e^{b_w - b} (dwords), e^b
+    //   wave 1 (Z = Q R, outputs): q hi/lo, Mo hi/lo, e^b
+    __shared__ __attribute__((aligned(16))) u32x4 st_k[SW ? 2 : 1][SW ? NW : 1][SW ? RTW : 1][2][64];
+    __shared__ __attribute__((aligned(16))) u32x4 st_w[SW ? 2 : 1][SW ? KS : 1][2][64];
+    __shared__ __attribute__((aligned(16))) u32x4 st_q[SW ? 2 : 1][SW ? KS : 1][2][64];
+    __shared__ __attribute__((aligned(16))) u32x4 st_m[SW ? 2 : 1][2][64];
+    __shared__ __attribute__((aligned(16))) float st_u[SW ? 2 : 1][SW ? 8 : 1][64];
+    __shared__ __attribute__((aligned(16))) float st_eb[SW ? 2 : 1][2][4][64];
     __shared__ __attribute__((aligned(16))) float st_ebw[SW ? 2 : 1][SW ? NW : 1][64];
 
     const UnitSlot us = xcd_unit_slot(blockIdx.x, NCB);
@@ -132,29 +130,10 @@ __global__ __launch_bounds__(64 * chain_waves(DK, SEAM)) void compose_dense_kern
     store_split(0);
     __syncthreads();
 
-    auto ldin8 = [&](const void* base, size_t e, float* out) {
-        if (sa.in_bf16) {
-            const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + e);
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                out[2 * x] = __uint_as_float(w[x] << 16);
-                out[2 * x + 1] = __uint_as_float(w[x] & 0xFFFF0000u);
-            }
-        } else {
-            const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + e);
-            const f32x4 a = p[0], b = p[1];
-#pragma unroll
-            for (int x = 0; x < 4; ++x) { out[x] = a[x]; out[4 + x] = b[x]; }
-        }
-    };
     auto ld8f = [&](const float* p, float* out) {
         const f32x4 a = reinterpret_cast<const f32x4*>(p)[0], b = reinterpret_cast<const f32x4*>(p)[1];
 #pragma unroll
         for (int x = 0; x < 4; ++x) { out[x] = a[x]; out[4 + x] = b[x]; }
-    };
-    auto zero8 = [&](float* a) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] = 0.f;
     };
     auto split8 = [&](const float* a, bf16x8& hi, bf16x8& lo) {
 #pragma unroll
@@ -165,14 +144,19 @@ __global__ __launch_bounds__(64 * chain_waves(DK, SEAM)) void compose_dense_kern
             lo[e] = y;
         }
     };
+    auto rfrag = [&](const uint16_t (*P)[LDB], int col, int k0) -> bf16x8 {
+        return *reinterpret_cast<const bf16x8*>(&P[col][k0]);
+    };
 
     // ---- everything a step reads besides the running state, loaded one step ahead into
     // one of two register sets (the loop is unrolled by two, so the sets never get copied)
     struct Step {
-        int id;                    // pair index, or -1
-        int64_t s0;                // seam window start, or -1
-        float ta[RTW][KS][8];      // T rows of this wave (A operand)
-        float sv[PF_S ? RTW : 1][PF_S ? CT : 1][4];  // S block (D layout), when prefetched
+        int id;                                        // pair index, or -1
+        int64_t s0;                                    // seam window start, or -1
+        u32x4 th[TS ? RTW : 1][TS ? KS : 1];           // T rows of this wave, bf16 hi (A operand)
+        u32x4 tl[TS ? RTW : 1][TS ? KS : 1];           //                      bf16 lo
+        float ta[TS ? 1 : RTW][TS ? 1 : KS][8];        // T rows, fp32
+        float sv[RTW][CT][4];                          // S block (D layout)
     };
     const int32_t* ids = pair_id ? pair_id + (size_t)c * n_step : nullptr;
     const int64_t* seams = SEAM ? sa.seam_start + (size_t)c * n_step : nullptr;
@@ -190,86 +174,91 @@ __global__ __launch_bounds__(64 * chain_waves(DK, SEAM)) void compose_dense_kern
         if constexpr (!SEAM) return -1;
         return ring_s0[j & (kRing - 1)];
     };
+    // The loads below are unconditional (addresses clamped into the pair; lanes and waves
+    // outside the tile are masked where the values are used): a load whose result is
+    // selected or copied right away makes the compiler wait for it, and with the in-order
+    // vector-memory counter that would wait for the whole prefetch.
     auto load_step = [&](int j, int id, int64_t s0, Step& st) {
-        id = (unsigned)id < (unsigned)n_pair ? id : -1;
-        if constexpr (SEAM) s0 = (s0 >= 0 && s0 + sa.w <= sa.n_tokens) ? s0 : -1;
+        id = __builtin_amdgcn_readfirstlane((unsigned)id < (unsigned)n_pair ? id : -1);
+        if constexpr (SEAM) {
+            s0 = (s0 >= 0 && s0 + sa.w <= sa.n_tokens) ? s0 : -1;
+            s0 = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane((unsigned)((uint64_t)s0 >> 32)) << 32) |
+                           (uint64_t)__builtin_amdgcn_readfirstlane((unsigned)(uint64_t)s0));
+        }
         st.id = id;
         st.s0 = s0;
         if (id >= 0) {
-            const float* T = Tc + ((size_t)id * H + h) * DK * DK;
             const float* S = Sc + ((size_t)id * H + h) * DK * DV + cb * NB;
 #pragma unroll
             for (int i = 0; i < RTW; ++i) {
-                const int rt = wave + NW * i;
+                const int rt = (RTW * NW == RT) ? wave + NW * i : min(wave + NW * i, RT - 1);
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const int k0 = ks * 32 + 8 * g4;
-                    if (rt < RT && k0 < DK) ld8f(T + (size_t)(rt * 16 + n16) * DK + k0, st.ta[i][ks]);
-                    else zero8(st.ta[i][ks]);
+                    const int k0 = KP == DK ? ks * 32 + 8 * g4 : min(ks * 32 + 8 * g4, DK - 8);
+                    if constexpr (TS) {   // fragment-ordered planes: the wave reads 1 KiB contiguous
+                        const uint16_t* T = reinterpret_cast<const uint16_t*>(Tc) + ((size_t)id * H + h) * 2 * DK * DK;
+                        const int e = frag_off(rt * 16 + n16, k0, DK);
+                        st.th[i][ks] = *reinterpret_cast<const u32x4*>(T + e);
+                        st.tl[i][ks] = *reinterpret_cast<const u32x4*>(T + DK * DK + e);
+                    } else {
+                        ld8f(reinterpret_cast<const float*>(Tc) + ((size_t)id * H + h) * DK * DK +
+                             (size_t)(rt * 16 + n16) * DK + k0, st.ta[i][ks]);
+                    }
                 }
-                if constexpr (PF_S) {
 #pragma unroll
-                    for (int ct = 0; ct < CT; ++ct)
+                for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            st.sv[i][ct][e] = rt < RT ? S[(size_t)(rt * 16 + 4 * g4 + e) * DV + ct * 16 + n16] : 0.f;
-                }
+                    for (int e = 0; e < 4; ++e)
+                        st.sv[i][ct][e] = S[(size_t)(rt * 16 + 4 * g4 + e) * DV + ct * 16 + n16];
             }
         }
         if constexpr (SEAM) {
             if (s0 >= 0) {
                 const int sg = j & 1;
                 const size_t cj = (size_t)c * n_step + j;
-                const float* rec = sa.ws + (cj * H + h) * SeamRec<DK>::kFloats;
-                auto dma16 = [&](const void* src, void* slot) {
+                const unsigned char* rec = reinterpret_cast<const unsigned char*>(sa.ws) + (cj * H + h) * Rec::kBytes;
+                auto dma16 = [&](const unsigned char* src, void* slot) {
                     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)slot, 16, 0, 0);
                 };
-                auto dma4 = [&](const void* src, void* slot) {
+                auto dma4 = [&](const unsigned char* src, void* slot) {
                     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)slot, 4, 0, 0);
                 };
-                const int gk = g4 & 1;   // lanes g4 >= 2 fetch a duplicate (ignored), keeping addresses valid
+                const int gk = g4 & 1;   // lanes g4 >= 2 fetch a duplicate (zeroed at use)
 #pragma unroll
                 for (int i = 0; i < RTW; ++i) {
                     const int rt = (wave + NW * i) < RT ? wave + NW * i : 0;
 #pragma unroll
-                    for (int hf = 0; hf < 2; ++hf)
-                        dma16(rec + SeamRec<DK>::kKt + (rt * 16 + n16) * W16 + 8 * gk + 4 * hf, &st_kt[sg][wave][2 * i + hf][0]);
+                    for (int p = 0; p < 2; ++p)
+                        dma16(rec + Rec::kK + p * Rec::kPlaneWD + frag_off(rt * 16 + n16, 8 * gk, 16) * 2, &st_k[sg][wave][i][p][0]);
                 }
-                dma4(rec + SeamRec<DK>::kEbW, &st_ebw[sg][wave][0]);
+                dma4(rec + Rec::kEbW, &st_ebw[sg][wave][0]);
                 if (wave < 2) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) dma4(rec + SeamRec<DK>::kEb + 4 * g4 + e, &st_eb[sg][wave][e][0]);
+                    for (int e = 0; e < 4; ++e) dma4(rec + Rec::kEb + (4 * g4 + e) * 4, &st_eb[sg][wave][e][0]);
                 }
                 if (wave == 0) {   // Y wave: Wt rows, U block, e^{b_w - b}
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks) {
-                        const int k0 = (ks * 32 + 8 * g4) < DK ? ks * 32 + 8 * g4 : 0;
+                        const int k0 = (ks * 32 + 8 * g4) < DK ? ks * 32 + 8 * g4 : 0;   // past DK: B rows are zero
 #pragma unroll
-                        for (int hf = 0; hf < 2; ++hf)
-                            dma16(rec + SeamRec<DK>::kWt + n16 * DK + k0 + 4 * hf, &st_xa[sg][0][2 * ks + hf][0]);
+                        for (int p = 0; p < 2; ++p)
+                            dma16(rec + Rec::kW + p * Rec::kPlaneWD + frag_off(n16, k0, DK) * 2, &st_w[sg][ks][p][0]);
                     }
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        dma4(rec + SeamRec<DK>::kU + (4 * g4 + e) * DV + cb * NB + n16, &st_yz[sg][0][e][0]);
-                        dma4(rec + SeamRec<DK>::kEbw + 4 * g4 + e, &st_yz[sg][0][4 + e][0]);
+                        dma4(rec + Rec::kU + ((4 * g4 + e) * DV + cb * NB + n16) * 4, &st_u[sg][e][0]);
+                        dma4(rec + Rec::kEbw + (4 * g4 + e) * 4, &st_u[sg][4 + e][0]);
                     }
-                } else if (wave == 1) {   // Z wave: q rows (raw bits), Mo row
-                    const int tq = n16 < sa.w ? n16 : sa.w - 1;   // rows past the window are masked at use
-                    const size_t tok = (size_t)(s0 + tq) * H * DK + (size_t)h * DK;
+                } else if (wave == 1) {   // Z wave: q rows, Mo rows
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks) {
                         const int k0 = (ks * 32 + 8 * g4) < DK ? ks * 32 + 8 * g4 : 0;
-                        if (sa.in_bf16) {
-                            dma16(reinterpret_cast<const uint16_t*>(sa.q) + tok + k0, &st_xa[sg][1][2 * ks][0]);
-                        } else {
-#pragma unroll
-                            for (int hf = 0; hf < 2; ++hf)
-                                dma16(reinterpret_cast<const float*>(sa.q) + tok + k0 + 4 * hf, &st_xa[sg][1][2 * ks + hf][0]);
-                        }
+                        dma16(rec + Rec::kQ + frag_off(n16, k0, DK) * 2, &st_q[sg][ks][0][0]);
+                        if (!sa.in_bf16) dma16(rec + Rec::kQ + Rec::kPlaneWD + frag_off(n16, k0, DK) * 2, &st_q[sg][ks][1][0]);
                     }
 #pragma unroll
-                    for (int hf = 0; hf < 2; ++hf)
-                        dma16(rec + SeamRec<DK>::kMo + n16 * W16 + 8 * gk + 4 * hf, &st_yz[sg][1][4 * hf][0]);
+                    for (int p = 0; p < 2; ++p)
+                        dma16(rec + Rec::kM + p * Rec::kPlaneM + frag_off(n16, 8 * gk, 16) * 2, &st_m[sg][p][0]);
                 }
             }
         }
@@ -277,85 +266,82 @@ __global__ __launch_bounds__(64 * chain_waves(DK, SEAM)) void compose_dense_kern
 
     // ---- R <- T R + S on the planes `buf` (result in the accumulators)
     auto compose_step = [&](const Step& st, int buf) {
-        const float* S = Sc + ((size_t)st.id * H + h) * DK * DV + cb * NB;
 #pragma unroll
         for (int i = 0; i < RTW; ++i) {
             const int rt = wave + NW * i;
             if (rt >= RT) continue;
-            float sv[CT][4];   // S block: prefetched, or loaded now (its latency overlaps the MFMAs)
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    sv[ct][e] = PF_S ? st.sv[PF_S ? i : 0][PF_S ? ct : 0][e]
-                                     : S[(size_t)(rt * 16 + 4 * g4 + e) * DV + ct * 16 + n16];
             f32x4 p[CT];
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) p[ct] = zero4();
+            for (int ct = 0; ct < CT; ++ct) p[ct] = f32x4{st.sv[i][ct][0], st.sv[i][ct][1], st.sv[i][ct][2], st.sv[i][ct][3]};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 bf16x8 ah, al;
-                split8(st.ta[i][ks], ah, al);
+                if constexpr (TS) {
+                    ah = as_frag<bf16x8>(st.th[i][ks]);
+                    al = as_frag<bf16x8>(st.tl[i][ks]);
+                } else {
+                    split8(st.ta[i][ks], ah, al);
+                }
+                if (KP > DK && ks * 32 + 8 * g4 >= DK) {   // columns past d_k (the loads were clamped)
+                    ah = as_frag<bf16x8>(u32x4{0, 0, 0, 0});
+                    al = ah;
+                }
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
-                    const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&Rh[buf][ct * 16 + n16][ks * 32 + 8 * g4]);
-                    const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&Rl[buf][ct * 16 + n16][ks * 32 + 8 * g4]);
+                    const bf16x8 bh = rfrag(Rh[buf], ct * 16 + n16, ks * 32 + 8 * g4);
+                    const bf16x8 bl = rfrag(Rl[buf], ct * 16 + n16, ks * 32 + 8 * g4);
                     p[ct] = mma_bf16(ah, bh, p[ct]);
                     p[ct] = mma_bf16(ah, bl, p[ct]);
                     p[ct] = mma_bf16(al, bh, p[ct]);
                 }
             }
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[i][ct][e] = p[ct][e] + sv[ct][e];
+            for (int ct = 0; ct < CT; ++ct) acc[i][ct] = p[ct];
         }
     };
 
-    // product of an A-operand row set (8 floats per k-step) with column tile ct of R (planes buf)
-    auto rowprod = [&](const float (*a)[8], int ct, int buf) -> f32x4 {
-        f32x4 y = zero4();
+    // ---- one seam window on the planes `buf`: R <- e^{b_w} R + K^T U'' and the window
+    // outputs.  The window factors come from the LDS stage `sg` this wave's direct loads
+    // filled.  The outputs are stored one step later (o_pend), so the wait at the top of
+    // the next step does not wait for their write acknowledgements.
+    f32x4 o_pend = zero4();
+    size_t o_cj = 0;
+    bool o_valid = false;
+    auto flush_out = [&]() {
+        if (o_valid) {
+            const int col = cb * NB + n16;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&Rh[buf][ct * 16 + n16][ks * 32 + 8 * g4]);
-            const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&Rl[buf][ct * 16 + n16][ks * 32 + 8 * g4]);
-            bf16x8 ah, al;
-            split8(a[ks], ah, al);
-            y = mma_bf16(ah, bh, y);
-            y = mma_bf16(ah, bl, y);
-            y = mma_bf16(al, bh, y);
+            for (int e = 0; e < 4; ++e) {
+                const int t = 4 * g4 + e;
+                if (t < sa.w) sa.out[((o_cj * sa.w + t) * H + h) * DV + col] = o_pend[e];
+            }
+            o_valid = false;
         }
-        return y;
     };
-
-    // ---- one seam window on the planes `buf`: R <- e^{b_w} R + K^T U'' and the window outputs.
-    // The window factors come from the LDS stage `sg` this wave's direct loads filled.
-    auto stage16 = [&](const f32x4* slot, float* out4) {
-        const f32x4 v = slot[lane];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) out4[x] = v[x];
-    };
-    auto seam_step = [&](const Step& st, int buf, size_t cj, int sg) {
+    auto seam_step = [&](int buf, size_t cj, int sg) {
         f32x4 z = zero4();
-        const bool zw = wave == 1;
         float eb[4];
         if (wave < 2) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) eb[e] = st_eb[sg][wave][e][lane];
         }
         if (wave == 0) {  // state path: Y = Wt R, U' = U - diag(e^b) Y, U'' = diag(e^{b_w - b}) U'
-            float xa[KS][8];
+            f32x4 y = zero4();
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                stage16(&st_xa[sg][0][2 * ks][0], xa[ks]);
-                stage16(&st_xa[sg][0][2 * ks + 1][0], xa[ks] + 4);
+                const bf16x8 wh = as_frag<bf16x8>(st_w[sg][ks][0][lane]);
+                const bf16x8 wl = as_frag<bf16x8>(st_w[sg][ks][1][lane]);
+                const bf16x8 bh = rfrag(Rh[buf], n16, ks * 32 + 8 * g4);
+                const bf16x8 bl = rfrag(Rl[buf], n16, ks * 32 + 8 * g4);
+                y = mma_bf16(wh, bh, y);
+                y = mma_bf16(wh, bl, y);
+                y = mma_bf16(wl, bh, y);
             }
-            const f32x4 y = rowprod(xa, 0, buf);
             f32x4 u, u2;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                u[e] = st_yz[sg][0][e][lane] - eb[e] * y[e];
-                u2[e] = st_yz[sg][0][4 + e][lane] * u[e];
+                u[e] = st_u[sg][e][lane] - eb[e] * y[e];
+                u2[e] = st_u[sg][4 + e][lane] * u[e];
             }
             unsigned h0, h1, l0, l1;
             pack_bf16_split(u2, h0, h1, l0, l1);
@@ -364,42 +350,27 @@ __global__ __launch_bounds__(64 * chain_waves(DK, SEAM)) void compose_dense_kern
             pack_bf16_split(u, h0, h1, l0, l1);
             *reinterpret_cast<u32x2*>(&Uh[1][n16][4 * g4]) = u32x2{h0, h1};
             *reinterpret_cast<u32x2*>(&Ul[1][n16][4 * g4]) = u32x2{l0, l1};
-        } else if (zw) {  // Z = scale Q R for the outputs (rows past the window are zero)
-            float qa[KS][8];
-            const float msk = n16 < sa.w ? sa.scale : 0.f;
+        } else if (wave == 1) {  // Z = Q R for the outputs (padded window rows of q are zero)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                if (sa.in_bf16) {
-                    float w4[4];
-                    stage16(&st_xa[sg][1][2 * ks][0], w4);
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) {
-                        const unsigned wv = __float_as_uint(w4[x]);
-                        qa[ks][2 * x] = msk * __uint_as_float(wv << 16);
-                        qa[ks][2 * x + 1] = msk * __uint_as_float(wv & 0xFFFF0000u);
-                    }
-                } else {
-                    stage16(&st_xa[sg][1][2 * ks][0], qa[ks]);
-                    stage16(&st_xa[sg][1][2 * ks + 1][0], qa[ks] + 4);
-#pragma unroll
-                    for (int x = 0; x < 8; ++x) qa[ks][x] *= msk;
-                }
+                const bf16x8 qh = as_frag<bf16x8>(st_q[sg][ks][0][lane]);
+                const bf16x8 bh = rfrag(Rh[buf], n16, ks * 32 + 8 * g4);
+                const bf16x8 bl = rfrag(Rl[buf], n16, ks * 32 + 8 * g4);
+                z = mma_bf16(qh, bh, z);
+                z = mma_bf16(qh, bl, z);
+                if (!sa.in_bf16) z = mma_bf16(as_frag<bf16x8>(st_q[sg][ks][1][lane]), bh, z);   // bf16 q has no lo part
             }
-            z = rowprod(qa, 0, buf);
         }
         lds_barrier();
         // state: R <- e^{b_w} R + K^T U''
         const float ebW = st_ebw[sg][wave][lane];
+        const u32x4 z4 = u32x4{0, 0, 0, 0};
 #pragma unroll
         for (int i = 0; i < RTW; ++i) {
             const int rt = wave + NW * i;
             if (rt >= RT) continue;
-            float kt[8];
-            stage16(&st_kt[sg][wave][2 * i][0], kt);
-            stage16(&st_kt[sg][wave][2 * i + 1][0], kt + 4);
-            if (g4 >= 2) zero8(kt);   // window tokens 16..31 do not exist
-            bf16x8 kh, kl;
-            split8(kt, kh, kl);
+            const bf16x8 kh = as_frag<bf16x8>(g4 < 2 ? st_k[sg][wave][i][0][lane] : z4);   // window tokens 16..31 do not exist
+            const bf16x8 kl = as_frag<bf16x8>(g4 < 2 ? st_k[sg][wave][i][1][lane] : z4);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
                 const bf16x8 uh = *reinterpret_cast<const bf16x8*>(&Uh[0][ct * 16 + n16][8 * g4]);
@@ -407,32 +378,25 @@ __global__ __launch_bounds__(64 * chain_waves(DK, SEAM)) void compose_dense_kern
                 f32x4 a = acc[i][ct] * ebW;
                 a = mma_bf16(kh, uh, a);
                 a = mma_bf16(kh, ul, a);
-                a = mma_bf16(kl, uh, a);
+                if (!sa.in_bf16) a = mma_bf16(kl, uh, a);   // bf16 keys have no lo part
                 acc[i][ct] = a;
             }
         }
-        // outputs: O = diag(e^b) Z + Mo U'   (off the state's critical path)
-        if (zw) {
-            float mo[8];
-            stage16(reinterpret_cast<const f32x4*>(&st_yz[sg][1][0][0]), mo);   // two 16-byte loads
-            stage16(reinterpret_cast<const f32x4*>(&st_yz[sg][1][4][0]), mo + 4);
-            if (g4 >= 2) zero8(mo);
-            bf16x8 mh, ml;
-            split8(mo, mh, ml);
+        // outputs: O = scale diag(e^b) Z + Mo U'   (off the state's critical path)
+        if (wave == 1) {
+            const bf16x8 mh = as_frag<bf16x8>(g4 < 2 ? st_m[sg][0][lane] : z4);
+            const bf16x8 ml = as_frag<bf16x8>(g4 < 2 ? st_m[sg][1][lane] : z4);
             const bf16x8 uh = *reinterpret_cast<const bf16x8*>(&Uh[1][n16][8 * g4]);
             const bf16x8 ul = *reinterpret_cast<const bf16x8*>(&Ul[1][n16][8 * g4]);
             f32x4 o;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = eb[e] * z[e];
+            for (int e = 0; e < 4; ++e) o[e] = sa.scale * eb[e] * z[e];
             o = mma_bf16(mh, uh, o);
             o = mma_bf16(mh, ul, o);
             o = mma_bf16(ml, uh, o);
-            const int col = cb * NB + n16;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 4 * g4 + e;
-                if (t < sa.w) sa.out[((cj * sa.w + t) * H + h) * DV + col] = o[e];
-            }
+            o_pend = o;
+            o_cj = cj;
+            o_valid = true;
         }
     };
 
@@ -440,7 +404,7 @@ __global__ __launch_bounds__(64 * chain_waves(DK, SEAM)) void compose_dense_kern
     auto run_step = [&](int j, const Step& st) {
         if constexpr (SEAM) {
             if (st.s0 >= 0) {  // uniform over the workgroup
-                seam_step(st, cur, (size_t)c * n_step + j, j & 1);
+                seam_step(cur, (size_t)c * n_step + j, j & 1);
                 store_split(cur ^ 1);
                 lds_barrier();
                 cur ^= 1;
@@ -462,11 +426,13 @@ __global__ __launch_bounds__(64 * chain_waves(DK, SEAM)) void compose_dense_kern
     int64_t s1 = read_s0(1);
     load_step(0, read_id(0), read_s0(0), sA);
     // Every load of step j was issued a whole step earlier: wait for all of them once, at the
-    // top of the step, then issue step j+1's loads.  (Using a value right after its load would
-    // make the in-order vector-memory counter drain the prefetch as well.)
+    // top of the step, then store the previous step's outputs and issue step j+1's loads.
+    // (Using a value right after its load would make the in-order vector-memory counter drain
+    // the prefetch as well.)
     for (int j = 0; j < n_step; j += 2) {
         // step j from sA; prefetch step j+1 into sB; ids of step j+2
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        if constexpr (SEAM) flush_out();
         if (j > 0 && (j & (kRingFill - 1)) == 0) {  // steps j+256 .. j+511 replace steps j-256 .. j-1
             fill_ring(j + kRingFill);
             lds_barrier();
@@ -478,11 +444,13 @@ __global__ __launch_bounds__(64 * chain_waves(DK, SEAM)) void compose_dense_kern
         if (j + 1 >= n_step) break;
         // step j+1 from sB; prefetch step j+2 into sA; ids of step j+3
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        if constexpr (SEAM) flush_out();
         id1 = read_id(j + 3);
         s1 = read_s0(j + 3);
         if (j + 2 < n_step) load_step(j + 2, id2, s2, sA);
         run_step(j + 1, sB);
     }
+    if constexpr (SEAM) flush_out();
 
 #pragma unroll
     for (int i = 0; i < RTW; ++i) {
@@ -523,24 +491,23 @@ __global__ __launch_bounds__(256) void compose_scalar_kernel(
 }
 
 // ---------------------------------------------------------------- launchers
-static constexpr int KP_OF(int dk) { return dk < 32 ? 32 : dk; }
-
-template <int DK, int DV, int NB>
+template <int DK, int DV, int NB, bool TS>
 static hipError_t launch_dense(int n_chain, int H, int n_step, const int32_t* pair_id, int n_pair,
-                               const float* Tc, const float* Sc, float* Srun, const SeamArgs* sa,
+                               const void* Tc, const float* Sc, float* Srun, const SeamArgs* sa,
                                hipStream_t st)
 {
     const int n_units = n_chain * H;
     const int grid = xcd_grid_size(n_units, DV / NB);
+    const dim3 block(64 * chain_waves(DK));
     if (sa) {
-        // the seam epilogue needs a Y wave and a Z wave per 16-column tile
+        // the seam epilogue works on 16-column blocks
         if constexpr (NB == 16)
-            hipLaunchKernelGGL((compose_dense_kernel<DK, DV, NB, true>), dim3(grid), dim3(64 * chain_waves(DK, true)), 0, st,
+            hipLaunchKernelGGL((compose_dense_kernel<DK, DV, NB, true, TS>), dim3(grid), block, 0, st,
                                n_units, H, n_step, pair_id, n_pair, Tc, Sc, Srun, *sa);
         else
             return hipErrorInvalidValue;
     } else
-        hipLaunchKernelGGL((compose_dense_kernel<DK, DV, NB, false>), dim3(grid), dim3(64 * chain_waves(DK, false)), 0, st,
+        hipLaunchKernelGGL((compose_dense_kernel<DK, DV, NB, false, TS>), dim3(grid), block, 0, st,
                            n_units, H, n_step, pair_id, n_pair, Tc, Sc, Srun, SeamArgs{});
     return hipGetLastError();
 }
@@ -555,12 +522,15 @@ static int pick_nb(long long n_units, int dv)
 }
 
 hipError_t compose_dense(int d, int n_chain, int H, int n_step, const int32_t* pair_id, int n_pair,
-                         const float* Tc, const float* Sc, float* Srun, const SeamArgs* sa, hipStream_t st)
+                         const void* Tc, bool t_split, const float* Sc, float* Srun, const SeamArgs* sa,
+                         hipStream_t st)
 {
     int nb = pick_nb((long long)n_chain * H, d);
     if (sa) nb = 16;   // the seam path works on 16-column blocks
-#define HYPIC_CASE(D_, NB_) \
-    if (d == D_ && nb == NB_) return launch_dense<D_, D_, NB_>(n_chain, H, n_step, pair_id, n_pair, Tc, Sc, Srun, sa, st);
+#define HYPIC_CASE(D_, NB_)                                                                                    \
+    if (d == D_ && nb == NB_)                                                                                  \
+        return t_split ? launch_dense<D_, D_, NB_, true>(n_chain, H, n_step, pair_id, n_pair, Tc, Sc, Srun, sa, st) \
+                       : launch_dense<D_, D_, NB_, false>(n_chain, H, n_step, pair_id, n_pair, Tc, Sc, Srun, sa, st);
     HYPIC_CASE(16, 16)
     HYPIC_CASE(32, 32) HYPIC_CASE(32, 16)
     HYPIC_CASE(64, 64) HYPIC_CASE(64, 32) HYPIC_CASE(64, 16)

@@ -101,6 +101,31 @@ __device__ __forceinline__ void pack_bf16_split(const f32x4& d, unsigned& h0, un
     l1 = pack2(bf16_bits(l[2]), bf16_bits(l[3]));
 }
 
+// ---- fragment-ordered bf16 planes ---------------------------------------------
+// A d_r x d_c matrix stored as [d_r/16][d_c/8][16][8] (16 x 8 blocks, row-major in a
+// block, blocks row-major): the A operand of v_mfma_f32_16x16x32_bf16 for row tile rt
+// and k-block ks -- lane l holding row rt*16 + l%16, columns ks*32 + 8(l/16) .. +7 --
+// is then the 1 KiB at element (rt*(d_c/8) + ks*4)*128 + 8 l, one contiguous load.
+__device__ __forceinline__ int frag_off(int row, int col, int dc) {
+    return ((row >> 4) * (dc >> 3) + (col >> 3)) * 128 + (row & 15) * 8 + (col & 7);
+}
+
+// ---- one entry of a dense T in the cache: fp32 [pair][d][d] row-major, or (split)
+// two bf16 planes [pair][2][d*d], hi = bf16(x) and lo = bf16(x - hi), fragment-ordered.
+__device__ __forceinline__ void put_t(void* T, bool split, size_t pair, int d, int row, int col, float x) {
+    const int dd = d * d;
+    if (split) {
+        __bf16 hi, lo;
+        split_bf16(x, hi, lo);
+        uint16_t* P = reinterpret_cast<uint16_t*>(T) + pair * 2 * dd;
+        const int off = frag_off(row, col, d);
+        P[off] = bf16_bits(hi);
+        P[dd + off] = bf16_bits(lo);
+    } else {
+        reinterpret_cast<float*>(T)[pair * dd + (size_t)row * d + col] = x;
+    }
+}
+
 // ---- workgroup barrier for LDS traffic only ------------------------------------
 // Waits for this wave's LDS operations (lgkmcnt = 0), then s_barrier.  Unlike
 // __syncthreads() it does not wait for outstanding vector-memory loads, so loads

@@ -14,36 +14,40 @@ struct SeamArgs {
     float scale;
     const void* q;
     const void* k;
-    const float* ws;            // records of seam_prep
+    const void* ws;             // records of seam_prep (seam_layout.h)
     float* out;                 // [n_chain][n_step][w][H][d_v]
 };
 
 // compose.hip (sa == nullptr: plain composition)
+// t_split: T as bf16 hi/lo planes [n_pair][H][2][d][d]; else fp32 [n_pair][H][d][d]
 hipError_t compose_dense(int d, int n_chain, int H, int n_step, const int32_t* pair_id, int n_pair,
-                         const float* Tc, const float* Sc, float* Srun, const SeamArgs* sa, hipStream_t st);
+                         const void* Tc, bool t_split, const float* Sc, float* Srun, const SeamArgs* sa,
+                         hipStream_t st);
 hipError_t compose_scalar(int dk, int dv, int n_chain, int H, int n_step, const int32_t* pair_id,
                           int n_pair, const float* Tc, const float* Sc, float* Srun, hipStream_t st);
 
+// Build kernels: t_split writes T as bf16 hi/lo planes [n_seg][H][2][d][d].
 // build_gdn.hip (scalar gate, delta rule)
 hipError_t build_gdn(int d, bool in_bf16, int n_seg, int H, const int64_t* sb, const int64_t* se,
                      int64_t n_tok, const void* k, const void* v, const void* g, const void* beta,
-                     float* T_out, float* S_out, hipStream_t st);
+                     void* T_out, bool t_split, float* S_out, hipStream_t st);
 
 // build_kda.hip (per-channel gate, delta rule; bf16 inputs)
 hipError_t build_kda(int d, bool in_bf16, int n_seg, int H, const int64_t* sb, const int64_t* se, int64_t n_tok,
-                     const void* k, const void* v, const void* g, const void* beta, float* T_out, float* S_out,
-                     hipStream_t st);
+                     const void* k, const void* v, const void* g, const void* beta, void* T_out, bool t_split,
+                     float* S_out, hipStream_t st);
 
-// build_decay.hip (scalar gate or head-constant decay, no erase)
+// build_decay.hip (scalar gate or head-constant decay, no erase); t_layout: 0 dense f32,
+// 1 scalar, 2 dense bf16 hi/lo planes
 hipError_t build_decay(int d, bool in_bf16, bool head_gate, int n_seg, int H, const int64_t* sb,
                        const int64_t* se, int64_t n_tok, const void* k, const void* v, const void* g,
-                       float* T_out, int t_scalar, float* S_out, hipStream_t st);
+                       void* T_out, int t_layout, float* S_out, hipStream_t st);
 
 // seam.hip
 hipError_t seam_prep(int d, int n_chain, int n_step, int H, const int64_t* seam_start, int64_t n_tokens,
                      int w, const void* q, const void* k, const void* v, const void* g, const void* beta,
-                     bool in_bf16, float scale, float* ws, hipStream_t st);
-size_t seam_record_floats(int d);
+                     bool in_bf16, float scale, void* ws, hipStream_t st);
+size_t seam_record_bytes(int d);
 
 // selftest.hip
 hipError_t selftest_layouts(const float* in, float* out, hipStream_t st);

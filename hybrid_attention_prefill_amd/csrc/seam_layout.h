@@ -1,4 +1,9 @@
 // seam_layout.h -- per-(chain, step, head) record of the seam workspace.
+//
+// Every matrix the chain kernel feeds to the MFMA units is stored as two bf16
+// planes, hi = bf16(x) and lo = bf16(x - hi), in fragment order (frag_off in
+// hypic_device.h): one contiguous 16-byte load per lane is one operand fragment,
+// and the chain kernel does no conversions.
 #pragma once
 
 namespace hypic {
@@ -7,14 +12,17 @@ constexpr int kSeamMaxW = 16;  // windows are padded to 16 tokens
 
 template <int D>
 struct SeamRec {
-    static constexpr int kWt = 0;                       // [16][D]  At diag(beta) K
-    static constexpr int kU = kWt + kSeamMaxW * D;      // [16][D]  A diag(beta) V
-    static constexpr int kMo = kU + kSeamMaxW * D;      // [16][16] output mixing matrix
-    static constexpr int kEb = kMo + kSeamMaxW * kSeamMaxW;  // [16] e^{b_t}
-    static constexpr int kEbw = kEb + kSeamMaxW;        // [16] e^{b_w - b_t}
-    static constexpr int kEbW = kEbw + kSeamMaxW;       // [1]  e^{b_w}
-    static constexpr int kKt = kEbW + 4;                // [D][16] window keys, channel-major (K^T)
-    static constexpr int kFloats = (kKt + D * kSeamMaxW + 63) / 64 * 64;  // 256-byte records
+    static constexpr int kPlaneWD = kSeamMaxW * D * 2;          // bytes of one [16][D] bf16 plane
+    static constexpr int kW = 0;                                // [2][16][D] bf16  Wt = At diag(beta) K
+    static constexpr int kQ = kW + 2 * kPlaneWD;                // [2][16][D] bf16  q (unscaled)
+    static constexpr int kK = kQ + 2 * kPlaneWD;                // [2][D][16] bf16  K^T (channel-major)
+    static constexpr int kM = kK + 2 * kPlaneWD;                // [2][16][16] bf16 output mixing matrix Mo
+    static constexpr int kPlaneM = kSeamMaxW * kSeamMaxW * 2;
+    static constexpr int kU = kM + 2 * kPlaneM;                 // [16][D] f32      U = A diag(beta) V
+    static constexpr int kEb = kU + kSeamMaxW * D * 4;          // [16] f32  e^{b_t}
+    static constexpr int kEbw = kEb + kSeamMaxW * 4;            // [16] f32  e^{b_w - b_t}
+    static constexpr int kEbW = kEbw + kSeamMaxW * 4;           // [1]  f32  e^{b_w}
+    static constexpr int kBytes = (kEbW + 16 + 255) / 256 * 256;  // 256-byte records
 };
 
 }  // namespace hypic

@@ -45,8 +45,18 @@
  *     k, q [n_tokens][H][d_k], v [n_tokens][H][d_v], beta [n_tokens][H],
  *     g [H] (HEAD, always fp32) | [n_tokens][H] (TOKEN) | [n_tokens][H][d_k] (DIAG).
  *     q, k, v, beta and token gates have dtype `in_dtype`.
- *     Pairs: T [n_pair][H][d_k][d_k] fp32 (or [n_pair][H] with HYPIC_T_SCALAR),
- *            S [n_pair][H][d_k][d_v] fp32.
+ *     Pairs: S [n_pair][H][d_k][d_v] fp32; T by hypic_t_layout:
+ *       DENSE  : fp32 [n_pair][H][d_k][d_k];
+ *       SCALAR : fp32 [n_pair][H], T = t I (RetNet-style decay only);
+ *       SPLIT  : bf16 [n_pair][H][2][d_k*d_k], plane 0 = hi = bf16(T) and
+ *                plane 1 = lo = bf16(T - hi), both round-to-nearest-even, so
+ *                T = hi + lo to about 2^-16 relative.  Within a plane, entry
+ *                (r, c) sits at ((r/16)*(d_k/8) + c/8)*128 + (r%16)*8 + c%8:
+ *                16 x 8 blocks, row-major inside a block and across blocks.
+ *                Same 4 bytes per entry as DENSE; it is the MFMA operand
+ *                format of the composition kernels, which load it as is, one
+ *                contiguous KiB per operand fragment (the layout to cache T
+ *                in when it is only ever composed).
  *   - Outputs of concurrent calls must not alias each other.
  */
 #ifndef HYPIC_H
@@ -59,7 +69,7 @@
 extern "C" {
 #endif
 
-#define HYPIC_ABI_VERSION 1
+#define HYPIC_ABI_VERSION 2
 
 typedef enum {
     HYPIC_OK = 0,
@@ -70,7 +80,7 @@ typedef enum {
 
 typedef enum { HYPIC_GATE_HEAD = 0, HYPIC_GATE_TOKEN = 1, HYPIC_GATE_DIAG = 2 } hypic_gate;
 typedef enum { HYPIC_F32 = 0, HYPIC_BF16 = 1 } hypic_dtype;
-typedef enum { HYPIC_T_DENSE = 0, HYPIC_T_SCALAR = 1 } hypic_t_layout;
+typedef enum { HYPIC_T_DENSE = 0, HYPIC_T_SCALAR = 1, HYPIC_T_SPLIT = 2 } hypic_t_layout;
 
 typedef struct {
     int32_t n_heads;  /* H >= 1                                                  */
@@ -93,7 +103,7 @@ typedef struct {
  *   seg_begin, seg_end : int64 [n_seg] token offsets into the packed arrays
  *   n_tokens           : length of the packed token arrays (ranges are clamped)
  *   beta               : ignored (may be NULL) when delta == 0
- *   T_out              : may be NULL to skip T (S only)
+ *   T_out              : in the dims' t_layout; may be NULL to skip T (S only)
  * Implemented (d_k == d_v = d):
  *   gate HEAD or TOKEN, delta 0 : d in {16, 32, 64, 128}, fp32 or bf16 inputs;
  *   gate TOKEN, delta 1         : d = 16 (fp32 or bf16), 64 or 128 (bf16);
@@ -105,7 +115,7 @@ hypic_status hypic_segment_build(const hypic_dims* dims, int32_t n_seg,
                                  const int64_t* seg_begin, const int64_t* seg_end,
                                  int64_t n_tokens, const void* k, const void* v,
                                  const void* g, const void* beta,
-                                 float* T_out, float* S_out, void* stream);
+                                 void* T_out, float* S_out, void* stream);
 
 /*
  * hypic_compose -- reuse of cached pairs ([ZH] 2.1: left-multiply by T_C,
@@ -116,11 +126,12 @@ hypic_status hypic_segment_build(const hypic_dims* dims, int32_t n_seg,
  * linear layer; several layers go in one call as separate chains whose ids
  * index that layer's part of the caches.
  *   pair_id : int32 [n_chain][n_step]
+ *   T_cache : in the dims' t_layout (any of the three)
  *   S_run   : fp32 [n_chain][H][d_k][d_v], read and written in place
  */
 hypic_status hypic_compose(const hypic_dims* dims, int32_t n_chain, int32_t n_step,
                            const int32_t* pair_id, int32_t n_pair,
-                           const float* T_cache, const float* S_cache,
+                           const void* T_cache, const float* S_cache,
                            float* S_run, void* stream);
 
 /*
@@ -141,14 +152,15 @@ hypic_status hypic_compose(const hypic_dims* dims, int32_t n_chain, int32_t n_st
  *   workspace  : device scratch of hypic_seam_workspace_bytes(...) bytes,
  *                owned by the caller, 256-byte aligned; contents are
  *                overwritten; concurrent calls need distinct workspaces.
- * Implemented: gate TOKEN, delta 1, d_k == d_v in {16, 32, 64, 128}, dense T.
+ *   T_cache    : t_layout DENSE or SPLIT
+ * Implemented: gate TOKEN, delta 1, d_k == d_v in {16, 32, 64, 128}.
  */
 hypic_status hypic_seam_advance(const hypic_dims* dims, int32_t n_chain, int32_t n_step,
                                 int32_t w, const int64_t* seam_start, int64_t n_tokens,
                                 const void* q, const void* k, const void* v,
                                 const void* g, const void* beta, float scale,
                                 const int32_t* pair_id, int32_t n_pair,
-                                const float* T_cache, const float* S_cache,
+                                const void* T_cache, const float* S_cache,
                                 float* S_run, float* out,
                                 void* workspace, size_t workspace_bytes, void* stream);
 

@@ -11,6 +11,38 @@ def dev(x, dtype):
     return t.to(device="cuda", dtype=dtype)
 
 
+def _frag_order(T):
+    """[..., d, d] -> [..., d*d] in the SPLIT layout's order: 16 x 8 blocks, row-major."""
+    d = T.shape[-1]
+    x = T.reshape(*T.shape[:-2], d // 16, 16, d // 8, 8)
+    return x.transpose(-3, -2).reshape(*T.shape[:-2], d * d)
+
+
+def _row_major(P, d):
+    """Inverse of _frag_order for a [..., d*d] plane."""
+    x = P.reshape(*P.shape[:-1], d // 16, d // 8, 16, 8)
+    return x.transpose(-3, -2).reshape(*P.shape[:-1], d, d)
+
+
+def t_split(T):
+    """fp32 T [..., d, d] (numpy or tensor) -> device bf16 SPLIT planes [..., 2, d*d]: hi = bf16(T),
+    lo = bf16(T - hi), both round-to-nearest-even (torch's conversion), in fragment order."""
+    T = torch.as_tensor(np.ascontiguousarray(T) if isinstance(T, np.ndarray) else T).to("cuda", torch.float32)
+    hi = T.to(torch.bfloat16)
+    lo = (T - hi.float()).to(torch.bfloat16)
+    return torch.stack([_frag_order(hi), _frag_order(lo)], dim=-2).contiguous()
+
+
+def t_value(T, d=None):
+    """A T cache tensor in a dense layout -> float64 numpy [..., d, d] (SPLIT: hi + lo)."""
+    if T.dtype == torch.bfloat16:
+        d = int(round(T.shape[-1] ** 0.5)) if d is None else d
+        hi = _row_major(T[..., 0, :].double(), d)
+        lo = _row_major(T[..., 1, :].double(), d)
+        return (hi + lo).cpu().numpy()
+    return T.double().cpu().numpy()
+
+
 def in_torch_dtype(W):
     return torch.bfloat16 if W.in_dtype == "bf16" else torch.float32
 

@@ -47,7 +47,8 @@ def _dims(**kw):
 
 
 @pytest.mark.parametrize("bad", [dict(H=0), dict(dk=24), dict(dv=256), dict(gate=3), dict(in_dtype=7),
-                                 dict(t_layout=1), dict(t_layout=1, delta=0, gate=hb.GATE_DIAG)])
+                                 dict(t_layout=1), dict(t_layout=1, delta=0, gate=hb.GATE_DIAG), dict(t_layout=3),
+                                 dict(t_layout=-1)])
 def test_invalid_dims_rejected(lib, bad):
     d = _dims(**bad)
     st = lib.hypic_compose(ctypes.byref(d), 1, 1, None, 0, None, None, None, None)
@@ -77,3 +78,12 @@ def test_unsupported_reported(lib):
     p = ctypes.c_void_p(16)  # never dereferenced: the shape is rejected first
     st = lib.hypic_segment_build(ctypes.byref(d), 1, p, p, 4, p, p, p, p, p, p, None)
     assert st == hb.HYPIC_E_UNSUPPORTED
+
+
+def test_seam_workspace_size(lib):
+    """Window records: 256-byte aligned, scaling with chains x steps x heads; 0 for bad arguments."""
+    one = hb.seam_workspace_bytes(2, 128, 128, 1, 1, 8)
+    assert one > 0 and one % 256 == 0 and one % 2 == 0
+    assert hb.seam_workspace_bytes(2, 128, 128, 3, 5, 8) == 15 * one
+    assert hb.seam_workspace_bytes(2, 128, 128, 1, 1, 17) == 0
+    assert hb.seam_workspace_bytes(2, 128, 64, 1, 1, 8) == 0

@@ -5,7 +5,7 @@ import torch
 
 import oracle
 from hybrid_attention_prefill_amd import binding as hb
-from _util import dev, rel_f
+from _util import dev, rel_f, t_split, t_value
 
 pytestmark = pytest.mark.gpu
 
@@ -18,49 +18,62 @@ def _pairs(seed, n_pair, H, d, t_norm=0.9):
     return T.astype(np.float32), S.astype(np.float32)
 
 
+def _t_cache(T, layout):
+    """The T cache in `layout` and the T values the oracle composes with."""
+    if layout == hb.T_SPLIT:
+        Tc = t_split(T)
+        return Tc, t_value(Tc)
+    return dev(T, torch.float32), T
+
+
+@pytest.mark.parametrize("layout", [hb.T_DENSE, hb.T_SPLIT])
 @pytest.mark.parametrize("d,H,n_chain,n_step", [(16, 1, 1, 2), (16, 3, 2, 9), (64, 8, 1, 16),
                                                 (128, 16, 1, 32), (128, 4, 3, 7), (32, 2, 2, 5)])
-def test_compose_matches_oracle(d, H, n_chain, n_step):
-    print(f"compose d={d} H={H} chains={n_chain} steps={n_step}", flush=True)
+def test_compose_matches_oracle(d, H, n_chain, n_step, layout):
+    print(f"compose d={d} H={H} chains={n_chain} steps={n_step} layout={layout}", flush=True)
     n_pair = 11
     T, S = _pairs(d * 7 + H, n_pair, H, d)
+    Tc, Tv = _t_cache(T, layout)
     rng = np.random.default_rng(5)
     ids = rng.integers(-1, n_pair, size=(n_chain, n_step)).astype(np.int32)
     ids[0, 0] = n_pair + 3          # out of range: skipped
     R0 = rng.standard_normal((n_chain, H, d, d)).astype(np.float32)
-    ref = oracle.compose(T, S, np.where(ids >= n_pair, -1, ids), R0)   # the ABI skips such ids
+    ref = oracle.compose(Tv, S, np.where(ids >= n_pair, -1, ids), R0)   # the ABI skips such ids
     Rg = dev(R0, torch.float32)
-    hb.compose(dev(T, torch.float32), dev(S, torch.float32), dev(ids, torch.int32), Rg)
+    hb.compose(Tc, dev(S, torch.float32), dev(ids, torch.int32), Rg)
     torch.cuda.synchronize()
     err = rel_f(Rg.cpu().numpy(), ref)
     assert err.max() < 1e-4, err.max()
 
 
-def test_compose_many_chains_full_width():
+@pytest.mark.parametrize("layout", [hb.T_DENSE, hb.T_SPLIT])
+def test_compose_many_chains_full_width(layout):
     """Enough (chain, head) units for the full-width column block (the batched path)."""
     d, H, n_chain, n_step, n_pair = 128, 16, 64, 3, 5
-    print("compose many chains", flush=True)
+    print("compose many chains", layout, flush=True)
     T, S = _pairs(3, n_pair, H, d)
+    Tc, Tv = _t_cache(T, layout)
     rng = np.random.default_rng(6)
     ids = rng.integers(0, n_pair, size=(n_chain, n_step)).astype(np.int32)
     R0 = np.zeros((n_chain, H, d, d), dtype=np.float32)
     Rg = dev(R0, torch.float32)
-    hb.compose(dev(T, torch.float32), dev(S, torch.float32), dev(ids, torch.int32), Rg)
+    hb.compose(Tc, dev(S, torch.float32), dev(ids, torch.int32), Rg)
     torch.cuda.synchronize()
     got = Rg.cpu().numpy()
     sample = [0, 17, 63]
-    ref = oracle.compose(T, S, ids[sample], R0[sample])
+    ref = oracle.compose(Tv, S, ids[sample], R0[sample])
     assert rel_f(got[sample], ref).max() < 1e-4
 
 
-def test_compose_identity_T_is_plain_sum():
+@pytest.mark.parametrize("layout", [hb.T_DENSE, hb.T_SPLIT])
+def test_compose_identity_T_is_plain_sum(layout):
     d, H = 64, 2
     rng = np.random.default_rng(8)
     T = np.broadcast_to(np.eye(d, dtype=np.float32), (3, H, d, d)).copy()
     S = rng.standard_normal((3, H, d, d)).astype(np.float32)
     R0 = rng.standard_normal((1, H, d, d)).astype(np.float32)
     Rg = dev(R0, torch.float32)
-    hb.compose(dev(T, torch.float32), dev(S, torch.float32), dev(np.array([[0, 1, 2]], np.int32), torch.int32), Rg)
+    hb.compose(_t_cache(T, layout)[0], dev(S, torch.float32), dev(np.array([[0, 1, 2]], np.int32), torch.int32), Rg)
     torch.cuda.synchronize()
     ref = R0[0].astype(np.float64) + S.astype(np.float64).sum(axis=0)
     assert rel_f(Rg.cpu().numpy()[0], ref).max() < 1e-5

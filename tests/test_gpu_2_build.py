@@ -11,7 +11,7 @@ import torch
 import oracle
 from hybrid_attention_prefill_amd import binding as hb
 from hybrid_attention_prefill_amd import workloads as wl
-from _util import assert_pairs_close, dev, rel_f, workload_tensors
+from _util import assert_pairs_close, dev, rel_f, t_split, t_value, workload_tensors
 
 pytestmark = pytest.mark.gpu
 TOL = {"f32": 1e-4, "bf16": 5e-3}
@@ -170,3 +170,34 @@ def test_cfg5_segment_shape_all_heads_sampled():
         T0, S0 = oracle.segment_build(W.k[b:e, h:h + 1], W.v[b:e, h:h + 1], W.g[b:e, h:h + 1],
                                       W.beta[b:e, h:h + 1], [0], [e - b], gate=W.gate, delta=True)
         assert_pairs_close(T[s:s + 1, h:h + 1], S[s:s + 1, h:h + 1], T0, S0, TOL["bf16"], f"seg {s} head {h}")
+
+
+@pytest.mark.parametrize("cfg,kw", [
+    (1, dict(stress=True)),
+    (2, dict(n_seg=3, seg_len=200)),
+    (3, dict(n_heads=2, lengths=[300, 65, 1])),
+    (5, dict(n_heads=2, lengths=[100, 33], n_req=1, n_step=1, n_layers=1)),
+])
+def test_split_T_layout(cfg, kw):
+    """T emitted as bf16 hi/lo planes (the layout the composition kernels read): the
+    planes are exactly the round-to-nearest-even split of the fp32 T the same kernel
+    writes in the dense layout, S is bit-identical, and hi + lo matches the oracle."""
+    W = wl.make(cfg, **kw)
+    print(W.name, "split T", flush=True)
+    x = workload_tensors(W)
+    sb, se = dev(W.cache_begin, torch.int64), dev(W.cache_end, torch.int64)
+    T32, S32 = hb.segment_build(x["k"], x["v"], x["g"], x["beta"], sb, se, gate=W.gate, delta=W.delta)
+    Tsp, Ssp = hb.segment_build(x["k"], x["v"], x["g"], x["beta"], sb, se, gate=W.gate, delta=W.delta,
+                                t_layout=hb.T_SPLIT)
+    torch.cuda.synchronize()
+    assert Tsp.dtype == torch.bfloat16 and tuple(Tsp.shape) == (W.n_seg, W.n_heads, 2, W.d_k * W.d_k)
+    assert torch.equal(Ssp, S32)
+    ref = t_split(T32)
+    normal = (t_split(T32.abs() >= 1e-30).float() > 0)            # fp32 normal range: exact split
+    normal[..., 1, :] = normal[..., 0, :]
+    assert torch.equal(Tsp[normal], ref[normal])
+    t64 = T32.double().cpu().numpy()
+    assert np.all(np.abs(t_value(Tsp) - t64) <= 2.0 ** -16 * np.abs(t64) + 1e-37)   # hi + lo carries 16 bits
+    T0, S0 = _oracle_build(W)
+    tol = TOL["f32"] if W.in_dtype == "f32" else TOL["bf16"]
+    assert_pairs_close(t_value(Tsp), Ssp.cpu().numpy(), T0, S0, tol, W.name)

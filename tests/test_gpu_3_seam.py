@@ -50,10 +50,10 @@ def _reference(W):
     return S, outs
 
 
-def _gpu(W, with_pairs=True):
+def _gpu(W, with_pairs=True, t_layout=hb.T_SPLIT):
     x = workload_tensors(W)
     T, S = hb.segment_build(x["k"], x["v"], x["g"], x["beta"], dev(W.cache_begin, torch.int64),
-                            dev(W.cache_end, torch.int64), gate=W.gate, delta=W.delta)
+                            dev(W.cache_end, torch.int64), gate=W.gate, delta=W.delta, t_layout=t_layout)
     n_step = W.n_seg
     R = torch.zeros((1, W.n_heads, W.d_k, W.d_v), device="cuda")
     out = torch.full((1, n_step, W.w, W.n_heads, W.d_v), float("nan"), device="cuda")
@@ -76,11 +76,11 @@ def _check(W, R, out, S_ref, outs_ref, tol):
     return worst
 
 
-@pytest.mark.parametrize("w", [8, 3, 16])
-def test_seam_gdn_bf16_ragged(w):
+@pytest.mark.parametrize("w,t_layout", [(8, hb.T_SPLIT), (3, hb.T_SPLIT), (16, hb.T_SPLIT), (8, hb.T_DENSE)])
+def test_seam_gdn_bf16_ragged(w, t_layout):
     W = _seam_workload(3, [150, 97, 64 + w, 300, 40], w, H=2)
-    print(W.name, "seam w", w, flush=True)
-    R, out = _gpu(W)
+    print(W.name, "seam w", w, "T layout", t_layout, flush=True)
+    R, out = _gpu(W, t_layout=t_layout)
     S_ref, outs_ref = _reference(W)
     _check(W, R, out, S_ref, outs_ref, TOL["bf16"])
 
@@ -92,10 +92,11 @@ def test_seam_gdn_bf16_stress():
     _check(W, R, out, S_ref, outs_ref, TOL["bf16"])
 
 
-@pytest.mark.parametrize("stress", [False, True])
-def test_seam_gdn_fp32_d16(stress):
+@pytest.mark.parametrize("stress,t_layout", [(False, hb.T_SPLIT), (True, hb.T_SPLIT), (True, hb.T_DENSE)])
+def test_seam_gdn_fp32_d16(stress, t_layout):
     W = _seam_workload(1, [64, 40, 77], 8, H=1, stress=stress)
-    R, out = _gpu(W)
+    print(W.name, "fp32 seam", stress, t_layout, flush=True)
+    R, out = _gpu(W, t_layout=t_layout)
     S_ref, outs_ref = _reference(W)
     _check(W, R, out, S_ref, outs_ref, TOL["f32"])
 
