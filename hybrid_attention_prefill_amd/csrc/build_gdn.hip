@@ -24,6 +24,14 @@
 // 16x16: diagonal blocks by forward substitution (fp32), the rest with
 // v_mfma_f32_16x16x4_f32.  Operands are fp16 (one rounding, NSPLIT = 1) for
 // bf16 inputs, or fp16 hi + lo with three products (NSPLIT = 2) for fp32 inputs.
+//
+// Data movement: the next chunk's k, v, gates and betas are loaded into
+// registers while the current chunk is processed (raw bits, unconditional
+// loads of clamped token rows); staging converts them and writes K token-major
+// and K^T, V^T channel-major through 4 x 8 register transposes.  Every LDS
+// operand matrix is kept in fragment order (frag_off), so each MFMA operand
+// fragment is one contiguous, conflict-free 1 KiB read; a wave reads each A
+// fragment once for all of its column tiles.
 #include "hypic_device.h"
 #include "hypic_kernels.h"
 #include "build_common.h"
@@ -34,25 +42,37 @@ namespace {
 using namespace bld;
 
 constexpr int CH = 64;       // chunk length
-constexpr int LDT = CH + 8;  // padded LDS row for token-indexed rows (16-bit units)
 constexpr int LDF = CH + 1;  // padded LDS row for fp32 64x64 matrices
 
 template <int D, int NSPLIT>
 struct alignas(16) GdnSmem {
     static constexpr int KP = D < 32 ? 32 : D;  // channel contraction padded to 32
-    static constexpr int LDK = KP + 8;
-    uint16_t Kr[NSPLIT][CH][LDK];  // K, token-major (channels >= D are zero)
-    uint16_t Kt[NSPLIT][D][LDT];   // K^T, channel-major
-    uint16_t Vt[NSPLIT][D][LDT];   // V^T, channel-major
-    uint16_t Ap[NSPLIT][CH][LDT];  // At diag(beta)
-    uint16_t Ad[NSPLIT][CH][LDT];  // A diag(beta)
-    uint16_t Wt[NSPLIT][CH][LDK];  // Wt, token-major (channels >= D are zero)
+    uint16_t Kr[NSPLIT][CH * KP];  // K, rows = tokens, cols = channels (>= D zero)
+    uint16_t Kt[NSPLIT][D * CH];   // K^T, rows = channels, cols = tokens
+    uint16_t Vt[NSPLIT][D * CH];   // V^T, rows = channels, cols = tokens
+    uint16_t Ap[NSPLIT][CH * CH];  // At diag(beta)
+    uint16_t Ad[NSPLIT][CH * CH];  // A diag(beta)
+    uint16_t Wt[NSPLIT][CH * KP];  // Wt, rows = tokens, cols = channels (>= D zero)
     float F1[CH][LDF];             // Lt (strictly lower)
     float F2[CH][LDF];             // At
     float F3[32][33];              // inverse scratch
     float gate[CH], beta[CH], b[CH], eb[CH], ebr[CH];
     float bC;
 };
+
+// A-operand fragment (row tile rt, k-block ks) of a fragment-ordered [rows][ncols] plane:
+// lane l gets row rt*16 + l%16, columns ks*32 + 8(l/16) .. +7.
+template <int NCOLS>
+__device__ __forceinline__ f16x8 lds_frag(const uint16_t* P, int rt, int ks, int lane) {
+    return *reinterpret_cast<const f16x8*>(P + (rt * (NCOLS / 8) + ks * 4) * 128 + lane * 8);
+}
+template <int NSPLIT, int NCOLS, typename Arr>
+__device__ __forceinline__ Frag<NSPLIT> frag_of(const Arr& a, int rt, int ks, int lane) {
+    Frag<NSPLIT> f;
+    f.h = lds_frag<NCOLS>(a[0], rt, ks, lane);
+    if constexpr (NSPLIT == 2) f.l = lds_frag<NCOLS>(a[1], rt, ks, lane);
+    return f;
+}
 
 // Inverse of I + Lt (64x64 unit lower triangular, Lt in F1) into F2.
 template <typename SM>
@@ -109,6 +129,24 @@ __device__ void tri_inverse(SM& sm, int wave, int lane) {
     __syncthreads();
 }
 
+// 16-bit operand bits of x (NSPLIT 1: fp16; NSPLIT 2: fp16 hi and lo)
+template <int NSPLIT>
+__device__ __forceinline__ void to16(float x, uint16_t& hi, uint16_t& lo) {
+    if constexpr (NSPLIT == 1) {
+        hi = f16_bits((_Float16)x);
+        lo = 0;
+    } else {
+        _Float16 a, b;
+        split_f16(x, a, b);
+        hi = f16_bits(a);
+        lo = f16_bits(b);
+    }
+}
+
+__device__ __forceinline__ u32x4 pack8(const uint16_t* x) {
+    return u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
+}
+
 }  // namespace
 
 template <int D, int NSPLIT, bool BF16>
@@ -124,12 +162,21 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
     constexpr int RT = D / 16;              // row tiles of X
     constexpr int NCT = 2 * RT;             // column tiles of X = [H | S]
     constexpr int CTW = (NCT + 7) / 8;      // column tiles per wave
+    constexpr int CB = D / 8;               // 8-channel blocks per token
+    constexpr int NBLK = (CH / 4) * CB;     // 4-token x 8-channel blocks per matrix
+    constexpr int WPR = BF16 ? 1 : 2;       // 16-byte words per 8 channels of one token
+    static_assert(2 * NBLK <= 512, "one block per thread");
     __shared__ SM sm;
 
     const int unit = blockIdx.x;
     const int seg = unit / H, h = unit % H;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g4 = lane >> 4, n16 = lane & 15;
+    // column tile ct = wave + 8 c of X is an S tile (ct >= RT); known at compile time when
+    // the H and S tiles split evenly over the 8 waves
+    auto s_tile = [&](int c) -> bool { return RT % 8 == 0 ? c * 8 >= RT : wave + 8 * c >= RT; };
+    auto own_tile = [&](int c) -> bool { return NCT % 8 == 0 || wave + 8 * c < NCT; };
 
     int64_t beg = seg_begin[seg], end = seg_end[seg];
     beg = beg < 0 ? 0 : (beg > n_tokens ? n_tokens : beg);
@@ -137,9 +184,9 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
 
     // zero the channel padding of Kr / Wt once (D < 32 only)
     if (KP > D) {
-        for (int i = tid; i < NSPLIT * CH * SM::LDK; i += 512) {
-            (&sm.Kr[0][0][0])[i] = 0;
-            (&sm.Wt[0][0][0])[i] = 0;
+        for (int i = tid; i < NSPLIT * CH * KP; i += 512) {
+            (&sm.Kr[0][0])[i] = 0;
+            (&sm.Wt[0][0])[i] = 0;
         }
     }
 
@@ -160,48 +207,90 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
     }
     float log_s = 0.f;  // log of the scalar decay factored out of T
 
+    // ---- next-chunk prefetch: thread -> (matrix K or V, 4-token block tb, 8-channel block cb)
+    const bool has_blk = tid < 2 * NBLK;
+    const int blk = has_blk ? tid : 0;
+    const bool blk_v = blk >= NBLK;
+    const int tb = (blk % NBLK) / CB, cb = (blk % NBLK) % CB;
+    const void* blk_src = blk_v ? v : k;
     const size_t tok_stride = (size_t)H * D;
+    u32x4 raw[4][WPR];            // 4 token rows x 8 channels, raw input bits
+    uint32_t graw = 0, braw = 0;  // gate and beta of token `lane` (wave 0), raw bits
+    auto prefetch = [&](int64_t c0) {
+        // rows past the segment are clamped into it (masked when staged); the loads are
+        // unconditional so that nothing waits for them before the next chunk's staging
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            int64_t t = c0 + tb * 4 + r;
+            t = t < end ? t : end - 1;
+            const size_t e = (size_t)t * tok_stride + (size_t)h * D + cb * 8;
+            if constexpr (BF16) {
+                raw[r][0] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(blk_src) + e);
+            } else {
+                const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(blk_src) + e);
+                raw[r][0] = p[0];
+                raw[r][WPR - 1] = p[1];
+            }
+        }
+        int64_t t = c0 + lane;
+        t = t < end ? t : end - 1;
+        const size_t e = (size_t)t * H + h;
+        if constexpr (BF16) {
+            graw = reinterpret_cast<const uint16_t*>(gl)[e];
+            braw = reinterpret_cast<const uint16_t*>(beta)[e];
+        } else {
+            graw = reinterpret_cast<const uint32_t*>(gl)[e];
+            braw = reinterpret_cast<const uint32_t*>(beta)[e];
+        }
+    };
+    auto raw_val = [&](int r, int c) -> float {   // channel c (0..7) of row r
+        if constexpr (BF16) {
+            const uint32_t w = raw[r][0][c >> 1];
+            return __uint_as_float((c & 1) ? (w & 0xFFFF0000u) : (w << 16));
+        } else {
+            return __uint_as_float(raw[r][c >> 2][c & 3]);
+        }
+    };
+    auto raw1 = [&](uint32_t x) -> float { return BF16 ? __uint_as_float(x << 16) : __uint_as_float(x); };
+
+    if (beg < end) prefetch(beg);
+
     for (int64_t c0 = beg; c0 < end; c0 += CH) {
         const int n = (int)((end - c0) < CH ? (end - c0) : CH);
-        // ---- 1. stage the chunk: K, V (16-bit planes, both orientations), gates
-        for (int it = tid; it < CH * (D / 8); it += 512) {
-            const int t = it / (D / 8), cg = it % (D / 8);
-            float kx[8], vx[8];
-            if (t < n) {
-                const size_t e = (size_t)(c0 + t) * tok_stride + (size_t)h * D + cg * 8;
-                load8<BF16>(k, e, kx);
-                load8<BF16>(v, e, vx);
-            } else {
+        // ---- 1. stage the chunk: K token-major, K^T and V^T channel-major (16-bit), gates
+        if (has_blk) {
+            uint16_t hb[4][8], lb[4][8];   // [token][channel]
 #pragma unroll
-                for (int e = 0; e < 8; ++e) { kx[e] = 0.f; vx[e] = 0.f; }
+            for (int r = 0; r < 4; ++r) {
+                const bool live = tb * 4 + r < n;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) to16<NSPLIT>(live ? raw_val(r, c) : 0.f, hb[r][c], lb[r][c]);
             }
-            uint16_t kh[8], kl[8], vh[8], vl[8];
+            if (!blk_v) {   // K rows (8 channels of one token = 16 contiguous bytes)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                put16<NSPLIT>(&kh[e], &kl[e], kx[e]);
-                put16<NSPLIT>(&vh[e], &vl[e], vx[e]);
-            }
-            *reinterpret_cast<u32x4*>(&sm.Kr[0][t][cg * 8]) =
-                u32x4{pack2(kh[0], kh[1]), pack2(kh[2], kh[3]), pack2(kh[4], kh[5]), pack2(kh[6], kh[7])};
-            if constexpr (NSPLIT == 2)
-                *reinterpret_cast<u32x4*>(&sm.Kr[1][t][cg * 8]) =
-                    u32x4{pack2(kl[0], kl[1]), pack2(kl[2], kl[3]), pack2(kl[4], kl[5]), pack2(kl[6], kl[7])};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                sm.Kt[0][cg * 8 + e][t] = kh[e];
-                sm.Vt[0][cg * 8 + e][t] = vh[e];
-                if constexpr (NSPLIT == 2) {
-                    sm.Kt[1][cg * 8 + e][t] = kl[e];
-                    sm.Vt[1][cg * 8 + e][t] = vl[e];
+                for (int r = 0; r < 4; ++r) {
+                    const int off = frag_off(tb * 4 + r, cb * 8, KP);
+                    *reinterpret_cast<u32x4*>(&sm.Kr[0][off]) = pack8(hb[r]);
+                    if constexpr (NSPLIT == 2) *reinterpret_cast<u32x4*>(&sm.Kr[1][off]) = pack8(lb[r]);
                 }
             }
+            // transposed: one channel row, 4 consecutive tokens = 8 contiguous bytes
+            uint16_t(*dst)[D * CH] = blk_v ? sm.Vt : sm.Kt;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const int off = frag_off(cb * 8 + c, tb * 4, CH);
+                *reinterpret_cast<u32x2*>(&dst[0][off]) = u32x2{pack2(hb[0][c], hb[1][c]), pack2(hb[2][c], hb[3][c])};
+                if constexpr (NSPLIT == 2)
+                    *reinterpret_cast<u32x2*>(&dst[1][off]) = u32x2{pack2(lb[0][c], lb[1][c]), pack2(lb[2][c], lb[3][c])};
+            }
         }
-        if (tid < CH) {
-            const bool ok = tid < n;
-            const size_t e = (size_t)(c0 + tid) * H + h;
-            sm.gate[tid] = ok ? load1<BF16>(gl, e) : 0.f;
-            sm.beta[tid] = ok ? load1<BF16>(beta, e) : 0.f;
+        if (wave == 0) {
+            const bool ok = lane < n;
+            sm.gate[lane] = ok ? raw1(graw) : 0.f;
+            sm.beta[lane] = ok ? raw1(braw) : 0.f;
         }
+        // the next chunk's loads fly during this chunk
+        if (c0 + CH < end) prefetch(c0 + CH);
         __syncthreads();
 
         // ---- 2. gate cumsum (wave 0, one token per lane) and Lt = tril(b K K^T, -1)
@@ -225,8 +314,8 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
             f32x4 gacc = zero4();
 #pragma unroll
             for (int ks = 0; ks < KSD; ++ks) {
-                const Frag<NSPLIT> a = frag_at<NSPLIT>(sm.Kr, ti * 16 + n16, ks * 32 + 8 * g4);
-                const Frag<NSPLIT> bb = frag_at<NSPLIT>(sm.Kr, tj * 16 + n16, ks * 32 + 8 * g4);
+                const Frag<NSPLIT> a = frag_of<NSPLIT, KP>(sm.Kr, ti, ks, lane);
+                const Frag<NSPLIT> bb = frag_of<NSPLIT, KP>(sm.Kr, tj, ks, lane);   // K^T as B = rows of K
                 gacc = mma<NSPLIT>(a, bb, gacc);
             }
 #pragma unroll
@@ -240,17 +329,30 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
         // ---- 3. At = (I + Lt)^-1
         tri_inverse(sm, wave, lane);
 
-        // ---- 4. Ap = At diag(beta), Ad = A diag(beta) with A[t][s] = e^{b_t - b_s} At[t][s]
-        for (int it = tid; it < CH * CH; it += 512) {
-            const int t = it / CH, s = it % CH;
-            float ap = 0.f, ad = 0.f;
-            if (s <= t) {
-                const float a = sm.F2[t][s] * sm.beta[s];
-                ap = a;
-                ad = a * expf(sm.b[t] - sm.b[s]);
+        // ---- 4. Ap = At diag(beta), Ad = A diag(beta) with A[t][s] = e^{b_t - b_s} At[t][s];
+        // one token row t and 8 consecutive s per thread (16-byte stores)
+        {
+            const int t = tid >> 3, s0 = (tid & 7) * 8;
+            uint16_t ph[8], pl[8], dh[8], dl[8];
+            const float bt = sm.b[t];
+#pragma unroll
+            for (int x = 0; x < 8; ++x) {
+                const int s = s0 + x;
+                float ap = 0.f, ad = 0.f;
+                if (s <= t) {
+                    ap = sm.F2[t][s] * sm.beta[s];
+                    ad = ap * expf(bt - sm.b[s]);
+                }
+                to16<NSPLIT>(ap, ph[x], pl[x]);
+                to16<NSPLIT>(ad, dh[x], dl[x]);
             }
-            put16<NSPLIT>(&sm.Ap[0][t][s], &sm.Ap[NSPLIT - 1][t][s], ap);
-            put16<NSPLIT>(&sm.Ad[0][t][s], &sm.Ad[NSPLIT - 1][t][s], ad);
+            const int off = frag_off(t, s0, CH);
+            *reinterpret_cast<u32x4*>(&sm.Ap[0][off]) = pack8(ph);
+            *reinterpret_cast<u32x4*>(&sm.Ad[0][off]) = pack8(dh);
+            if constexpr (NSPLIT == 2) {
+                *reinterpret_cast<u32x4*>(&sm.Ap[1][off]) = pack8(pl);
+                *reinterpret_cast<u32x4*>(&sm.Ad[1][off]) = pack8(dl);
+            }
         }
         __syncthreads();
 
@@ -260,19 +362,18 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
             f32x4 acc = zero4();
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const Frag<NSPLIT> a = frag_at<NSPLIT>(sm.Kt, mt * 16 + n16, ks * 32 + 8 * g4);
-                const Frag<NSPLIT> bb = frag_at<NSPLIT>(sm.Ap, nt * 16 + n16, ks * 32 + 8 * g4);
+                const Frag<NSPLIT> a = frag_of<NSPLIT, CH>(sm.Kt, mt, ks, lane);
+                const Frag<NSPLIT> bb = frag_of<NSPLIT, CH>(sm.Ap, nt, ks, lane);   // Ap^T as B = rows of Ap
                 acc = mma<NSPLIT>(a, bb, acc);
             }
             // lane holds Wt[token nt*16+n16][channels mt*16+4*g4 .. +3]
             uint16_t hh[4], ll[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) put16<NSPLIT>(&hh[e], &ll[e], acc[e]);
-            *reinterpret_cast<u32x2*>(&sm.Wt[0][nt * 16 + n16][mt * 16 + 4 * g4]) =
-                u32x2{pack2(hh[0], hh[1]), pack2(hh[2], hh[3])};
+            for (int e = 0; e < 4; ++e) to16<NSPLIT>(acc[e], hh[e], ll[e]);
+            const int off = frag_off(nt * 16 + n16, mt * 16 + 4 * g4, KP);
+            *reinterpret_cast<u32x2*>(&sm.Wt[0][off]) = u32x2{pack2(hh[0], hh[1]), pack2(hh[2], hh[3])};
             if constexpr (NSPLIT == 2)
-                *reinterpret_cast<u32x2*>(&sm.Wt[1][nt * 16 + n16][mt * 16 + 4 * g4]) =
-                    u32x2{pack2(ll[0], ll[1]), pack2(ll[2], ll[3])};
+                *reinterpret_cast<u32x2*>(&sm.Wt[1][off]) = u32x2{pack2(ll[0], ll[1]), pack2(ll[2], ll[3])};
         }
         f32x4 U[4][CTW];
 #pragma unroll
@@ -281,12 +382,12 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
                 U[tt][c] = zero4();
-                if (ct >= RT && ct < NCT) {
+                if (s_tile(c) && ct < NCT) {
                     const int vt = ct - RT;  // value-channel tile
 #pragma unroll
                     for (int ks = 0; ks < 2; ++ks) {
-                        const Frag<NSPLIT> a = frag_at<NSPLIT>(sm.Ad, tt * 16 + n16, ks * 32 + 8 * g4);
-                        const Frag<NSPLIT> bb = frag_at<NSPLIT>(sm.Vt, vt * 16 + n16, ks * 32 + 8 * g4);
+                        const Frag<NSPLIT> a = frag_of<NSPLIT, CH>(sm.Ad, tt, ks, lane);
+                        const Frag<NSPLIT> bb = frag_of<NSPLIT, CH>(sm.Vt, vt, ks, lane);   // V as B = rows of V^T
                         U[tt][c] = mma<NSPLIT>(a, bb, U[tt][c]);
                     }
                 }
@@ -294,50 +395,60 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
         }
         __syncthreads();
 
-        // ---- 6..8. per owned column tile: Y = Wt X, R, X += K^T R
+        // ---- 6..8. Y = Wt X, R, X += K^T R for all owned column tiles at once (each A
+        // fragment is read once per wave)
         const float bC = sm.bC;
         const float ebC = expf(bC);
+        if (wave < NCT) {
+            f32x4 R[4][CTW];
 #pragma unroll
-        for (int c = 0; c < CTW; ++c) {
-            const int ct = wave + 8 * c;
-            if (ct >= NCT) continue;
-            const bool is_s = ct >= RT;
-            // X column tile as B fragments (k = X rows)
-            Frag<NSPLIT> xb[KSD];
+            for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                for (int c = 0; c < CTW; ++c) R[tt][c] = zero4();
 #pragma unroll
             for (int kb = 0; kb < KSD; ++kb) {
-                const f32x4 d0 = X[2 * kb][c];
-                const f32x4 d1 = (2 * kb + 1 < RT) ? X[2 * kb + 1 < RT ? 2 * kb + 1 : 0][c] : zero4();
-                xb[kb] = dpair_to_frag<NSPLIT>(d0, d1);
-            }
-            f32x4 R[4];
+                Frag<NSPLIT> xb[CTW];   // rows 32 kb .. 32 kb + 31 of the X column tiles as B fragments
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                f32x4 y = zero4();
-#pragma unroll
-                for (int kb = 0; kb < KSD; ++kb) {
-                    const Frag<NSPLIT> a = frag_at<NSPLIT>(sm.Wt, tt * 16 + n16, kb * 32 + 8 * g4);
-                    y = mma<NSPLIT>(a, xb[kb], y);
+                for (int c = 0; c < CTW; ++c) {
+                    const f32x4 d0 = X[2 * kb][c];
+                    const f32x4 d1 = (2 * kb + 1 < RT) ? X[2 * kb + 1 < RT ? 2 * kb + 1 : 0][c] : zero4();
+                    xb[c] = dpair_to_frag<NSPLIT>(d0, d1);
                 }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = tt * 16 + 4 * g4 + e;
-                    R[tt][e] = is_s ? sm.ebr[t] * (U[tt][c][e] - sm.eb[t] * y[e]) : -y[e];
+                for (int tt = 0; tt < 4; ++tt) {
+                    const Frag<NSPLIT> a = frag_of<NSPLIT, KP>(sm.Wt, tt, kb, lane);
+#pragma unroll
+                    for (int c = 0; c < CTW; ++c)
+                        if (own_tile(c)) R[tt][c] = mma<NSPLIT>(a, xb[c], R[tt][c]);
                 }
             }
-            Frag<NSPLIT> rb[2];
-            rb[0] = dpair_to_frag<NSPLIT>(R[0], R[1]);
-            rb[1] = dpair_to_frag<NSPLIT>(R[2], R[3]);
+            Frag<NSPLIT> rb[2][CTW];
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                f32x4 acc = is_s ? X[rt][c] * ebC : X[rt][c];
+            for (int c = 0; c < CTW; ++c) {
+                const bool is_s = s_tile(c);
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = tt * 16 + 4 * g4 + e;
+                        R[tt][c][e] = is_s ? sm.ebr[t] * (U[tt][c][e] - sm.eb[t] * R[tt][c][e]) : -R[tt][c][e];
+                    }
+                rb[0][c] = dpair_to_frag<NSPLIT>(R[0][c], R[1][c]);
+                rb[1][c] = dpair_to_frag<NSPLIT>(R[2][c], R[3][c]);
+                if (is_s) {
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) X[rt][c] *= ebC;
+                }
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    const Frag<NSPLIT> a = frag_at<NSPLIT>(sm.Kt, rt * 16 + n16, kb * 32 + 8 * g4);
-                    acc = mma<NSPLIT>(a, rb[kb], acc);
+                    const Frag<NSPLIT> a = frag_of<NSPLIT, CH>(sm.Kt, rt, kb, lane);
+#pragma unroll
+                    for (int c = 0; c < CTW; ++c)
+                        if (own_tile(c)) X[rt][c] = mma<NSPLIT>(a, rb[kb][c], X[rt][c]);
                 }
-                X[rt][c] = acc;
-            }
         }
         log_s += bC;
         __syncthreads();
