@@ -42,6 +42,7 @@ namespace {
 using namespace bld;
 
 constexpr int CH = 64;       // chunk length
+constexpr float kLog2e = 1.4426950408889634f;
 constexpr int LDF = CH + 1;  // padded LDS row for fp32 64x64 matrices
 
 template <int D, int NSPLIT>
@@ -56,21 +57,37 @@ struct alignas(16) GdnSmem {
     float F1[CH][LDF];             // Lt (strictly lower)
     float F2[CH][LDF];             // At
     float F3[32][33];              // inverse scratch
-    float gate[CH], beta[CH], b[CH], eb[CH], ebr[CH];
+    float gate[CH], beta[CH], b[CH], eb[CH], ebr[CH];   // b in log2 units
     float bC;
 };
 
-// A-operand fragment (row tile rt, k-block ks) of a fragment-ordered [rows][ncols] plane:
-// lane l gets row rt*16 + l%16, columns ks*32 + 8(l/16) .. +7.
+// LDS operand planes are fragment-ordered (frag_off) with the 16-byte chunks XOR-swizzled:
+// chunk c is stored at c ^ ((c >> 4 ^ c >> 7) & 7).  The swizzle permutes chunks within
+// aligned groups of 8, so a fragment read stays one 1 KiB block read conflict-free, while
+// the staging stores (token rows, channel rows, 8 lanes on 8 different rows) spread over
+// the banks instead of landing on one.
+__device__ __forceinline__ int swz(int off) {
+    const int c = off >> 3;
+    return ((c ^ (((c >> 4) ^ (c >> 7)) & 7)) << 3) | (off & 7);
+}
+__device__ __forceinline__ int lds_off(int row, int col, int ncols) { return swz(frag_off(row, col, ncols)); }
+
+// A-operand fragment (row tile rt, k-block ks) of a [rows][ncols] plane: lane l gets
+// row rt*16 + l%16, columns ks*32 + 8(l/16) .. +7.  Fragment F = rt*(ncols/32) + ks is
+// chunks 64F .. 64F+63; for those the swizzle reduces to l -> l ^ (l >> 4) ^ K_F with
+// K_F = 4(F & 1) ^ ((F >> 1) & 7), so with lx = l ^ (l >> 4) per thread every read is a
+// lane offset from 8 fixed values plus an immediate.
 template <int NCOLS>
-__device__ __forceinline__ f16x8 lds_frag(const uint16_t* P, int rt, int ks, int lane) {
-    return *reinterpret_cast<const f16x8*>(P + (rt * (NCOLS / 8) + ks * 4) * 128 + lane * 8);
+__device__ __forceinline__ f16x8 lds_frag(const uint16_t* P, int rt, int ks, int lx) {
+    const int F = rt * (NCOLS / 32) + ks;
+    const int K = ((F & 1) << 2) ^ ((F >> 1) & 7);
+    return *reinterpret_cast<const f16x8*>(P + F * 512 + 8 * (lx ^ K));
 }
 template <int NSPLIT, int NCOLS, typename Arr>
-__device__ __forceinline__ Frag<NSPLIT> frag_of(const Arr& a, int rt, int ks, int lane) {
+__device__ __forceinline__ Frag<NSPLIT> frag_of(const Arr& a, int rt, int ks, int lx) {
     Frag<NSPLIT> f;
-    f.h = lds_frag<NCOLS>(a[0], rt, ks, lane);
-    if constexpr (NSPLIT == 2) f.l = lds_frag<NCOLS>(a[1], rt, ks, lane);
+    f.h = lds_frag<NCOLS>(a[0], rt, ks, lx);
+    if constexpr (NSPLIT == 2) f.l = lds_frag<NCOLS>(a[1], rt, ks, lx);
     return f;
 }
 
@@ -143,6 +160,13 @@ __device__ __forceinline__ void to16(float x, uint16_t& hi, uint16_t& lo) {
     }
 }
 
+// An empty asm that "modifies" x: values derived from it inside a loop body are
+// recomputed each iteration instead of being hoisted (and then spilled) by the compiler.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 __device__ __forceinline__ u32x4 pack8(const uint16_t* x) {
     return u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
 }
@@ -211,7 +235,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
     const bool has_blk = tid < 2 * NBLK;
     const int blk = has_blk ? tid : 0;
     const bool blk_v = blk >= NBLK;
-    const int tb = (blk % NBLK) / CB, cb = (blk % NBLK) % CB;
+    const int tb0 = (blk % NBLK) / CB, cb0 = (blk % NBLK) % CB;
     const void* blk_src = blk_v ? v : k;
     const size_t tok_stride = (size_t)H * D;
     u32x4 raw[4][WPR];            // 4 token rows x 8 channels, raw input bits
@@ -219,6 +243,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
     auto prefetch = [&](int64_t c0) {
         // rows past the segment are clamped into it (masked when staged); the loads are
         // unconditional so that nothing waits for them before the next chunk's staging
+        const int tb = opaque(tb0), cb = opaque(cb0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             int64_t t = c0 + tb * 4 + r;
@@ -257,31 +282,58 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
 
     for (int64_t c0 = beg; c0 < end; c0 += CH) {
         const int n = (int)((end - c0) < CH ? (end - c0) : CH);
+        // lane-derived indices, recomputed per chunk (cheap) rather than kept live across it
+        const int lane_c = opaque(lane);
+        const int g4 = lane_c >> 4, n16 = lane_c & 15, lx = lane_c ^ g4;
+        const int tb = opaque(tb0), cb = opaque(cb0);
         // ---- 1. stage the chunk: K token-major, K^T and V^T channel-major (16-bit), gates
         if (has_blk) {
-            uint16_t hb[4][8], lb[4][8];   // [token][channel]
+            // masked values of the 4 x 8 block; rows past the segment are zero
+            float f[4][8];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const bool live = tb * 4 + r < n;
 #pragma unroll
-                for (int c = 0; c < 8; ++c) to16<NSPLIT>(live ? raw_val(r, c) : 0.f, hb[r][c], lb[r][c]);
+                for (int c = 0; c < 8; ++c) f[r][c] = live ? raw_val(r, c) : 0.f;
             }
-            if (!blk_v) {   // K rows (8 channels of one token = 16 contiguous bytes)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int off = frag_off(tb * 4 + r, cb * 8, KP);
-                    *reinterpret_cast<u32x4*>(&sm.Kr[0][off]) = pack8(hb[r]);
-                    if constexpr (NSPLIT == 2) *reinterpret_cast<u32x4*>(&sm.Kr[1][off]) = pack8(lb[r]);
-                }
-            }
-            // transposed: one channel row, 4 consecutive tokens = 8 contiguous bytes
             uint16_t(*dst)[D * CH] = blk_v ? sm.Vt : sm.Kt;
+            if constexpr (NSPLIT == 1 && BF16) {
+                // bf16 values are exact in fp16 (inside its range): round-toward-zero packing is exact
+                auto pk = [](float a, float b) -> unsigned {
+                    return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a, b));
+                };
+                if (!blk_v) {   // K rows (8 channels of one token = 16 contiguous bytes)
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const int off = frag_off(cb * 8 + c, tb * 4, CH);
-                *reinterpret_cast<u32x2*>(&dst[0][off]) = u32x2{pack2(hb[0][c], hb[1][c]), pack2(hb[2][c], hb[3][c])};
-                if constexpr (NSPLIT == 2)
-                    *reinterpret_cast<u32x2*>(&dst[1][off]) = u32x2{pack2(lb[0][c], lb[1][c]), pack2(lb[2][c], lb[3][c])};
+                    for (int r = 0; r < 4; ++r)
+                        *reinterpret_cast<u32x4*>(&sm.Kr[0][lds_off(tb * 4 + r, cb * 8, KP)]) =
+                            u32x4{pk(f[r][0], f[r][1]), pk(f[r][2], f[r][3]), pk(f[r][4], f[r][5]), pk(f[r][6], f[r][7])};
+                }
+                // transposed: one channel row, 4 consecutive tokens = 8 contiguous bytes
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+                    *reinterpret_cast<u32x2*>(&dst[0][lds_off(cb * 8 + c, tb * 4, CH)]) =
+                        u32x2{pk(f[0][c], f[1][c]), pk(f[2][c], f[3][c])};
+            } else {
+                uint16_t hb[4][8], lb[4][8];   // [token][channel]
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) to16<NSPLIT>(f[r][c], hb[r][c], lb[r][c]);
+                if (!blk_v) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int off = lds_off(tb * 4 + r, cb * 8, KP);
+                        *reinterpret_cast<u32x4*>(&sm.Kr[0][off]) = pack8(hb[r]);
+                        if constexpr (NSPLIT == 2) *reinterpret_cast<u32x4*>(&sm.Kr[1][off]) = pack8(lb[r]);
+                    }
+                }
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const int off = lds_off(cb * 8 + c, tb * 4, CH);
+                    *reinterpret_cast<u32x2*>(&dst[0][off]) = u32x2{pack2(hb[0][c], hb[1][c]), pack2(hb[2][c], hb[3][c])};
+                    if constexpr (NSPLIT == 2)
+                        *reinterpret_cast<u32x2*>(&dst[1][off]) = u32x2{pack2(lb[0][c], lb[1][c]), pack2(lb[2][c], lb[3][c])};
+                }
             }
         }
         if (wave == 0) {
@@ -301,10 +353,12 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                 const float y = __shfl_up(x, off, 64);
                 if (lane >= off) x += y;
             }
+            // decay factors through v_exp_f32 (2^x) on log2-scaled sums; b is kept in log2 units
             const float bc = __shfl(x, 63, 64);
-            sm.b[lane] = x;
-            sm.eb[lane] = expf(x);
-            sm.ebr[lane] = expf(bc - x);
+            const float x2 = x * kLog2e, bc2 = bc * kLog2e;
+            sm.b[lane] = x2;
+            sm.eb[lane] = __builtin_amdgcn_exp2f(x2);
+            sm.ebr[lane] = __builtin_amdgcn_exp2f(bc2 - x2);
             if (lane == 0) sm.bC = bc;
         }
         for (int tile = wave; tile < 10; tile += 8) {
@@ -314,8 +368,8 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
             f32x4 gacc = zero4();
 #pragma unroll
             for (int ks = 0; ks < KSD; ++ks) {
-                const Frag<NSPLIT> a = frag_of<NSPLIT, KP>(sm.Kr, ti, ks, lane);
-                const Frag<NSPLIT> bb = frag_of<NSPLIT, KP>(sm.Kr, tj, ks, lane);   // K^T as B = rows of K
+                const Frag<NSPLIT> a = frag_of<NSPLIT, KP>(sm.Kr, ti, ks, lx);
+                const Frag<NSPLIT> bb = frag_of<NSPLIT, KP>(sm.Kr, tj, ks, lx);   // K^T as B = rows of K
                 gacc = mma<NSPLIT>(a, bb, gacc);
             }
 #pragma unroll
@@ -341,12 +395,12 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                 float ap = 0.f, ad = 0.f;
                 if (s <= t) {
                     ap = sm.F2[t][s] * sm.beta[s];
-                    ad = ap * expf(bt - sm.b[s]);
+                    ad = ap * __builtin_amdgcn_exp2f(bt - sm.b[s]);   // e^{b_t - b_s}, exponent <= 0
                 }
                 to16<NSPLIT>(ap, ph[x], pl[x]);
                 to16<NSPLIT>(ad, dh[x], dl[x]);
             }
-            const int off = frag_off(t, s0, CH);
+            const int off = lds_off(t, s0, CH);
             *reinterpret_cast<u32x4*>(&sm.Ap[0][off]) = pack8(ph);
             *reinterpret_cast<u32x4*>(&sm.Ad[0][off]) = pack8(dh);
             if constexpr (NSPLIT == 2) {
@@ -362,15 +416,15 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
             f32x4 acc = zero4();
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const Frag<NSPLIT> a = frag_of<NSPLIT, CH>(sm.Kt, mt, ks, lane);
-                const Frag<NSPLIT> bb = frag_of<NSPLIT, CH>(sm.Ap, nt, ks, lane);   // Ap^T as B = rows of Ap
+                const Frag<NSPLIT> a = frag_of<NSPLIT, CH>(sm.Kt, mt, ks, lx);
+                const Frag<NSPLIT> bb = frag_of<NSPLIT, CH>(sm.Ap, nt, ks, lx);   // Ap^T as B = rows of Ap
                 acc = mma<NSPLIT>(a, bb, acc);
             }
             // lane holds Wt[token nt*16+n16][channels mt*16+4*g4 .. +3]
             uint16_t hh[4], ll[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) to16<NSPLIT>(acc[e], hh[e], ll[e]);
-            const int off = frag_off(nt * 16 + n16, mt * 16 + 4 * g4, KP);
+            const int off = lds_off(nt * 16 + n16, mt * 16 + 4 * g4, KP);
             *reinterpret_cast<u32x2*>(&sm.Wt[0][off]) = u32x2{pack2(hh[0], hh[1]), pack2(hh[2], hh[3])};
             if constexpr (NSPLIT == 2)
                 *reinterpret_cast<u32x2*>(&sm.Wt[1][off]) = u32x2{pack2(ll[0], ll[1]), pack2(ll[2], ll[3])};
@@ -386,8 +440,8 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                     const int vt = ct - RT;  // value-channel tile
 #pragma unroll
                     for (int ks = 0; ks < 2; ++ks) {
-                        const Frag<NSPLIT> a = frag_of<NSPLIT, CH>(sm.Ad, tt, ks, lane);
-                        const Frag<NSPLIT> bb = frag_of<NSPLIT, CH>(sm.Vt, vt, ks, lane);   // V as B = rows of V^T
+                        const Frag<NSPLIT> a = frag_of<NSPLIT, CH>(sm.Ad, tt, ks, lx);
+                        const Frag<NSPLIT> bb = frag_of<NSPLIT, CH>(sm.Vt, vt, ks, lx);   // V as B = rows of V^T
                         U[tt][c] = mma<NSPLIT>(a, bb, U[tt][c]);
                     }
                 }
@@ -398,7 +452,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
         // ---- 6..8. Y = Wt X, R, X += K^T R for all owned column tiles at once (each A
         // fragment is read once per wave)
         const float bC = sm.bC;
-        const float ebC = expf(bC);
+        const float ebC = __builtin_amdgcn_exp2f(bC * kLog2e);
         if (wave < NCT) {
             f32x4 R[4][CTW];
 #pragma unroll
@@ -416,7 +470,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                 }
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
-                    const Frag<NSPLIT> a = frag_of<NSPLIT, KP>(sm.Wt, tt, kb, lane);
+                    const Frag<NSPLIT> a = frag_of<NSPLIT, KP>(sm.Wt, tt, kb, lx);
 #pragma unroll
                     for (int c = 0; c < CTW; ++c)
                         if (own_tile(c)) R[tt][c] = mma<NSPLIT>(a, xb[c], R[tt][c]);
@@ -444,7 +498,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    const Frag<NSPLIT> a = frag_of<NSPLIT, CH>(sm.Kt, rt, kb, lane);
+                    const Frag<NSPLIT> a = frag_of<NSPLIT, CH>(sm.Kt, rt, kb, lx);
 #pragma unroll
                     for (int c = 0; c < CTW; ++c)
                         if (own_tile(c)) X[rt][c] = mma<NSPLIT>(a, rb[kb][c], X[rt][c]);
