@@ -72,8 +72,8 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void compose_dense_kernel(
     __shared__ __attribute__((aligned(16))) u32x4 st_w[SW ? 2 : 1][SW ? KS : 1][2][64];
     __shared__ __attribute__((aligned(16))) u32x4 st_q[SW ? 2 : 1][SW ? KS : 1][2][64];
     __shared__ __attribute__((aligned(16))) u32x4 st_m[SW ? 2 : 1][2][64];
-    __shared__ __attribute__((aligned(16))) float st_u[SW ? 2 : 1][SW ? 8 : 1][64];
-    __shared__ __attribute__((aligned(16))) float st_eb[SW ? 2 : 1][2][4][64];
+    __shared__ __attribute__((aligned(16))) f32x4 st_u[SW ? 2 : 1][2][SW ? 64 : 1];   // U block, e^{b_w - b} (wave 0)
+    __shared__ __attribute__((aligned(16))) f32x4 st_eb[SW ? 2 : 1][2][SW ? 64 : 1];          // e^b (waves 0, 1)
     __shared__ __attribute__((aligned(16))) float st_ebw[SW ? 2 : 1][SW ? NW : 1][64];
 
     const UnitSlot us = xcd_unit_slot(blockIdx.x, NCB);
@@ -229,12 +229,12 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void compose_dense_kernel(
                     const int rt = (wave + NW * i) < RT ? wave + NW * i : 0;
 #pragma unroll
                     for (int p = 0; p < 2; ++p)
-                        dma16(rec + Rec::kK + p * Rec::kPlaneWD + frag_off(rt * 16 + n16, 8 * gk, 16) * 2, &st_k[sg][wave][i][p][0]);
+                        if (p == 0 || !sa.in_bf16)   // bf16 keys have no lo part
+                            dma16(rec + Rec::kK + p * Rec::kPlaneWD + frag_off(rt * 16 + n16, 8 * gk, 16) * 2, &st_k[sg][wave][i][p][0]);
                 }
                 dma4(rec + Rec::kEbW, &st_ebw[sg][wave][0]);
                 if (wave < 2) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) dma4(rec + Rec::kEb + (4 * g4 + e) * 4, &st_eb[sg][wave][e][0]);
+                    dma16(rec + Rec::kEbL + lane * 16, &st_eb[sg][wave][0]);
                 }
                 if (wave == 0) {   // Y wave: Wt rows, U block, e^{b_w - b}
 #pragma unroll
@@ -244,11 +244,8 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void compose_dense_kernel(
                         for (int p = 0; p < 2; ++p)
                             dma16(rec + Rec::kW + p * Rec::kPlaneWD + frag_off(n16, k0, DK) * 2, &st_w[sg][ks][p][0]);
                     }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        dma4(rec + Rec::kU + ((4 * g4 + e) * DV + cb * NB + n16) * 4, &st_u[sg][e][0]);
-                        dma4(rec + Rec::kEbw + (4 * g4 + e) * 4, &st_u[sg][4 + e][0]);
-                    }
+                    dma16(rec + Rec::kU + (cb * 64 + lane) * 16, &st_u[sg][0][0]);
+                    dma16(rec + Rec::kEbwL + lane * 16, &st_u[sg][1][0]);
                 } else if (wave == 1) {   // Z wave: q rows, Mo rows
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks) {
@@ -323,7 +320,7 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void compose_dense_kernel(
         float eb[4];
         if (wave < 2) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) eb[e] = st_eb[sg][wave][e][lane];
+            for (int e = 0; e < 4; ++e) eb[e] = st_eb[sg][wave][lane][e];
         }
         if (wave == 0) {  // state path: Y = Wt R, U' = U - diag(e^b) Y, U'' = diag(e^{b_w - b}) U'
             f32x4 y = zero4();
@@ -340,8 +337,8 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void compose_dense_kernel(
             f32x4 u, u2;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                u[e] = st_u[sg][e][lane] - eb[e] * y[e];
-                u2[e] = st_u[sg][4 + e][lane] * u[e];
+                u[e] = st_u[sg][0][lane][e] - eb[e] * y[e];
+                u2[e] = st_u[sg][1][lane][e] * u[e];
             }
             unsigned h0, h1, l0, l1;
             pack_bf16_split(u2, h0, h1, l0, l1);
@@ -370,7 +367,7 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void compose_dense_kernel(
             const int rt = wave + NW * i;
             if (rt >= RT) continue;
             const bf16x8 kh = as_frag<bf16x8>(g4 < 2 ? st_k[sg][wave][i][0][lane] : z4);   // window tokens 16..31 do not exist
-            const bf16x8 kl = as_frag<bf16x8>(g4 < 2 ? st_k[sg][wave][i][1][lane] : z4);
+            const bf16x8 kl = as_frag<bf16x8>(g4 < 2 && !sa.in_bf16 ? st_k[sg][wave][i][1][lane] : z4);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
                 const bf16x8 uh = *reinterpret_cast<const bf16x8*>(&Uh[0][ct * 16 + n16][8 * g4]);

@@ -172,9 +172,10 @@ __global__ __launch_bounds__(256) void seam_prep_kernel(
         split_bf16(mo, x, y);
         reinterpret_cast<uint16_t*>(rp + R::kM)[frag_off(t, s, W)] = bf16_bits(x);
         reinterpret_cast<uint16_t*>(rp + R::kM + R::kPlaneM)[frag_off(t, s, W)] = bf16_bits(y);
-        if (tid < W) {
-            reinterpret_cast<float*>(rp + R::kEb)[tid] = expf(bs[tid]);
-            reinterpret_cast<float*>(rp + R::kEbw)[tid] = expf(bs[W - 1] - bs[tid]);
+        {   // lane-ordered copies: thread (l, e) -> lane l, row t = 4 (l / 16) + e
+            const int l = tid >> 2, e = tid & 3, tl = 4 * (l >> 4) + e;
+            reinterpret_cast<float*>(rp + R::kEbL)[tid] = expf(bs[tl]);
+            reinterpret_cast<float*>(rp + R::kEbwL)[tid] = expf(bs[W - 1] - bs[tl]);
         }
         if (tid == 0) reinterpret_cast<float*>(rp + R::kEbW)[0] = expf(bs[W - 1]);
     }
@@ -224,9 +225,12 @@ __global__ __launch_bounds__(256) void seam_prep_kernel(
                        reinterpret_cast<uint16_t*>(rp + R::kW + R::kPlaneWD + off), wk);
             put_split8(reinterpret_cast<uint16_t*>(rp + R::kQ + off),
                        reinterpret_cast<uint16_t*>(rp + R::kQ + R::kPlaneWD + off), qx);
-            float* up = reinterpret_cast<float*>(rp + R::kU) + t * D + c0;
-            *reinterpret_cast<f32x4*>(up) = f32x4{uv[0], uv[1], uv[2], uv[3]};
-            *reinterpret_cast<f32x4*>(up + 4) = f32x4{uv[4], uv[5], uv[6], uv[7]};
+            float* up = reinterpret_cast<float*>(rp + R::kU);
+#pragma unroll
+            for (int x = 0; x < 8; ++x) {   // block cb = ch / 16, lane (t / 4, ch % 16), element t % 4
+                const int ch = c0 + x;
+                up[((ch >> 4) * 64 + (t >> 2) * 16 + (ch & 15)) * 4 + (t & 3)] = uv[x];
+            }
         }
         for (int it = tid; it < D * 2; it += 256) {
             const int ch = it >> 1, t0 = (it & 1) * 8;

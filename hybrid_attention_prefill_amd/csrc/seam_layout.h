@@ -18,10 +18,13 @@ struct SeamRec {
     static constexpr int kK = kQ + 2 * kPlaneWD;                // [2][D][16] bf16  K^T (channel-major)
     static constexpr int kM = kK + 2 * kPlaneWD;                // [2][16][16] bf16 output mixing matrix Mo
     static constexpr int kPlaneM = kSeamMaxW * kSeamMaxW * 2;
-    static constexpr int kU = kM + 2 * kPlaneM;                 // [16][D] f32      U = A diag(beta) V
-    static constexpr int kEb = kU + kSeamMaxW * D * 4;          // [16] f32  e^{b_t}
-    static constexpr int kEbw = kEb + kSeamMaxW * 4;            // [16] f32  e^{b_w - b_t}
-    static constexpr int kEbW = kEbw + kSeamMaxW * 4;           // [1]  f32  e^{b_w}
+    // Dword data in the D-fragment lane order of a 16 x 16 tile (lane l = 16 g + n holds
+    // rows 4g .. 4g+3 of column n), so each wave fetches it with one 16-byte load per lane:
+    static constexpr int kU = kM + 2 * kPlaneM;                 // [D/16][64][4] f32  U = A diag(beta) V,
+                                                                //   block cb, lane (g, n): U[4g+e][16 cb + n]
+    static constexpr int kEbL = kU + kSeamMaxW * D * 4;         // [64][4] f32  lane (g, n): e^{b_t}, t = 4g+e
+    static constexpr int kEbwL = kEbL + 64 * 16;                // [64][4] f32  lane (g, n): e^{b_w - b_t}
+    static constexpr int kEbW = kEbwL + 64 * 16;                // [1]  f32  e^{b_w}
     static constexpr int kBytes = (kEbW + 16 + 255) / 256 * 256;  // 256-byte records
 };
 
