@@ -1,18 +1,19 @@
 #!/usr/bin/env python3
 """Benchmark of the HYPIC linear-attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4|2|3|5] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 One step = one pass of the hot path over one synthetic request with all inputs
 resident in HBM:
 
-* config 4 (default): a 100,000-token prompt of 128 lognormal segments (16
-  gated-DeltaNet heads, d = 128, bf16): build (T_C, S(C|0)) for the 26 cold
-  segments, then one seam-advance call that steps the w = 8 seam window of
-  every internal segment (emitting its outputs) and composes all 128 cached
-  pairs in order.  Warm pairs come from an untimed earlier build.
-* config 2 / 3 / 5: build every segment, then compose as the workload says
-  (config 5: 64 requests x 256 cached segments per layer x 30 layers).
+* gdn-16h-d128-100k-seam (default): a 100,000-token prompt of 128 lognormal
+  segments (16 gated-DeltaNet heads, d = 128, bf16): build (T_C, S(C|0)) for
+  the 26 cold segments, then one seam-advance call that steps the w = 8 seam
+  window of every internal segment (emitting its outputs) and composes all 128
+  cached pairs in order.  Warm pairs come from an untimed earlier build.
+* retnet-8h-d64, gdn-16h-d128-32k, kda-32h-d128-131k: build every segment,
+  then compose as the workload says (kda-32h-d128-131k: 64 requests x 256
+  cached segments per layer x 30 layers).
 
 Prints one JSON line.  `value` is segment-build tokens/s (tokens built per
 second of build-kernel time); `compose_us_per_segment` is the chain kernel time
@@ -44,8 +45,12 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--config", type=int, default=4, choices=[2, 3, 4, 5])
+    p.add_argument("--workload", default="gdn-16h-d128-100k-seam",
+                   choices=["retnet-8h-d64", "gdn-16h-d128-32k", "gdn-16h-d128-100k-seam", "kda-32h-d128-131k"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="before warm-up, copy MIB MiB device-to-device once (a plain copy kernel of known "
+                        "size, the reference for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
 
 
@@ -91,7 +96,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    W = wl.make(args.config)
+    W = wl.make(args.workload)
+    seam_plan = W.seam_start is not None
+    layered = W.n_layers > 1
     H, d = W.n_heads, W.d_k
     dt = torch.bfloat16 if W.in_dtype == "bf16" else torch.float32
     T = lambda a, t: torch.from_numpy(np.ascontiguousarray(a)).to(device=dev, dtype=t)
@@ -103,14 +110,14 @@ def main():
     gate_elems = {0: 0, 1: 1, 2: d}[W.gate]
     # constant decay caches T as one number; dense T is cached in the composition kernels'
     # operand format (bf16 hi/lo planes, 4 bytes per entry like fp32)
-    t_layout = hb.T_SCALAR if args.config == 2 else hb.T_SPLIT
+    t_layout = hb.T_SCALAR if W.gate == hb.GATE_HEAD else hb.T_SPLIT
     tsz = 1 if t_layout == hb.T_SCALAR else d * d
     tdt = torch.bfloat16 if t_layout == hb.T_SPLIT else torch.float32
     tshape = lambda n: (n, H) if t_layout == hb.T_SCALAR else (n, H, 2, d * d)
     timer = Timer(torch)
     info = {}
 
-    if args.config == 4:
+    if seam_plan:
         cold = np.flatnonzero(W.cold)
         warm = np.flatnonzero(~W.cold)
         order = np.concatenate([warm, cold])           # cache slots: warm pairs first, cold last
@@ -156,7 +163,7 @@ def main():
         sb, se = T(W.cache_begin, torch.int64), T(W.cache_end, torch.int64)
         Tb = torch.empty(tshape(W.n_seg), device=dev, dtype=tdt)
         Sb = torch.empty((W.n_seg, H, d, d), device=dev)
-        if args.config == 5:
+        if layered:
             # one distinct cache copy per layer, so re-reads are not served from the 256 MB MALL
             Tc = torch.empty(tshape(W.n_layers * W.n_seg), device=dev, dtype=tdt)
             Sc = torch.empty((W.n_layers * W.n_seg, H, d, d), device=dev)
@@ -167,7 +174,7 @@ def main():
         R = torch.zeros((n_chain, H, d, d), device=dev)
         built_tokens = int((W.cache_end - W.cache_begin).sum())
 
-        if args.config == 5:
+        if layered:
             # the 30 per-layer caches: copies of one untimed earlier build
             hb.segment_build(k, v, g, beta, sb, se, gate=W.gate, delta=W.delta, t_layout=t_layout,
                              T_out=Tb, S_out=Sb)
@@ -186,13 +193,21 @@ def main():
             "segment_build": dict(
                 bytes=built_tokens * H * (2 * d * in_bytes + (gate_elems + 1) * in_bytes)
                 + W.n_seg * H * (tsz + d * d) * 4,
-                flops=built_tokens * H * (2 * d * d if args.config == 2 else 4 * d * (d + d))),
+                flops=built_tokens * H * (2 * d * d if W.gate == hb.GATE_HEAD else 4 * d * (d + d))),
             "compose": dict(bytes=n_segments_composed * H * (tsz + d * d) * 4,
                             flops=n_segments_composed * H * (2 * d * d if tsz == 1 else 2 * d * d * d)),
         }
         info.update(segments=W.n_seg, built_tokens=built_tokens, chains=n_chain, steps_per_chain=n_step,
                     layers=W.n_layers)
 
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -220,7 +235,8 @@ def main():
     dom = max(kern, key=lambda n: kern[n]["avg_us"])
     dk = kern[dom]
     roofline = {"bound": "hbm", "achieved": dk["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(dk["GBps"] / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom}
+                "frac": round(dk["GBps"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(W.name, dom),
+                "kernel": dom}
 
     line = {
         "metric": METRIC,
@@ -243,22 +259,57 @@ def main():
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(W, args.config)
+        line["cpu_baseline"] = cpu_baseline(W)
     print(json.dumps(line), flush=True)
     return 0
 
 
-def cpu_baseline(W, config):
+# Sources of the kernels each library call launches (a stored counter measurement is
+# reported only while these files are unchanged).
+CALL_SOURCES = {
+    "seam_advance": ["seam.hip", "compose.hip", "seam_layout.h", "hypic_device.h", "hypic_kernels.h"],
+    "compose": ["compose.hip", "hypic_device.h", "hypic_kernels.h"],
+    "segment_build": ["build_gdn.hip", "build_kda.hip", "build_decay.hip", "build_common.h", "hypic_device.h"],
+}
+
+
+def sources_digest(call):
+    import hashlib
+    h = hashlib.sha256()
+    for f in CALL_SOURCES[call]:
+        with open(os.path.join(ROOT, "hybrid_attention_prefill_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, call):
+    """HBM bytes per call from the stored rocprofv3 FETCH_SIZE + WRITE_SIZE passes
+    (profiles/traffic_<workload>.md), or None when there is none for this call or the
+    kernels' sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        for ln in fh:
+            if ln.startswith("traffic-json: "):
+                rec = json.loads(ln[len("traffic-json: "):])
+                if rec.get("call") == call and rec.get("sources") == sources_digest(call):
+                    return int(rec["bytes_per_call"])
+    return None
+
+
+def cpu_baseline(W):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload:
     a few of the segments the step builds, all heads (8 of them for the 32-head
     workload), packed and converted to fp64 before the clock starts."""
     import oracle
     n_thr = oracle.num_threads()
-    # about 10 s on 8-16 cores: config 4 builds every segment of the prompt (as for a fully
-    # cold request), config 3 all 32 segments, configs 2 and 5 a handful
+    # about 10 s on 8-16 cores: the 100k prompt builds every segment (as for a fully cold
+    # request), the 32k workload 24 of its 32 segments, the others a handful
     pool = np.arange(W.n_seg)
-    segs = {2: pool, 3: pool[:24], 4: pool, 5: pool[:6]}[config]
-    heads = W.n_heads if config != 5 else 8
+    segs = {"retnet-8h-d64": pool, "gdn-16h-d128-32k": pool[:24], "gdn-16h-d128-100k-seam": pool,
+            "kda-32h-d128-131k": pool[:6]}[W.name]
+    heads = W.n_heads if W.n_heads <= 16 else 8
     parts = [np.arange(W.cache_begin[s], W.cache_end[s]) for s in segs]
     idx = np.concatenate(parts)
     lens = np.array([len(p) for p in parts])

@@ -111,7 +111,7 @@ def _tokens(rng_k, rng_v, n_tok, H, dk, dv, *, k_unit, kv_scale, in_dtype):
     return _finish(k, in_dtype), _finish(v, in_dtype)
 
 
-def _cfg1(seed, *, stress, n_heads=1, d=16, n_seg=2, seg_len=64, lengths=None):
+def _gdn_tiny(seed, *, stress, n_heads=1, d=16, n_seg=2, seg_len=64, lengths=None):
     """Tiny gated DeltaNet, fp32: 1 head, d=16, 2 segments of 64 tokens."""
     ss = np.random.SeedSequence(seed).spawn(6)
     rk, rv, rb, rg, rq, _ = [np.random.default_rng(s) for s in ss]
@@ -128,7 +128,7 @@ def _cfg1(seed, *, stress, n_heads=1, d=16, n_seg=2, seg_len=64, lengths=None):
         g = -_softplus(zg)
     q = _finish(_unit_rows(rq.standard_normal((N, n_heads, d))), "f32")
     starts = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
-    return Workload(name="cfg1-gdn-tiny-f32" + ("-stress" if stress else ""), n_heads=n_heads,
+    return Workload(name="gdn-tiny-f32" + ("-stress" if stress else ""), n_heads=n_heads,
                     d_k=d, d_v=d, gate=GATE_TOKEN, delta=True, in_dtype="f32", k=k, v=v,
                     g=_finish(g, "f32"), beta=_finish(beta, "f32"), seg_start=starts,
                     cache_begin=starts[:-1].copy(), cache_end=starts[1:].copy(), q=q,
@@ -141,7 +141,7 @@ def retnet_gamma(n_heads):
     return 1.0 - 2.0 ** (-5.0 - np.arange(n_heads, dtype=np.float64))
 
 
-def _cfg2(seed, *, stress, n_heads=8, d=64, n_seg=16, seg_len=512, lengths=None):
+def _retnet(seed, *, stress, n_heads=8, d=64, n_seg=16, seg_len=512, lengths=None):
     """RetNet-style scalar decay, bf16 k/v, fp32 decay: 8 heads, d=64, 16 x 512."""
     ss = np.random.SeedSequence(seed).spawn(4)
     rk, rv, rq, _ = [np.random.default_rng(s) for s in ss]
@@ -152,7 +152,7 @@ def _cfg2(seed, *, stress, n_heads=8, d=64, n_seg=16, seg_len=512, lengths=None)
     g = np.log(retnet_gamma(n_heads)).astype(np.float32)   # decay stays fp32
     q = _finish(rq.standard_normal((N, n_heads, d)) / math.sqrt(d), "bf16")
     starts = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
-    return Workload(name="cfg2-retnet-bf16", n_heads=n_heads, d_k=d, d_v=d, gate=GATE_HEAD,
+    return Workload(name="retnet-8h-d64", n_heads=n_heads, d_k=d, d_v=d, gate=GATE_HEAD,
                     delta=False, in_dtype="bf16", k=k, v=v, g=g, beta=None, seg_start=starts,
                     cache_begin=starts[:-1].copy(), cache_end=starts[1:].copy(), q=q,
                     scale=1.0 / math.sqrt(d),
@@ -175,13 +175,13 @@ def _gdn_tokens(seed, N, H, d, *, stress, mean_len, gate_scale=0.1):
     return k, v, _finish(beta, "bf16"), _finish(g, "bf16"), q
 
 
-def _cfg3(seed, *, stress, n_heads=16, d=128, n_seg=32, seg_len=1024, lengths=None):
+def _gdn_32k(seed, *, stress, n_heads=16, d=128, n_seg=32, seg_len=1024, lengths=None):
     """Gated DeltaNet, bf16 inputs: 16 heads, d=128, 32 segments x 1024 tokens."""
     lens = np.full(n_seg, seg_len) if lengths is None else np.asarray(lengths)
     N = int(lens.sum())
     k, v, beta, g, q = _gdn_tokens(seed, N, n_heads, d, stress=stress, mean_len=float(np.mean(lens)))
     starts = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
-    return Workload(name="cfg3-gdn-bf16" + ("-stress" if stress else ""), n_heads=n_heads, d_k=d,
+    return Workload(name="gdn-16h-d128-32k" + ("-stress" if stress else ""), n_heads=n_heads, d_k=d,
                     d_v=d, gate=GATE_TOKEN, delta=True, in_dtype="bf16", k=k, v=v, g=g, beta=beta,
                     seg_start=starts, cache_begin=starts[:-1].copy(), cache_end=starts[1:].copy(),
                     q=q, scale=1.0 / math.sqrt(d),
@@ -209,7 +209,7 @@ def lognormal_lengths(seed, n_seg=128, total=100_000, median=700, sigma=0.5, min
     return L
 
 
-def _cfg4(seed, *, stress, n_heads=16, d=128, n_seg=128, total=100_000, w=8, minimum=512,
+def _gdn_100k_seam(seed, *, stress, n_heads=16, d=128, n_seg=128, total=100_000, w=8, minimum=512,
           median=700, cold_frac=0.2):
     """Gated DeltaNet 100k-token prompt: 128 lognormal segments (median 700, min 512),
     80% warm / 20% cold, seam window w=8 at every internal segment."""
@@ -226,14 +226,14 @@ def _cfg4(seed, *, stress, n_heads=16, d=128, n_seg=128, total=100_000, w=8, min
     n_cold = int(round(cold_frac * n_seg))
     cold = np.zeros(n_seg, dtype=bool)
     cold[rng.permutation(n_seg)[:n_cold]] = True
-    return Workload(name="cfg4-gdn-100k-seam" + ("-stress" if stress else ""), n_heads=n_heads,
+    return Workload(name="gdn-16h-d128-100k-seam" + ("-stress" if stress else ""), n_heads=n_heads,
                     d_k=d, d_v=d, gate=GATE_TOKEN, delta=True, in_dtype="bf16", k=k, v=v, g=g,
                     beta=beta, seg_start=starts, cache_begin=cb, cache_end=ce, q=q,
                     scale=1.0 / math.sqrt(d), w=w, seam_start=seam,
                     pair_id=np.arange(n_seg, dtype=np.int32)[None, :], cold=cold)
 
 
-def _cfg5(seed, *, stress, n_heads=32, d=128, n_seg=64, seg_len=2048, n_req=64, n_step=256,
+def _kda_131k(seed, *, stress, n_heads=32, d=128, n_seg=64, seg_len=2048, n_req=64, n_step=256,
           n_layers=30, lengths=None):
     """KDA-style per-channel gate, bf16: 32 heads, d=128, 64 x 2048 tokens; then
     n_req requests x n_step cached segments per layer x n_layers layers."""
@@ -256,7 +256,7 @@ def _cfg5(seed, *, stress, n_heads=32, d=128, n_seg=64, seg_len=2048, n_req=64, 
     # pair index = l * n_seg + segment (one distinct cache copy per layer)
     ids = rp.integers(0, n_seg, size=(n_layers, n_req, n_step)).astype(np.int32)
     ids = ids + (np.arange(n_layers, dtype=np.int32) * n_seg)[:, None, None]
-    return Workload(name="cfg5-kda-bf16" + ("-stress" if stress else ""), n_heads=n_heads, d_k=d,
+    return Workload(name="kda-32h-d128-131k" + ("-stress" if stress else ""), n_heads=n_heads, d_k=d,
                     d_v=d, gate=GATE_DIAG, delta=True, in_dtype="bf16", k=k, v=v,
                     g=_finish(g, "bf16"), beta=_finish(beta, "bf16"), seg_start=starts,
                     cache_begin=starts[:-1].copy(), cache_end=starts[1:].copy(), q=q,
@@ -264,13 +264,21 @@ def _cfg5(seed, *, stress, n_heads=32, d=128, n_seg=64, seg_len=2048, n_req=64, 
                     n_layers=n_layers)
 
 
-_MAKERS = {1: _cfg1, 2: _cfg2, 3: _cfg3, 4: _cfg4, 5: _cfg5}
+# name -> (maker, default seed)
+_MAKERS = {
+    "gdn-tiny-f32": (_gdn_tiny, 1),
+    "retnet-8h-d64": (_retnet, 2),
+    "gdn-16h-d128-32k": (_gdn_32k, 3),
+    "gdn-16h-d128-100k-seam": (_gdn_100k_seam, 4),
+    "kda-32h-d128-131k": (_kda_131k, 5),
+}
+NAMES = tuple(_MAKERS)
 
 
-def make(config: int, *, stress: bool = False, seed: int | None = None, **overrides) -> Workload:
-    """Build workload `config` (1..5).  The seed defaults to the config number.
-    Keyword overrides shrink a workload for tests (n_heads, n_seg, seg_len,
-    lengths, total, n_req, n_step, n_layers, ...)."""
-    if config not in _MAKERS:
-        raise ValueError("config must be 1..5")
-    return _MAKERS[config](config if seed is None else seed, stress=stress, **overrides)
+def make(name: str, *, stress: bool = False, seed: int | None = None, **overrides) -> Workload:
+    """Build the named workload (see NAMES).  Keyword overrides shrink a workload for
+    tests (n_heads, n_seg, seg_len, lengths, total, n_req, n_step, n_layers, ...)."""
+    if name not in _MAKERS:
+        raise ValueError(f"unknown workload {name!r}; one of {', '.join(_MAKERS)}")
+    maker, default_seed = _MAKERS[name]
+    return maker(default_seed if seed is None else seed, stress=stress, **overrides)

@@ -34,9 +34,9 @@ def _oracle_build(W, begin=None, end=None):
 
 
 @pytest.mark.parametrize("stress", [False, True])
-def test_cfg1_tiny_gdn_fp32(stress):
+def test_tiny_gdn_fp32(stress):
     """1 head, d=16, 2 x 64 tokens, fp32: pairs, composition and the full recurrence."""
-    W = wl.make(1, stress=stress)
+    W = wl.make("gdn-tiny-f32", stress=stress)
     print(W.name, flush=True)
     T, S = _gpu_build(W)
     T0, S0 = _oracle_build(W)
@@ -49,10 +49,10 @@ def test_cfg1_tiny_gdn_fp32(stress):
 
 
 @pytest.mark.parametrize("t_layout", [hb.T_SCALAR, hb.T_DENSE])
-def test_cfg2_retnet_full(t_layout):
+def test_retnet_full(t_layout):
     """RetNet-style decay, 8 heads, d=64, 16 x 512 (full size): T = gamma^L I,
     S by the oracle, and the ordered composition against the full recurrence."""
-    W = wl.make(2)
+    W = wl.make("retnet-8h-d64")
     print(W.name, t_layout, flush=True)
     T, S = _gpu_build(W, t_layout=t_layout)
     T0, S0 = _oracle_build(W)
@@ -71,11 +71,11 @@ def test_cfg2_retnet_full(t_layout):
 
 
 @pytest.mark.parametrize("stress", [False, True])
-def test_cfg3_shape_ragged(stress):
+def test_gdn_d128_ragged(stress):
     """GDN d=128, bf16: segments spanning several chunks with ragged tails,
     a one-token segment and an empty one."""
     lens = [1024, 700, 129, 1, 65]
-    W = wl.make(3, stress=stress, n_heads=3, lengths=lens)
+    W = wl.make("gdn-16h-d128-32k", stress=stress, n_heads=3, lengths=lens)
     begin = np.concatenate([W.cache_begin, [5]])
     end = np.concatenate([W.cache_end, [5]])          # empty range -> identity pair
     print(W.name, "ragged", flush=True)
@@ -86,10 +86,10 @@ def test_cfg3_shape_ragged(stress):
     assert np.all(S[-1] == 0)
 
 
-def test_cfg3_stress_compose_needs_T():
+def test_gdn_stress_compose_needs_T():
     """Stress variant: composing the GPU pairs matches the full recurrence while the
     naive sum does not, so T is genuinely tested."""
-    W = wl.make(3, stress=True, n_heads=2, n_seg=4, seg_len=512)
+    W = wl.make("gdn-16h-d128-32k", stress=True, n_heads=2, n_seg=4, seg_len=512)
     T, S = _gpu_build(W)
     Rg = torch.zeros((1, 2, 128, 128), device="cuda")
     hb.compose(dev(T, torch.float32), dev(S, torch.float32), dev(W.pair_id, torch.int32), Rg)
@@ -103,7 +103,7 @@ def test_cfg3_stress_compose_needs_T():
 def test_prefix_independence_bit_identical():
     """A segment's pair does not depend on where it sits in the packed batch or on
     its neighbours: bit-identical results for the same tokens at another offset."""
-    W = wl.make(3, n_heads=2, n_seg=3, seg_len=300)
+    W = wl.make("gdn-16h-d128-32k", n_heads=2, n_seg=3, seg_len=300)
     x = workload_tensors(W)
     n = W.n_tokens
     # second copy: the same tokens shifted behind a 77-token prefix of other tokens
@@ -121,10 +121,10 @@ def test_prefix_independence_bit_identical():
 
 
 @pytest.mark.slow
-def test_cfg3_full_size_sampled():
+def test_gdn_32k_full_size_sampled():
     """Full GDN workload (16 heads, 32 x 1024, d=128) in the benchmark's launch
     configuration; sampled (segment, head) pairs checked against the oracle."""
-    W = wl.make(3)
+    W = wl.make("gdn-16h-d128-32k")
     print(W.name, "full", flush=True)
     T, S = _gpu_build(W)
     assert np.all(np.isfinite(S)) and np.all(np.isfinite(T))
@@ -137,9 +137,9 @@ def test_cfg3_full_size_sampled():
 
 
 @pytest.mark.parametrize("stress", [False, True])
-def test_cfg5_kda_ragged(stress):
+def test_kda_ragged(stress):
     """KDA-style per-channel gate, d=128, bf16: several chunks, ragged tails, one token."""
-    W = wl.make(5, stress=stress, n_heads=2, lengths=[256, 100, 33, 1], n_req=1, n_step=1, n_layers=1)
+    W = wl.make("kda-32h-d128-131k", stress=stress, n_heads=2, lengths=[256, 100, 33, 1], n_req=1, n_step=1, n_layers=1)
     print(W.name, "ragged", flush=True)
     T, S = _gpu_build(W)
     T0, S0 = _oracle_build(W)
@@ -147,8 +147,8 @@ def test_cfg5_kda_ragged(stress):
     print(f"{W.name}: S {eS:.2e} T {eT}")
 
 
-def test_cfg5_kda_stress_compose_matches_full():
-    W = wl.make(5, stress=True, n_heads=2, n_seg=4, seg_len=300, n_req=1, n_step=1, n_layers=1)
+def test_kda_stress_compose_matches_full():
+    W = wl.make("kda-32h-d128-131k", stress=True, n_heads=2, n_seg=4, seg_len=300, n_req=1, n_step=1, n_layers=1)
     T, S = _gpu_build(W)
     Rg = torch.zeros((1, 2, 128, 128), device="cuda")
     hb.compose(dev(T, torch.float32), dev(S, torch.float32), dev(np.arange(4, dtype=np.int32)[None, :], torch.int32), Rg)
@@ -159,9 +159,9 @@ def test_cfg5_kda_stress_compose_matches_full():
     assert rel_f(naive, full).min() > 20 * TOL["bf16"]
 
 
-def test_cfg5_segment_shape_all_heads_sampled():
+def test_kda_segment_shape_all_heads_sampled():
     """32 heads x 2048-token segments (the KDA workload's segment shape), sampled checks."""
-    W = wl.make(5, n_seg=3, n_req=1, n_step=1, n_layers=1)
+    W = wl.make("kda-32h-d128-131k", n_seg=3, n_req=1, n_step=1, n_layers=1)
     print(W.name, "32 heads x 3 x 2048", flush=True)
     T, S = _gpu_build(W)
     assert np.all(np.isfinite(S)) and np.all(np.isfinite(T))
@@ -172,17 +172,17 @@ def test_cfg5_segment_shape_all_heads_sampled():
         assert_pairs_close(T[s:s + 1, h:h + 1], S[s:s + 1, h:h + 1], T0, S0, TOL["bf16"], f"seg {s} head {h}")
 
 
-@pytest.mark.parametrize("cfg,kw", [
-    (1, dict(stress=True)),
-    (2, dict(n_seg=3, seg_len=200)),
-    (3, dict(n_heads=2, lengths=[300, 65, 1])),
-    (5, dict(n_heads=2, lengths=[100, 33], n_req=1, n_step=1, n_layers=1)),
+@pytest.mark.parametrize("name,kw", [
+    ("gdn-tiny-f32", dict(stress=True)),
+    ("retnet-8h-d64", dict(n_seg=3, seg_len=200)),
+    ("gdn-16h-d128-32k", dict(n_heads=2, lengths=[300, 65, 1])),
+    ("kda-32h-d128-131k", dict(n_heads=2, lengths=[100, 33], n_req=1, n_step=1, n_layers=1)),
 ])
-def test_split_T_layout(cfg, kw):
+def test_split_T_layout(name, kw):
     """T emitted as bf16 hi/lo planes (the layout the composition kernels read): the
     planes are exactly the round-to-nearest-even split of the fp32 T the same kernel
     writes in the dense layout, S is bit-identical, and hi + lo matches the oracle."""
-    W = wl.make(cfg, **kw)
+    W = wl.make(name, **kw)
     print(W.name, "split T", flush=True)
     x = workload_tensors(W)
     sb, se = dev(W.cache_begin, torch.int64), dev(W.cache_end, torch.int64)

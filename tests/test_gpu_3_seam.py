@@ -18,10 +18,11 @@ pytestmark = pytest.mark.gpu
 TOL = {"f32": 1e-4, "bf16": 5e-3}
 
 
-def _seam_workload(cfg, lens, w, H, stress=False):
-    """A cfg-shaped prompt with explicit segment lengths, seams at internal segments."""
+def _seam_workload(name, lens, w, H, stress=False):
+    """A prompt shaped like workload `name` with explicit segment lengths, seams at
+    internal segments."""
     kw = dict(n_heads=H, lengths=lens, stress=stress)
-    W = wl.make(cfg, **kw)
+    W = wl.make(name, **kw)
     starts = W.seg_start
     W.cache_begin = starts[:-1].copy()
     W.cache_begin[1:] += w
@@ -78,7 +79,7 @@ def _check(W, R, out, S_ref, outs_ref, tol):
 
 @pytest.mark.parametrize("w,t_layout", [(8, hb.T_SPLIT), (3, hb.T_SPLIT), (16, hb.T_SPLIT), (8, hb.T_DENSE)])
 def test_seam_gdn_bf16_ragged(w, t_layout):
-    W = _seam_workload(3, [150, 97, 64 + w, 300, 40], w, H=2)
+    W = _seam_workload("gdn-16h-d128-32k", [150, 97, 64 + w, 300, 40], w, H=2)
     print(W.name, "seam w", w, "T layout", t_layout, flush=True)
     R, out = _gpu(W, t_layout=t_layout)
     S_ref, outs_ref = _reference(W)
@@ -86,7 +87,7 @@ def test_seam_gdn_bf16_ragged(w, t_layout):
 
 
 def test_seam_gdn_bf16_stress():
-    W = _seam_workload(3, [512, 530, 600, 520], 8, H=2, stress=True)
+    W = _seam_workload("gdn-16h-d128-32k", [512, 530, 600, 520], 8, H=2, stress=True)
     R, out = _gpu(W)
     S_ref, outs_ref = _reference(W)
     _check(W, R, out, S_ref, outs_ref, TOL["bf16"])
@@ -94,7 +95,7 @@ def test_seam_gdn_bf16_stress():
 
 @pytest.mark.parametrize("stress,t_layout", [(False, hb.T_SPLIT), (True, hb.T_SPLIT), (True, hb.T_DENSE)])
 def test_seam_gdn_fp32_d16(stress, t_layout):
-    W = _seam_workload(1, [64, 40, 77], 8, H=1, stress=stress)
+    W = _seam_workload("gdn-tiny-f32", [64, 40, 77], 8, H=1, stress=stress)
     print(W.name, "fp32 seam", stress, t_layout, flush=True)
     R, out = _gpu(W, t_layout=t_layout)
     S_ref, outs_ref = _reference(W)
@@ -103,7 +104,7 @@ def test_seam_gdn_fp32_d16(stress, t_layout):
 
 def test_seam_only_without_pairs():
     """pair_id NULL: only the seam windows advance the state."""
-    W = _seam_workload(3, [40, 30, 50], 8, H=2)
+    W = _seam_workload("gdn-16h-d128-32k", [40, 30, 50], 8, H=2)
     R, out = _gpu(W, with_pairs=False)
     S = np.zeros((2, 128, 128))
     for i in (1, 2):
@@ -115,12 +116,12 @@ def test_seam_only_without_pairs():
     assert rel_f(R, S).max() <= TOL["bf16"]
 
 
-def test_cfg4_full_100k():
+def test_gdn_100k_prompt_full():
     """The 100k-token prompt (128 lognormal segments, 16 heads, d=128, w=8) in the
     benchmark's launch configuration: final state and all 127 windows' outputs."""
-    W = wl.make(4)
+    W = wl.make("gdn-16h-d128-100k-seam")
     print(W.name, flush=True)
     R, out = _gpu(W)
     S_ref, outs_ref = _reference(W)
     worst = _check(W, R, out, S_ref, outs_ref, TOL["bf16"])
-    print(f"cfg4: final state rel_F {rel_f(R, S_ref).max():.2e}, worst window output {worst:.2e}")
+    print(f"100k prompt: final state rel_F {rel_f(R, S_ref).max():.2e}, worst window output {worst:.2e}")

@@ -189,7 +189,7 @@ def test_identity_transition_gives_plain_sum():
 @pytest.mark.parametrize("h", range(8))
 def test_retnet_closed_form(h):
     """Constant decay gamma: T_C = gamma^L I and S(C|0) = sum_t gamma^(L-1-t) k_t v_t^T."""
-    W = wl.make(2, n_heads=8, n_seg=2, seg_len=96)
+    W = wl.make("retnet-8h-d64", n_heads=8, n_seg=2, seg_len=96)
     T, S = oracle.segment_build(W.k, W.v, W.g, None, W.cache_begin, W.cache_end,
                                 gate=W.gate, delta=W.delta)
     gam = math.exp(float(W.g[h]))
@@ -262,7 +262,7 @@ def test_transition_product_is_a_contraction(gate):
 def test_naive_sum_closed_form_and_failure():
     """Two RetNet segments: the naive sum drops T(C2), so its error is
     ||(1 - gamma^L2) S1|| / ||gamma^L2 S1 + S2||, at least five times the bf16 tolerance on every head."""
-    W = wl.make(2, n_heads=8, n_seg=2, seg_len=256)
+    W = wl.make("retnet-8h-d64", n_heads=8, n_seg=2, seg_len=256)
     T, S = oracle.segment_build(W.k, W.v, W.g, None, W.cache_begin, W.cache_end,
                                 gate=W.gate, delta=W.delta)
     good = oracle.compose(T, S, [[0, 1]])[0]
@@ -279,7 +279,7 @@ def test_naive_sum_loses_the_decayed_prefix():
     """If C2 writes nothing, the naive sum's error relative to the prefix state is
     1 - gamma^L2: 0.2213 for gamma = 1 - 2^-10 over 256 tokens, one reading of
     the 22% slow-head figure the pages quote."""
-    W = wl.make(2, n_heads=8, n_seg=2, seg_len=256)
+    W = wl.make("retnet-8h-d64", n_heads=8, n_seg=2, seg_len=256)
     v = W.v.copy()
     v[256:] = 0.0
     T, S = oracle.segment_build(W.k, v, W.g, None, W.cache_begin, W.cache_end,

@@ -14,14 +14,14 @@ def test_round_bf16_matches_torch_rne():
 
 
 def test_deterministic():
-    a = wl.make(3, n_heads=2, n_seg=2, seg_len=64)
-    b = wl.make(3, n_heads=2, n_seg=2, seg_len=64)
+    a = wl.make("gdn-16h-d128-32k", n_heads=2, n_seg=2, seg_len=64)
+    b = wl.make("gdn-16h-d128-32k", n_heads=2, n_seg=2, seg_len=64)
     for f in ("k", "v", "g", "beta", "q"):
         assert np.array_equal(getattr(a, f), getattr(b, f))
 
 
-def test_cfg4_lengths_and_plan():
-    W = wl.make(4, n_heads=1, d=16)
+def test_100k_prompt_lengths_and_plan():
+    W = wl.make("gdn-16h-d128-100k-seam", n_heads=1, d=16)
     L = W.seg_len
     assert L.sum() == 100_000 and L.min() >= 512 and len(L) == 128
     assert 600 < np.median(L) < 800
@@ -33,7 +33,7 @@ def test_cfg4_lengths_and_plan():
 
 
 def test_bf16_inputs_are_representable_and_keys_unit():
-    W = wl.make(3, n_heads=2, n_seg=1, seg_len=256)
+    W = wl.make("gdn-16h-d128-32k", n_heads=2, n_seg=1, seg_len=256)
     for f in ("k", "v", "g", "beta", "q"):
         x = getattr(W, f)
         assert np.array_equal(wl.round_bf16(x), x)
@@ -43,18 +43,18 @@ def test_bf16_inputs_are_representable_and_keys_unit():
 
 
 def test_retnet_decay_stays_fp32():
-    W = wl.make(2, n_heads=8, n_seg=1, seg_len=16)
+    W = wl.make("retnet-8h-d64", n_heads=8, n_seg=1, seg_len=16)
     gam = np.exp(W.g.astype(np.float64))
     assert np.all(gam < 1.0)
     assert abs(gam[7] - (1 - 2.0 ** -12)) < 1e-7
 
 
-@pytest.mark.parametrize("cfg", [1, 3, 5])
-def test_stress_gates_mean_total(cfg):
+@pytest.mark.parametrize("name", ["gdn-tiny-f32", "gdn-16h-d128-32k", "kda-32h-d128-131k"])
+def test_stress_gates_mean_total(name):
     kw = dict(n_heads=2, n_seg=4)
-    if cfg != 1:
+    if name != "gdn-tiny-f32":
         kw["seg_len"] = 256
-    W = wl.make(cfg, stress=True, **kw)
+    W = wl.make(name, stress=True, **kw)
     L = int(W.seg_len[0])
     g = W.g.astype(np.float64).reshape(W.n_tokens, -1)
     tot = g.mean() * L      # expected log-decay over one segment
@@ -62,8 +62,8 @@ def test_stress_gates_mean_total(cfg):
     assert W.beta.mean() < 0.05
 
 
-def test_cfg5_plan():
-    W = wl.make(5, n_heads=2, n_seg=4, seg_len=64, n_req=3, n_step=5, n_layers=2)
+def test_kda_reuse_plan():
+    W = wl.make("kda-32h-d128-131k", n_heads=2, n_seg=4, seg_len=64, n_req=3, n_step=5, n_layers=2)
     assert W.pair_id.shape == (6, 5)
     assert np.all(W.pair_id[:3] < 4) and np.all(W.pair_id[3:] >= 4) and np.all(W.pair_id[3:] < 8)
     assert W.g.shape == (W.n_tokens, 2, 128)
