@@ -43,7 +43,6 @@ using namespace bld;
 
 constexpr int CH = 64;       // chunk length
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int LDF = CH + 1;  // padded LDS row for fp32 64x64 matrices
 
 template <int D, int NSPLIT>
 struct alignas(16) GdnSmem {
@@ -51,12 +50,13 @@ struct alignas(16) GdnSmem {
     uint16_t Kr[NSPLIT][CH * KP];  // K, rows = tokens, cols = channels (>= D zero)
     uint16_t Kt[NSPLIT][D * CH];   // K^T, rows = channels, cols = tokens
     uint16_t Vt[NSPLIT][D * CH];   // V^T, rows = channels, cols = tokens
-    uint16_t Ap[NSPLIT][CH * CH];  // At diag(beta)
-    uint16_t Ad[NSPLIT][CH * CH];  // A diag(beta)
     uint16_t Wt[NSPLIT][CH * KP];  // Wt, rows = tokens, cols = channels (>= D zero)
-    float F1[CH][LDF];             // Lt (strictly lower)
-    float F2[CH][LDF];             // At
-    float F3[32][33];              // inverse scratch
+    // block forward substitution operands (fp16 hi/lo planes):
+    uint16_t Ln[2][CH * CH];       // -Lt off the 16 x 16 diagonal blocks (rows t, cols s; zero elsewhere)
+    uint16_t Lnd[2][CH * CH];      // the same with the decay: -e^{b_t - b_s} Lt
+    uint16_t Dv[2][4][512];        // A fragments of (I + Lt_ii)^-1, diagonal block i (cols 16..31 zero)
+    uint16_t Dvd[2][4][512];       // the same with the decay e^{b_t - b_s}
+    float Sd[4][16][20];           // per diagonal block: Lt_ii, then its inverse (fp32)
     float gate[CH], beta[CH], b[CH], eb[CH], ebr[CH];   // b in log2 units
     float bC;
 };
@@ -89,61 +89,6 @@ __device__ __forceinline__ Frag<NSPLIT> frag_of(const Arr& a, int rt, int ks, in
     f.h = lds_frag<NCOLS>(a[0], rt, ks, lx);
     if constexpr (NSPLIT == 2) f.l = lds_frag<NCOLS>(a[1], rt, ks, lx);
     return f;
-}
-
-// Inverse of I + Lt (64x64 unit lower triangular, Lt in F1) into F2.
-template <typename SM>
-__device__ void tri_inverse(SM& sm, int wave, int lane) {
-    // (1) the four 16x16 diagonal blocks, one column per lane
-    if (wave < 4 && lane < 16) {
-        const int o = wave * 16, j = lane;
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float s = (r == j) ? 1.f : 0.f;
-#pragma unroll
-            for (int q = 0; q < r; ++q) s -= sm.F1[o + r][o + q] * x[q];
-            x[r] = s;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sm.F2[o + r][o + j] = x[r];
-    }
-    __syncthreads();
-    // (2) blocks (1,0) and (3,2):  A_ij = -D_i L_ij D_j
-    if (wave < 2) {
-        const int i = 2 * wave + 1, j = 2 * wave;
-        f32x4 p = mm16_f32(&sm.F1[i * 16][j * 16], LDF, &sm.F2[j * 16][j * 16], LDF, lane);
-        float* tmp = &sm.F3[wave * 16][0];
-        st16_f32(tmp, 33, p, lane, 1.f);
-    }
-    __syncthreads();
-    if (wave < 2) {
-        const int i = 2 * wave + 1, j = 2 * wave;
-        f32x4 q = mm16_f32(&sm.F2[i * 16][i * 16], LDF, &sm.F3[wave * 16][0], 33, lane);
-        st16_f32(&sm.F2[i * 16][j * 16], LDF, q, lane, -1.f);
-    }
-    __syncthreads();
-    // (3) lower-left 32x32 block: -E1 Lt[2:4, 0:2] E0 with E0, E1 the 32x32 inverses
-    if (wave < 4) {
-        const int r = 2 + (wave >> 1), cc = wave & 1;
-        f32x4 p = mm16_f32(&sm.F1[r * 16][cc * 16], LDF, &sm.F2[cc * 16][cc * 16], LDF, lane);
-        if (cc == 0) {
-            const f32x4 p2 = mm16_f32(&sm.F1[r * 16][16], LDF, &sm.F2[16][0], LDF, lane);
-            p += p2;
-        }
-        st16_f32(&sm.F3[(r - 2) * 16][cc * 16], 33, p, lane, 1.f);
-    }
-    __syncthreads();
-    if (wave < 4) {
-        const int r = 2 + (wave >> 1), cc = wave & 1;
-        f32x4 q = mm16_f32(&sm.F2[r * 16][r * 16], LDF, &sm.F3[(r - 2) * 16][cc * 16], 33, lane);
-        if (r == 3) {
-            const f32x4 q2 = mm16_f32(&sm.F2[48][32], LDF, &sm.F3[0][cc * 16], 33, lane);
-            q += q2;
-        }
-        st16_f32(&sm.F2[r * 16][cc * 16], LDF, q, lane, -1.f);
-    }
-    __syncthreads();
 }
 
 // 16-bit operand bits of x (NSPLIT 1: fp16; NSPLIT 2: fp16 hi and lo)
@@ -206,6 +151,11 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
     beg = beg < 0 ? 0 : (beg > n_tokens ? n_tokens : beg);
     end = end < beg ? beg : (end > n_tokens ? n_tokens : end);
 
+    // the diagonal and upper blocks of the substitution matrices are never written: zero once
+    for (int i = tid; i < 2 * CH * CH; i += 512) {
+        (&sm.Ln[0][0])[i] = 0;
+        (&sm.Lnd[0][0])[i] = 0;
+    }
     // zero the channel padding of Kr / Wt once (D < 32 only)
     if (KP > D) {
         for (int i = tid; i < NSPLIT * CH * KP; i += 512) {
@@ -345,26 +295,28 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
         if (c0 + CH < end) prefetch(c0 + CH);
         __syncthreads();
 
-        // ---- 2. gate cumsum (wave 0, one token per lane) and Lt = tril(b K K^T, -1)
-        if (wave == 0) {
+        // ---- 2. gate cumsum (every wave, one token per lane, in log2 units) and the Gram
+        // blocks Lt = tril(b K K^T, -1): the diagonal 16 x 16 blocks are inverted by waves 0..3
+        // (forward substitution, fp32), the off-diagonal blocks stored negated by waves 4..7
+        float b2;   // b_lane * log2(e)
+        {
             float x = sm.gate[lane];
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float y = __shfl_up(x, off, 64);
                 if (lane >= off) x += y;
             }
-            // decay factors through v_exp_f32 (2^x) on log2-scaled sums; b is kept in log2 units
             const float bc = __shfl(x, 63, 64);
-            const float x2 = x * kLog2e, bc2 = bc * kLog2e;
-            sm.b[lane] = x2;
-            sm.eb[lane] = __builtin_amdgcn_exp2f(x2);
-            sm.ebr[lane] = __builtin_amdgcn_exp2f(bc2 - x2);
-            if (lane == 0) sm.bC = bc;
+            b2 = x * kLog2e;
+            if (wave == 0) {   // decay factors of the state update, through v_exp_f32 (2^x)
+                const float bc2 = bc * kLog2e;
+                sm.b[lane] = b2;
+                sm.eb[lane] = __builtin_amdgcn_exp2f(b2);
+                sm.ebr[lane] = __builtin_amdgcn_exp2f(bc2 - b2);
+                if (lane == 0) sm.bC = bc;
+            }
         }
-        for (int tile = wave; tile < 10; tile += 8) {
-            // lower-triangular 16x16 tiles (ti >= tj) of the 64x64 Gram matrix
-            const int ti = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
-            const int tj = tile - ti * (ti + 1) / 2;
+        auto gram = [&](int ti, int tj) -> f32x4 {   // lane (g, n): G[16 ti + 4g + e][16 tj + n]
             f32x4 gacc = zero4();
 #pragma unroll
             for (int ks = 0; ks < KSD; ++ks) {
@@ -372,79 +324,139 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                 const Frag<NSPLIT> bb = frag_of<NSPLIT, KP>(sm.Kr, tj, ks, lx);   // K^T as B = rows of K
                 gacc = mma<NSPLIT>(a, bb, gacc);
             }
+            return gacc;
+        };
+        if (wave < 4) {
+            const int i = wave;
+            const f32x4 gacc = gram(i, i);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int t = ti * 16 + 4 * g4 + e, s = tj * 16 + n16;
-                sm.F1[t][s] = (s < t) ? sm.beta[t] * gacc[e] : 0.f;
+                const int r = 4 * g4 + e;
+                sm.Sd[i][r][n16] = (n16 < r) ? sm.beta[16 * i + r] * gacc[e] : 0.f;
             }
-        }
-        __syncthreads();
-
-        // ---- 3. At = (I + Lt)^-1
-        tri_inverse(sm, wave, lane);
-
-        // ---- 4. Ap = At diag(beta), Ad = A diag(beta) with A[t][s] = e^{b_t - b_s} At[t][s];
-        // one token row t and 8 consecutive s per thread (16-byte stores)
-        {
-            const int t = tid >> 3, s0 = (tid & 7) * 8;
-            uint16_t ph[8], pl[8], dh[8], dl[8];
-            const float bt = sm.b[t];
+            // column j = lane of (I + Lt_ii)^-1 by forward substitution; every read of the block
+            // precedes the first write back (one wave, in order)
+            if (lane < 16) {
+                float x[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float acc = (r == lane) ? 1.f : 0.f;
+#pragma unroll
+                    for (int q = 0; q < r; ++q) acc -= sm.Sd[i][r][q] * x[q];
+                    x[r] = acc;
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sm.Sd[i][r][lane] = x[r];
+            }
+            // A fragment: lane (n, g) holds row n, columns 8g .. 8g+7 (zero for g >= 2)
+            const float bt = __shfl(b2, 16 * i + n16, 64);
+            uint16_t dh[8], dl[8], ddh[8], ddl[8];
 #pragma unroll
             for (int x = 0; x < 8; ++x) {
-                const int s = s0 + x;
-                float ap = 0.f, ad = 0.f;
-                if (s <= t) {
-                    ap = sm.F2[t][s] * sm.beta[s];
-                    ad = ap * __builtin_amdgcn_exp2f(bt - sm.b[s]);   // e^{b_t - b_s}, exponent <= 0
-                }
-                to16<NSPLIT>(ap, ph[x], pl[x]);
-                to16<NSPLIT>(ad, dh[x], dl[x]);
+                const int col = 8 * (g4 & 1) + x;
+                const float bs = __shfl(b2, 16 * i + col, 64);
+                const float dv = g4 < 2 ? sm.Sd[i][n16][col] : 0.f;
+                const float dd = col <= n16 ? dv * __builtin_amdgcn_exp2f(bt - bs) : 0.f;
+                to16<2>(dv, dh[x], dl[x]);
+                to16<2>(dd, ddh[x], ddl[x]);
             }
-            const int off = lds_off(t, s0, CH);
-            *reinterpret_cast<u32x4*>(&sm.Ap[0][off]) = pack8(ph);
-            *reinterpret_cast<u32x4*>(&sm.Ad[0][off]) = pack8(dh);
-            if constexpr (NSPLIT == 2) {
-                *reinterpret_cast<u32x4*>(&sm.Ap[1][off]) = pack8(pl);
-                *reinterpret_cast<u32x4*>(&sm.Ad[1][off]) = pack8(dl);
+            *reinterpret_cast<u32x4*>(&sm.Dv[0][i][lane * 8]) = pack8(dh);
+            *reinterpret_cast<u32x4*>(&sm.Dv[1][i][lane * 8]) = pack8(dl);
+            *reinterpret_cast<u32x4*>(&sm.Dvd[0][i][lane * 8]) = pack8(ddh);
+            *reinterpret_cast<u32x4*>(&sm.Dvd[1][i][lane * 8]) = pack8(ddl);
+        } else {
+            // off-diagonal blocks (1,0) (2,0) (2,1) (3,0) (3,1) (3,2), two waves taking two
+            for (int k = wave - 4; k < 6; k += 4) {
+                const int ti = k < 1 ? 1 : k < 3 ? 2 : 3;
+                const int tj = k - (ti * (ti - 1)) / 2;
+                const f32x4 gacc = gram(ti, tj);
+                const int s_ = 16 * tj + n16;
+                const float bs = __shfl(b2, s_, 64);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 16 * ti + 4 * g4 + e;
+                    const float l = -sm.beta[t] * gacc[e];
+                    const float ld = l * __builtin_amdgcn_exp2f(__shfl(b2, t, 64) - bs);
+                    const int off = lds_off(t, s_, CH);
+                    uint16_t h, lo;
+                    to16<2>(l, h, lo);
+                    sm.Ln[0][off] = h;
+                    sm.Ln[1][off] = lo;
+                    to16<2>(ld, h, lo);
+                    sm.Lnd[0][off] = h;
+                    sm.Lnd[1][off] = lo;
+                }
             }
         }
         __syncthreads();
 
-        // ---- 5. Wt^T = K^T Ap^T (written token-major into Wt), and U for own S tiles
-        for (int tile = wave; tile < RT * 4; tile += 8) {
-            const int mt = tile / 4, nt = tile % 4;  // channel tile, token tile
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const Frag<NSPLIT> a = frag_of<NSPLIT, CH>(sm.Kt, mt, ks, lx);
-                const Frag<NSPLIT> bb = frag_of<NSPLIT, CH>(sm.Ap, nt, ks, lx);   // Ap^T as B = rows of Ap
-                acc = mma<NSPLIT>(a, bb, acc);
-            }
-            // lane holds Wt[token nt*16+n16][channels mt*16+4*g4 .. +3]
-            uint16_t hh[4], ll[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) to16<NSPLIT>(acc[e], hh[e], ll[e]);
-            const int off = lds_off(nt * 16 + n16, mt * 16 + 4 * g4, KP);
-            *reinterpret_cast<u32x2*>(&sm.Wt[0][off]) = u32x2{pack2(hh[0], hh[1]), pack2(hh[2], hh[3])};
-            if constexpr (NSPLIT == 2)
-                *reinterpret_cast<u32x2*>(&sm.Wt[1][off]) = u32x2{pack2(ll[0], ll[1]), pack2(ll[2], ll[3])};
-        }
+        // ---- 3. block forward substitution, one chain per owned column tile (no barriers):
+        //   Wt_i = (I + Lt_ii)^-1 (diag(beta) K_i - sum_{j<i} Lt_ij Wt_j)       (H tiles: channel tile)
+        //   U_i  = the same with the decayed blocks and diag(beta) V_i           (S tiles: value tile)
+        // on fp16 hi/lo operands (three products).  Wt goes to LDS for every wave's Y = Wt X;
+        // U stays in this wave's registers for its S tile.
         f32x4 U[4][CTW];
 #pragma unroll
         for (int c = 0; c < CTW; ++c) {
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) U[tt][c] = zero4();
             const int ct = wave + 8 * c;
+            if (!own_tile(c)) continue;
+            const bool is_s = s_tile(c);
+            const int q = is_s ? ct - RT : ct;                 // channel / value tile
+            const uint16_t(*rhs_src)[D * CH] = is_s ? sm.Vt : sm.Kt;
+            Frag<2> prev[2];                                   // solved blocks as B fragments (k = tokens)
+            f32x4 sol[4];
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                U[tt][c] = zero4();
-                if (s_tile(c) && ct < NCT) {
-                    const int vt = ct - RT;  // value-channel tile
+            for (int i = 0; i < 4; ++i) {
+                // right-hand side diag(beta) K_i (or V_i): lane (g, n) = rows 16i + 4g + e, column 16q + n
+                f32x4 acc;
+                {
+                    const int off = lds_off(16 * q + n16, 16 * i + 4 * g4, CH);
+                    const u32x2 hw = *reinterpret_cast<const u32x2*>(&rhs_src[0][off]);
+                    u32x2 lw = u32x2{0u, 0u};
+                    if constexpr (NSPLIT == 2) lw = *reinterpret_cast<const u32x2*>(&rhs_src[1][off]);
 #pragma unroll
-                    for (int ks = 0; ks < 2; ++ks) {
-                        const Frag<NSPLIT> a = frag_of<NSPLIT, CH>(sm.Ad, tt, ks, lx);
-                        const Frag<NSPLIT> bb = frag_of<NSPLIT, CH>(sm.Vt, vt, ks, lx);   // V as B = rows of V^T
-                        U[tt][c] = mma<NSPLIT>(a, bb, U[tt][c]);
+                    for (int e = 0; e < 4; ++e) {
+                        const unsigned hb = (hw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                        const unsigned lb = (lw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                        const float v = (float)__builtin_bit_cast(_Float16, (uint16_t)hb) +
+                                        (float)__builtin_bit_cast(_Float16, (uint16_t)lb);
+                        acc[e] = sm.beta[16 * i + 4 * g4 + e] * v;
                     }
                 }
+                // - sum_{j<i} Lt_ij X_j over the 32-token k-blocks that hold solved blocks
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    if (32 * ks >= 16 * i) break;
+                    Frag<2> a;
+                    a.h = lds_frag<CH>(is_s ? sm.Lnd[0] : sm.Ln[0], i, ks, lx);
+                    a.l = lds_frag<CH>(is_s ? sm.Lnd[1] : sm.Ln[1], i, ks, lx);
+                    acc = mma<2>(a, prev[ks], acc);
+                }
+                // X_i = (I + Lt_ii)^-1 acc
+                Frag<2> dinv;
+                dinv.h = *reinterpret_cast<const f16x8*>(&(is_s ? sm.Dvd[0] : sm.Dv[0])[i][lane * 8]);
+                dinv.l = *reinterpret_cast<const f16x8*>(&(is_s ? sm.Dvd[1] : sm.Dv[1])[i][lane * 8]);
+                sol[i] = mma<2>(dinv, dpair_to_frag<2>(acc, zero4()), zero4());
+                if (i == 0) prev[0] = dpair_to_frag<2>(sol[0], zero4());
+                if (i == 1) prev[0] = dpair_to_frag<2>(sol[0], sol[1]);
+                if (i == 2) prev[1] = dpair_to_frag<2>(sol[2], zero4());
+            }
+            if (is_s) {
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) U[tt][c] = sol[tt];
+            } else {   // Wt rows 16i + 4g + e, channel 16q + n, token-major
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int off = lds_off(16 * i + 4 * g4 + e, 16 * q + n16, KP);
+                        uint16_t h, lo;
+                        to16<NSPLIT>(sol[i][e], h, lo);
+                        sm.Wt[0][off] = h;
+                        if constexpr (NSPLIT == 2) sm.Wt[1][off] = lo;
+                    }
             }
         }
         __syncthreads();
