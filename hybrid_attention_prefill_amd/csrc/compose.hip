@@ -323,17 +323,23 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void compose_dense_kernel(
             for (int e = 0; e < 4; ++e) eb[e] = st_eb[sg][wave][lane][e];
         }
         if (wave == 0) {  // state path: Y = Wt R, U' = U - diag(e^b) Y, U'' = diag(e^{b_w - b}) U'
-            f32x4 y = zero4();
+            // all operand fragments first (one LDS wait), then the products
+            bf16x8 wh[KS], wl[KS], bh[KS], bl[KS];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 wh = as_frag<bf16x8>(st_w[sg][ks][0][lane]);
-                const bf16x8 wl = as_frag<bf16x8>(st_w[sg][ks][1][lane]);
-                const bf16x8 bh = rfrag(Rh[buf], n16, ks * 32 + 8 * g4);
-                const bf16x8 bl = rfrag(Rl[buf], n16, ks * 32 + 8 * g4);
-                y = mma_bf16(wh, bh, y);
-                y = mma_bf16(wh, bl, y);
-                y = mma_bf16(wl, bh, y);
+                wh[ks] = as_frag<bf16x8>(st_w[sg][ks][0][lane]);
+                wl[ks] = as_frag<bf16x8>(st_w[sg][ks][1][lane]);
+                bh[ks] = rfrag(Rh[buf], n16, ks * 32 + 8 * g4);
+                bl[ks] = rfrag(Rl[buf], n16, ks * 32 + 8 * g4);
             }
+            f32x4 y = zero4(), y2 = zero4();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                y = mma_bf16(wh[ks], bh[ks], y);
+                y2 = mma_bf16(wh[ks], bl[ks], y2);
+                y = mma_bf16(wl[ks], bh[ks], y);
+            }
+            y += y2;
             f32x4 u, u2;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -348,15 +354,24 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void compose_dense_kernel(
             *reinterpret_cast<u32x2*>(&Uh[1][n16][4 * g4]) = u32x2{h0, h1};
             *reinterpret_cast<u32x2*>(&Ul[1][n16][4 * g4]) = u32x2{l0, l1};
         } else if (wave == 1) {  // Z = Q R for the outputs (padded window rows of q are zero)
+            bf16x8 qh[KS], bh[KS], bl[KS];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 qh = as_frag<bf16x8>(st_q[sg][ks][0][lane]);
-                const bf16x8 bh = rfrag(Rh[buf], n16, ks * 32 + 8 * g4);
-                const bf16x8 bl = rfrag(Rl[buf], n16, ks * 32 + 8 * g4);
-                z = mma_bf16(qh, bh, z);
-                z = mma_bf16(qh, bl, z);
-                if (!sa.in_bf16) z = mma_bf16(as_frag<bf16x8>(st_q[sg][ks][1][lane]), bh, z);   // bf16 q has no lo part
+                qh[ks] = as_frag<bf16x8>(st_q[sg][ks][0][lane]);
+                bh[ks] = rfrag(Rh[buf], n16, ks * 32 + 8 * g4);
+                bl[ks] = rfrag(Rl[buf], n16, ks * 32 + 8 * g4);
             }
+            f32x4 z2 = zero4();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                z = mma_bf16(qh[ks], bh[ks], z);
+                z2 = mma_bf16(qh[ks], bl[ks], z2);
+            }
+            if (!sa.in_bf16) {   // bf16 q has no lo part
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) z = mma_bf16(as_frag<bf16x8>(st_q[sg][ks][1][lane]), bh[ks], z);
+            }
+            z += z2;
         }
         lds_barrier();
         // state: R <- e^{b_w} R + K^T U''
