@@ -396,67 +396,75 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
         // on fp16 hi/lo operands (three products).  Wt goes to LDS for every wave's Y = Wt X;
         // U stays in this wave's registers for its S tile.
         f32x4 U[4][CTW];
-#pragma unroll
-        for (int c = 0; c < CTW; ++c) {
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) U[tt][c] = zero4();
-            const int ct = wave + 8 * c;
-            if (!own_tile(c)) continue;
-            const bool is_s = s_tile(c);
-            const int q = is_s ? ct - RT : ct;                 // channel / value tile
-            const uint16_t(*rhs_src)[D * CH] = is_s ? sm.Vt : sm.Kt;
-            Frag<2> prev[2];                                   // solved blocks as B fragments (k = tokens)
-            f32x4 sol[4];
+        {
+            // the chains of this wave's tiles advance block by block together, so the
+            // latency of one chain's step overlaps the other's
+            Frag<2> prev[2][CTW];                              // solved blocks as B fragments (k = tokens)
+            f32x4 sol[4][CTW];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                // right-hand side diag(beta) K_i (or V_i): lane (g, n) = rows 16i + 4g + e, column 16q + n
-                f32x4 acc;
-                {
-                    const int off = lds_off(16 * q + n16, 16 * i + 4 * g4, CH);
-                    const u32x2 hw = *reinterpret_cast<const u32x2*>(&rhs_src[0][off]);
-                    u32x2 lw = u32x2{0u, 0u};
-                    if constexpr (NSPLIT == 2) lw = *reinterpret_cast<const u32x2*>(&rhs_src[1][off]);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const unsigned hb = (hw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                        const unsigned lb = (lw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                        const float v = (float)__builtin_bit_cast(_Float16, (uint16_t)hb) +
-                                        (float)__builtin_bit_cast(_Float16, (uint16_t)lb);
-                        acc[e] = sm.beta[16 * i + 4 * g4 + e] * v;
+                for (int c = 0; c < CTW; ++c) {
+                    if (!own_tile(c)) continue;
+                    const bool is_s = s_tile(c);
+                    const int q = is_s ? wave + 8 * c - RT : wave + 8 * c;   // channel / value tile
+                    const uint16_t(*rhs_src)[D * CH] = is_s ? sm.Vt : sm.Kt;
+                    // right-hand side diag(beta) K_i (or V_i): lane (g, n) = rows 16i + 4g + e, column 16q + n
+                    f32x4 acc;
+                    {
+                        const int off = lds_off(16 * q + n16, 16 * i + 4 * g4, CH);
+                        const u32x2 hw = *reinterpret_cast<const u32x2*>(&rhs_src[0][off]);
+                        u32x2 lw = u32x2{0u, 0u};
+                        if constexpr (NSPLIT == 2) lw = *reinterpret_cast<const u32x2*>(&rhs_src[1][off]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const unsigned hb = (hw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                            const unsigned lb = (lw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                            const float v = (float)__builtin_bit_cast(_Float16, (uint16_t)hb) +
+                                            (float)__builtin_bit_cast(_Float16, (uint16_t)lb);
+                            acc[e] = sm.beta[16 * i + 4 * g4 + e] * v;
+                        }
                     }
-                }
-                // - sum_{j<i} Lt_ij X_j over the 32-token k-blocks that hold solved blocks
+                    // - sum_{j<i} Lt_ij X_j over the 32-token k-blocks that hold solved blocks
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    if (32 * ks >= 16 * i) break;
-                    Frag<2> a;
-                    a.h = lds_frag<CH>(is_s ? sm.Lnd[0] : sm.Ln[0], i, ks, lx);
-                    a.l = lds_frag<CH>(is_s ? sm.Lnd[1] : sm.Ln[1], i, ks, lx);
-                    acc = mma<2>(a, prev[ks], acc);
+                    for (int ks = 0; ks < 2; ++ks) {
+                        if (32 * ks >= 16 * i) break;
+                        Frag<2> a;
+                        a.h = lds_frag<CH>(is_s ? sm.Lnd[0] : sm.Ln[0], i, ks, lx);
+                        a.l = lds_frag<CH>(is_s ? sm.Lnd[1] : sm.Ln[1], i, ks, lx);
+                        acc = mma<2>(a, prev[ks][c], acc);
+                    }
+                    // X_i = (I + Lt_ii)^-1 acc
+                    Frag<2> dinv;
+                    dinv.h = *reinterpret_cast<const f16x8*>(&(is_s ? sm.Dvd[0] : sm.Dv[0])[i][lane * 8]);
+                    dinv.l = *reinterpret_cast<const f16x8*>(&(is_s ? sm.Dvd[1] : sm.Dv[1])[i][lane * 8]);
+                    sol[i][c] = mma<2>(dinv, dpair_to_frag<2>(acc, zero4()), zero4());
+                    if (i == 0) prev[0][c] = dpair_to_frag<2>(sol[0][c], zero4());
+                    if (i == 1) prev[0][c] = dpair_to_frag<2>(sol[0][c], sol[1][c]);
+                    if (i == 2) prev[1][c] = dpair_to_frag<2>(sol[2][c], zero4());
                 }
-                // X_i = (I + Lt_ii)^-1 acc
-                Frag<2> dinv;
-                dinv.h = *reinterpret_cast<const f16x8*>(&(is_s ? sm.Dvd[0] : sm.Dv[0])[i][lane * 8]);
-                dinv.l = *reinterpret_cast<const f16x8*>(&(is_s ? sm.Dvd[1] : sm.Dv[1])[i][lane * 8]);
-                sol[i] = mma<2>(dinv, dpair_to_frag<2>(acc, zero4()), zero4());
-                if (i == 0) prev[0] = dpair_to_frag<2>(sol[0], zero4());
-                if (i == 1) prev[0] = dpair_to_frag<2>(sol[0], sol[1]);
-                if (i == 2) prev[1] = dpair_to_frag<2>(sol[2], zero4());
             }
-            if (is_s) {
 #pragma unroll
-                for (int tt = 0; tt < 4; ++tt) U[tt][c] = sol[tt];
-            } else {   // Wt rows 16i + 4g + e, channel 16q + n, token-major
+            for (int c = 0; c < CTW; ++c) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int tt = 0; tt < 4; ++tt) U[tt][c] = zero4();
+                if (!own_tile(c)) continue;
+                if (s_tile(c)) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int off = lds_off(16 * i + 4 * g4 + e, 16 * q + n16, KP);
-                        uint16_t h, lo;
-                        to16<NSPLIT>(sol[i][e], h, lo);
-                        sm.Wt[0][off] = h;
-                        if constexpr (NSPLIT == 2) sm.Wt[1][off] = lo;
-                    }
+                    for (int tt = 0; tt < 4; ++tt) U[tt][c] = sol[tt][c];
+                } else {   // Wt rows 16i + 4g + e, channel 16q + n, token-major
+                    const int q = wave + 8 * c;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int off = lds_off(16 * i + 4 * g4 + e, 16 * q + n16, KP);
+                            uint16_t h, lo;
+                            to16<NSPLIT>(sol[i][c][e], h, lo);
+                            sm.Wt[0][off] = h;
+                            if constexpr (NSPLIT == 2) sm.Wt[1][off] = lo;
+                        }
+                }
             }
         }
         __syncthreads();
