@@ -122,7 +122,7 @@ hypic_status hypic_compose(const hypic_dims* dims, int32_t n_chain, int32_t n_st
                         "hypic_compose");
     if (dims->d_k != dims->d_v) return fail(HYPIC_E_UNSUPPORTED, "d_k != d_v is not implemented");
     return from_hip(hypic::compose_dense(dims->d_k, n_chain, dims->n_heads, n_step, pair_id, n_pair, T_cache,
-                                         dims->t_layout == HYPIC_T_SPLIT, S_cache, S_run, nullptr, st),
+                                         dims->t_layout == HYPIC_T_SPLIT, S_cache, S_run, st),
                     "hypic_compose");
 }
 
@@ -166,9 +166,8 @@ hypic_status hypic_seam_advance(const hypic_dims* dims, int32_t n_chain, int32_t
                                     g, beta, bf16, scale, ws, st);
     if (e != hipSuccess) return from_hip(e, "hypic_seam_advance (window preparation)");
     hypic::SeamArgs sa{seam_start, n_tokens, w, (int)bf16, scale, q, k, ws, out};
-    return from_hip(hypic::compose_dense(dims->d_k, n_chain, dims->n_heads, n_step, pair_id,
-                                         pair_id ? n_pair : 0, T_cache, dims->t_layout == HYPIC_T_SPLIT, S_cache,
-                                         S_run, &sa, st),
+    return from_hip(hypic::seam_chain(dims->d_k, n_chain, dims->n_heads, n_step, pair_id, pair_id ? n_pair : 0,
+                                      T_cache, dims->t_layout == HYPIC_T_SPLIT, S_cache, S_run, sa, st),
                     "hypic_seam_advance");
 }
 

@@ -15,34 +15,26 @@
 // SPLIT, loaded as is) or split in registers from fp32.  The product is taken as
 // hi*hi + hi*lo + lo*hi on v_mfma_f32_16x16x32_bf16 (relative error ~2^-16, with
 // fp32's exponent range, so tiny T entries are not flushed).
-//
-// With SEAM (hypic_seam_advance, [ZH] section 2.2) a step may first advance the
-// state through its seam window using the state-independent window factors
-// prepared by seam.hip: Y = Wt R and Z = Q R on MFMA, then the window outputs
-// O = scale diag(e^b) Z + Mo U' and the rank-16 update
-// R <- e^{b_w} R + K^T diag(e^{b_w-b}) U', U' = U - diag(e^b) Y.
+// (hypic_seam_advance, which also steps seam windows, runs seam_chain.hip.)
 #include "hypic_device.h"
 #include "hypic_kernels.h"
-#include "seam_layout.h"
 
 namespace hypic {
 
 // s_waitcnt immediate (gfx9 encoding) that waits for every outstanding vector-memory
-// operation (loads, stores and global->LDS direct loads) and every LDS access:
-// vmcnt = 0, expcnt = 7 (unconstrained), lgkmcnt = 0.
+// operation and every LDS access: vmcnt = 0, expcnt = 7 (unconstrained), lgkmcnt = 0.
 constexpr unsigned kWaitVmcnt0 = 0x0070;
-constexpr int kRing = 512, kRingFill = 256;   // LDS ring of per-step pair ids / seam starts
+constexpr int kRing = 512, kRingFill = 256;   // LDS ring of per-step pair ids
 
 // waves per workgroup: one 16-row tile of the state per wave at d_k = 128
 constexpr int chain_waves(int dk) { return dk >= 128 ? 8 : 4; }
 
 // TS: T cached as bf16 hi/lo planes ([n_pair][H][2][DK][DK], hypic_t_layout SPLIT),
 // fed to the MFMA units as loaded; otherwise fp32 T, split in registers.
-template <int DK, int DV, int NB, bool SEAM, bool TS>
+template <int DK, int DV, int NB, bool TS>
 __global__ __launch_bounds__(64 * chain_waves(DK)) void compose_dense_kernel(
     int n_units, int H, int n_step, const int32_t* __restrict__ pair_id, int n_pair,
-    const void* __restrict__ Tc, const float* __restrict__ Sc, float* __restrict__ Srun,
-    SeamArgs sa)
+    const void* __restrict__ Tc, const float* __restrict__ Sc, float* __restrict__ Srun)
 {
     constexpr int NCB = DV / NB;
     constexpr int KP = DK < 32 ? 32 : DK;   // contraction length padded to the MFMA K
@@ -52,29 +44,9 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void compose_dense_kernel(
     constexpr int NW = chain_waves(DK);
     constexpr int RTW = (RT + NW - 1) / NW; // row tiles per wave
     constexpr int LDB = KP + 8;             // LDS row length (16-bit units), padded
-    constexpr int LDW = 32 + 8;
-    constexpr int SW = SEAM ? 1 : 0;
-    using Rec = SeamRec<DK>;
-    static_assert(!SEAM || CT == 1, "seam path: one 16-column tile per workgroup");
     __shared__ __attribute__((aligned(16))) uint16_t Rh[2][NB][LDB];   // R, bf16 hi, [column][row]
     __shared__ __attribute__((aligned(16))) uint16_t Rl[2][NB][LDB];   // R, bf16 lo
-    __shared__ __attribute__((aligned(16))) uint16_t Uh[SW ? 2 : 1][SW ? NB : 1][LDW];  // [U'' | U'] hi, [col][token]
-    __shared__ __attribute__((aligned(16))) uint16_t Ul[SW ? 2 : 1][SW ? NB : 1][LDW];
     __shared__ int ring_id[kRing];
-    __shared__ int64_t ring_s0[SW ? kRing : 1];
-    // Seam window factors of the next step, fetched by global->LDS direct loads into
-    // wave-private slots (two stages).  Lane l's 16 (or 4) bytes land at byte 16 l (4 l)
-    // of a slot, and each lane reads back exactly what it fetched.
-    //   every wave: K^T hi/lo of its row tiles, e^{b_w}
-    //   wave 0 (Y = Wt R): Wt hi/lo, U block and e^{b_w - b} (dwords), e^b
-    //   wave 1 (Z = Q R, outputs): q hi/lo, Mo hi/lo, e^b
-    __shared__ __attribute__((aligned(16))) u32x4 st_k[SW ? 2 : 1][SW ? NW : 1][SW ? RTW : 1][2][64];
-    __shared__ __attribute__((aligned(16))) u32x4 st_w[SW ? 2 : 1][SW ? KS : 1][2][64];
-    __shared__ __attribute__((aligned(16))) u32x4 st_q[SW ? 2 : 1][SW ? KS : 1][2][64];
-    __shared__ __attribute__((aligned(16))) u32x4 st_m[SW ? 2 : 1][2][64];
-    __shared__ __attribute__((aligned(16))) f32x4 st_u[SW ? 2 : 1][2][SW ? 64 : 1];   // U block, e^{b_w - b} (wave 0)
-    __shared__ __attribute__((aligned(16))) f32x4 st_eb[SW ? 2 : 1][2][SW ? 64 : 1];          // e^b (waves 0, 1)
-    __shared__ __attribute__((aligned(16))) float st_ebw[SW ? 2 : 1][SW ? NW : 1][64];
 
     const UnitSlot us = xcd_unit_slot(blockIdx.x, NCB);
     if (us.unit >= n_units) return;
@@ -86,12 +58,6 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void compose_dense_kernel(
         for (int i = threadIdx.x; i < 2 * NB * LDB; i += blockDim.x) {
             (&Rh[0][0][0])[i] = 0;
             (&Rl[0][0][0])[i] = 0;
-        }
-    }
-    if constexpr (SEAM) {  // window tokens 16..31 of the k = token operands stay zero
-        for (int i = threadIdx.x; i < 2 * NB * LDW; i += blockDim.x) {
-            (&Uh[0][0][0])[i] = 0;
-            (&Ul[0][0][0])[i] = 0;
         }
     }
     __syncthreads();
@@ -152,41 +118,29 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void compose_dense_kernel(
     // one of two register sets (the loop is unrolled by two, so the sets never get copied)
     struct Step {
         int id;                                        // pair index, or -1
-        int64_t s0;                                    // seam window start, or -1
         u32x4 th[TS ? RTW : 1][TS ? KS : 1];           // T rows of this wave, bf16 hi (A operand)
         u32x4 tl[TS ? RTW : 1][TS ? KS : 1];           //                      bf16 lo
         float ta[TS ? 1 : RTW][TS ? 1 : KS][8];        // T rows, fp32
         float sv[RTW][CT][4];                          // S block (D layout)
     };
-    const int32_t* ids = pair_id ? pair_id + (size_t)c * n_step : nullptr;
-    const int64_t* seams = SEAM ? sa.seam_start + (size_t)c * n_step : nullptr;
-    // Pair ids and seam starts go through an LDS ring of 512 steps, filled 256 steps ahead, so
-    // the per-step lookups are LDS reads and never wait on the vector-memory counter.
+    const int32_t* ids = pair_id + (size_t)c * n_step;
+    // Pair ids go through an LDS ring of 512 steps, filled 256 steps ahead, so the per-step
+    // lookups are LDS reads and never wait on the vector-memory counter.
     auto fill_ring = [&](int base) {   // steps [base, base + 256)
         for (int x = threadIdx.x; x < kRingFill; x += blockDim.x) {
             const int j = base + x;
-            ring_id[j & (kRing - 1)] = (j < n_step && ids) ? ids[j] : -1;
-            if constexpr (SEAM) ring_s0[j & (kRing - 1)] = j < n_step ? seams[j] : -1;
+            ring_id[j & (kRing - 1)] = j < n_step ? ids[j] : -1;
         }
     };
     auto read_id = [&](int j) -> int { return ring_id[j & (kRing - 1)]; };
-    auto read_s0 = [&](int j) -> int64_t {
-        if constexpr (!SEAM) return -1;
-        return ring_s0[j & (kRing - 1)];
-    };
-    // The loads below are unconditional (addresses clamped into the pair; lanes and waves
-    // outside the tile are masked where the values are used): a load whose result is
-    // selected or copied right away makes the compiler wait for it, and with the in-order
-    // vector-memory counter that would wait for the whole prefetch.
-    auto load_step = [&](int j, int id, int64_t s0, Step& st) {
+    // The loads below are unconditional within a step that has a pair (addresses clamped
+    // into the pair; lanes and waves outside the tile are masked where the values are
+    // used): a load whose result is selected or copied right away makes the compiler wait
+    // for it, and with the in-order vector-memory counter that would wait for the whole
+    // prefetch.
+    auto load_step = [&](int id, Step& st) {
         id = __builtin_amdgcn_readfirstlane((unsigned)id < (unsigned)n_pair ? id : -1);
-        if constexpr (SEAM) {
-            s0 = (s0 >= 0 && s0 + sa.w <= sa.n_tokens) ? s0 : -1;
-            s0 = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane((unsigned)((uint64_t)s0 >> 32)) << 32) |
-                           (uint64_t)__builtin_amdgcn_readfirstlane((unsigned)(uint64_t)s0));
-        }
         st.id = id;
-        st.s0 = s0;
         if (id >= 0) {
             const float* S = Sc + ((size_t)id * H + h) * DK * DV + cb * NB;
 #pragma unroll
@@ -212,64 +166,26 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void compose_dense_kernel(
                         st.sv[i][ct][e] = S[(size_t)(rt * 16 + 4 * g4 + e) * DV + ct * 16 + n16];
             }
         }
-        if constexpr (SEAM) {
-            if (s0 >= 0) {
-                const int sg = j & 1;
-                const size_t cj = (size_t)c * n_step + j;
-                const unsigned char* rec = reinterpret_cast<const unsigned char*>(sa.ws) + (cj * H + h) * Rec::kBytes;
-                auto dma16 = [&](const unsigned char* src, void* slot) {
-                    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)slot, 16, 0, 0);
-                };
-                auto dma4 = [&](const unsigned char* src, void* slot) {
-                    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)slot, 4, 0, 0);
-                };
-                const int gk = g4 & 1;   // lanes g4 >= 2 fetch a duplicate (zeroed at use)
-#pragma unroll
-                for (int i = 0; i < RTW; ++i) {
-                    const int rt = (wave + NW * i) < RT ? wave + NW * i : 0;
-#pragma unroll
-                    for (int p = 0; p < 2; ++p)
-                        if (p == 0 || !sa.in_bf16)   // bf16 keys have no lo part
-                            dma16(rec + Rec::kK + p * Rec::kPlaneWD + frag_off(rt * 16 + n16, 8 * gk, 16) * 2, &st_k[sg][wave][i][p][0]);
-                }
-                dma4(rec + Rec::kEbW, &st_ebw[sg][wave][0]);
-                if (wave < 2) {
-                    dma16(rec + Rec::kEbL + lane * 16, &st_eb[sg][wave][0]);
-                }
-                if (wave == 0) {   // Y wave: Wt rows, U block, e^{b_w - b}
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) {
-                        const int k0 = (ks * 32 + 8 * g4) < DK ? ks * 32 + 8 * g4 : 0;   // past DK: B rows are zero
-#pragma unroll
-                        for (int p = 0; p < 2; ++p)
-                            dma16(rec + Rec::kW + p * Rec::kPlaneWD + frag_off(n16, k0, DK) * 2, &st_w[sg][ks][p][0]);
-                    }
-                    dma16(rec + Rec::kU + (cb * 64 + lane) * 16, &st_u[sg][0][0]);
-                    dma16(rec + Rec::kEbwL + lane * 16, &st_u[sg][1][0]);
-                } else if (wave == 1) {   // Z wave: q rows, Mo rows
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) {
-                        const int k0 = (ks * 32 + 8 * g4) < DK ? ks * 32 + 8 * g4 : 0;
-                        dma16(rec + Rec::kQ + frag_off(n16, k0, DK) * 2, &st_q[sg][ks][0][0]);
-                        if (!sa.in_bf16) dma16(rec + Rec::kQ + Rec::kPlaneWD + frag_off(n16, k0, DK) * 2, &st_q[sg][ks][1][0]);
-                    }
-#pragma unroll
-                    for (int p = 0; p < 2; ++p)
-                        dma16(rec + Rec::kM + p * Rec::kPlaneM + frag_off(n16, 8 * gk, 16) * 2, &st_m[sg][p][0]);
-                }
-            }
-        }
     };
 
-    // ---- R <- T R + S on the planes `buf` (result in the accumulators)
+    // ---- R <- T R + S on the planes `buf` (result in the accumulators); the three
+    // products hi*hi, hi*lo, lo*hi go to separate accumulators (shorter dependency chains)
     auto compose_step = [&](const Step& st, int buf) {
 #pragma unroll
         for (int i = 0; i < RTW; ++i) {
             const int rt = wave + NW * i;
             if (rt >= RT) continue;
-            f32x4 p[CT];
+            // separate accumulators only where the column tiles give too little independent work
+            constexpr int NA = CT >= 4 ? 1 : 3;
+            f32x4 p0[CT], p1[NA == 3 ? CT : 1], p2[NA == 3 ? CT : 1];
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) p[ct] = f32x4{st.sv[i][ct][0], st.sv[i][ct][1], st.sv[i][ct][2], st.sv[i][ct][3]};
+            for (int ct = 0; ct < CT; ++ct) {
+                p0[ct] = f32x4{st.sv[i][ct][0], st.sv[i][ct][1], st.sv[i][ct][2], st.sv[i][ct][3]};
+                if constexpr (NA == 3) {
+                    p1[ct] = zero4();
+                    p2[ct] = zero4();
+                }
+            }
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 bf16x8 ah, al;
@@ -287,141 +203,26 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void compose_dense_kernel(
                 for (int ct = 0; ct < CT; ++ct) {
                     const bf16x8 bh = rfrag(Rh[buf], ct * 16 + n16, ks * 32 + 8 * g4);
                     const bf16x8 bl = rfrag(Rl[buf], ct * 16 + n16, ks * 32 + 8 * g4);
-                    p[ct] = mma_bf16(ah, bh, p[ct]);
-                    p[ct] = mma_bf16(ah, bl, p[ct]);
-                    p[ct] = mma_bf16(al, bh, p[ct]);
+                    p0[ct] = mma_bf16(ah, bh, p0[ct]);
+                    if constexpr (NA == 3) {
+                        p1[ct] = mma_bf16(ah, bl, p1[ct]);
+                        p2[ct] = mma_bf16(al, bh, p2[ct]);
+                    } else {
+                        p0[ct] = mma_bf16(ah, bl, p0[ct]);
+                        p0[ct] = mma_bf16(al, bh, p0[ct]);
+                    }
                 }
             }
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) acc[i][ct] = p[ct];
-        }
-    };
-
-    // ---- one seam window on the planes `buf`: R <- e^{b_w} R + K^T U'' and the window
-    // outputs.  The window factors come from the LDS stage `sg` this wave's direct loads
-    // filled.  The outputs are stored one step later (o_pend), so the wait at the top of
-    // the next step does not wait for their write acknowledgements.
-    f32x4 o_pend = zero4();
-    size_t o_cj = 0;
-    bool o_valid = false;
-    auto flush_out = [&]() {
-        if (o_valid) {
-            const int col = cb * NB + n16;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 4 * g4 + e;
-                if (t < sa.w) sa.out[((o_cj * sa.w + t) * H + h) * DV + col] = o_pend[e];
-            }
-            o_valid = false;
-        }
-    };
-    auto seam_step = [&](int buf, size_t cj, int sg) {
-        f32x4 z = zero4();
-        float eb[4];
-        if (wave < 2) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) eb[e] = st_eb[sg][wave][lane][e];
-        }
-        if (wave == 0) {  // state path: Y = Wt R, U' = U - diag(e^b) Y, U'' = diag(e^{b_w - b}) U'
-            // all operand fragments first (one LDS wait), then the products
-            bf16x8 wh[KS], wl[KS], bh[KS], bl[KS];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                wh[ks] = as_frag<bf16x8>(st_w[sg][ks][0][lane]);
-                wl[ks] = as_frag<bf16x8>(st_w[sg][ks][1][lane]);
-                bh[ks] = rfrag(Rh[buf], n16, ks * 32 + 8 * g4);
-                bl[ks] = rfrag(Rl[buf], n16, ks * 32 + 8 * g4);
-            }
-            f32x4 y = zero4(), y2 = zero4();
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                y = mma_bf16(wh[ks], bh[ks], y);
-                y2 = mma_bf16(wh[ks], bl[ks], y2);
-                y = mma_bf16(wl[ks], bh[ks], y);
-            }
-            y += y2;
-            f32x4 u, u2;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                u[e] = st_u[sg][0][lane][e] - eb[e] * y[e];
-                u2[e] = st_u[sg][1][lane][e] * u[e];
-            }
-            unsigned h0, h1, l0, l1;
-            pack_bf16_split(u2, h0, h1, l0, l1);
-            *reinterpret_cast<u32x2*>(&Uh[0][n16][4 * g4]) = u32x2{h0, h1};
-            *reinterpret_cast<u32x2*>(&Ul[0][n16][4 * g4]) = u32x2{l0, l1};
-            pack_bf16_split(u, h0, h1, l0, l1);
-            *reinterpret_cast<u32x2*>(&Uh[1][n16][4 * g4]) = u32x2{h0, h1};
-            *reinterpret_cast<u32x2*>(&Ul[1][n16][4 * g4]) = u32x2{l0, l1};
-        } else if (wave == 1) {  // Z = Q R for the outputs (padded window rows of q are zero)
-            bf16x8 qh[KS], bh[KS], bl[KS];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                qh[ks] = as_frag<bf16x8>(st_q[sg][ks][0][lane]);
-                bh[ks] = rfrag(Rh[buf], n16, ks * 32 + 8 * g4);
-                bl[ks] = rfrag(Rl[buf], n16, ks * 32 + 8 * g4);
-            }
-            f32x4 z2 = zero4();
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                z = mma_bf16(qh[ks], bh[ks], z);
-                z2 = mma_bf16(qh[ks], bl[ks], z2);
-            }
-            if (!sa.in_bf16) {   // bf16 q has no lo part
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) z = mma_bf16(as_frag<bf16x8>(st_q[sg][ks][1][lane]), bh[ks], z);
-            }
-            z += z2;
-        }
-        lds_barrier();
-        // state: R <- e^{b_w} R + K^T U''
-        const float ebW = st_ebw[sg][wave][lane];
-        const u32x4 z4 = u32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int i = 0; i < RTW; ++i) {
-            const int rt = wave + NW * i;
-            if (rt >= RT) continue;
-            const bf16x8 kh = as_frag<bf16x8>(g4 < 2 ? st_k[sg][wave][i][0][lane] : z4);   // window tokens 16..31 do not exist
-            const bf16x8 kl = as_frag<bf16x8>(g4 < 2 && !sa.in_bf16 ? st_k[sg][wave][i][1][lane] : z4);
-#pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
-                const bf16x8 uh = *reinterpret_cast<const bf16x8*>(&Uh[0][ct * 16 + n16][8 * g4]);
-                const bf16x8 ul = *reinterpret_cast<const bf16x8*>(&Ul[0][ct * 16 + n16][8 * g4]);
-                f32x4 a = acc[i][ct] * ebW;
-                a = mma_bf16(kh, uh, a);
-                a = mma_bf16(kh, ul, a);
-                if (!sa.in_bf16) a = mma_bf16(kl, uh, a);   // bf16 keys have no lo part
-                acc[i][ct] = a;
+                if constexpr (NA == 3) acc[i][ct] = p0[ct] + (p1[ct] + p2[ct]);
+                else acc[i][ct] = p0[ct];
             }
-        }
-        // outputs: O = scale diag(e^b) Z + Mo U'   (off the state's critical path)
-        if (wave == 1) {
-            const bf16x8 mh = as_frag<bf16x8>(g4 < 2 ? st_m[sg][0][lane] : z4);
-            const bf16x8 ml = as_frag<bf16x8>(g4 < 2 ? st_m[sg][1][lane] : z4);
-            const bf16x8 uh = *reinterpret_cast<const bf16x8*>(&Uh[1][n16][8 * g4]);
-            const bf16x8 ul = *reinterpret_cast<const bf16x8*>(&Ul[1][n16][8 * g4]);
-            f32x4 o;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = sa.scale * eb[e] * z[e];
-            o = mma_bf16(mh, uh, o);
-            o = mma_bf16(mh, ul, o);
-            o = mma_bf16(ml, uh, o);
-            o_pend = o;
-            o_cj = cj;
-            o_valid = true;
         }
     };
 
     int cur = 0;
-    auto run_step = [&](int j, const Step& st) {
-        if constexpr (SEAM) {
-            if (st.s0 >= 0) {  // uniform over the workgroup
-                seam_step(cur, (size_t)c * n_step + j, j & 1);
-                store_split(cur ^ 1);
-                lds_barrier();
-                cur ^= 1;
-            }
-        }
+    auto run_step = [&](const Step& st) {
         if (st.id >= 0) {  // uniform over the workgroup
             compose_step(st, cur);
             store_split(cur ^ 1);
@@ -435,34 +236,27 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void compose_dense_kernel(
     lds_barrier();
     Step sA, sB;
     int id1 = read_id(1);
-    int64_t s1 = read_s0(1);
-    load_step(0, read_id(0), read_s0(0), sA);
+    load_step(read_id(0), sA);
     // Every load of step j was issued a whole step earlier: wait for all of them once, at the
-    // top of the step, then store the previous step's outputs and issue step j+1's loads.
-    // (Using a value right after its load would make the in-order vector-memory counter drain
-    // the prefetch as well.)
+    // top of the step, then issue step j+1's loads.  (Using a value right after its load
+    // would make the in-order vector-memory counter drain the prefetch as well.)
     for (int j = 0; j < n_step; j += 2) {
-        // step j from sA; prefetch step j+1 into sB; ids of step j+2
+        // step j from sA; prefetch step j+1 into sB; id of step j+2
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        if constexpr (SEAM) flush_out();
         if (j > 0 && (j & (kRingFill - 1)) == 0) {  // steps j+256 .. j+511 replace steps j-256 .. j-1
             fill_ring(j + kRingFill);
             lds_barrier();
         }
         const int id2 = read_id(j + 2);
-        const int64_t s2 = read_s0(j + 2);
-        if (j + 1 < n_step) load_step(j + 1, id1, s1, sB);
-        run_step(j, sA);
+        if (j + 1 < n_step) load_step(id1, sB);
+        run_step(sA);
         if (j + 1 >= n_step) break;
-        // step j+1 from sB; prefetch step j+2 into sA; ids of step j+3
+        // step j+1 from sB; prefetch step j+2 into sA; id of step j+3
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        if constexpr (SEAM) flush_out();
         id1 = read_id(j + 3);
-        s1 = read_s0(j + 3);
-        if (j + 2 < n_step) load_step(j + 2, id2, s2, sA);
-        run_step(j + 1, sB);
+        if (j + 2 < n_step) load_step(id2, sA);
+        run_step(sB);
     }
-    if constexpr (SEAM) flush_out();
 
 #pragma unroll
     for (int i = 0; i < RTW; ++i) {
@@ -505,22 +299,12 @@ __global__ __launch_bounds__(256) void compose_scalar_kernel(
 // ---------------------------------------------------------------- launchers
 template <int DK, int DV, int NB, bool TS>
 static hipError_t launch_dense(int n_chain, int H, int n_step, const int32_t* pair_id, int n_pair,
-                               const void* Tc, const float* Sc, float* Srun, const SeamArgs* sa,
-                               hipStream_t st)
+                               const void* Tc, const float* Sc, float* Srun, hipStream_t st)
 {
     const int n_units = n_chain * H;
     const int grid = xcd_grid_size(n_units, DV / NB);
-    const dim3 block(64 * chain_waves(DK));
-    if (sa) {
-        // the seam epilogue works on 16-column blocks
-        if constexpr (NB == 16)
-            hipLaunchKernelGGL((compose_dense_kernel<DK, DV, NB, true, TS>), dim3(grid), block, 0, st,
-                               n_units, H, n_step, pair_id, n_pair, Tc, Sc, Srun, *sa);
-        else
-            return hipErrorInvalidValue;
-    } else
-        hipLaunchKernelGGL((compose_dense_kernel<DK, DV, NB, false, TS>), dim3(grid), block, 0, st,
-                           n_units, H, n_step, pair_id, n_pair, Tc, Sc, Srun, SeamArgs{});
+    hipLaunchKernelGGL((compose_dense_kernel<DK, DV, NB, TS>), dim3(grid), dim3(64 * chain_waves(DK)), 0, st,
+                       n_units, H, n_step, pair_id, n_pair, Tc, Sc, Srun);
     return hipGetLastError();
 }
 
@@ -534,15 +318,13 @@ static int pick_nb(long long n_units, int dv)
 }
 
 hipError_t compose_dense(int d, int n_chain, int H, int n_step, const int32_t* pair_id, int n_pair,
-                         const void* Tc, bool t_split, const float* Sc, float* Srun, const SeamArgs* sa,
-                         hipStream_t st)
+                         const void* Tc, bool t_split, const float* Sc, float* Srun, hipStream_t st)
 {
-    int nb = pick_nb((long long)n_chain * H, d);
-    if (sa) nb = 16;   // the seam path works on 16-column blocks
+    const int nb = pick_nb((long long)n_chain * H, d);
 #define HYPIC_CASE(D_, NB_)                                                                                    \
     if (d == D_ && nb == NB_)                                                                                  \
-        return t_split ? launch_dense<D_, D_, NB_, true>(n_chain, H, n_step, pair_id, n_pair, Tc, Sc, Srun, sa, st) \
-                       : launch_dense<D_, D_, NB_, false>(n_chain, H, n_step, pair_id, n_pair, Tc, Sc, Srun, sa, st);
+        return t_split ? launch_dense<D_, D_, NB_, true>(n_chain, H, n_step, pair_id, n_pair, Tc, Sc, Srun, st) \
+                       : launch_dense<D_, D_, NB_, false>(n_chain, H, n_step, pair_id, n_pair, Tc, Sc, Srun, st);
     HYPIC_CASE(16, 16)
     HYPIC_CASE(32, 32) HYPIC_CASE(32, 16)
     HYPIC_CASE(64, 64) HYPIC_CASE(64, 32) HYPIC_CASE(64, 16)

@@ -5,7 +5,7 @@
 
 namespace hypic {
 
-// Seam-window arguments of the chain kernel (hypic_seam_advance).
+// Seam-window arguments of the seam chain kernel (hypic_seam_advance).
 struct SeamArgs {
     const int64_t* seam_start;  // [n_chain][n_step], -1 = none
     int64_t n_tokens;
@@ -18,11 +18,10 @@ struct SeamArgs {
     float* out;                 // [n_chain][n_step][w][H][d_v]
 };
 
-// compose.hip (sa == nullptr: plain composition)
+// compose.hip
 // t_split: T as bf16 hi/lo planes [n_pair][H][2][d][d]; else fp32 [n_pair][H][d][d]
 hipError_t compose_dense(int d, int n_chain, int H, int n_step, const int32_t* pair_id, int n_pair,
-                         const void* Tc, bool t_split, const float* Sc, float* Srun, const SeamArgs* sa,
-                         hipStream_t st);
+                         const void* Tc, bool t_split, const float* Sc, float* Srun, hipStream_t st);
 hipError_t compose_scalar(int dk, int dv, int n_chain, int H, int n_step, const int32_t* pair_id,
                           int n_pair, const float* Tc, const float* Sc, float* Srun, hipStream_t st);
 
@@ -48,6 +47,11 @@ hipError_t seam_prep(int d, int n_chain, int n_step, int H, const int64_t* seam_
                      int w, const void* q, const void* k, const void* v, const void* g, const void* beta,
                      bool in_bf16, float scale, void* ws, hipStream_t st);
 size_t seam_record_bytes(int d);
+
+// seam_chain.hip (pair_id may be NULL: windows only)
+hipError_t seam_chain(int d, int n_chain, int H, int n_step, const int32_t* pair_id, int n_pair,
+                      const void* Tc, bool t_split, const float* Sc, float* Srun, const SeamArgs& sa,
+                      hipStream_t st);
 
 // selftest.hip
 hipError_t selftest_layouts(const float* in, float* out, hipStream_t st);

@@ -12,14 +12,14 @@
 //     Wt[t] = sum_s At[t][s] beta_s k_s                 (16 x d_k)
 //     U[t]  = sum_s e^{b_t-b_s} At[t][s] beta_s v_s     (16 x d_v)
 //     Mo[t][s] = scale e^{b_t-b_s} (q_t . k_s), s <= t  (16 x 16)
-// and the chain kernel then needs only (chunk form of the gated delta rule with
-// its in-chunk outputs):
+// and the chain kernel (seam_chain.hip) then needs only (chunk form of the gated
+// delta rule with its in-chunk outputs):
 //     U' = U - diag(e^b) (Wt R)
 //     O  = scale diag(e^b) (Q R) + Mo U'                 (window outputs)
 //     R <- e^{b_w} R + K^T diag(e^{b_w - b}) U'          (state after the window)
 // One workgroup (4 waves) per (chain, step, head) window.  The two 16 x 16 Gram
 // products K K^T and Q K^T run on MFMA (bf16 operands: exact for bf16 inputs, a
-// hi/lo split for fp32 inputs), the rest in fp32 on the vector ALUs.  Wt, q, K^T
+// hi/lo split for fp32 inputs), the rest in fp32 on the vector ALUs.  Wt, q, k
 // and Mo are written as bf16 hi/lo planes in MFMA fragment order (frag_off), so
 // the chain kernel fetches each operand fragment as one contiguous 1 KiB.
 #include "hypic_device.h"
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(256) void seam_prep_kernel(
     }
     __syncthreads();
 
-    // ---- Wt, U, q planes ([16][D], 8 channels per thread) and K^T planes ([D][16])
+    // ---- Wt, U, q and k planes ([16][D], 8 channels per thread)
     {
         constexpr int CG = D / 8;
         for (int it = tid; it < W * CG; it += 256) {
@@ -225,21 +225,14 @@ __global__ __launch_bounds__(256) void seam_prep_kernel(
                        reinterpret_cast<uint16_t*>(rp + R::kW + R::kPlaneWD + off), wk);
             put_split8(reinterpret_cast<uint16_t*>(rp + R::kQ + off),
                        reinterpret_cast<uint16_t*>(rp + R::kQ + R::kPlaneWD + off), qx);
+            put_split8(reinterpret_cast<uint16_t*>(rp + R::kK + off),
+                       reinterpret_cast<uint16_t*>(rp + R::kK + R::kPlaneWD + off), &Ks[t][c0]);
             float* up = reinterpret_cast<float*>(rp + R::kU);
 #pragma unroll
             for (int x = 0; x < 8; ++x) {   // block cb = ch / 16, lane (t / 4, ch % 16), element t % 4
                 const int ch = c0 + x;
                 up[((ch >> 4) * 64 + (t >> 2) * 16 + (ch & 15)) * 4 + (t & 3)] = uv[x];
             }
-        }
-        for (int it = tid; it < D * 2; it += 256) {
-            const int ch = it >> 1, t0 = (it & 1) * 8;
-            float kx[8];
-#pragma unroll
-            for (int x = 0; x < 8; ++x) kx[x] = Ks[t0 + x][ch];
-            const int off = frag_off(ch, t0, W) * 2;
-            put_split8(reinterpret_cast<uint16_t*>(rp + R::kK + off),
-                       reinterpret_cast<uint16_t*>(rp + R::kK + R::kPlaneWD + off), kx);
         }
     }
 }

@@ -3,7 +3,7 @@
 // Every matrix the chain kernel feeds to the MFMA units is stored as two bf16
 // planes, hi = bf16(x) and lo = bf16(x - hi), in fragment order (frag_off in
 // hypic_device.h): one contiguous 16-byte load per lane is one operand fragment,
-// and the chain kernel does no conversions.
+// and the chain kernel (seam_chain.hip) does no conversions.
 #pragma once
 
 namespace hypic {
@@ -15,7 +15,7 @@ struct SeamRec {
     static constexpr int kPlaneWD = kSeamMaxW * D * 2;          // bytes of one [16][D] bf16 plane
     static constexpr int kW = 0;                                // [2][16][D] bf16  Wt = At diag(beta) K
     static constexpr int kQ = kW + 2 * kPlaneWD;                // [2][16][D] bf16  q (unscaled)
-    static constexpr int kK = kQ + 2 * kPlaneWD;                // [2][D][16] bf16  K^T (channel-major)
+    static constexpr int kK = kQ + 2 * kPlaneWD;                // [2][16][D] bf16  k (token-major)
     static constexpr int kM = kK + 2 * kPlaneWD;                // [2][16][16] bf16 output mixing matrix Mo
     static constexpr int kPlaneM = kSeamMaxW * kSeamMaxW * 2;
     // Dword data in the D-fragment lane order of a 16 x 16 tile (lane l = 16 g + n holds
