@@ -51,11 +51,12 @@ struct alignas(16) GdnSmem {
     uint16_t Kt[NSPLIT][D * CH];   // K^T, rows = channels, cols = tokens
     uint16_t Vt[NSPLIT][D * CH];   // V^T, rows = channels, cols = tokens
     uint16_t Wt[NSPLIT][CH * KP];  // Wt, rows = tokens, cols = channels (>= D zero)
-    // block forward substitution operands (fp16 hi/lo planes):
-    uint16_t Ln[2][CH * CH];       // -Lt off the 16 x 16 diagonal blocks (rows t, cols s; zero elsewhere)
-    uint16_t Lnd[2][CH * CH];      // the same with the decay: -e^{b_t - b_s} Lt
-    uint16_t Dv[2][4][512];        // A fragments of (I + Lt_ii)^-1, diagonal block i (cols 16..31 zero)
-    uint16_t Dvd[2][4][512];       // the same with the decay e^{b_t - b_s}
+    // block forward substitution operands: A fragments of v_mfma_f32_16x16x16_f16 (lane
+    // 16 g + r holds row r, columns 4 g .. 4 g + 3), fp16 hi / lo planes
+    uint16_t Ln[2][6][256];        // -Lt_ij for the blocks j < i (index i (i - 1) / 2 + j)
+    uint16_t Lnd[2][6][256];       // the same with the decay: -e^{b_t - b_s} Lt
+    uint16_t Dv[2][4][256];        // (I + Lt_ii)^-1, diagonal block i
+    uint16_t Dvd[2][4][256];       // the same with the decay e^{b_t - b_s}
     float Sd[4][16][20];           // per diagonal block: Lt_ii, then its inverse (fp32)
     float gate[CH], beta[CH], b[CH], eb[CH], ebr[CH];   // b in log2 units
     float bC;
@@ -151,11 +152,6 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
     beg = beg < 0 ? 0 : (beg > n_tokens ? n_tokens : beg);
     end = end < beg ? beg : (end > n_tokens ? n_tokens : end);
 
-    // the diagonal and upper blocks of the substitution matrices are never written: zero once
-    for (int i = tid; i < 2 * CH * CH; i += 512) {
-        (&sm.Ln[0][0])[i] = 0;
-        (&sm.Lnd[0][0])[i] = 0;
-    }
     // zero the channel padding of Kr / Wt once (D < 32 only)
     if (KP > D) {
         for (int i = tid; i < NSPLIT * CH * KP; i += 512) {
@@ -348,43 +344,45 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
 #pragma unroll
                 for (int r = 0; r < 16; ++r) sm.Sd[i][r][lane] = x[r];
             }
-            // A fragment: lane (n, g) holds row n, columns 8g .. 8g+7 (zero for g >= 2)
+            // A fragment: lane (g, n) holds row n, columns 4g .. 4g+3
             const float bt = __shfl(b2, 16 * i + n16, 64);
-            uint16_t dh[8], dl[8], ddh[8], ddl[8];
+            f32x4 dv, dd;
 #pragma unroll
-            for (int x = 0; x < 8; ++x) {
-                const int col = 8 * (g4 & 1) + x;
+            for (int x = 0; x < 4; ++x) {
+                const int col = 4 * g4 + x;
                 const float bs = __shfl(b2, 16 * i + col, 64);
-                const float dv = g4 < 2 ? sm.Sd[i][n16][col] : 0.f;
-                const float dd = col <= n16 ? dv * __builtin_amdgcn_exp2f(bt - bs) : 0.f;
-                to16<2>(dv, dh[x], dl[x]);
-                to16<2>(dd, ddh[x], ddl[x]);
+                dv[x] = sm.Sd[i][n16][col];
+                dd[x] = col <= n16 ? dv[x] * __builtin_amdgcn_exp2f(bt - bs) : 0.f;
             }
-            *reinterpret_cast<u32x4*>(&sm.Dv[0][i][lane * 8]) = pack8(dh);
-            *reinterpret_cast<u32x4*>(&sm.Dv[1][i][lane * 8]) = pack8(dl);
-            *reinterpret_cast<u32x4*>(&sm.Dvd[0][i][lane * 8]) = pack8(ddh);
-            *reinterpret_cast<u32x4*>(&sm.Dvd[1][i][lane * 8]) = pack8(ddl);
+            unsigned h0, h1, l0, l1;
+            pack_f16_split(dv, h0, h1, l0, l1);
+            *reinterpret_cast<u32x2*>(&sm.Dv[0][i][lane * 4]) = u32x2{h0, h1};
+            *reinterpret_cast<u32x2*>(&sm.Dv[1][i][lane * 4]) = u32x2{l0, l1};
+            pack_f16_split(dd, h0, h1, l0, l1);
+            *reinterpret_cast<u32x2*>(&sm.Dvd[0][i][lane * 4]) = u32x2{h0, h1};
+            *reinterpret_cast<u32x2*>(&sm.Dvd[1][i][lane * 4]) = u32x2{l0, l1};
         } else {
             // off-diagonal blocks (1,0) (2,0) (2,1) (3,0) (3,1) (3,2), two waves taking two
             for (int k = wave - 4; k < 6; k += 4) {
                 const int ti = k < 1 ? 1 : k < 3 ? 2 : 3;
                 const int tj = k - (ti * (ti - 1)) / 2;
                 const f32x4 gacc = gram(ti, tj);
-                const int s_ = 16 * tj + n16;
-                const float bs = __shfl(b2, s_, 64);
+                const float bs = __shfl(b2, 16 * tj + n16, 64);
+                // D layout (row 4g + e, column n) -> A fragment lane 16 (n / 4) + 4g + e, entry n % 4
+                uint16_t* const P = &sm.Ln[0][k][(16 * (n16 >> 2) + 4 * g4) * 4 + (n16 & 3)];
+                uint16_t* const Pd = &sm.Lnd[0][k][(16 * (n16 >> 2) + 4 * g4) * 4 + (n16 & 3)];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int t = 16 * ti + 4 * g4 + e;
                     const float l = -sm.beta[t] * gacc[e];
                     const float ld = l * __builtin_amdgcn_exp2f(__shfl(b2, t, 64) - bs);
-                    const int off = lds_off(t, s_, CH);
                     uint16_t h, lo;
                     to16<2>(l, h, lo);
-                    sm.Ln[0][off] = h;
-                    sm.Ln[1][off] = lo;
+                    P[4 * e] = h;
+                    P[6 * 256 + 4 * e] = lo;
                     to16<2>(ld, h, lo);
-                    sm.Lnd[0][off] = h;
-                    sm.Lnd[1][off] = lo;
+                    Pd[4 * e] = h;
+                    Pd[6 * 256 + 4 * e] = lo;
                 }
             }
         }
@@ -393,13 +391,21 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
         // ---- 3. block forward substitution, one chain per owned column tile (no barriers):
         //   Wt_i = (I + Lt_ii)^-1 (diag(beta) K_i - sum_{j<i} Lt_ij Wt_j)       (H tiles: channel tile)
         //   U_i  = the same with the decayed blocks and diag(beta) V_i           (S tiles: value tile)
-        // on fp16 hi/lo operands (three products).  Wt goes to LDS for every wave's Y = Wt X;
-        // U stays in this wave's registers for its S tile.
+        // on v_mfma_f32_16x16x16_f16 with fp16 hi/lo operands (three products): its B operand
+        // has the accumulator's lane layout, so a solved block feeds the next products as
+        // packed, without cross-lane moves.  Wt goes to LDS for every wave's Y = Wt X; U stays
+        // in this wave's registers for its S tile.
         f32x4 U[4][CTW];
         {
+            auto mma16 = [](const u32x2& ah, const u32x2& al, const u32x2& bh, const u32x2& bl, f32x4 c) {
+                c = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, ah), __builtin_bit_cast(f16x4, bh), c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, ah), __builtin_bit_cast(f16x4, bl), c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, al), __builtin_bit_cast(f16x4, bh), c, 0, 0, 0);
+                return c;
+            };
             // the chains of this wave's tiles advance block by block together, so the
             // latency of one chain's step overlaps the other's
-            Frag<2> prev[2][CTW];                              // solved blocks as B fragments (k = tokens)
+            u32x2 xh[3][CTW], xl[3][CTW];   // solved blocks 0..2 as packed B operands (hi / lo)
             f32x4 sol[4][CTW];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -414,34 +420,36 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                     {
                         const int off = lds_off(16 * q + n16, 16 * i + 4 * g4, CH);
                         const u32x2 hw = *reinterpret_cast<const u32x2*>(&rhs_src[0][off]);
-                        u32x2 lw = u32x2{0u, 0u};
-                        if constexpr (NSPLIT == 2) lw = *reinterpret_cast<const u32x2*>(&rhs_src[1][off]);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const unsigned hb = (hw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                            const unsigned lb = (lw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                            const float v = (float)__builtin_bit_cast(_Float16, (uint16_t)hb) +
-                                            (float)__builtin_bit_cast(_Float16, (uint16_t)lb);
-                            acc[e] = sm.beta[16 * i + 4 * g4 + e] * v;
+                        f32x2 v0 = f16x2_to_f32(hw[0]), v1 = f16x2_to_f32(hw[1]);
+                        if constexpr (NSPLIT == 2) {
+                            const u32x2 lw = *reinterpret_cast<const u32x2*>(&rhs_src[1][off]);
+                            v0 += f16x2_to_f32(lw[0]);
+                            v1 += f16x2_to_f32(lw[1]);
                         }
+                        const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[16 * i + 4 * g4]);
+                        acc = f32x4{bt[0] * v0.x, bt[1] * v0.y, bt[2] * v1.x, bt[3] * v1.y};
                     }
-                    // - sum_{j<i} Lt_ij X_j over the 32-token k-blocks that hold solved blocks
+                    // - sum_{j<i} Lt_ij X_j
 #pragma unroll
-                    for (int ks = 0; ks < 2; ++ks) {
-                        if (32 * ks >= 16 * i) break;
-                        Frag<2> a;
-                        a.h = lds_frag<CH>(is_s ? sm.Lnd[0] : sm.Ln[0], i, ks, lx);
-                        a.l = lds_frag<CH>(is_s ? sm.Lnd[1] : sm.Ln[1], i, ks, lx);
-                        acc = mma<2>(a, prev[ks][c], acc);
+                    for (int j = 0; j < i; ++j) {
+                        const int kb = i * (i - 1) / 2 + j;
+                        const uint16_t(*L)[6][256] = is_s ? sm.Lnd : sm.Ln;
+                        const u32x2 ah = *reinterpret_cast<const u32x2*>(&L[0][kb][lane * 4]);
+                        const u32x2 al = *reinterpret_cast<const u32x2*>(&L[1][kb][lane * 4]);
+                        acc = mma16(ah, al, xh[j][c], xl[j][c], acc);
                     }
                     // X_i = (I + Lt_ii)^-1 acc
-                    Frag<2> dinv;
-                    dinv.h = *reinterpret_cast<const f16x8*>(&(is_s ? sm.Dvd[0] : sm.Dv[0])[i][lane * 8]);
-                    dinv.l = *reinterpret_cast<const f16x8*>(&(is_s ? sm.Dvd[1] : sm.Dv[1])[i][lane * 8]);
-                    sol[i][c] = mma<2>(dinv, dpair_to_frag<2>(acc, zero4()), zero4());
-                    if (i == 0) prev[0][c] = dpair_to_frag<2>(sol[0][c], zero4());
-                    if (i == 1) prev[0][c] = dpair_to_frag<2>(sol[0][c], sol[1][c]);
-                    if (i == 2) prev[1][c] = dpair_to_frag<2>(sol[2][c], zero4());
+                    const uint16_t(*Dm)[4][256] = is_s ? sm.Dvd : sm.Dv;
+                    const u32x2 dh = *reinterpret_cast<const u32x2*>(&Dm[0][i][lane * 4]);
+                    const u32x2 dl = *reinterpret_cast<const u32x2*>(&Dm[1][i][lane * 4]);
+                    unsigned b0, b1, b2, b3;
+                    pack_f16_split(acc, b0, b1, b2, b3);
+                    sol[i][c] = mma16(dh, dl, u32x2{b0, b1}, u32x2{b2, b3}, zero4());
+                    if (i < 3) {
+                        pack_f16_split(sol[i][c], b0, b1, b2, b3);
+                        xh[i][c] = u32x2{b0, b1};
+                        xl[i][c] = u32x2{b2, b3};
+                    }
                 }
             }
 #pragma unroll

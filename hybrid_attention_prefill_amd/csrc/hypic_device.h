@@ -5,6 +5,9 @@
 //     A: lane l holds A[l%16][8*(l/16) + j], j = 0..7
 //     B: lane l holds B[8*(l/16) + j][l%16], j = 0..7
 //     D: lane l holds D[4*(l/16) + i][l%16], i = 0..3
+//   v_mfma_f32_16x16x16_f16 : D(16x16,f32) += A(16x16) B(16x16)
+//     A: lane l holds A[l%16][4*(l/16) + j], j = 0..3
+//     B: lane l holds B[4*(l/16) + j][l%16]  (the D layout: a D tile packed to fp16 is a B operand)
 //   v_mfma_f32_16x16x4_f32 : D(16x16) += A(16x4) B(4x16)
 //     A: lane l holds A[l%16][l/16];  B: lane l holds B[l/16][l%16]
 // These lane layouts are checked on the device by the test-suite.
@@ -15,6 +18,7 @@
 namespace hypic {
 
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
@@ -75,30 +79,44 @@ __device__ __forceinline__ u32x4 dtiles_to_bfrag(unsigned p0, unsigned p1, unsig
 template <typename T8>
 __device__ __forceinline__ T8 as_frag(const u32x4& u) { return __builtin_bit_cast(T8, u); }
 
-// Pack the 4 floats of a D tile lane into two 16-bit pairs of the operand type.
+// Pack the 4 floats of a D tile lane into two 16-bit pairs of the operand type.  The
+// pairs are converted together (round to nearest even, one v_cvt_pk_f16_f32 or
+// v_cvt_pk_bf16_f32 per pair on gfx950); _split also returns the rounded remainders
+// lo = x - hi (exact in fp32), rounded the same way.
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+__device__ __forceinline__ unsigned cvt2_f16(float a, float b) {
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, f16x2));
+}
+__device__ __forceinline__ unsigned cvt2_bf16(float a, float b) {
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+__device__ __forceinline__ f32x2 f16x2_to_f32(unsigned w) {
+    return __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
+}
+__device__ __forceinline__ f32x2 bf16x2_to_f32(unsigned w) {
+    return f32x2{__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u)};
+}
 __device__ __forceinline__ void pack_f16(const f32x4& d, unsigned& w0, unsigned& w1) {
-    w0 = pack2(f16_bits((_Float16)d[0]), f16_bits((_Float16)d[1]));
-    w1 = pack2(f16_bits((_Float16)d[2]), f16_bits((_Float16)d[3]));
+    w0 = cvt2_f16(d[0], d[1]);
+    w1 = cvt2_f16(d[2], d[3]);
 }
 __device__ __forceinline__ void pack_f16_split(const f32x4& d, unsigned& h0, unsigned& h1,
                                                unsigned& l0, unsigned& l1) {
-    _Float16 h[4], l[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) split_f16(d[i], h[i], l[i]);
-    h0 = pack2(f16_bits(h[0]), f16_bits(h[1]));
-    h1 = pack2(f16_bits(h[2]), f16_bits(h[3]));
-    l0 = pack2(f16_bits(l[0]), f16_bits(l[1]));
-    l1 = pack2(f16_bits(l[2]), f16_bits(l[3]));
+    h0 = cvt2_f16(d[0], d[1]);
+    h1 = cvt2_f16(d[2], d[3]);
+    const f32x2 b0 = f16x2_to_f32(h0), b1 = f16x2_to_f32(h1);
+    l0 = cvt2_f16(d[0] - b0.x, d[1] - b0.y);
+    l1 = cvt2_f16(d[2] - b1.x, d[3] - b1.y);
 }
 __device__ __forceinline__ void pack_bf16_split(const f32x4& d, unsigned& h0, unsigned& h1,
                                                 unsigned& l0, unsigned& l1) {
-    __bf16 h[4], l[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) split_bf16(d[i], h[i], l[i]);
-    h0 = pack2(bf16_bits(h[0]), bf16_bits(h[1]));
-    h1 = pack2(bf16_bits(h[2]), bf16_bits(h[3]));
-    l0 = pack2(bf16_bits(l[0]), bf16_bits(l[1]));
-    l1 = pack2(bf16_bits(l[2]), bf16_bits(l[3]));
+    h0 = cvt2_bf16(d[0], d[1]);
+    h1 = cvt2_bf16(d[2], d[3]);
+    const f32x2 b0 = bf16x2_to_f32(h0), b1 = bf16x2_to_f32(h1);
+    l0 = cvt2_bf16(d[0] - b0.x, d[1] - b0.y);
+    l1 = cvt2_bf16(d[2] - b1.x, d[3] - b1.y);
 }
 
 // ---- fragment-ordered bf16 planes ---------------------------------------------
