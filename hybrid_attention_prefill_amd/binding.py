@@ -221,10 +221,10 @@ def seam_advance(q, k, v, g, beta, seam_start, S_run, out, *, gate, delta, w, sc
 
 
 def selftest_layouts(device="cuda"):
-    """Run the lane-layout self-test kernel on in = [0, 1, ..., 255]; returns its 1600 raw floats (host)."""
+    """Run the lane-layout self-test kernel on in = [0, 1, ..., 255]; returns its 2112 raw floats (host)."""
     lib = load_library()
     inp = torch.arange(256, device=device, dtype=torch.float32)
-    out = torch.full((1600,), float("nan"), device=device, dtype=torch.float32)
+    out = torch.full((2112,), float("nan"), device=device, dtype=torch.float32)
     _check(lib.hypic_selftest_layouts(_ptr(inp), _ptr(out), _stream(None)))
     torch.cuda.synchronize()
     return out.cpu().numpy()

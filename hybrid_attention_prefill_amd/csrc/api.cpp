@@ -172,7 +172,7 @@ hypic_status hypic_seam_advance(const hypic_dims* dims, int32_t n_chain, int32_t
 }
 
 // Diagnostic: runs the lane-layout self-test kernel into a device buffer of
-// 1600 floats from 256 input floats (see selftest.hip).  Not part of the method.
+// 2112 floats from 256 input floats (see selftest.hip).  Not part of the method.
 hypic_status hypic_selftest_layouts(const float* in, float* out, void* stream)
 {
     if (!in || !out) return fail(HYPIC_E_INVALID, "in or out is NULL");

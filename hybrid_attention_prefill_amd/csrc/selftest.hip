@@ -7,7 +7,7 @@
 
 namespace hypic {
 
-// out layout (floats), 1280 entries:
+// out layout (floats), 2112 entries:
 //   [0,256)    D (16x16, row-major) of mfma_f32_16x16x32_f16
 //   [256,512)  D of mfma_f32_16x16x32_bf16
 //   [512,768)  D of mfma_f32_16x16x4f32
@@ -15,6 +15,9 @@ namespace hypic {
 //   [1280,1536) 16-byte global->LDS loads: lane l fetches in[4 g .. 4 g + 3] with
 //              g = (7 l) % 64 and reads back LDS bytes [16 l, 16 l + 16)
 //   [1536,1600) 4-byte global->LDS loads: lane l fetches in[(5 l) % 256], reads back [4 l, 4 l + 4)
+//   [1600,1856) D of mfma_f32_16x16x16_f16 (A and B the first 16 columns / rows of the above)
+//   [1856,2112) D of mfma_f32_16x16x16_f16 with the shuffle's tile0 packed as is as the B
+//               operand (the accumulator layout is that operand's layout)
 // Operands are filled assuming the documented lane layouts with small integer
 // matrices (exact in every type); the host recomputes D = A B and the expected
 // shuffle result and compares.
@@ -59,6 +62,19 @@ __global__ void selftest_layout_kernel(const float* in, float* out)
     // global -> LDS direct loads (each lane's destination is implied by its lane id)
     __builtin_amdgcn_global_load_lds(in + ((7 * l) % 64) * 4, (__attribute__((address_space(3))) void*)lds16, 16, 0, 0);
     __builtin_amdgcn_global_load_lds(in + (5 * l) % 256, (__attribute__((address_space(3))) void*)lds4, 4, 0, 0);
+    // 16x16x16 f16: A lane l holds A[l%16][4(l/16) + j], B lane l holds B[4(l/16) + j][l%16]
+    {
+        f16x4 a4, b4;
+        for (int j = 0; j < 4; ++j) {
+            const int k = 4 * g4 + j;
+            a4[j] = (_Float16)(float)((n16 * 3 + k) % 7 - 3);
+            b4[j] = (_Float16)(float)((k * 5 + n16 * 2) % 5 - 2);
+        }
+        d = __builtin_amdgcn_mfma_f32_16x16x16f16(a4, b4, zero4(), 0, 0, 0);
+        for (int i = 0; i < 4; ++i) out[1600 + (4 * g4 + i) * 16 + n16] = d[i];
+        d = __builtin_amdgcn_mfma_f32_16x16x16f16(a4, __builtin_bit_cast(f16x4, u32x2{p0, p1}), zero4(), 0, 0, 0);
+        for (int i = 0; i < 4; ++i) out[1856 + (4 * g4 + i) * 16 + n16] = d[i];
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     for (int j = 0; j < 4; ++j) out[1280 + l * 4 + j] = lds16[l * 4 + j];

@@ -178,7 +178,7 @@ int32_t hypic_abi_version(void);
  * Diagnostic, not part of the method: runs one wave that exercises the MFMA
  * lane layouts, the accumulator-to-operand lane shuffle and the global-to-LDS
  * direct loads the kernels rely on.  Reads 256 floats from the device buffer
- * `in`, writes 1600 floats to the device buffer `out` (layout documented in
+ * `in`, writes 2112 floats to the device buffer `out` (layout documented in
  * the library source).  The test-suite recomputes the expected values.
  */
 hypic_status hypic_selftest_layouts(const float* in, float* out, void* stream);

@@ -33,3 +33,7 @@ def test_mfma_layouts_and_shuffle():
     g = (7 * lane) % 64
     np.testing.assert_array_equal(out[1280:1536].reshape(64, 4), (4 * g)[:, None] + np.arange(4)[None, :])
     np.testing.assert_array_equal(out[1536:1600], (5 * lane) % 256)
+    # v_mfma_f32_16x16x16_f16, and a packed accumulator tile used directly as its B operand
+    np.testing.assert_array_equal(out[1600:1856].reshape(16, 16), A[:, :16] @ B[:16, :])
+    tile0 = np.arange(16)[:, None] * 16 + np.arange(16)[None, :]
+    np.testing.assert_array_equal(out[1856:2112].reshape(16, 16), A[:, :16] @ tile0)
