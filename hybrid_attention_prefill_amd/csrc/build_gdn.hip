@@ -234,14 +234,19 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
         const int tb = opaque(tb0), cb = opaque(cb0);
         // ---- 1. stage the chunk: K token-major, K^T and V^T channel-major (16-bit), gates
         if (has_blk) {
-            // masked values of the 4 x 8 block; rows past the segment are zero
+            // the 4 x 8 block; rows past the segment are zeroed (only the last chunk has any)
+            if (n < CH) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (tb * 4 + r >= n)
+#pragma unroll
+                        for (int x = 0; x < WPR; ++x) raw[r][x] = u32x4{0u, 0u, 0u, 0u};
+            }
             float f[4][8];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const bool live = tb * 4 + r < n;
+            for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int c = 0; c < 8; ++c) f[r][c] = live ? raw_val(r, c) : 0.f;
-            }
+                for (int c = 0; c < 8; ++c) f[r][c] = raw_val(r, c);
             uint16_t(*dst)[D * CH] = blk_v ? sm.Vt : sm.Kt;
             if constexpr (NSPLIT == 1 && BF16) {
                 // bf16 values are exact in fp16 (inside its range): round-toward-zero packing is exact

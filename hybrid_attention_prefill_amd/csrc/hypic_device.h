@@ -102,13 +102,24 @@ __device__ __forceinline__ void pack_f16(const f32x4& d, unsigned& w0, unsigned&
     w0 = cvt2_f16(d[0], d[1]);
     w1 = cvt2_f16(d[2], d[3]);
 }
+// x - (low / high fp16 half of w), exact (x - hi of x's fp16 rounding is representable in
+// fp32), in one v_fma_mix_f32 that reads the fp16 operand in place
+__device__ __forceinline__ float sub_f16_lo(unsigned w, float x) {
+    float r;
+    asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(x));
+    return r;
+}
+__device__ __forceinline__ float sub_f16_hi(unsigned w, float x) {
+    float r;
+    asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(x));
+    return r;
+}
 __device__ __forceinline__ void pack_f16_split(const f32x4& d, unsigned& h0, unsigned& h1,
                                                unsigned& l0, unsigned& l1) {
     h0 = cvt2_f16(d[0], d[1]);
     h1 = cvt2_f16(d[2], d[3]);
-    const f32x2 b0 = f16x2_to_f32(h0), b1 = f16x2_to_f32(h1);
-    l0 = cvt2_f16(d[0] - b0.x, d[1] - b0.y);
-    l1 = cvt2_f16(d[2] - b1.x, d[3] - b1.y);
+    l0 = cvt2_f16(sub_f16_lo(h0, d[0]), sub_f16_hi(h0, d[1]));
+    l1 = cvt2_f16(sub_f16_lo(h1, d[2]), sub_f16_hi(h1, d[3]));
 }
 __device__ __forceinline__ void pack_bf16_split(const f32x4& d, unsigned& h0, unsigned& h1,
                                                 unsigned& l0, unsigned& l1) {
