@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libhypic.so")
 HYPIC_OK, HYPIC_E_INVALID, HYPIC_E_UNSUPPORTED, HYPIC_E_DEVICE = 0, 1, 2, 3
 GATE_HEAD, GATE_TOKEN, GATE_DIAG = 0, 1, 2
 F32, BF16 = 0, 1
-T_DENSE, T_SCALAR, T_SPLIT = 0, 1, 2
+T_DENSE, T_SCALAR, T_SPLIT, T_DIAG = 0, 1, 2, 3
 
 EXPORTED = ("hypic_segment_build", "hypic_compose", "hypic_seam_advance", "hypic_seam_workspace_bytes",
             "hypic_last_error", "hypic_abi_version", "hypic_selftest_layouts")
@@ -102,7 +102,7 @@ def _in_dtype(t):
 
 
 def _t_shape(t_layout, n, H, dk):
-    return {T_DENSE: (n, H, dk, dk), T_SCALAR: (n, H), T_SPLIT: (n, H, 2, dk * dk)}[t_layout]
+    return {T_DENSE: (n, H, dk, dk), T_SCALAR: (n, H), T_SPLIT: (n, H, 2, dk * dk), T_DIAG: (n, H, dk)}[t_layout]
 
 
 def _t_dtype(t_layout):
@@ -110,11 +110,14 @@ def _t_dtype(t_layout):
 
 
 def t_layout_of(T):
-    """Layout of a T cache tensor: bf16 [n,H,2,d*d] SPLIT, fp32 [n,H] SCALAR, fp32 [n,H,d,d] DENSE."""
+    """Layout of a T cache tensor: bf16 [n,H,2,d*d] SPLIT, fp32 [n,H] SCALAR, fp32 [n,H,d] DIAG,
+    fp32 [n,H,d,d] DENSE."""
     if T.dtype == torch.bfloat16 and T.dim() == 4:
         return T_SPLIT
     if T.dtype == torch.float32 and T.dim() == 2:
         return T_SCALAR
+    if T.dtype == torch.float32 and T.dim() == 3:
+        return T_DIAG
     if T.dtype == torch.float32 and T.dim() == 4:
         return T_DENSE
     raise ValueError(f"T cache of dtype {T.dtype} and shape {tuple(T.shape)} matches no T layout")
@@ -174,8 +177,8 @@ def compose(T_cache, S_cache, pair_id, S_run, *, t_layout=None, stream=None):
     _dev(pair_id, "pair_id", torch.int32)
     n_chain, n_step = pair_id.shape
     _dev(S_run, "S_run", torch.float32, (n_chain, H, dk, dv))
-    d = make_dims(H, dk, dv, gate=GATE_HEAD if t_layout == T_SCALAR else GATE_TOKEN, delta=0,
-                  in_dtype=F32, t_layout=t_layout)
+    gate = {T_SCALAR: GATE_HEAD, T_DIAG: GATE_DIAG}.get(t_layout, GATE_TOKEN)
+    d = make_dims(H, dk, dv, gate=gate, delta=0, in_dtype=F32, t_layout=t_layout)
     _check(lib.hypic_compose(ctypes.byref(d), n_chain, n_step, _ptr(pair_id), n_pair, _ptr(T_cache),
                              _ptr(S_cache), _ptr(S_run), _stream(stream)))
     return S_run
@@ -206,7 +209,7 @@ def seam_advance(q, k, v, g, beta, seam_start, S_run, out, *, gate, delta, w, sc
         _dev(S_cache, "S_cache", torch.float32)
         n_pair = S_cache.shape[0]
         t_layout = t_layout_of(T_cache)
-        if t_layout == T_SCALAR:
+        if t_layout in (T_SCALAR, T_DIAG):
             raise ValueError("seam_advance needs a dense T cache (DENSE or SPLIT layout)")
         _dev(T_cache, "T_cache", _t_dtype(t_layout), _t_shape(t_layout, n_pair, H, dk))
     need = seam_workspace_bytes(H, dk, dv, n_chain, n_step, w, gate=gate, delta=delta, in_dtype=dt)

@@ -50,10 +50,13 @@ hypic_status check_dims(const hypic_dims* d)
     if (d->delta != 0 && d->delta != 1) return fail(HYPIC_E_INVALID, "delta must be 0 or 1 (got %d)", d->delta);
     if (d->in_dtype != HYPIC_F32 && d->in_dtype != HYPIC_BF16)
         return fail(HYPIC_E_INVALID, "in_dtype must be 0 (f32) or 1 (bf16) (got %d)", d->in_dtype);
-    if (d->t_layout != HYPIC_T_DENSE && d->t_layout != HYPIC_T_SCALAR && d->t_layout != HYPIC_T_SPLIT)
-        return fail(HYPIC_E_INVALID, "t_layout must be 0 (dense), 1 (scalar) or 2 (split) (got %d)", d->t_layout);
+    if (d->t_layout < HYPIC_T_DENSE || d->t_layout > HYPIC_T_DIAG)
+        return fail(HYPIC_E_INVALID, "t_layout must be 0 (dense), 1 (scalar), 2 (split) or 3 (diag) (got %d)",
+                    d->t_layout);
     if (d->t_layout == HYPIC_T_SCALAR && (d->delta || d->gate == HYPIC_GATE_DIAG))
         return fail(HYPIC_E_INVALID, "a scalar T exists only for scalar gates without the delta rule");
+    if (d->t_layout == HYPIC_T_DIAG && (d->delta || d->gate != HYPIC_GATE_DIAG))
+        return fail(HYPIC_E_INVALID, "a diagonal T exists only for the diagonal gate without the delta rule");
     return ok();
 }
 
@@ -83,10 +86,9 @@ hypic_status hypic_segment_build(const hypic_dims* dims, int32_t n_seg, const in
     if (dims->d_k != dims->d_v) return fail(HYPIC_E_UNSUPPORTED, "d_k != d_v is not implemented");
     const bool bf16 = dims->in_dtype == HYPIC_BF16;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    if (!dims->delta && dims->gate != HYPIC_GATE_DIAG) {
-        return from_hip(hypic::build_decay(dims->d_k, bf16, dims->gate == HYPIC_GATE_HEAD, n_seg,
-                                           dims->n_heads, seg_begin, seg_end, n_tokens, k, v, g, T_out,
-                                           dims->t_layout, S_out, st),
+    if (!dims->delta) {
+        return from_hip(hypic::build_decay(dims->d_k, bf16, dims->gate, n_seg, dims->n_heads, seg_begin, seg_end,
+                                           n_tokens, k, v, g, T_out, dims->t_layout, S_out, st),
                         "hypic_segment_build");
     }
     if (dims->delta && dims->gate == HYPIC_GATE_TOKEN) {
@@ -114,11 +116,14 @@ hypic_status hypic_compose(const hypic_dims* dims, int32_t n_chain, int32_t n_st
     if (n_chain == 0 || n_step == 0) return ok();
     if (!pair_id || !S_run) return fail(HYPIC_E_INVALID, "pair_id or S_run is NULL");
     if (n_pair > 0 && (!T_cache || !S_cache)) return fail(HYPIC_E_INVALID, "T_cache or S_cache is NULL");
-    if ((long long)n_chain * dims->n_heads * 8 > kMaxGrid) return fail(HYPIC_E_INVALID, "too many chains");
+    if ((long long)n_chain * dims->n_heads * 8 > kMaxGrid ||
+        (long long)n_chain * dims->n_heads * (dims->d_k * dims->d_v / 4) / 256 > kMaxGrid)
+        return fail(HYPIC_E_INVALID, "too many chains");
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    if (dims->t_layout == HYPIC_T_SCALAR)
-        return from_hip(hypic::compose_scalar(dims->d_k, dims->d_v, n_chain, dims->n_heads, n_step, pair_id,
-                                              n_pair, static_cast<const float*>(T_cache), S_cache, S_run, st),
+    if (dims->t_layout == HYPIC_T_SCALAR || dims->t_layout == HYPIC_T_DIAG)
+        return from_hip(hypic::compose_scalar(dims->d_k, dims->d_v, dims->t_layout == HYPIC_T_DIAG, n_chain,
+                                              dims->n_heads, n_step, pair_id, n_pair,
+                                              static_cast<const float*>(T_cache), S_cache, S_run, st),
                         "hypic_compose");
     if (dims->d_k != dims->d_v) return fail(HYPIC_E_UNSUPPORTED, "d_k != d_v is not implemented");
     return from_hip(hypic::compose_dense(dims->d_k, n_chain, dims->n_heads, n_step, pair_id, n_pair, T_cache,
@@ -150,7 +155,7 @@ hypic_status hypic_seam_advance(const hypic_dims* dims, int32_t n_chain, int32_t
     if (pair_id && n_pair > 0 && (!T_cache || !S_cache)) return fail(HYPIC_E_INVALID, "T_cache or S_cache is NULL");
     if (dims->gate != HYPIC_GATE_TOKEN || !dims->delta)
         return fail(HYPIC_E_UNSUPPORTED, "hypic_seam_advance: only the scalar-gated delta rule is implemented");
-    if (dims->t_layout == HYPIC_T_SCALAR)
+    if (dims->t_layout == HYPIC_T_SCALAR || dims->t_layout == HYPIC_T_DIAG)
         return fail(HYPIC_E_UNSUPPORTED, "hypic_seam_advance needs a dense T (layout DENSE or SPLIT)");
     if (dims->d_k != dims->d_v) return fail(HYPIC_E_UNSUPPORTED, "d_k != d_v is not implemented");
     if ((long long)n_chain * n_step * dims->n_heads > kMaxGrid || (long long)n_chain * dims->n_heads * 8 > kMaxGrid)

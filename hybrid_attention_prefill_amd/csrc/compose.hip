@@ -270,27 +270,31 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void compose_dense_kernel(
     }
 }
 
-// Scalar T (constant-decay families cache T_C = gamma^L I as one number):
-// S_run <- t S_run + S, elementwise; 4 consecutive state entries per thread.
+// Scalar or diagonal T (gates without the delta rule cache T_C = t I as one number per
+// (pair, head), or T_C = diag(t) for the per-channel gate): S_run <- T S_run + S is
+// elementwise, S_run[r][c] <- t_r S_run[r][c] + S[r][c]; 4 consecutive state entries
+// (one row) per thread.
+template <bool DIAG>
 __global__ __launch_bounds__(256) void compose_scalar_kernel(
-    int n_chain, int H, int DKV, int n_step, const int32_t* __restrict__ pair_id, int n_pair,
+    int n_chain, int H, int DK, int DV, int n_step, const int32_t* __restrict__ pair_id, int n_pair,
     const float* __restrict__ Tc, const float* __restrict__ Sc, float* __restrict__ Srun)
 {
-    const int per_unit = DKV / 4;  // float4 groups per (chain, head)
+    const int per_unit = DK * DV / 4;  // float4 groups per (chain, head)
     const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     const long long total = (long long)n_chain * H * per_unit;
     if (gid >= total) return;
     const int q = (int)(gid % per_unit);
+    const int row = 4 * q / DV;
     const long long unit = gid / per_unit;
     const int c = (int)(unit / H), h = (int)(unit % H);
-    f32x4* R = reinterpret_cast<f32x4*>(Srun + unit * (long long)DKV) + q;
+    f32x4* R = reinterpret_cast<f32x4*>(Srun + unit * (long long)(DK * DV)) + q;
     f32x4 r = *R;
     const int32_t* ids = pair_id + (size_t)c * n_step;
     for (int j = 0; j < n_step; ++j) {
         const int id = ids[j];
         if ((unsigned)id >= (unsigned)n_pair) continue;
-        const float t = Tc[(size_t)id * H + h];
-        const f32x4 s = reinterpret_cast<const f32x4*>(Sc + ((size_t)id * H + h) * DKV)[q];
+        const float t = DIAG ? Tc[((size_t)id * H + h) * DK + row] : Tc[(size_t)id * H + h];
+        const f32x4 s = reinterpret_cast<const f32x4*>(Sc + ((size_t)id * H + h) * DK * DV)[q];
         r = t * r + s;
     }
     *R = r;
@@ -333,13 +337,17 @@ hipError_t compose_dense(int d, int n_chain, int H, int n_step, const int32_t* p
     return hipErrorInvalidValue;
 }
 
-hipError_t compose_scalar(int dk, int dv, int n_chain, int H, int n_step, const int32_t* pair_id,
+hipError_t compose_scalar(int dk, int dv, bool diag, int n_chain, int H, int n_step, const int32_t* pair_id,
                           int n_pair, const float* Tc, const float* Sc, float* Srun, hipStream_t st)
 {
     const long long total = (long long)n_chain * H * (dk * dv / 4);
     const int grid = (int)((total + 255) / 256);
-    hipLaunchKernelGGL(compose_scalar_kernel, dim3(grid), dim3(256), 0, st, n_chain, H, dk * dv,
-                       n_step, pair_id, n_pair, Tc, Sc, Srun);
+    if (diag)
+        hipLaunchKernelGGL(compose_scalar_kernel<true>, dim3(grid), dim3(256), 0, st, n_chain, H, dk, dv,
+                           n_step, pair_id, n_pair, Tc, Sc, Srun);
+    else
+        hipLaunchKernelGGL(compose_scalar_kernel<false>, dim3(grid), dim3(256), 0, st, n_chain, H, dk, dv,
+                           n_step, pair_id, n_pair, Tc, Sc, Srun);
     return hipGetLastError();
 }
 

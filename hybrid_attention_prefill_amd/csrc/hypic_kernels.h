@@ -22,7 +22,8 @@ struct SeamArgs {
 // t_split: T as bf16 hi/lo planes [n_pair][H][2][d][d]; else fp32 [n_pair][H][d][d]
 hipError_t compose_dense(int d, int n_chain, int H, int n_step, const int32_t* pair_id, int n_pair,
                          const void* Tc, bool t_split, const float* Sc, float* Srun, hipStream_t st);
-hipError_t compose_scalar(int dk, int dv, int n_chain, int H, int n_step, const int32_t* pair_id,
+// diag: T cached as fp32 [n_pair][H][dk] (T = diag(t)); else fp32 [n_pair][H] (T = t I)
+hipError_t compose_scalar(int dk, int dv, bool diag, int n_chain, int H, int n_step, const int32_t* pair_id,
                           int n_pair, const float* Tc, const float* Sc, float* Srun, hipStream_t st);
 
 // Build kernels: t_split writes T as bf16 hi/lo planes [n_seg][H][2][d][d].
@@ -36,9 +37,9 @@ hipError_t build_kda(int d, bool in_bf16, int n_seg, int H, const int64_t* sb, c
                      const void* k, const void* v, const void* g, const void* beta, void* T_out, bool t_split,
                      float* S_out, hipStream_t st);
 
-// build_decay.hip (scalar gate or head-constant decay, no erase); t_layout: 0 dense f32,
-// 1 scalar, 2 dense bf16 hi/lo planes
-hipError_t build_decay(int d, bool in_bf16, bool head_gate, int n_seg, int H, const int64_t* sb,
+// build_decay.hip (gate: 0 head-constant, 1 per-token scalar, 2 per-channel; no erase);
+// t_layout: 0 dense f32, 1 scalar, 2 dense bf16 hi/lo planes, 3 diagonal
+hipError_t build_decay(int d, bool in_bf16, int gate, int n_seg, int H, const int64_t* sb,
                        const int64_t* se, int64_t n_tok, const void* k, const void* v, const void* g,
                        void* T_out, int t_layout, float* S_out, hipStream_t st);
 

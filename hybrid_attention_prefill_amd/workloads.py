@@ -6,7 +6,7 @@ input dtype, segment lengths and reuse plans.  It contains none of the state
 arithmetic of the method, and it is the only module shared by the GPU tests and
 the CPU oracle's tests.
 
-The five workloads follow the shapes the pages give for HYPIC's prompts (tens
+The workloads follow the shapes the pages give for HYPIC's prompts (tens
 to hundreds of independent segments, segments usually longer than 512 tokens,
 32k and 100k-token prompts, 30 linear layers in a hybrid model) with the value
 distributions listed below.  They stand in for the public datasets and the
@@ -19,6 +19,7 @@ oracle consume bit-identical inputs.
 from __future__ import annotations
 
 import dataclasses
+import functools
 import math
 
 import numpy as np
@@ -264,6 +265,48 @@ def _kda_131k(seed, *, stress, n_heads=32, d=128, n_seg=64, seg_len=2048, n_req=
                     n_layers=n_layers)
 
 
+def _variant(family, seed, *, stress, n_heads=16, d=None, n_seg=16, seg_len=1024, lengths=None,
+             in_dtype="bf16"):
+    """The other transition families, 16 segments x 1024 tokens of bf16 inputs:
+      gla      : per-channel gate, no erase; g = -softplus(z) / 16 (log-sigmoid gates
+                 with temperature 16), d = 128;
+      mamba2   : token scalar gate, no erase; g = -0.1 softplus(z), d = 64;
+      deltanet : erase and write with beta = sigmoid(z), no gate (g = 0), d = 128.
+    Stress: gates scaled to a mean total log-decay of -1 per segment, beta = sigmoid(z - 4)."""
+    d = (64 if family == "mamba2" else 128) if d is None else d
+    lens = np.full(n_seg, seg_len) if lengths is None else np.asarray(lengths)
+    N = int(lens.sum())
+    ss = np.random.SeedSequence(seed).spawn(6)
+    rk, rv, rb, rg, rq, _ = [np.random.default_rng(s) for s in ss]
+    k, v = _tokens(rk, rv, N, n_heads, d, d, k_unit=True, kv_scale=1.0, in_dtype=in_dtype)
+    mean_len = float(np.mean(lens))
+    beta = None
+    if family == "gla":
+        gate, delta = GATE_DIAG, False
+        zg = rg.standard_normal((N, n_heads, d))
+        g = -_softplus(zg) / (mean_len * _e_softplus() if stress else 16.0)
+    elif family == "mamba2":
+        gate, delta = GATE_TOKEN, False
+        zg = rg.standard_normal((N, n_heads))
+        g = -_softplus(zg) / (mean_len * _e_softplus()) if stress else -0.1 * _softplus(zg)
+    elif family == "deltanet":
+        gate, delta = GATE_TOKEN, True
+        g = np.zeros((N, n_heads))
+        zb = rb.standard_normal((N, n_heads))
+        beta = _finish(_sigmoid(zb - 4.0) if stress else _sigmoid(zb), in_dtype)
+    else:
+        raise ValueError(f"unknown family {family!r}")
+    q = _finish(_unit_rows(rq.standard_normal((N, n_heads, d))), in_dtype)
+    starts = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    name = {"gla": "gla-16h-d128-16k", "mamba2": "mamba2-16h-d64-16k",
+            "deltanet": "deltanet-16h-d128-16k"}[family]
+    return Workload(name=name + ("-stress" if stress else ""), n_heads=n_heads, d_k=d, d_v=d,
+                    gate=gate, delta=delta, in_dtype=in_dtype, k=k, v=v, g=_finish(g, in_dtype),
+                    beta=beta, seg_start=starts, cache_begin=starts[:-1].copy(),
+                    cache_end=starts[1:].copy(), q=q, scale=1.0 / math.sqrt(d),
+                    pair_id=np.arange(len(lens), dtype=np.int32)[None, :])
+
+
 # name -> (maker, default seed)
 _MAKERS = {
     "gdn-tiny-f32": (_gdn_tiny, 1),
@@ -271,6 +314,9 @@ _MAKERS = {
     "gdn-16h-d128-32k": (_gdn_32k, 3),
     "gdn-16h-d128-100k-seam": (_gdn_100k_seam, 4),
     "kda-32h-d128-131k": (_kda_131k, 5),
+    "gla-16h-d128-16k": (functools.partial(_variant, "gla"), 6),
+    "mamba2-16h-d64-16k": (functools.partial(_variant, "mamba2"), 7),
+    "deltanet-16h-d128-16k": (functools.partial(_variant, "deltanet"), 8),
 }
 NAMES = tuple(_MAKERS)
 

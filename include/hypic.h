@@ -24,6 +24,9 @@
  *     gate HEAD,  delta 0 : M_t = gamma_h I,                  c_t = 1   (RetNet-style)
  *     gate TOKEN, delta 1 : M_t = alpha_t (I - b_t k_t k_t^T), c_t = b_t (gated DeltaNet)
  *     gate DIAG,  delta 1 : M_t = diag(a_t)(I - b_t k_t k_t^T), c_t = b_t (KDA-style)
+ *     gate TOKEN, delta 0 : M_t = alpha_t I,                 c_t = 1   (Mamba2-style)
+ *     gate DIAG,  delta 0 : M_t = diag(a_t),                 c_t = 1   (GLA-style)
+ * (DeltaNet is gate TOKEN, delta 1 with all g = 0.)
  * Gates are passed as log-gates g <= 0 (gamma = exp(g), alpha_t = exp(g_t),
  * a_t = exp(g_t) per key channel).
  *
@@ -47,7 +50,8 @@
  *     q, k, v, beta and token gates have dtype `in_dtype`.
  *     Pairs: S [n_pair][H][d_k][d_v] fp32; T by hypic_t_layout:
  *       DENSE  : fp32 [n_pair][H][d_k][d_k];
- *       SCALAR : fp32 [n_pair][H], T = t I (RetNet-style decay only);
+ *       SCALAR : fp32 [n_pair][H], T = t I (scalar gates without the delta rule);
+ *       DIAG   : fp32 [n_pair][H][d_k], T = diag(t) (gate DIAG without the delta rule);
  *       SPLIT  : bf16 [n_pair][H][2][d_k*d_k], plane 0 = hi = bf16(T) and
  *                plane 1 = lo = bf16(T - hi), both round-to-nearest-even, so
  *                T = hi + lo to about 2^-16 relative.  Within a plane, entry
@@ -69,7 +73,7 @@
 extern "C" {
 #endif
 
-#define HYPIC_ABI_VERSION 2
+#define HYPIC_ABI_VERSION 3
 
 typedef enum {
     HYPIC_OK = 0,
@@ -80,7 +84,7 @@ typedef enum {
 
 typedef enum { HYPIC_GATE_HEAD = 0, HYPIC_GATE_TOKEN = 1, HYPIC_GATE_DIAG = 2 } hypic_gate;
 typedef enum { HYPIC_F32 = 0, HYPIC_BF16 = 1 } hypic_dtype;
-typedef enum { HYPIC_T_DENSE = 0, HYPIC_T_SCALAR = 1, HYPIC_T_SPLIT = 2 } hypic_t_layout;
+typedef enum { HYPIC_T_DENSE = 0, HYPIC_T_SCALAR = 1, HYPIC_T_SPLIT = 2, HYPIC_T_DIAG = 3 } hypic_t_layout;
 
 typedef struct {
     int32_t n_heads;  /* H >= 1                                                  */
@@ -89,7 +93,8 @@ typedef struct {
     int32_t gate;     /* hypic_gate                                             */
     int32_t delta;    /* 1: delta-rule erase + beta-weighted write; 0: plain     */
     int32_t in_dtype; /* hypic_dtype of q, k, v, beta and token gates            */
-    int32_t t_layout; /* hypic_t_layout of T (SCALAR only for gate HEAD, delta 0) */
+    int32_t t_layout; /* hypic_t_layout of T (SCALAR: gate HEAD or TOKEN, delta 0;
+                         DIAG: gate DIAG, delta 0)                              */
 } hypic_dims;
 
 /*
@@ -105,7 +110,7 @@ typedef struct {
  *   beta               : ignored (may be NULL) when delta == 0
  *   T_out              : in the dims' t_layout; may be NULL to skip T (S only)
  * Implemented (d_k == d_v = d):
- *   gate HEAD or TOKEN, delta 0 : d in {16, 32, 64, 128}, fp32 or bf16 inputs;
+ *   gate HEAD, TOKEN or DIAG, delta 0 : d in {16, 32, 64, 128}, fp32 or bf16 inputs;
  *   gate TOKEN, delta 1         : d = 16 (fp32 or bf16), 64 or 128 (bf16);
  *   gate DIAG,  delta 1         : d = 64 or 128, bf16 inputs.
  * Other combinations return HYPIC_E_UNSUPPORTED.  For the delta-rule kernels
@@ -126,7 +131,8 @@ hypic_status hypic_segment_build(const hypic_dims* dims, int32_t n_seg,
  * linear layer; several layers go in one call as separate chains whose ids
  * index that layer's part of the caches.
  *   pair_id : int32 [n_chain][n_step]
- *   T_cache : in the dims' t_layout (any of the three)
+ *   T_cache : in the dims' t_layout (any of the four; DENSE and SPLIT need
+ *             d_k == d_v)
  *   S_run   : fp32 [n_chain][H][d_k][d_v], read and written in place
  */
 hypic_status hypic_compose(const hypic_dims* dims, int32_t n_chain, int32_t n_step,

@@ -1,0 +1,137 @@
+"""The other transition families against the fp64 oracle: GLA-style per-channel
+gates without the erase (diagonal T, cached as its diagonal), Mamba2-style token
+gates without the erase (scalar T) and DeltaNet (erase without a gate).
+
+Tolerances as for the other builds: relative Frobenius error per (segment, head)
+<= 1e-4 for fp32 inputs and <= 5e-3 for bf16 inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from hybrid_attention_prefill_amd import binding as hb
+from hybrid_attention_prefill_amd import workloads as wl
+from _util import assert_pairs_close, dev, rel_f, t_value, workload_tensors
+
+pytestmark = pytest.mark.gpu
+TOL = {"f32": 1e-4, "bf16": 5e-3}
+
+
+def _build(W, t_layout, begin=None, end=None):
+    x = workload_tensors(W)
+    b = W.cache_begin if begin is None else begin
+    e = W.cache_end if end is None else end
+    T, S = hb.segment_build(x["k"], x["v"], x["g"], x["beta"], dev(b, torch.int64), dev(e, torch.int64),
+                            gate=W.gate, delta=W.delta, t_layout=t_layout)
+    torch.cuda.synchronize()
+    return T, S.cpu().numpy()
+
+
+def _dense(T, t_layout, d):
+    """A T cache of any layout as float64 [..., d, d]."""
+    if t_layout == hb.T_DIAG:
+        t = T.double().cpu().numpy()
+        return t[..., :, None] * np.eye(d)
+    if t_layout == hb.T_SCALAR:
+        return T.double().cpu().numpy()[..., None, None] * np.eye(d)
+    return t_value(T, d)
+
+
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("t_layout", [hb.T_DIAG, hb.T_DENSE, hb.T_SPLIT])
+def test_gla_build(t_layout, d, in_dtype):
+    """Per-channel gate, no erase: chunks, ragged tails, one token, an empty range."""
+    W = wl.make("gla-16h-d128-16k", n_heads=3, d=d, lengths=[300, 64, 1, 129], in_dtype=in_dtype)
+    begin = np.concatenate([W.cache_begin, [7]])
+    end = np.concatenate([W.cache_end, [7]])
+    print(W.name, d, in_dtype, t_layout, flush=True)
+    T, S = _build(W, t_layout, begin, end)
+    T0, S0 = oracle.segment_build(W.k, W.v, W.g, W.beta, begin, end, gate=W.gate, delta=False)
+    Td = _dense(T, t_layout, d)
+    assert_pairs_close(Td, S, T0, S0, TOL[in_dtype], W.name)
+    if t_layout == hb.T_DENSE:
+        off = Td * (1 - np.eye(d))
+        assert np.all(off == 0)                      # diagonal T has exact zeros off the diagonal
+    assert np.array_equal(Td[-1], np.broadcast_to(np.eye(d), Td[-1].shape))
+    assert np.all(S[-1] == 0)
+
+
+@pytest.mark.parametrize("stress", [False, True])
+def test_gla_full_size_compose_matches_full(stress):
+    """16 heads x 16 x 1024 tokens at d=128 (the workload's full shape): the diagonal
+    pairs composed in order equal the full recurrence; under stress the naive sum does not."""
+    W = wl.make("gla-16h-d128-16k", stress=stress)
+    print(W.name, "full", flush=True)
+    T, S = _build(W, hb.T_DIAG)
+    assert tuple(T.shape) == (16, 16, 128) and T.dtype == torch.float32
+    Rg = torch.zeros((1, 16, 128, 128), device="cuda")
+    hb.compose(T, dev(S, torch.float32), dev(W.pair_id, torch.int32), Rg)
+    torch.cuda.synchronize()
+    full, _ = oracle.run(W.k, W.v, W.g, None, gate=W.gate, delta=False)
+    assert rel_f(Rg.cpu().numpy()[0], full).max() <= TOL["bf16"]
+    rng = np.random.default_rng(2)
+    for s, h in zip(rng.integers(0, 16, 3), rng.integers(0, 16, 3)):
+        b, e = W.cache_begin[s], W.cache_end[s]
+        T0, S0 = oracle.segment_build(W.k[b:e, h:h + 1], W.v[b:e, h:h + 1], W.g[b:e, h:h + 1], None,
+                                      [0], [e - b], gate=W.gate, delta=False)
+        assert_pairs_close(_dense(T[s:s + 1, h:h + 1], hb.T_DIAG, 128), S[s:s + 1, h:h + 1], T0, S0,
+                           TOL["bf16"], f"seg {s} head {h}")
+    if stress:
+        naive = oracle.naive_sum(S, W.pair_id)[0]
+        assert rel_f(naive, full).min() > 20 * TOL["bf16"]
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (64, 64), (128, 128), (128, 64), (32, 128)])
+def test_compose_diag_T(dk, dv):
+    """Elementwise composition with diagonal T: row r of the state scales by t[r]."""
+    H, n_pair, n_chain, n_step = 5, 7, 3, 9
+    rng = np.random.default_rng(dk + dv)
+    t = rng.uniform(0.3, 1.0, size=(n_pair, H, dk)).astype(np.float32)
+    S = rng.standard_normal((n_pair, H, dk, dv)).astype(np.float32)
+    ids = rng.integers(-1, n_pair, size=(n_chain, n_step)).astype(np.int32)
+    ids[1, 2] = n_pair + 4                            # out of range: skipped
+    R0 = rng.standard_normal((n_chain, H, dk, dv)).astype(np.float32)
+    Td = t.astype(np.float64)[..., :, None] * np.eye(dk)
+    ref = oracle.compose(Td, S, np.where(ids >= n_pair, -1, ids), R0)
+    Rg = dev(R0, torch.float32)
+    hb.compose(dev(t, torch.float32), dev(S, torch.float32), dev(ids, torch.int32), Rg, t_layout=hb.T_DIAG)
+    torch.cuda.synchronize()
+    assert rel_f(Rg.cpu().numpy(), ref).max() < 1e-6
+
+
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("t_layout", [hb.T_SCALAR, hb.T_DENSE])
+def test_mamba2_build_and_compose(t_layout, in_dtype):
+    """Token scalar gate, no erase (d=64): pairs with ragged tails, then the ordered
+    composition against the full recurrence."""
+    W = wl.make("mamba2-16h-d64-16k", n_heads=4, lengths=[1024, 77, 1, 640], in_dtype=in_dtype)
+    print(W.name, in_dtype, t_layout, flush=True)
+    T, S = _build(W, t_layout)
+    T0, S0 = oracle.segment_build(W.k, W.v, W.g, None, W.cache_begin, W.cache_end, gate=W.gate, delta=False)
+    assert_pairs_close(_dense(T, t_layout, 64), S, T0, S0, TOL[in_dtype], W.name)
+    Rg = torch.zeros((1, 4, 64, 64), device="cuda")
+    hb.compose(T, dev(S, torch.float32), dev(W.pair_id, torch.int32), Rg, t_layout=t_layout)
+    torch.cuda.synchronize()
+    full, _ = oracle.run(W.k, W.v, W.g, None, gate=W.gate, delta=False)
+    assert rel_f(Rg.cpu().numpy()[0], full).max() <= TOL[in_dtype]
+
+
+@pytest.mark.parametrize("stress", [False, True])
+def test_deltanet_build_and_compose(stress):
+    """Erase without a gate (g = 0), d=128, bf16: T is a product of I - b k k^T, which
+    stays O(1), so the composition exercises T at full weight."""
+    W = wl.make("deltanet-16h-d128-16k", stress=stress, n_heads=2, lengths=[1024, 300, 65, 1])
+    print(W.name, flush=True)
+    T, S = _build(W, hb.T_DENSE)
+    T = T.cpu().numpy()
+    T0, S0 = oracle.segment_build(W.k, W.v, W.g, W.beta, W.cache_begin, W.cache_end, gate=W.gate, delta=True)
+    assert_pairs_close(T, S, T0, S0, TOL["bf16"], W.name)
+    Rg = torch.zeros((1, 2, 128, 128), device="cuda")
+    hb.compose(dev(T, torch.float32), dev(S, torch.float32), dev(W.pair_id, torch.int32), Rg)
+    torch.cuda.synchronize()
+    full, _ = oracle.run(W.k, W.v, W.g, W.beta, gate=W.gate, delta=True)
+    assert rel_f(Rg.cpu().numpy()[0], full).max() <= TOL["bf16"]
+    naive = oracle.naive_sum(S, W.pair_id)[0]
+    assert rel_f(naive, full).min() > 10 * TOL["bf16"]
