@@ -89,7 +89,7 @@ def _check_tokens(k, v, H, dk, dv):
     assert v.ndim == 3 and v.shape[1:] == (H, dv) and v.shape[0] == k.shape[0], v.shape
 
 
-def segment_build(k, v, g, beta, seg_begin, seg_end, *, gate: int, delta: bool, want_T: bool = True):
+def segment_build(k, v, g, beta, seg_begin, seg_end, *, gate: int, delta: int, want_T: bool = True):
     """(T_C, S(C|0)) per (segment, head) by the token recurrence ([ZH] 2.1).
 
     Returns ``T`` [n_seg, H, d_k, d_k] (or None) and ``S`` [n_seg, H, d_k, d_v].
@@ -112,7 +112,7 @@ def segment_build(k, v, g, beta, seg_begin, seg_end, *, gate: int, delta: bool, 
     return T, S
 
 
-def run(k, v, g, beta, *, gate: int, delta: bool, t0: int = 0, t1: int | None = None,
+def run(k, v, g, beta, *, gate: int, delta: int, t0: int = 0, t1: int | None = None,
         S0=None, q=None, scale: float = 1.0):
     """Plain recurrence over tokens [t0, t1) from state S0 (default 0).
 
@@ -158,7 +158,7 @@ def compose(T_cache, S_cache, pair_id, S_run=None, *, t_scalar: bool = False):
     return R
 
 
-def seam_advance(q, k, v, g, beta, seam_start, *, gate: int, delta: bool, w: int, scale: float,
+def seam_advance(q, k, v, g, beta, seam_start, *, gate: int, delta: int, w: int, scale: float,
                  pair_id=None, T_cache=None, S_cache=None, S_run=None, t_scalar: bool = False):
     """Seam windows then composition, step by step along each chain ([ZH] 2.2).
 

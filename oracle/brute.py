@@ -21,15 +21,16 @@ import numpy as np
 GATE_HEAD, GATE_TOKEN, GATE_DIAG = 0, 1, 2
 
 
-def transition(k_t, beta_t, g_t, *, gate: int, delta: bool) -> np.ndarray:
-    """Dense M_t = G_t (I - beta_t k_t k_t^T) (delta rule) or M_t = G_t."""
+def transition(k_t, beta_t, g_t, *, gate: int, delta: int) -> np.ndarray:
+    """Dense M_t = G_t (I - beta_t k_t k_t^T) (delta 1), (I - beta_t k_t k_t^T) G_t
+    (delta 2: gate before the erase) or M_t = G_t (delta 0)."""
     dk = k_t.shape[0]
     E = np.eye(dk) - beta_t * np.outer(k_t, k_t) if delta else np.eye(dk)
     if gate == GATE_DIAG:
         G = np.diag(np.exp(np.asarray(g_t, dtype=np.float64)))
     else:
         G = np.exp(float(g_t)) * np.eye(dk)
-    return G @ E
+    return E @ G if delta == 2 else G @ E
 
 
 def _gate_of(g, t, h, gate):

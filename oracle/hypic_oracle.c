@@ -31,8 +31,11 @@
  *   - state S is d_k x d_v, transitions are d_k x d_k and act from the left,
  *     later tokens on the left of the product (forced by "T(C2) S(C1)");
  *   - transition of token t:  M_t = G_t (I - beta_t k_t k_t^T) with the
- *     delta rule, M_t = G_t without it; G_t = exp(g) (per-head constant or
- *     per-token scalar) or diag(exp(g_t)) (per-token, per key channel);
+ *     delta rule (delta = 1, gate applied after the erase), M_t =
+ *     (I - beta_t k_t k_t^T) G_t with delta = 2 (gate applied before the
+ *     erase, the order of the Kimi Delta Attention write-ups; the same matrix
+ *     for scalar gates), M_t = G_t without it; G_t = exp(g) (per-head constant
+ *     or per-token scalar) or diag(exp(g_t)) (per-token, per key channel);
  *   - write term: beta_t k_t v_t^T with the delta rule, k_t v_t^T without;
  *   - output of a stepped token: o_t = S_t^T (scale q_t) with S_t the state
  *     after the token's update.
@@ -54,7 +57,8 @@
 typedef struct {
     int32_t n_heads, d_k, d_v;
     int32_t gate;  /* 0 head constant, 1 token scalar, 2 token per-channel */
-    int32_t delta; /* 1: erase with beta k k^T and write beta k v^T       */
+    int32_t delta; /* 1: erase with beta k k^T, then gate, write beta k v^T;
+                      2: gate, then erase, write beta k v^T; 0: gate, k v^T */
 } ora_dims;
 
 int oracle_num_threads(void)
@@ -76,6 +80,15 @@ static double log_gate(const ora_dims *d, const double *g, int64_t t, int h, int
     }
 }
 
+/* gate: X <- G_t X (row i scaled by exp of its log-gate) */
+static void gate_rows(const ora_dims *d, int64_t t, int h, const double *g, double *X, int ncol)
+{
+    for (int i = 0; i < d->d_k; ++i) {
+        const double G = exp(log_gate(d, g, t, h, i));
+        for (int n = 0; n < ncol; ++n) X[i * ncol + n] *= G;
+    }
+}
+
 /*
  * One token of one head, in place on a d_k x ncol matrix X (the state S, or
  * the running transition product T): X <- M_t X, then, if `v` is given, the
@@ -89,6 +102,7 @@ static void apply_token(const ora_dims *d, int64_t t, int h, const double *k,
     const int dk = d->d_k, H = d->n_heads;
     const double *kt = k + (t * H + h) * (int64_t)dk;
     const double b = d->delta ? beta[t * H + h] : 0.0;
+    if (d->delta == 2) gate_rows(d, t, h, g, X, ncol);
     if (d->delta) {
         /* erase: X <- (I - b k k^T) X */
         for (int n = 0; n < ncol; ++n) {
@@ -99,11 +113,7 @@ static void apply_token(const ora_dims *d, int64_t t, int h, const double *k,
         for (int i = 0; i < dk; ++i)
             for (int n = 0; n < ncol; ++n) X[i * ncol + n] -= b * kt[i] * u[n];
     }
-    /* gate: X <- G X */
-    for (int i = 0; i < dk; ++i) {
-        const double G = exp(log_gate(d, g, t, h, i));
-        for (int n = 0; n < ncol; ++n) X[i * ncol + n] *= G;
-    }
+    if (d->delta != 2) gate_rows(d, t, h, g, X, ncol);
     if (v) {
         /* write: X <- X + c k v^T, c = beta with the delta rule, else 1 */
         const double *vt = v + (t * H + h) * (int64_t)ncol;

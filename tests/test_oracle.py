@@ -28,6 +28,7 @@ VARIANTS = [  # (gate, delta)
     (wl.GATE_TOKEN, False),  # scalar-gated, no erase
     (wl.GATE_DIAG, False),   # per-channel gate, no erase
     (wl.GATE_HEAD, True),    # constant decay with erase
+    (wl.GATE_DIAG, 2),       # KDA, gate before the erase: (I - b k k^T) diag(a)
 ]
 
 
@@ -78,6 +79,19 @@ def test_golden_diagonal_gate_order():
     T, S = oracle.segment_build(k, v, g, beta, [0], [2], gate=wl.GATE_DIAG, delta=True)
     np.testing.assert_allclose(T[0, 0], fx["T"], atol=1e-14)
     np.testing.assert_allclose(S[0, 0], fx["S"], atol=1e-14)
+
+
+def test_golden_diagonal_gate_before_erase():
+    fx = json.load(open(GOLDEN))["diagonal_gate_before_erase"]
+    k = np.array(fx["k"])[:, None, :]
+    v = np.array(fx["v"])[:, None, :]
+    beta = np.array(fx["beta"])[:, None]
+    g = np.log(np.array(fx["a"]))[:, None, :]
+    T, S = oracle.segment_build(k, v, g, beta, [0], [2], gate=wl.GATE_DIAG, delta=2)
+    np.testing.assert_allclose(T[0, 0], fx["T"], atol=1e-14)
+    np.testing.assert_allclose(S[0, 0], fx["S"], atol=1e-14)
+    _, S1 = oracle.segment_build(k, v, g, beta, [0], [2], gate=wl.GATE_DIAG, delta=1)
+    np.testing.assert_allclose(S1[0, 0], fx["S_other_order"], atol=1e-14)
 
 
 # ---------------------------------------------------------------- brute force
