@@ -124,7 +124,8 @@ def t_layout_of(T):
 
 
 def make_dims(H, dk, dv, *, gate, delta, in_dtype, t_layout=T_DENSE):
-    return Dims(int(H), int(dk), int(dv), int(gate), int(bool(delta)), int(in_dtype), int(t_layout))
+    """delta: False/0 plain write, True/1 erase then gate, 2 gate then erase."""
+    return Dims(int(H), int(dk), int(dv), int(gate), int(delta), int(in_dtype), int(t_layout))
 
 
 def abi_version() -> int:

@@ -47,7 +47,7 @@ hypic_status check_dims(const hypic_dims* d)
         return fail(HYPIC_E_INVALID, "d_k and d_v must be 16, 32, 64 or 128 (got %d, %d)", d->d_k, d->d_v);
     if (d->gate < HYPIC_GATE_HEAD || d->gate > HYPIC_GATE_DIAG)
         return fail(HYPIC_E_INVALID, "gate must be 0, 1 or 2 (got %d)", d->gate);
-    if (d->delta != 0 && d->delta != 1) return fail(HYPIC_E_INVALID, "delta must be 0 or 1 (got %d)", d->delta);
+    if (d->delta < 0 || d->delta > 2) return fail(HYPIC_E_INVALID, "delta must be 0, 1 or 2 (got %d)", d->delta);
     if (d->in_dtype != HYPIC_F32 && d->in_dtype != HYPIC_BF16)
         return fail(HYPIC_E_INVALID, "in_dtype must be 0 (f32) or 1 (bf16) (got %d)", d->in_dtype);
     if (d->t_layout < HYPIC_T_DENSE || d->t_layout > HYPIC_T_DIAG)
@@ -81,7 +81,7 @@ hypic_status hypic_segment_build(const hypic_dims* dims, int32_t n_seg, const in
     if (!seg_begin || !seg_end) return fail(HYPIC_E_INVALID, "seg_begin / seg_end is NULL");
     if (!S_out) return fail(HYPIC_E_INVALID, "S_out is NULL");
     if (n_tokens > 0 && (!k || !v || !g)) return fail(HYPIC_E_INVALID, "k, v or g is NULL");
-    if (dims->delta && n_tokens > 0 && !beta) return fail(HYPIC_E_INVALID, "beta is NULL with delta = 1");
+    if (dims->delta && n_tokens > 0 && !beta) return fail(HYPIC_E_INVALID, "beta is NULL with the delta rule");
     if ((long long)n_seg * dims->n_heads > kMaxGrid) return fail(HYPIC_E_INVALID, "n_seg * n_heads too large");
     if (dims->d_k != dims->d_v) return fail(HYPIC_E_UNSUPPORTED, "d_k != d_v is not implemented");
     const bool bf16 = dims->in_dtype == HYPIC_BF16;
@@ -98,7 +98,7 @@ hypic_status hypic_segment_build(const hypic_dims* dims, int32_t n_seg, const in
                         "hypic_segment_build");
     }
     if (dims->delta && dims->gate == HYPIC_GATE_DIAG) {
-        return from_hip(hypic::build_kda(dims->d_k, bf16, n_seg, dims->n_heads, seg_begin, seg_end, n_tokens, k,
+        return from_hip(hypic::build_kda(dims->d_k, bf16, dims->delta == 2, n_seg, dims->n_heads, seg_begin, seg_end, n_tokens, k,
                                          v, g, beta, T_out, dims->t_layout == HYPIC_T_SPLIT, S_out, st),
                         "hypic_segment_build");
     }

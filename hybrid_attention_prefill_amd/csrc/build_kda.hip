@@ -1,21 +1,28 @@
 // build_kda.hip -- segment build (T_C, S(C|0)) for the per-channel (diagonal)
-// gate with the delta rule, gate applied after the erase:
-//     M_t = diag(a_t) (I - b_t k_t k_t^T),   S_t = M_t S_{t-1} + b_t k_t v_t^T,
+// gate with the delta rule, in either order of gate and erase:
+//     M_t = diag(a_t) (I - b_t k_t k_t^T)   (gate after the erase), or
+//     M_t = (I - b_t k_t k_t^T) diag(a_t)   (gate before the erase, GF),
+//     S_t = M_t S_{t-1} + b_t k_t v_t^T,
 // a_t = e^{g_t} per key channel.  The cached pair is T_C = M_L..M_1 and S(C|0)
 // ([ZH] = the Chinese HYPIC page, section 2.1, which names KDA among the
-// families the transition operator covers; the gate-left-of-erase order is the
-// reading documented with the oracle).
+// families the transition operator covers without fixing the order).
 //
-// Chunked form (C = 32; derivation in the design notes).  Per key channel let
-// a_t be the exclusive in-chunk cumulative log-gate (a_0 = 0, a_C = b_C).  With
-//     Lp[t][s] = b_t sum_c k_t k_s e^{a_t - a_s},  L'[t][s] = sum_c k_t k_s e^{a_t - a_{s+1}}  (s < t)
-//     A = (I + Lp)^-1,  W = A diag(b) (e^{a} o K),  U = A diag(b) L' diag(b) V
-//     Kh = e^{b_C - a} o K,  Kh' = e^{b_C - a_{+1}} o K
+// Chunked form (C = 32; derivation in the design notes).  In the coordinates
+// Z_t = Gamma_t^-1 S_t (Gamma_t = diag of the inclusive cumulative gate) a token
+// is Z <- Z - b e_t (f_t^T Z) + b w_t v_t^T with write vector w_t = Gamma_t^-1 k_t
+// and erase vectors e_t = G^-1 k_t, f_t = G k_t, where G = Gamma_{t-1} when the
+// gate follows the erase and G = Gamma_t when it comes first.  Per key channel
+// let i_t be the inclusive in-chunk cumulative log-gate (the write vector's) and
+// c_t the erase vectors' one: the exclusive sum (c_0 = 0) for the first order,
+// c_t = i_t for GF; b_C is the chunk total.  With
+//     Lp[t][s] = b_t sum_c k_t k_s e^{c_t - c_s},  L'[t][s] = sum_c k_t k_s e^{c_t - i_s}  (s < t)
+//     A = (I + Lp)^-1,  W = A diag(b) (e^{c} o K),  U = A diag(b) L' diag(b) V
+//     Kh = e^{b_C - c} o K,  Kh' = e^{b_C - i} o K
 // the augmented state X = [T | S] advances as
 //     X <- diag(e^{b_C}) X - Kh^T (W X) + [0 | Kh'^T diag(b) V - Kh^T U].
 // Every exponential has a non-positive exponent except inside the decay-weighted
 // Gram matrices, which are factored per 16-token row block I around
-// rho_I = a_{16 I}: left e^{a_t - rho_I} <= 1 and right e^{rho_I - a_s}, which is
+// rho_I = c_{16 I}: left e^{c_t - rho_I} <= 1 and right e^{rho_I - c_s}, which is
 // <= 1 off the diagonal block and bounded by one 16-token block's decay on it.
 // Those two Gram matrices, W and every product of the T columns use bf16 hi + lo
 // operands (three products on v_mfma_f32_16x16x32_bf16, fp32 range): with strong
@@ -46,7 +53,7 @@ constexpr int LDF = CK + 1;   // fp32 32x32 matrices
 template <int D>
 struct alignas(16) KdaSmem {
     uint16_t Kb[CK][D + 8];        // K (bf16 bits), token-major
-    float Ag[CK + 1][D + 4];       // exclusive cumulative log-gate per channel; row CK = b_C
+    float Ag[CK + 1][D + 4];       // exclusive cumulative log-gate per channel; row t+1 inclusive, row CK = b_C
     float beta[CK];
     float F1[CK][LDF];             // Lp (strictly lower, beta folded)
     float F1p[CK][LDF];            // L'
@@ -77,7 +84,7 @@ __device__ __forceinline__ Frag<1> f16frag(const uint16_t* base, int ld, int row
 
 }  // namespace
 
-template <int D>
+template <int D, bool GF>
 __global__ __launch_bounds__(512) void build_kda_kernel(
     int n_seg, int H, const int64_t* __restrict__ seg_begin, const int64_t* __restrict__ seg_end,
     int64_t n_tokens, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -90,6 +97,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
     constexpr int CTW = (NCT + 7) / 8;
     constexpr int KSD = D / 32;
     static_assert(D % 32 == 0, "d must be a multiple of 32");
+    constexpr int E1 = GF ? 1 : 0;   // row of Ag holding the erase vectors' cumulative gate of token 0
     __shared__ SM sm;
 
     const int unit = blockIdx.x;
@@ -174,9 +182,9 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int c = ks * 32 + 8 * g4 + e;
-                    const float rho = sm.Ag[16 * I][c];
-                    const float a = bf(sm.Kb[t][c]) * __expf(sm.Ag[t][c] - rho);
-                    const float b = bf(sm.Kb[s][c]) * __expf(rho - sm.Ag[lp ? s : s + 1][c]);
+                    const float rho = sm.Ag[16 * I + E1][c];
+                    const float a = bf(sm.Kb[t][c]) * __expf(sm.Ag[t + E1][c] - rho);
+                    const float b = bf(sm.Kb[s][c]) * __expf(rho - sm.Ag[lp ? s + E1 : s + 1][c]);
                     __bf16 x, y;
                     split_bf16(a, x, y);
                     ah[e] = x; al[e] = y;
@@ -198,7 +206,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
             for (int it = tid - 384; it < D * CK; it += 128) {
                 const int c = it / CK, t = it % CK;
                 const float kx = bf(sm.Kb[t][c]);
-                const float at = sm.Ag[t][c], at1 = sm.Ag[t + 1][c], bc = sm.Ag[CK][c];
+                const float at = sm.Ag[t + E1][c], at1 = sm.Ag[t + 1][c], bc = sm.Ag[CK][c];
                 put_bf16_split(&sm.RmT[0][c][t], &sm.RmT[1][c][t], kx * __expf(at));
                 const float kh = kx * __expf(bc - at);
                 sm.KhT[c][t] = f16_bits((_Float16)kh);
@@ -408,23 +416,24 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
     }
 }
 
-hipError_t build_kda(int d, bool in_bf16, int n_seg, int H, const int64_t* sb, const int64_t* se, int64_t n_tok,
+hipError_t build_kda(int d, bool in_bf16, bool gate_first, int n_seg, int H, const int64_t* sb, const int64_t* se, int64_t n_tok,
                      const void* k, const void* v, const void* g, const void* beta, void* T_out, bool t_split,
                      float* S_out, hipStream_t st)
 {
     if (!in_bf16) return hipErrorNotSupported;
     const uint16_t *k16 = static_cast<const uint16_t*>(k), *v16 = static_cast<const uint16_t*>(v),
                    *g16 = static_cast<const uint16_t*>(g), *b16 = static_cast<const uint16_t*>(beta);
-    if (d == 128) {
-        hipLaunchKernelGGL(build_kda_kernel<128>, dim3(n_seg * H), dim3(512), 0, st, n_seg, H, sb, se, n_tok, k16,
-                           v16, g16, b16, T_out, (int)t_split, S_out);
-        return hipGetLastError();
+#define HYPIC_KDA(DD, GFV)                                                                                      \
+    if (d == DD && gate_first == GFV) {                                                                          \
+        hipLaunchKernelGGL((build_kda_kernel<DD, GFV>), dim3(n_seg * H), dim3(512), 0, st, n_seg, H, sb, se,      \
+                           n_tok, k16, v16, g16, b16, T_out, (int)t_split, S_out);                              \
+        return hipGetLastError();                                                                                \
     }
-    if (d == 64) {
-        hipLaunchKernelGGL(build_kda_kernel<64>, dim3(n_seg * H), dim3(512), 0, st, n_seg, H, sb, se, n_tok, k16,
-                           v16, g16, b16, T_out, (int)t_split, S_out);
-        return hipGetLastError();
-    }
+    HYPIC_KDA(128, false)
+    HYPIC_KDA(128, true)
+    HYPIC_KDA(64, false)
+    HYPIC_KDA(64, true)
+#undef HYPIC_KDA
     return hipErrorNotSupported;
 }
 

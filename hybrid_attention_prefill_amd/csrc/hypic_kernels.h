@@ -33,7 +33,7 @@ hipError_t build_gdn(int d, bool in_bf16, int n_seg, int H, const int64_t* sb, c
                      void* T_out, bool t_split, float* S_out, hipStream_t st);
 
 // build_kda.hip (per-channel gate, delta rule; bf16 inputs)
-hipError_t build_kda(int d, bool in_bf16, int n_seg, int H, const int64_t* sb, const int64_t* se, int64_t n_tok,
+hipError_t build_kda(int d, bool in_bf16, bool gate_first, int n_seg, int H, const int64_t* sb, const int64_t* se, int64_t n_tok,
                      const void* k, const void* v, const void* g, const void* beta, void* T_out, bool t_split,
                      float* S_out, hipStream_t st);
 

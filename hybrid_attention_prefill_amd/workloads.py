@@ -69,7 +69,7 @@ class Workload:
     d_k: int
     d_v: int
     gate: int
-    delta: bool
+    delta: int                    # 0 plain write, 1 erase then gate, 2 gate then erase
     in_dtype: str                 # "f32" or "bf16"
     k: np.ndarray
     v: np.ndarray
@@ -235,9 +235,11 @@ def _gdn_100k_seam(seed, *, stress, n_heads=16, d=128, n_seg=128, total=100_000,
 
 
 def _kda_131k(seed, *, stress, n_heads=32, d=128, n_seg=64, seg_len=2048, n_req=64, n_step=256,
-          n_layers=30, lengths=None):
+          n_layers=30, lengths=None, gate_first=False, gate_sigma=0.05):
     """KDA-style per-channel gate, bf16: 32 heads, d=128, 64 x 2048 tokens; then
-    n_req requests x n_step cached segments per layer x n_layers layers."""
+    n_req requests x n_step cached segments per layer x n_layers layers.
+    gate_first: the gate applied before the erase (delta 2) instead of after it;
+    gate_sigma: spread of the per-channel log-gates, g = -softplus(gate_sigma z)."""
     lens = np.full(n_seg, seg_len) if lengths is None else np.asarray(lengths)
     N = int(lens.sum())
     ss = np.random.SeedSequence(seed).spawn(7)
@@ -247,18 +249,19 @@ def _kda_131k(seed, *, stress, n_heads=32, d=128, n_seg=64, seg_len=2048, n_req=
     zg = rg.standard_normal((N, n_heads, d))
     if stress:
         beta = _sigmoid(zb - 4.0)
-        g = -_softplus(zg * 0.05) / (float(np.mean(lens)) * _e_softplus(0.05))
+        g = -_softplus(zg * gate_sigma) / (float(np.mean(lens)) * _e_softplus(gate_sigma))
     else:
         beta = _sigmoid(zb)
-        g = -_softplus(zg * 0.05)
+        g = -_softplus(zg * gate_sigma)
     q = _finish(_unit_rows(rq.standard_normal((N, n_heads, d))), "bf16")
     starts = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
     # chain (request r, layer l) draws n_step ids uniformly from that layer's n_seg pairs;
     # pair index = l * n_seg + segment (one distinct cache copy per layer)
     ids = rp.integers(0, n_seg, size=(n_layers, n_req, n_step)).astype(np.int32)
     ids = ids + (np.arange(n_layers, dtype=np.int32) * n_seg)[:, None, None]
-    return Workload(name="kda-32h-d128-131k" + ("-stress" if stress else ""), n_heads=n_heads, d_k=d,
-                    d_v=d, gate=GATE_DIAG, delta=True, in_dtype="bf16", k=k, v=v,
+    return Workload(name="kda-32h-d128-131k" + ("-gate-first" if gate_first else "") + ("-stress" if stress else ""),
+                    n_heads=n_heads, d_k=d, d_v=d, gate=GATE_DIAG, delta=2 if gate_first else 1,
+                    in_dtype="bf16", k=k, v=v,
                     g=_finish(g, "bf16"), beta=_finish(beta, "bf16"), seg_start=starts,
                     cache_begin=starts[:-1].copy(), cache_end=starts[1:].copy(), q=q,
                     scale=1.0 / math.sqrt(d), pair_id=ids.reshape(n_layers * n_req, n_step),

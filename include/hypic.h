@@ -24,9 +24,11 @@
  *     gate HEAD,  delta 0 : M_t = gamma_h I,                  c_t = 1   (RetNet-style)
  *     gate TOKEN, delta 1 : M_t = alpha_t (I - b_t k_t k_t^T), c_t = b_t (gated DeltaNet)
  *     gate DIAG,  delta 1 : M_t = diag(a_t)(I - b_t k_t k_t^T), c_t = b_t (KDA-style)
+ *     gate DIAG,  delta 2 : M_t = (I - b_t k_t k_t^T)diag(a_t), c_t = b_t (KDA, gate first)
  *     gate TOKEN, delta 0 : M_t = alpha_t I,                 c_t = 1   (Mamba2-style)
  *     gate DIAG,  delta 0 : M_t = diag(a_t),                 c_t = 1   (GLA-style)
- * (DeltaNet is gate TOKEN, delta 1 with all g = 0.)
+ * (DeltaNet is gate TOKEN, delta 1 with all g = 0.  For scalar gates delta 2,
+ * the gate applied before the erase, is the same transition as delta 1.)
  * Gates are passed as log-gates g <= 0 (gamma = exp(g), alpha_t = exp(g_t),
  * a_t = exp(g_t) per key channel).
  *
@@ -73,7 +75,7 @@
 extern "C" {
 #endif
 
-#define HYPIC_ABI_VERSION 3
+#define HYPIC_ABI_VERSION 4
 
 typedef enum {
     HYPIC_OK = 0,
@@ -91,7 +93,8 @@ typedef struct {
     int32_t d_k;      /* key dim: 16, 32, 64 or 128                             */
     int32_t d_v;      /* value dim: 16, 32, 64 or 128                           */
     int32_t gate;     /* hypic_gate                                             */
-    int32_t delta;    /* 1: delta-rule erase + beta-weighted write; 0: plain     */
+    int32_t delta;    /* 0: plain write; 1: delta-rule erase, then the gate, and
+                         beta-weighted write; 2: as 1 with the gate first      */
     int32_t in_dtype; /* hypic_dtype of q, k, v, beta and token gates            */
     int32_t t_layout; /* hypic_t_layout of T (SCALAR: gate HEAD or TOKEN, delta 0;
                          DIAG: gate DIAG, delta 0)                              */
@@ -111,8 +114,8 @@ typedef struct {
  *   T_out              : in the dims' t_layout; may be NULL to skip T (S only)
  * Implemented (d_k == d_v = d):
  *   gate HEAD, TOKEN or DIAG, delta 0 : d in {16, 32, 64, 128}, fp32 or bf16 inputs;
- *   gate TOKEN, delta 1         : d = 16 (fp32 or bf16), 64 or 128 (bf16);
- *   gate DIAG,  delta 1         : d = 64 or 128, bf16 inputs.
+ *   gate TOKEN, delta 1 or 2    : d = 16 (fp32 or bf16), 64 or 128 (bf16);
+ *   gate DIAG,  delta 1 or 2    : d = 64 or 128, bf16 inputs.
  * Other combinations return HYPIC_E_UNSUPPORTED.  For the delta-rule kernels
  * the state and values must stay within fp16 range (|entries| < 6e4).
  */
@@ -159,7 +162,7 @@ hypic_status hypic_compose(const hypic_dims* dims, int32_t n_chain, int32_t n_st
  *                owned by the caller, 256-byte aligned; contents are
  *                overwritten; concurrent calls need distinct workspaces.
  *   T_cache    : t_layout DENSE or SPLIT
- * Implemented: gate TOKEN, delta 1, d_k == d_v in {16, 32, 64, 128}.
+ * Implemented: gate TOKEN, delta 1 or 2, d_k == d_v in {16, 32, 64, 128}.
  */
 hypic_status hypic_seam_advance(const hypic_dims* dims, int32_t n_chain, int32_t n_step,
                                 int32_t w, const int64_t* seam_start, int64_t n_tokens,

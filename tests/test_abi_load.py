@@ -49,7 +49,8 @@ def _dims(**kw):
 @pytest.mark.parametrize("bad", [dict(H=0), dict(dk=24), dict(dv=256), dict(gate=3), dict(in_dtype=7),
                                  dict(t_layout=1), dict(t_layout=1, delta=0, gate=hb.GATE_DIAG), dict(t_layout=3),
                                  dict(t_layout=3, gate=hb.GATE_DIAG), dict(t_layout=3, delta=0),
-                                 dict(t_layout=4), dict(t_layout=-1)])
+                                 dict(t_layout=4), dict(t_layout=-1), dict(delta=3), dict(delta=-1),
+                                 dict(t_layout=3, gate=hb.GATE_DIAG, delta=2)])
 def test_invalid_dims_rejected(lib, bad):
     d = _dims(**bad)
     st = lib.hypic_compose(ctypes.byref(d), 1, 1, None, 0, None, None, None, None)
@@ -60,7 +61,9 @@ def test_invalid_dims_rejected(lib, bad):
 @pytest.mark.parametrize("ok", [dict(t_layout=hb.T_SCALAR, gate=hb.GATE_HEAD, delta=0),
                                 dict(t_layout=hb.T_SCALAR, gate=hb.GATE_TOKEN, delta=0),
                                 dict(t_layout=hb.T_DIAG, gate=hb.GATE_DIAG, delta=0),
-                                dict(t_layout=hb.T_SPLIT, gate=hb.GATE_DIAG, delta=0)])
+                                dict(t_layout=hb.T_SPLIT, gate=hb.GATE_DIAG, delta=0),
+                                dict(t_layout=hb.T_SPLIT, gate=hb.GATE_DIAG, delta=2),
+                                dict(t_layout=hb.T_DENSE, gate=hb.GATE_TOKEN, delta=2)])
 def test_valid_layout_gate_pairs_accepted(lib, ok):
     d = _dims(**ok)
     assert lib.hypic_compose(ctypes.byref(d), 0, 1, None, 0, None, None, None, None) == hb.HYPIC_OK

@@ -135,3 +135,41 @@ def test_deltanet_build_and_compose(stress):
     assert rel_f(Rg.cpu().numpy()[0], full).max() <= TOL["bf16"]
     naive = oracle.naive_sum(S, W.pair_id)[0]
     assert rel_f(naive, full).min() > 10 * TOL["bf16"]
+
+
+@pytest.mark.parametrize("stress", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_kda_gate_first_ragged(d, stress):
+    """KDA with the gate applied before the erase, (I - b k k^T) diag(a_t), and log-gates
+    spread widely over the channels (g = -softplus(2 z)): several chunks, ragged tails, one
+    token, an empty range.  Without stress the gate-after-erase states of the same tokens
+    differ from these by more than three times the tolerance, so the order is tested."""
+    W = wl.make("kda-32h-d128-131k", gate_first=True, gate_sigma=2.0, stress=stress, n_heads=2, d=d,
+                lengths=[256, 100, 33, 1], n_req=1, n_step=1, n_layers=1)
+    assert W.delta == 2
+    begin = np.concatenate([W.cache_begin, [3]])
+    end = np.concatenate([W.cache_end, [3]])
+    print(W.name, d, flush=True)
+    T, S = _build(W, hb.T_DENSE, begin, end)
+    T = T.cpu().numpy()
+    T0, S0 = oracle.segment_build(W.k, W.v, W.g, W.beta, begin, end, gate=W.gate, delta=2)
+    assert_pairs_close(T, S, T0, S0, TOL["bf16"], W.name)
+    assert np.array_equal(T[-1], np.broadcast_to(np.eye(d, dtype=np.float32), T[-1].shape)) and np.all(S[-1] == 0)
+    if not stress:
+        _, S1 = oracle.segment_build(W.k, W.v, W.g, W.beta, begin, end, gate=W.gate, delta=1)
+        assert rel_f(S1[:3], S0[:3]).min() > 3 * TOL["bf16"]
+
+
+def test_kda_gate_first_split_compose_matches_full():
+    """Gate-first KDA pairs cached with SPLIT T and composed in order equal the full recurrence."""
+    W = wl.make("kda-32h-d128-131k", gate_first=True, gate_sigma=2.0, stress=True, n_heads=2, n_seg=4,
+                seg_len=300, n_req=1, n_step=1, n_layers=1)
+    print(W.name, "split compose", flush=True)
+    T, S = _build(W, hb.T_SPLIT)
+    Rg = torch.zeros((1, 2, 128, 128), device="cuda")
+    hb.compose(T, dev(S, torch.float32), dev(np.arange(4, dtype=np.int32)[None, :], torch.int32), Rg)
+    torch.cuda.synchronize()
+    full, _ = oracle.run(W.k, W.v, W.g, W.beta, gate=W.gate, delta=2)
+    assert rel_f(Rg.cpu().numpy()[0], full).max() <= TOL["bf16"]
+    naive = oracle.naive_sum(S, np.arange(4)[None, :])[0]
+    assert rel_f(naive, full).min() > 20 * TOL["bf16"]
