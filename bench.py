@@ -114,6 +114,11 @@ def main():
     tsz = 1 if t_layout == hb.T_SCALAR else d * d
     tdt = torch.bfloat16 if t_layout == hb.T_SPLIT else torch.float32
     tshape = lambda n: (n, H) if t_layout == hb.T_SCALAR else (n, H, 2, d * d)
+
+    def build_workspace(n_seg):   # allocated outside the timed region (None: no cutting)
+        nb = hb.build_workspace_bytes(H, d, d, n_seg, W.n_tokens, gate=W.gate, delta=W.delta,
+                                      in_dtype=hb.BF16 if W.in_dtype == "bf16" else hb.F32)
+        return torch.empty(nb, device=dev, dtype=torch.uint8) if nb > 0 else None
     timer = Timer(torch)
     info = {}
 
@@ -136,12 +141,13 @@ def main():
         R = torch.zeros((1, H, d, d), device=dev)
         out = torch.zeros((1, W.n_seg, W.w, H, d), device=dev)
         ws = torch.empty(hb.seam_workspace_bytes(H, d, d, 1, W.n_seg, W.w), device=dev, dtype=torch.uint8)
+        wsb = build_workspace(len(cold))
         cold_tokens = int((W.cache_end[cold] - W.cache_begin[cold]).sum())
 
         def step():
             timer.run("segment_build", lambda: hb.segment_build(k, v, g, beta, sb_c, se_c, gate=W.gate,
                                                                 delta=W.delta, t_layout=t_layout,
-                                                                T_out=Tcold, S_out=Scold))
+                                                                T_out=Tcold, S_out=Scold, workspace=wsb))
             R.zero_()
             timer.run("seam_advance", lambda: hb.seam_advance(q, k, v, g, beta, seam, R, out, gate=W.gate,
                                                               delta=W.delta, w=W.w, scale=W.scale, pair_id=ids,
@@ -182,9 +188,12 @@ def main():
                 Tc[l * W.n_seg:(l + 1) * W.n_seg].copy_(Tb)
                 Sc[l * W.n_seg:(l + 1) * W.n_seg].copy_(Sb)
 
+        wsb = build_workspace(W.n_seg)
+
         def step():
             timer.run("segment_build", lambda: hb.segment_build(k, v, g, beta, sb, se, gate=W.gate, delta=W.delta,
-                                                                t_layout=t_layout, T_out=Tb, S_out=Sb))
+                                                                t_layout=t_layout, T_out=Tb, S_out=Sb,
+                                                                workspace=wsb))
             R.zero_()
             timer.run("compose", lambda: hb.compose(Tc, Sc, ids, R, t_layout=t_layout))
 
@@ -269,7 +278,8 @@ def main():
 CALL_SOURCES = {
     "seam_advance": ["seam.hip", "seam_chain.hip", "seam_layout.h", "hypic_device.h", "hypic_kernels.h"],
     "compose": ["compose.hip", "hypic_device.h", "hypic_kernels.h"],
-    "segment_build": ["build_gdn.hip", "build_kda.hip", "build_decay.hip", "build_common.h", "hypic_device.h"],
+    "segment_build": ["build_gdn.hip", "build_split.hip", "build_kda.hip", "build_decay.hip", "build_common.h",
+                      "hypic_device.h", "hypic_kernels.h"],
 }
 
 

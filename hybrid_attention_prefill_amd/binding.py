@@ -20,8 +20,8 @@ GATE_HEAD, GATE_TOKEN, GATE_DIAG = 0, 1, 2
 F32, BF16 = 0, 1
 T_DENSE, T_SCALAR, T_SPLIT, T_DIAG = 0, 1, 2, 3
 
-EXPORTED = ("hypic_segment_build", "hypic_compose", "hypic_seam_advance", "hypic_seam_workspace_bytes",
-            "hypic_last_error", "hypic_abi_version", "hypic_selftest_layouts")
+EXPORTED = ("hypic_segment_build", "hypic_build_workspace_bytes", "hypic_compose", "hypic_seam_advance",
+            "hypic_seam_workspace_bytes", "hypic_last_error", "hypic_abi_version", "hypic_selftest_layouts")
 
 
 class HypicError(RuntimeError):
@@ -49,8 +49,10 @@ def load_library(path: str = LIB_PATH):
     lib = ctypes.CDLL(path)
     P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     D = ctypes.POINTER(Dims)
-    lib.hypic_segment_build.argtypes = [D, I32, P, P, I64, P, P, P, P, P, P, P]
+    lib.hypic_segment_build.argtypes = [D, I32, P, P, I64, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.hypic_segment_build.restype = ctypes.c_int
+    lib.hypic_build_workspace_bytes.argtypes = [D, I32, I64]
+    lib.hypic_build_workspace_bytes.restype = ctypes.c_size_t
     lib.hypic_compose.argtypes = [D, I32, I32, P, I32, P, P, P, P]
     lib.hypic_compose.restype = ctypes.c_int
     lib.hypic_seam_advance.argtypes = [D, I32, I32, I32, P, I64, P, P, P, P, P, ctypes.c_float, P, I32,
@@ -132,9 +134,16 @@ def abi_version() -> int:
     return int(load_library().hypic_abi_version())
 
 
+def build_workspace_bytes(H, dk, dv, n_seg, n_tokens, *, gate=GATE_TOKEN, delta=True, in_dtype=BF16):
+    d = make_dims(H, dk, dv, gate=gate, delta=delta, in_dtype=in_dtype)
+    return int(load_library().hypic_build_workspace_bytes(ctypes.byref(d), n_seg, n_tokens))
+
+
 def segment_build(k, v, g, beta, seg_begin, seg_end, *, gate, delta, t_layout=T_DENSE,
-                  want_T=True, T_out=None, S_out=None, stream=None):
-    """(T_C, S(C|0)) for every (segment, head) -- hypic_segment_build."""
+                  want_T=True, T_out=None, S_out=None, workspace="auto", stream=None):
+    """(T_C, S(C|0)) for every (segment, head) -- hypic_segment_build.
+    workspace: "auto" allocates the build workspace (long segments are cut into pieces
+    built in parallel), None builds every segment as one chain, or a uint8 device tensor."""
     lib = load_library()
     _dev(k, "k")
     n_tok, H, dk = k.shape
@@ -160,9 +169,17 @@ def segment_build(k, v, g, beta, seg_begin, seg_end, *, gate, delta, t_layout=T_
     if T_out is not None:
         _dev(T_out, "T_out", _t_dtype(t_layout), _t_shape(t_layout, n_seg, H, dk))
     d = make_dims(H, dk, dv, gate=gate, delta=delta, in_dtype=dt, t_layout=t_layout)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError(f"workspace must be 'auto', None or a tensor (got {workspace!r})")
+        need = int(lib.hypic_build_workspace_bytes(ctypes.byref(d), n_seg, n_tok))
+        workspace = torch.empty(need, device=k.device, dtype=torch.uint8) if need > 0 else None
+    if workspace is not None:
+        _dev(workspace, "workspace", torch.uint8)
     _check(lib.hypic_segment_build(ctypes.byref(d), n_seg, _ptr(seg_begin), _ptr(seg_end), n_tok, _ptr(k),
                                    _ptr(v), _ptr(g), _ptr(beta) if delta else None, _ptr(T_out),
-                                   _ptr(S_out), _stream(stream)))
+                                   _ptr(S_out), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                   _stream(stream)))
     return T_out, S_out
 
 

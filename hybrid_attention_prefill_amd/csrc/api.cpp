@@ -70,9 +70,17 @@ int32_t hypic_abi_version(void) { return HYPIC_ABI_VERSION; }
 
 const char* hypic_last_error(void) { return g_last_error.c_str(); }
 
+size_t hypic_build_workspace_bytes(const hypic_dims* dims, int32_t n_seg, int64_t n_tokens)
+{
+    if (!dims || dims->n_heads < 1 || dims->d_k != dims->d_v || n_seg < 1 || n_tokens < 0) return 0;
+    if (dims->gate != HYPIC_GATE_TOKEN || !dims->delta || dims->in_dtype != HYPIC_BF16) return 0;
+    return hypic::split_workspace_bytes(dims->d_k, dims->n_heads, n_seg, n_tokens);
+}
+
 hypic_status hypic_segment_build(const hypic_dims* dims, int32_t n_seg, const int64_t* seg_begin,
                                  const int64_t* seg_end, int64_t n_tokens, const void* k, const void* v,
-                                 const void* g, const void* beta, void* T_out, float* S_out, void* stream)
+                                 const void* g, const void* beta, void* T_out, float* S_out,
+                                 void* workspace, size_t workspace_bytes, void* stream)
 {
     if (hypic_status s = check_dims(dims)) return s;
     if (n_seg < 0) return fail(HYPIC_E_INVALID, "n_seg must be >= 0 (got %d)", n_seg);
@@ -92,9 +100,20 @@ hypic_status hypic_segment_build(const hypic_dims* dims, int32_t n_seg, const in
                         "hypic_segment_build");
     }
     if (dims->delta && dims->gate == HYPIC_GATE_TOKEN) {
+        const size_t need = workspace ? hypic_build_workspace_bytes(dims, n_seg, n_tokens) : 0;
+        if (need > 0) {
+            if (workspace_bytes < need)
+                return fail(HYPIC_E_INVALID, "build workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+            if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+                return fail(HYPIC_E_INVALID, "workspace must be 256-byte aligned");
+            return from_hip(hypic::build_gdn_split(dims->d_k, bf16, n_seg, dims->n_heads, seg_begin, seg_end,
+                                                   n_tokens, k, v, g, beta, T_out,
+                                                   dims->t_layout == HYPIC_T_SPLIT, S_out, workspace, st),
+                            "hypic_segment_build");
+        }
         return from_hip(hypic::build_gdn(dims->d_k, bf16, n_seg, dims->n_heads, seg_begin, seg_end,
                                          n_tokens, k, v, g, beta, T_out,
-                                         dims->t_layout == HYPIC_T_SPLIT, S_out, st),
+                                         dims->t_layout == HYPIC_T_SPLIT, S_out, hypic::BuildItems{}, st),
                         "hypic_segment_build");
     }
     if (dims->delta && dims->gate == HYPIC_GATE_DIAG) {

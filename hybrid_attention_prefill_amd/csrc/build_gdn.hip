@@ -124,7 +124,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
     int n_seg, int H, const int64_t* __restrict__ seg_begin, const int64_t* __restrict__ seg_end,
     int64_t n_tokens, const void* __restrict__ k, const void* __restrict__ v,
     const void* __restrict__ gl, const void* __restrict__ beta, void* __restrict__ T_out, int t_split,
-    float* __restrict__ S_out)
+    float* __restrict__ S_out, BuildItems items)
 {
     using SM = GdnSmem<D, NSPLIT>;
     constexpr int KP = SM::KP;
@@ -140,6 +140,23 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
 
     const int unit = blockIdx.x;
     const int seg = unit / H, h = unit % H;
+    // items mode: range `seg` of the plan is a segment or a piece of one; its pair goes to
+    // the caller's slot out >= 0 or to workspace slot -1 - out (T as bf16 hi/lo planes)
+    int64_t beg = seg_begin[seg], end = seg_end[seg];
+    int out = seg;
+    if (items.out) {
+        // the item's fields are read before the live-item check (the arrays hold n_seg
+        // entries), so the loads go out together
+        const int n_live = *items.n_items;
+        out = items.out[seg];
+        if (seg >= n_live) return;
+        if (out < 0) {
+            T_out = items.T_ws;
+            t_split = 1;
+            S_out = items.S_ws;
+            out = -1 - out;
+        }
+    }
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g4 = lane >> 4, n16 = lane & 15;
@@ -148,7 +165,6 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
     auto s_tile = [&](int c) -> bool { return RT % 8 == 0 ? c * 8 >= RT : wave + 8 * c >= RT; };
     auto own_tile = [&](int c) -> bool { return NCT % 8 == 0 || wave + 8 * c < NCT; };
 
-    int64_t beg = seg_begin[seg], end = seg_end[seg];
     beg = beg < 0 ? 0 : (beg > n_tokens ? n_tokens : beg);
     end = end < beg ? beg : (end > n_tokens ? n_tokens : end);
 
@@ -543,7 +559,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
 
     // ---- emit T_C = e^{log_s} H and S(C|0)
     const float tscale = expf(log_s);
-    const size_t pair = (size_t)seg * H + h;
+    const size_t pair = (size_t)out * H + h;
 #pragma unroll
     for (int c = 0; c < CTW; ++c) {
         const int ct = wave + 8 * c;
@@ -559,26 +575,31 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                 else put_t(T_out, t_split, pair, D, row, ct * 16 + n16, tscale * X[rt][c][e]);
             }
     }
+
 }
 
 template <int D, int NSPLIT, bool BF16>
 static hipError_t launch_gdn(int n_seg, int H, const int64_t* sb, const int64_t* se, int64_t n_tok,
                              const void* k, const void* v, const void* g, const void* beta,
-                             void* T_out, bool t_split, float* S_out, hipStream_t st)
+                             void* T_out, bool t_split, float* S_out, const BuildItems& items, hipStream_t st)
 {
     hipLaunchKernelGGL((build_gdn_kernel<D, NSPLIT, BF16>), dim3(n_seg * H), dim3(512), 0, st, n_seg,
-                       H, sb, se, n_tok, k, v, g, beta, T_out, (int)t_split, S_out);
+                       H, sb, se, n_tok, k, v, g, beta, T_out, (int)t_split, S_out, items);
     return hipGetLastError();
 }
 
 hipError_t build_gdn(int d, bool in_bf16, int n_seg, int H, const int64_t* sb, const int64_t* se,
                      int64_t n_tok, const void* k, const void* v, const void* g, const void* beta,
-                     void* T_out, bool t_split, float* S_out, hipStream_t st)
+                     void* T_out, bool t_split, float* S_out, const BuildItems& items, hipStream_t st)
 {
-    if (d == 128 && in_bf16) return launch_gdn<128, 1, true>(n_seg, H, sb, se, n_tok, k, v, g, beta, T_out, t_split, S_out, st);
-    if (d == 64 && in_bf16) return launch_gdn<64, 1, true>(n_seg, H, sb, se, n_tok, k, v, g, beta, T_out, t_split, S_out, st);
-    if (d == 16 && !in_bf16) return launch_gdn<16, 2, false>(n_seg, H, sb, se, n_tok, k, v, g, beta, T_out, t_split, S_out, st);
-    if (d == 16 && in_bf16) return launch_gdn<16, 1, true>(n_seg, H, sb, se, n_tok, k, v, g, beta, T_out, t_split, S_out, st);
+#define HYPIC_GDN(D_, NS_, BF_)                                                                          \
+    if (d == D_ && in_bf16 == BF_)                                                                       \
+        return launch_gdn<D_, NS_, BF_>(n_seg, H, sb, se, n_tok, k, v, g, beta, T_out, t_split, S_out, items, st);
+    HYPIC_GDN(128, 1, true)
+    HYPIC_GDN(64, 1, true)
+    HYPIC_GDN(16, 2, false)
+    HYPIC_GDN(16, 1, true)
+#undef HYPIC_GDN
     return hipErrorNotSupported;
 }
 

@@ -155,6 +155,17 @@ __device__ __forceinline__ void put_t(void* T, bool split, size_t pair, int d, i
     }
 }
 
+// the inverse of put_t: one entry of a dense T (split: hi + lo)
+__device__ __forceinline__ float get_t(const void* T, bool split, size_t pair, int d, int row, int col) {
+    const int dd = d * d;
+    if (split) {
+        const uint16_t* P = reinterpret_cast<const uint16_t*>(T) + pair * 2 * dd;
+        const int off = frag_off(row, col, d);
+        return bf16_bits_to_f32(P[off]) + bf16_bits_to_f32(P[dd + off]);
+    }
+    return reinterpret_cast<const float*>(T)[pair * dd + (size_t)row * d + col];
+}
+
 // ---- workgroup barrier for LDS traffic only ------------------------------------
 // Waits for this wave's LDS operations (lgkmcnt = 0), then s_barrier.  Unlike
 // __syncthreads() it does not wait for outstanding vector-memory loads, so loads

@@ -27,10 +27,26 @@ hipError_t compose_scalar(int dk, int dv, bool diag, int n_chain, int H, int n_s
                           int n_pair, const float* Tc, const float* Sc, float* Srun, hipStream_t st);
 
 // Build kernels: t_split writes T as bf16 hi/lo planes [n_seg][H][2][d][d].
+// Items mode of the GDN build (out != NULL): the n_seg ranges are the plan's items, of
+// which the first *n_items are live; item i writes its pair to slot out[i] of T_out /
+// S_out when out[i] >= 0, else to slot -1 - out[i] of T_ws (bf16 hi/lo planes) / S_ws.
+struct BuildItems {
+    const int32_t* n_items = nullptr;
+    const int32_t* out = nullptr;
+    void* T_ws = nullptr;
+    float* S_ws = nullptr;
+};
 // build_gdn.hip (scalar gate, delta rule)
 hipError_t build_gdn(int d, bool in_bf16, int n_seg, int H, const int64_t* sb, const int64_t* se,
                      int64_t n_tok, const void* k, const void* v, const void* g, const void* beta,
-                     void* T_out, bool t_split, float* S_out, hipStream_t st);
+                     void* T_out, bool t_split, float* S_out, const BuildItems& items, hipStream_t st);
+
+// build_split.hip: long segments built as pieces in parallel and folded by composition
+// (GDN, d in {64, 128}).  Workspace bytes for (d, H, n_seg, n_tokens); 0 = never cut.
+size_t split_workspace_bytes(int d, int H, int n_seg, int64_t n_tokens);
+hipError_t build_gdn_split(int d, bool in_bf16, int n_seg, int H, const int64_t* sb, const int64_t* se,
+                           int64_t n_tok, const void* k, const void* v, const void* g, const void* beta,
+                           void* T_out, bool t_split, float* S_out, void* ws, hipStream_t st);
 
 // build_kda.hip (per-channel gate, delta rule; bf16 inputs)
 hipError_t build_kda(int d, bool in_bf16, bool gate_first, int n_seg, int H, const int64_t* sb, const int64_t* se, int64_t n_tok,

@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define HYPIC_ABI_VERSION 4
+#define HYPIC_ABI_VERSION 5
 
 typedef enum {
     HYPIC_OK = 0,
@@ -112,6 +112,17 @@ typedef struct {
  *   n_tokens           : length of the packed token arrays (ranges are clamped)
  *   beta               : ignored (may be NULL) when delta == 0
  *   T_out              : in the dims' t_layout; may be NULL to skip T (S only)
+ *   workspace          : NULL, or device scratch of at least
+ *                        hypic_build_workspace_bytes(dims, n_seg, n_tokens) bytes,
+ *                        256-byte aligned, owned by the caller, contents overwritten;
+ *                        concurrent calls need distinct workspaces.  With it, long
+ *                        segments are built as pieces in parallel and the pieces'
+ *                        pairs folded by the composition law ([ZH] 2.1 and the segment
+ *                        parallelism of 2.3): a segment of c > 14 64-token chunks is cut
+ *                        on chunk boundaries into ceil(c / 14) near-equal pieces.  How a
+ *                        segment is cut depends on its length only, so its pair does
+ *                        not depend on the other segments of the call.  Without it (or
+ *                        where the query returns 0) every segment is one serial chain.
  * Implemented (d_k == d_v = d):
  *   gate HEAD, TOKEN or DIAG, delta 0 : d in {16, 32, 64, 128}, fp32 or bf16 inputs;
  *   gate TOKEN, delta 1 or 2    : d = 16 (fp32 or bf16), 64 or 128 (bf16);
@@ -123,7 +134,15 @@ hypic_status hypic_segment_build(const hypic_dims* dims, int32_t n_seg,
                                  const int64_t* seg_begin, const int64_t* seg_end,
                                  int64_t n_tokens, const void* k, const void* v,
                                  const void* g, const void* beta,
-                                 void* T_out, float* S_out, void* stream);
+                                 void* T_out, float* S_out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of build workspace that let hypic_segment_build cut long segments: non-zero
+ * for gate TOKEN with the delta rule, bf16 inputs, d in {64, 128} and n_tokens of at
+ * least 896; 0 otherwise (the workspace is then ignored).  Sized for segments that do
+ * not overlap: (2 d^2 4 bytes per head) per slot, floor(n_tokens / 896) slots, plus
+ * the plan; a segment whose pieces do not fit is built uncut. */
+size_t hypic_build_workspace_bytes(const hypic_dims* dims, int32_t n_seg, int64_t n_tokens);
 
 /*
  * hypic_compose -- reuse of cached pairs ([ZH] 2.1: left-multiply by T_C,

@@ -74,23 +74,45 @@ def test_null_pointers_rejected(lib):
     assert lib.hypic_compose(None, 1, 1, None, 0, None, None, None, None) == hb.HYPIC_E_INVALID
     assert lib.hypic_compose(ctypes.byref(d), 1, 1, None, 1, None, None, None, None) == hb.HYPIC_E_INVALID
     assert lib.hypic_segment_build(ctypes.byref(d), 2, None, None, 10, None, None, None, None, None, None,
-                                   None) == hb.HYPIC_E_INVALID
+                                   None, 0, None) == hb.HYPIC_E_INVALID
     assert lib.hypic_segment_build(ctypes.byref(d), -1, None, None, 10, None, None, None, None, None, None,
-                                   None) == hb.HYPIC_E_INVALID
+                                   None, 0, None) == hb.HYPIC_E_INVALID
 
 
 def test_empty_work_is_ok(lib):
     d = _dims()
     assert lib.hypic_compose(ctypes.byref(d), 0, 5, None, 0, None, None, None, None) == hb.HYPIC_OK
     assert lib.hypic_segment_build(ctypes.byref(d), 0, None, None, 0, None, None, None, None, None, None,
-                                   None) == hb.HYPIC_OK
+                                   None, 0, None) == hb.HYPIC_OK
 
 
 def test_unsupported_reported(lib):
     d = _dims(dk=16, dv=32)
     p = ctypes.c_void_p(16)  # never dereferenced: the shape is rejected first
-    st = lib.hypic_segment_build(ctypes.byref(d), 1, p, p, 4, p, p, p, p, p, p, None)
+    st = lib.hypic_segment_build(ctypes.byref(d), 1, p, p, 4, p, p, p, p, p, p, None, 0, None)
     assert st == hb.HYPIC_E_UNSUPPORTED
+
+
+def test_build_workspace_size(lib):
+    """Build workspace: only for the bf16 gated delta rule at d in {64, 128}, zero below
+    one 896-token piece, growing with the token count."""
+    assert hb.build_workspace_bytes(16, 128, 128, 128, 100_000) > 0
+    assert hb.build_workspace_bytes(16, 128, 128, 128, 895) == 0
+    assert hb.build_workspace_bytes(16, 16, 16, 128, 100_000) == 0
+    assert hb.build_workspace_bytes(16, 128, 128, 128, 100_000, in_dtype=hb.F32) == 0
+    assert hb.build_workspace_bytes(16, 128, 128, 128, 100_000, gate=hb.GATE_DIAG) == 0
+    assert hb.build_workspace_bytes(16, 128, 128, 128, 100_000, delta=False) == 0
+    one = hb.build_workspace_bytes(16, 128, 128, 128, 896)
+    two = hb.build_workspace_bytes(16, 128, 128, 128, 2 * 896)
+    assert two - one == 16 * 2 * 128 * 128 * 4            # one more slot: T planes + S per head
+
+
+def test_short_build_workspace_rejected(lib):
+    d = _dims(H=16, dk=128, dv=128, in_dtype=hb.BF16)
+    need = hb.build_workspace_bytes(16, 128, 128, 4, 10_000)
+    p = ctypes.c_void_p(256)  # never dereferenced: the size is rejected first
+    st = lib.hypic_segment_build(ctypes.byref(d), 4, p, p, 10_000, p, p, p, p, p, p, p, need - 1, None)
+    assert st == hb.HYPIC_E_INVALID and "workspace" in lib.hypic_last_error().decode()
 
 
 def test_seam_workspace_size(lib):

@@ -201,3 +201,74 @@ def test_split_T_layout(name, kw):
     T0, S0 = _oracle_build(W)
     tol = TOL["f32"] if W.in_dtype == "f32" else TOL["bf16"]
     assert_pairs_close(t_value(Tsp), Ssp.cpu().numpy(), T0, S0, tol, W.name)
+
+
+def _build_ws(W, begin, end, workspace, t_layout=hb.T_DENSE, want_T=True):
+    x = workload_tensors(W)
+    T, S = hb.segment_build(x["k"], x["v"], x["g"], x["beta"], dev(begin, torch.int64), dev(end, torch.int64),
+                            gate=W.gate, delta=W.delta, t_layout=t_layout, want_T=want_T, workspace=workspace)
+    torch.cuda.synchronize()
+    return T, S
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_cut_segments_match_oracle(d):
+    """Segments longer than 14 chunks are cut into pieces built in parallel and folded by
+    composition: lengths on both sides of the cut points (896 = 14 chunks, 897, 1771 = 28
+    chunks with a ragged tail, 2000 = 3 pieces), short and empty segments in the same call."""
+    lens = [1771, 2000, 896, 897, 64, 1, 1030]
+    W = wl.make("gdn-16h-d128-32k", stress=True, n_heads=3, d=d, lengths=lens)
+    begin = np.concatenate([W.cache_begin, [9]])
+    end = np.concatenate([W.cache_end, [9]])
+    assert hb.build_workspace_bytes(3, d, d, len(begin), W.n_tokens) > 0
+    print(W.name, d, "cut", flush=True)
+    T, S = _build_ws(W, begin, end, "auto")
+    T0, S0 = oracle.segment_build(W.k, W.v, W.g, W.beta, begin, end, gate=W.gate, delta=W.delta)
+    assert_pairs_close(T.cpu().numpy(), S.cpu().numpy(), T0, S0, TOL["bf16"], W.name)
+    assert np.array_equal(T[-1].cpu().numpy(), np.broadcast_to(np.eye(d, dtype=np.float32), T[-1].shape))
+    # uncut segments are bit-identical with and without the workspace
+    Tu, Su = _build_ws(W, begin, end, None)
+    short = [2, 4, 5, 7]
+    assert torch.equal(T[short], Tu[short]) and torch.equal(S[short], Su[short])
+    assert not torch.equal(S[0], Su[0])     # the cut segment took the other path
+
+
+def test_cut_segments_split_T_and_S_only():
+    """Cut segments with T cached as bf16 hi/lo planes, and with T not requested."""
+    W = wl.make("gdn-16h-d128-32k", stress=True, n_heads=2, lengths=[1771, 300, 2000])
+    print(W.name, "cut split-T", flush=True)
+    T0, S0 = oracle.segment_build(W.k, W.v, W.g, W.beta, W.cache_begin, W.cache_end, gate=W.gate, delta=W.delta)
+    Tsp, Ssp = _build_ws(W, W.cache_begin, W.cache_end, "auto", t_layout=hb.T_SPLIT)
+    assert_pairs_close(t_value(Tsp), Ssp.cpu().numpy(), T0, S0, TOL["bf16"], W.name)
+    Tn, Sn = _build_ws(W, W.cache_begin, W.cache_end, "auto", want_T=False)
+    assert Tn is None and torch.equal(Sn, Ssp)
+
+
+def test_cut_segment_independent_of_neighbours():
+    """A cut segment's pair is bit-identical whatever the other segments of the call and
+    its offset in the packed arrays."""
+    W = wl.make("gdn-16h-d128-32k", n_heads=2, lengths=[1900, 700, 1000])
+    x = workload_tensors(W)
+    sb, se = W.cache_begin, W.cache_end
+    T1, S1 = hb.segment_build(x["k"], x["v"], x["g"], x["beta"], dev(sb, torch.int64), dev(se, torch.int64),
+                              gate=W.gate, delta=True)
+    pre = 333
+    cat = lambda a: torch.cat([a[-pre:], a])
+    T2, S2 = hb.segment_build(cat(x["k"]), cat(x["v"]), cat(x["g"]), cat(x["beta"]),
+                              dev(sb[:1] + pre, torch.int64), dev(se[:1] + pre, torch.int64), gate=W.gate, delta=True)
+    torch.cuda.synchronize()
+    assert torch.equal(T1[:1], T2) and torch.equal(S1[:1], S2)
+
+
+def test_overlapping_segments_beyond_workspace_built_uncut():
+    """Overlapping ranges can ask for more pieces than the workspace holds (it is sized for
+    disjoint segments): the segments that do not fit are built uncut, every pair is still right."""
+    W = wl.make("gdn-16h-d128-32k", stress=True, n_heads=2, lengths=[1800])
+    begin = np.array([0, 0, 5, 0], dtype=np.int64)
+    end = np.array([1800, 1800, 1795, 1800], dtype=np.int64)
+    print(W.name, "overlap", flush=True)
+    T, S = _build_ws(W, begin, end, "auto")
+    T0, S0 = oracle.segment_build(W.k, W.v, W.g, W.beta, begin, end, gate=W.gate, delta=W.delta)
+    assert_pairs_close(T.cpu().numpy(), S.cpu().numpy(), T0, S0, TOL["bf16"], W.name)
+    Tu, Su = _build_ws(W, begin, end, None)
+    assert not torch.equal(S[0], Su[0]) and torch.equal(S[3], Su[3])   # first cut, last uncut
