@@ -28,7 +28,7 @@ namespace hypic {
 namespace {
 
 constexpr int kChunk = 64;         // tokens per chunk of the GDN build
-constexpr int kPieceChunks = 14;   // longest piece, in chunks
+constexpr int kPieceChunks = 16;   // longest piece, in chunks (segments up to this long are not cut)
 constexpr int kBuckets = 64;       // LPT buckets by piece length (the last collects the rest)
 
 struct SplitPlan {

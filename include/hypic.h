@@ -118,8 +118,8 @@ typedef struct {
  *                        concurrent calls need distinct workspaces.  With it, long
  *                        segments are built as pieces in parallel and the pieces'
  *                        pairs folded by the composition law ([ZH] 2.1 and the segment
- *                        parallelism of 2.3): a segment of c > 14 64-token chunks is cut
- *                        on chunk boundaries into ceil(c / 14) near-equal pieces.  How a
+ *                        parallelism of 2.3): a segment of c > 16 64-token chunks is cut
+ *                        on chunk boundaries into ceil(c / 16) near-equal pieces.  How a
  *                        segment is cut depends on its length only, so its pair does
  *                        not depend on the other segments of the call.  Without it (or
  *                        where the query returns 0) every segment is one serial chain.
@@ -139,8 +139,8 @@ hypic_status hypic_segment_build(const hypic_dims* dims, int32_t n_seg,
 
 /* Bytes of build workspace that let hypic_segment_build cut long segments: non-zero
  * for gate TOKEN with the delta rule, bf16 inputs, d in {64, 128} and n_tokens of at
- * least 896; 0 otherwise (the workspace is then ignored).  Sized for segments that do
- * not overlap: (2 d^2 4 bytes per head) per slot, floor(n_tokens / 896) slots, plus
+ * least 1024; 0 otherwise (the workspace is then ignored).  Sized for segments that do
+ * not overlap: (2 d^2 4 bytes per head) per slot, floor(n_tokens / 1024) slots, plus
  * the plan; a segment whose pieces do not fit is built uncut. */
 size_t hypic_build_workspace_bytes(const hypic_dims* dims, int32_t n_seg, int64_t n_tokens);
 

@@ -95,15 +95,15 @@ def test_unsupported_reported(lib):
 
 def test_build_workspace_size(lib):
     """Build workspace: only for the bf16 gated delta rule at d in {64, 128}, zero below
-    one 896-token piece, growing with the token count."""
+    one 1024-token piece, growing with the token count."""
     assert hb.build_workspace_bytes(16, 128, 128, 128, 100_000) > 0
-    assert hb.build_workspace_bytes(16, 128, 128, 128, 895) == 0
+    assert hb.build_workspace_bytes(16, 128, 128, 128, 1023) == 0
     assert hb.build_workspace_bytes(16, 16, 16, 128, 100_000) == 0
     assert hb.build_workspace_bytes(16, 128, 128, 128, 100_000, in_dtype=hb.F32) == 0
     assert hb.build_workspace_bytes(16, 128, 128, 128, 100_000, gate=hb.GATE_DIAG) == 0
     assert hb.build_workspace_bytes(16, 128, 128, 128, 100_000, delta=False) == 0
-    one = hb.build_workspace_bytes(16, 128, 128, 128, 896)
-    two = hb.build_workspace_bytes(16, 128, 128, 128, 2 * 896)
+    one = hb.build_workspace_bytes(16, 128, 128, 128, 1024)
+    two = hb.build_workspace_bytes(16, 128, 128, 128, 2 * 1024)
     assert two - one == 16 * 2 * 128 * 128 * 4            # one more slot: T planes + S per head
 
 

@@ -213,10 +213,10 @@ def _build_ws(W, begin, end, workspace, t_layout=hb.T_DENSE, want_T=True):
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_cut_segments_match_oracle(d):
-    """Segments longer than 14 chunks are cut into pieces built in parallel and folded by
-    composition: lengths on both sides of the cut points (896 = 14 chunks, 897, 1771 = 28
-    chunks with a ragged tail, 2000 = 3 pieces), short and empty segments in the same call."""
-    lens = [1771, 2000, 896, 897, 64, 1, 1030]
+    """Segments longer than 16 chunks are cut into pieces built in parallel and folded by
+    composition: lengths on both sides of the cut points (1024 = 16 chunks, 1025, 1771 = 28
+    chunks with a ragged tail, 2100 = 3 pieces), short and empty segments in the same call."""
+    lens = [1771, 2100, 1024, 1025, 64, 1, 1100]
     W = wl.make("gdn-16h-d128-32k", stress=True, n_heads=3, d=d, lengths=lens)
     begin = np.concatenate([W.cache_begin, [9]])
     end = np.concatenate([W.cache_end, [9]])
