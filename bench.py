@@ -154,6 +154,7 @@ def main():
                                                               T_cache=Tc, S_cache=Sc, workspace=ws))
 
         built_tokens = cold_tokens
+        prefill_segs = (sb_c, se_c)
         n_segments_composed = W.n_seg
         n_windows = int((W.seam_start >= 0).sum())
         work = {
@@ -179,6 +180,7 @@ def main():
         n_chain, n_step = W.pair_id.shape
         R = torch.zeros((n_chain, H, d, d), device=dev)
         built_tokens = int((W.cache_end - W.cache_begin).sum())
+        prefill_segs = (sb, se)
 
         if layered:
             # the 30 per-layer caches: copies of one untimed earlier build
@@ -229,6 +231,36 @@ def main():
     wall = time.perf_counter() - t0
     timer.collect()
 
+    # After the timed steps: the fused cold prefill of the same (built) segments, with and
+    # without T -- T's share of the linear layer's prefill on these segments (outputs need
+    # each token's prefix state, so these segments are not cut).
+    prefill = None
+    if W.gate == hb.GATE_TOKEN and W.delta and W.in_dtype == "bf16" and d in (64, 128):
+        pb, pe = prefill_segs
+        n_pf = pb.shape[0]
+        pout = torch.empty((W.n_tokens, H, d), device=dev)
+        pS = torch.empty((n_pf, H, d, d), device=dev)
+        pT = torch.empty(tshape(n_pf), device=dev, dtype=tdt)
+        calls = {
+            "with_T": lambda: hb.segment_prefill(q, k, v, g, beta, pb, pe, scale=W.scale, t_layout=t_layout,
+                                                 T_out=pT, S_out=pS, out=pout),
+            "S_only": lambda: hb.segment_prefill(q, k, v, g, beta, pb, pe, scale=W.scale, want_T=False,
+                                                 S_out=pS, out=pout),
+        }
+        ptimer = Timer(torch)
+        for _ in range(2):
+            for fn in calls.values():
+                fn()
+        torch.cuda.synchronize()
+        for _ in range(max(3, min(args.steps, 10))):
+            for name, fn in calls.items():
+                ptimer.run(name, fn)
+        ptimer.collect()
+        pt = {name: ptimer.totals[name] / ptimer.counts[name] for name in calls}
+        prefill = {"with_T_us": round(pt["with_T"] * 1e6, 2), "S_only_us": round(pt["S_only"] * 1e6, 2),
+                   "T_overhead": round(pt["with_T"] / pt["S_only"] - 1, 4),
+                   "tokens_per_s_with_T": round(built_tokens / pt["with_T"], 1)}
+
     kern = {}
     for name, tot in timer.totals.items():
         avg = tot / timer.counts[name]
@@ -267,6 +299,8 @@ def main():
         "kernels": kern,
         "roofline": roofline,
     }
+    if prefill is not None:
+        line["prefill"] = prefill
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(W)
     print(json.dumps(line), flush=True)

@@ -20,7 +20,8 @@ GATE_HEAD, GATE_TOKEN, GATE_DIAG = 0, 1, 2
 F32, BF16 = 0, 1
 T_DENSE, T_SCALAR, T_SPLIT, T_DIAG = 0, 1, 2, 3
 
-EXPORTED = ("hypic_segment_build", "hypic_build_workspace_bytes", "hypic_compose", "hypic_seam_advance",
+EXPORTED = ("hypic_segment_build", "hypic_build_workspace_bytes", "hypic_segment_prefill", "hypic_compose",
+            "hypic_seam_advance",
             "hypic_seam_workspace_bytes", "hypic_last_error", "hypic_abi_version", "hypic_selftest_layouts")
 
 
@@ -52,6 +53,8 @@ def load_library(path: str = LIB_PATH):
     lib.hypic_segment_build.argtypes = [D, I32, P, P, I64, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.hypic_segment_build.restype = ctypes.c_int
     lib.hypic_build_workspace_bytes.argtypes = [D, I32, I64]
+    lib.hypic_segment_prefill.argtypes = [D, I32, P, P, I64, P, P, P, P, P, ctypes.c_float, P, P, P, P]
+    lib.hypic_segment_prefill.restype = ctypes.c_int
     lib.hypic_build_workspace_bytes.restype = ctypes.c_size_t
     lib.hypic_compose.argtypes = [D, I32, I32, P, I32, P, P, P, P]
     lib.hypic_compose.restype = ctypes.c_int
@@ -181,6 +184,40 @@ def segment_build(k, v, g, beta, seg_begin, seg_end, *, gate, delta, t_layout=T_
                                    _ptr(S_out), _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                    _stream(stream)))
     return T_out, S_out
+
+
+def segment_prefill(q, k, v, g, beta, seg_begin, seg_end, *, scale, t_layout=T_DENSE, want_T=True, T_out=None,
+                    S_out=None, out=None, stream=None):
+    """Cold prefill of every segment in isolation -- hypic_segment_prefill: the pair
+    (T_C, S(C|0)) and every token's output out[t] = S_t^T (scale q_t) (fp32 [n_tok][H][d_v];
+    rows of tokens outside the segments are left as they are)."""
+    lib = load_library()
+    _dev(k, "k")
+    n_tok, H, dk = k.shape
+    dv = v.shape[2]
+    dt = _in_dtype(k)
+    _dev(q, "q", k.dtype, (n_tok, H, dk))
+    _dev(v, "v", k.dtype, (n_tok, H, dv))
+    _dev(g, "g", k.dtype, (n_tok, H))
+    _dev(beta, "beta", k.dtype, (n_tok, H))
+    _dev(seg_begin, "seg_begin", torch.int64)
+    n_seg = seg_begin.shape[0]
+    _dev(seg_end, "seg_end", torch.int64, (n_seg,))
+    if S_out is None:
+        S_out = torch.empty((n_seg, H, dk, dv), device=k.device, dtype=torch.float32)
+    _dev(S_out, "S_out", torch.float32, (n_seg, H, dk, dv))
+    if want_T and T_out is None:
+        T_out = torch.empty(_t_shape(t_layout, n_seg, H, dk), device=k.device, dtype=_t_dtype(t_layout))
+    if T_out is not None:
+        _dev(T_out, "T_out", _t_dtype(t_layout), _t_shape(t_layout, n_seg, H, dk))
+    if out is None:
+        out = torch.zeros((n_tok, H, dv), device=k.device, dtype=torch.float32)
+    _dev(out, "out", torch.float32, (n_tok, H, dv))
+    d = make_dims(H, dk, dv, gate=GATE_TOKEN, delta=True, in_dtype=dt, t_layout=t_layout)
+    _check(lib.hypic_segment_prefill(ctypes.byref(d), n_seg, _ptr(seg_begin), _ptr(seg_end), n_tok, _ptr(q), _ptr(k),
+                                     _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(T_out), _ptr(S_out), _ptr(out),
+                                     _stream(stream)))
+    return T_out, S_out, out
 
 
 def compose(T_cache, S_cache, pair_id, S_run, *, t_layout=None, stream=None):

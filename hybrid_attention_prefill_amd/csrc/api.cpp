@@ -113,7 +113,8 @@ hypic_status hypic_segment_build(const hypic_dims* dims, int32_t n_seg, const in
         }
         return from_hip(hypic::build_gdn(dims->d_k, bf16, n_seg, dims->n_heads, seg_begin, seg_end,
                                          n_tokens, k, v, g, beta, T_out,
-                                         dims->t_layout == HYPIC_T_SPLIT, S_out, hypic::BuildItems{}, st),
+                                         dims->t_layout == HYPIC_T_SPLIT, S_out, hypic::BuildItems{},
+                                         hypic::BuildOut{}, st),
                         "hypic_segment_build");
     }
     if (dims->delta && dims->gate == HYPIC_GATE_DIAG) {
@@ -123,6 +124,35 @@ hypic_status hypic_segment_build(const hypic_dims* dims, int32_t n_seg, const in
     }
     return fail(HYPIC_E_UNSUPPORTED, "hypic_segment_build: gate %d with delta %d is not implemented",
                 dims->gate, dims->delta);
+}
+
+hypic_status hypic_segment_prefill(const hypic_dims* dims, int32_t n_seg, const int64_t* seg_begin,
+                                   const int64_t* seg_end, int64_t n_tokens, const void* q, const void* k,
+                                   const void* v, const void* g, const void* beta, float scale, void* T_out,
+                                   float* S_out, float* out, void* stream)
+{
+    if (hypic_status s = check_dims(dims)) return s;
+    if (n_seg < 0) return fail(HYPIC_E_INVALID, "n_seg must be >= 0 (got %d)", n_seg);
+    if (n_tokens < 0) return fail(HYPIC_E_INVALID, "n_tokens must be >= 0");
+    if (n_seg == 0) return ok();
+    if (!seg_begin || !seg_end) return fail(HYPIC_E_INVALID, "seg_begin / seg_end is NULL");
+    if (!S_out || !out) return fail(HYPIC_E_INVALID, "S_out or out is NULL");
+    if (n_tokens > 0 && (!q || !k || !v || !g || !beta)) return fail(HYPIC_E_INVALID, "q, k, v, g or beta is NULL");
+    if ((long long)n_seg * dims->n_heads > kMaxGrid) return fail(HYPIC_E_INVALID, "n_seg * n_heads too large");
+    if (dims->gate != HYPIC_GATE_TOKEN || !dims->delta || dims->in_dtype != HYPIC_BF16 || dims->d_k != dims->d_v ||
+        (dims->d_k != 64 && dims->d_k != 128))
+        return fail(HYPIC_E_UNSUPPORTED,
+                    "hypic_segment_prefill: implemented for gate TOKEN with the delta rule, bf16, d_k = d_v in {64, 128}");
+    if (dims->t_layout != HYPIC_T_DENSE && dims->t_layout != HYPIC_T_SPLIT)
+        return fail(HYPIC_E_INVALID, "hypic_segment_prefill: T layout DENSE or SPLIT");
+    hypic::BuildOut ob;
+    ob.q = q;
+    ob.scale = scale;
+    ob.out = out;
+    return from_hip(hypic::build_gdn(dims->d_k, true, n_seg, dims->n_heads, seg_begin, seg_end, n_tokens, k, v, g,
+                                     beta, T_out, dims->t_layout == HYPIC_T_SPLIT, S_out, hypic::BuildItems{}, ob,
+                                     reinterpret_cast<hipStream_t>(stream)),
+                    "hypic_segment_prefill");
 }
 
 hypic_status hypic_compose(const hypic_dims* dims, int32_t n_chain, int32_t n_step, const int32_t* pair_id,

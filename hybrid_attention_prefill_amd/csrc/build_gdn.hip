@@ -62,6 +62,17 @@ struct alignas(16) GdnSmem {
     float bC;
 };
 
+// LDS of the per-token outputs (OUT): q of this or the next chunk as loaded (bf16,
+// token-major, direct global->LDS), q of this chunk as an fp16 operand plane like Kr, and the masked
+// product M = scale (Q K^T o e^{b_t - b_s}, s <= t) as an fp16 operand plane.
+template <int D>
+struct alignas(16) GdnOutSmem {
+    static constexpr int KP = D < 32 ? 32 : D;
+    uint16_t Qraw[2][CH * D];      // by chunk parity
+    uint16_t Qr[1][CH * KP];
+    uint16_t Mq[1][CH * CH];
+};
+
 // LDS operand planes are fragment-ordered (frag_off) with the 16-byte chunks XOR-swizzled:
 // chunk c is stored at c ^ ((c >> 4 ^ c >> 7) & 7).  The swizzle permutes chunks within
 // aligned groups of 8, so a fragment read stays one 1 KiB block read conflict-free, while
@@ -119,14 +130,15 @@ __device__ __forceinline__ u32x4 pack8(const uint16_t* x) {
 
 }  // namespace
 
-template <int D, int NSPLIT, bool BF16>
+template <int D, int NSPLIT, bool BF16, bool WANT_T, bool OUT>
 __global__ __launch_bounds__(512) void build_gdn_kernel(
     int n_seg, int H, const int64_t* __restrict__ seg_begin, const int64_t* __restrict__ seg_end,
     int64_t n_tokens, const void* __restrict__ k, const void* __restrict__ v,
     const void* __restrict__ gl, const void* __restrict__ beta, void* __restrict__ T_out, int t_split,
-    float* __restrict__ S_out, BuildItems items)
+    float* __restrict__ S_out, BuildItems items, BuildOut ob)
 {
     using SM = GdnSmem<D, NSPLIT>;
+    static_assert(!OUT || (NSPLIT == 1 && BF16 && D >= 64), "outputs: bf16 inputs, d 64 or 128");
     constexpr int KP = SM::KP;
     constexpr int KSD = KP / 32;            // k-steps over channels
     constexpr int RT = D / 16;              // row tiles of X
@@ -137,6 +149,8 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
     constexpr int WPR = BF16 ? 1 : 2;       // 16-byte words per 8 channels of one token
     static_assert(2 * NBLK <= 512, "one block per thread");
     __shared__ SM sm;
+    __shared__ GdnOutSmem<OUT ? D : 16> so_;   // used only with OUT
+    auto& so = so_;
 
     const int unit = blockIdx.x;
     const int seg = unit / H, h = unit % H;
@@ -165,6 +179,9 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
     auto s_tile = [&](int c) -> bool { return RT % 8 == 0 ? c * 8 >= RT : wave + 8 * c >= RT; };
     auto own_tile = [&](int c) -> bool { return NCT % 8 == 0 || wave + 8 * c < NCT; };
 
+    // WANT_T false (T not requested): only the S columns of X are advanced (the Wt solve
+    // is shared by both)
+    auto upd_tile = [&](int c) -> bool { return own_tile(c) && (WANT_T || s_tile(c)); };
     beg = beg < 0 ? 0 : (beg > n_tokens ? n_tokens : beg);
     end = end < beg ? beg : (end > n_tokens ? n_tokens : end);
 
@@ -240,7 +257,39 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
     };
     auto raw1 = [&](uint32_t x) -> float { return BF16 ? __uint_as_float(x << 16) : __uint_as_float(x); };
 
-    if (beg < end) prefetch(beg);
+    // q of a chunk, global -> LDS direct (16 bytes per lane, token-major; rows past the
+    // segment are clamped into it and masked when converted)
+    auto fetch_q = [&](int64_t c0, int buf) {
+        if constexpr (OUT) {
+            constexpr int NQ = CH * D / 8;   // 16-byte pieces
+#pragma unroll
+            for (int r = 0; r < NQ / 512; ++r) {
+                const int m = r * 512 + wave * 64 + lane;
+                int64_t t = c0 + m / (D / 8);
+                t = t < end ? t : end - 1;
+                const uint16_t* src = reinterpret_cast<const uint16_t*>(ob.q) + (t * H + h) * D + (m % (D / 8)) * 8;
+                __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(so.Qraw[buf] + (r * 512 + wave * 64) * 8),
+                                                 16, 0, 0);
+            }
+        }
+    };
+
+    if (beg < end) {
+        fetch_q(beg, 0);
+        if (beg + CH < end) fetch_q(beg + CH, 1);
+        prefetch(beg);
+    }
+    if constexpr (OUT) {
+        // the output products read M in 32-column blocks: of the tiles above the diagonal,
+        // (0, 1) and (2, 3) fall inside one and stay zero (the others are never read)
+        for (int i = tid; i < 512; i += 512) {
+            const int ti = i < 256 ? 0 : 2, r = (i & 255) >> 4, c = i & 15;
+            so.Mq[0][lds_off(16 * ti + r, 16 * (ti + 1) + c, CH)] = 0;
+        }
+        // the first chunk's q is in LDS before it is staged
+        __builtin_amdgcn_s_waitcnt(0x0070);
+        __syncthreads();
+    }
 
     for (int64_t c0 = beg; c0 < end; c0 += CH) {
         const int n = (int)((end - c0) < CH ? (end - c0) : CH);
@@ -248,6 +297,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
         const int lane_c = opaque(lane);
         const int g4 = lane_c >> 4, n16 = lane_c & 15, lx = lane_c ^ g4;
         const int tb = opaque(tb0), cb = opaque(cb0);
+        const int qbuf = (int)(((c0 - beg) / CH) & 1);
         // ---- 1. stage the chunk: K token-major, K^T and V^T channel-major (16-bit), gates
         if (has_blk) {
             // the 4 x 8 block; rows past the segment are zeroed (only the last chunk has any)
@@ -303,6 +353,24 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                 }
             }
         }
+        if constexpr (OUT) {
+            if (has_blk && blk_v) {   // q block (tb, cb) to the fp16 plane Qr; rows past the segment zeroed
+                auto pk = [](float a, float b) -> unsigned {
+                    return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a, b));
+                };
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = tb * 4 + r;
+                    u32x4 w = *reinterpret_cast<const u32x4*>(&so.Qraw[qbuf][t * D + cb * 8]);
+                    if (t >= n) w = u32x4{0u, 0u, 0u, 0u};
+                    u32x4 o;
+#pragma unroll
+                    for (int x = 0; x < 4; ++x)
+                        o[x] = pk(__uint_as_float(w[x] << 16), __uint_as_float(w[x] & 0xFFFF0000u));
+                    *reinterpret_cast<u32x4*>(&so.Qr[0][lds_off(t, cb * 8, KP)]) = o;
+                }
+            }
+        }
         if (wave == 0) {
             const bool ok = lane < n;
             sm.gate[lane] = ok ? raw1(graw) : 0.f;
@@ -342,6 +410,31 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                 gacc = mma<NSPLIT>(a, bb, gacc);
             }
             return gacc;
+        };
+        // M = scale (Q K^T o e^{b_t - b_s}), s <= t, as an fp16 operand plane, tile by tile:
+        // tile idx = 0..9 is (ti, tj), tj <= ti, row-major over the lower triangle of 16 x 16
+        // tiles (the tiles above it are zero or never read).  Log-decays by lane shuffles of
+        // b2 (every wave holds them; sm.b is written during this phase).
+        auto mq_tile = [&](int idx) {
+            if constexpr (OUT) {
+                const int ti = idx < 1 ? 0 : idx < 3 ? 1 : idx < 6 ? 2 : 3;
+                const int tj = idx - (ti * (ti + 1)) / 2;
+                f32x4 m = zero4();
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks) {
+                    const Frag<1> a = frag_of<1, KP>(so.Qr, ti, ks, lx);
+                    const Frag<1> bb = frag_of<1, KP>(sm.Kr, tj, ks, lx);
+                    m = mma<1>(a, bb, m);
+                }
+                const float bs = __shfl(b2, 16 * tj + n16, 64);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 16 * ti + 4 * g4 + e;
+                    const float bt = __shfl(b2, t, 64);
+                    const float x = (16 * tj + n16 <= t) ? ob.scale * m[e] * __builtin_amdgcn_exp2f(bt - bs) : 0.f;
+                    so.Mq[0][lds_off(t, 16 * tj + n16, CH)] = f16_bits((_Float16)x);
+                }
+            }
         };
         if (wave < 4) {
             const int i = wave;
@@ -405,6 +498,11 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                     Pd[4 * e] = h;
                     Pd[6 * 256 + 4 * e] = lo;
                 }
+            }
+            if constexpr (OUT) {   // waves 4, 5: tiles 0, 4 | 1, 5; waves 6, 7 (one L tile fewer): 2, 6, 8 | 3, 7, 9
+                mq_tile(wave - 4);
+                mq_tile(wave);
+                if (wave >= 6) mq_tile(wave + 2);
             }
         }
         __syncthreads();
@@ -496,6 +594,14 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                 }
             }
         }
+        // q goes two chunks ahead: wait for everything in flight -- the next chunk's q (sent
+        // at this point of the previous chunk), its k, v, g, beta (sent at the end of staging)
+        // and the previous chunk's output stores -- then send q of the chunk after next into
+        // the buffer this chunk's q was converted from
+        if constexpr (OUT) {
+            __builtin_amdgcn_s_waitcnt(0x0070);
+            if (c0 + 2 * CH < end) fetch_q(c0 + 2 * CH, qbuf);
+        }
         __syncthreads();
 
         // ---- 6..8. Y = Wt X, R, X += K^T R for all owned column tiles at once (each A
@@ -508,11 +614,15 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
             for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
                 for (int c = 0; c < CTW; ++c) R[tt][c] = zero4();
+            f32x4 P[OUT ? 4 : 1];   // Q S_0 for this wave's S tile (OUT)
+#pragma unroll
+            for (int tt = 0; tt < (OUT ? 4 : 1); ++tt) P[tt] = zero4();
 #pragma unroll
             for (int kb = 0; kb < KSD; ++kb) {
                 Frag<NSPLIT> xb[CTW];   // rows 32 kb .. 32 kb + 31 of the X column tiles as B fragments
 #pragma unroll
                 for (int c = 0; c < CTW; ++c) {
+                    if (!upd_tile(c)) continue;
                     const f32x4 d0 = X[2 * kb][c];
                     const f32x4 d1 = (2 * kb + 1 < RT) ? X[2 * kb + 1 < RT ? 2 * kb + 1 : 0][c] : zero4();
                     xb[c] = dpair_to_frag<NSPLIT>(d0, d1);
@@ -522,22 +632,59 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                     const Frag<NSPLIT> a = frag_of<NSPLIT, KP>(sm.Wt, tt, kb, lx);
 #pragma unroll
                     for (int c = 0; c < CTW; ++c)
-                        if (own_tile(c)) R[tt][c] = mma<NSPLIT>(a, xb[c], R[tt][c]);
+                        if (upd_tile(c)) R[tt][c] = mma<NSPLIT>(a, xb[c], R[tt][c]);
+                }
+                if constexpr (OUT) {
+#pragma unroll
+                    for (int c = 0; c < CTW; ++c) {
+                        if (!own_tile(c) || !s_tile(c)) continue;
+#pragma unroll
+                        for (int tt = 0; tt < 4; ++tt)
+                            P[tt] = mma<1>(frag_of<1, KP>(so.Qr, tt, kb, lx), xb[c], P[tt]);
+                    }
                 }
             }
             Frag<NSPLIT> rb[2][CTW];
 #pragma unroll
             for (int c = 0; c < CTW; ++c) {
+                if (!upd_tile(c)) continue;
                 const bool is_s = s_tile(c);
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int t = tt * 16 + 4 * g4 + e;
-                        R[tt][c][e] = is_s ? sm.ebr[t] * (U[tt][c][e] - sm.eb[t] * R[tt][c][e]) : -R[tt][c][e];
+                        if (is_s) {   // new values U' = U - diag(e^b) Wt S_0; R = diag(e^{b_C - b}) U'
+                            const float up = U[tt][c][e] - sm.eb[t] * R[tt][c][e];
+                            U[tt][c][e] = up;
+                            R[tt][c][e] = sm.ebr[t] * up;
+                        } else {
+                            R[tt][c][e] = -R[tt][c][e];
+                        }
                     }
                 rb[0][c] = dpair_to_frag<NSPLIT>(R[0][c], R[1][c]);
                 rb[1][c] = dpair_to_frag<NSPLIT>(R[2][c], R[3][c]);
+                if constexpr (OUT) {
+                    if (is_s) {   // o_t = scale e^{b_t} (Q S_0)_t + (M U')_t for the tile's 16 value columns
+                        const Frag<1> ub0 = dpair_to_frag<1>(U[0][c], U[1][c]);
+                        const Frag<1> ub1 = dpair_to_frag<1>(U[2][c], U[3][c]);
+                        const int vq = wave + 8 * c - RT;
+#pragma unroll
+                        for (int tt = 0; tt < 4; ++tt) {
+                            f32x4 o;
+                            const f32x4 ebt = *reinterpret_cast<const f32x4*>(&sm.eb[tt * 16 + 4 * g4]);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) o[e] = ob.scale * ebt[e] * P[tt][e];
+                            o = mma<1>(frag_of<1, CH>(so.Mq, tt, 0, lx), ub0, o);
+                            if (tt >= 2) o = mma<1>(frag_of<1, CH>(so.Mq, tt, 1, lx), ub1, o);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const int t = tt * 16 + 4 * g4 + e;
+                                if (t < n) ob.out[((size_t)(c0 + t) * H + h) * D + vq * 16 + n16] = o[e];
+                            }
+                        }
+                    }
+                }
                 if (is_s) {
 #pragma unroll
                     for (int rt = 0; rt < RT; ++rt) X[rt][c] *= ebC;
@@ -550,7 +697,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                     const Frag<NSPLIT> a = frag_of<NSPLIT, CH>(sm.Kt, rt, kb, lx);
 #pragma unroll
                     for (int c = 0; c < CTW; ++c)
-                        if (own_tile(c)) X[rt][c] = mma<NSPLIT>(a, rb[kb][c], X[rt][c]);
+                        if (upd_tile(c)) X[rt][c] = mma<NSPLIT>(a, rb[kb][c], X[rt][c]);
                 }
         }
         log_s += bC;
@@ -578,27 +725,38 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
 
 }
 
-template <int D, int NSPLIT, bool BF16>
+template <int D, int NSPLIT, bool BF16, bool OUT>
 static hipError_t launch_gdn(int n_seg, int H, const int64_t* sb, const int64_t* se, int64_t n_tok,
                              const void* k, const void* v, const void* g, const void* beta,
-                             void* T_out, bool t_split, float* S_out, const BuildItems& items, hipStream_t st)
+                             void* T_out, bool t_split, float* S_out, const BuildItems& items,
+                             const BuildOut& ob, hipStream_t st)
 {
-    hipLaunchKernelGGL((build_gdn_kernel<D, NSPLIT, BF16>), dim3(n_seg * H), dim3(512), 0, st, n_seg,
-                       H, sb, se, n_tok, k, v, g, beta, T_out, (int)t_split, S_out, items);
+    // pieces of cut segments always produce T (the fold needs it)
+    if (T_out != nullptr || items.out != nullptr)
+        hipLaunchKernelGGL((build_gdn_kernel<D, NSPLIT, BF16, true, OUT>), dim3(n_seg * H), dim3(512), 0, st, n_seg,
+                           H, sb, se, n_tok, k, v, g, beta, T_out, (int)t_split, S_out, items, ob);
+    else
+        hipLaunchKernelGGL((build_gdn_kernel<D, NSPLIT, BF16, false, OUT>), dim3(n_seg * H), dim3(512), 0, st, n_seg,
+                           H, sb, se, n_tok, k, v, g, beta, T_out, (int)t_split, S_out, items, ob);
     return hipGetLastError();
 }
 
 hipError_t build_gdn(int d, bool in_bf16, int n_seg, int H, const int64_t* sb, const int64_t* se,
                      int64_t n_tok, const void* k, const void* v, const void* g, const void* beta,
-                     void* T_out, bool t_split, float* S_out, const BuildItems& items, hipStream_t st)
+                     void* T_out, bool t_split, float* S_out, const BuildItems& items, const BuildOut& ob,
+                     hipStream_t st)
 {
-#define HYPIC_GDN(D_, NS_, BF_)                                                                          \
-    if (d == D_ && in_bf16 == BF_)                                                                       \
-        return launch_gdn<D_, NS_, BF_>(n_seg, H, sb, se, n_tok, k, v, g, beta, T_out, t_split, S_out, items, st);
-    HYPIC_GDN(128, 1, true)
-    HYPIC_GDN(64, 1, true)
-    HYPIC_GDN(16, 2, false)
-    HYPIC_GDN(16, 1, true)
+    const bool out = ob.out != nullptr;
+#define HYPIC_GDN(D_, NS_, BF_, OUT_)                                                                     \
+    if (d == D_ && in_bf16 == BF_ && out == OUT_)                                                         \
+        return launch_gdn<D_, NS_, BF_, OUT_>(n_seg, H, sb, se, n_tok, k, v, g, beta, T_out, t_split, S_out, \
+                                              items, ob, st);
+    HYPIC_GDN(128, 1, true, false)
+    HYPIC_GDN(128, 1, true, true)
+    HYPIC_GDN(64, 1, true, false)
+    HYPIC_GDN(64, 1, true, true)
+    HYPIC_GDN(16, 2, false, false)
+    HYPIC_GDN(16, 1, true, false)
 #undef HYPIC_GDN
     return hipErrorNotSupported;
 }

@@ -316,7 +316,7 @@ hipError_t build_gdn_split(int d, bool in_bf16, int n_seg, int H, const int64_t*
 {
     const SplitLayout L = split_layout(d, H, n_seg, n_tok);
     if (L.total == 0 || ws == nullptr || (long long)L.n_items_max * H > 0x7fffffffLL)
-        return build_gdn(d, in_bf16, n_seg, H, sb, se, n_tok, k, v, g, beta, T_out, t_split, S_out, BuildItems{}, st);
+        return build_gdn(d, in_bf16, n_seg, H, sb, se, n_tok, k, v, g, beta, T_out, t_split, S_out, BuildItems{}, BuildOut{}, st);
     const SplitPlan pl = carve(ws, L);
     hipLaunchKernelGGL(plan_pieces_kernel, dim3(1), dim3(1024), 0, st, n_seg, sb, se, n_tok, L.p_ws, L.max_cut, pl);
     hipError_t e = hipGetLastError();
@@ -326,7 +326,8 @@ hipError_t build_gdn_split(int d, bool in_bf16, int n_seg, int H, const int64_t*
     it.out = pl.out;
     it.T_ws = pl.T_ws;
     it.S_ws = pl.S_ws;
-    e = build_gdn(d, in_bf16, L.n_items_max, H, pl.ib, pl.ie, n_tok, k, v, g, beta, T_out, t_split, S_out, it, st);
+    e = build_gdn(d, in_bf16, L.n_items_max, H, pl.ib, pl.ie, n_tok, k, v, g, beta, T_out, t_split, S_out, it,
+                  BuildOut{}, st);
     if (e != hipSuccess) return e;
     const int grid = xcd_grid_size(L.max_cut * H, 2 * d / 64);
     if (d == 128)

@@ -36,10 +36,19 @@ struct BuildItems {
     void* T_ws = nullptr;
     float* S_ws = nullptr;
 };
+// Per-token outputs of the GDN build (out != NULL; bf16 inputs, d 64 or 128, uncut):
+// out[t][h][:] = S_t^T (scale q_t), S_t the state after token t from S = 0 at the
+// segment's first token.
+struct BuildOut {
+    const void* q = nullptr;
+    float scale = 0.f;
+    float* out = nullptr;
+};
 // build_gdn.hip (scalar gate, delta rule)
 hipError_t build_gdn(int d, bool in_bf16, int n_seg, int H, const int64_t* sb, const int64_t* se,
                      int64_t n_tok, const void* k, const void* v, const void* g, const void* beta,
-                     void* T_out, bool t_split, float* S_out, const BuildItems& items, hipStream_t st);
+                     void* T_out, bool t_split, float* S_out, const BuildItems& items, const BuildOut& ob,
+                     hipStream_t st);
 
 // build_split.hip: long segments built as pieces in parallel and folded by composition
 // (GDN, d in {64, 128}).  Workspace bytes for (d, H, n_seg, n_tokens); 0 = never cut.

@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define HYPIC_ABI_VERSION 5
+#define HYPIC_ABI_VERSION 6
 
 typedef enum {
     HYPIC_OK = 0,
@@ -143,6 +143,27 @@ hypic_status hypic_segment_build(const hypic_dims* dims, int32_t n_seg,
  * not overlap: (2 d^2 4 bytes per head) per slot, floor(n_tokens / 1024) slots, plus
  * the plan; a segment whose pieces do not fit is built uncut. */
 size_t hypic_build_workspace_bytes(const hypic_dims* dims, int32_t n_seg, int64_t n_tokens);
+
+/*
+ * hypic_segment_prefill -- a segment's first (cold) prefill through the linear layer
+ * with the pair built on the way ([ZH] 2.1: the pair is cached at the segment's first
+ * prefill; each segment is prefilled in isolation, its state starting from zero): for
+ * every segment i, head h and token t of [seg_begin[i], seg_end[i]),
+ *     out[t][h][:] = S_t^T (scale * q_t),
+ * S_t the state after token t (the first token starts from S = 0), plus the pair as
+ * hypic_segment_build writes it (T_out may be NULL).  Rows of tokens outside the segments
+ * are not written; segments must not overlap.  Segments are not cut (the outputs need
+ * every token's prefix state).
+ *   q     : [n_tokens][H][d_k], dtype in_dtype
+ *   out   : fp32 [n_tokens][H][d_v]
+ * Implemented: gate TOKEN, delta 1 or 2, bf16 inputs, d_k == d_v in {64, 128}; T layout
+ * DENSE or SPLIT.  Other combinations return HYPIC_E_UNSUPPORTED.
+ */
+hypic_status hypic_segment_prefill(const hypic_dims* dims, int32_t n_seg,
+                                   const int64_t* seg_begin, const int64_t* seg_end,
+                                   int64_t n_tokens, const void* q, const void* k, const void* v,
+                                   const void* g, const void* beta, float scale,
+                                   void* T_out, float* S_out, float* out, void* stream);
 
 /*
  * hypic_compose -- reuse of cached pairs ([ZH] 2.1: left-multiply by T_C,

@@ -272,3 +272,35 @@ def test_overlapping_segments_beyond_workspace_built_uncut():
     assert_pairs_close(T.cpu().numpy(), S.cpu().numpy(), T0, S0, TOL["bf16"], W.name)
     Tu, Su = _build_ws(W, begin, end, None)
     assert not torch.equal(S[0], Su[0]) and torch.equal(S[3], Su[3])   # first cut, last uncut
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("stress", [False, True])
+@pytest.mark.parametrize("want_T", [True, False])
+def test_prefill_outputs(d, stress, want_T):
+    """Cold prefill of each segment in isolation: every token's output S_t^T (scale q_t)
+    and the pair, against the oracle's recurrence per segment (several chunks, ragged
+    tails, one token, an empty segment); tokens outside the segments stay untouched."""
+    lens = [300, 129, 1, 64, 200]
+    W = wl.make("gdn-16h-d128-32k", stress=stress, n_heads=3, d=d, lengths=lens)
+    # segments [0, 300) [307, 436) [436, 437) [437, 501) [501, 694) and an empty one;
+    # tokens [300, 307) belong to none
+    begin = np.array([0, 307, 436, 437, 501, 436], dtype=np.int64)
+    end = np.array([300, 436, 437, 501, 694, 436], dtype=np.int64)
+    assert W.n_tokens == 694
+    x = workload_tensors(W)
+    out0 = torch.full((W.n_tokens, 3, d), 7.0, device="cuda")
+    print(W.name, d, "prefill", stress, want_T, flush=True)
+    T, S, out = hb.segment_prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], dev(begin, torch.int64),
+                                   dev(end, torch.int64), scale=W.scale, want_T=want_T, out=out0)
+    torch.cuda.synchronize()
+    T0, S0 = oracle.segment_build(W.k, W.v, W.g, W.beta, begin, end, gate=W.gate, delta=W.delta)
+    assert_pairs_close(T.cpu().numpy() if want_T else None, S.cpu().numpy(), T0, S0, TOL["bf16"], W.name)
+    o = out.cpu().numpy().astype(np.float64)
+    for b, e in zip(begin, end):
+        if e == b:
+            continue
+        _, ref = oracle.run(W.k, W.v, W.g, W.beta, gate=W.gate, delta=W.delta, t0=b, t1=e, q=W.q, scale=W.scale)
+        err = np.linalg.norm(o[b:e] - ref, axis=(0, 2)) / np.linalg.norm(ref, axis=(0, 2))
+        assert err.max() <= TOL["bf16"], f"segment [{b}, {e}): output rel_F {err.max():.2e}"
+    assert np.all(o[300:307] == 7.0)
