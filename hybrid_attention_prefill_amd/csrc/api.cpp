@@ -176,7 +176,7 @@ hypic_status hypic_compose(const hypic_dims* dims, int32_t n_chain, int32_t n_st
                         "hypic_compose");
     if (dims->d_k != dims->d_v) return fail(HYPIC_E_UNSUPPORTED, "d_k != d_v is not implemented");
     return from_hip(hypic::compose_dense(dims->d_k, n_chain, dims->n_heads, n_step, pair_id, n_pair, T_cache,
-                                         dims->t_layout == HYPIC_T_SPLIT, S_cache, S_run, st),
+                                         dims->t_layout == HYPIC_T_SPLIT, S_cache, S_run, nullptr, st),
                     "hypic_compose");
 }
 
@@ -184,7 +184,7 @@ size_t hypic_seam_workspace_bytes(const hypic_dims* dims, int32_t n_chain, int32
 {
     if (!dims || dims->n_heads < 1 || !valid_d(dims->d_k) || dims->d_k != dims->d_v) return 0;
     if (n_chain < 0 || n_step < 0 || w < 1 || w > 16) return 0;
-    return (size_t)n_chain * n_step * dims->n_heads * hypic::seam_record_bytes(dims->d_k);
+    return hypic::seam_plan(dims->d_k, n_chain, dims->n_heads, n_step, w).bytes;
 }
 
 hypic_status hypic_seam_advance(const hypic_dims* dims, int32_t n_chain, int32_t n_step, int32_t w,
@@ -215,14 +215,33 @@ hypic_status hypic_seam_advance(const hypic_dims* dims, int32_t n_chain, int32_t
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(HYPIC_E_INVALID, "workspace must be 256-byte aligned");
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const bool bf16 = dims->in_dtype == HYPIC_BF16;
-    void* ws = workspace;
-    hipError_t e = hypic::seam_prep(dims->d_k, n_chain, n_step, dims->n_heads, seam_start, n_tokens, w, q, k, v,
-                                    g, beta, bf16, scale, ws, st);
+    const int d = dims->d_k, H = dims->n_heads;
+    const hypic::SeamPlan pl = hypic::seam_plan(d, n_chain, H, n_step, w);
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    hipError_t e = hypic::seam_prep(d, n_chain, n_step, H, seam_start, n_tokens, w, q, k, v, g, beta, bf16, scale,
+                                    ws, st);
     if (e != hipSuccess) return from_hip(e, "hypic_seam_advance (window preparation)");
     hypic::SeamArgs sa{seam_start, n_tokens, w, (int)bf16, scale, q, k, ws, out};
-    return from_hip(hypic::seam_chain(dims->d_k, n_chain, dims->n_heads, n_step, pair_id, pair_id ? n_pair : 0,
-                                      T_cache, dims->t_layout == HYPIC_T_SPLIT, S_cache, S_run, sa, st),
-                    "hypic_seam_advance");
+    sa.nblk = pl.nblk;
+    sa.blk = pl.blk;
+    if (pl.nblk > 1) {
+        sa.ox = reinterpret_cast<float*>(ws + pl.ox_off);
+        sa.agg_T = ws + pl.agg_t_off;
+        sa.agg_S = reinterpret_cast<float*>(ws + pl.agg_s_off);
+    }
+    const int np = pair_id ? n_pair : 0;
+    e = hypic::seam_chain(d, pl.nb, n_chain, H, n_step, pair_id, np, T_cache, dims->t_layout == HYPIC_T_SPLIT,
+                          S_cache, S_run, sa, st);
+    if (e != hipSuccess || pl.nblk == 1) return from_hip(e, "hypic_seam_advance");
+    // blocked scan: block aggregates composed in order (the state entering every block
+    // kept), then the windows of blocks >= 1 read out from those states
+    float* trail = reinterpret_cast<float*>(ws + pl.trail_off);
+    e = hypic::compose_dense(d, n_chain, H, pl.nblk - 1, nullptr, n_chain * (pl.nblk - 1), sa.agg_T, true, sa.agg_S,
+                             S_run, trail, st);
+    if (e != hipSuccess) return from_hip(e, "hypic_seam_advance (composition of the block aggregates)");
+    return from_hip(hypic::seam_readout(d, n_chain, H, n_step, pl.nblk, pl.blk, w, seam_start, n_tokens, sa.ox, trail,
+                                        out, st),
+                    "hypic_seam_advance (window outputs)");
 }
 
 // Diagnostic: runs the lane-layout self-test kernel into a device buffer of

@@ -34,7 +34,7 @@ constexpr int chain_waves(int dk) { return dk >= 128 ? 8 : 4; }
 template <int DK, int DV, int NB, bool TS>
 __global__ __launch_bounds__(64 * chain_waves(DK)) void compose_dense_kernel(
     int n_units, int H, int n_step, const int32_t* __restrict__ pair_id, int n_pair,
-    const void* __restrict__ Tc, const float* __restrict__ Sc, float* __restrict__ Srun)
+    const void* __restrict__ Tc, const float* __restrict__ Sc, float* __restrict__ Srun, float* __restrict__ trail)
 {
     constexpr int NCB = DV / NB;
     constexpr int KP = DK < 32 ? 32 : DK;   // contraction length padded to the MFMA K
@@ -123,13 +123,29 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void compose_dense_kernel(
         float ta[TS ? 1 : RTW][TS ? 1 : KS][8];        // T rows, fp32
         float sv[RTW][CT][4];                          // S block (D layout)
     };
-    const int32_t* ids = pair_id + (size_t)c * n_step;
+    // without an id array, step j of chain c applies pair c * n_step + j
+    const int32_t* ids = pair_id ? pair_id + (size_t)c * n_step : nullptr;
     // Pair ids go through an LDS ring of 512 steps, filled 256 steps ahead, so the per-step
     // lookups are LDS reads and never wait on the vector-memory counter.
     auto fill_ring = [&](int base) {   // steps [base, base + 256)
         for (int x = threadIdx.x; x < kRingFill; x += blockDim.x) {
             const int j = base + x;
-            ring_id[j & (kRing - 1)] = j < n_step ? ids[j] : -1;
+            ring_id[j & (kRing - 1)] = j < n_step ? (ids ? ids[j] : c * n_step + j) : -1;
+        }
+    };
+    // the state before step j, when the caller keeps the trail
+    auto put_trail = [&](int j) {
+        if (!trail) return;
+        float* Tr = trail + (((size_t)c * n_step + j) * H + h) * DK * DV + cb * NB;
+#pragma unroll
+        for (int i = 0; i < RTW; ++i) {
+            const int rt = wave + NW * i;
+            if (rt >= RT) continue;
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    Tr[(size_t)(rt * 16 + 4 * g4 + e) * DV + ct * 16 + n16] = acc[i][ct][e];
         }
     };
     auto read_id = [&](int j) -> int { return ring_id[j & (kRing - 1)]; };
@@ -249,12 +265,14 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void compose_dense_kernel(
         }
         const int id2 = read_id(j + 2);
         if (j + 1 < n_step) load_step(id1, sB);
+        put_trail(j);
         run_step(sA);
         if (j + 1 >= n_step) break;
         // step j+1 from sB; prefetch step j+2 into sA; id of step j+3
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         id1 = read_id(j + 3);
         if (j + 2 < n_step) load_step(id2, sA);
+        put_trail(j + 1);
         run_step(sB);
     }
 
@@ -303,12 +321,12 @@ __global__ __launch_bounds__(256) void compose_scalar_kernel(
 // ---------------------------------------------------------------- launchers
 template <int DK, int DV, int NB, bool TS>
 static hipError_t launch_dense(int n_chain, int H, int n_step, const int32_t* pair_id, int n_pair,
-                               const void* Tc, const float* Sc, float* Srun, hipStream_t st)
+                               const void* Tc, const float* Sc, float* Srun, float* trail, hipStream_t st)
 {
     const int n_units = n_chain * H;
     const int grid = xcd_grid_size(n_units, DV / NB);
     hipLaunchKernelGGL((compose_dense_kernel<DK, DV, NB, TS>), dim3(grid), dim3(64 * chain_waves(DK)), 0, st,
-                       n_units, H, n_step, pair_id, n_pair, Tc, Sc, Srun);
+                       n_units, H, n_step, pair_id, n_pair, Tc, Sc, Srun, trail);
     return hipGetLastError();
 }
 
@@ -322,13 +340,15 @@ static int pick_nb(long long n_units, int dv)
 }
 
 hipError_t compose_dense(int d, int n_chain, int H, int n_step, const int32_t* pair_id, int n_pair,
-                         const void* Tc, bool t_split, const float* Sc, float* Srun, hipStream_t st)
+                         const void* Tc, bool t_split, const float* Sc, float* Srun, float* trail,
+                         hipStream_t st)
 {
     const int nb = pick_nb((long long)n_chain * H, d);
-#define HYPIC_CASE(D_, NB_)                                                                                    \
-    if (d == D_ && nb == NB_)                                                                                  \
-        return t_split ? launch_dense<D_, D_, NB_, true>(n_chain, H, n_step, pair_id, n_pair, Tc, Sc, Srun, st) \
-                       : launch_dense<D_, D_, NB_, false>(n_chain, H, n_step, pair_id, n_pair, Tc, Sc, Srun, st);
+#define HYPIC_CASE(D_, NB_)                                                                                   \
+    if (d == D_ && nb == NB_)                                                                                 \
+        return t_split                                                                                        \
+                   ? launch_dense<D_, D_, NB_, true>(n_chain, H, n_step, pair_id, n_pair, Tc, Sc, Srun, trail, st) \
+                   : launch_dense<D_, D_, NB_, false>(n_chain, H, n_step, pair_id, n_pair, Tc, Sc, Srun, trail, st);
     HYPIC_CASE(16, 16)
     HYPIC_CASE(32, 32) HYPIC_CASE(32, 16)
     HYPIC_CASE(64, 64) HYPIC_CASE(64, 32) HYPIC_CASE(64, 16)

@@ -16,12 +16,31 @@ struct SeamArgs {
     const void* k;
     const void* ws;             // records of seam_prep (seam_layout.h)
     float* out;                 // [n_chain][n_step][w][H][d_v]
+    // blocked scan (nblk > 1): blocks of blk steps run at once (seam_chain.hip)
+    int nblk = 1;
+    int blk = 0;
+    float* ox = nullptr;        // readouts of X at the windows: [n_chain][n_step][w][H][2 d_v]
+    void* agg_T = nullptr;      // block aggregates, T as bf16 hi/lo planes [n_chain][nblk-1][H][2][d][d]
+    float* agg_S = nullptr;     //                   S fp32 [n_chain][nblk-1][H][d][d]
+};
+
+// Launch plan of hypic_seam_advance and the byte offsets of its workspace parts:
+// window records at 0, then (blocked scan only) the readouts, aggregates and the
+// trail of block entry states.
+struct SeamPlan {
+    int nb;        // state columns per workgroup of the chain kernel
+    int nblk;      // blocks of steps per chain (1: the plain chain)
+    int blk;       // steps per block
+    size_t ox_off, agg_t_off, agg_s_off, trail_off, bytes;
 };
 
 // compose.hip
 // t_split: T as bf16 hi/lo planes [n_pair][H][2][d][d]; else fp32 [n_pair][H][d][d]
+// pair_id NULL: step j of chain c applies pair c * n_step + j.  trail (may be NULL): the
+// state before each step, fp32 [n_chain][n_step][H][d][d].
 hipError_t compose_dense(int d, int n_chain, int H, int n_step, const int32_t* pair_id, int n_pair,
-                         const void* Tc, bool t_split, const float* Sc, float* Srun, hipStream_t st);
+                         const void* Tc, bool t_split, const float* Sc, float* Srun, float* trail,
+                         hipStream_t st);
 // diag: T cached as fp32 [n_pair][H][dk] (T = diag(t)); else fp32 [n_pair][H] (T = t I)
 hipError_t compose_scalar(int dk, int dv, bool diag, int n_chain, int H, int n_step, const int32_t* pair_id,
                           int n_pair, const float* Tc, const float* Sc, float* Srun, hipStream_t st);
@@ -75,9 +94,13 @@ hipError_t seam_prep(int d, int n_chain, int n_step, int H, const int64_t* seam_
 size_t seam_record_bytes(int d);
 
 // seam_chain.hip (pair_id may be NULL: windows only)
-hipError_t seam_chain(int d, int n_chain, int H, int n_step, const int32_t* pair_id, int n_pair,
+SeamPlan seam_plan(int d, int n_chain, int H, int n_step, int w);
+hipError_t seam_chain(int d, int nb, int n_chain, int H, int n_step, const int32_t* pair_id, int n_pair,
                       const void* Tc, bool t_split, const float* Sc, float* Srun, const SeamArgs& sa,
                       hipStream_t st);
+hipError_t seam_readout(int d, int n_chain, int H, int n_step, int nblk, int blk, int w,
+                        const int64_t* seam_start, int64_t n_tokens, const float* ox, const float* trail,
+                        float* out, hipStream_t st);
 
 // selftest.hip
 hipError_t selftest_layouts(const float* in, float* out, hipStream_t st);

@@ -18,10 +18,10 @@ pytestmark = pytest.mark.gpu
 TOL = {"f32": 1e-4, "bf16": 5e-3}
 
 
-def _seam_workload(name, lens, w, H, stress=False):
+def _seam_workload(name, lens, w, H, stress=False, **extra):
     """A prompt shaped like workload `name` with explicit segment lengths, seams at
     internal segments."""
-    kw = dict(n_heads=H, lengths=lens, stress=stress)
+    kw = dict(n_heads=H, lengths=lens, stress=stress, **extra)
     W = wl.make(name, **kw)
     starts = W.seg_start
     W.cache_begin = starts[:-1].copy()
@@ -125,3 +125,86 @@ def test_gdn_100k_prompt_full():
     S_ref, outs_ref = _reference(W)
     worst = _check(W, R, out, S_ref, outs_ref, TOL["bf16"])
     print(f"100k prompt: final state rel_F {rel_f(R, S_ref).max():.2e}, worst window output {worst:.2e}")
+
+
+# ---- long chains: the call runs as a blocked scan (blocks of steps at once, block
+# aggregates composed in order, window outputs read out from the block entry states)
+
+def _short_lengths(rng, n, w, lo=20, hi=60):
+    return list(int(x) for x in rng.integers(lo, hi, size=n) + w)
+
+
+@pytest.mark.parametrize("stress,t_layout", [(False, hb.T_SPLIT), (True, hb.T_SPLIT), (True, hb.T_DENSE)])
+def test_seam_scan_many_steps(stress, t_layout):
+    rng = np.random.default_rng(11)
+    W = _seam_workload("gdn-16h-d128-32k", _short_lengths(rng, 40, 8), 8, H=2, stress=stress)
+    print(W.name, "scan, 40 steps, stress", stress, "T layout", t_layout, flush=True)
+    R, out = _gpu(W, t_layout=t_layout)
+    S_ref, outs_ref = _reference(W)
+    _check(W, R, out, S_ref, outs_ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("stress", [False, True])
+def test_seam_scan_fp32_d16(stress):
+    rng = np.random.default_rng(12)
+    W = _seam_workload("gdn-tiny-f32", _short_lengths(rng, 26, 8, 10, 40), 8, H=1, stress=stress)
+    print(W.name, "fp32 scan, 26 steps, stress", stress, flush=True)
+    R, out = _gpu(W)
+    S_ref, outs_ref = _reference(W)
+    _check(W, R, out, S_ref, outs_ref, TOL["f32"])
+
+
+def test_seam_scan_without_pairs():
+    rng = np.random.default_rng(13)
+    W = _seam_workload("gdn-16h-d128-32k", _short_lengths(rng, 24, 8, 8, 12), 8, H=2, stress=True)
+    R, out = _gpu(W, with_pairs=False)
+    S = np.zeros((2, 128, 128))
+    for i in range(1, W.n_seg):
+        a = int(W.seg_start[i])
+        S, o = oracle.run(W.k, W.v, W.g, W.beta, gate=W.gate, delta=True, t0=a, t1=a + 8, S0=S, q=W.q,
+                          scale=W.scale)
+        e = rel_f(np.transpose(out[i], (1, 0, 2)), np.transpose(o, (1, 0, 2)))
+        assert e.max() <= TOL["bf16"], (i, e.max())
+    assert rel_f(R, S).max() <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_seam_scan_two_chains_mixed_plan(d):
+    """Two chains from nonzero states; chain 1 skips some windows and some pairs and
+    reuses segments out of order.  Reference: oracle windows and fp64 composition with
+    the oracle's own pairs, step by step."""
+    rng = np.random.default_rng(14 + d)
+    H, w, n = 2, 8, 24
+    W = _seam_workload("gdn-16h-d128-32k", _short_lengths(rng, n, w), w, H=H, stress=True, d=d)
+    starts = W.seg_start
+    seam = np.stack([starts[:-1], starts[:-1]]).astype(np.int64)
+    seam[:, 0] = -1
+    seam[1, rng.choice(np.arange(1, n), 6, replace=False)] = -1
+    pid = np.stack([np.arange(n), rng.permutation(n)]).astype(np.int32)
+    pid[1, rng.choice(n, 5, replace=False)] = -1
+    R0 = rng.standard_normal((2, H, d, d)) * 0.3
+    x = workload_tensors(W)
+    T, S = hb.segment_build(x["k"], x["v"], x["g"], x["beta"], dev(W.cache_begin, torch.int64),
+                            dev(W.cache_end, torch.int64), gate=W.gate, delta=W.delta, t_layout=hb.T_SPLIT)
+    R = dev(R0, torch.float32)
+    out = torch.full((2, n, w, H, d), float("nan"), device="cuda")
+    hb.seam_advance(x["q"], x["k"], x["v"], x["g"], x["beta"], dev(seam, torch.int64), R, out,
+                    gate=W.gate, delta=W.delta, w=w, scale=W.scale, pair_id=dev(pid, torch.int32),
+                    T_cache=T, S_cache=S)
+    torch.cuda.synchronize()
+    R, out = R.cpu().numpy(), out.cpu().numpy()
+    T0, S0 = oracle.segment_build(W.k, W.v, W.g, W.beta, W.cache_begin, W.cache_end, gate=W.gate, delta=True)
+    for c in range(2):
+        Sr = R0[c].copy()
+        for j in range(n):
+            if seam[c, j] >= 0:
+                a = int(seam[c, j])
+                Sr, o = oracle.run(W.k, W.v, W.g, W.beta, gate=W.gate, delta=True, t0=a, t1=a + w, S0=Sr,
+                                   q=W.q, scale=W.scale)
+                e = rel_f(np.transpose(out[c, j], (1, 0, 2)), np.transpose(o, (1, 0, 2)))
+                assert e.max() <= TOL["bf16"], (c, j, e.max())
+            else:
+                assert np.all(np.isnan(out[c, j])), (c, j)
+            if pid[c, j] >= 0:
+                Sr = T0[pid[c, j]] @ Sr + S0[pid[c, j]]
+        assert rel_f(R[c], Sr).max() <= TOL["bf16"], (c, rel_f(R[c], Sr).max())
