@@ -310,7 +310,7 @@ def main():
 # Sources of the kernels each library call launches (a stored counter measurement is
 # reported only while these files are unchanged).
 CALL_SOURCES = {
-    "seam_advance": ["seam.hip", "seam_chain.hip", "seam_layout.h", "hypic_device.h", "hypic_kernels.h"],
+    "seam_advance": ["seam.hip", "seam_chain.hip", "seam_layout.h", "compose.hip", "hypic_device.h", "hypic_kernels.h"],
     "compose": ["compose.hip", "hypic_device.h", "hypic_kernels.h"],
     "segment_build": ["build_gdn.hip", "build_split.hip", "build_kda.hip", "build_decay.hip", "build_common.h",
                       "hypic_device.h", "hypic_kernels.h"],

@@ -153,13 +153,29 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
         }
         if (tid < CK) sm.beta[tid] = tid < n ? bf(beta[(size_t)(c0 + tid) * H + h]) : 0.f;
         __syncthreads();
-        if (tid < D) {  // exclusive cumulative log-gate of channel tid, in place
-            float acc = 0.f;
-            sm.Ag[0][tid] = 0.f;
-#pragma unroll 8
-            for (int t = 0; t < CK; ++t) {
-                acc += sm.Ag[t + 1][tid];
-                sm.Ag[t + 1][tid] = acc;
+        {   // exclusive cumulative log-gate per channel, in place: thread (channel c, quarter q)
+            // scans tokens 8q .. 8q+7, then adds the totals of the quarters before it (the four
+            // quarters of a channel are four consecutive lanes)
+            static_assert(4 * D <= 512 && CK == 32, "4 threads per channel");
+            const int c = tid >> 2, q = tid & 3;
+            float x[8], run = 0.f;
+            if (c < D) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    run += sm.Ag[8 * q + i + 1][c];
+                    x[i] = run;
+                }
+            }
+            float pre = 0.f;   // sum of the quarters before q
+#pragma unroll
+            for (int o = 1; o < 4; ++o) {
+                const float y = __shfl_up(run, o, 4);
+                if (q >= o) pre += y;
+            }
+            if (c < D) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) sm.Ag[8 * q + i + 1][c] = x[i] + pre;
+                if (q == 0) sm.Ag[0][c] = 0.f;
             }
         }
         if (vt >= 0) {   // (diag(b) V)^T, fp16
@@ -201,9 +217,11 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                 if (lp) sm.F1[tt][ss] = ss < tt ? sm.beta[tt] * acc[e] : 0.f;
                 else sm.F1p[tt][ss] = ss < tt ? acc[e] : 0.f;
             }
-        } else {
-            // waves 6-7: decay-scaled key operands (channel-major, token-contiguous), fp16
-            for (int it = tid - 384; it < D * CK; it += 128) {
+        }
+        // decay-scaled key operands (channel-major, token-contiguous), spread over all waves
+        // (waves 6 and 7 start at once, the others after their Gram tile)
+        {
+            for (int it = tid; it < D * CK; it += 512) {
                 const int c = it / CK, t = it % CK;
                 const float kx = bf(sm.Kb[t][c]);
                 const float at = sm.Ag[t + E1][c], at1 = sm.Ag[t + 1][c], bc = sm.Ag[CK][c];

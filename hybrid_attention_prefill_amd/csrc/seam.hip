@@ -30,7 +30,8 @@ namespace hypic {
 
 namespace {
 
-// hi/lo bf16 planes of 8 consecutive floats, written as two 16-byte stores
+// hi/lo bf16 planes of 8 consecutive floats, written as two 16-byte stores (lo == NULL:
+// the hi plane only, for values that bf16 holds exactly)
 __device__ __forceinline__ void put_split8(uint16_t* hi, uint16_t* lo, const float* x)
 {
     unsigned h[4], l[4];
@@ -43,7 +44,7 @@ __device__ __forceinline__ void put_split8(uint16_t* hi, uint16_t* lo, const flo
         l[i] = pack2(bf16_bits(b0), bf16_bits(b1));
     }
     *reinterpret_cast<u32x4*>(hi) = u32x4{h[0], h[1], h[2], h[3]};
-    *reinterpret_cast<u32x4*>(lo) = u32x4{l[0], l[1], l[2], l[3]};
+    if (lo) *reinterpret_cast<u32x4*>(lo) = u32x4{l[0], l[1], l[2], l[3]};
 }
 
 }  // namespace
@@ -223,10 +224,11 @@ __global__ __launch_bounds__(256) void seam_prep_kernel(
             const int off = frag_off(t, c0, D) * 2;
             put_split8(reinterpret_cast<uint16_t*>(rp + R::kW + off),
                        reinterpret_cast<uint16_t*>(rp + R::kW + R::kPlaneWD + off), wk);
+            // bf16 q and k are exact in the hi plane; their lo planes are neither written nor read
             put_split8(reinterpret_cast<uint16_t*>(rp + R::kQ + off),
-                       reinterpret_cast<uint16_t*>(rp + R::kQ + R::kPlaneWD + off), qx);
+                       in_bf16 ? nullptr : reinterpret_cast<uint16_t*>(rp + R::kQ + R::kPlaneWD + off), qx);
             put_split8(reinterpret_cast<uint16_t*>(rp + R::kK + off),
-                       reinterpret_cast<uint16_t*>(rp + R::kK + R::kPlaneWD + off), &Ks[t][c0]);
+                       in_bf16 ? nullptr : reinterpret_cast<uint16_t*>(rp + R::kK + R::kPlaneWD + off), &Ks[t][c0]);
             float* up = reinterpret_cast<float*>(rp + R::kU);
 #pragma unroll
             for (int x = 0; x < 8; ++x) {   // block cb = ch / 16, lane (t / 4, ch % 16), element t % 4

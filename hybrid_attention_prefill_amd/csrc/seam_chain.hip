@@ -535,85 +535,115 @@ __global__ __launch_bounds__(64 * (DK / 16 + NB / 16)) void seam_chain_kernel(
 }
 
 // ---- phase 3 of the blocked scan: window outputs from the readouts of X.  One workgroup
-// (4 waves, d_v/64 column tiles each) per (chain, window step j of a block b >= 1, head):
-//     out_j = Gx_j R_in + Hx_j,   Gx_j = readout of the transition half, Hx_j = of the state half,
-// with R_in the state entering block b (fp32, split into bf16 hi/lo B fragments in registers).
+// (8 waves) per (chain, block b >= 1, head, group of 8 windows): R_in, the state entering
+// the block (fp32), is split into bf16 hi/lo planes in LDS ([column][row], the B operand),
+// then each wave forms the outputs of one window:
+//     out_j = Gx_j R_in + Hx_j,   Gx_j = readout of the transition half, Hx_j = of the state half.
 template <int DK>
-__global__ __launch_bounds__(256) void seam_readout_kernel(
+__global__ __launch_bounds__(512) void seam_readout_kernel(
     int n_chain, int H, int n_step, int nblk, int blk, int w, const int64_t* __restrict__ seam_start,
     int64_t n_tokens, const float* __restrict__ ox, const float* __restrict__ trail, float* __restrict__ out)
 {
     constexpr int DV = DK;
     constexpr int KP = DK < 32 ? 32 : DK;
     constexpr int KS = KP / 32;
+    constexpr int LDB = KP + 8;
     constexpr int NT = DV / 16;                  // column tiles
-    constexpr int TW = NT >= 4 ? NT / 4 : 1;     // column tiles per wave
-    const int nj = n_step - blk;                 // steps of blocks >= 1
-    const int unit = blockIdx.x;
-    const int h = unit % H, r = unit / H;
-    const int j = blk + r % nj, c = r / nj;
+    __shared__ __attribute__((aligned(16))) uint16_t Rh[DV][LDB];
+    __shared__ __attribute__((aligned(16))) uint16_t Rl[DV][LDB];
+    // unit: (chain, block b >= 1, head, group of 8 windows); one window per wave
+    const int ngrp = (blk + 7) / 8;
+    const int unit = blockIdx.x / ngrp, grp = blockIdx.x % ngrp;
+    const int h = unit % H, cbk = unit / H;
+    const int b = 1 + cbk % (nblk - 1), c = cbk / (nblk - 1);
     if (c >= n_chain) return;
-    const int b = j / blk;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g4 = lane >> 4, n16 = lane & 15;
-    if (wave * TW >= NT) return;   // uniform: d_v < 64 leaves waves idle
-    const size_t cj = (size_t)c * n_step + j;
-    const int64_t s0 = seam_start[cj];
-    if (s0 < 0 || s0 + w > n_tokens) return;   // no window at this step
     const float* R = trail + (((size_t)c * (nblk - 1) + (b - 1)) * H + h) * DK * DV;
-
-    // A fragments: row t = n16 of the transition readout, k = 32 ks + 8 g4 + 0..7
-    bf16x8 ah[KS], al[KS];
+    {   // 4 consecutive columns of one row per item; all of a thread's loads issued together
+        constexpr int NI = DK * DV / 4, PER = (NI + 511) / 512;
+        f32x4 r4[PER];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const int k0 = ks * 32 + 8 * g4;
-        float a[8];
-        if (n16 < w && k0 < DK) {
-            const f32x4* p = reinterpret_cast<const f32x4*>(ox + ((cj * w + n16) * H + h) * 2 * DV + k0);
-            const f32x4 a0 = p[0], a1 = p[1];
-#pragma unroll
-            for (int x = 0; x < 4; ++x) { a[x] = a0[x]; a[4 + x] = a1[x]; }
-        } else {
-#pragma unroll
-            for (int x = 0; x < 8; ++x) a[x] = 0.f;
+        for (int x = 0; x < PER; ++x) {
+            const int i = threadIdx.x + 512 * x;
+            r4[x] = i < NI ? reinterpret_cast<const f32x4*>(R)[i] : zero4();
         }
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-            __bf16 hi, lo;
-            split_bf16(a[x], hi, lo);
-            ah[ks][x] = hi;
-            al[ks][x] = lo;
+        for (int x = 0; x < PER; ++x) {
+            const int i = threadIdx.x + 512 * x;
+            if (i < NI) {
+                const int k = 4 * i / DV, col = 4 * i % DV;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    __bf16 hi, lo;
+                    split_bf16(r4[x][e], hi, lo);
+                    Rh[col + e][k] = bf16_bits(hi);
+                    Rl[col + e][k] = bf16_bits(lo);
+                }
+            }
+        }
+        for (int i = threadIdx.x; i < (KP - DK) * DV; i += blockDim.x) {   // rows past d_k are zero
+            Rh[i % DV][DK + i / DV] = 0;
+            Rl[i % DV][DK + i / DV] = 0;
         }
     }
-#pragma unroll
-    for (int i = 0; i < TW; ++i) {
-        const int col = (wave * TW + i) * 16 + n16;
-        f32x4 o0, o1 = zero4(), o2 = zero4();
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = 4 * g4 + e;
-            o0[e] = t < w ? ox[((cj * w + t) * H + h) * 2 * DV + DV + col] : 0.f;
-        }
+    __syncthreads();
+
+    const int j = b * blk + grp * 8 + wave;
+    if (grp * 8 + wave >= blk || j >= n_step) return;
+    {
+        const size_t cj = (size_t)c * n_step + j;
+        const int64_t s0 = seam_start[cj];
+        if (s0 < 0 || s0 + w > n_tokens) return;   // no window at this step (uniform)
+        // A fragments: row t = n16 of the transition readout, k = 32 ks + 8 g4 + 0..7; the
+        // state-half readout (the accumulators' initial values) loaded with them
+        f32x4 a0[KS], a1[KS], hx[NT];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            bf16x8 bh, bl;   // rows k = 32 ks + 8 g4 + x of column col
+            const int k0 = ks * 32 + 8 * g4;
+            a0[ks] = a1[ks] = zero4();
+            if (n16 < w && k0 < DK) {
+                const f32x4* p = reinterpret_cast<const f32x4*>(ox + ((cj * w + n16) * H + h) * 2 * DV + k0);
+                a0[ks] = p[0];
+                a1[ks] = p[1];
+            }
+        }
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 4 * g4 + e;
+                hx[ct][e] = t < w ? ox[((cj * w + t) * H + h) * 2 * DV + DV + ct * 16 + n16] : 0.f;
+            }
+        bf16x8 ah[KS], al[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
             for (int x = 0; x < 8; ++x) {
-                const int k = ks * 32 + 8 * g4 + x;
                 __bf16 hi, lo;
-                split_bf16(k < DK ? R[(size_t)k * DV + col] : 0.f, hi, lo);
-                bh[x] = hi;
-                bl[x] = lo;
+                split_bf16(x < 4 ? a0[ks][x] : a1[ks][x - 4], hi, lo);
+                ah[ks][x] = hi;
+                al[ks][x] = lo;
             }
-            o0 = mma_bf16(ah[ks], bh, o0);
-            o1 = mma_bf16(ah[ks], bl, o1);
-            o2 = mma_bf16(al[ks], bh, o2);
         }
-        const f32x4 o = o0 + (o1 + o2);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = 4 * g4 + e;
-            if (t < w) out[((cj * w + t) * H + h) * DV + col] = o[e];
+        for (int ct = 0; ct < NT; ++ct) {
+            const int col = ct * 16 + n16;
+            f32x4 o0 = hx[ct], o1 = zero4(), o2 = zero4();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&Rh[col][ks * 32 + 8 * g4]);
+                const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&Rl[col][ks * 32 + 8 * g4]);
+                o0 = mma_bf16(ah[ks], bh, o0);
+                o1 = mma_bf16(ah[ks], bl, o1);
+                o2 = mma_bf16(al[ks], bh, o2);
+            }
+            const f32x4 o = o0 + (o1 + o2);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 4 * g4 + e;
+                if (t < w) out[((cj * w + t) * H + h) * DV + col] = o[e];
+            }
         }
     }
 }
@@ -690,11 +720,11 @@ hipError_t seam_readout(int d, int n_chain, int H, int n_step, int nblk, int blk
                         const int64_t* seam_start, int64_t n_tokens, const float* ox, const float* trail,
                         float* out, hipStream_t st)
 {
-    const long long grid = (long long)n_chain * (n_step - blk) * H;
+    const long long grid = (long long)n_chain * (nblk - 1) * H * ((blk + 7) / 8);
     if (nblk < 2 || grid <= 0) return hipSuccess;
 #define HYPIC_CASE(D_)                                                                                   \
     if (d == D_) {                                                                                       \
-        hipLaunchKernelGGL(seam_readout_kernel<D_>, dim3((unsigned)grid), dim3(256), 0, st, n_chain, H, \
+        hipLaunchKernelGGL(seam_readout_kernel<D_>, dim3((unsigned)grid), dim3(512), 0, st, n_chain, H, \
                            n_step, nblk, blk, w, seam_start, n_tokens, ox, trail, out);                  \
         return hipGetLastError();                                                                        \
     }
