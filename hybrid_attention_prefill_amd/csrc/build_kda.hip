@@ -57,19 +57,28 @@ struct alignas(16) KdaSmem {
     float beta[CK];
     float F1[CK][LDF];             // Lp (strictly lower, beta folded)
     float F1p[CK][LDF];            // L'
-    float F2[CK][LDF];             // A = (I + Lp)^-1
-    float F3[16][17];
     uint16_t RmT[2][D][LDT];       // (e^{a} o K)^T, bf16 hi / lo
     uint16_t KhTb[2][D][LDT];      // Kh^T, bf16 hi / lo (T columns)
-    uint16_t ApB[2][CK][LDT];      // A diag(b), bf16 hi / lo
-    uint16_t WpB[2][CK][D + 8];    // W, token-major, bf16 hi / lo (T columns)
     uint16_t KhT[D][LDT];          // Kh^T
     uint16_t KhpT[D][LDT];         // Kh'^T
     uint16_t bVT[D][LDT];          // (diag(b) V)^T
-    uint16_t Ap[CK][LDT];          // A diag(b)
-    uint16_t Lpb[CK][LDT];         // L' (fp16)
-    uint16_t Z1T[D][LDT];          // (L' diag(b) V)^T
-    uint16_t Wp[CK][D + 8];        // W, token-major (S columns)
+    union {
+        struct {                       // phases 3-5
+            float F2[CK][LDF];             // A = (I + Lp)^-1
+            float F3[16][17];
+            uint16_t ApB[2][CK][LDT];      // A diag(b), bf16 hi / lo
+            uint16_t WpB[2][CK][D + 8];    // W, token-major, bf16 hi / lo (T columns)
+            uint16_t Ap[CK][LDT];          // A diag(b)
+            uint16_t Lpb[CK][LDT];         // L' (fp16)
+            uint16_t Z1T[D][LDT];          // (L' diag(b) V)^T
+            uint16_t Wp[CK][D + 8];        // W, token-major (S columns)
+        } p;
+        struct {                       // phase 2: operands of the decay-weighted Gram products
+            uint16_t GL[2][CK][D + 8];     // k_t e^{c_t - rho}, bf16 hi / lo, token-major
+            uint16_t GR[2][CK][D + 8];     // k_s e^{rho - c_s}            (Lp)
+            uint16_t GR1[2][CK][D + 8];    // k_s e^{rho - i_s}            (L'; the gate-first order reuses GR)
+        } g;
+    } u;
     float red[8];
 };
 
@@ -132,7 +141,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
         float vx[8];
         int vt = -1, vcg = 0;
         for (int it = tid; it < CK * (D / 8); it += 512) {
-            const int t = it / (D / 8), cg = it % (D / 8);
+            const int cg = it / CK, t = it % CK;   // token fastest: the transposed stores below are contiguous
             u32x4 kw = u32x4{0, 0, 0, 0}, vw = u32x4{0, 0, 0, 0}, gw = u32x4{0, 0, 0, 0};
             if (t < n) {
                 const size_t e = (size_t)(c0 + t) * tok_stride + (size_t)h * D + cg * 8;
@@ -185,28 +194,60 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
         }
         __syncthreads();
 
-        // ---- 2. decay-weighted Gram matrices Lp (waves 0-2) and L' (waves 3-5), bf16 hi+lo
+        // ---- 2. decay-weighted Gram matrices Lp (waves 0-2) and L' (waves 3-5), bf16 hi+lo.
+        // Their operands are formed once per chunk by all waves (one token, 8 channels per item):
+        // with one reference rho = c_16 per channel (the second 16-token block's first gate)
+        // every factor is <= 1 except on a diagonal block, where it is bounded by one block's
+        // decay, and the products are exactly the decay-weighted ones (rho cancels).
+        for (int it = tid; it < CK * (D / 8); it += 512) {   // item: token t, channels c .. c+7
+            {
+                const int t = it / (D / 8), c = (it % (D / 8)) * 8;
+                const u32x4 kw = *reinterpret_cast<const u32x4*>(&sm.Kb[t][c]);
+                float kx[8], gl[8], gr[8], gr1[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    kx[2 * e] = __uint_as_float(kw[e] << 16);
+                    kx[2 * e + 1] = __uint_as_float(kw[e] & 0xFFFF0000u);
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float rho = sm.Ag[16 + E1][c + e];
+                    const float ct = sm.Ag[t + E1][c + e];
+                    gl[e] = kx[e] * __expf(ct - rho);
+                    gr[e] = kx[e] * __expf(rho - ct);
+                    gr1[e] = E1 ? gr[e] : kx[e] * __expf(rho - sm.Ag[t + 1][c + e]);
+                }
+                auto put = [&](uint16_t (*P)[CK][D + 8], const float* v) {
+                    unsigned h[4], l[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        h[e] = cvt2_bf16(v[2 * e], v[2 * e + 1]);
+                        const f32x2 hv = bf16x2_to_f32(h[e]);
+                        l[e] = cvt2_bf16(v[2 * e] - hv.x, v[2 * e + 1] - hv.y);
+                    }
+                    *reinterpret_cast<u32x4*>(&P[0][t][c]) = u32x4{h[0], h[1], h[2], h[3]};
+                    *reinterpret_cast<u32x4*>(&P[1][t][c]) = u32x4{l[0], l[1], l[2], l[3]};
+                };
+                put(sm.u.g.GL, gl);
+                put(sm.u.g.GR, gr);
+                if (!E1) put(sm.u.g.GR1, gr1);
+            }
+        }
+        __syncthreads();
         if (wave < 6) {
             const bool lp = wave < 3;
             const int tile = lp ? wave : wave - 3;
             const int I = tile == 0 ? 0 : 1, J = tile == 2 ? 1 : 0;
             const int t = 16 * I + n16, s = 16 * J + n16;
+            const uint16_t(*R)[CK][D + 8] = (lp || E1) ? sm.u.g.GR : sm.u.g.GR1;
             f32x4 acc = zero4();
 #pragma unroll
             for (int ks = 0; ks < KSD; ++ks) {
-                bf16x8 ah, al, bh, bl;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int c = ks * 32 + 8 * g4 + e;
-                    const float rho = sm.Ag[16 * I + E1][c];
-                    const float a = bf(sm.Kb[t][c]) * __expf(sm.Ag[t + E1][c] - rho);
-                    const float b = bf(sm.Kb[s][c]) * __expf(rho - sm.Ag[lp ? s + E1 : s + 1][c]);
-                    __bf16 x, y;
-                    split_bf16(a, x, y);
-                    ah[e] = x; al[e] = y;
-                    split_bf16(b, x, y);
-                    bh[e] = x; bl[e] = y;
-                }
+                const int c = ks * 32 + 8 * g4;
+                const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&sm.u.g.GL[0][t][c]);
+                const bf16x8 al = *reinterpret_cast<const bf16x8*>(&sm.u.g.GL[1][t][c]);
+                const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&R[0][s][c]);
+                const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&R[1][s][c]);
                 acc = mma_bf16(ah, bh, acc);
                 acc = mma_bf16(ah, bl, acc);
                 acc = mma_bf16(al, bh, acc);
@@ -219,18 +260,38 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
             }
         }
         // decay-scaled key operands (channel-major, token-contiguous), spread over all waves
-        // (waves 6 and 7 start at once, the others after their Gram tile)
-        {
-            for (int it = tid; it < D * CK; it += 512) {
-                const int c = it / CK, t = it % CK;
-                const float kx = bf(sm.Kb[t][c]);
-                const float at = sm.Ag[t + E1][c], at1 = sm.Ag[t + 1][c], bc = sm.Ag[CK][c];
-                put_bf16_split(&sm.RmT[0][c][t], &sm.RmT[1][c][t], kx * __expf(at));
-                const float kh = kx * __expf(bc - at);
-                sm.KhT[c][t] = f16_bits((_Float16)kh);
-                put_bf16_split(&sm.KhTb[0][c][t], &sm.KhTb[1][c][t], kh);
-                sm.KhpT[c][t] = f16_bits((_Float16)(kx * __expf(bc - at1)));
+        // (waves 6 and 7 start at once, the others after their Gram tile): item = (4-token
+        // group, channel), channel fastest, so a wave reads consecutive channels of a token row
+        // and writes 4 consecutive tokens of a channel row per store
+        for (int it = tid; it < D * (CK / 4); it += 512) {
+            const int c = it % D, t0 = 4 * (it / D);
+            const float bc = sm.Ag[CK][c];
+            unsigned rh[2], rl[2], kh16[2], khh[2], khl[2], kp16[2];
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                float rm[2], kh[2], kp[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int t = t0 + 2 * p + i;
+                    const float kx = bf(sm.Kb[t][c]);
+                    const float at = sm.Ag[t + E1][c], at1 = sm.Ag[t + 1][c];
+                    rm[i] = kx * __expf(at);
+                    kh[i] = kx * __expf(bc - at);
+                    kp[i] = kx * __expf(bc - at1);
+                }
+                rh[p] = cvt2_bf16(rm[0], rm[1]);
+                rl[p] = cvt2_bf16(rm[0] - bf16x2_to_f32(rh[p]).x, rm[1] - bf16x2_to_f32(rh[p]).y);
+                khh[p] = cvt2_bf16(kh[0], kh[1]);
+                khl[p] = cvt2_bf16(kh[0] - bf16x2_to_f32(khh[p]).x, kh[1] - bf16x2_to_f32(khh[p]).y);
+                kh16[p] = cvt2_f16(kh[0], kh[1]);
+                kp16[p] = cvt2_f16(kp[0], kp[1]);
             }
+            *reinterpret_cast<u32x2*>(&sm.RmT[0][c][t0]) = u32x2{rh[0], rh[1]};
+            *reinterpret_cast<u32x2*>(&sm.RmT[1][c][t0]) = u32x2{rl[0], rl[1]};
+            *reinterpret_cast<u32x2*>(&sm.KhTb[0][c][t0]) = u32x2{khh[0], khh[1]};
+            *reinterpret_cast<u32x2*>(&sm.KhTb[1][c][t0]) = u32x2{khl[0], khl[1]};
+            *reinterpret_cast<u32x2*>(&sm.KhT[c][t0]) = u32x2{kh16[0], kh16[1]};
+            *reinterpret_cast<u32x2*>(&sm.KhpT[c][t0]) = u32x2{kp16[0], kp16[1]};
         }
         __syncthreads();
 
@@ -246,28 +307,28 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                 x[r] = s;
             }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sm.F2[o + r][o + j] = x[r];
+            for (int r = 0; r < 16; ++r) sm.u.p.F2[o + r][o + j] = x[r];
         }
         for (int it = tid; it < CK * CK; it += 512) {  // L' to fp16 (row-major); the block above
             const int t = it / CK, s = it % CK;          // the diagonal is never computed
-            sm.Lpb[t][s] = f16_bits((_Float16)(s < t ? sm.F1p[t][s] : 0.f));
+            sm.u.p.Lpb[t][s] = f16_bits((_Float16)(s < t ? sm.F1p[t][s] : 0.f));
         }
         __syncthreads();
         if (wave == 0) {
-            const f32x4 p = mm16_f32(&sm.F1[16][0], LDF, &sm.F2[0][0], LDF, lane);
-            st16_f32(&sm.F3[0][0], 17, p, lane, 1.f);
+            const f32x4 p = mm16_f32(&sm.F1[16][0], LDF, &sm.u.p.F2[0][0], LDF, lane);
+            st16_f32(&sm.u.p.F3[0][0], 17, p, lane, 1.f);
         }
         __syncthreads();
         if (wave == 0) {
-            const f32x4 q = mm16_f32(&sm.F2[16][16], LDF, &sm.F3[0][0], 17, lane);
-            st16_f32(&sm.F2[16][0], LDF, q, lane, -1.f);
+            const f32x4 q = mm16_f32(&sm.u.p.F2[16][16], LDF, &sm.u.p.F3[0][0], 17, lane);
+            st16_f32(&sm.u.p.F2[16][0], LDF, q, lane, -1.f);
         }
         __syncthreads();
         for (int it = tid; it < CK * CK; it += 512) {
             const int t = it / CK, s = it % CK;
-            const float ap = s <= t ? sm.F2[t][s] * sm.beta[s] : 0.f;
-            sm.Ap[t][s] = f16_bits((_Float16)ap);
-            put_bf16_split(&sm.ApB[0][t][s], &sm.ApB[1][t][s], ap);
+            const float ap = s <= t ? sm.u.p.F2[t][s] * sm.beta[s] : 0.f;
+            sm.u.p.Ap[t][s] = f16_bits((_Float16)ap);
+            put_bf16_split(&sm.u.p.ApB[0][t][s], &sm.u.p.ApB[1][t][s], ap);
         }
         __syncthreads();
 
@@ -279,7 +340,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
             f32x4 acc = zero4();
             if (isw) {
                 const FragB a = fragb_at(&sm.RmT[0][0][0], &sm.RmT[1][0][0], LDT, mt * 16 + n16, 8 * g4);
-                const FragB b = fragb_at(&sm.ApB[0][0][0], &sm.ApB[1][0][0], LDT, nt * 16 + n16, 8 * g4);
+                const FragB b = fragb_at(&sm.u.p.ApB[0][0][0], &sm.u.p.ApB[1][0][0], LDT, nt * 16 + n16, 8 * g4);
                 acc = mma3(a, b, acc);
                 uint16_t hh[4], bh[4], bl[4];
 #pragma unroll
@@ -288,15 +349,15 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                     put_bf16_split(&bh[e], &bl[e], acc[e]);
                 }
                 const int row = nt * 16 + n16, col = mt * 16 + 4 * g4;
-                *reinterpret_cast<u32x2*>(&sm.Wp[row][col]) = u32x2{pack2(hh[0], hh[1]), pack2(hh[2], hh[3])};
-                *reinterpret_cast<u32x2*>(&sm.WpB[0][row][col]) = u32x2{pack2(bh[0], bh[1]), pack2(bh[2], bh[3])};
-                *reinterpret_cast<u32x2*>(&sm.WpB[1][row][col]) = u32x2{pack2(bl[0], bl[1]), pack2(bl[2], bl[3])};
+                *reinterpret_cast<u32x2*>(&sm.u.p.Wp[row][col]) = u32x2{pack2(hh[0], hh[1]), pack2(hh[2], hh[3])};
+                *reinterpret_cast<u32x2*>(&sm.u.p.WpB[0][row][col]) = u32x2{pack2(bh[0], bh[1]), pack2(bh[2], bh[3])};
+                *reinterpret_cast<u32x2*>(&sm.u.p.WpB[1][row][col]) = u32x2{pack2(bl[0], bl[1]), pack2(bl[2], bl[3])};
             } else {
                 const Frag<1> a = f16frag(&sm.bVT[0][0], LDT, mt * 16 + n16, 8 * g4);
-                const Frag<1> b = f16frag(&sm.Lpb[0][0], LDT, nt * 16 + n16, 8 * g4);
+                const Frag<1> b = f16frag(&sm.u.p.Lpb[0][0], LDT, nt * 16 + n16, 8 * g4);
                 acc = mma<1>(a, b, acc);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sm.Z1T[mt * 16 + 4 * g4 + e][nt * 16 + n16] = f16_bits((_Float16)acc[e]);
+                for (int e = 0; e < 4; ++e) sm.u.p.Z1T[mt * 16 + 4 * g4 + e][nt * 16 + n16] = f16_bits((_Float16)acc[e]);
             }
         }
         __syncthreads();
@@ -319,7 +380,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                     f32x4 y = zero4();
 #pragma unroll
                     for (int kb = 0; kb < KSD; ++kb)
-                        y = mma3(fragb_at(&sm.WpB[0][0][0], &sm.WpB[1][0][0], D + 8, tt * 16 + n16, kb * 32 + 8 * g4),
+                        y = mma3(fragb_at(&sm.u.p.WpB[0][0][0], &sm.u.p.WpB[1][0][0], D + 8, tt * 16 + n16, kb * 32 + 8 * g4),
                                  xb[kb], y);
                     R[tt] = -y;
                 }
@@ -337,8 +398,8 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
             if (is_s) {  // U = Ap Z1 for this value tile
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) {
-                    const Frag<1> a = f16frag(&sm.Ap[0][0], LDT, tt * 16 + n16, 8 * g4);
-                    const Frag<1> b = f16frag(&sm.Z1T[0][0], LDT, vt16 * 16 + n16, 8 * g4);
+                    const Frag<1> a = f16frag(&sm.u.p.Ap[0][0], LDT, tt * 16 + n16, 8 * g4);
+                    const Frag<1> b = f16frag(&sm.u.p.Z1T[0][0], LDT, vt16 * 16 + n16, 8 * g4);
                     U[tt] = mma<1>(a, b, U[tt]);
                 }
             }
@@ -351,7 +412,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                 f32x4 y = zero4();
 #pragma unroll
                 for (int kb = 0; kb < KSD; ++kb) {
-                    const Frag<1> a = f16frag(&sm.Wp[0][0], D + 8, tt * 16 + n16, kb * 32 + 8 * g4);
+                    const Frag<1> a = f16frag(&sm.u.p.Wp[0][0], D + 8, tt * 16 + n16, kb * 32 + 8 * g4);
                     y = mma<1>(a, xb[kb], y);
                 }
                 R[tt] = -(y + U[tt]);
