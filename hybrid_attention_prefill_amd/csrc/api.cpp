@@ -73,7 +73,10 @@ const char* hypic_last_error(void) { return g_last_error.c_str(); }
 size_t hypic_build_workspace_bytes(const hypic_dims* dims, int32_t n_seg, int64_t n_tokens)
 {
     if (!dims || dims->n_heads < 1 || dims->d_k != dims->d_v || n_seg < 1 || n_tokens < 0) return 0;
-    if (dims->gate != HYPIC_GATE_TOKEN || !dims->delta || dims->in_dtype != HYPIC_BF16) return 0;
+    if (!valid_d(dims->d_k) || dims->gate < HYPIC_GATE_HEAD || dims->gate > HYPIC_GATE_DIAG) return 0;
+    if (!dims->delta)
+        return hypic::decay_workspace_bytes(dims->d_k, dims->n_heads, n_seg, n_tokens, dims->gate == HYPIC_GATE_DIAG);
+    if (dims->gate != HYPIC_GATE_TOKEN || dims->in_dtype != HYPIC_BF16) return 0;
     return hypic::split_workspace_bytes(dims->d_k, dims->n_heads, n_seg, n_tokens);
 }
 
@@ -95,8 +98,16 @@ hypic_status hypic_segment_build(const hypic_dims* dims, int32_t n_seg, const in
     const bool bf16 = dims->in_dtype == HYPIC_BF16;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (!dims->delta) {
+        const size_t need = workspace ? hypic_build_workspace_bytes(dims, n_seg, n_tokens) : 0;
+        if (need > 0) {
+            if (workspace_bytes < need)
+                return fail(HYPIC_E_INVALID, "build workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+            if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+                return fail(HYPIC_E_INVALID, "workspace must be 256-byte aligned");
+        }
         return from_hip(hypic::build_decay(dims->d_k, bf16, dims->gate, n_seg, dims->n_heads, seg_begin, seg_end,
-                                           n_tokens, k, v, g, T_out, dims->t_layout, S_out, st),
+                                           n_tokens, k, v, g, T_out, dims->t_layout, S_out,
+                                           need > 0 ? workspace : nullptr, st),
                         "hypic_segment_build");
     }
     if (dims->delta && dims->gate == HYPIC_GATE_TOKEN) {

@@ -17,6 +17,11 @@
 // the weighted V is split into bf16 hi + lo (bf16 keys are exact; fp32 keys
 // are split too), keeping the fp32 exponent range for the tiny weights of
 // fast-decaying heads.
+//
+// With a workspace, a segment is cut into up to 8 runs of whole chunks built in parallel
+// (one workgroup each) and composed by decay_fold_kernel: without the erase every piece's
+// transition is a scalar (or diagonal), so the composition law ([ZH] section 2.1) is an
+// elementwise weighted sum.
 #include "hypic_device.h"
 #include "hypic_kernels.h"
 
@@ -26,6 +31,50 @@ namespace {
 constexpr int CH = 64;
 constexpr int LDT = CH + 8;
 
+// Pieces of a segment (decay builds with a workspace): the segment's ceil(L / 64) chunks
+// are cut into min(8, chunks) near-equal runs of whole chunks.  How a segment is cut
+// depends on its length only.
+constexpr int kMaxPieces = 8;
+struct PieceRange { int64_t beg, end; int n_pieces; };
+__host__ __device__ inline PieceRange piece_range(int64_t beg, int64_t end, int p) {
+    const int64_t chunks = (end - beg + CH - 1) / CH;
+    const int np = (int)(chunks < kMaxPieces ? chunks : kMaxPieces);
+    PieceRange r{beg, beg, np};
+    if (p < np) {
+        const int64_t c0 = chunks * p / np, c1 = chunks * (p + 1) / np;
+        r.beg = beg + c0 * CH;
+        r.end = beg + c1 * CH < end ? beg + c1 * CH : end;
+    }
+    return r;
+}
+// workspace: piece states [n_seg][H][8][D][D] fp32, then piece log-decays [n_seg][H][8][D]
+__host__ __device__ inline size_t piece_log_offset(int n_seg, int H, int D) {
+    return (size_t)n_seg * H * kMaxPieces * D * D;
+}
+
+// 8 consecutive values at element e (zeros when !on; the address is not formed then)
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* base, size_t e, bool on, float* x) {
+    if constexpr (BF16) {
+        u32x4 w = u32x4{0u, 0u, 0u, 0u};
+        if (on) w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + e);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(w[i] << 16);
+            x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    } else {
+        f32x4 a = zero4(), b = zero4();
+        if (on) {
+            const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + e);
+            a = p[0];
+            b = p[1];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[4 + i] = b[i]; }
+    }
+}
+
 template <bool BF16>
 __device__ __forceinline__ float ld1(const void* base, size_t e) {
     if constexpr (BF16) return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[e]);
@@ -33,16 +82,19 @@ __device__ __forceinline__ float ld1(const void* base, size_t e) {
 }
 }  // namespace
 
-template <int D, bool BF16, int GATE>
+template <int D, bool BF16, int GATE, bool PIECES>
 __global__ __launch_bounds__(256) void build_decay_kernel(
     int n_seg, int H, const int64_t* __restrict__ seg_begin, const int64_t* __restrict__ seg_end,
     int64_t n_tokens, const void* __restrict__ k, const void* __restrict__ v,
-    const void* __restrict__ gl, void* __restrict__ T_out, int t_layout, float* __restrict__ S_out)
+    const void* __restrict__ gl, void* __restrict__ T_out, int t_layout, float* __restrict__ S_out,
+    float* __restrict__ piece_ws)
 {
     constexpr bool DIAG = GATE == 2;       // per-channel gate: the weights move from V to K
     constexpr int RT = D / 16;
     constexpr int NT = RT * RT;            // output tiles
     constexpr int TW = (NT + 3) / 4;       // tiles per wave
+    constexpr int CG = D / 8;              // 8-channel groups per token
+    constexpr int NIT = (CH * CG + 255) / 256;   // staging items per thread
     constexpr bool KSPLIT = !BF16 || DIAG; // keys need a lo plane (fp32, or weighted per channel)
     constexpr bool VSPLIT = !BF16 || !DIAG;
     __shared__ __attribute__((aligned(16))) uint16_t Kt[2][D][LDT];   // K^T (hi, lo); DIAG: weighted
@@ -52,12 +104,21 @@ __global__ __launch_bounds__(256) void build_decay_kernel(
     __shared__ float bcd[DIAG ? D : 1], logd[DIAG ? D : 1];  // DIAG: chunk total and segment total per channel
     __shared__ float bCs;
 
-    const int unit = blockIdx.x, seg = unit / H, h = unit % H;
+    // PIECES: one workgroup per (segment, head, piece); the piece's pair goes to the
+    // workspace and decay_fold_kernel composes the pieces
+    const int piece = PIECES ? blockIdx.x % kMaxPieces : 0;
+    const int unit = PIECES ? blockIdx.x / kMaxPieces : blockIdx.x, seg = unit / H, h = unit % H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g4 = lane >> 4, n16 = lane & 15;
     int64_t beg = seg_begin[seg], end = seg_end[seg];
     beg = beg < 0 ? 0 : (beg > n_tokens ? n_tokens : beg);
     end = end < beg ? beg : (end > n_tokens ? n_tokens : end);
+    if constexpr (PIECES) {
+        const PieceRange pr = piece_range(beg, end, piece);
+        if (pr.n_pieces <= piece) return;   // uniform: the segment has fewer pieces
+        beg = pr.beg;
+        end = pr.end;
+    }
 
     f32x4 acc[TW];
 #pragma unroll
@@ -74,9 +135,20 @@ __global__ __launch_bounds__(256) void build_decay_kernel(
         if constexpr (DIAG) {
             // per-channel gates, then the in-chunk inclusive cumulative sums b_t[ch] (one
             // channel per thread) and the chunk totals b_C[ch]
-            for (int it = tid; it < CH * D; it += 256) {
-                const int t = it / D, ch = it % D;
-                gd[t][ch] = t < n ? ld1<BF16>(gl, (size_t)(c0 + t) * stride + (size_t)h * D + ch) : 0.f;
+            {   // 8 channels of one token per item, every load of the thread issued first
+                float gx[NIT][8];
+#pragma unroll
+                for (int r = 0; r < NIT; ++r) {
+                    const int it = tid + 256 * r, t = it / CG, c8 = (it % CG) * 8;
+                    load8<BF16>(gl, (size_t)(c0 + t) * stride + (size_t)h * D + c8, it < CH * CG && t < n, gx[r]);
+                }
+#pragma unroll
+                for (int r = 0; r < NIT; ++r) {
+                    const int it = tid + 256 * r, t = it / CG, c8 = (it % CG) * 8;
+                    if (it < CH * CG)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) gd[t][c8 + e] = gx[r][e];
+                }
             }
             __syncthreads();
             for (int ch = tid; ch < D; ch += 256) {
@@ -108,23 +180,49 @@ __global__ __launch_bounds__(256) void build_decay_kernel(
             }
         }
         __syncthreads();
-        for (int it = tid; it < CH * D; it += 256) {
-            const int t = it / D, ch = it % D;  // consecutive threads: consecutive channels
-            float kx = 0.f, vx = 0.f;
-            if (t < n) {
-                const size_t e = (size_t)(c0 + t) * stride + (size_t)h * D + ch;
-                kx = ld1<BF16>(k, e);
-                vx = ld1<BF16>(v, e);
-                if constexpr (DIAG) kx *= expf(bcd[ch] - gd[t][ch]);   // key channel ch decays by e^{b_C - b_t}
-                else vx *= wsh[t];
+        {   // item: 4 tokens x 8 channels (4 loads of 8 channels), written as 4-token runs of 8
+            // channel rows of K^T and V^T; the token block is fastest across lanes, so the runs of
+            // one row from 16 lanes are contiguous
+            constexpr int NTB = CH / 4, NI = NTB * CG;
+            for (int it = tid; it < NI; it += 256) {
+                const int tb = it % NTB, c8 = (it / NTB) * 8;
+                float kx[4][8], vx[4][8];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 4 * tb + r;
+                    const size_t e = (size_t)(c0 + t) * stride + (size_t)h * D + c8;
+                    load8<BF16>(k, e, t < n, kx[r]);
+                    load8<BF16>(v, e, t < n, vx[r]);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 4 * tb + r;
+                    if (t < n) {
+#pragma unroll
+                        for (int x = 0; x < 8; ++x) {
+                            if constexpr (DIAG) kx[r][x] *= expf(bcd[c8 + x] - gd[t][c8 + x]);   // channel decays by e^{b_C - b_t}
+                            else vx[r][x] *= wsh[t];
+                        }
+                    }
+                }
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    unsigned kh[2], kl[2], vh[2], vl[2];
+#pragma unroll
+                    for (int r = 0; r < 2; ++r) {
+                        kh[r] = cvt2_bf16(kx[2 * r][x], kx[2 * r + 1][x]);
+                        const f32x2 kf = bf16x2_to_f32(kh[r]);
+                        kl[r] = cvt2_bf16(kx[2 * r][x] - kf.x, kx[2 * r + 1][x] - kf.y);
+                        vh[r] = cvt2_bf16(vx[2 * r][x], vx[2 * r + 1][x]);
+                        const f32x2 vf = bf16x2_to_f32(vh[r]);
+                        vl[r] = cvt2_bf16(vx[2 * r][x] - vf.x, vx[2 * r + 1][x] - vf.y);
+                    }
+                    *reinterpret_cast<u32x2*>(&Kt[0][c8 + x][4 * tb]) = u32x2{kh[0], kh[1]};
+                    *reinterpret_cast<u32x2*>(&Kt[1][c8 + x][4 * tb]) = u32x2{kl[0], kl[1]};
+                    *reinterpret_cast<u32x2*>(&Vt[0][c8 + x][4 * tb]) = u32x2{vh[0], vh[1]};
+                    *reinterpret_cast<u32x2*>(&Vt[1][c8 + x][4 * tb]) = u32x2{vl[0], vl[1]};
+                }
             }
-            __bf16 kh, kl, vh, vl;
-            split_bf16(kx, kh, kl);
-            split_bf16(vx, vh, vl);
-            Kt[0][ch][t] = bf16_bits(kh);
-            Kt[1][ch][t] = bf16_bits(kl);
-            Vt[0][ch][t] = bf16_bits(vh);
-            Vt[1][ch][t] = bf16_bits(vl);
         }
         __syncthreads();
         const float ebc = DIAG ? 0.f : expf(bCs);
@@ -161,7 +259,8 @@ __global__ __launch_bounds__(256) void build_decay_kernel(
     }
 
     const size_t pair = (size_t)seg * H + h;
-    float* S = S_out + pair * D * D;
+    const size_t slot = PIECES ? pair * kMaxPieces + piece : pair;
+    float* S = (PIECES ? piece_ws : S_out) + slot * D * D;
 #pragma unroll
     for (int i = 0; i < TW; ++i) {
         const int tile = wave + 4 * i;
@@ -169,6 +268,15 @@ __global__ __launch_bounds__(256) void build_decay_kernel(
         const int mt = tile / RT, nt = tile % RT;
 #pragma unroll
         for (int e = 0; e < 4; ++e) S[(size_t)(mt * 16 + 4 * g4 + e) * D + nt * 16 + n16] = acc[i][e];
+    }
+    if constexpr (PIECES) {   // the piece's log-decay (per key channel for the diagonal gate)
+        float* L = piece_ws + piece_log_offset(n_seg, H, D) + slot * (DIAG ? D : 1);
+        if constexpr (DIAG) {
+            for (int ch = tid; ch < D; ch += 256) L[ch] = logd[ch];
+        } else {
+            if (tid == 0) L[0] = log_t;
+        }
+        return;
     }
     if (T_out) {
         if constexpr (DIAG) {
@@ -190,24 +298,117 @@ __global__ __launch_bounds__(256) void build_decay_kernel(
     }
 }
 
+// Composition of a segment's pieces, in order: S = sum_p (prod_{q > p} t_q) S_p and
+// T = prod_p t_p, with t_p = e^{(log-decay of piece p)} a scalar, or per key channel (row of S)
+// for the diagonal gate.  One workgroup per (segment, head); 4 consecutive entries of one row per
+// thread and step.  A segment without tokens gets the identity pair.
+template <int D, bool DIAG>
+__global__ __launch_bounds__(256) void decay_fold_kernel(int n_seg, int H, const int64_t* __restrict__ seg_begin,
+                                                         const int64_t* __restrict__ seg_end, int64_t n_tokens,
+                                                         const float* __restrict__ piece_ws, void* __restrict__ T_out,
+                                                         int t_layout, float* __restrict__ S_out)
+{
+    const int unit = blockIdx.x, seg = unit / H, h = unit % H;
+    const int tid = threadIdx.x;
+    int64_t beg = seg_begin[seg], end = seg_end[seg];
+    beg = beg < 0 ? 0 : (beg > n_tokens ? n_tokens : beg);
+    end = end < beg ? beg : (end > n_tokens ? n_tokens : end);
+    const int np = piece_range(beg, end, 0).n_pieces;
+    const size_t pair = (size_t)seg * H + h;
+    const float* Lg = piece_ws + piece_log_offset(n_seg, H, D) + pair * kMaxPieces * (DIAG ? D : 1);
+    const f32x4* Sp = reinterpret_cast<const f32x4*>(piece_ws + pair * kMaxPieces * D * D);
+    f32x4* S = reinterpret_cast<f32x4*>(S_out + pair * D * D);
+    constexpr int NQ = D * D / 4;
+    // weight of piece p for row r: e^{log-decay of the pieces after p} (one row for scalar T)
+    __shared__ float wt[kMaxPieces][DIAG ? D : 1];
+    for (int r = tid; r < (DIAG ? D : 1); r += 256) {
+        float l[kMaxPieces];
+#pragma unroll
+        for (int p = 0; p < kMaxPieces; ++p) l[p] = p < np ? Lg[p * (DIAG ? D : 1) + r] : 0.f;
+        float lsum = 0.f;
+#pragma unroll
+        for (int p = kMaxPieces - 1; p >= 0; --p) {
+            wt[p][r] = __expf(lsum);
+            lsum += l[p];
+        }
+    }
+    __syncthreads();
+    for (int q = tid; q < NQ; q += 256) {
+        const int row = DIAG ? 4 * q / D : 0;
+        f32x4 sp[kMaxPieces];
+#pragma unroll
+        for (int p = 0; p < kMaxPieces; ++p) sp[p] = p < np ? Sp[(size_t)p * NQ + q] : zero4();
+        f32x4 x = zero4();
+#pragma unroll
+        for (int p = kMaxPieces - 1; p >= 0; --p)
+            if (p < np) x = x + wt[p][row] * sp[p];
+        S[q] = x;
+    }
+    if (T_out) {
+        if constexpr (DIAG) {
+            for (int ch = tid; ch < D; ch += 256) {
+                float l = 0.f;
+                for (int p = 0; p < np; ++p) l += Lg[p * D + ch];
+                if (t_layout == 3) reinterpret_cast<float*>(T_out)[pair * D + ch] = __expf(l);
+            }
+            if (t_layout != 3) {   // dense diag(t), fp32 or bf16 hi/lo planes
+                for (int it = tid; it < D * D; it += 256) {
+                    const int r = it / D, c = it % D;
+                    float l = 0.f;
+                    if (r == c)
+                        for (int p = 0; p < np; ++p) l += Lg[p * D + r];
+                    put_t(T_out, t_layout == 2, pair, D, r, c, r == c ? __expf(l) : 0.f);
+                }
+            }
+        } else {
+            float l = 0.f;
+            for (int p = 0; p < np; ++p) l += Lg[p];
+            const float tval = __expf(l);
+            if (t_layout == 1) {   // scalar
+                if (tid == 0) reinterpret_cast<float*>(T_out)[pair] = tval;
+            } else {               // dense t I, fp32 or bf16 hi/lo planes
+                for (int it = tid; it < D * D; it += 256)
+                    put_t(T_out, t_layout == 2, pair, D, it / D, it % D, (it / D == it % D) ? tval : 0.f);
+            }
+        }
+    }
+}
+
 template <int D, bool BF16, int GATE>
 static hipError_t launch_decay(int n_seg, int H, const int64_t* sb, const int64_t* se, int64_t n_tok,
                                const void* k, const void* v, const void* g, void* T_out, int t_layout,
-                               float* S_out, hipStream_t st)
+                               float* S_out, float* ws, hipStream_t st)
 {
-    hipLaunchKernelGGL((build_decay_kernel<D, BF16, GATE>), dim3(n_seg * H), dim3(256), 0, st, n_seg, H,
-                       sb, se, n_tok, k, v, g, T_out, t_layout, S_out);
+    if (ws == nullptr) {
+        hipLaunchKernelGGL((build_decay_kernel<D, BF16, GATE, false>), dim3(n_seg * H), dim3(256), 0, st, n_seg, H,
+                           sb, se, n_tok, k, v, g, T_out, t_layout, S_out, nullptr);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((build_decay_kernel<D, BF16, GATE, true>), dim3(n_seg * H * kMaxPieces), dim3(256), 0, st,
+                       n_seg, H, sb, se, n_tok, k, v, g, T_out, t_layout, S_out, ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decay_fold_kernel<D, GATE == 2>), dim3(n_seg * H), dim3(256), 0, st, n_seg, H, sb, se, n_tok,
+                       ws, T_out, t_layout, S_out);
     return hipGetLastError();
+}
+
+size_t decay_workspace_bytes(int d, int H, int n_seg, int64_t n_tokens, bool diag)
+{
+    // pieces pay where segments average at least 4 chunks (256 tokens)
+    if (n_seg < 1 || H < 1 || n_tokens < (int64_t)n_seg * 4 * CH) return 0;
+    return ((size_t)n_seg * H * kMaxPieces * ((size_t)d * d + (diag ? d : 1)) * sizeof(float) + 255) / 256 * 256;
 }
 
 hipError_t build_decay(int d, bool in_bf16, int gate, int n_seg, int H, const int64_t* sb,
                        const int64_t* se, int64_t n_tok, const void* k, const void* v, const void* g,
-                       void* T_out, int t_layout, float* S_out, hipStream_t st)
+                       void* T_out, int t_layout, float* S_out, void* ws, hipStream_t st)
 {
-#define HYPIC_GATES(D_, B_)                                                                                  \
-    if (gate == 0) return launch_decay<D_, B_, 0>(n_seg, H, sb, se, n_tok, k, v, g, T_out, t_layout, S_out, st); \
-    if (gate == 1) return launch_decay<D_, B_, 1>(n_seg, H, sb, se, n_tok, k, v, g, T_out, t_layout, S_out, st); \
-    return launch_decay<D_, B_, 2>(n_seg, H, sb, se, n_tok, k, v, g, T_out, t_layout, S_out, st);
+    float* w = static_cast<float*>(ws);
+#define HYPIC_GATES(D_, B_)                                                                                     \
+    if (gate == 0) return launch_decay<D_, B_, 0>(n_seg, H, sb, se, n_tok, k, v, g, T_out, t_layout, S_out, w, st); \
+    if (gate == 1) return launch_decay<D_, B_, 1>(n_seg, H, sb, se, n_tok, k, v, g, T_out, t_layout, S_out, w, st); \
+    return launch_decay<D_, B_, 2>(n_seg, H, sb, se, n_tok, k, v, g, T_out, t_layout, S_out, w, st);
 #define HYPIC_CASE(D_)                    \
     if (d == D_) {                        \
         if (in_bf16) { HYPIC_GATES(D_, true) } \

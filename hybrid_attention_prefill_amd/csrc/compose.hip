@@ -308,12 +308,27 @@ __global__ __launch_bounds__(256) void compose_scalar_kernel(
     f32x4* R = reinterpret_cast<f32x4*>(Srun + unit * (long long)(DK * DV)) + q;
     f32x4 r = *R;
     const int32_t* ids = pair_id + (size_t)c * n_step;
-    for (int j = 0; j < n_step; ++j) {
-        const int id = ids[j];
-        if ((unsigned)id >= (unsigned)n_pair) continue;
-        const float t = DIAG ? Tc[((size_t)id * H + h) * DK + row] : Tc[(size_t)id * H + h];
-        const f32x4 s = reinterpret_cast<const f32x4*>(Sc + ((size_t)id * H + h) * DK * DV)[q];
-        r = t * r + s;
+    // groups of 8 steps: the ids first, then every T and S of the group, then the updates
+    // (the loads of a group are in flight together instead of one dependent pair per step)
+    constexpr int G = 8;
+    for (int j0 = 0; j0 < n_step; j0 += G) {
+        int id[G];
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const int x = j0 + i < n_step ? ids[j0 + i] : -1;
+            id[i] = (unsigned)x < (unsigned)n_pair ? x : -1;
+        }
+        float t[G];
+        f32x4 sv[G];
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const size_t p = (size_t)(id[i] < 0 ? 0 : id[i]) * H + h;   // a skipped step reads pair 0, unused
+            t[i] = n_pair > 0 ? (DIAG ? Tc[p * DK + row] : Tc[p]) : 1.f;
+            sv[i] = n_pair > 0 ? reinterpret_cast<const f32x4*>(Sc + p * DK * DV)[q] : zero4();
+        }
+#pragma unroll
+        for (int i = 0; i < G; ++i)
+            if (id[i] >= 0) r = t[i] * r + sv[i];
     }
     *R = r;
 }

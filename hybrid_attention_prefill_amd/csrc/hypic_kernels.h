@@ -82,10 +82,13 @@ hipError_t build_kda(int d, bool in_bf16, bool gate_first, int n_seg, int H, con
                      float* S_out, hipStream_t st);
 
 // build_decay.hip (gate: 0 head-constant, 1 per-token scalar, 2 per-channel; no erase);
-// t_layout: 0 dense f32, 1 scalar, 2 dense bf16 hi/lo planes, 3 diagonal
+// t_layout: 0 dense f32, 1 scalar, 2 dense bf16 hi/lo planes, 3 diagonal.  ws (may be NULL):
+// decay_workspace_bytes(...) bytes; segments are then built as up to 8 pieces in parallel
+// and the pieces composed.  The bytes are 0 where pieces would not pay.
+size_t decay_workspace_bytes(int d, int H, int n_seg, int64_t n_tokens, bool diag);
 hipError_t build_decay(int d, bool in_bf16, int gate, int n_seg, int H, const int64_t* sb,
                        const int64_t* se, int64_t n_tok, const void* k, const void* v, const void* g,
-                       void* T_out, int t_layout, float* S_out, hipStream_t st);
+                       void* T_out, int t_layout, float* S_out, void* ws, hipStream_t st);
 
 // seam.hip
 hipError_t seam_prep(int d, int n_chain, int n_step, int H, const int64_t* seam_start, int64_t n_tokens,

@@ -118,11 +118,15 @@ typedef struct {
  *                        concurrent calls need distinct workspaces.  With it, long
  *                        segments are built as pieces in parallel and the pieces'
  *                        pairs folded by the composition law ([ZH] 2.1 and the segment
- *                        parallelism of 2.3): a segment of c > 16 64-token chunks is cut
- *                        on chunk boundaries into ceil(c / 16) near-equal pieces.  How a
- *                        segment is cut depends on its length only, so its pair does
- *                        not depend on the other segments of the call.  Without it (or
- *                        where the query returns 0) every segment is one serial chain.
+ *                        parallelism of 2.3).  Gated delta rule: a segment of c > 16
+ *                        64-token chunks is cut on chunk boundaries into ceil(c / 16)
+ *                        near-equal pieces.  Without the delta rule (delta 0): every
+ *                        segment of c chunks is cut into min(8, c) near-equal runs of
+ *                        chunks, whose scalar or diagonal transitions make the fold an
+ *                        elementwise weighted sum.  How a segment is cut depends on its
+ *                        length only, so its pair does not depend on the other segments
+ *                        of the call.  Without it (or where the query returns 0) every
+ *                        segment is one serial chain.
  * Implemented (d_k == d_v = d):
  *   gate HEAD, TOKEN or DIAG, delta 0 : d in {16, 32, 64, 128}, fp32 or bf16 inputs;
  *   gate TOKEN, delta 1 or 2    : d = 16 (fp32 or bf16), 64 or 128 (bf16);
@@ -137,11 +141,15 @@ hypic_status hypic_segment_build(const hypic_dims* dims, int32_t n_seg,
                                  void* T_out, float* S_out,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of build workspace that let hypic_segment_build cut long segments: non-zero
- * for gate TOKEN with the delta rule, bf16 inputs, d in {64, 128} and n_tokens of at
- * least 1024; 0 otherwise (the workspace is then ignored).  Sized for segments that do
- * not overlap: (2 d^2 4 bytes per head) per slot, floor(n_tokens / 1024) slots, plus
- * the plan; a segment whose pieces do not fit is built uncut. */
+/* Bytes of build workspace that let hypic_segment_build cut long segments; 0 where it
+ * would not (the workspace is then ignored).
+ *   gate TOKEN with the delta rule, bf16 inputs, d in {64, 128}, n_tokens >= 1024: sized
+ *     for segments that do not overlap, (2 d^2 4 bytes per head) per slot,
+ *     floor(n_tokens / 1024) slots, plus the plan; a segment whose pieces do not fit is
+ *     built uncut;
+ *   without the delta rule, segments averaging at least 256 tokens (n_tokens >= 256 n_seg):
+ *     8 pieces per (segment, head) of (d^2 + d) 4 bytes (diagonal gate; d^2 + 1 otherwise).
+ *   other combinations: 0. */
 size_t hypic_build_workspace_bytes(const hypic_dims* dims, int32_t n_seg, int64_t n_tokens);
 
 /*

@@ -94,14 +94,18 @@ def test_unsupported_reported(lib):
 
 
 def test_build_workspace_size(lib):
-    """Build workspace: only for the bf16 gated delta rule at d in {64, 128}, zero below
-    one 1024-token piece, growing with the token count."""
+    """Build workspace: for the bf16 gated delta rule at d in {64, 128}, zero below one
+    1024-token piece, growing with the token count; without the delta rule, 8 pieces per
+    (segment, head) where segments average at least 256 tokens."""
     assert hb.build_workspace_bytes(16, 128, 128, 128, 100_000) > 0
     assert hb.build_workspace_bytes(16, 128, 128, 128, 1023) == 0
     assert hb.build_workspace_bytes(16, 16, 16, 128, 100_000) == 0
     assert hb.build_workspace_bytes(16, 128, 128, 128, 100_000, in_dtype=hb.F32) == 0
     assert hb.build_workspace_bytes(16, 128, 128, 128, 100_000, gate=hb.GATE_DIAG) == 0
-    assert hb.build_workspace_bytes(16, 128, 128, 128, 100_000, delta=False) == 0
+    piece = lambda diag: 128 * 16 * 8 * (128 * 128 + (128 if diag else 1)) * 4
+    assert hb.build_workspace_bytes(16, 128, 128, 128, 100_000, delta=False) >= piece(False)
+    assert hb.build_workspace_bytes(16, 128, 128, 128, 100_000, gate=hb.GATE_DIAG, delta=False) >= piece(True)
+    assert hb.build_workspace_bytes(16, 128, 128, 128, 128 * 256 - 1, delta=False) == 0
     one = hb.build_workspace_bytes(16, 128, 128, 128, 1024)
     two = hb.build_workspace_bytes(16, 128, 128, 128, 2 * 1024)
     assert two - one == 16 * 2 * 128 * 128 * 4            # one more slot: T planes + S per head

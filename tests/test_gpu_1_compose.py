@@ -79,12 +79,15 @@ def test_compose_identity_T_is_plain_sum(layout):
     assert rel_f(Rg.cpu().numpy()[0], ref).max() < 1e-5
 
 
-def test_compose_scalar_T():
+@pytest.mark.parametrize("n_step", [5, 21])
+def test_compose_scalar_T(n_step):
+    """Scalar T (steps taken in groups of 8 by the kernel: 5 and 21 cover a partial group
+    and several), a skipped step and a repeated pair."""
     d, H = 64, 8
-    rng = np.random.default_rng(9)
+    rng = np.random.default_rng(9 + n_step)
     t = rng.uniform(0.5, 1.0, size=(6, H)).astype(np.float32)
     S = rng.standard_normal((6, H, d, d)).astype(np.float32)
-    ids = np.array([[0, 1, -1, 5, 2]], np.int32)
+    ids = np.array([[0, 1, -1, 5, 2]], np.int32) if n_step == 5 else rng.integers(-1, 6, size=(1, n_step)).astype(np.int32)
     ref = oracle.compose(t, S, ids, t_scalar=True)
     Rg = torch.zeros((1, H, d, d), device="cuda")
     hb.compose(dev(t, torch.float32), dev(S, torch.float32), dev(ids, torch.int32), Rg, t_layout=hb.T_SCALAR)

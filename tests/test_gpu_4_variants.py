@@ -173,3 +173,43 @@ def test_kda_gate_first_split_compose_matches_full():
     assert rel_f(Rg.cpu().numpy()[0], full).max() <= TOL["bf16"]
     naive = oracle.naive_sum(S, np.arange(4)[None, :])[0]
     assert rel_f(naive, full).min() > 20 * TOL["bf16"]
+
+
+# ---- builds without the erase cut into pieces (build workspace): up to 8 runs of whole
+# chunks per segment built in parallel and composed elementwise
+
+@pytest.mark.parametrize("name,in_dtype,t_layout", [
+    ("retnet-8h-d64", "bf16", hb.T_SCALAR), ("retnet-8h-d64", "bf16", hb.T_SPLIT),
+    ("mamba2-16h-d64-16k", "f32", hb.T_SCALAR), ("mamba2-16h-d64-16k", "bf16", hb.T_DENSE),
+    ("gla-16h-d128-16k", "bf16", hb.T_DIAG), ("gla-16h-d128-16k", "f32", hb.T_SPLIT)])
+def test_decay_build_in_pieces(name, in_dtype, t_layout):
+    """21, 1, 1, 10 and 4 chunks (ragged tails, one token) and an empty range, built in
+    pieces and as one chain, both against the oracle; a segment's pair is bit-identical
+    whether it is built alone or in the batch."""
+    kw = {} if name.startswith("retnet") else {"in_dtype": in_dtype}
+    W = wl.make(name, n_heads=2, lengths=[1300, 64, 1, 577, 200], **kw)
+    begin = np.concatenate([W.cache_begin, [7]])
+    end = np.concatenate([W.cache_end, [7]])
+    d = W.d_k
+    x = workload_tensors(W)
+    need = hb.build_workspace_bytes(2, d, d, len(begin), W.n_tokens, gate=W.gate, delta=False,
+                                    in_dtype=hb.BF16 if W.in_dtype == "bf16" else hb.F32)
+    assert need > 0
+    ws = torch.empty(need, device="cuda", dtype=torch.uint8)
+    print(W.name, in_dtype, t_layout, need, flush=True)
+
+    def build(b, e, workspace):
+        T, S = hb.segment_build(x["k"], x["v"], x["g"], x["beta"], dev(b, torch.int64), dev(e, torch.int64),
+                                gate=W.gate, delta=False, t_layout=t_layout, workspace=workspace)
+        torch.cuda.synchronize()
+        return T, S.cpu().numpy()
+
+    T0, S0 = oracle.segment_build(W.k, W.v, W.g, W.beta, begin, end, gate=W.gate, delta=False)
+    for workspace in (ws, None):
+        T, S = build(begin, end, workspace)
+        assert_pairs_close(_dense(T, t_layout, d), S, T0, S0, TOL[W.in_dtype], f"{W.name} ws={workspace is not None}")
+        assert np.all(S[-1] == 0)
+    Tb, Sb = build(begin, end, ws)
+    Ta, Sa = build(begin[3:4], end[3:4], ws)
+    assert np.array_equal(Sa[0], Sb[3])
+    assert torch.equal(Ta[0], Tb[3])
