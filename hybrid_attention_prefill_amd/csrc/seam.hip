@@ -18,8 +18,9 @@
 //     O  = scale diag(e^b) (Q R) + Mo U'                 (window outputs)
 //     R <- e^{b_w} R + K^T diag(e^{b_w - b}) U'          (state after the window)
 // One workgroup (4 waves) per (chain, step, head) window.  The two 16 x 16 Gram
-// products K K^T and Q K^T run on MFMA (bf16 operands: exact for bf16 inputs, a
-// hi/lo split for fp32 inputs), the rest in fp32 on the vector ALUs.  Wt, q, k
+// products K K^T and Q K^T and the products Wt = Cw K, U = Cu V run on MFMA (bf16
+// operands: exact for bf16 inputs, a hi/lo split for fp32 inputs and for the
+// coefficients), the small triangular solve in fp32 on the vector ALUs.  Wt, q, k
 // and Mo are written as bf16 hi/lo planes in MFMA fragment order (frag_off), so
 // the chain kernel fetches each operand fragment as one contiguous 1 KiB.
 #include "hypic_device.h"
@@ -205,36 +206,57 @@ __global__ __launch_bounds__(256) void seam_prep_kernel(
     }
     __syncthreads();
 
-    // ---- Wt, U, q and k planes ([16][D], 8 channels per thread)
+    // ---- Wt = Cw K and U = Cu V on MFMA: 16 x 16 times 16 x 16 tiles on v_mfma_f32_16x16x32_bf16
+    // with the k-rows 16..31 zero (lanes g >= 2 carry zeros), Cw / Cu split into bf16 hi + lo,
+    // K / V exact in bf16 for bf16 inputs (split too for fp32).  One tile (matrix, 16-column
+    // block) per wave at a time.  U's accumulator tile is its record's lane order (one 16-byte
+    // store per lane); Wt goes to its bf16 hi/lo planes.
+    for (int tile = wave; tile < 2 * (D / 16); tile += 4) {
+        const bool isu = tile >= D / 16;
+        const int cb = isu ? tile - D / 16 : tile;
+        const float (*C)[W + 1] = isu ? Cu : Cw;
+        const float (*X)[LD] = isu ? Vs : Ks;
+        bf16x8 ah, al, bh, bl;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const bool on = g4 < 2;
+            const float a = on ? C[n16][8 * g4 + j] : 0.f;
+            const float x = on ? X[8 * g4 + j][cb * 16 + n16] : 0.f;
+            __bf16 h, l;
+            split_bf16(a, h, l);
+            ah[j] = h;
+            al[j] = l;
+            split_bf16(x, h, l);
+            bh[j] = h;
+            bl[j] = l;
+        }
+        f32x4 acc = mma_bf16(ah, bh, zero4());
+        acc = mma_bf16(al, bh, acc);
+        if (!in_bf16) acc = mma_bf16(ah, bl, acc);
+        if (isu) {   // block cb, lane (g, n): rows 4g .. 4g+3 of column 16 cb + n
+            reinterpret_cast<f32x4*>(rp + R::kU)[cb * 64 + lane] = acc;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int off = frag_off(4 * g4 + e, cb * 16 + n16, D);
+                __bf16 h, l;
+                split_bf16(acc[e], h, l);
+                reinterpret_cast<uint16_t*>(rp + R::kW)[off] = bf16_bits(h);
+                reinterpret_cast<uint16_t*>(rp + R::kW + R::kPlaneWD)[off] = bf16_bits(l);
+            }
+        }
+    }
+    // ---- q and k planes ([16][D], 8 channels per thread; bf16 q and k are exact in the hi
+    // plane, their lo planes are neither written nor read)
     {
         constexpr int CG = D / 8;
         for (int it = tid; it < W * CG; it += 256) {
             const int t = it / CG, c0 = (it % CG) * 8;
-            float wk[8], uv[8], qx[8];
-#pragma unroll
-            for (int x = 0; x < 8; ++x) { wk[x] = 0.f; uv[x] = 0.f; qx[x] = Qs[t][c0 + x]; }
-            for (int s = 0; s <= t; ++s) {
-                const float cw = Cw[t][s], cu = Cu[t][s];
-#pragma unroll
-                for (int x = 0; x < 8; ++x) {
-                    wk[x] += cw * Ks[s][c0 + x];
-                    uv[x] += cu * Vs[s][c0 + x];
-                }
-            }
             const int off = frag_off(t, c0, D) * 2;
-            put_split8(reinterpret_cast<uint16_t*>(rp + R::kW + off),
-                       reinterpret_cast<uint16_t*>(rp + R::kW + R::kPlaneWD + off), wk);
-            // bf16 q and k are exact in the hi plane; their lo planes are neither written nor read
             put_split8(reinterpret_cast<uint16_t*>(rp + R::kQ + off),
-                       in_bf16 ? nullptr : reinterpret_cast<uint16_t*>(rp + R::kQ + R::kPlaneWD + off), qx);
+                       in_bf16 ? nullptr : reinterpret_cast<uint16_t*>(rp + R::kQ + R::kPlaneWD + off), &Qs[t][c0]);
             put_split8(reinterpret_cast<uint16_t*>(rp + R::kK + off),
                        in_bf16 ? nullptr : reinterpret_cast<uint16_t*>(rp + R::kK + R::kPlaneWD + off), &Ks[t][c0]);
-            float* up = reinterpret_cast<float*>(rp + R::kU);
-#pragma unroll
-            for (int x = 0; x < 8; ++x) {   // block cb = ch / 16, lane (t / 4, ch % 16), element t % 4
-                const int ch = c0 + x;
-                up[((ch >> 4) * 64 + (t >> 2) * 16 + (ch & 15)) * 4 + (t & 3)] = uv[x];
-            }
         }
     }
 }

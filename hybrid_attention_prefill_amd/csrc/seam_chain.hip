@@ -560,61 +560,60 @@ __global__ __launch_bounds__(512) void seam_readout_kernel(
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g4 = lane >> 4, n16 = lane & 15;
     const float* R = trail + (((size_t)c * (nblk - 1) + (b - 1)) * H + h) * DK * DV;
-    {   // 4 consecutive columns of one row per item; all of a thread's loads issued together
-        constexpr int NI = DK * DV / 4, PER = (NI + 511) / 512;
-        f32x4 r4[PER];
+    const int j = b * blk + grp * 8 + wave;
+    const bool live = grp * 8 + wave < blk && j < n_step;
+    const size_t cj = (size_t)c * n_step + (live ? j : 0);
+    const int64_t s0 = live ? seam_start[cj] : -1;
+    const bool has = live && s0 >= 0 && s0 + w <= n_tokens;   // a window at this step (uniform)
+    // this wave's readout rows first (they do not depend on R_in): A fragments of the
+    // transition half (row t = n16, k = 32 ks + 8 g4 + 0..7) and the state half (the
+    // accumulators' initial values)
+    f32x4 a0[KS], a1[KS], hx[NT];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const int k0 = ks * 32 + 8 * g4;
+        a0[ks] = a1[ks] = zero4();
+        if (has && n16 < w && k0 < DK) {
+            const f32x4* p = reinterpret_cast<const f32x4*>(ox + ((cj * w + n16) * H + h) * 2 * DV + k0);
+            a0[ks] = p[0];
+            a1[ks] = p[1];
+        }
+    }
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t = 4 * g4 + e;
+            hx[ct][e] = has && t < w ? ox[((cj * w + t) * H + h) * 2 * DV + DV + ct * 16 + n16] : 0.f;
+        }
+    {   // R_in: item = (4 rows, 1 column), columns fastest across lanes (coalesced loads), written
+        // as 4-row runs of a column row of the planes; every load of the thread issued first
+        constexpr int NI = (KP / 4) * DV, PER = (NI + 511) / 512;
+        float r4[PER][4];
 #pragma unroll
         for (int x = 0; x < PER; ++x) {
-            const int i = threadIdx.x + 512 * x;
-            r4[x] = i < NI ? reinterpret_cast<const f32x4*>(R)[i] : zero4();
+            const int i = threadIdx.x + 512 * x, col = i % DV, k0 = 4 * (i / DV);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r4[x][e] = (i < NI && k0 + e < DK) ? R[(size_t)(k0 + e) * DV + col] : 0.f;
         }
 #pragma unroll
         for (int x = 0; x < PER; ++x) {
-            const int i = threadIdx.x + 512 * x;
-            if (i < NI) {
-                const int k = 4 * i / DV, col = 4 * i % DV;
+            const int i = threadIdx.x + 512 * x, col = i % DV, k0 = 4 * (i / DV);
+            if (i >= NI) continue;
+            unsigned hh[2], ll[2];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    __bf16 hi, lo;
-                    split_bf16(r4[x][e], hi, lo);
-                    Rh[col + e][k] = bf16_bits(hi);
-                    Rl[col + e][k] = bf16_bits(lo);
-                }
+            for (int e = 0; e < 2; ++e) {
+                hh[e] = cvt2_bf16(r4[x][2 * e], r4[x][2 * e + 1]);
+                const f32x2 hv = bf16x2_to_f32(hh[e]);
+                ll[e] = cvt2_bf16(r4[x][2 * e] - hv.x, r4[x][2 * e + 1] - hv.y);
             }
-        }
-        for (int i = threadIdx.x; i < (KP - DK) * DV; i += blockDim.x) {   // rows past d_k are zero
-            Rh[i % DV][DK + i / DV] = 0;
-            Rl[i % DV][DK + i / DV] = 0;
+            *reinterpret_cast<u32x2*>(&Rh[col][k0]) = u32x2{hh[0], hh[1]};
+            *reinterpret_cast<u32x2*>(&Rl[col][k0]) = u32x2{ll[0], ll[1]};
         }
     }
     __syncthreads();
-
-    const int j = b * blk + grp * 8 + wave;
-    if (grp * 8 + wave >= blk || j >= n_step) return;
+    if (!has) return;
     {
-        const size_t cj = (size_t)c * n_step + j;
-        const int64_t s0 = seam_start[cj];
-        if (s0 < 0 || s0 + w > n_tokens) return;   // no window at this step (uniform)
-        // A fragments: row t = n16 of the transition readout, k = 32 ks + 8 g4 + 0..7; the
-        // state-half readout (the accumulators' initial values) loaded with them
-        f32x4 a0[KS], a1[KS], hx[NT];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int k0 = ks * 32 + 8 * g4;
-            a0[ks] = a1[ks] = zero4();
-            if (n16 < w && k0 < DK) {
-                const f32x4* p = reinterpret_cast<const f32x4*>(ox + ((cj * w + n16) * H + h) * 2 * DV + k0);
-                a0[ks] = p[0];
-                a1[ks] = p[1];
-            }
-        }
-#pragma unroll
-        for (int ct = 0; ct < NT; ++ct)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 4 * g4 + e;
-                hx[ct][e] = t < w ? ox[((cj * w + t) * H + h) * 2 * DV + DV + ct * 16 + n16] : 0.f;
-            }
         bf16x8 ah[KS], al[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {

@@ -208,3 +208,43 @@ def test_seam_scan_two_chains_mixed_plan(d):
             if pid[c, j] >= 0:
                 Sr = T0[pid[c, j]] @ Sr + S0[pid[c, j]]
         assert rel_f(R[c], Sr).max() <= TOL["bf16"], (c, rel_f(R[c], Sr).max())
+
+
+def test_seam_scan_blocks_longer_than_the_id_ring():
+    """32 chains x 600 steps, 4 heads, d = 64, w = 2: the call runs 2 blocks of 300 steps
+    (longer than the kernel's 256-step id ring, so the ring refills inside a block).
+    Every chain starts from its own state and reuses the same segments; all outputs and
+    final states against the oracle (fp64 composition of the oracle's own pairs)."""
+    rng = np.random.default_rng(21)
+    H, d, w, n, n_chain = 4, 64, 2, 600, 32
+    W = _seam_workload("gdn-16h-d128-32k", [6] * n, w, H=H, stress=True, d=d)
+    starts = W.seg_start
+    seam = np.tile(starts[:-1], (n_chain, 1)).astype(np.int64)
+    seam[:, 0] = -1
+    pid = np.tile(np.arange(n, dtype=np.int32), (n_chain, 1))
+    R0 = rng.standard_normal((n_chain, H, d, d)) * 0.3
+    x = workload_tensors(W)
+    T, S = hb.segment_build(x["k"], x["v"], x["g"], x["beta"], dev(W.cache_begin, torch.int64),
+                            dev(W.cache_end, torch.int64), gate=W.gate, delta=W.delta, t_layout=hb.T_SPLIT)
+    R = dev(R0, torch.float32)
+    out = torch.full((n_chain, n, w, H, d), float("nan"), device="cuda")
+    print("600-step chains", flush=True)
+    hb.seam_advance(x["q"], x["k"], x["v"], x["g"], x["beta"], dev(seam, torch.int64), R, out,
+                    gate=W.gate, delta=W.delta, w=w, scale=W.scale, pair_id=dev(pid, torch.int32),
+                    T_cache=T, S_cache=S)
+    torch.cuda.synchronize()
+    R, out = R.cpu().numpy(), out.cpu().numpy()
+    T0, S0 = oracle.segment_build(W.k, W.v, W.g, W.beta, W.cache_begin, W.cache_end, gate=W.gate, delta=True)
+    Sr = R0.copy()                                   # [chain][head][d][d], all chains at once
+    worst = 0.0
+    for j in range(n):
+        if j > 0:
+            a = int(starts[j])
+            for c in range(n_chain):
+                Sr[c], o = oracle.run(W.k, W.v, W.g, W.beta, gate=W.gate, delta=True, t0=a, t1=a + w, S0=Sr[c],
+                                      q=W.q, scale=W.scale)
+                worst = max(worst, float(rel_f(np.transpose(out[c, j], (1, 0, 2)), np.transpose(o, (1, 0, 2))).max()))
+        Sr = T0[j][None] @ Sr + S0[j][None]
+    assert worst <= TOL["bf16"], worst
+    assert np.all(np.isnan(out[:, 0]))
+    assert rel_f(R, Sr).max() <= TOL["bf16"], rel_f(R, Sr).max()
