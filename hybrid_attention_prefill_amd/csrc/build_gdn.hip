@@ -44,11 +44,11 @@ using namespace bld;
 constexpr int CH = 64;       // chunk length
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <int D, int NSPLIT>
+template <int D, int NSPLIT, int KTB>
 struct alignas(16) GdnSmem {
     static constexpr int KP = D < 32 ? 32 : D;  // channel contraction padded to 32
     uint16_t Kr[NSPLIT][CH * KP];  // K, rows = tokens, cols = channels (>= D zero)
-    uint16_t Kt[NSPLIT][D * CH];   // K^T, rows = channels, cols = tokens
+    uint16_t Kt[KTB][NSPLIT][D * CH];   // K^T, rows = channels, cols = tokens (KTB = 2: by chunk parity)
     uint16_t Vt[NSPLIT][D * CH];   // V^T, rows = channels, cols = tokens
     uint16_t Wt[NSPLIT][CH * KP];  // Wt, rows = tokens, cols = channels (>= D zero)
     // block forward substitution operands: A fragments of v_mfma_f32_16x16x16_f16 (lane
@@ -137,7 +137,11 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
     const void* __restrict__ gl, const void* __restrict__ beta, void* __restrict__ T_out, int t_split,
     float* __restrict__ S_out, BuildItems items, BuildOut ob)
 {
-    using SM = GdnSmem<D, NSPLIT>;
+    // Without outputs the next chunk is staged at the end of this chunk's state update (K^T
+    // double-buffered by chunk parity), which saves a barrier and overlaps the staging with
+    // the tail of the state-update products; with outputs q's plane is still in use then.
+    constexpr bool PIPE = !OUT;
+    using SM = GdnSmem<D, NSPLIT, PIPE ? 2 : 1>;
     static_assert(!OUT || (NSPLIT == 1 && BF16 && D >= 64), "outputs: bf16 inputs, d 64 or 128");
     constexpr int KP = SM::KP;
     constexpr int KSD = KP / 32;            // k-steps over channels
@@ -274,37 +278,16 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
         }
     };
 
-    if (beg < end) {
-        fetch_q(beg, 0);
-        if (beg + CH < end) fetch_q(beg + CH, 1);
-        prefetch(beg);
-    }
-    if constexpr (OUT) {
-        // the output products read M in 32-column blocks: of the tiles above the diagonal,
-        // (0, 1) and (2, 3) fall inside one and stay zero (the others are never read)
-        for (int i = tid; i < 512; i += 512) {
-            const int ti = i < 256 ? 0 : 2, r = (i & 255) >> 4, c = i & 15;
-            so.Mq[0][lds_off(16 * ti + r, 16 * (ti + 1) + c, CH)] = 0;
-        }
-        // the first chunk's q is in LDS before it is staged
-        __builtin_amdgcn_s_waitcnt(0x0070);
-        __syncthreads();
-    }
-
-    for (int64_t c0 = beg; c0 < end; c0 += CH) {
-        const int n = (int)((end - c0) < CH ? (end - c0) : CH);
-        // lane-derived indices, recomputed per chunk (cheap) rather than kept live across it
-        const int lane_c = opaque(lane);
-        const int g4 = lane_c >> 4, n16 = lane_c & 15, lx = lane_c ^ g4;
+    // ---- stage a chunk of n_s tokens from the prefetched registers: K token-major, K^T (into
+    // buffer kbuf) and V^T channel-major (16-bit), gates and betas
+    auto stage_kv = [&](int n_s, int kbuf) {
         const int tb = opaque(tb0), cb = opaque(cb0);
-        const int qbuf = (int)(((c0 - beg) / CH) & 1);
-        // ---- 1. stage the chunk: K token-major, K^T and V^T channel-major (16-bit), gates
         if (has_blk) {
             // the 4 x 8 block; rows past the segment are zeroed (only the last chunk has any)
-            if (n < CH) {
+            if (n_s < CH) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    if (tb * 4 + r >= n)
+                    if (tb * 4 + r >= n_s)
 #pragma unroll
                         for (int x = 0; x < WPR; ++x) raw[r][x] = u32x4{0u, 0u, 0u, 0u};
             }
@@ -313,7 +296,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
             for (int r = 0; r < 4; ++r)
 #pragma unroll
                 for (int c = 0; c < 8; ++c) f[r][c] = raw_val(r, c);
-            uint16_t(*dst)[D * CH] = blk_v ? sm.Vt : sm.Kt;
+            uint16_t(*dst)[D * CH] = blk_v ? sm.Vt : sm.Kt[kbuf];
             if constexpr (NSPLIT == 1 && BF16) {
                 // bf16 values are exact in fp16 (inside its range): round-toward-zero packing is exact
                 auto pk = [](float a, float b) -> unsigned {
@@ -353,6 +336,46 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                 }
             }
         }
+        if (wave == 0) {
+            const bool ok = lane < n_s;
+            sm.gate[lane] = ok ? raw1(graw) : 0.f;
+            sm.beta[lane] = ok ? raw1(braw) : 0.f;
+        }
+    };
+
+    if (beg < end) {
+        fetch_q(beg, 0);
+        if (beg + CH < end) fetch_q(beg + CH, 1);
+        prefetch(beg);
+    }
+    if constexpr (OUT) {
+        // the output products read M in 32-column blocks: of the tiles above the diagonal,
+        // (0, 1) and (2, 3) fall inside one and stay zero (the others are never read)
+        for (int i = tid; i < 512; i += 512) {
+            const int ti = i < 256 ? 0 : 2, r = (i & 255) >> 4, c = i & 15;
+            so.Mq[0][lds_off(16 * ti + r, 16 * (ti + 1) + c, CH)] = 0;
+        }
+        // the first chunk's q is in LDS before it is staged
+        __builtin_amdgcn_s_waitcnt(0x0070);
+        __syncthreads();
+    }
+
+    if constexpr (PIPE) {   // the first chunk staged before the loop
+        if (beg < end) {
+            stage_kv((int)((end - beg) < CH ? (end - beg) : CH), 0);
+            if (beg + CH < end) prefetch(beg + CH);
+        }
+        __syncthreads();
+    }
+
+    for (int64_t c0 = beg; c0 < end; c0 += CH) {
+        const int n = (int)((end - c0) < CH ? (end - c0) : CH);
+        // lane-derived indices, recomputed per chunk (cheap) rather than kept live across it
+        const int lane_c = opaque(lane);
+        const int g4 = lane_c >> 4, n16 = lane_c & 15, lx = lane_c ^ g4;
+        const int tb = opaque(tb0), cb = opaque(cb0);
+        const int qbuf = (int)(((c0 - beg) / CH) & 1);
+        const int ktb = PIPE ? qbuf : 0;   // K^T buffer of this chunk
         if constexpr (OUT) {
             if (has_blk && blk_v) {   // q block (tb, cb) to the fp16 plane Qr; rows past the segment zeroed
                 auto pk = [](float a, float b) -> unsigned {
@@ -371,14 +394,12 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                 }
             }
         }
-        if (wave == 0) {
-            const bool ok = lane < n;
-            sm.gate[lane] = ok ? raw1(graw) : 0.f;
-            sm.beta[lane] = ok ? raw1(braw) : 0.f;
+        if constexpr (!PIPE) {
+            stage_kv(n, 0);
+            // the next chunk's loads fly during this chunk
+            if (c0 + CH < end) prefetch(c0 + CH);
+            __syncthreads();
         }
-        // the next chunk's loads fly during this chunk
-        if (c0 + CH < end) prefetch(c0 + CH);
-        __syncthreads();
 
         // ---- 2. gate cumsum (every wave, one token per lane, in log2 units) and the Gram
         // blocks Lt = tril(b K K^T, -1): the diagonal 16 x 16 blocks are inverted by waves 0..3
@@ -533,7 +554,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                     if (!own_tile(c)) continue;
                     const bool is_s = s_tile(c);
                     const int q = is_s ? wave + 8 * c - RT : wave + 8 * c;   // channel / value tile
-                    const uint16_t(*rhs_src)[D * CH] = is_s ? sm.Vt : sm.Kt;
+                    const uint16_t(*rhs_src)[D * CH] = is_s ? sm.Vt : sm.Kt[ktb];
                     // right-hand side diag(beta) K_i (or V_i): lane (g, n) = rows 16i + 4g + e, column 16q + n
                     f32x4 acc;
                     {
@@ -693,12 +714,18 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const Frag<NSPLIT> a = frag_of<NSPLIT, CH>(sm.Kt, rt, kb, lx);
+                for (int kbk = 0; kbk < 2; ++kbk) {
+                    const Frag<NSPLIT> a = frag_of<NSPLIT, CH>(sm.Kt[ktb], rt, kbk, lx);
 #pragma unroll
                     for (int c = 0; c < CTW; ++c)
-                        if (upd_tile(c)) X[rt][c] = mma<NSPLIT>(a, rb[kb][c], X[rt][c]);
+                        if (upd_tile(c)) X[rt][c] = mma<NSPLIT>(a, rb[kbk][c], X[rt][c]);
                 }
+        }
+        if constexpr (PIPE) {   // the next chunk into the other K^T buffer, then the one after into registers
+            if (c0 + CH < end) {
+                stage_kv((int)((end - c0 - CH) < CH ? (end - c0 - CH) : CH), ktb ^ 1);
+                if (c0 + 2 * CH < end) prefetch(c0 + 2 * CH);
+            }
         }
         log_s += bC;
         __syncthreads();
