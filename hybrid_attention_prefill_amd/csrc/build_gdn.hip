@@ -44,12 +44,13 @@ using namespace bld;
 constexpr int CH = 64;       // chunk length
 constexpr float kLog2e = 1.4426950408889634f;
 
+// KTB = 2: the per-chunk inputs and decay factors are double-buffered by chunk parity
 template <int D, int NSPLIT, int KTB>
 struct alignas(16) GdnSmem {
     static constexpr int KP = D < 32 ? 32 : D;  // channel contraction padded to 32
     uint16_t Kr[NSPLIT][CH * KP];  // K, rows = tokens, cols = channels (>= D zero)
-    uint16_t Kt[KTB][NSPLIT][D * CH];   // K^T, rows = channels, cols = tokens (KTB = 2: by chunk parity)
-    uint16_t Vt[NSPLIT][D * CH];   // V^T, rows = channels, cols = tokens
+    uint16_t Kt[KTB][NSPLIT][D * CH];   // K^T, rows = channels, cols = tokens
+    uint16_t Vt[KTB][NSPLIT][D * CH];   // V^T, rows = channels, cols = tokens
     uint16_t Wt[NSPLIT][CH * KP];  // Wt, rows = tokens, cols = channels (>= D zero)
     // block forward substitution operands: A fragments of v_mfma_f32_16x16x16_f16 (lane
     // 16 g + r holds row r, columns 4 g .. 4 g + 3), fp16 hi / lo planes
@@ -58,8 +59,9 @@ struct alignas(16) GdnSmem {
     uint16_t Dv[2][4][256];        // (I + Lt_ii)^-1, diagonal block i
     uint16_t Dvd[2][4][256];       // the same with the decay e^{b_t - b_s}
     float Sd[4][16][20];           // per diagonal block: Lt_ii, then its inverse (fp32)
-    float gate[CH], beta[CH], b[CH], eb[CH], ebr[CH];   // b in log2 units
-    float bC;
+    float beta[KTB][CH];
+    float lb[KTB][CH], eb[KTB][CH], ebr[KTB][CH];   // b_t (log2 units), e^{b_t}, e^{b_C - b_t}
+    float bC[KTB];
 };
 
 // LDS of the per-token outputs (OUT): q of this or the next chunk as loaded (bf16,
@@ -278,8 +280,8 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
         }
     };
 
-    // ---- stage a chunk of n_s tokens from the prefetched registers: K token-major, K^T (into
-    // buffer kbuf) and V^T channel-major (16-bit), gates and betas
+    // ---- stage a chunk of n_s tokens from the prefetched registers into the buffers of
+    // parity kbuf: K token-major, K^T and V^T channel-major (16-bit), betas and log-decays
     auto stage_kv = [&](int n_s, int kbuf) {
         const int tb = opaque(tb0), cb = opaque(cb0);
         if (has_blk) {
@@ -296,7 +298,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
             for (int r = 0; r < 4; ++r)
 #pragma unroll
                 for (int c = 0; c < 8; ++c) f[r][c] = raw_val(r, c);
-            uint16_t(*dst)[D * CH] = blk_v ? sm.Vt : sm.Kt[kbuf];
+            uint16_t(*dst)[D * CH] = blk_v ? sm.Vt[kbuf] : sm.Kt[kbuf];
             if constexpr (NSPLIT == 1 && BF16) {
                 // bf16 values are exact in fp16 (inside its range): round-toward-zero packing is exact
                 auto pk = [](float a, float b) -> unsigned {
@@ -337,9 +339,22 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
             }
         }
         if (wave == 0) {
+            // betas, and the log-decays b_t = g_1 + .. + g_t of the chunk (inclusive scan over
+            // the lanes, one token each) with the decay factors of the state update (v_exp_f32)
             const bool ok = lane < n_s;
-            sm.gate[lane] = ok ? raw1(graw) : 0.f;
-            sm.beta[lane] = ok ? raw1(braw) : 0.f;
+            sm.beta[kbuf][lane] = ok ? raw1(braw) : 0.f;
+            float x = ok ? raw1(graw) : 0.f;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(x, off, 64);
+                if (lane >= off) x += y;
+            }
+            const float bc = __shfl(x, 63, 64);
+            const float b2 = x * kLog2e;
+            sm.lb[kbuf][lane] = b2;
+            sm.eb[kbuf][lane] = __builtin_amdgcn_exp2f(b2);
+            sm.ebr[kbuf][lane] = __builtin_amdgcn_exp2f(bc * kLog2e - b2);
+            if (lane == 0) sm.bC[kbuf] = bc;
         }
     };
 
@@ -360,68 +375,18 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
         __syncthreads();
     }
 
-    if constexpr (PIPE) {   // the first chunk staged before the loop
-        if (beg < end) {
-            stage_kv((int)((end - beg) < CH ? (end - beg) : CH), 0);
-            if (beg + CH < end) prefetch(beg + CH);
-        }
-        __syncthreads();
-    }
+    // lane-derived indices are recomputed in each phase (cheap) rather than kept live
+    // across it.  Buffers of parity `par` hold the chunk's K^T, V^T, gates, betas and
+    // decay factors.
+    f32x4 U[4][CTW];   // the solved value block of this wave's S tiles (phase 3 -> phase 4)
 
-    for (int64_t c0 = beg; c0 < end; c0 += CH) {
-        const int n = (int)((end - c0) < CH ? (end - c0) : CH);
-        // lane-derived indices, recomputed per chunk (cheap) rather than kept live across it
+    // ---- 2. Gram blocks Lt = tril(b K K^T, -1) of the chunk at c0: the diagonal 16 x 16
+    // blocks are inverted by waves 0..3 (forward substitution, fp32), the off-diagonal blocks
+    // stored negated by waves 4..7
+    auto phase_gram = [&](int64_t c0, int par) {
         const int lane_c = opaque(lane);
         const int g4 = lane_c >> 4, n16 = lane_c & 15, lx = lane_c ^ g4;
-        const int tb = opaque(tb0), cb = opaque(cb0);
-        const int qbuf = (int)(((c0 - beg) / CH) & 1);
-        const int ktb = PIPE ? qbuf : 0;   // K^T buffer of this chunk
-        if constexpr (OUT) {
-            if (has_blk && blk_v) {   // q block (tb, cb) to the fp16 plane Qr; rows past the segment zeroed
-                auto pk = [](float a, float b) -> unsigned {
-                    return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a, b));
-                };
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = tb * 4 + r;
-                    u32x4 w = *reinterpret_cast<const u32x4*>(&so.Qraw[qbuf][t * D + cb * 8]);
-                    if (t >= n) w = u32x4{0u, 0u, 0u, 0u};
-                    u32x4 o;
-#pragma unroll
-                    for (int x = 0; x < 4; ++x)
-                        o[x] = pk(__uint_as_float(w[x] << 16), __uint_as_float(w[x] & 0xFFFF0000u));
-                    *reinterpret_cast<u32x4*>(&so.Qr[0][lds_off(t, cb * 8, KP)]) = o;
-                }
-            }
-        }
-        if constexpr (!PIPE) {
-            stage_kv(n, 0);
-            // the next chunk's loads fly during this chunk
-            if (c0 + CH < end) prefetch(c0 + CH);
-            __syncthreads();
-        }
-
-        // ---- 2. gate cumsum (every wave, one token per lane, in log2 units) and the Gram
-        // blocks Lt = tril(b K K^T, -1): the diagonal 16 x 16 blocks are inverted by waves 0..3
-        // (forward substitution, fp32), the off-diagonal blocks stored negated by waves 4..7
-        float b2;   // b_lane * log2(e)
-        {
-            float x = sm.gate[lane];
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(x, off, 64);
-                if (lane >= off) x += y;
-            }
-            const float bc = __shfl(x, 63, 64);
-            b2 = x * kLog2e;
-            if (wave == 0) {   // decay factors of the state update, through v_exp_f32 (2^x)
-                const float bc2 = bc * kLog2e;
-                sm.b[lane] = b2;
-                sm.eb[lane] = __builtin_amdgcn_exp2f(b2);
-                sm.ebr[lane] = __builtin_amdgcn_exp2f(bc2 - b2);
-                if (lane == 0) sm.bC = bc;
-            }
-        }
+        const float* const lb = sm.lb[par];
         auto gram = [&](int ti, int tj) -> f32x4 {   // lane (g, n): G[16 ti + 4g + e][16 tj + n]
             f32x4 gacc = zero4();
 #pragma unroll
@@ -434,8 +399,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
         };
         // M = scale (Q K^T o e^{b_t - b_s}), s <= t, as an fp16 operand plane, tile by tile:
         // tile idx = 0..9 is (ti, tj), tj <= ti, row-major over the lower triangle of 16 x 16
-        // tiles (the tiles above it are zero or never read).  Log-decays by lane shuffles of
-        // b2 (every wave holds them; sm.b is written during this phase).
+        // tiles (the tiles above it are zero or never read).
         auto mq_tile = [&](int idx) {
             if constexpr (OUT) {
                 const int ti = idx < 1 ? 0 : idx < 3 ? 1 : idx < 6 ? 2 : 3;
@@ -447,12 +411,12 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                     const Frag<1> bb = frag_of<1, KP>(sm.Kr, tj, ks, lx);
                     m = mma<1>(a, bb, m);
                 }
-                const float bs = __shfl(b2, 16 * tj + n16, 64);
+                const float bs = lb[16 * tj + n16];
+                const f32x4 bt = *reinterpret_cast<const f32x4*>(&lb[16 * ti + 4 * g4]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int t = 16 * ti + 4 * g4 + e;
-                    const float bt = __shfl(b2, t, 64);
-                    const float x = (16 * tj + n16 <= t) ? ob.scale * m[e] * __builtin_amdgcn_exp2f(bt - bs) : 0.f;
+                    const float x = (16 * tj + n16 <= t) ? ob.scale * m[e] * __builtin_amdgcn_exp2f(bt[e] - bs) : 0.f;
                     so.Mq[0][lds_off(t, 16 * tj + n16, CH)] = f16_bits((_Float16)x);
                 }
             }
@@ -460,11 +424,9 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
         if (wave < 4) {
             const int i = wave;
             const f32x4 gacc = gram(i, i);
+            const f32x4 bet = *reinterpret_cast<const f32x4*>(&sm.beta[par][16 * i + 4 * g4]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * g4 + e;
-                sm.Sd[i][r][n16] = (n16 < r) ? sm.beta[16 * i + r] * gacc[e] : 0.f;
-            }
+            for (int e = 0; e < 4; ++e) sm.Sd[i][4 * g4 + e][n16] = (n16 < 4 * g4 + e) ? bet[e] * gacc[e] : 0.f;
             // column j = lane of (I + Lt_ii)^-1 by forward substitution; every read of the block
             // precedes the first write back (one wave, in order)
             if (lane < 16) {
@@ -480,14 +442,14 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                 for (int r = 0; r < 16; ++r) sm.Sd[i][r][lane] = x[r];
             }
             // A fragment: lane (g, n) holds row n, columns 4g .. 4g+3
-            const float bt = __shfl(b2, 16 * i + n16, 64);
+            const float bt = lb[16 * i + n16];
+            const f32x4 bs = *reinterpret_cast<const f32x4*>(&lb[16 * i + 4 * g4]);
             f32x4 dv, dd;
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 const int col = 4 * g4 + x;
-                const float bs = __shfl(b2, 16 * i + col, 64);
                 dv[x] = sm.Sd[i][n16][col];
-                dd[x] = col <= n16 ? dv[x] * __builtin_amdgcn_exp2f(bt - bs) : 0.f;
+                dd[x] = col <= n16 ? dv[x] * __builtin_amdgcn_exp2f(bt - bs[x]) : 0.f;
             }
             unsigned h0, h1, l0, l1;
             pack_f16_split(dv, h0, h1, l0, l1);
@@ -502,15 +464,16 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                 const int ti = k < 1 ? 1 : k < 3 ? 2 : 3;
                 const int tj = k - (ti * (ti - 1)) / 2;
                 const f32x4 gacc = gram(ti, tj);
-                const float bs = __shfl(b2, 16 * tj + n16, 64);
+                const float bs = lb[16 * tj + n16];
+                const f32x4 bt = *reinterpret_cast<const f32x4*>(&lb[16 * ti + 4 * g4]);
+                const f32x4 bet = *reinterpret_cast<const f32x4*>(&sm.beta[par][16 * ti + 4 * g4]);
                 // D layout (row 4g + e, column n) -> A fragment lane 16 (n / 4) + 4g + e, entry n % 4
                 uint16_t* const P = &sm.Ln[0][k][(16 * (n16 >> 2) + 4 * g4) * 4 + (n16 & 3)];
                 uint16_t* const Pd = &sm.Lnd[0][k][(16 * (n16 >> 2) + 4 * g4) * 4 + (n16 & 3)];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int t = 16 * ti + 4 * g4 + e;
-                    const float l = -sm.beta[t] * gacc[e];
-                    const float ld = l * __builtin_amdgcn_exp2f(__shfl(b2, t, 64) - bs);
+                    const float l = -bet[e] * gacc[e];
+                    const float ld = l * __builtin_amdgcn_exp2f(bt[e] - bs);
                     uint16_t h, lo;
                     to16<2>(l, h, lo);
                     P[4 * e] = h;
@@ -526,8 +489,12 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                 if (wave >= 6) mq_tile(wave + 2);
             }
         }
-        __syncthreads();
+    };
 
+    // ---- 3. forward substitution (Wt to LDS, U to registers)
+    auto phase_solve = [&](int par) {
+        const int lane_c = opaque(lane);
+        const int g4 = lane_c >> 4, n16 = lane_c & 15, lx = lane_c ^ g4;
         // ---- 3. block forward substitution, one chain per owned column tile (no barriers):
         //   Wt_i = (I + Lt_ii)^-1 (diag(beta) K_i - sum_{j<i} Lt_ij Wt_j)       (H tiles: channel tile)
         //   U_i  = the same with the decayed blocks and diag(beta) V_i           (S tiles: value tile)
@@ -535,7 +502,6 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
         // has the accumulator's lane layout, so a solved block feeds the next products as
         // packed, without cross-lane moves.  Wt goes to LDS for every wave's Y = Wt X; U stays
         // in this wave's registers for its S tile.
-        f32x4 U[4][CTW];
         {
             auto mma16 = [](const u32x2& ah, const u32x2& al, const u32x2& bh, const u32x2& bl, f32x4 c) {
                 c = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, ah), __builtin_bit_cast(f16x4, bh), c, 0, 0, 0);
@@ -554,7 +520,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                     if (!own_tile(c)) continue;
                     const bool is_s = s_tile(c);
                     const int q = is_s ? wave + 8 * c - RT : wave + 8 * c;   // channel / value tile
-                    const uint16_t(*rhs_src)[D * CH] = is_s ? sm.Vt : sm.Kt[ktb];
+                    const uint16_t(*rhs_src)[D * CH] = is_s ? sm.Vt[par] : sm.Kt[par];
                     // right-hand side diag(beta) K_i (or V_i): lane (g, n) = rows 16i + 4g + e, column 16q + n
                     f32x4 acc;
                     {
@@ -566,7 +532,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                             v0 += f16x2_to_f32(lw[0]);
                             v1 += f16x2_to_f32(lw[1]);
                         }
-                        const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[16 * i + 4 * g4]);
+                        const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[par][16 * i + 4 * g4]);
                         acc = f32x4{bt[0] * v0.x, bt[1] * v0.y, bt[2] * v1.x, bt[3] * v1.y};
                     }
                     // - sum_{j<i} Lt_ij X_j
@@ -615,19 +581,15 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                 }
             }
         }
-        // q goes two chunks ahead: wait for everything in flight -- the next chunk's q (sent
-        // at this point of the previous chunk), its k, v, g, beta (sent at the end of staging)
-        // and the previous chunk's output stores -- then send q of the chunk after next into
-        // the buffer this chunk's q was converted from
-        if constexpr (OUT) {
-            __builtin_amdgcn_s_waitcnt(0x0070);
-            if (c0 + 2 * CH < end) fetch_q(c0 + 2 * CH, qbuf);
-        }
-        __syncthreads();
+    };
 
+    // ---- 4. the state update of the chunk at c0 (n tokens)
+    auto phase_update = [&](int64_t c0, int n, int par) {
+        const int lane_c = opaque(lane);
+        const int g4 = lane_c >> 4, n16 = lane_c & 15, lx = lane_c ^ g4;
         // ---- 6..8. Y = Wt X, R, X += K^T R for all owned column tiles at once (each A
         // fragment is read once per wave)
-        const float bC = sm.bC;
+        const float bC = sm.bC[par];
         const float ebC = __builtin_amdgcn_exp2f(bC * kLog2e);
         if (wave < NCT) {
             f32x4 R[4][CTW];
@@ -676,9 +638,9 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                     for (int e = 0; e < 4; ++e) {
                         const int t = tt * 16 + 4 * g4 + e;
                         if (is_s) {   // new values U' = U - diag(e^b) Wt S_0; R = diag(e^{b_C - b}) U'
-                            const float up = U[tt][c][e] - sm.eb[t] * R[tt][c][e];
+                            const float up = U[tt][c][e] - sm.eb[par][t] * R[tt][c][e];
                             U[tt][c][e] = up;
-                            R[tt][c][e] = sm.ebr[t] * up;
+                            R[tt][c][e] = sm.ebr[par][t] * up;
                         } else {
                             R[tt][c][e] = -R[tt][c][e];
                         }
@@ -693,7 +655,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
 #pragma unroll
                         for (int tt = 0; tt < 4; ++tt) {
                             f32x4 o;
-                            const f32x4 ebt = *reinterpret_cast<const f32x4*>(&sm.eb[tt * 16 + 4 * g4]);
+                            const f32x4 ebt = *reinterpret_cast<const f32x4*>(&sm.eb[par][tt * 16 + 4 * g4]);
 #pragma unroll
                             for (int e = 0; e < 4; ++e) o[e] = ob.scale * ebt[e] * P[tt][e];
                             o = mma<1>(frag_of<1, CH>(so.Mq, tt, 0, lx), ub0, o);
@@ -715,20 +677,85 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int kbk = 0; kbk < 2; ++kbk) {
-                    const Frag<NSPLIT> a = frag_of<NSPLIT, CH>(sm.Kt[ktb], rt, kbk, lx);
+                    const Frag<NSPLIT> a = frag_of<NSPLIT, CH>(sm.Kt[par], rt, kbk, lx);
 #pragma unroll
                     for (int c = 0; c < CTW; ++c)
                         if (upd_tile(c)) X[rt][c] = mma<NSPLIT>(a, rb[kbk][c], X[rt][c]);
                 }
         }
-        if constexpr (PIPE) {   // the next chunk into the other K^T buffer, then the one after into registers
-            if (c0 + CH < end) {
-                stage_kv((int)((end - c0 - CH) < CH ? (end - c0 - CH) : CH), ktb ^ 1);
-                if (c0 + 2 * CH < end) prefetch(c0 + 2 * CH);
-            }
-        }
         log_s += bC;
-        __syncthreads();
+    };
+
+    auto chunk_len = [&](int64_t c0) -> int { return (int)((end - c0) < CH ? (end - c0) : CH); };
+    if constexpr (PIPE) {
+        // Two steps per chunk i, one barrier after each:
+        //   solve(i), stage(i + 1)    |    update(i), gram(i + 1)
+        // The Gram blocks and the diagonal inverses of the next chunk do not depend on the
+        // state, so they fill the SIMD time that the state update leaves; the staging fills
+        // the substitution's latency.
+        const int nch = (int)((end - beg + CH - 1) / CH);
+        if (nch > 0) {
+            stage_kv(chunk_len(beg), 0);
+            if (nch > 1) prefetch(beg + CH);
+            __syncthreads();
+            phase_gram(beg, 0);
+            __syncthreads();
+        }
+        for (int ci = 0; ci < nch; ++ci) {
+            const int64_t c0 = beg + (int64_t)ci * CH;
+            const int par = ci & 1;
+            phase_solve(par);
+            if (ci + 1 < nch) {
+                stage_kv(chunk_len(c0 + CH), par ^ 1);
+                if (ci + 2 < nch) prefetch(c0 + 2 * CH);
+            }
+            __syncthreads();
+            phase_update(c0, chunk_len(c0), par);
+            if (ci + 1 < nch) phase_gram(c0 + CH, par ^ 1);
+            __syncthreads();
+        }
+    } else {
+        for (int64_t c0 = beg; c0 < end; c0 += CH) {
+            const int n = chunk_len(c0);
+            const int tb = opaque(tb0), cb = opaque(cb0);
+            const int qbuf = (int)(((c0 - beg) / CH) & 1);
+            if constexpr (OUT) {
+                if (has_blk && blk_v) {   // q block (tb, cb) to the fp16 plane Qr; rows past the segment zeroed
+                    auto pk = [](float a, float b) -> unsigned {
+                        return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a, b));
+                    };
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int t = tb * 4 + r;
+                        u32x4 w = *reinterpret_cast<const u32x4*>(&so.Qraw[qbuf][t * D + cb * 8]);
+                        if (t >= n) w = u32x4{0u, 0u, 0u, 0u};
+                        u32x4 o;
+#pragma unroll
+                        for (int x = 0; x < 4; ++x)
+                            o[x] = pk(__uint_as_float(w[x] << 16), __uint_as_float(w[x] & 0xFFFF0000u));
+                        *reinterpret_cast<u32x4*>(&so.Qr[0][lds_off(t, cb * 8, KP)]) = o;
+                    }
+                }
+            }
+            stage_kv(n, 0);
+            // the next chunk's loads fly during this chunk
+            if (c0 + CH < end) prefetch(c0 + CH);
+            __syncthreads();
+            phase_gram(c0, 0);
+            __syncthreads();
+            phase_solve(0);
+            // q goes two chunks ahead: wait for everything in flight -- the next chunk's q (sent
+            // at this point of the previous chunk), its k, v, g, beta (sent at the end of staging)
+            // and the previous chunk's output stores -- then send q of the chunk after next into
+            // the buffer this chunk's q was converted from
+            if constexpr (OUT) {
+                __builtin_amdgcn_s_waitcnt(0x0070);
+                if (c0 + 2 * CH < end) fetch_q(c0 + 2 * CH, qbuf);
+            }
+            __syncthreads();
+            phase_update(c0, n, 0);
+            __syncthreads();
+        }
     }
 
     // ---- emit T_C = e^{log_s} H and S(C|0)
