@@ -44,8 +44,9 @@ using namespace bld;
 constexpr int CH = 64;       // chunk length
 constexpr float kLog2e = 1.4426950408889634f;
 
-// KTB = 2: the per-chunk inputs and decay factors are double-buffered by chunk parity
-template <int D, int NSPLIT, int KTB>
+// K^T and V^T come in KTB buffers (by chunk parity), the betas, log-decays and decay
+// factors in RB (by chunk index modulo RB)
+template <int D, int NSPLIT, int KTB, int RB>
 struct alignas(16) GdnSmem {
     static constexpr int KP = D < 32 ? 32 : D;  // channel contraction padded to 32
     uint16_t Kr[NSPLIT][CH * KP];  // K, rows = tokens, cols = channels (>= D zero)
@@ -58,10 +59,30 @@ struct alignas(16) GdnSmem {
     uint16_t Lnd[2][6][256];       // the same with the decay: -e^{b_t - b_s} Lt
     uint16_t Dv[2][4][256];        // (I + Lt_ii)^-1, diagonal block i
     uint16_t Dvd[2][4][256];       // the same with the decay e^{b_t - b_s}
-    float Sd[4][16][20];           // per diagonal block: Lt_ii, then its inverse (fp32)
-    float beta[KTB][CH];
-    float lb[KTB][CH], eb[KTB][CH], ebr[KTB][CH];   // b_t (log2 units), e^{b_t}, e^{b_C - b_t}
-    float bC[KTB];
+    float Sd[4][16][20];           // per diagonal block: (I + Lt_ii)^-1 (fp32)
+    float beta[RB][CH];
+    float lb[RB][CH], eb[RB][CH], ebr[RB][CH];   // b_t (log2 units), e^{b_t}, e^{b_C - b_t}
+    float bC[RB];
+};
+
+// The chunk's inverse with the betas folded in, Ab = (I + Lt)^-1 diag(b), and its decayed
+// form D Ab D^-1, as A-operand planes of v_mfma_f32_16x16x32_f16 (fp16 hi / lo): fragment
+// f = (row tile, 32-token k-step) for the six pairs (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+// that hold the lower triangle; lane l holds row l % 16, columns 8 (l / 16) .. + 7.  The
+// blocks above the diagonal inside them, (0,1) and (2,3), stay zero.
+template <bool ON>
+struct alignas(16) GdnInvSmem {
+    uint16_t Ab[2][2][6][512];   // [plain, decayed][hi, lo][fragment][lane * 8 + j]
+};
+template <>
+struct alignas(16) GdnInvSmem<false> {
+    uint16_t Ab[1][1][1][8];
+};
+__device__ __forceinline__ int ab_frag(int rt, int ks) { return rt < 2 ? rt : 2 * rt - 2 + ks; }
+
+template <int J>
+struct IntC {
+    static constexpr int value = J;
 };
 
 // LDS of the per-token outputs (OUT): q of this or the next chunk as loaded (bf16,
@@ -139,11 +160,10 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
     const void* __restrict__ gl, const void* __restrict__ beta, void* __restrict__ T_out, int t_split,
     float* __restrict__ S_out, BuildItems items, BuildOut ob)
 {
-    // Without outputs the next chunk is staged at the end of this chunk's state update (K^T
-    // double-buffered by chunk parity), which saves a barrier and overlaps the staging with
-    // the tail of the state-update products; with outputs q's plane is still in use then.
+    // Without outputs the chunks are pipelined (two steps per chunk, see the loop below);
+    // with outputs they run one after the other, in four steps.
     constexpr bool PIPE = !OUT;
-    using SM = GdnSmem<D, NSPLIT, PIPE ? 2 : 1>;
+    using SM = GdnSmem<D, NSPLIT, PIPE ? 2 : 1, PIPE ? 3 : 1>;
     static_assert(!OUT || (NSPLIT == 1 && BF16 && D >= 64), "outputs: bf16 inputs, d 64 or 128");
     constexpr int KP = SM::KP;
     constexpr int KSD = KP / 32;            // k-steps over channels
@@ -157,6 +177,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
     __shared__ SM sm;
     __shared__ GdnOutSmem<OUT ? D : 16> so_;   // used only with OUT
     auto& so = so_;
+    __shared__ GdnInvSmem<PIPE> si;
 
     const int unit = blockIdx.x;
     const int seg = unit / H, h = unit % H;
@@ -180,10 +201,12 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g4 = lane >> 4, n16 = lane & 15;
-    // column tile ct = wave + 8 c of X is an S tile (ct >= RT); known at compile time when
-    // the H and S tiles split evenly over the 8 waves
-    auto s_tile = [&](int c) -> bool { return RT % 8 == 0 ? c * 8 >= RT : wave + 8 * c >= RT; };
-    auto own_tile = [&](int c) -> bool { return NCT % 8 == 0 || wave + 8 * c < NCT; };
+    // column tiles of X owned by this wave: ct = tile(c) = wave + 8 c, c < CTW; ct >= RT is
+    // an S tile, known at compile time when the H and S tiles split evenly over the 8 waves
+    // (two tiles per wave: one of each kind, which balances the state update's work)
+    auto tile = [&](int c) -> int { return wave + 8 * c; };
+    auto s_tile = [&](int c) -> bool { return RT % 8 == 0 ? c * 8 >= RT : tile(c) >= RT; };
+    auto own_tile = [&](int c) -> bool { return NCT % 8 == 0 || tile(c) < NCT; };
 
     // WANT_T false (T not requested): only the S columns of X are advanced (the Wt solve
     // is shared by both)
@@ -191,6 +214,13 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
     beg = beg < 0 ? 0 : (beg > n_tokens ? n_tokens : beg);
     end = end < beg ? beg : (end > n_tokens ? n_tokens : end);
 
+    // the blocks above the diagonal inside the inverse planes: lanes 32..63 of fragments 0, 3
+    if constexpr (PIPE) {
+        for (int i = tid; i < 2 * 2 * 2 * 256; i += 512) {
+            const int pl = i >> 9, f = ((i >> 8) & 1) ? 3 : 0;
+            (&si.Ab[0][0][0][0])[pl * 6 * 512 + f * 512 + 256 + (i & 255)] = 0;
+        }
+    }
     // zero the channel padding of Kr / Wt once (D < 32 only)
     if (KP > D) {
         for (int i = tid; i < NSPLIT * CH * KP; i += 512) {
@@ -203,7 +233,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
     f32x4 X[RT][CTW];
 #pragma unroll
     for (int c = 0; c < CTW; ++c) {
-        const int ct = wave + 8 * c;
+        const int ct = tile(c);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             X[rt][c] = zero4();
@@ -280,69 +310,51 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
         }
     };
 
-    // ---- stage a chunk of n_s tokens from the prefetched registers into the buffers of
-    // parity kbuf: K token-major, K^T and V^T channel-major (16-bit), betas and log-decays
-    auto stage_kv = [&](int n_s, int kbuf) {
-        const int tb = opaque(tb0), cb = opaque(cb0);
-        if (has_blk) {
-            // the 4 x 8 block; rows past the segment are zeroed (only the last chunk has any)
-            if (n_s < CH) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (tb * 4 + r >= n_s)
-#pragma unroll
-                        for (int x = 0; x < WPR; ++x) raw[r][x] = u32x4{0u, 0u, 0u, 0u};
-            }
-            float f[4][8];
+    // ---- staging of a chunk of n_s tokens from the prefetched registers, in two parts:
+    // (a) K token-major, betas and log-decays into ring slot rb; (b) K^T and V^T channel-major
+    // into buffer kbuf (16-bit operands).  Rows past the segment are zeroed (only the last
+    // chunk has any).
+    auto stage_rows = [&](int n_s, float (&f)[4][8]) {
+        const int tb = opaque(tb0);
+        if (n_s < CH) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
+                if (tb * 4 + r >= n_s)
 #pragma unroll
-                for (int c = 0; c < 8; ++c) f[r][c] = raw_val(r, c);
-            uint16_t(*dst)[D * CH] = blk_v ? sm.Vt[kbuf] : sm.Kt[kbuf];
-            if constexpr (NSPLIT == 1 && BF16) {
-                // bf16 values are exact in fp16 (inside its range): round-toward-zero packing is exact
-                auto pk = [](float a, float b) -> unsigned {
-                    return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a, b));
-                };
-                if (!blk_v) {   // K rows (8 channels of one token = 16 contiguous bytes)
+                    for (int x = 0; x < WPR; ++x) raw[r][x] = u32x4{0u, 0u, 0u, 0u};
+        }
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        *reinterpret_cast<u32x4*>(&sm.Kr[0][lds_off(tb * 4 + r, cb * 8, KP)]) =
-                            u32x4{pk(f[r][0], f[r][1]), pk(f[r][2], f[r][3]), pk(f[r][4], f[r][5]), pk(f[r][6], f[r][7])};
-                }
-                // transposed: one channel row, 4 consecutive tokens = 8 contiguous bytes
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int c = 0; c < 8; ++c)
-                    *reinterpret_cast<u32x2*>(&dst[0][lds_off(cb * 8 + c, tb * 4, CH)]) =
-                        u32x2{pk(f[0][c], f[1][c]), pk(f[2][c], f[3][c])};
-            } else {
-                uint16_t hb[4][8], lb[4][8];   // [token][channel]
+            for (int c = 0; c < 8; ++c) f[r][c] = raw_val(r, c);
+    };
+    // bf16 values are exact in fp16 (inside its range): round-toward-zero packing is exact
+    auto pk = [](float a, float b) -> unsigned { return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a, b)); };
+    auto stage_a = [&](int n_s, int rb) {
+        const int tb = opaque(tb0), cb = opaque(cb0);
+        if (has_blk && !blk_v) {   // K rows (8 channels of one token = 16 contiguous bytes)
+            float f[4][8];
+            stage_rows(n_s, f);
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
+            for (int r = 0; r < 4; ++r) {
+                const int off = lds_off(tb * 4 + r, cb * 8, KP);
+                if constexpr (NSPLIT == 1 && BF16) {
+                    *reinterpret_cast<u32x4*>(&sm.Kr[0][off]) =
+                        u32x4{pk(f[r][0], f[r][1]), pk(f[r][2], f[r][3]), pk(f[r][4], f[r][5]), pk(f[r][6], f[r][7])};
+                } else {
+                    uint16_t hb[8], lw[8];
 #pragma unroll
-                    for (int c = 0; c < 8; ++c) to16<NSPLIT>(f[r][c], hb[r][c], lb[r][c]);
-                if (!blk_v) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int off = lds_off(tb * 4 + r, cb * 8, KP);
-                        *reinterpret_cast<u32x4*>(&sm.Kr[0][off]) = pack8(hb[r]);
-                        if constexpr (NSPLIT == 2) *reinterpret_cast<u32x4*>(&sm.Kr[1][off]) = pack8(lb[r]);
-                    }
-                }
-#pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    const int off = lds_off(cb * 8 + c, tb * 4, CH);
-                    *reinterpret_cast<u32x2*>(&dst[0][off]) = u32x2{pack2(hb[0][c], hb[1][c]), pack2(hb[2][c], hb[3][c])};
-                    if constexpr (NSPLIT == 2)
-                        *reinterpret_cast<u32x2*>(&dst[1][off]) = u32x2{pack2(lb[0][c], lb[1][c]), pack2(lb[2][c], lb[3][c])};
+                    for (int c = 0; c < 8; ++c) to16<NSPLIT>(f[r][c], hb[c], lw[c]);
+                    *reinterpret_cast<u32x4*>(&sm.Kr[0][off]) = pack8(hb);
+                    if constexpr (NSPLIT == 2) *reinterpret_cast<u32x4*>(&sm.Kr[1][off]) = pack8(lw);
                 }
             }
         }
-        if (wave == 0) {
+        if (wave == 7) {
             // betas, and the log-decays b_t = g_1 + .. + g_t of the chunk (inclusive scan over
             // the lanes, one token each) with the decay factors of the state update (v_exp_f32)
             const bool ok = lane < n_s;
-            sm.beta[kbuf][lane] = ok ? raw1(braw) : 0.f;
+            sm.beta[rb][lane] = ok ? raw1(braw) : 0.f;
             float x = ok ? raw1(graw) : 0.f;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
@@ -351,10 +363,32 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
             }
             const float bc = __shfl(x, 63, 64);
             const float b2 = x * kLog2e;
-            sm.lb[kbuf][lane] = b2;
-            sm.eb[kbuf][lane] = __builtin_amdgcn_exp2f(b2);
-            sm.ebr[kbuf][lane] = __builtin_amdgcn_exp2f(bc * kLog2e - b2);
-            if (lane == 0) sm.bC[kbuf] = bc;
+            sm.lb[rb][lane] = b2;
+            sm.eb[rb][lane] = __builtin_amdgcn_exp2f(b2);
+            sm.ebr[rb][lane] = __builtin_amdgcn_exp2f(bc * kLog2e - b2);
+            if (lane == 0) sm.bC[rb] = bc;
+        }
+    };
+    auto stage_b = [&](int n_s, int kbuf) {
+        const int tb = opaque(tb0), cb = opaque(cb0);
+        if (has_blk) {   // transposed: one channel row, 4 consecutive tokens = 8 contiguous bytes
+            float f[4][8];
+            stage_rows(n_s, f);
+            uint16_t(*dst)[D * CH] = blk_v ? sm.Vt[kbuf] : sm.Kt[kbuf];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const int off = lds_off(cb * 8 + c, tb * 4, CH);
+                if constexpr (NSPLIT == 1 && BF16) {
+                    *reinterpret_cast<u32x2*>(&dst[0][off]) = u32x2{pk(f[0][c], f[1][c]), pk(f[2][c], f[3][c])};
+                } else {
+                    uint16_t hb[4], lw[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) to16<NSPLIT>(f[r][c], hb[r], lw[r]);
+                    *reinterpret_cast<u32x2*>(&dst[0][off]) = u32x2{pack2(hb[0], hb[1]), pack2(hb[2], hb[3])};
+                    if constexpr (NSPLIT == 2)
+                        *reinterpret_cast<u32x2*>(&dst[1][off]) = u32x2{pack2(lw[0], lw[1]), pack2(lw[2], lw[3])};
+                }
+            }
         }
     };
 
@@ -380,13 +414,32 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
     // decay factors.
     f32x4 U[4][CTW];   // the solved value block of this wave's S tiles (phase 3 -> phase 4)
 
+    // 16 x 16 x 16 product with fp16 hi / lo operands (three products; lo x lo dropped)
+    auto mma16 = [](const u32x2& ah, const u32x2& al, const u32x2& bh, const u32x2& bl, f32x4 c) {
+        c = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, ah), __builtin_bit_cast(f16x4, bh), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, ah), __builtin_bit_cast(f16x4, bl), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, al), __builtin_bit_cast(f16x4, bh), c, 0, 0, 0);
+        return c;
+    };
+    // a 16 x 16 block in the accumulator layout as fp16 hi / lo operand bits: the B operand of
+    // v_mfma_f32_16x16x16_f16, or the A operand of the transposed block
+    struct Hl16 {
+        u32x2 h, l;
+    };
+    auto hl16 = [](const f32x4& x) {
+        unsigned a, b, c, d;
+        pack_f16_split(x, a, b, c, d);
+        return Hl16{u32x2{a, b}, u32x2{c, d}};
+    };
+    auto mm16 = [&](const Hl16& a, const Hl16& b) { return mma16(a.h, a.l, b.h, b.l, zero4()); };
+
     // ---- 2. Gram blocks Lt = tril(b K K^T, -1) of the chunk at c0: the diagonal 16 x 16
-    // blocks are inverted by waves 0..3 (forward substitution, fp32), the off-diagonal blocks
-    // stored negated by waves 4..7
-    auto phase_gram = [&](int64_t c0, int par) {
+    // blocks are inverted by waves 0..3, the off-diagonal blocks stored negated (fp16 hi / lo
+    // operand planes, plain and decayed)
+    auto phase_gram = [&](int64_t c0, int rb) {
         const int lane_c = opaque(lane);
         const int g4 = lane_c >> 4, n16 = lane_c & 15, lx = lane_c ^ g4;
-        const float* const lb = sm.lb[par];
+        const float* const lb = sm.lb[rb];
         auto gram = [&](int ti, int tj) -> f32x4 {   // lane (g, n): G[16 ti + 4g + e][16 tj + n]
             f32x4 gacc = zero4();
 #pragma unroll
@@ -422,68 +475,79 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
             }
         };
         if (wave < 4) {
+            // (I + Lt_ii)^-1 = (I - N)^-1 with N = -Lt_ii strictly lower (N^16 = 0):
+            //   (I - N)^-1 = (I + N)(I + N^2)(I + N^4)(I + N^8)
+            // as 16 x 16 products on MFMA (hi / lo operands).  A product's A operand is the
+            // accumulator layout of the transposed factor, so the transposes are carried
+            // along; N^T comes from the same Gram block (it is symmetric).
             const int i = wave;
             const f32x4 gacc = gram(i, i);
-            const f32x4 bet = *reinterpret_cast<const f32x4*>(&sm.beta[par][16 * i + 4 * g4]);
+            const f32x4 bet = *reinterpret_cast<const f32x4*>(&sm.beta[rb][16 * i + 4 * g4]);
+            const float bn = sm.beta[rb][16 * i + n16];
+            f32x4 nd, nt;   // N[4g + e][n], N^T[4g + e][n]
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sm.Sd[i][4 * g4 + e][n16] = (n16 < 4 * g4 + e) ? bet[e] * gacc[e] : 0.f;
-            // column j = lane of (I + Lt_ii)^-1 by forward substitution; every read of the block
-            // precedes the first write back (one wave, in order)
-            if (lane < 16) {
-                float x[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float acc = (r == lane) ? 1.f : 0.f;
-#pragma unroll
-                    for (int q = 0; q < r; ++q) acc -= sm.Sd[i][r][q] * x[q];
-                    x[r] = acc;
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sm.Sd[i][r][lane] = x[r];
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g4 + e;
+                nd[e] = n16 < r ? -bet[e] * gacc[e] : 0.f;
+                nt[e] = r < n16 ? -bn * gacc[e] : 0.f;
             }
-            // A fragment: lane (g, n) holds row n, columns 4g .. 4g+3
+            auto eye = [&](f32x4 x) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] += (4 * g4 + e == n16) ? 1.f : 0.f;
+                return x;
+            };
+            const Hl16 n1 = hl16(nd), n1t = hl16(nt);
+            const f32x4 n2 = mm16(n1t, n1), n2t = mm16(n1, n1t);                    // N^2, (N^2)^T
+            const Hl16 q2 = hl16(n2), q2t = hl16(n2t), e1t = hl16(eye(nt)), e2 = hl16(eye(n2));
+            const f32x4 n4 = mm16(q2t, q2), n4t = mm16(q2, q2t);                    // N^4, (N^4)^T
+            const f32x4 p1t = mm16(e2, e1t);                                        // ((I + N)(I + N^2))^T
+            const Hl16 q4 = hl16(n4), q4t = hl16(n4t), e4 = hl16(eye(n4)), r1t = hl16(p1t);
+            const f32x4 n8 = mm16(q4t, q4);                                         // N^8
+            const f32x4 p2t = mm16(e4, r1t);                                        // (P1 (I + N^4))^T
+            const Hl16 e8 = hl16(eye(n8)), r2t = hl16(p2t);
+            const f32x4 y = mm16(r2t, e8), yt = mm16(e8, r2t);                      // the inverse and its transpose
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm.Sd[i][4 * g4 + e][n16] = y[e];
+            // A fragment (lane (g, n): row n, columns 4g .. 4g+3) = accumulator layout of the
+            // transpose; the decayed block has the factors e^{b_t - b_s}, t >= s
             const float bt = lb[16 * i + n16];
             const f32x4 bs = *reinterpret_cast<const f32x4*>(&lb[16 * i + 4 * g4]);
-            f32x4 dv, dd;
+            f32x4 dd;
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int col = 4 * g4 + x;
-                dv[x] = sm.Sd[i][n16][col];
-                dd[x] = col <= n16 ? dv[x] * __builtin_amdgcn_exp2f(bt - bs[x]) : 0.f;
-            }
-            unsigned h0, h1, l0, l1;
-            pack_f16_split(dv, h0, h1, l0, l1);
-            *reinterpret_cast<u32x2*>(&sm.Dv[0][i][lane * 4]) = u32x2{h0, h1};
-            *reinterpret_cast<u32x2*>(&sm.Dv[1][i][lane * 4]) = u32x2{l0, l1};
-            pack_f16_split(dd, h0, h1, l0, l1);
-            *reinterpret_cast<u32x2*>(&sm.Dvd[0][i][lane * 4]) = u32x2{h0, h1};
-            *reinterpret_cast<u32x2*>(&sm.Dvd[1][i][lane * 4]) = u32x2{l0, l1};
-        } else {
-            // off-diagonal blocks (1,0) (2,0) (2,1) (3,0) (3,1) (3,2), two waves taking two
-            for (int k = wave - 4; k < 6; k += 4) {
+            for (int x = 0; x < 4; ++x) dd[x] = 4 * g4 + x <= n16 ? yt[x] * __builtin_amdgcn_exp2f(bt - bs[x]) : 0.f;
+            const Hl16 dv = hl16(yt), dvd = hl16(dd);
+            *reinterpret_cast<u32x2*>(&sm.Dv[0][i][lane * 4]) = dv.h;
+            *reinterpret_cast<u32x2*>(&sm.Dv[1][i][lane * 4]) = dv.l;
+            *reinterpret_cast<u32x2*>(&sm.Dvd[0][i][lane * 4]) = dvd.h;
+            *reinterpret_cast<u32x2*>(&sm.Dvd[1][i][lane * 4]) = dvd.l;
+        }
+        // off-diagonal blocks k = (1,0) (2,0) (2,1) (3,0) (3,1) (3,2): waves 4..7 take k = 0..3,
+        // waves 2, 3 k = 4, 5.  The transposed Gram block G_ji = K_j K_i^T has, in the
+        // accumulator layout, the A-operand layout of Lt_ij (lane (g, n): row n, columns 4g..)
+        {
+            const int k = wave >= 4 ? wave - 4 : (wave >= 2 ? wave + 2 : -1);
+            if (k >= 0) {
                 const int ti = k < 1 ? 1 : k < 3 ? 2 : 3;
                 const int tj = k - (ti * (ti - 1)) / 2;
-                const f32x4 gacc = gram(ti, tj);
-                const float bs = lb[16 * tj + n16];
-                const f32x4 bt = *reinterpret_cast<const f32x4*>(&lb[16 * ti + 4 * g4]);
-                const f32x4 bet = *reinterpret_cast<const f32x4*>(&sm.beta[par][16 * ti + 4 * g4]);
-                // D layout (row 4g + e, column n) -> A fragment lane 16 (n / 4) + 4g + e, entry n % 4
-                uint16_t* const P = &sm.Ln[0][k][(16 * (n16 >> 2) + 4 * g4) * 4 + (n16 & 3)];
-                uint16_t* const Pd = &sm.Lnd[0][k][(16 * (n16 >> 2) + 4 * g4) * 4 + (n16 & 3)];
+                const f32x4 gacc = gram(tj, ti);
+                const float bn = sm.beta[rb][16 * ti + n16];
+                const float bt = lb[16 * ti + n16];
+                const f32x4 bs = *reinterpret_cast<const f32x4*>(&lb[16 * tj + 4 * g4]);
+                f32x4 l, ld;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float l = -bet[e] * gacc[e];
-                    const float ld = l * __builtin_amdgcn_exp2f(bt[e] - bs);
-                    uint16_t h, lo;
-                    to16<2>(l, h, lo);
-                    P[4 * e] = h;
-                    P[6 * 256 + 4 * e] = lo;
-                    to16<2>(ld, h, lo);
-                    Pd[4 * e] = h;
-                    Pd[6 * 256 + 4 * e] = lo;
+                    l[e] = -bn * gacc[e];
+                    ld[e] = l[e] * __builtin_amdgcn_exp2f(bt - bs[e]);
                 }
+                const Hl16 lq = hl16(l), lqd = hl16(ld);
+                *reinterpret_cast<u32x2*>(&sm.Ln[0][k][lane * 4]) = lq.h;
+                *reinterpret_cast<u32x2*>(&sm.Ln[1][k][lane * 4]) = lq.l;
+                *reinterpret_cast<u32x2*>(&sm.Lnd[0][k][lane * 4]) = lqd.h;
+                *reinterpret_cast<u32x2*>(&sm.Lnd[1][k][lane * 4]) = lqd.l;
             }
-            if constexpr (OUT) {   // waves 4, 5: tiles 0, 4 | 1, 5; waves 6, 7 (one L tile fewer): 2, 6, 8 | 3, 7, 9
+        }
+        if (wave >= 4) {
+            if constexpr (OUT) {   // the masked Q K^T tiles: waves 4, 5: 0, 4 | 1, 5; waves 6, 7: 2, 6, 8 | 3, 7, 9
                 mq_tile(wave - 4);
                 mq_tile(wave);
                 if (wave >= 6) mq_tile(wave + 2);
@@ -491,7 +555,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
         }
     };
 
-    // ---- 3. forward substitution (Wt to LDS, U to registers)
+    // ---- 3. forward substitution (Wt to LDS, U to registers); the chunks one after the other
     auto phase_solve = [&](int par) {
         const int lane_c = opaque(lane);
         const int g4 = lane_c >> 4, n16 = lane_c & 15, lx = lane_c ^ g4;
@@ -503,12 +567,6 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
         // packed, without cross-lane moves.  Wt goes to LDS for every wave's Y = Wt X; U stays
         // in this wave's registers for its S tile.
         {
-            auto mma16 = [](const u32x2& ah, const u32x2& al, const u32x2& bh, const u32x2& bl, f32x4 c) {
-                c = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, ah), __builtin_bit_cast(f16x4, bh), c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, ah), __builtin_bit_cast(f16x4, bl), c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, al), __builtin_bit_cast(f16x4, bh), c, 0, 0, 0);
-                return c;
-            };
             // the chains of this wave's tiles advance block by block together, so the
             // latency of one chain's step overlaps the other's
             u32x2 xh[3][CTW], xl[3][CTW];   // solved blocks 0..2 as packed B operands (hi / lo)
@@ -519,7 +577,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                 for (int c = 0; c < CTW; ++c) {
                     if (!own_tile(c)) continue;
                     const bool is_s = s_tile(c);
-                    const int q = is_s ? wave + 8 * c - RT : wave + 8 * c;   // channel / value tile
+                    const int q = is_s ? tile(c) - RT : tile(c);   // channel / value tile
                     const uint16_t(*rhs_src)[D * CH] = is_s ? sm.Vt[par] : sm.Kt[par];
                     // right-hand side diag(beta) K_i (or V_i): lane (g, n) = rows 16i + 4g + e, column 16q + n
                     f32x4 acc;
@@ -567,7 +625,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
 #pragma unroll
                     for (int tt = 0; tt < 4; ++tt) U[tt][c] = sol[tt][c];
                 } else {   // Wt rows 16i + 4g + e, channel 16q + n, token-major
-                    const int q = wave + 8 * c;
+                    const int q = tile(c);
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -583,13 +641,14 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
         }
     };
 
-    // ---- 4. the state update of the chunk at c0 (n tokens)
-    auto phase_update = [&](int64_t c0, int n, int par) {
+    // ---- 4. the state update of the chunk at c0 (n tokens; K^T in buffer kpar, decay
+    // factors in ring slot rs)
+    auto phase_update = [&](int64_t c0, int n, int kpar, int rs) {
         const int lane_c = opaque(lane);
         const int g4 = lane_c >> 4, n16 = lane_c & 15, lx = lane_c ^ g4;
         // ---- 6..8. Y = Wt X, R, X += K^T R for all owned column tiles at once (each A
         // fragment is read once per wave)
-        const float bC = sm.bC[par];
+        const float bC = sm.bC[rs];
         const float ebC = __builtin_amdgcn_exp2f(bC * kLog2e);
         if (wave < NCT) {
             f32x4 R[4][CTW];
@@ -638,9 +697,9 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                     for (int e = 0; e < 4; ++e) {
                         const int t = tt * 16 + 4 * g4 + e;
                         if (is_s) {   // new values U' = U - diag(e^b) Wt S_0; R = diag(e^{b_C - b}) U'
-                            const float up = U[tt][c][e] - sm.eb[par][t] * R[tt][c][e];
+                            const float up = U[tt][c][e] - sm.eb[rs][t] * R[tt][c][e];
                             U[tt][c][e] = up;
-                            R[tt][c][e] = sm.ebr[par][t] * up;
+                            R[tt][c][e] = sm.ebr[rs][t] * up;
                         } else {
                             R[tt][c][e] = -R[tt][c][e];
                         }
@@ -651,11 +710,11 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                     if (is_s) {   // o_t = scale e^{b_t} (Q S_0)_t + (M U')_t for the tile's 16 value columns
                         const Frag<1> ub0 = dpair_to_frag<1>(U[0][c], U[1][c]);
                         const Frag<1> ub1 = dpair_to_frag<1>(U[2][c], U[3][c]);
-                        const int vq = wave + 8 * c - RT;
+                        const int vq = tile(c) - RT;
 #pragma unroll
                         for (int tt = 0; tt < 4; ++tt) {
                             f32x4 o;
-                            const f32x4 ebt = *reinterpret_cast<const f32x4*>(&sm.eb[par][tt * 16 + 4 * g4]);
+                            const f32x4 ebt = *reinterpret_cast<const f32x4*>(&sm.eb[rs][tt * 16 + 4 * g4]);
 #pragma unroll
                             for (int e = 0; e < 4; ++e) o[e] = ob.scale * ebt[e] * P[tt][e];
                             o = mma<1>(frag_of<1, CH>(so.Mq, tt, 0, lx), ub0, o);
@@ -677,7 +736,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int kbk = 0; kbk < 2; ++kbk) {
-                    const Frag<NSPLIT> a = frag_of<NSPLIT, CH>(sm.Kt[par], rt, kbk, lx);
+                    const Frag<NSPLIT> a = frag_of<NSPLIT, CH>(sm.Kt[kpar], rt, kbk, lx);
 #pragma unroll
                     for (int c = 0; c < CTW; ++c)
                         if (upd_tile(c)) X[rt][c] = mma<NSPLIT>(a, rb[kbk][c], X[rt][c]);
@@ -686,33 +745,181 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
         log_s += bC;
     };
 
+    // ---- 3a. the inverse blocks Ab_ij (i >= j) of the chunk whose Gram blocks are in LDS
+    // (betas in ring slot rb), block column j = wave / 2 of the plain (even waves) or decayed
+    // (odd waves) inverse:
+    //   Ab_jj = (I + Lt_jj)^-1 diag(b_j),   Ab_ij = (I + Lt_ii)^-1 sum_{j <= k < i} (-Lt_ik) Ab_kj
+    // on v_mfma_f32_16x16x16_f16 with hi / lo operands, whose B operand has the accumulator's
+    // lane layout; each block goes to the inverse planes as soon as it is known
+    auto phase_ainv = [&](int rb) {
+        if constexpr (PIPE) {
+            const int lane_c = opaque(lane);
+            const int g4 = lane_c >> 4, n16 = lane_c & 15;
+            const int v = wave & 1;
+            const uint16_t(*const Lm)[6][256] = v ? sm.Lnd : sm.Ln;
+            const uint16_t(*const Dm)[4][256] = v ? sm.Dvd : sm.Dv;
+            auto chain = [&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                auto put_block = [&](int i, const f32x4& z) {   // D layout -> A fragment entries
+                    const int f = ab_frag(i, j >> 1), col = 16 * (j & 1) + n16;
+                    uint16_t* const ph = &si.Ab[v][0][f][0];
+                    uint16_t* const pl = &si.Ab[v][1][f][0];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int idx = (4 * g4 + e + 16 * (col >> 3)) * 8 + (col & 7);
+                        uint16_t h, lo;
+                        to16<2>(z[e], h, lo);
+                        ph[idx] = h;
+                        pl[idx] = lo;
+                    }
+                };
+                // Ab_jj from the fp32 diagonal inverse (decayed: times e^{b_t - b_s}, t >= s)
+                f32x4 z;
+                {
+                    const float* const lbr = sm.lb[rb];
+                    const float bs = lbr[16 * j + n16], bet = sm.beta[rb][16 * j + n16];
+                    const f32x4 bt = *reinterpret_cast<const f32x4*>(&lbr[16 * j + 4 * g4]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * g4 + e;
+                        float d = sm.Sd[j][r][n16];
+                        if (v) d = n16 <= r ? d * __builtin_amdgcn_exp2f(bt[e] - bs) : 0.f;
+                        z[e] = d * bet;
+                    }
+                }
+                put_block(j, z);
+                u32x2 zh[3], zl[3];   // Ab_kj (k = j .. 2) as B operands
+                if constexpr (j < 3) {
+                    unsigned b0, b1, b2, b3;
+                    pack_f16_split(z, b0, b1, b2, b3);
+                    zh[j] = u32x2{b0, b1};
+                    zl[j] = u32x2{b2, b3};
+                }
+#pragma unroll
+                for (int i = j + 1; i < 4; ++i) {
+                    f32x4 acc = zero4();
+#pragma unroll
+                    for (int k = j; k < i; ++k) {
+                        const int kb = i * (i - 1) / 2 + k;
+                        const u32x2 ah = *reinterpret_cast<const u32x2*>(&Lm[0][kb][lane * 4]);
+                        const u32x2 al = *reinterpret_cast<const u32x2*>(&Lm[1][kb][lane * 4]);
+                        acc = mma16(ah, al, zh[k], zl[k], acc);
+                    }
+                    unsigned b0, b1, b2, b3;
+                    pack_f16_split(acc, b0, b1, b2, b3);
+                    const u32x2 dh = *reinterpret_cast<const u32x2*>(&Dm[0][i][lane * 4]);
+                    const u32x2 dl = *reinterpret_cast<const u32x2*>(&Dm[1][i][lane * 4]);
+                    z = mma16(dh, dl, u32x2{b0, b1}, u32x2{b2, b3}, zero4());
+                    put_block(i, z);
+                    if (i < 3) {
+                        pack_f16_split(z, b0, b1, b2, b3);
+                        zh[i] = u32x2{b0, b1};
+                        zl[i] = u32x2{b2, b3};
+                    }
+                }
+            };
+            switch (wave >> 1) {
+                case 0: chain(IntC<0>{}); break;
+                case 1: chain(IntC<1>{}); break;
+                case 2: chain(IntC<2>{}); break;
+                default: chain(IntC<3>{}); break;
+            }
+        }
+    };
+
+    // ---- 3b. Wt = Ab K and U = (D Ab D^-1) V for this wave's column tiles, as dense products
+    // over the lower triangle (K, V exact in fp16 for bf16 inputs: two products per step);
+    // K^T, V^T in buffer kpar.  Wt goes to LDS, U stays in registers.
+    auto phase_dsolve = [&](int kpar) {
+        if constexpr (PIPE) {
+            const int lane_c = opaque(lane);
+            const int g4 = lane_c >> 4, n16 = lane_c & 15, lx = lane_c ^ g4;
+#pragma unroll
+            for (int c = 0; c < CTW; ++c) {
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) U[tt][c] = zero4();
+                if (!own_tile(c)) continue;
+                const bool is_s = s_tile(c);
+                const int q = is_s ? tile(c) - RT : tile(c);   // value / channel tile
+                const int v = is_s ? 1 : 0;
+                const uint16_t(*src)[D * CH] = is_s ? sm.Vt[kpar] : sm.Kt[kpar];
+                const Frag<NSPLIT> kf[2] = {frag_of<NSPLIT, CH>(src, q, 0, lx), frag_of<NSPLIT, CH>(src, q, 1, lx)};
+                f32x4 acc[4];
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    acc[tt] = zero4();
+#pragma unroll
+                    for (int ks = 0; ks <= (tt >> 1); ++ks) {
+                        const int f = ab_frag(tt, ks);
+                        const f16x8 ah = *reinterpret_cast<const f16x8*>(&si.Ab[v][0][f][lane * 8]);
+                        const f16x8 al = *reinterpret_cast<const f16x8*>(&si.Ab[v][1][f][lane * 8]);
+                        acc[tt] = mma_f16(ah, kf[ks].h, acc[tt]);
+                        acc[tt] = mma_f16(al, kf[ks].h, acc[tt]);
+                        if constexpr (NSPLIT == 2) acc[tt] = mma_f16(ah, kf[ks].l, acc[tt]);
+                    }
+                }
+                if (is_s) {
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt) U[tt][c] = acc[tt];
+                } else {   // Wt rows 16 tt + 4 g + e, channel 16 q + n, token-major
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int off = lds_off(16 * tt + 4 * g4 + e, 16 * q + n16, KP);
+                            uint16_t h, lo;
+                            to16<NSPLIT>(acc[tt][e], h, lo);
+                            sm.Wt[0][off] = h;
+                            if constexpr (NSPLIT == 2) sm.Wt[1][off] = lo;
+                        }
+                }
+            }
+        }
+    };
+
     auto chunk_len = [&](int64_t c0) -> int { return (int)((end - c0) < CH ? (end - c0) : CH); };
     if constexpr (PIPE) {
-        // Two steps per chunk i, one barrier after each:
-        //   solve(i), stage(i + 1)    |    update(i), gram(i + 1)
-        // The Gram blocks and the diagonal inverses of the next chunk do not depend on the
-        // state, so they fill the SIMD time that the state update leaves; the staging fills
-        // the substitution's latency.
+        // Chunk i's state update needs its Wt and U; nothing else in a chunk depends on the
+        // state.  So the chunks are pipelined, two steps per chunk, one barrier after each:
+        //   1: update(i), inverse(i + 1), stage K rows, betas, log-decays of i + 2
+        //   2: dense solve(i + 1), Gram blocks(i + 2), stage K^T, V^T of i + 2
+        // The state-independent parts fill the SIMD time that the state update leaves.
+        // K^T and V^T are double-buffered (chunk parity), the per-token scalars kept for three
+        // chunks (index modulo 3); Kr, Wt, the Gram blocks and the inverse planes are single.
         const int nch = (int)((end - beg + CH - 1) / CH);
-        if (nch > 0) {
-            stage_kv(chunk_len(beg), 0);
+        if (nch > 0) {   // prologue: chunk 0 up to its dense solve, chunk 1 up to its Gram blocks
+            stage_a(chunk_len(beg), 0);
+            stage_b(chunk_len(beg), 0);
             if (nch > 1) prefetch(beg + CH);
             __syncthreads();
             phase_gram(beg, 0);
+            if (nch > 1) stage_b(chunk_len(beg + CH), 1);
+            __syncthreads();
+            phase_ainv(0);
+            if (nch > 1) {
+                stage_a(chunk_len(beg + CH), 1);
+                if (nch > 2) prefetch(beg + 2 * CH);
+            }
+            __syncthreads();
+            phase_dsolve(0);
+            if (nch > 1) phase_gram(beg + CH, 1);
             __syncthreads();
         }
         for (int ci = 0; ci < nch; ++ci) {
             const int64_t c0 = beg + (int64_t)ci * CH;
-            const int par = ci & 1;
-            phase_solve(par);
+            phase_update(c0, chunk_len(c0), ci & 1, ci % 3);
+            if (ci + 1 < nch) phase_ainv((ci + 1) % 3);
+            if (ci + 2 < nch) stage_a(chunk_len(c0 + 2 * CH), (ci + 2) % 3);
+            __syncthreads();
             if (ci + 1 < nch) {
-                stage_kv(chunk_len(c0 + CH), par ^ 1);
-                if (ci + 2 < nch) prefetch(c0 + 2 * CH);
+                phase_dsolve((ci + 1) & 1);
+                if (ci + 2 < nch) {
+                    phase_gram(c0 + 2 * CH, (ci + 2) % 3);
+                    stage_b(chunk_len(c0 + 2 * CH), ci & 1);
+                    if (ci + 3 < nch) prefetch(c0 + 3 * CH);
+                }
+                __syncthreads();
             }
-            __syncthreads();
-            phase_update(c0, chunk_len(c0), par);
-            if (ci + 1 < nch) phase_gram(c0 + CH, par ^ 1);
-            __syncthreads();
         }
     } else {
         for (int64_t c0 = beg; c0 < end; c0 += CH) {
@@ -737,7 +944,8 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                     }
                 }
             }
-            stage_kv(n, 0);
+            stage_a(n, 0);
+            stage_b(n, 0);
             // the next chunk's loads fly during this chunk
             if (c0 + CH < end) prefetch(c0 + CH);
             __syncthreads();
@@ -753,7 +961,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                 if (c0 + 2 * CH < end) fetch_q(c0 + 2 * CH, qbuf);
             }
             __syncthreads();
-            phase_update(c0, n, 0);
+            phase_update(c0, n, 0, 0);
             __syncthreads();
         }
     }
@@ -763,7 +971,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
     const size_t pair = (size_t)out * H + h;
 #pragma unroll
     for (int c = 0; c < CTW; ++c) {
-        const int ct = wave + 8 * c;
+        const int ct = tile(c);
         if (ct >= NCT) continue;
         const bool is_s = ct >= RT;
         if (!is_s && T_out == nullptr) continue;
