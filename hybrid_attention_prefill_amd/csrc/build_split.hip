@@ -35,7 +35,7 @@ struct SplitPlan {
     int64_t* ib;          // [n_items_max] item token range
     int64_t* ie;
     int32_t* out;         // [n_items_max] >= 0: caller's slot; < 0: workspace slot -1 - out
-    int32_t* counts;      // [0] items
+    int32_t* counts;      // [0] items, [1] cut segments
     int4* cut;            // [max_cut] cut segment, pieces, workspace slot of its second piece;
                           // pieces = 0 past the cut segments
     int32_t* npieces;     // [n_seg]
@@ -113,14 +113,16 @@ __device__ int block_exclusive_scan(int x, int* wsum, int* total) {
     }
     if (lane == 63) wsum[wave] = v;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int acc = 0;
-        for (int w = 0; w < 16; ++w) {
-            const int t = wsum[w];
-            wsum[w] = acc;
-            acc += t;
+    if (wave == 0) {   // exclusive scan of the 16 wave totals
+        const int t = lane < 16 ? wsum[lane] : 0;
+        int u = t;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            const int y = __shfl_up(u, o, 64);
+            if (lane >= o) u += y;
         }
-        wsum[16] = acc;
+        if (lane < 16) wsum[lane] = u - t;
+        if (lane == 15) wsum[16] = u;
     }
     __syncthreads();
     const int r = wsum[wave] + v - x;
@@ -168,13 +170,18 @@ __global__ __launch_bounds__(1024) void plan_pieces_kernel(int n_seg, const int6
         }
     }
     __syncthreads();
-    if (tid == 0) {   // longest pieces first
-        int acc = 0;
-        for (int b = kBuckets - 1; b >= 0; --b) {
-            off[b] = acc;
-            acc += hist[b];
+    if (tid < 64) {   // longest pieces first: exclusive scan of the buckets from the last
+        static_assert(kBuckets == 64, "one lane per bucket");
+        const int b = kBuckets - 1 - tid;
+        const int t = hist[b];
+        int u = t;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(u, o, 64);
+            if (tid >= o) u += y;
         }
-        pl.counts[0] = acc;
+        off[b] = u - t;
+        if (tid == 63) pl.counts[0] = u;
     }
     __syncthreads();
 
@@ -198,6 +205,7 @@ __global__ __launch_bounds__(1024) void plan_pieces_kernel(int n_seg, const int6
         if (n > 1) pl.cut[atomicAdd(&ncut, 1)] = int4{i, n, wb, 0};
     }
     __syncthreads();
+    if (tid == 0) pl.counts[1] = ncut;
     for (int j = ncut + tid; j < max_cut; j += 1024) pl.cut[j] = int4{0, 0, 0, 0};
 }
 
@@ -210,20 +218,21 @@ __global__ __launch_bounds__(1024) void plan_pieces_kernel(int n_seg, const int6
 // a group of the block's 16-column tiles.  The first step's operands are loaded together
 // with the block's initial values.
 template <int D>
-__global__ __launch_bounds__(512) void fold_pieces_kernel(int H, int max_cut, SplitPlan pl, void* __restrict__ T_out,
-                                                          int t_split, float* __restrict__ S_out)
-{
-    constexpr int NB = 64;               // columns per block
-    constexpr int NBLK = 2 * D / NB;     // blocks of X (T's, then S's)
-    constexpr int RTN = D / 16;          // row tiles
-    constexpr int WPT = 8 / RTN;         // waves per row tile
-    constexpr int CTF = NB / 16 / WPT;   // column tiles per wave
-    constexpr int KS = D / 32, LDB = D + 8;
-    __shared__ __attribute__((aligned(16))) uint16_t Rh[NB * LDB];   // [column][row], bf16 hi
-    __shared__ __attribute__((aligned(16))) uint16_t Rl[NB * LDB];   //                bf16 lo
+struct FoldShape {
+    static constexpr int NB = 64;               // columns per block
+    static constexpr int NBLK = 2 * D / NB;     // blocks of X (T's, then S's)
+    static constexpr int RTN = D / 16;          // row tiles
+    static constexpr int WPT = 8 / RTN;         // waves per row tile
+    static constexpr int CTF = NB / 16 / WPT;   // column tiles per wave
+    static constexpr int KS = D / 32, LDB = D + 8;
+};
 
-    const UnitSlot us = xcd_unit_slot(blockIdx.x, NBLK);
-    if (us.unit >= max_cut * H) return;
+template <int D>
+__device__ __forceinline__ void fold_unit(int H, const SplitPlan& pl, void* __restrict__ T_out, int t_split,
+                                          float* __restrict__ S_out, UnitSlot us, uint16_t* Rh, uint16_t* Rl)
+{
+    using F = FoldShape<D>;
+    constexpr int NB = F::NB, NBLK = F::NBLK, RTN = F::RTN, CTF = F::CTF, KS = F::KS, LDB = F::LDB;
     const bool is_s = us.sub >= NBLK / 2;
     if (!is_s && T_out == nullptr) return;
     const int4 rec = pl.cut[us.unit / H];
@@ -303,6 +312,26 @@ __global__ __launch_bounds__(512) void fold_pieces_kernel(int H, int max_cut, Sp
         }
 }
 
+
+// The grid strides over the (cut segment, head, block) units of this call (the plan's
+// count of cut segments): a block's units stay on one XCD, and the blocks of one unit,
+// which read the same T_k, are neighbours there.
+template <int D>
+__global__ __launch_bounds__(512) void fold_pieces_kernel(int H, SplitPlan pl, void* __restrict__ T_out, int t_split,
+                                                          float* __restrict__ S_out)
+{
+    using F = FoldShape<D>;
+    __shared__ __attribute__((aligned(16))) uint16_t Rh[F::NB * F::LDB];   // [column][row], bf16 hi
+    __shared__ __attribute__((aligned(16))) uint16_t Rl[F::NB * F::LDB];   //                bf16 lo
+    const int n_units = pl.counts[1] * H;
+    for (int x = blockIdx.x;; x += gridDim.x) {
+        const UnitSlot us = xcd_unit_slot(x, F::NBLK);
+        if (us.unit >= n_units) return;
+        if (x != (int)blockIdx.x) __syncthreads();   // the previous unit's LDS readers are done
+        fold_unit<D>(H, pl, T_out, t_split, S_out, us, Rh, Rl);
+    }
+}
+
 }  // namespace
 
 size_t split_workspace_bytes(int d, int H, int n_seg, int64_t n_tokens)
@@ -329,13 +358,13 @@ hipError_t build_gdn_split(int d, bool in_bf16, int n_seg, int H, const int64_t*
     e = build_gdn(d, in_bf16, L.n_items_max, H, pl.ib, pl.ie, n_tok, k, v, g, beta, T_out, t_split, S_out, it,
                   BuildOut{}, st);
     if (e != hipSuccess) return e;
-    const int grid = xcd_grid_size(L.max_cut * H, 2 * d / 64);
+    // one block per unit up to 1024 blocks (the units of this call are counted on the GPU)
+    int grid = xcd_grid_size(L.max_cut * H, 2 * d / 64);
+    grid = grid < 1024 ? grid : 1024;
     if (d == 128)
-        hipLaunchKernelGGL(fold_pieces_kernel<128>, dim3(grid), dim3(512), 0, st, H, L.max_cut, pl, T_out,
-                           (int)t_split, S_out);
+        hipLaunchKernelGGL(fold_pieces_kernel<128>, dim3(grid), dim3(512), 0, st, H, pl, T_out, (int)t_split, S_out);
     else
-        hipLaunchKernelGGL(fold_pieces_kernel<64>, dim3(grid), dim3(512), 0, st, H, L.max_cut, pl, T_out,
-                           (int)t_split, S_out);
+        hipLaunchKernelGGL(fold_pieces_kernel<64>, dim3(grid), dim3(512), 0, st, H, pl, T_out, (int)t_split, S_out);
     return hipGetLastError();
 }
 
