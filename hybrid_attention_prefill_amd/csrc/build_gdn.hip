@@ -330,9 +330,35 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
     };
     // bf16 values are exact in fp16 (inside its range): round-toward-zero packing is exact
     auto pk = [](float a, float b) -> unsigned { return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a, b)); };
+    // bf16 inputs: the transposed words are packed in part (a), with the rows, and written
+    // in part (b) (they take the prefetch registers' place in between)
+    u32x2 tw[8];
+    auto pack_t = [&](int n_s) {   // the transposed words alone (before a part (b) without (a))
+        if constexpr (NSPLIT == 1 && BF16) {
+            if (has_blk) {
+                float f[4][8];
+                stage_rows(n_s, f);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) tw[c] = u32x2{pk(f[0][c], f[1][c]), pk(f[2][c], f[3][c])};
+            }
+        }
+    };
     auto stage_a = [&](int n_s, int rb) {
         const int tb = opaque(tb0), cb = opaque(cb0);
-        if (has_blk && !blk_v) {   // K rows (8 channels of one token = 16 contiguous bytes)
+        if constexpr (NSPLIT == 1 && BF16) {
+            if (has_blk) {
+                float f[4][8];
+                stage_rows(n_s, f);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) tw[c] = u32x2{pk(f[0][c], f[1][c]), pk(f[2][c], f[3][c])};
+                if (!blk_v) {   // K rows (8 channels of one token = 16 contiguous bytes)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        *reinterpret_cast<u32x4*>(&sm.Kr[0][lds_off(tb * 4 + r, cb * 8, KP)]) =
+                            u32x4{pk(f[r][0], f[r][1]), pk(f[r][2], f[r][3]), pk(f[r][4], f[r][5]), pk(f[r][6], f[r][7])};
+                }
+            }
+        } else if (has_blk && !blk_v) {   // K rows (8 channels of one token = 16 contiguous bytes)
             float f[4][8];
             stage_rows(n_s, f);
 #pragma unroll
@@ -372,14 +398,14 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
     auto stage_b = [&](int n_s, int kbuf) {
         const int tb = opaque(tb0), cb = opaque(cb0);
         if (has_blk) {   // transposed: one channel row, 4 consecutive tokens = 8 contiguous bytes
-            float f[4][8];
-            stage_rows(n_s, f);
             uint16_t(*dst)[D * CH] = blk_v ? sm.Vt[kbuf] : sm.Kt[kbuf];
+            float f[4][8];
+            if constexpr (!(NSPLIT == 1 && BF16)) stage_rows(n_s, f);
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
                 const int off = lds_off(cb * 8 + c, tb * 4, CH);
                 if constexpr (NSPLIT == 1 && BF16) {
-                    *reinterpret_cast<u32x2*>(&dst[0][off]) = u32x2{pk(f[0][c], f[1][c]), pk(f[2][c], f[3][c])};
+                    *reinterpret_cast<u32x2*>(&dst[0][off]) = tw[c];
                 } else {
                     uint16_t hb[4], lw[4];
 #pragma unroll
@@ -644,7 +670,10 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
     // ---- 4. the state update of the chunk at c0 (n tokens; K^T in buffer kpar, decay
     // factors in ring slot rs)
     auto phase_update = [&](int64_t c0, int n, int kpar, int rs) {
-        const int lane_c = opaque(lane);
+        // pipelined, the fragment reads' lane offsets (lx ^ K, eight values) stay live
+        // across the loop; with outputs (no registers to spare) they are recomputed
+        int lane_c = lane;
+        if constexpr (!PIPE) lane_c = opaque(lane);
         const int g4 = lane_c >> 4, n16 = lane_c & 15, lx = lane_c ^ g4;
         // ---- 6..8. Y = Wt X, R, X += K^T R for all owned column tiles at once (each A
         // fragment is read once per wave)
@@ -761,17 +790,21 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
             auto chain = [&](auto jc) {
                 constexpr int j = decltype(jc)::value;
                 auto put_block = [&](int i, const f32x4& z) {   // D layout -> A fragment entries
+                    // row 4g + e of the block: A lane 4g + e + 16 (col / 8), entry col % 8
                     const int f = ab_frag(i, j >> 1), col = 16 * (j & 1) + n16;
-                    uint16_t* const ph = &si.Ab[v][0][f][0];
-                    uint16_t* const pl = &si.Ab[v][1][f][0];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int idx = (4 * g4 + e + 16 * (col >> 3)) * 8 + (col & 7);
-                        uint16_t h, lo;
-                        to16<2>(z[e], h, lo);
-                        ph[idx] = h;
-                        pl[idx] = lo;
-                    }
+                    const int idx = (4 * g4 + 16 * (col >> 3)) * 8 + (col & 7);
+                    uint16_t* const ph = &si.Ab[v][0][f][idx];
+                    uint16_t* const pl = &si.Ab[v][1][f][idx];
+                    unsigned h0, h1, l0, l1;
+                    pack_f16_split(z, h0, h1, l0, l1);
+                    ph[0] = (uint16_t)h0;
+                    ph[8] = (uint16_t)(h0 >> 16);
+                    ph[16] = (uint16_t)h1;
+                    ph[24] = (uint16_t)(h1 >> 16);
+                    pl[0] = (uint16_t)l0;
+                    pl[8] = (uint16_t)(l0 >> 16);
+                    pl[16] = (uint16_t)l1;
+                    pl[24] = (uint16_t)(l1 >> 16);
                 };
                 // Ab_jj from the fp32 diagonal inverse (decayed: times e^{b_t - b_s}, t >= s)
                 f32x4 z;
@@ -893,7 +926,10 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
             if (nch > 1) prefetch(beg + CH);
             __syncthreads();
             phase_gram(beg, 0);
-            if (nch > 1) stage_b(chunk_len(beg + CH), 1);
+            if (nch > 1) {
+                pack_t(chunk_len(beg + CH));
+                stage_b(chunk_len(beg + CH), 1);
+            }
             __syncthreads();
             phase_ainv(0);
             if (nch > 1) {
