@@ -502,10 +502,12 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
         };
         if (wave < 4) {
             // (I + Lt_ii)^-1 = (I - N)^-1 with N = -Lt_ii strictly lower (N^16 = 0):
-            //   (I - N)^-1 = (I + N)(I + N^2)(I + N^4)(I + N^8)
-            // as 16 x 16 products on MFMA (hi / lo operands).  A product's A operand is the
-            // accumulator layout of the transposed factor, so the transposes are carried
-            // along; N^T comes from the same Gram block (it is symmetric).
+            //   (I - N)^-1 = P1 (I + N^4)(I + N^8),   P1 = (I + N)(I + N^2) = I + N + N^2 + N^3
+            // as 16 x 16 products on MFMA (hi / lo operands), formed transposed (Y^T = (I +
+            // N^8)^T (I + N^4)^T P1^T) with each identity term as the product's fp32
+            // accumulator input.  A product's A operand is the accumulator layout of the
+            // transposed factor, so N and N^T are carried along; N^T comes from the same
+            // Gram block (it is symmetric).
             const int i = wave;
             const f32x4 gacc = gram(i, i);
             const f32x4 bet = *reinterpret_cast<const f32x4*>(&sm.beta[rb][16 * i + 4 * g4]);
@@ -517,23 +519,21 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                 nd[e] = n16 < r ? -bet[e] * gacc[e] : 0.f;
                 nt[e] = r < n16 ? -bn * gacc[e] : 0.f;
             }
-            auto eye = [&](f32x4 x) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] += (4 * g4 + e == n16) ? 1.f : 0.f;
-                return x;
-            };
             const Hl16 n1 = hl16(nd), n1t = hl16(nt);
             const f32x4 n2 = mm16(n1t, n1), n2t = mm16(n1, n1t);                    // N^2, (N^2)^T
-            const Hl16 q2 = hl16(n2), q2t = hl16(n2t), e1t = hl16(eye(nt)), e2 = hl16(eye(n2));
-            const f32x4 n4 = mm16(q2t, q2), n4t = mm16(q2, q2t);                    // N^4, (N^4)^T
-            const f32x4 p1t = mm16(e2, e1t);                                        // ((I + N)(I + N^2))^T
-            const Hl16 q4 = hl16(n4), q4t = hl16(n4t), e4 = hl16(eye(n4)), r1t = hl16(p1t);
-            const f32x4 n8 = mm16(q4t, q4);                                         // N^8
-            const f32x4 p2t = mm16(e4, r1t);                                        // (P1 (I + N^4))^T
-            const Hl16 e8 = hl16(eye(n8)), r2t = hl16(p2t);
-            const f32x4 y = mm16(r2t, e8), yt = mm16(e8, r2t);                      // the inverse and its transpose
+            const Hl16 q2 = hl16(n2), q2t = hl16(n2t);
+            f32x4 c1;   // I + N^T + (N^2)^T
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sm.Sd[i][4 * g4 + e][n16] = y[e];
+            for (int e = 0; e < 4; ++e) c1[e] = nt[e] + n2t[e] + ((4 * g4 + e == n16) ? 1.f : 0.f);
+            const f32x4 n4 = mm16(q2t, q2), n4t = mm16(q2, q2t);                    // N^4, (N^4)^T
+            const f32x4 p1t = mma16(q2.h, q2.l, n1t.h, n1t.l, c1);                  // P1^T = c1 + (N^2)^T N^T
+            const Hl16 q4 = hl16(n4), q4t = hl16(n4t), r1t = hl16(p1t);
+            const f32x4 n8 = mm16(q4t, q4);                                         // N^8
+            const f32x4 p2t = mma16(q4.h, q4.l, r1t.h, r1t.l, p1t);                 // (P1 (I + N^4))^T
+            const Hl16 q8 = hl16(n8), r2t = hl16(p2t);
+            const f32x4 yt = mma16(q8.h, q8.l, r2t.h, r2t.l, p2t);                  // the inverse, transposed
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm.Sd[i][n16][4 * g4 + e] = yt[e];   // row-major (fp32)
             // A fragment (lane (g, n): row n, columns 4g .. 4g+3) = accumulator layout of the
             // transpose; the decayed block has the factors e^{b_t - b_s}, t >= s
             const float bt = lb[16 * i + n16];
@@ -789,22 +789,20 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
             const uint16_t(*const Dm)[4][256] = v ? sm.Dvd : sm.Dv;
             auto chain = [&](auto jc) {
                 constexpr int j = decltype(jc)::value;
-                auto put_block = [&](int i, const f32x4& z) {   // D layout -> A fragment entries
+                auto put_block = [&](int i, const Hl16& z) {   // D layout (hi / lo pairs) -> A fragment entries
                     // row 4g + e of the block: A lane 4g + e + 16 (col / 8), entry col % 8
                     const int f = ab_frag(i, j >> 1), col = 16 * (j & 1) + n16;
                     const int idx = (4 * g4 + 16 * (col >> 3)) * 8 + (col & 7);
                     uint16_t* const ph = &si.Ab[v][0][f][idx];
                     uint16_t* const pl = &si.Ab[v][1][f][idx];
-                    unsigned h0, h1, l0, l1;
-                    pack_f16_split(z, h0, h1, l0, l1);
-                    ph[0] = (uint16_t)h0;
-                    ph[8] = (uint16_t)(h0 >> 16);
-                    ph[16] = (uint16_t)h1;
-                    ph[24] = (uint16_t)(h1 >> 16);
-                    pl[0] = (uint16_t)l0;
-                    pl[8] = (uint16_t)(l0 >> 16);
-                    pl[16] = (uint16_t)l1;
-                    pl[24] = (uint16_t)(l1 >> 16);
+                    ph[0] = (uint16_t)z.h[0];
+                    ph[8] = (uint16_t)(z.h[0] >> 16);
+                    ph[16] = (uint16_t)z.h[1];
+                    ph[24] = (uint16_t)(z.h[1] >> 16);
+                    pl[0] = (uint16_t)z.l[0];
+                    pl[8] = (uint16_t)(z.l[0] >> 16);
+                    pl[16] = (uint16_t)z.l[1];
+                    pl[24] = (uint16_t)(z.l[1] >> 16);
                 };
                 // Ab_jj from the fp32 diagonal inverse (decayed: times e^{b_t - b_s}, t >= s)
                 f32x4 z;
@@ -820,14 +818,9 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                         z[e] = d * bet;
                     }
                 }
-                put_block(j, z);
-                u32x2 zh[3], zl[3];   // Ab_kj (k = j .. 2) as B operands
-                if constexpr (j < 3) {
-                    unsigned b0, b1, b2, b3;
-                    pack_f16_split(z, b0, b1, b2, b3);
-                    zh[j] = u32x2{b0, b1};
-                    zl[j] = u32x2{b2, b3};
-                }
+                Hl16 zs[4];   // Ab_kj (k = j .. 3) as hi / lo pairs: the B operands of the chain
+                zs[j] = hl16(z);
+                put_block(j, zs[j]);
 #pragma unroll
                 for (int i = j + 1; i < 4; ++i) {
                     f32x4 acc = zero4();
@@ -836,19 +829,14 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                         const int kb = i * (i - 1) / 2 + k;
                         const u32x2 ah = *reinterpret_cast<const u32x2*>(&Lm[0][kb][lane * 4]);
                         const u32x2 al = *reinterpret_cast<const u32x2*>(&Lm[1][kb][lane * 4]);
-                        acc = mma16(ah, al, zh[k], zl[k], acc);
+                        acc = mma16(ah, al, zs[k].h, zs[k].l, acc);
                     }
                     unsigned b0, b1, b2, b3;
                     pack_f16_split(acc, b0, b1, b2, b3);
                     const u32x2 dh = *reinterpret_cast<const u32x2*>(&Dm[0][i][lane * 4]);
                     const u32x2 dl = *reinterpret_cast<const u32x2*>(&Dm[1][i][lane * 4]);
-                    z = mma16(dh, dl, u32x2{b0, b1}, u32x2{b2, b3}, zero4());
-                    put_block(i, z);
-                    if (i < 3) {
-                        pack_f16_split(z, b0, b1, b2, b3);
-                        zh[i] = u32x2{b0, b1};
-                        zl[i] = u32x2{b2, b3};
-                    }
+                    zs[i] = hl16(mma16(dh, dl, u32x2{b0, b1}, u32x2{b2, b3}, zero4()));
+                    put_block(i, zs[i]);
                 }
             };
             switch (wave >> 1) {
