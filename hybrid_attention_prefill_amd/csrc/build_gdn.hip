@@ -147,6 +147,23 @@ __device__ __forceinline__ int opaque(int x) {
     return x;
 }
 
+// a lane's value moved by a DPP control (lanes without a source, or outside row_mask, get 0)
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xf, true));
+}
+// Inclusive sum over the 64 lanes of a wave on DPP: shifts by 1, 2, 4, 8 inside each row of
+// 16 lanes, then the last lane of row r added to the rows above it (row_bcast:15, :31).
+__device__ __forceinline__ float wave_inclusive_sum(float x) {
+    x += dpp_move<0x111, 0xf>(x);   // row_shr:1
+    x += dpp_move<0x112, 0xf>(x);   // row_shr:2
+    x += dpp_move<0x114, 0xf>(x);   // row_shr:4
+    x += dpp_move<0x118, 0xf>(x);   // row_shr:8
+    x += dpp_move<0x142, 0xa>(x);   // row_bcast:15 into rows 1, 3
+    x += dpp_move<0x143, 0xc>(x);   // row_bcast:31 into rows 2, 3
+    return x;
+}
+
 __device__ __forceinline__ u32x4 pack8(const uint16_t* x) {
     return u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
 }
@@ -381,13 +398,8 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
             // the lanes, one token each) with the decay factors of the state update (v_exp_f32)
             const bool ok = lane < n_s;
             sm.beta[rb][lane] = ok ? raw1(braw) : 0.f;
-            float x = ok ? raw1(graw) : 0.f;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(x, off, 64);
-                if (lane >= off) x += y;
-            }
-            const float bc = __shfl(x, 63, 64);
+            const float x = wave_inclusive_sum(ok ? raw1(graw) : 0.f);
+            const float bc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
             const float b2 = x * kLog2e;
             sm.lb[rb][lane] = b2;
             sm.eb[rb][lane] = __builtin_amdgcn_exp2f(b2);
