@@ -833,18 +833,24 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                 Hl16 zs[4];   // Ab_kj (k = j .. 3) as hi / lo pairs: the B operands of the chain
                 zs[j] = hl16(z);
                 put_block(j, zs[j]);
+                // right-looking: as soon as Ab_kj is known, its terms of every later block go
+                // out together (independent products), then the next block is finished; each
+                // block's terms still accumulate in the order k = j, j + 1, ..
+                f32x4 acc[4];
 #pragma unroll
-                for (int i = j + 1; i < 4; ++i) {
-                    f32x4 acc = zero4();
+                for (int i = 0; i < 4; ++i) acc[i] = zero4();
 #pragma unroll
-                    for (int k = j; k < i; ++k) {
+                for (int k = j; k < 3; ++k) {
+#pragma unroll
+                    for (int i = k + 1; i < 4; ++i) {
                         const int kb = i * (i - 1) / 2 + k;
                         const u32x2 ah = *reinterpret_cast<const u32x2*>(&Lm[0][kb][lane * 4]);
                         const u32x2 al = *reinterpret_cast<const u32x2*>(&Lm[1][kb][lane * 4]);
-                        acc = mma16(ah, al, zs[k].h, zs[k].l, acc);
+                        acc[i] = mma16(ah, al, zs[k].h, zs[k].l, acc[i]);
                     }
+                    const int i = k + 1;
                     unsigned b0, b1, b2, b3;
-                    pack_f16_split(acc, b0, b1, b2, b3);
+                    pack_f16_split(acc[i], b0, b1, b2, b3);
                     const u32x2 dh = *reinterpret_cast<const u32x2*>(&Dm[0][i][lane * 4]);
                     const u32x2 dl = *reinterpret_cast<const u32x2*>(&Dm[1][i][lane * 4]);
                     zs[i] = hl16(mma16(dh, dl, u32x2{b0, b1}, u32x2{b2, b3}, zero4()));
