@@ -883,18 +883,26 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                 const int v = is_s ? 1 : 0;
                 const uint16_t(*src)[D * CH] = is_s ? sm.Vt[kpar] : sm.Kt[kpar];
                 const Frag<NSPLIT> kf[2] = {frag_of<NSPLIT, CH>(src, q, 0, lx), frag_of<NSPLIT, CH>(src, q, 1, lx)};
+                // the six fragment pairs are read together, then the products go out in an
+                // order where consecutive ones feed different accumulators
+                f16x8 ah[6], al[6];
+#pragma unroll
+                for (int f = 0; f < 6; ++f) {
+                    ah[f] = *reinterpret_cast<const f16x8*>(&si.Ab[v][0][f][lane * 8]);
+                    al[f] = *reinterpret_cast<const f16x8*>(&si.Ab[v][1][f][lane * 8]);
+                }
                 f32x4 acc[4];
 #pragma unroll
-                for (int tt = 0; tt < 4; ++tt) {
-                    acc[tt] = zero4();
+                for (int tt = 0; tt < 4; ++tt) acc[tt] = zero4();
 #pragma unroll
-                    for (int ks = 0; ks <= (tt >> 1); ++ks) {
-                        const int f = ab_frag(tt, ks);
-                        const f16x8 ah = *reinterpret_cast<const f16x8*>(&si.Ab[v][0][f][lane * 8]);
-                        const f16x8 al = *reinterpret_cast<const f16x8*>(&si.Ab[v][1][f][lane * 8]);
-                        acc[tt] = mma_f16(ah, kf[ks].h, acc[tt]);
-                        acc[tt] = mma_f16(al, kf[ks].h, acc[tt]);
-                        if constexpr (NSPLIT == 2) acc[tt] = mma_f16(ah, kf[ks].l, acc[tt]);
+                for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+                    for (int tt = 2 * ks; tt < 4; ++tt) acc[tt] = mma_f16(ah[ab_frag(tt, ks)], kf[ks].h, acc[tt]);
+#pragma unroll
+                    for (int tt = 2 * ks; tt < 4; ++tt) acc[tt] = mma_f16(al[ab_frag(tt, ks)], kf[ks].h, acc[tt]);
+                    if constexpr (NSPLIT == 2) {
+#pragma unroll
+                        for (int tt = 2 * ks; tt < 4; ++tt) acc[tt] = mma_f16(ah[ab_frag(tt, ks)], kf[ks].l, acc[tt]);
                     }
                 }
                 if (is_s) {
