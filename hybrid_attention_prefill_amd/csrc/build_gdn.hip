@@ -52,7 +52,7 @@ struct alignas(16) GdnSmem {
     uint16_t Kr[NSPLIT][CH * KP];  // K, rows = tokens, cols = channels (>= D zero)
     uint16_t Kt[KTB][NSPLIT][D * CH];   // K^T, rows = channels, cols = tokens
     uint16_t Vt[KTB][NSPLIT][D * CH];   // V^T, rows = channels, cols = tokens
-    uint16_t Wt[NSPLIT][CH * KP];  // Wt, rows = tokens, cols = channels (>= D zero)
+    uint16_t Wt[NSPLIT][CH * KP];  // -Wt, rows = tokens, cols = channels (>= D zero)
     // block forward substitution operands: A fragments of v_mfma_f32_16x16x16_f16 (lane
     // 16 g + r holds row r, columns 4 g .. 4 g + 3), fp16 hi / lo planes
     uint16_t Ln[2][6][256];        // -Lt_ij for the blocks j < i (index i (i - 1) / 2 + j)
@@ -662,7 +662,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                 if (s_tile(c)) {
 #pragma unroll
                     for (int tt = 0; tt < 4; ++tt) U[tt][c] = sol[tt][c];
-                } else {   // Wt rows 16i + 4g + e, channel 16q + n, token-major
+                } else {   // -Wt rows 16i + 4g + e, channel 16q + n, token-major
                     const int q = tile(c);
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
@@ -670,7 +670,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                         for (int e = 0; e < 4; ++e) {
                             const int off = lds_off(16 * i + 4 * g4 + e, 16 * q + n16, KP);
                             uint16_t h, lo;
-                            to16<NSPLIT>(sol[i][c][e], h, lo);
+                            to16<NSPLIT>(-sol[i][c][e], h, lo);
                             sm.Wt[0][off] = h;
                             if constexpr (NSPLIT == 2) sm.Wt[1][off] = lo;
                         }
@@ -737,12 +737,11 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int t = tt * 16 + 4 * g4 + e;
+                        // the plane holds -Wt, so R = -Wt X already for the H tiles
                         if (is_s) {   // new values U' = U - diag(e^b) Wt S_0; R = diag(e^{b_C - b}) U'
-                            const float up = U[tt][c][e] - sm.eb[rs][t] * R[tt][c][e];
+                            const float up = U[tt][c][e] + sm.eb[rs][t] * R[tt][c][e];
                             U[tt][c][e] = up;
                             R[tt][c][e] = sm.ebr[rs][t] * up;
-                        } else {
-                            R[tt][c][e] = -R[tt][c][e];
                         }
                     }
                 rb[0][c] = dpair_to_frag<NSPLIT>(R[0][c], R[1][c]);
@@ -908,14 +907,14 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                 if (is_s) {
 #pragma unroll
                     for (int tt = 0; tt < 4; ++tt) U[tt][c] = acc[tt];
-                } else {   // Wt rows 16 tt + 4 g + e, channel 16 q + n, token-major
+                } else {   // -Wt rows 16 tt + 4 g + e, channel 16 q + n, token-major
 #pragma unroll
                     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int off = lds_off(16 * tt + 4 * g4 + e, 16 * q + n16, KP);
                             uint16_t h, lo;
-                            to16<NSPLIT>(acc[tt][e], h, lo);
+                            to16<NSPLIT>(-acc[tt][e], h, lo);
                             sm.Wt[0][off] = h;
                             if constexpr (NSPLIT == 2) sm.Wt[1][off] = lo;
                         }
