@@ -25,6 +25,7 @@ bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -55,31 +56,62 @@ def parse():
 
 
 class Timer:
-    """HIP-event timing of library calls on the current stream."""
+    """HIP-event timing of library calls on the current stream.
+
+    The events are created with hipEventDisableSystemFence: timing-only events.  A default
+    event's record ends with a system-scope fence (cache write-back and invalidation), which
+    costs the GPU about 5 us per record and lands inside the measured interval; the elapsed
+    times are read only after a device synchronisation, which is all these events need."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence
 
     def __init__(self, torch):
         self.torch = torch
         self.pending = {}
         self.totals = {}
         self.counts = {}
+        # the HIP runtime torch and the library already share (same soname)
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.free = []
+
+    def _event(self):
+        if self.free:
+            return self.free.pop()
+        ev = ctypes.c_void_p()
+        if self.hip.hipEventCreateWithFlags(ctypes.byref(ev), self.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        return ev
 
     def run(self, name, fn):
-        s = self.torch.cuda.Event(enable_timing=True)
-        e = self.torch.cuda.Event(enable_timing=True)
-        s.record()
+        stream = ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream)
+        s, e = self._event(), self._event()
+        if self.hip.hipEventRecord(s, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
         fn()
-        e.record()
+        if self.hip.hipEventRecord(e, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
         self.pending.setdefault(name, []).append((s, e))
 
     def collect(self):
         self.torch.cuda.synchronize()
+        ms = ctypes.c_float()
         for name, evs in self.pending.items():
             for s, e in evs:
-                self.totals[name] = self.totals.get(name, 0.0) + s.elapsed_time(e) * 1e-3
+                if self.hip.hipEventElapsedTime(ctypes.byref(ms), s, e) != 0:
+                    raise RuntimeError("hipEventElapsedTime failed")
+                self.totals[name] = self.totals.get(name, 0.0) + ms.value * 1e-3
                 self.counts[name] = self.counts.get(name, 0) + 1
+                self.free += [s, e]
         self.pending = {}
 
     def reset(self):
+        for evs in self.pending.values():
+            for s, e in evs:
+                self.free += [s, e]
         self.pending, self.totals, self.counts = {}, {}, {}
 
 
