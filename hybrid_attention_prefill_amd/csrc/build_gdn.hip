@@ -329,17 +329,12 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
 
     // ---- staging of a chunk of n_s tokens from the prefetched registers, in two parts:
     // (a) K token-major, betas and log-decays into ring slot rb; (b) K^T and V^T channel-major
-    // into buffer kbuf (16-bit operands).  Rows past the segment are zeroed (only the last
-    // chunk has any).
-    auto stage_rows = [&](int n_s, float (&f)[4][8]) {
-        const int tb = opaque(tb0);
-        if (n_s < CH) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (tb * 4 + r >= n_s)
-#pragma unroll
-                    for (int x = 0; x < WPR; ++x) raw[r][x] = u32x4{0u, 0u, 0u, 0u};
-        }
+    // into buffer kbuf (16-bit operands).
+    // Rows past the segment (the last chunk's) hold copies of its last row, finite values:
+    // their betas are staged as zero, so their rows and columns of Ab are zero (Lt has zero
+    // rows there and (I + Lt)^-1 diag(b) zero columns), and with them their rows of Wt, U and
+    // R: they enter no product with a nonzero weight and need no zeroing.
+    auto stage_rows = [&](float (&f)[4][8]) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -354,7 +349,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
         if constexpr (NSPLIT == 1 && BF16) {
             if (has_blk) {
                 float f[4][8];
-                stage_rows(n_s, f);
+                stage_rows(f);
 #pragma unroll
                 for (int c = 0; c < 8; ++c) tw[c] = u32x2{pk(f[0][c], f[1][c]), pk(f[2][c], f[3][c])};
             }
@@ -365,7 +360,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
         if constexpr (NSPLIT == 1 && BF16) {
             if (has_blk) {
                 float f[4][8];
-                stage_rows(n_s, f);
+                stage_rows(f);
 #pragma unroll
                 for (int c = 0; c < 8; ++c) tw[c] = u32x2{pk(f[0][c], f[1][c]), pk(f[2][c], f[3][c])};
                 if (!blk_v) {   // K rows (8 channels of one token = 16 contiguous bytes)
@@ -377,7 +372,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
             }
         } else if (has_blk && !blk_v) {   // K rows (8 channels of one token = 16 contiguous bytes)
             float f[4][8];
-            stage_rows(n_s, f);
+            stage_rows(f);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int off = lds_off(tb * 4 + r, cb * 8, KP);
@@ -412,7 +407,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
         if (has_blk) {   // transposed: one channel row, 4 consecutive tokens = 8 contiguous bytes
             uint16_t(*dst)[D * CH] = blk_v ? sm.Vt[kbuf] : sm.Kt[kbuf];
             float f[4][8];
-            if constexpr (!(NSPLIT == 1 && BF16)) stage_rows(n_s, f);
+            if constexpr (!(NSPLIT == 1 && BF16)) stage_rows(f);
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
                 const int off = lds_off(cb * 8 + c, tb * 4, CH);
