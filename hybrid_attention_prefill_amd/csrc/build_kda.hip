@@ -44,6 +44,11 @@
 namespace hypic {
 
 namespace {
+
+template <int V>
+struct IntConst {
+    static constexpr int value = V;
+};
 using namespace bld;
 
 constexpr int CK = 32;        // chunk length
@@ -175,12 +180,15 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                     x[i] = run;
                 }
             }
-            float pre = 0.f;   // sum of the quarters before q
-#pragma unroll
-            for (int o = 1; o < 4; ++o) {
-                const float y = __shfl_up(run, o, 4);
-                if (q >= o) pre += y;
-            }
+            // sum of the quarters before q: the quad's lanes 0, 1, 2 broadcast by DPP quad_perm
+            auto quad_bcast = [](float v, auto ctrl) {
+                return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v),
+                                                                          decltype(ctrl)::value, 0xf, 0xf, false));
+            };
+            const float r0 = quad_bcast(run, IntConst<0x00>{});   // quad_perm:[0,0,0,0]
+            const float r1 = quad_bcast(run, IntConst<0x55>{});   // quad_perm:[1,1,1,1]
+            const float r2 = quad_bcast(run, IntConst<0xAA>{});   // quad_perm:[2,2,2,2]
+            const float pre = (q >= 1 ? r0 : 0.f) + (q >= 2 ? r1 : 0.f) + (q >= 3 ? r2 : 0.f);
             if (c < D) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) sm.Ag[8 * q + i + 1][c] = x[i] + pre;
