@@ -18,12 +18,16 @@
 //
 // One workgroup (8 waves) per (segment, head).  The augmented state X = [H | S]
 // (d x 2d, fp32) lives in MFMA accumulators, 16-column tiles dealt to waves;
-// every product runs on v_mfma_f32_16x16x32_f16 with fp32 accumulation:
+// the chunk products run on v_mfma_f32_16x16x32_f16 with fp32 accumulation:
 // K K^T, Wt, U, Y = Wt X and X += K^T R.  X and R reach the B operand without
-// LDS through two cross-lane swaps.  The 64x64 triangular inverse is blocked
-// 16x16: diagonal blocks by forward substitution (fp32), the rest with
-// v_mfma_f32_16x16x4_f32.  Operands are fp16 (one rounding, NSPLIT = 1) for
-// bf16 inputs, or fp16 hi + lo with three products (NSPLIT = 2) for fp32 inputs.
+// LDS through two cross-lane swaps.  Operands are fp16 (one rounding, NSPLIT = 1)
+// for bf16 inputs, or fp16 hi + lo with three products (NSPLIT = 2) for fp32
+// inputs.  The 64 x 64 triangular system is blocked 16 x 16: each diagonal block
+// is inverted as the product (I + N)(I + N^2)(I + N^4)(I + N^8), N = -Lt_ii, on
+// v_mfma_f32_16x16x16_f16 with hi / lo operands.  Without per-token outputs the
+// chunks are pipelined (two steps per chunk, described at the loop): the inverse
+// At diag(b) is formed explicitly from the blocks and Wt, U are dense products
+// with it.  With outputs, Wt and U come from block forward substitution.
 //
 // Data movement: the next chunk's k, v, gates and betas are loaded into
 // registers while the current chunk is processed (raw bits, unconditional
