@@ -12,9 +12,10 @@
 // (A[t][s] = e^{b_t - b_s} At[t][s] has only non-positive exponents).  Then
 //     S <- e^{b_C} S + K^T diag(e^{b_C - b}) (U - D Wt S)
 //     H <- H - K^T (Wt H),      T_C = e^{sum of all g} H
-// where H is the undecayed transition product, so the T columns never
-// underflow the 16-bit MFMA operands however strong the decay; the decay of T
-// is one fp32 scale at the end.
+// where H is the undecayed transition product, so the decay never pushes the T
+// columns out of the 16-bit MFMA operands' range; the decay of T is one fp32
+// scale at the end.  The erase alone still shrinks H over long segments, so H
+// is renormalised by powers of two between chunks (exponent kept apart).
 //
 // One workgroup (8 waves) per (segment, head).  The augmented state X = [H | S]
 // (d x 2d, fp32) lives in MFMA accumulators, 16-column tiles dealt to waves;
@@ -67,6 +68,7 @@ struct alignas(16) GdnSmem {
     float beta[RB][CH];
     float lb[RB][CH], eb[RB][CH], ebr[RB][CH];   // b_t (log2 units), e^{b_t}, e^{b_C - b_t}
     float bC[RB];
+    float hmax[2][8];              // per wave: max |H| after a chunk's update (by chunk parity)
 };
 
 // The chunk's inverse with the betas folded in, Ab = (I + Lt)^-1 diag(b), and its decayed
@@ -266,6 +268,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
         }
     }
     float log_s = 0.f;  // log of the scalar decay factored out of T
+    int h2 = 0;         // power of two factored out of H: T_C = e^{log_s} 2^{h2} H
 
     // ---- next-chunk prefetch: thread -> (matrix K or V, 4-token block tb, 8-channel block cb)
     const bool has_blk = tid < 2 * NBLK;
@@ -680,7 +683,49 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
 
     // ---- 4. the state update of the chunk at c0 (n tokens; K^T in buffer kpar, decay
     // factors in ring slot rs)
-    auto phase_update = [&](int64_t c0, int n, int kpar, int rs) {
+    // The erase alone contracts H (token by token in the direction of k_t), so over long
+    // segments with weak decay its entries fall towards fp16's subnormal range, where they
+    // lose precision and then flush to zero as MFMA operands.  After every update each wave
+    // posts the largest |H| of its tiles; before the next update, once the largest over the
+    // workgroup is below 1/4, H is scaled by the power of two that brings it into [1/2, 1)
+    // (exact) and the exponent is kept in h2.
+    auto h_renorm = [&](int slot) {
+        if constexpr (WANT_T) {
+            float mm = 0.f;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) mm = fmaxf(mm, sm.hmax[slot][w]);
+            if (mm > 0.f && mm < 0.25f) {
+                int em;
+                frexpf(mm, &em);
+                const float sc = ldexpf(1.f, -em);
+#pragma unroll
+                for (int c = 0; c < CTW; ++c)
+                    if (own_tile(c) && !s_tile(c))
+#pragma unroll
+                        for (int rt = 0; rt < RT; ++rt) X[rt][c] *= sc;
+                h2 += em;
+            }
+        }
+    };
+    auto h_post = [&](int slot) {
+        if constexpr (WANT_T) {
+            float m = 0.f;
+#pragma unroll
+            for (int c = 0; c < CTW; ++c)
+                if (own_tile(c) && !s_tile(c))
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(X[rt][c][e]));
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+            if (lane == 0) sm.hmax[slot][wave] = m;
+        }
+    };
+
+    auto phase_update = [&](int64_t c0, int n, int kpar, int rs, int slot) {
+        // slot: parity of the chunk's index in the segment (renormalisation records)
+        if (c0 != beg) h_renorm(slot ^ 1);
         // pipelined, the fragment reads' lane offsets (lx ^ K, eight values) stay live
         // across the loop; with outputs (no registers to spare) they are recomputed
         int lane_c = lane;
@@ -782,6 +827,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                 }
         }
         log_s += bC;
+        h_post(slot);
     };
 
     // ---- 3a. the inverse blocks Ab_ij (i >= j) of the chunk whose Gram blocks are in LDS
@@ -955,7 +1001,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
         }
         for (int ci = 0; ci < nch; ++ci) {
             const int64_t c0 = beg + (int64_t)ci * CH;
-            phase_update(c0, chunk_len(c0), ci & 1, ci % 3);
+            phase_update(c0, chunk_len(c0), ci & 1, ci % 3, ci & 1);
             if (ci + 1 < nch) phase_ainv((ci + 1) % 3);
             if (ci + 2 < nch) stage_a(chunk_len(c0 + 2 * CH), (ci + 2) % 3);
             __syncthreads();
@@ -1009,13 +1055,13 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
                 if (c0 + 2 * CH < end) fetch_q(c0 + 2 * CH, qbuf);
             }
             __syncthreads();
-            phase_update(c0, n, 0, 0);
+            phase_update(c0, n, 0, 0, qbuf);
             __syncthreads();
         }
     }
 
-    // ---- emit T_C = e^{log_s} H and S(C|0)
-    const float tscale = expf(log_s);
+    // ---- emit T_C = e^{log_s} 2^{h2} H and S(C|0)
+    const float tscale = ldexpf(expf(log_s), h2);
     const size_t pair = (size_t)out * H + h;
 #pragma unroll
     for (int c = 0; c < CTW; ++c) {

@@ -260,6 +260,10 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void compose_dense_kernel(
         // step j from sA; prefetch step j+1 into sB; id of step j+2
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         if (j > 0 && (j & (kRingFill - 1)) == 0) {  // steps j+256 .. j+511 replace steps j-256 .. j-1
+            // Waves meet only at steps that have a pair, so after a run of skipped steps a
+            // wave may still have to read the id of step j-1 (slot (j+255) & 511): every wave
+            // gets here before any of them refills.
+            lds_barrier();
             fill_ring(j + kRingFill);
             lds_barrier();
         }

@@ -18,9 +18,11 @@ oracle consume bit-identical inputs.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import functools
 import math
+import os
 
 import numpy as np
 
@@ -35,11 +37,46 @@ def _e_softplus(sigma: float = 1.0) -> float:
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to the nearest bfloat16 (ties to even); result is float32."""
+    """Round finite float32 values to the nearest bfloat16 (ties to even); result is float32.
+    (In 32-bit integer arithmetic: the largest finite pattern plus the rounding bias stays
+    below 2^32.)"""
     a = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
-    u = a.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32).reshape(a.shape)
+    u = a.view(np.uint32)
+    r = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) & np.uint32(0xFFFF0000)
+    return r.view(np.float32).reshape(a.shape)
+
+
+_CHUNK = 1 << 21          # values per chunk of a draw
+
+
+def _draw(ss, shape, post=None):
+    """float32 standard normals of `shape`, drawn in chunks of whole leading-axis rows: chunk i
+    comes from child i of the SeedSequence `ss` (so the values do not depend on how many
+    threads draw them), and `post` (a row-wise map) turns each chunk into the stored float32
+    values.  The chunks are drawn and mapped on a thread pool (numpy releases the GIL)."""
+    shape = tuple(int(x) for x in shape)
+    n = shape[0]
+    row = int(np.prod(shape[1:], dtype=np.int64)) if len(shape) > 1 else 1
+    per = max(1, _CHUNK // max(row, 1))
+    nch = max(1, (n + per - 1) // per)
+    kids = ss.spawn(nch)
+    out = np.empty(shape, dtype=np.float32)
+
+    def work(i):
+        a, b = i * per, min(n, (i + 1) * per)
+        if b <= a:
+            return
+        z = np.random.default_rng(kids[i]).standard_normal((b - a,) + shape[1:], dtype=np.float32)
+        out[a:b] = z if post is None else post(z)
+
+    workers = min(16, os.cpu_count() or 1, nch)
+    if workers <= 1:
+        for i in range(nch):
+            work(i)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(work, range(nch)))
+    return out
 
 
 def _softplus(x):
@@ -51,6 +88,8 @@ def _sigmoid(x):
 
 
 def _unit_rows(x):
+    """Rows scaled to unit L2 norm, in float64."""
+    x = np.asarray(x, dtype=np.float64)
     return x / np.linalg.norm(x, axis=-1, keepdims=True)
 
 
@@ -105,29 +144,36 @@ def _finish(x, in_dtype):
     return round_bf16(x) if in_dtype == "bf16" else x
 
 
-def _tokens(rng_k, rng_v, n_tok, H, dk, dv, *, k_unit, kv_scale, in_dtype):
-    k = rng_k.standard_normal((n_tok, H, dk))
-    k = _unit_rows(k) if k_unit else k * kv_scale
-    v = rng_v.standard_normal((n_tok, H, dv)) * (kv_scale if not k_unit else 1.0)
-    return _finish(k, in_dtype), _finish(v, in_dtype)
+def _tokens(ss_k, ss_v, n_tok, H, dk, dv, *, k_unit, kv_scale, in_dtype):
+    """Keys (unit rows, normalised in float64 before rounding, or scaled normals) and values."""
+    if k_unit:
+        k = _draw(ss_k, (n_tok, H, dk), lambda z: _finish(_unit_rows(z), in_dtype))
+    else:
+        k = _draw(ss_k, (n_tok, H, dk), lambda z: _finish(z * np.float32(kv_scale), in_dtype))
+    vs = np.float32(kv_scale if not k_unit else 1.0)
+    v = _draw(ss_v, (n_tok, H, dv), lambda z: _finish(z * vs, in_dtype))
+    return k, v
+
+
+def _unit_q(ss_q, n_tok, H, d, in_dtype):
+    return _draw(ss_q, (n_tok, H, d), lambda z: _finish(_unit_rows(z), in_dtype))
 
 
 def _gdn_tiny(seed, *, stress, n_heads=1, d=16, n_seg=2, seg_len=64, lengths=None):
     """Tiny gated DeltaNet, fp32: 1 head, d=16, 2 segments of 64 tokens."""
-    ss = np.random.SeedSequence(seed).spawn(6)
-    rk, rv, rb, rg, rq, _ = [np.random.default_rng(s) for s in ss]
+    ss_k, ss_v, ss_b, ss_g, ss_q, _ = np.random.SeedSequence(seed).spawn(6)
     lens = np.full(n_seg, seg_len) if lengths is None else np.asarray(lengths)
     N = int(lens.sum())
-    k, v = _tokens(rk, rv, N, n_heads, d, d, k_unit=True, kv_scale=1.0, in_dtype="f32")
-    zb = rb.standard_normal((N, n_heads))
-    zg = rg.standard_normal((N, n_heads))
+    k, v = _tokens(ss_k, ss_v, N, n_heads, d, d, k_unit=True, kv_scale=1.0, in_dtype="f32")
+    zb = _draw(ss_b, (N, n_heads)).astype(np.float64)
+    zg = _draw(ss_g, (N, n_heads)).astype(np.float64)
     if stress:
         beta = _sigmoid(zb - 4.0)
         g = -_softplus(zg) / (float(np.mean(lens)) * _e_softplus())
     else:
         beta = _sigmoid(zb)
         g = -_softplus(zg)
-    q = _finish(_unit_rows(rq.standard_normal((N, n_heads, d))), "f32")
+    q = _unit_q(ss_q, N, n_heads, d, "f32")
     starts = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
     return Workload(name="gdn-tiny-f32" + ("-stress" if stress else ""), n_heads=n_heads,
                     d_k=d, d_v=d, gate=GATE_TOKEN, delta=True, in_dtype="f32", k=k, v=v,
@@ -144,14 +190,14 @@ def retnet_gamma(n_heads):
 
 def _retnet(seed, *, stress, n_heads=8, d=64, n_seg=16, seg_len=512, lengths=None):
     """RetNet-style scalar decay, bf16 k/v, fp32 decay: 8 heads, d=64, 16 x 512."""
-    ss = np.random.SeedSequence(seed).spawn(4)
-    rk, rv, rq, _ = [np.random.default_rng(s) for s in ss]
+    ss_k, ss_v, ss_q, _ = np.random.SeedSequence(seed).spawn(4)
     lens = np.full(n_seg, seg_len) if lengths is None else np.asarray(lengths)
     N = int(lens.sum())
-    k, v = _tokens(rk, rv, N, n_heads, d, d, k_unit=False, kv_scale=1.0 / math.sqrt(d),
+    k, v = _tokens(ss_k, ss_v, N, n_heads, d, d, k_unit=False, kv_scale=1.0 / math.sqrt(d),
                    in_dtype="bf16")
     g = np.log(retnet_gamma(n_heads)).astype(np.float32)   # decay stays fp32
-    q = _finish(rq.standard_normal((N, n_heads, d)) / math.sqrt(d), "bf16")
+    qs = np.float32(1.0 / math.sqrt(d))
+    q = _draw(ss_q, (N, n_heads, d), lambda z: _finish(z * qs, "bf16"))
     starts = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
     return Workload(name="retnet-8h-d64", n_heads=n_heads, d_k=d, d_v=d, gate=GATE_HEAD,
                     delta=False, in_dtype="bf16", k=k, v=v, g=g, beta=None, seg_start=starts,
@@ -161,18 +207,17 @@ def _retnet(seed, *, stress, n_heads=8, d=64, n_seg=16, seg_len=512, lengths=Non
 
 
 def _gdn_tokens(seed, N, H, d, *, stress, mean_len, gate_scale=0.1):
-    ss = np.random.SeedSequence(seed).spawn(6)
-    rk, rv, rb, rg, rq, _ = [np.random.default_rng(s) for s in ss]
-    k, v = _tokens(rk, rv, N, H, d, d, k_unit=True, kv_scale=1.0, in_dtype="bf16")
-    zb = rb.standard_normal((N, H))
-    zg = rg.standard_normal((N, H))
+    ss_k, ss_v, ss_b, ss_g, ss_q, _ = np.random.SeedSequence(seed).spawn(6)
+    k, v = _tokens(ss_k, ss_v, N, H, d, d, k_unit=True, kv_scale=1.0, in_dtype="bf16")
+    zb = _draw(ss_b, (N, H)).astype(np.float64)
+    zg = _draw(ss_g, (N, H)).astype(np.float64)
     if stress:
         beta = _sigmoid(zb - 4.0)
         g = -_softplus(zg) / (mean_len * _e_softplus())
     else:
         beta = _sigmoid(zb)
         g = -_softplus(zg) * gate_scale
-    q = _finish(_unit_rows(rq.standard_normal((N, H, d))), "bf16")
+    q = _unit_q(ss_q, N, H, d, "bf16")
     return k, v, _finish(beta, "bf16"), _finish(g, "bf16"), q
 
 
@@ -242,18 +287,15 @@ def _kda_131k(seed, *, stress, n_heads=32, d=128, n_seg=64, seg_len=2048, n_req=
     gate_sigma: spread of the per-channel log-gates, g = -softplus(gate_sigma z)."""
     lens = np.full(n_seg, seg_len) if lengths is None else np.asarray(lengths)
     N = int(lens.sum())
-    ss = np.random.SeedSequence(seed).spawn(7)
-    rk, rv, rb, rg, rq, rp, _ = [np.random.default_rng(s) for s in ss]
-    k, v = _tokens(rk, rv, N, n_heads, d, d, k_unit=True, kv_scale=1.0, in_dtype="bf16")
-    zb = rb.standard_normal((N, n_heads))
-    zg = rg.standard_normal((N, n_heads, d))
-    if stress:
-        beta = _sigmoid(zb - 4.0)
-        g = -_softplus(zg * gate_sigma) / (float(np.mean(lens)) * _e_softplus(gate_sigma))
-    else:
-        beta = _sigmoid(zb)
-        g = -_softplus(zg * gate_sigma)
-    q = _finish(_unit_rows(rq.standard_normal((N, n_heads, d))), "bf16")
+    ss_k, ss_v, ss_b, ss_g, ss_q, ss_p, _ = np.random.SeedSequence(seed).spawn(7)
+    rp = np.random.default_rng(ss_p)
+    k, v = _tokens(ss_k, ss_v, N, n_heads, d, d, k_unit=True, kv_scale=1.0, in_dtype="bf16")
+    zb = _draw(ss_b, (N, n_heads)).astype(np.float64)
+    gscale = 1.0 / (float(np.mean(lens)) * _e_softplus(gate_sigma)) if stress else 1.0
+    g = _draw(ss_g, (N, n_heads, d),
+              lambda z: _finish(-_softplus(z.astype(np.float64) * gate_sigma) * gscale, "bf16"))
+    beta = _sigmoid(zb - 4.0) if stress else _sigmoid(zb)
+    # the reuse plan has no seam windows, so no token is read out and no q is drawn
     starts = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
     # chain (request r, layer l) draws n_step ids uniformly from that layer's n_seg pairs;
     # pair index = l * n_seg + segment (one distinct cache copy per layer)
@@ -262,8 +304,8 @@ def _kda_131k(seed, *, stress, n_heads=32, d=128, n_seg=64, seg_len=2048, n_req=
     return Workload(name="kda-32h-d128-131k" + ("-gate-first" if gate_first else "") + ("-stress" if stress else ""),
                     n_heads=n_heads, d_k=d, d_v=d, gate=GATE_DIAG, delta=2 if gate_first else 1,
                     in_dtype="bf16", k=k, v=v,
-                    g=_finish(g, "bf16"), beta=_finish(beta, "bf16"), seg_start=starts,
-                    cache_begin=starts[:-1].copy(), cache_end=starts[1:].copy(), q=q,
+                    g=g, beta=_finish(beta, "bf16"), seg_start=starts,
+                    cache_begin=starts[:-1].copy(), cache_end=starts[1:].copy(), q=None,
                     scale=1.0 / math.sqrt(d), pair_id=ids.reshape(n_layers * n_req, n_step),
                     n_layers=n_layers)
 
@@ -279,27 +321,26 @@ def _variant(family, seed, *, stress, n_heads=16, d=None, n_seg=16, seg_len=1024
     d = (64 if family == "mamba2" else 128) if d is None else d
     lens = np.full(n_seg, seg_len) if lengths is None else np.asarray(lengths)
     N = int(lens.sum())
-    ss = np.random.SeedSequence(seed).spawn(6)
-    rk, rv, rb, rg, rq, _ = [np.random.default_rng(s) for s in ss]
-    k, v = _tokens(rk, rv, N, n_heads, d, d, k_unit=True, kv_scale=1.0, in_dtype=in_dtype)
+    if family not in ("gla", "mamba2", "deltanet"):
+        raise ValueError(f"unknown family {family!r}")
+    ss_k, ss_v, ss_b, ss_g, ss_q, _ = np.random.SeedSequence(seed).spawn(6)
+    k, v = _tokens(ss_k, ss_v, N, n_heads, d, d, k_unit=True, kv_scale=1.0, in_dtype=in_dtype)
     mean_len = float(np.mean(lens))
     beta = None
     if family == "gla":
         gate, delta = GATE_DIAG, False
-        zg = rg.standard_normal((N, n_heads, d))
+        zg = _draw(ss_g, (N, n_heads, d)).astype(np.float64)
         g = -_softplus(zg) / (mean_len * _e_softplus() if stress else 16.0)
     elif family == "mamba2":
         gate, delta = GATE_TOKEN, False
-        zg = rg.standard_normal((N, n_heads))
+        zg = _draw(ss_g, (N, n_heads)).astype(np.float64)
         g = -_softplus(zg) / (mean_len * _e_softplus()) if stress else -0.1 * _softplus(zg)
-    elif family == "deltanet":
+    else:
         gate, delta = GATE_TOKEN, True
         g = np.zeros((N, n_heads))
-        zb = rb.standard_normal((N, n_heads))
+        zb = _draw(ss_b, (N, n_heads)).astype(np.float64)
         beta = _finish(_sigmoid(zb - 4.0) if stress else _sigmoid(zb), in_dtype)
-    else:
-        raise ValueError(f"unknown family {family!r}")
-    q = _finish(_unit_rows(rq.standard_normal((N, n_heads, d))), in_dtype)
+    q = _unit_q(ss_q, N, n_heads, d, in_dtype)
     starts = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
     name = {"gla": "gla-16h-d128-16k", "mamba2": "mamba2-16h-d64-16k",
             "deltanet": "deltanet-16h-d128-16k"}[family]

@@ -9,7 +9,9 @@ Two independent implementations live here:
 * ``liboracle.so`` (``hypic_oracle.c``): the plain token-by-token recurrence,
   fp64, OpenMP over independent (segment, head) / (chain, head) units;
 * :mod:`oracle.brute`: numpy brute force that forms every token transition
-  matrix explicitly and multiplies the ordered products out (tiny inputs only).
+  matrix explicitly and multiplies the ordered products out (tiny inputs only);
+* :func:`compose_gemm`: the composition with numpy's fp64 matrix product per
+  step (for request batches too large for the C loop), pinned to the C routine.
 
 Sources are cited by short key, as in ``hypic_oracle.c``: [ZH] is the Chinese
 page "首 token 延迟降 3.25 倍！…HYPIC…" (sections 2.1 linear layers, 2.2 seam
@@ -155,6 +157,48 @@ def compose(T_cache, S_cache, pair_id, S_run=None, *, t_scalar: bool = False):
          else np.array(S_run, dtype=np.float64, copy=True, order="C"))
     _load().oracle_compose(H, dk, dv, int(bool(t_scalar)), n_chain, n_step, _ptr(ids), _ptr(T_cache),
                            _ptr(S_cache), _ptr(R))
+    return R
+
+
+def compose_gemm(T_cache, S_cache, pair_id, S_run=None, *, workers: int | None = None):
+    """The composition of :func:`compose` -- S_run <- T[id] S_run + S[id] for every step of
+    every chain, in order ([ZH] 2.1: left-multiply by the cached T_C, then add S(C|0)) --
+    with each step's product taken by numpy's fp64 matrix product over all heads at once.
+    Chains are independent and run on a thread pool (one BLAS thread each).  For chain sets
+    that the token-loop C routine would take minutes over (a batch of requests composing
+    hundreds of cached segments); the tests pin it to :func:`compose`.
+
+    ``pair_id`` [n_chain, n_step] (id < 0 skips); T_cache [n_pair, H, d_k, d_k] (dense),
+    S_cache [n_pair, H, d_k, d_v]; S_run [n_chain, H, d_k, d_v] (default zeros).  Returns the
+    new S_run (a copy)."""
+    import concurrent.futures
+
+    from threadpoolctl import threadpool_limits
+
+    S_cache = _f64(S_cache)
+    T_cache = _f64(T_cache)
+    n_pair, H, dk, dv = S_cache.shape
+    assert T_cache.shape == (n_pair, H, dk, dk)
+    ids = np.ascontiguousarray(np.asarray(pair_id, dtype=np.int64))
+    n_chain, n_step = ids.shape
+    assert np.all(ids < n_pair)
+    R = (np.zeros((n_chain, H, dk, dv)) if S_run is None
+         else np.array(S_run, dtype=np.float64, copy=True, order="C"))
+
+    def chain(c):
+        r, nxt = R[c].copy(), np.empty_like(R[c])
+        for j in range(n_step):
+            i = ids[c, j]
+            if i >= 0:
+                np.matmul(T_cache[i], r, out=nxt)
+                nxt += S_cache[i]
+                r, nxt = nxt, r
+        R[c] = r
+
+    n_workers = workers or min(16, os.cpu_count() or 1)
+    with threadpool_limits(1):
+        with concurrent.futures.ThreadPoolExecutor(n_workers) as ex:
+            list(ex.map(chain, range(n_chain)))
     return R
 
 

@@ -93,3 +93,33 @@ def test_compose_scalar_T(n_step):
     hb.compose(dev(t, torch.float32), dev(S, torch.float32), dev(ids, torch.int32), Rg, t_layout=hb.T_SCALAR)
     torch.cuda.synchronize()
     assert rel_f(Rg.cpu().numpy(), ref).max() < 1e-6
+
+
+@pytest.mark.parametrize("layout", [hb.T_DENSE, hb.T_SPLIT])
+@pytest.mark.parametrize("n_chain,H", [(3, 2), (64, 16)])
+def test_compose_long_chain_ring_refill(layout, n_chain, H):
+    """Chains of 800 steps: the kernel's LDS ring of pair ids is refilled at steps 256, 512
+    and 768, and runs of skipped ids end right before those points (the waves then meet at
+    no step for a while).  Few chains run the narrow column blocks, 64 x 16 (chain, head)
+    units the full-width ones; the latter are checked on sampled chains."""
+    d, n_step, n_pair = 128, 800, 9
+    print(f"compose long chain chains={n_chain} H={H} layout={layout}", flush=True)
+    T, S = _pairs(41 + H, n_pair, H, d)
+    Tc, Tv = _t_cache(T, layout)
+    rng = np.random.default_rng(42)
+    ids = rng.integers(0, n_pair, size=(n_chain, n_step)).astype(np.int32)
+    for r in (256, 512, 768):
+        ids[:, r - 7:r] = -1
+        ids[::2, r - 1] = -1
+        ids[1::2, r - 1] = 3
+    ids[-1, 250:520] = -1
+    R0 = rng.standard_normal((n_chain, H, d, d)).astype(np.float32)
+    Rg = dev(R0, torch.float32)
+    hb.compose(Tc, dev(S, torch.float32), dev(ids, torch.int32), Rg)
+    torch.cuda.synchronize()
+    got = Rg.cpu().numpy()
+    sample = list(range(n_chain)) if n_chain <= 4 else [0, 1, 30, n_chain - 1]
+    ref = oracle.compose_gemm(Tv, S, ids[sample], R0[sample])
+    err = rel_f(got[sample], ref)
+    print(f"  max rel_F {err.max():.2e}", flush=True)
+    assert err.max() < 1e-4, err.max()

@@ -143,7 +143,8 @@ def test_kda_gate_first_ragged(d, stress):
     """KDA with the gate applied before the erase, (I - b k k^T) diag(a_t), and log-gates
     spread widely over the channels (g = -softplus(2 z)): several chunks, ragged tails, one
     token, an empty range.  Without stress the gate-after-erase states of the same tokens
-    differ from these by more than three times the tolerance, so the order is tested."""
+    differ from these (by more than three times the tolerance at the median), and the
+    GPU's states are checked to be far from them, so the order is tested."""
     W = wl.make("kda-32h-d128-131k", gate_first=True, gate_sigma=2.0, stress=stress, n_heads=2, d=d,
                 lengths=[256, 100, 33, 1], n_req=1, n_step=1, n_layers=1)
     assert W.delta == 2
@@ -157,7 +158,8 @@ def test_kda_gate_first_ragged(d, stress):
     assert np.array_equal(T[-1], np.broadcast_to(np.eye(d, dtype=np.float32), T[-1].shape)) and np.all(S[-1] == 0)
     if not stress:
         _, S1 = oracle.segment_build(W.k, W.v, W.g, W.beta, begin, end, gate=W.gate, delta=1)
-        assert rel_f(S1[:3], S0[:3]).min() > 3 * TOL["bf16"]
+        assert np.median(rel_f(S1[:3], S0[:3])) > 3 * TOL["bf16"]
+        assert rel_f(S[:3], S1[:3]).max() > 2 * TOL["bf16"]
 
 
 def test_kda_gate_first_split_compose_matches_full():

@@ -183,6 +183,37 @@ def test_skipped_steps_and_scalar_T_layout():
     assert _rel(a[0], ref) < 1e-14 and _rel(b[0], ref) < 1e-14
 
 
+def test_compose_gemm_matches_token_loop():
+    """The matrix-product composition equals the C routine's on chains with skipped and
+    repeated pairs, several heads, d_k != d_v and a nonzero starting state."""
+    H, dk, dv, n_pair = 3, 7, 5, 6
+    rng = np.random.default_rng(31)
+    T = rng.standard_normal((n_pair, H, dk, dk)) * 0.4
+    S = rng.standard_normal((n_pair, H, dk, dv))
+    ids = rng.integers(-1, n_pair, size=(4, 23))
+    R0 = rng.standard_normal((4, H, dk, dv))
+    a = oracle.compose(T, S, ids, R0)
+    b = oracle.compose_gemm(T, S, ids, R0, workers=3)
+    assert _rel(b, a).max() < 1e-13
+    assert np.array_equal(oracle.compose_gemm(T, S, np.full((2, 4), -1), R0[:2]), R0[:2])
+
+
+@pytest.mark.parametrize("gate,delta", [(wl.GATE_TOKEN, True), (wl.GATE_DIAG, True)])
+def test_compose_gemm_split_invariance(gate, delta):
+    """Pairs of a cut sequence composed by the matrix-product routine give the full
+    recurrence's state (the composition law, [ZH] 2.1), and the identity transition gives
+    the plain sum of the states."""
+    H, dk, dv, N = 2, 6, 4, 70
+    _, k, v, g, beta = _rand(33, N, H, dk, dv, gate)
+    bounds = [0, 9, 30, 31, 70]
+    T, S = oracle.segment_build(k, v, g, beta, bounds[:-1], bounds[1:], gate=gate, delta=delta)
+    full, _ = oracle.run(k, v, g, beta, gate=gate, delta=delta)
+    R = oracle.compose_gemm(T, S, [list(range(4))])
+    assert _rel(R[0], full).max() < 1e-12
+    I = np.broadcast_to(np.eye(dk), T.shape).copy()
+    assert _rel(oracle.compose_gemm(I, S, [[0, 2, 3]])[0], S[0] + S[2] + S[3]).max() < 1e-14
+
+
 # ---------------------------------------------------------------- closed forms
 def test_identity_transition_gives_plain_sum():
     """Plain linear attention (no gate, no erase): T = I exactly, S = K^T V, and the
