@@ -21,8 +21,9 @@ F32, BF16 = 0, 1
 T_DENSE, T_SCALAR, T_SPLIT, T_DIAG = 0, 1, 2, 3
 
 EXPORTED = ("hypic_segment_build", "hypic_build_workspace_bytes", "hypic_segment_prefill", "hypic_compose",
-            "hypic_seam_advance",
+            "hypic_seam_advance", "hypic_seam_advance_noalloc",
             "hypic_seam_workspace_bytes", "hypic_last_error", "hypic_abi_version", "hypic_selftest_layouts")
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class HypicError(RuntimeError):
@@ -61,6 +62,9 @@ def load_library(path: str = LIB_PATH):
     lib.hypic_seam_advance.argtypes = [D, I32, I32, I32, P, I64, P, P, P, P, P, ctypes.c_float, P, I32,
                                        P, P, P, P, P, ctypes.c_size_t, P]
     lib.hypic_seam_advance.restype = ctypes.c_int
+    lib.hypic_seam_advance_noalloc.argtypes = [D, I32, I32, I32, P, I64, P, P, P, P, P, ctypes.c_float, P, I32,
+                                               P, P, P, P, P]
+    lib.hypic_seam_advance_noalloc.restype = ctypes.c_int
     lib.hypic_seam_workspace_bytes.argtypes = [D, I32, I32, I32]
     lib.hypic_seam_workspace_bytes.restype = ctypes.c_size_t
     lib.hypic_last_error.restype = ctypes.c_char_p
@@ -275,6 +279,36 @@ def seam_advance(q, k, v, g, beta, seam_start, S_run, out, *, gate, delta, w, sc
                                   _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(pair_id), n_pair,
                                   _ptr(T_cache), _ptr(S_cache), _ptr(S_run), _ptr(out), _ptr(workspace),
                                   0 if workspace is None else workspace.numel(), _stream(stream)))
+    return S_run, out
+
+
+def seam_advance_noalloc(q, k, v, g, beta, seam_start, S_run, out, *, gate, delta, w, scale, pair_id=None,
+                         T_cache=None, S_cache=None, stream=None):
+    """hypic_seam_advance_noalloc: seam_advance with the library's static device scratch instead of
+    a workspace (nothing is allocated; calls that overlap on one device race)."""
+    lib = load_library()
+    _dev(k, "k")
+    n_tok, H, dk = k.shape
+    dv = v.shape[2]
+    dt = _in_dtype(k)
+    _dev(q, "q", k.dtype, (n_tok, H, dk))
+    _dev(v, "v", k.dtype, (n_tok, H, dv))
+    _dev(seam_start, "seam_start", torch.int64)
+    n_chain, n_step = seam_start.shape
+    _dev(S_run, "S_run", torch.float32, (n_chain, H, dk, dv))
+    _dev(out, "out", torch.float32, (n_chain, n_step, w, H, dv))
+    n_pair, t_layout = 0, T_DENSE
+    if pair_id is not None:
+        _dev(pair_id, "pair_id", torch.int32, (n_chain, n_step))
+        _dev(S_cache, "S_cache", torch.float32)
+        n_pair = S_cache.shape[0]
+        t_layout = t_layout_of(T_cache)
+        _dev(T_cache, "T_cache", _t_dtype(t_layout), _t_shape(t_layout, n_pair, H, dk))
+    d = make_dims(H, dk, dv, gate=gate, delta=delta, in_dtype=dt, t_layout=t_layout)
+    _check(lib.hypic_seam_advance_noalloc(ctypes.byref(d), n_chain, n_step, w, _ptr(seam_start), n_tok, _ptr(q),
+                                          _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(pair_id),
+                                          n_pair, _ptr(T_cache), _ptr(S_cache), _ptr(S_run), _ptr(out),
+                                          _stream(stream)))
     return S_run, out
 
 

@@ -8,6 +8,7 @@
 #include <string>
 
 #include "../../include/hypic.h"
+#include "api_internal.h"
 #include "hypic_kernels.h"
 
 namespace {
@@ -63,6 +64,11 @@ hypic_status check_dims(const hypic_dims* d)
 constexpr long long kMaxGrid = 0x7fffffffLL;
 
 }  // namespace
+
+hypic_status hypic::api_error(hypic_status st, const char* msg)
+{
+    return fail(st, "%s", msg);
+}
 
 extern "C" {
 
@@ -205,6 +211,20 @@ hypic_status hypic_seam_advance(const hypic_dims* dims, int32_t n_chain, int32_t
                                 const float* S_cache, float* S_run, float* out, void* workspace,
                                 size_t workspace_bytes, void* stream)
 {
+    return hypic::seam_advance_with(dims, n_chain, n_step, w, seam_start, n_tokens, q, k, v, g, beta, scale,
+                                    pair_id, n_pair, T_cache, S_cache, S_run, out, workspace, workspace_bytes,
+                                    stream);
+}
+
+}  // extern "C"
+
+hypic_status hypic::seam_advance_with(const hypic_dims* dims, int32_t n_chain, int32_t n_step, int32_t w,
+                                      const int64_t* seam_start, int64_t n_tokens, const void* q, const void* k,
+                                      const void* v, const void* g, const void* beta, float scale,
+                                      const int32_t* pair_id, int32_t n_pair, const void* T_cache,
+                                      const float* S_cache, float* S_run, float* out, void* workspace,
+                                      size_t workspace_bytes, void* stream)
+{
     if (hypic_status s = check_dims(dims)) return s;
     if (n_chain < 0 || n_step < 0 || n_pair < 0 || n_tokens < 0)
         return fail(HYPIC_E_INVALID, "n_chain, n_step, n_pair and n_tokens must be >= 0");
@@ -254,6 +274,8 @@ hypic_status hypic_seam_advance(const hypic_dims* dims, int32_t n_chain, int32_t
                                         out, st),
                     "hypic_seam_advance (window outputs)");
 }
+
+extern "C" {
 
 // Diagnostic: runs the lane-layout self-test kernel into a device buffer of
 // 2112 floats from 256 input floats (see selftest.hip).  Not part of the method.

@@ -34,7 +34,9 @@
  *
  * Conventions for every entry point
  *   - All array arguments are DEVICE pointers owned by the caller; nothing is
- *     copied, retained or freed.  The library allocates no device memory.
+ *     copied, retained or freed.  The library allocates no device memory (its one
+ *     static device array, used only by hypic_seam_advance_noalloc, is described
+ *     there).
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream) and returns once the kernels are enqueued.
  *   - Argument errors return HYPIC_E_INVALID before anything is launched;
@@ -224,6 +226,30 @@ hypic_status hypic_seam_advance(const hypic_dims* dims, int32_t n_chain, int32_t
 /* Bytes of device workspace hypic_seam_advance needs (0 on invalid dims). */
 size_t hypic_seam_workspace_bytes(const hypic_dims* dims, int32_t n_chain, int32_t n_step,
                                   int32_t w);
+
+/*
+ * hypic_seam_advance_noalloc -- for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation, arguments and results as hypic_seam_advance, with the workspace taken from a
+ * static device array of the library instead of the caller.
+ *   - The array holds HYPIC_NOALLOC_SCRATCH_BYTES (128 MiB) on every device the library
+ *     runs on, from its first use there until the process ends; a call whose
+ *     hypic_seam_workspace_bytes exceeds that returns HYPIC_E_INVALID before any launch
+ *     (e.g. 1 chain x 128 steps x 16 heads at d = 128 needs 107.5 MiB).
+ *   - The device is the stream's (the current device for the NULL stream).  The call
+ *     allocates nothing: no hipMalloc, hipFree or allocating library routine.
+ *   - Every call on one device uses that device's one array, so calls that overlap on a
+ *     device (other streams, other threads) race; serialise them.  The array keeps the last
+ *     call's contents; nothing in it needs to start cleared.
+ */
+#define HYPIC_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+hypic_status hypic_seam_advance_noalloc(const hypic_dims* dims, int32_t n_chain, int32_t n_step,
+                                        int32_t w, const int64_t* seam_start, int64_t n_tokens,
+                                        const void* q, const void* k, const void* v,
+                                        const void* g, const void* beta, float scale,
+                                        const int32_t* pair_id, int32_t n_pair,
+                                        const void* T_cache, const float* S_cache,
+                                        float* S_run, float* out, void* stream);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* hypic_last_error(void);
