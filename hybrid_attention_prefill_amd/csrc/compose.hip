@@ -25,6 +25,10 @@ namespace hypic {
 // operation and every LDS access: vmcnt = 0, expcnt = 7 (unconstrained), lgkmcnt = 0.
 constexpr unsigned kWaitVmcnt0 = 0x0070;
 constexpr int kRing = 512, kRingFill = 256;   // LDS ring of per-step pair ids
+// column blocks of the full-width composition (4 x this waves per workgroup; one column
+// block, 4 waves, measured 28% slower at the 64-request reuse plan: one wave per SIMD
+// leaves the loads and LDS reads of a step exposed)
+constexpr int kWideCB = 2;
 
 // waves per workgroup: one 16-row tile of the state per wave at d_k = 128
 constexpr int chain_waves(int dk) { return dk >= 128 ? 8 : 4; }
@@ -292,6 +296,228 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void compose_dense_kernel(
     }
 }
 
+// Full width at d_k = d_v = 128 (many chains: one workgroup per (chain, head) holding all
+// 128 state columns).  The 8 waves split the state 4 x 2: wave w owns rows 32 (w >> 1) ..
+// +31 and columns 64 (w & 1) .. +63, a 2 x 4 block of 16 x 16 accumulator tiles, so per
+// step a wave reads 2 A fragments of T per k-block (from global memory, SPLIT planes as is
+// or fp32 split in registers) and 4 B fragments of the running state's planes from LDS:
+// 256 KiB of LDS operand reads per step instead of the 512 KiB of one 16-row tile per wave
+// with all columns.  The pair ids go through an LDS ring that holds the valid ids only
+// (compacted as each block of 256 steps is read), so every iteration is a real step and
+// the next step's T and S are always loaded: T_{j+1} k-block by k-block into the registers
+// that step j's products of that k-block have just read, S_{j+1} once step j's first
+// products have read S_j as their accumulator input.  Nothing is loaded conditionally, so
+// the register sets are never merged or copied.
+template <bool TS, int CB>
+__global__ __launch_bounds__(256 * CB) void compose_wide_kernel(
+    int n_units, int H, int n_step, const int32_t* __restrict__ pair_id, int n_pair,
+    const void* __restrict__ Tc, const float* __restrict__ Sc, float* __restrict__ Srun)
+{
+    // planes [column][row] with a row stride of 66 dwords: the B-fragment reads (16 bytes,
+    // 8-byte aligned on odd columns) and the 8-byte split stores are both free of bank
+    // conflicts at this stride (measured; 68 and 64 dwords conflict on both)
+    constexpr int D = 128, LDB = D + 4, KS = D / 32;
+    constexpr int CT = 8 / CB;   // column tiles per wave
+    __shared__ __attribute__((aligned(16))) uint16_t Rh[2][D][LDB];   // R, bf16 hi, [column][row]
+    __shared__ __attribute__((aligned(16))) uint16_t Rl[2][D][LDB];   // R, bf16 lo
+    __shared__ int ring_id[kRing];                                     // valid pair ids, in step order
+    __shared__ int wave_cnt[8];
+
+    // Units in head-major order (u = h n_chain + c), each XCD a contiguous eighth of them:
+    // the workgroups an XCD runs at one time are consecutive chains of one head, and chains
+    // of one layer are consecutive, so they all read the pairs of one (layer, head) -- 64
+    // pairs x 128 KiB for the 64-segment cache, about twice that XCD's L2 -- instead of
+    // several heads' pairs each.
+    const int per_xcd = (n_units + 7) / 8;
+    const int li = blockIdx.x >> 3;
+    const int u = (blockIdx.x & 7) * per_xcd + li;
+    if (li >= per_xcd || u >= n_units) return;
+    const int n_chain = n_units / H;
+    const int h = u / n_chain, c = u % n_chain;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g4 = lane >> 4, n16 = lane & 15;
+    const int rt0 = 2 * (wave / CB), ct0 = CT * (wave % CB);   // first row / column tile of the block
+
+    float* Rg = Srun + ((size_t)c * H + h) * D * D;
+    f32x4 acc[2][CT];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                acc[i][ct][e] = Rg[(size_t)((rt0 + i) * 16 + 4 * g4 + e) * D + (ct0 + ct) * 16 + n16];
+
+    auto store_split = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                unsigned h0, h1, l0, l1;
+                pack_bf16_split(acc[i][ct], h0, h1, l0, l1);
+                const int col = (ct0 + ct) * 16 + n16, row = (rt0 + i) * 16 + 4 * g4;
+                *reinterpret_cast<u32x2*>(&Rh[buf][col][row]) = u32x2{h0, h1};
+                *reinterpret_cast<u32x2*>(&Rl[buf][col][row]) = u32x2{l0, l1};
+            }
+    };
+    store_split(0);
+
+    // ---- the ring: steps are read 256 at a time; the valid ids of a block are appended at
+    // wpos (ballot + popcount prefix within each wave, wave totals through LDS).  Positions
+    // are uniform counters; the loop consumes at rpos and refills before it runs dry.
+    const int32_t* ids = pair_id ? pair_id + (size_t)c * n_step : nullptr;
+    int wpos = 0, rpos = 0, next_raw = 0;
+    auto fill_block = [&]() {
+        int id = -1;
+        if (threadIdx.x < kRingFill) {
+            const int j = next_raw + threadIdx.x;
+            if (j < n_step) {
+                const int x = ids ? ids[j] : c * n_step + j;
+                id = (unsigned)x < (unsigned)n_pair ? x : -1;
+            }
+        }
+        const unsigned long long m = __ballot(id >= 0);
+        const int pre = __popcll(m & ((1ull << lane) - 1ull));
+        if (lane == 0) wave_cnt[wave] = __popcll(m);
+        lds_barrier();
+        int base = wpos, tot = 0;
+#pragma unroll
+        for (int w = 0; w < kRingFill / 64; ++w) {
+            const int n = wave_cnt[w];
+            base += w < wave ? n : 0;
+            tot += n;
+        }
+        if (id >= 0) ring_id[(base + pre) & (kRing - 1)] = id;
+        lds_barrier();   // the ring entries are visible; wave_cnt is read before the next block
+        wpos += __builtin_amdgcn_readfirstlane(tot);
+        next_raw += kRingFill;
+    };
+    // at least the current step and the one after it in the ring (or every step read)
+    auto ensure = [&]() {
+        while (wpos < rpos + 2 && next_raw < n_step) fill_block();
+    };
+    auto ring = [&](int pos) -> int { return __builtin_amdgcn_readfirstlane(ring_id[pos & (kRing - 1)]); };
+
+    // registers of one step: this wave's A fragments of T and its block of S
+    u32x4 th[2][KS], tl[2][KS];   // SPLIT: bf16 hi / lo planes as loaded
+    float ta[TS ? 1 : 2][TS ? 1 : KS][8];
+    float sv[2][CT][4];
+    auto load_t = [&](int id, int ks) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int row = (rt0 + i) * 16 + n16, k0 = ks * 32 + 8 * g4;
+            if constexpr (TS) {   // fragment-ordered planes: 1 KiB contiguous per fragment
+                const uint16_t* T = reinterpret_cast<const uint16_t*>(Tc) + ((size_t)id * H + h) * 2 * D * D;
+                const int e = frag_off(row, k0, D);
+                th[i][ks] = *reinterpret_cast<const u32x4*>(T + e);
+                tl[i][ks] = *reinterpret_cast<const u32x4*>(T + D * D + e);
+            } else {
+                const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(Tc) +
+                                                                 ((size_t)id * H + h) * D * D + (size_t)row * D + k0);
+                const f32x4 a = p[0], b = p[1];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    ta[i][ks][x] = a[x];
+                    ta[i][ks][4 + x] = b[x];
+                }
+            }
+        }
+    };
+    auto load_s = [&](int id) {
+        const float* S = Sc + ((size_t)id * H + h) * D * D;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sv[i][ct][e] = S[(size_t)((rt0 + i) * 16 + 4 * g4 + e) * D + (ct0 + ct) * 16 + n16];
+    };
+    auto a_frags = [&](int i, int ks, bf16x8& ah, bf16x8& al) {
+        if constexpr (TS) {
+            ah = as_frag<bf16x8>(th[i][ks]);
+            al = as_frag<bf16x8>(tl[i][ks]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                __bf16 x, y;
+                split_bf16(ta[i][ks][e], x, y);
+                ah[e] = x;
+                al[e] = y;
+            }
+        }
+    };
+
+    ensure();
+    if (wpos > 0) {
+        const int id0 = ring(0);
+        load_s(id0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) load_t(id0, ks);
+    }
+    int cur = 0;
+    while (rpos < wpos) {
+        // R <- T R + S on the planes `cur`: hi*hi + hi*lo + lo*hi into the accumulators, which
+        // start from S; the next step's id is in the ring (or there is none: then this step's
+        // own pair is fetched again, unused).  Per k-block the three products go out product by
+        // product over the 8 tiles, so consecutive products feed different accumulators (a
+        // dependent product waits for the previous one's result); the next k-block's B
+        // fragments are read from LDS before this block's products.
+        const int idn = rpos + 1 < wpos ? ring(rpos + 1) : ring(rpos);
+        bf16x8 bh[2][CT], bl[2][CT];
+        auto read_b = [&](int ks, int slot) {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                const int col = (ct0 + ct) * 16 + n16, k0 = ks * 32 + 8 * g4;
+                bh[slot][ct] = *reinterpret_cast<const bf16x8*>(&Rh[cur][col][k0]);
+                bl[slot][ct] = *reinterpret_cast<const bf16x8*>(&Rl[cur][col][k0]);
+            }
+        };
+        read_b(0, 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int sl = ks & 1;
+            if (ks + 1 < KS) read_b(ks + 1, sl ^ 1);
+            bf16x8 ah[2], al[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) a_frags(i, ks, ah[i], al[i]);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const f32x4 a0 = ks == 0 ? f32x4{sv[i][ct][0], sv[i][ct][1], sv[i][ct][2], sv[i][ct][3]} : acc[i][ct];
+                    acc[i][ct] = mma_bf16(ah[i], bh[sl][ct], a0);
+                }
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int i = 0; i < 2; ++i) acc[i][ct] = mma_bf16(ah[i], bl[sl][ct], acc[i][ct]);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int i = 0; i < 2; ++i) acc[i][ct] = mma_bf16(al[i], bh[sl][ct], acc[i][ct]);
+            if (ks == 0) load_s(idn);
+            load_t(idn, ks);
+            // keep the k-blocks in order (the scheduler would otherwise hoist every block's
+            // LDS reads to the top of the step and run out of registers)
+            if (ks + 1 < KS) __builtin_amdgcn_sched_barrier(0);
+        }
+        store_split(cur ^ 1);
+        lds_barrier();
+        cur ^= 1;
+        ++rpos;
+        ensure();
+    }
+
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                Rg[(size_t)((rt0 + i) * 16 + 4 * g4 + e) * D + (ct0 + ct) * 16 + n16] = acc[i][ct][e];
+}
+
 // Scalar or diagonal T (gates without the delta rule cache T_C = t I as one number per
 // (pair, head), or T_C = diag(t) for the per-channel gate): S_run <- T S_run + S is
 // elementwise, S_run[r][c] <- t_r S_run[r][c] + S[r][c]; 4 consecutive state entries
@@ -363,6 +589,17 @@ hipError_t compose_dense(int d, int n_chain, int H, int n_step, const int32_t* p
                          hipStream_t st)
 {
     const int nb = pick_nb((long long)n_chain * H, d);
+    if (d == 128 && nb == 128 && trail == nullptr) {
+        const int n_units = n_chain * H;
+        const int grid = (n_units + 7) / 8 * 8;
+        if (t_split)
+            hipLaunchKernelGGL((compose_wide_kernel<true, kWideCB>), dim3(grid), dim3(256 * kWideCB), 0, st, n_units,
+                               H, n_step, pair_id, n_pair, Tc, Sc, Srun);
+        else
+            hipLaunchKernelGGL((compose_wide_kernel<false, kWideCB>), dim3(grid), dim3(256 * kWideCB), 0, st,
+                               n_units, H, n_step, pair_id, n_pair, Tc, Sc, Srun);
+        return hipGetLastError();
+    }
 #define HYPIC_CASE(D_, NB_)                                                                                   \
     if (d == D_ && nb == NB_)                                                                                 \
         return t_split                                                                                        \
