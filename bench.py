@@ -128,8 +128,9 @@ class Timer:
 
 
 def roofline(flops, bytes_, t, traffic=None):
-    """t_roof = max(F / P, B / BW) with B the measured HBM bytes when given, else the
-    algorithmic bytes; the binding roof, its achieved rate and the fractions of both roofs."""
+    """t_roof = max(F / P, B / BW), B the measured HBM bytes when given (L2 <-> fabric
+    traffic from FETCH_SIZE + WRITE_SIZE), else the algorithmic bytes; the binding roof, the
+    rate achieved against it (with that same B) and the fractions of both roofs."""
     b = traffic if traffic is not None else bytes_
     t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
     t_hbm = b / (HBM_PEAK_GBS * 1e9)
@@ -137,7 +138,8 @@ def roofline(flops, bytes_, t, traffic=None):
         r = {"bound": "mfma", "achieved": round(flops / t / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
              "unit": "TFLOP/s"}
     else:
-        r = {"bound": "hbm", "achieved": round(bytes_ / t / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+        r = {"bound": "hbm", "achieved": round(b / t / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "bytes": "measured" if traffic is not None else "algorithmic"}
     r["frac"] = round(max(t_mfma, t_hbm) / t, 4)
     r["mfma_frac"] = round(t_mfma / t, 4)
     r["hbm_frac"] = round(t_hbm / t, 4)
@@ -436,6 +438,8 @@ CALL_SOURCES = {
     "compose": ["compose.hip", "hypic_device.h", "hypic_kernels.h"],
     "segment_build": ["build_gdn.hip", "build_split.hip", "build_kda.hip", "build_decay.hip", "build_common.h",
                       "hypic_device.h", "hypic_kernels.h"],
+    "prefill_with_T": ["build_gdn.hip", "build_common.h", "hypic_device.h", "hypic_kernels.h"],
+    "prefill_S_only": ["build_gdn.hip", "build_common.h", "hypic_device.h", "hypic_kernels.h"],
 }
 
 
