@@ -60,6 +60,7 @@ struct alignas(16) KdaSmem {
     uint16_t Kb[CK][D + 8];        // K (bf16 bits), token-major
     float Ag[CK + 1][D + 4];       // exclusive cumulative log-gate per channel; row t+1 inclusive, row CK = b_C
     float beta[CK];
+    float eBC[D];                  // e^{b_C} per channel (the chunk's decay of the state rows)
     float F1[CK][LDF];             // Lp (strictly lower, beta folded)
     float F1p[CK][LDF];            // L'
     uint16_t RmT[2][D][LDT];       // (e^{a} o K)^T, bf16 hi / lo
@@ -84,7 +85,7 @@ struct alignas(16) KdaSmem {
             uint16_t GR1[2][CK][D + 8];    // k_s e^{rho - i_s}            (L'; the gate-first order reuses GR)
         } g;
     } u;
-    float red[8];
+    float red2[2][8];              // per wave: max |T| after a chunk's update (by chunk parity)
 };
 
 __device__ __forceinline__ float bf(uint16_t b) { return bf16_bits_to_f32(b); }
@@ -142,6 +143,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
     const size_t tok_stride = (size_t)H * D;
     for (int64_t c0 = beg; c0 < end; c0 += CK) {
         const int n = (int)((end - c0) < CK ? (end - c0) : CK);
+        const int par = (int)(((c0 - beg) / CK) & 1);   // chunk parity (renormalisation records)
         // ---- 1. stage K (bf16), V (registers), beta, gates; per-channel cumsum
         float vx[8];
         int vt = -1, vcg = 0;
@@ -193,6 +195,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
 #pragma unroll
                 for (int i = 0; i < 8; ++i) sm.Ag[8 * q + i + 1][c] = x[i] + pre;
                 if (q == 0) sm.Ag[0][c] = 0.f;
+                if (q == 3) sm.eBC[c] = __expf(x[7] + pre);
             }
         }
         if (vt >= 0) {   // (diag(b) V)^T, fp16
@@ -201,6 +204,37 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
             for (int e = 0; e < 8; ++e) sm.bVT[vcg * 8 + e][vt] = f16_bits((_Float16)(bt * vx[e]));
         }
         __syncthreads();
+
+        // ---- 2a. renormalise the T columns by a power of two when they have become small: the
+        // largest |T| each wave posted after the previous chunk's update (read here, past this
+        // chunk's first two barriers); once every T entry is below 2^-120 the T columns are dropped.  One
+        // chunk of delay is safe: a chunk decays T by at most e^{-32 max|g|}, far inside fp32.
+        if (c0 != beg) {
+            float mm = 0.f;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) mm = fmaxf(mm, sm.red2[par ^ 1][w]);
+            int em = 0;
+            if (mm > 0.f) frexpf(mm, &em);
+            if (t_live && (mm == 0.f || log2s + em < -120)) {  // T is below the floor for good
+                t_live = false;
+#pragma unroll
+                for (int c = 0; c < CTW; ++c)
+                    if (wave + 8 * c < RT)
+#pragma unroll
+                        for (int rt = 0; rt < RT; ++rt) X[rt][c] = zero4();
+            } else if (mm < 0x1p-16f) {
+                const float sc = ldexpf(1.f, -em);
+#pragma unroll
+                for (int c = 0; c < CTW; ++c) {
+                    if (wave + 8 * c < RT) {
+#pragma unroll
+                        for (int rt = 0; rt < RT; ++rt) X[rt][c] *= sc;
+                    }
+                }
+                log2s += em;
+            }
+        }
+
 
         // ---- 2. decay-weighted Gram matrices Lp (waves 0-2) and L' (waves 3-5), bf16 hi+lo.
         // Their operands are formed once per chunk by all waves (one token, 8 channels per item):
@@ -395,9 +429,10 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                 const FragB rb = dpair_to_fragb(R[0], R[1]);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
+                    const f32x4 eb = *reinterpret_cast<const f32x4*>(&sm.eBC[rt * 16 + 4 * g4]);
                     f32x4 acc;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[e] = X[rt][c][e] * __expf(sm.Ag[CK][rt * 16 + 4 * g4 + e]);
+                    for (int e = 0; e < 4; ++e) acc[e] = X[rt][c][e] * eb[e];
                     X[rt][c] = mma3(fragb_at(&sm.KhTb[0][0][0], &sm.KhTb[1][0][0], LDT, rt * 16 + n16, 8 * g4), rb, acc);
                 }
                 continue;
@@ -430,9 +465,10 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
             if (is_s) vb = f16frag(&sm.bVT[0][0], LDT, vt16 * 16 + n16, 8 * g4);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
+                const f32x4 eb = *reinterpret_cast<const f32x4*>(&sm.eBC[rt * 16 + 4 * g4]);
                 f32x4 acc;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] = X[rt][c][e] * __expf(sm.Ag[CK][rt * 16 + 4 * g4 + e]);
+                for (int e = 0; e < 4; ++e) acc[e] = X[rt][c][e] * eb[e];
                 const Frag<1> a = f16frag(&sm.KhT[0][0], LDT, rt * 16 + n16, 8 * g4);
                 acc = mma<1>(a, rb, acc);
                 if (is_s) {
@@ -442,7 +478,9 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                 X[rt][c] = acc;
             }
         }
-        // ---- 6. renormalise the T columns by a power of two when they get small
+        // ---- 6. post this wave's largest |T| for the next chunk's renormalisation (no barrier:
+        // the next chunk's staging writes nothing this update reads, and its barriers come
+        // before the read)
         float m = 0.f;
 #pragma unroll
         for (int c = 0; c < CTW; ++c) {
@@ -456,33 +494,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
         }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-        if (lane == 0) sm.red[wave] = m;
-        __syncthreads();
-        float mm = 0.f;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) mm = fmaxf(mm, sm.red[w]);
-        int em = 0;
-        if (mm > 0.f) frexpf(mm, &em);
-        if (t_live && (mm == 0.f || log2s + em < -120)) {  // T is below the floor for good
-            t_live = false;
-#pragma unroll
-            for (int c = 0; c < CTW; ++c)
-                if (wave + 8 * c < RT)
-#pragma unroll
-                    for (int rt = 0; rt < RT; ++rt) X[rt][c] = zero4();
-        } else if (mm < 0x1p-16f) {
-            const int e = em;
-            const float sc = ldexpf(1.f, -e);
-#pragma unroll
-            for (int c = 0; c < CTW; ++c) {
-                if (wave + 8 * c < RT) {
-#pragma unroll
-                    for (int rt = 0; rt < RT; ++rt) X[rt][c] *= sc;
-                }
-            }
-            log2s += e;
-        }
-        __syncthreads();
+        if (lane == 0) sm.red2[par][wave] = m;
     }
 
     const size_t pair = (size_t)seg * H + h;
