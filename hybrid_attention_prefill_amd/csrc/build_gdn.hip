@@ -347,8 +347,10 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
 #pragma unroll
             for (int c = 0; c < 8; ++c) f[r][c] = raw_val(r, c);
     };
-    // bf16 values are exact in fp16 (inside its range): round-toward-zero packing is exact
-    auto pk = [](float a, float b) -> unsigned { return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a, b)); };
+    // bf16 values are exact in fp16 inside its range; round-to-nearest packing (one
+    // instruction on this chip) turns a value beyond it into an infinity, not the largest
+    // finite fp16 that round-toward-zero would give, so the overflow shows in the results
+    auto pk = [](float a, float b) -> unsigned { return cvt2_f16(a, b); };
     // bf16 inputs: the transposed words are packed in part (a), with the rows, and written
     // in part (b) (they take the prefetch registers' place in between)
     u32x2 tw[8];
@@ -1022,9 +1024,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
             const int qbuf = (int)(((c0 - beg) / CH) & 1);
             if constexpr (OUT) {
                 if (has_blk && blk_v) {   // q block (tb, cb) to the fp16 plane Qr; rows past the segment zeroed
-                    auto pk = [](float a, float b) -> unsigned {
-                        return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a, b));
-                    };
+                    auto pk = [](float a, float b) -> unsigned { return cvt2_f16(a, b); };
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int t = tb * 4 + r;

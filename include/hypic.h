@@ -134,7 +134,13 @@ typedef struct {
  *   gate TOKEN, delta 1 or 2    : d = 16 (fp32 or bf16), 64 or 128 (bf16);
  *   gate DIAG,  delta 1 or 2    : d = 64 or 128, bf16 inputs.
  * Other combinations return HYPIC_E_UNSUPPORTED.  For the delta-rule kernels
- * the state and values must stay within fp16 range (|entries| < 6e4).
+ * the state and values must stay within fp16 range (|entries| < 6e4): they are
+ * fp16 operands of the matrix products (v itself with the scalar gate, beta * v
+ * with the per-channel gate).  This is not checked (the call is asynchronous); an
+ * operand beyond it is rounded to an infinity, never clamped to a finite value, so
+ * the S of its (segment, head) comes out non-finite while T and the other
+ * (segment, head) pairs are unaffected: S is either non-finite or accurate.  A
+ * caller that cannot bound its values tests S for finite entries.
  */
 hypic_status hypic_segment_build(const hypic_dims* dims, int32_t n_seg,
                                  const int64_t* seg_begin, const int64_t* seg_end,

@@ -340,3 +340,41 @@ def test_deltanet_d16_fp32_T():
     T0, S0 = _oracle_build(W)
     eS, eT = assert_pairs_close(T, S, T0, S0, TOL["f32"], W.name)
     print(f"  S {eS:.2e} T {eT:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("mag", [1e5, 1e6])
+@pytest.mark.parametrize("name,kw,bad", [
+    ("gdn-16h-d128-32k", dict(n_heads=2, lengths=[300, 200]), 10),
+    ("gdn-16h-d128-32k", dict(n_heads=2, lengths=[1500, 200]), 1200),   # in a cut segment's second piece
+    ("kda-32h-d128-131k", dict(n_heads=2, lengths=[300, 200], n_req=1, n_step=1, n_layers=1), 10),
+])
+def test_values_beyond_fp16_range_give_non_finite_S(name, kw, bad, mag):
+    """The delta-rule builds take values (GDN: v; KDA: beta * v) and states as fp16 MFMA
+    operands.  An operand past fp16's range is not clamped to the largest finite fp16: it
+    becomes an infinity and the S of its (segment, head) comes out non-finite, a visible
+    failure rather than a wrong finite state.  So S is either non-finite or within the
+    tolerance of the oracle, and at beta * |v| well past the range (here 1e6 with beta >
+    0.38) it is non-finite.  T (which does not depend on v) and every other (segment, head)
+    are bit for bit those of the same call without the large value."""
+    W = wl.make(name, **kw)
+    print(W.name, W.cache_end - W.cache_begin, "bad token", bad, "magnitude", mag, flush=True)
+    x = workload_tensors(W)
+    sb, se = dev(W.cache_begin, torch.int64), dev(W.cache_end, torch.int64)
+    T0, S0 = hb.segment_build(x["k"], x["v"], x["g"], x["beta"], sb, se, gate=W.gate, delta=W.delta)
+    v = x["v"].clone()
+    v[bad, 0, :] = mag
+    T1, S1 = hb.segment_build(x["k"], v, x["g"], x["beta"], sb, se, gate=W.gate, delta=W.delta)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(S0).all())
+    assert torch.equal(T1, T0)
+    assert torch.equal(S1[0, 1], S0[0, 1]) and torch.equal(S1[1], S0[1])
+    finite = bool(torch.isfinite(S1[0, 0]).all())
+    print("S finite:", finite, flush=True)
+    if mag * W.beta[bad, 0] > 3e5:
+        assert not finite
+    if finite:
+        b, e = W.cache_begin[0], W.cache_end[0]
+        vb = v[b:e, 0:1].float().cpu().numpy()
+        _, Sr = oracle.segment_build(W.k[b:e, 0:1], vb, W.g[b:e, 0:1], W.beta[b:e, 0:1], [0], [e - b],
+                                     gate=W.gate, delta=True)
+        assert rel_f(S1[0:1, 0:1].cpu().numpy(), Sr).max() <= TOL["bf16"]
