@@ -51,19 +51,30 @@ struct IntConst {
 };
 using namespace bld;
 
+constexpr float kLog2e = 1.4426950408889634f;
+// 2^x on the transcendental unit (v_exp_f32): log-gates are carried in log2 units, so each
+// decay factor is one instruction
+__device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 constexpr int CK = 32;        // chunk length
 constexpr int LDT = CK + 8;   // token-indexed 16-bit rows
 constexpr int LDF = CK + 1;   // fp32 32x32 matrices
 
 template <int D>
 struct alignas(16) KdaSmem {
-    uint16_t Kb[CK][D + 8];        // K (bf16 bits), token-major
-    float Ag[CK + 1][D + 4];       // exclusive cumulative log-gate per channel; row t+1 inclusive, row CK = b_C
+    uint16_t Kb[CK][D];            // K (bf16 bits), token-major, loaded global -> LDS directly
+    float Ag[CK + 1][D + 4];       // exclusive cumulative log2-gate per channel; row t+1 inclusive, row CK = b_C
     float beta[CK];
     float eBC[D];                  // e^{b_C} per channel (the chunk's decay of the state rows)
     float F1[CK][LDF];             // Lp (strictly lower, beta folded)
     float F1p[CK][LDF];            // L'
-    uint16_t RmT[2][D][LDT];       // (e^{a} o K)^T, bf16 hi / lo
+    union {
+        uint16_t RmT[2][D][LDT];   // (e^{a} o K)^T, bf16 hi / lo
+        struct {                   // the next chunk's v and log-gates (bf16 bits), loaded global -> LDS
+            uint16_t Vr[CK * D];   // directly, 8 channels of one token per staging item, item-major
+            uint16_t Gr[CK * D];
+        } nx;
+    } rv;
     uint16_t KhTb[2][D][LDT];      // Kh^T, bf16 hi / lo (T columns)
     uint16_t KhT[D][LDT];          // Kh^T
     uint16_t KhpT[D][LDT];         // Kh'^T
@@ -141,69 +152,101 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
     bool t_live = true;  // false once every T entry is below 2^-120
 
     const size_t tok_stride = (size_t)H * D;
+    // A chunk's k, log-gates and v are loaded global -> LDS directly, one chunk ahead (16 bytes
+    // per lane, so one wave's load fills 1 KiB), while the previous chunk's state is updated:
+    // K into Kb, v and the log-gates over RmT (both read last before the update).  v and the
+    // log-gates go item-major: staging item i (channel group i / CK, token i % CK) is thread i,
+    // whose own wave loaded it, so no barrier is needed before it reads them.  Rows past the
+    // segment are read clamped to its last token (finite values) and masked where they are
+    // consumed: their log-gates count as zero and their betas are zero, which takes them out
+    // of every product.
+    constexpr int NPC = CK * D * 2 / 1024;   // 1-KiB pieces of a chunk's [CK][D] bf16 plane
+    static_assert(NPC <= 8 && CK * (D / 8) <= 512, "one piece per wave, one staging item per thread");
+    static_assert(sizeof(sm.rv.nx) <= sizeof(sm.rv.RmT), "v and log-gates fit over RmT");
+    auto tok_off = [&](int64_t c0n, int t) -> size_t {
+        const int64_t tt = c0n + t < end ? c0n + t : end - 1;
+        return (size_t)tt * tok_stride + (size_t)h * D;
+    };
+    uint16_t braw = 0;   // beta of token (tid mod CK) of the chunk being fetched
+    auto fetch = [&](int64_t c0n) {
+        if (wave < NPC) {
+            const int e = wave * 512 + lane * 8;   // K: element e of the token-major plane
+            // (the addresses are locals: as calls inside the builtin's arguments they stop the
+            // host pass from emitting the kernel's launch stub)
+            const uint16_t* pk = k + tok_off(c0n, e / D) + e % D;
+            __builtin_amdgcn_global_load_lds(pk, (__attribute__((address_space(3))) void*)(&sm.Kb[0][0] + wave * 512), 16, 0, 0);
+            const int i = wave * 64 + lane;        // v, log-gates: staging item i
+            const size_t oi = tok_off(c0n, i % CK) + (i / CK) * 8;
+            const uint16_t* pv = v + oi;
+            const uint16_t* pg = gl + oi;
+            __builtin_amdgcn_global_load_lds(pv, (__attribute__((address_space(3))) void*)(sm.rv.nx.Vr + wave * 512), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(pg, (__attribute__((address_space(3))) void*)(sm.rv.nx.Gr + wave * 512), 16, 0, 0);
+        }
+        const int64_t tt = c0n + (tid & (CK - 1)) < end ? c0n + (tid & (CK - 1)) : end - 1;
+        braw = beta[(size_t)tt * H + h];
+    };
+    if (beg < end) fetch(beg);
     for (int64_t c0 = beg; c0 < end; c0 += CK) {
         const int n = (int)((end - c0) < CK ? (end - c0) : CK);
         const int par = (int)(((c0 - beg) / CK) & 1);   // chunk parity (renormalisation records)
-        // ---- 1. stage K (bf16), V (registers), beta, gates; per-channel cumsum
+        // ---- 1. staging: thread = item (channel group vcg, token vt): v, log-gates and beta to
+        // registers; the inclusive cumulative log2-gate of its 8 channels over the chunk by a
+        // 32-lane scan (the item's token is its lane within the half-wave), written to Ag with
+        // (diag(b) V)^T and the betas
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0): this wave's direct loads have landed
+        asm volatile("" ::: "memory");
         float vx[8];
         int vt = -1, vcg = 0;
-        for (int it = tid; it < CK * (D / 8); it += 512) {
-            const int cg = it / CK, t = it % CK;   // token fastest: the transposed stores below are contiguous
-            u32x4 kw = u32x4{0, 0, 0, 0}, vw = u32x4{0, 0, 0, 0}, gw = u32x4{0, 0, 0, 0};
-            if (t < n) {
-                const size_t e = (size_t)(c0 + t) * tok_stride + (size_t)h * D + cg * 8;
-                kw = *reinterpret_cast<const u32x4*>(k + e);
-                vw = *reinterpret_cast<const u32x4*>(v + e);
-                gw = *reinterpret_cast<const u32x4*>(gl + e);
-            }
-            *reinterpret_cast<u32x4*>(&sm.Kb[t][cg * 8]) = kw;
+        if (tid < CK * (D / 8)) {
+            vt = tid % CK;
+            vcg = tid / CK;
+            const bool live = vt < n;
+            const u32x4 vw = *reinterpret_cast<const u32x4*>(&sm.rv.nx.Vr[tid * 8]);
+            const u32x4 gw = *reinterpret_cast<const u32x4*>(&sm.rv.nx.Gr[tid * 8]);
+            const float bt = live ? bf(braw) : 0.f;
+            float x[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                sm.Ag[t + 1][cg * 8 + 2 * e] = __uint_as_float(gw[e] << 16);       // g_t, scanned below
-                sm.Ag[t + 1][cg * 8 + 2 * e + 1] = __uint_as_float(gw[e] & 0xFFFF0000u);
-                vx[2 * e] = __uint_as_float(vw[e] << 16);
-                vx[2 * e + 1] = __uint_as_float(vw[e] & 0xFFFF0000u);
+                vx[2 * e] = bt * __uint_as_float(vw[e] << 16);
+                vx[2 * e + 1] = bt * __uint_as_float(vw[e] & 0xFFFF0000u);
+                x[2 * e] = live ? __uint_as_float(gw[e] << 16) * kLog2e : 0.f;
+                x[2 * e + 1] = live ? __uint_as_float(gw[e] & 0xFFFF0000u) * kLog2e : 0.f;
             }
-            vt = t;
-            vcg = cg;
-        }
-        if (tid < CK) sm.beta[tid] = tid < n ? bf(beta[(size_t)(c0 + tid) * H + h]) : 0.f;
-        __syncthreads();
-        {   // exclusive cumulative log-gate per channel, in place: thread (channel c, quarter q)
-            // scans tokens 8q .. 8q+7, then adds the totals of the quarters before it (the four
-            // quarters of a channel are four consecutive lanes)
-            static_assert(4 * D <= 512 && CK == 32, "4 threads per channel");
-            const int c = tid >> 2, q = tid & 3;
-            float x[8], run = 0.f;
-            if (c < D) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    run += sm.Ag[8 * q + i + 1][c];
-                    x[i] = run;
-                }
-            }
-            // sum of the quarters before q: the quad's lanes 0, 1, 2 broadcast by DPP quad_perm
-            auto quad_bcast = [](float v, auto ctrl) {
-                return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v),
-                                                                          decltype(ctrl)::value, 0xf, 0xf, false));
+            // inclusive scan over the 32 lanes of each half-wave: within rows of 16 lanes by
+            // row shifts (lanes shifted in from outside the row read 0), then row 1 (3) adds the
+            // total of row 0 (2) by row_bcast:15
+            auto dpp_add = [](float a, auto ctrl, auto rmask) {
+                return a + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a),
+                                                       decltype(ctrl)::value, decltype(rmask)::value, 0xf, true));
             };
-            const float r0 = quad_bcast(run, IntConst<0x00>{});   // quad_perm:[0,0,0,0]
-            const float r1 = quad_bcast(run, IntConst<0x55>{});   // quad_perm:[1,1,1,1]
-            const float r2 = quad_bcast(run, IntConst<0xAA>{});   // quad_perm:[2,2,2,2]
-            const float pre = (q >= 1 ? r0 : 0.f) + (q >= 2 ? r1 : 0.f) + (q >= 3 ? r2 : 0.f);
-            if (c < D) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) sm.Ag[8 * q + i + 1][c] = x[i] + pre;
-                if (q == 0) sm.Ag[0][c] = 0.f;
-                if (q == 3) sm.eBC[c] = __expf(x[7] + pre);
+            for (int e = 0; e < 8; ++e) {
+                float r = x[e];
+                r = dpp_add(r, IntConst<0x111>{}, IntConst<0xf>{});   // row_shr:1
+                r = dpp_add(r, IntConst<0x112>{}, IntConst<0xf>{});   // row_shr:2
+                r = dpp_add(r, IntConst<0x114>{}, IntConst<0xf>{});   // row_shr:4
+                r = dpp_add(r, IntConst<0x118>{}, IntConst<0xf>{});   // row_shr:8
+                r = dpp_add(r, IntConst<0x142>{}, IntConst<0xa>{});   // row_bcast:15 into rows 1, 3
+                x[e] = r;
             }
+            *reinterpret_cast<f32x4*>(&sm.Ag[vt + 1][vcg * 8]) = f32x4{x[0], x[1], x[2], x[3]};
+            *reinterpret_cast<f32x4*>(&sm.Ag[vt + 1][vcg * 8 + 4]) = f32x4{x[4], x[5], x[6], x[7]};
+            if (vt == 0) {
+                *reinterpret_cast<f32x4*>(&sm.Ag[0][vcg * 8]) = zero4();
+                *reinterpret_cast<f32x4*>(&sm.Ag[0][vcg * 8 + 4]) = zero4();
+            }
+            if (vt == CK - 1) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sm.eBC[vcg * 8 + e] = exp2_raw(x[e]);
+            }
+            if (vcg == 0) sm.beta[vt] = bt;
         }
         if (vt >= 0) {   // (diag(b) V)^T, fp16
-            const float bt = sm.beta[vt];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sm.bVT[vcg * 8 + e][vt] = f16_bits((_Float16)(bt * vx[e]));
+            for (int e = 0; e < 8; ++e) sm.bVT[vcg * 8 + e][vt] = f16_bits((_Float16)vx[e]);
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- 2a. renormalise the T columns by a power of two when they have become small: the
         // largest |T| each wave posted after the previous chunk's update (read here, past this
@@ -255,9 +298,9 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                 for (int e = 0; e < 8; ++e) {
                     const float rho = sm.Ag[16 + E1][c + e];
                     const float ct = sm.Ag[t + E1][c + e];
-                    gl[e] = kx[e] * __expf(ct - rho);
-                    gr[e] = kx[e] * __expf(rho - ct);
-                    gr1[e] = E1 ? gr[e] : kx[e] * __expf(rho - sm.Ag[t + 1][c + e]);
+                    gl[e] = kx[e] * exp2_raw(ct - rho);
+                    gr[e] = kx[e] * exp2_raw(rho - ct);
+                    gr1[e] = E1 ? gr[e] : kx[e] * exp2_raw(rho - sm.Ag[t + 1][c + e]);
                 }
                 auto put = [&](uint16_t (*P)[CK][D + 8], const float* v) {
                     unsigned h[4], l[4];
@@ -275,7 +318,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                 if (!E1) put(sm.u.g.GR1, gr1);
             }
         }
-        __syncthreads();
+        lds_barrier();
         if (wave < 6) {
             const bool lp = wave < 3;
             const int tile = lp ? wave : wave - 3;
@@ -317,9 +360,9 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                     const int t = t0 + 2 * p + i;
                     const float kx = bf(sm.Kb[t][c]);
                     const float at = sm.Ag[t + E1][c], at1 = sm.Ag[t + 1][c];
-                    rm[i] = kx * __expf(at);
-                    kh[i] = kx * __expf(bc - at);
-                    kp[i] = kx * __expf(bc - at1);
+                    rm[i] = kx * exp2_raw(at);
+                    kh[i] = kx * exp2_raw(bc - at);
+                    kp[i] = kx * exp2_raw(bc - at1);
                 }
                 rh[p] = cvt2_bf16(rm[0], rm[1]);
                 rl[p] = cvt2_bf16(rm[0] - bf16x2_to_f32(rh[p]).x, rm[1] - bf16x2_to_f32(rh[p]).y);
@@ -328,14 +371,14 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                 kh16[p] = cvt2_f16(kh[0], kh[1]);
                 kp16[p] = cvt2_f16(kp[0], kp[1]);
             }
-            *reinterpret_cast<u32x2*>(&sm.RmT[0][c][t0]) = u32x2{rh[0], rh[1]};
-            *reinterpret_cast<u32x2*>(&sm.RmT[1][c][t0]) = u32x2{rl[0], rl[1]};
+            *reinterpret_cast<u32x2*>(&sm.rv.RmT[0][c][t0]) = u32x2{rh[0], rh[1]};
+            *reinterpret_cast<u32x2*>(&sm.rv.RmT[1][c][t0]) = u32x2{rl[0], rl[1]};
             *reinterpret_cast<u32x2*>(&sm.KhTb[0][c][t0]) = u32x2{khh[0], khh[1]};
             *reinterpret_cast<u32x2*>(&sm.KhTb[1][c][t0]) = u32x2{khl[0], khl[1]};
             *reinterpret_cast<u32x2*>(&sm.KhT[c][t0]) = u32x2{kh16[0], kh16[1]};
             *reinterpret_cast<u32x2*>(&sm.KhpT[c][t0]) = u32x2{kp16[0], kp16[1]};
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- 3. A = (I + Lp)^-1: diagonal 16x16 blocks, then A10 = -D1 L10 D0
         if (wave < 2 && lane < 16) {
@@ -355,24 +398,24 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
             const int t = it / CK, s = it % CK;          // the diagonal is never computed
             sm.u.p.Lpb[t][s] = f16_bits((_Float16)(s < t ? sm.F1p[t][s] : 0.f));
         }
-        __syncthreads();
+        lds_barrier();
         if (wave == 0) {
             const f32x4 p = mm16_f32(&sm.F1[16][0], LDF, &sm.u.p.F2[0][0], LDF, lane);
             st16_f32(&sm.u.p.F3[0][0], 17, p, lane, 1.f);
         }
-        __syncthreads();
+        lds_barrier();
         if (wave == 0) {
             const f32x4 q = mm16_f32(&sm.u.p.F2[16][16], LDF, &sm.u.p.F3[0][0], 17, lane);
             st16_f32(&sm.u.p.F2[16][0], LDF, q, lane, -1.f);
         }
-        __syncthreads();
+        lds_barrier();
         for (int it = tid; it < CK * CK; it += 512) {
             const int t = it / CK, s = it % CK;
             const float ap = s <= t ? sm.u.p.F2[t][s] * sm.beta[s] : 0.f;
             sm.u.p.Ap[t][s] = f16_bits((_Float16)ap);
             put_bf16_split(&sm.u.p.ApB[0][t][s], &sm.u.p.ApB[1][t][s], ap);
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- 4. W^T = Rm^T Ap^T (-> W token-major) and Z1^T = (bV)^T L'^T
         for (int tile = wave; tile < 2 * RT * 2; tile += 8) {
@@ -381,7 +424,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
             const int mt = tl / 2, nt = tl % 2;   // channel tile, token tile
             f32x4 acc = zero4();
             if (isw) {
-                const FragB a = fragb_at(&sm.RmT[0][0][0], &sm.RmT[1][0][0], LDT, mt * 16 + n16, 8 * g4);
+                const FragB a = fragb_at(&sm.rv.RmT[0][0][0], &sm.rv.RmT[1][0][0], LDT, mt * 16 + n16, 8 * g4);
                 const FragB b = fragb_at(&sm.u.p.ApB[0][0][0], &sm.u.p.ApB[1][0][0], LDT, nt * 16 + n16, 8 * g4);
                 acc = mma3(a, b, acc);
                 uint16_t hh[4], bh[4], bl[4];
@@ -402,8 +445,9 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                 for (int e = 0; e < 4; ++e) sm.u.p.Z1T[mt * 16 + 4 * g4 + e][nt * 16 + n16] = f16_bits((_Float16)acc[e]);
             }
         }
-        __syncthreads();
+        lds_barrier();
 
+        if (c0 + CK < end) fetch(c0 + CK);   // Kb and RmT are not read again in this chunk
         // ---- 5. per owned column tile: Y = W X, R = -(Y [+ U]), X <- e^{b_C} X + Kh^T R [+ Kh'^T bV]
 #pragma unroll
         for (int c = 0; c < CTW; ++c) {
