@@ -58,7 +58,7 @@ __device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp
 
 constexpr int CK = 32;        // chunk length
 constexpr int LDT = CK + 8;   // token-indexed 16-bit rows
-constexpr int LDF = CK + 1;   // fp32 32x32 matrices
+constexpr int LDF = CK + 4;   // fp32 32x32 matrices (16-byte aligned rows)
 
 template <int D>
 struct alignas(16) KdaSmem {
@@ -81,8 +81,7 @@ struct alignas(16) KdaSmem {
     uint16_t bVT[D][LDT];          // (diag(b) V)^T
     union {
         struct {                       // phases 3-5
-            float F2[CK][LDF];             // A = (I + Lp)^-1
-            float F3[16][17];
+            float F2[CK][LDF];             // A = (I + Lp)^-1 (diagonal blocks)
             uint16_t ApB[2][CK][LDT];      // A diag(b), bf16 hi / lo
             uint16_t WpB[2][CK][D + 8];    // W, token-major, bf16 hi / lo (T columns)
             uint16_t Ap[CK][LDT];          // A diag(b)
@@ -366,30 +365,36 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                 }
                 rh[p] = cvt2_bf16(rm[0], rm[1]);
                 rl[p] = cvt2_bf16(rm[0] - bf16x2_to_f32(rh[p]).x, rm[1] - bf16x2_to_f32(rh[p]).y);
-                khh[p] = cvt2_bf16(kh[0], kh[1]);
-                khl[p] = cvt2_bf16(kh[0] - bf16x2_to_f32(khh[p]).x, kh[1] - bf16x2_to_f32(khh[p]).y);
+                if (t_live) {
+                    khh[p] = cvt2_bf16(kh[0], kh[1]);
+                    khl[p] = cvt2_bf16(kh[0] - bf16x2_to_f32(khh[p]).x, kh[1] - bf16x2_to_f32(khh[p]).y);
+                }
                 kh16[p] = cvt2_f16(kh[0], kh[1]);
                 kp16[p] = cvt2_f16(kp[0], kp[1]);
             }
             *reinterpret_cast<u32x2*>(&sm.rv.RmT[0][c][t0]) = u32x2{rh[0], rh[1]};
             *reinterpret_cast<u32x2*>(&sm.rv.RmT[1][c][t0]) = u32x2{rl[0], rl[1]};
-            *reinterpret_cast<u32x2*>(&sm.KhTb[0][c][t0]) = u32x2{khh[0], khh[1]};
-            *reinterpret_cast<u32x2*>(&sm.KhTb[1][c][t0]) = u32x2{khl[0], khl[1]};
+            if (t_live) {
+                *reinterpret_cast<u32x2*>(&sm.KhTb[0][c][t0]) = u32x2{khh[0], khh[1]};
+                *reinterpret_cast<u32x2*>(&sm.KhTb[1][c][t0]) = u32x2{khl[0], khl[1]};
+            }
             *reinterpret_cast<u32x2*>(&sm.KhT[c][t0]) = u32x2{kh16[0], kh16[1]};
             *reinterpret_cast<u32x2*>(&sm.KhpT[c][t0]) = u32x2{kp16[0], kp16[1]};
         }
         lds_barrier();
 
-        // ---- 3. A = (I + Lp)^-1: diagonal 16x16 blocks, then A10 = -D1 L10 D0
+        // ---- 3. A = (I + Lp)^-1: diagonal 16x16 blocks D0, D1 by forward substitution (one
+        // lane per column), then A10 = -D1 (L10 D0) by one wave, then A diag(b) to its operand
+        // planes (fp16, and bf16 hi + lo)
         if (wave < 2 && lane < 16) {
             const int o = wave * 16, j = lane;
             float x[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float s = (r == j) ? 1.f : 0.f;
+            for (int r = 0; r < 16; ++r) {   // row r of L0 (or L1) is read as four 16-byte pieces
+                float s_ = (r == j) ? 1.f : 0.f;
 #pragma unroll
-                for (int q = 0; q < r; ++q) s -= sm.F1[o + r][o + q] * x[q];
-                x[r] = s;
+                for (int q = 0; q < r; ++q) s_ -= sm.F1[o + r][o + q] * x[q];
+                x[r] = s_;
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) sm.u.p.F2[o + r][o + j] = x[r];
@@ -400,13 +405,15 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
         }
         lds_barrier();
         if (wave == 0) {
-            const f32x4 p = mm16_f32(&sm.F1[16][0], LDF, &sm.u.p.F2[0][0], LDF, lane);
-            st16_f32(&sm.u.p.F3[0][0], 17, p, lane, 1.f);
-        }
-        lds_barrier();
-        if (wave == 0) {
-            const f32x4 q = mm16_f32(&sm.u.p.F2[16][16], LDF, &sm.u.p.F3[0][0], 17, lane);
-            st16_f32(&sm.u.p.F2[16][0], LDF, q, lane, -1.f);
+            // F = L10 D0 in MFMA accumulators (lane (g4, n16) holds rows 4 g4 .. 4 g4 + 3 of
+            // column n16), then -D1 F with the contraction index of k-step kb taken as
+            // 4 g4 + kb, so that F's accumulators are the B operand as they stand
+            const f32x4 f = mm16_f32(&sm.F1[16][0], LDF, &sm.u.p.F2[0][0], LDF, lane);
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                acc = mma_f32(sm.u.p.F2[16 + n16][16 + 4 * g4 + kb], f[kb], acc);
+            st16_f32(&sm.u.p.F2[16][0], LDF, acc, lane, -1.f);
         }
         lds_barrier();
         for (int it = tid; it < CK * CK; it += 512) {
@@ -427,16 +434,15 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                 const FragB a = fragb_at(&sm.rv.RmT[0][0][0], &sm.rv.RmT[1][0][0], LDT, mt * 16 + n16, 8 * g4);
                 const FragB b = fragb_at(&sm.u.p.ApB[0][0][0], &sm.u.p.ApB[1][0][0], LDT, nt * 16 + n16, 8 * g4);
                 acc = mma3(a, b, acc);
-                uint16_t hh[4], bh[4], bl[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    hh[e] = f16_bits((_Float16)acc[e]);
-                    put_bf16_split(&bh[e], &bl[e], acc[e]);
-                }
                 const int row = nt * 16 + n16, col = mt * 16 + 4 * g4;
-                *reinterpret_cast<u32x2*>(&sm.u.p.Wp[row][col]) = u32x2{pack2(hh[0], hh[1]), pack2(hh[2], hh[3])};
-                *reinterpret_cast<u32x2*>(&sm.u.p.WpB[0][row][col]) = u32x2{pack2(bh[0], bh[1]), pack2(bh[2], bh[3])};
-                *reinterpret_cast<u32x2*>(&sm.u.p.WpB[1][row][col]) = u32x2{pack2(bl[0], bl[1]), pack2(bl[2], bl[3])};
+                *reinterpret_cast<u32x2*>(&sm.u.p.Wp[row][col]) = u32x2{cvt2_f16(acc[0], acc[1]), cvt2_f16(acc[2], acc[3])};
+                if (t_live) {
+                    uint16_t bh[4], bl[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) put_bf16_split(&bh[e], &bl[e], acc[e]);
+                    *reinterpret_cast<u32x2*>(&sm.u.p.WpB[0][row][col]) = u32x2{pack2(bh[0], bh[1]), pack2(bh[2], bh[3])};
+                    *reinterpret_cast<u32x2*>(&sm.u.p.WpB[1][row][col]) = u32x2{pack2(bl[0], bl[1]), pack2(bl[2], bl[3])};
+                }
             } else {
                 const Frag<1> a = f16frag(&sm.bVT[0][0], LDT, mt * 16 + n16, 8 * g4);
                 const Frag<1> b = f16frag(&sm.u.p.Lpb[0][0], LDT, nt * 16 + n16, 8 * g4);
