@@ -162,27 +162,28 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
     constexpr int NPC = CK * D * 2 / 1024;   // 1-KiB pieces of a chunk's [CK][D] bf16 plane
     static_assert(NPC <= 8 && CK * (D / 8) <= 512, "one piece per wave, one staging item per thread");
     static_assert(sizeof(sm.rv.nx) <= sizeof(sm.rv.RmT), "v and log-gates fit over RmT");
-    auto tok_off = [&](int64_t c0n, int t) -> size_t {
-        const int64_t tt = c0n + t < end ? c0n + t : end - 1;
-        return (size_t)tt * tok_stride + (size_t)h * D;
-    };
     uint16_t braw = 0;   // beta of token (tid mod CK) of the chunk being fetched
     auto fetch = [&](int64_t c0n) {
+        // chunk base (uniform, 64-bit) + row offset below 32 tokens (32-bit); rows past the
+        // segment clamped to its last token
+        const int last = (end - 1 - c0n) < CK - 1 ? (int)(end - 1 - c0n) : CK - 1;
+        const size_t base = (size_t)c0n * tok_stride + (size_t)h * D;
+        const unsigned ts = (unsigned)tok_stride;
         if (wave < NPC) {
             const int e = wave * 512 + lane * 8;   // K: element e of the token-major plane
+            const int i = wave * 64 + lane;        // v, log-gates: staging item i
+            const unsigned ok = (unsigned)min(e / D, last) * ts + (unsigned)(e % D);
+            const unsigned oi = (unsigned)min(i % CK, last) * ts + (unsigned)((i / CK) * 8);
             // (the addresses are locals: as calls inside the builtin's arguments they stop the
             // host pass from emitting the kernel's launch stub)
-            const uint16_t* pk = k + tok_off(c0n, e / D) + e % D;
+            const uint16_t* pk = k + base + ok;
+            const uint16_t* pv = v + base + oi;
+            const uint16_t* pg = gl + base + oi;
             __builtin_amdgcn_global_load_lds(pk, (__attribute__((address_space(3))) void*)(&sm.Kb[0][0] + wave * 512), 16, 0, 0);
-            const int i = wave * 64 + lane;        // v, log-gates: staging item i
-            const size_t oi = tok_off(c0n, i % CK) + (i / CK) * 8;
-            const uint16_t* pv = v + oi;
-            const uint16_t* pg = gl + oi;
             __builtin_amdgcn_global_load_lds(pv, (__attribute__((address_space(3))) void*)(sm.rv.nx.Vr + wave * 512), 16, 0, 0);
             __builtin_amdgcn_global_load_lds(pg, (__attribute__((address_space(3))) void*)(sm.rv.nx.Gr + wave * 512), 16, 0, 0);
         }
-        const int64_t tt = c0n + (tid & (CK - 1)) < end ? c0n + (tid & (CK - 1)) : end - 1;
-        braw = beta[(size_t)tt * H + h];
+        braw = beta[(size_t)(c0n + min(tid & (CK - 1), last)) * H + h];
     };
     if (beg < end) fetch(beg);
     for (int64_t c0 = beg; c0 < end; c0 += CK) {
@@ -424,16 +425,33 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
         }
         lds_barrier();
 
-        // ---- 4. W^T = Rm^T Ap^T (-> W token-major) and Z1^T = (bV)^T L'^T
-        for (int tile = wave; tile < 2 * RT * 2; tile += 8) {
-            const bool isw = tile < RT * 2;
-            const int tl = isw ? tile : tile - RT * 2;
-            const int mt = tl / 2, nt = tl % 2;   // channel tile, token tile
-            f32x4 acc = zero4();
-            if (isw) {
-                const FragB a = fragb_at(&sm.rv.RmT[0][0][0], &sm.rv.RmT[1][0][0], LDT, mt * 16 + n16, 8 * g4);
-                const FragB b = fragb_at(&sm.u.p.ApB[0][0][0], &sm.u.p.ApB[1][0][0], LDT, nt * 16 + n16, 8 * g4);
-                acc = mma3(a, b, acc);
+        // ---- 4. W^T = Rm^T Ap^T (-> W token-major) and Z1^T = (bV)^T L'^T: wave w takes tiles
+        // w, w + 8, ... of each (channel tile t / 2, token tile t % 2, so one token tile per
+        // wave and one shared B fragment); every fragment is read before the first product
+        {
+            constexpr int TPW = RT * 2 / 8;   // W (and Z1) tiles per wave
+            static_assert((RT * 2) % 8 == 0, "tiles spread evenly over the waves");
+            const int nt = wave % 2;
+            const FragB wb = fragb_at(&sm.u.p.ApB[0][0][0], &sm.u.p.ApB[1][0][0], LDT, nt * 16 + n16, 8 * g4);
+            const Frag<1> zb = f16frag(&sm.u.p.Lpb[0][0], LDT, nt * 16 + n16, 8 * g4);
+            FragB wa[TPW];
+            Frag<1> za[TPW];
+#pragma unroll
+            for (int c = 0; c < TPW; ++c) {
+                const int mt = (wave + 8 * c) / 2;
+                wa[c] = fragb_at(&sm.rv.RmT[0][0][0], &sm.rv.RmT[1][0][0], LDT, mt * 16 + n16, 8 * g4);
+                za[c] = f16frag(&sm.bVT[0][0], LDT, mt * 16 + n16, 8 * g4);
+            }
+            f32x4 wacc[TPW], zacc[TPW];
+#pragma unroll
+            for (int c = 0; c < TPW; ++c) {
+                wacc[c] = mma3(wa[c], wb, zero4());
+                zacc[c] = mma<1>(za[c], zb, zero4());
+            }
+#pragma unroll
+            for (int c = 0; c < TPW; ++c) {
+                const int mt = (wave + 8 * c) / 2;
+                const f32x4 acc = wacc[c];
                 const int row = nt * 16 + n16, col = mt * 16 + 4 * g4;
                 *reinterpret_cast<u32x2*>(&sm.u.p.Wp[row][col]) = u32x2{cvt2_f16(acc[0], acc[1]), cvt2_f16(acc[2], acc[3])};
                 if (t_live) {
@@ -443,12 +461,9 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                     *reinterpret_cast<u32x2*>(&sm.u.p.WpB[0][row][col]) = u32x2{pack2(bh[0], bh[1]), pack2(bh[2], bh[3])};
                     *reinterpret_cast<u32x2*>(&sm.u.p.WpB[1][row][col]) = u32x2{pack2(bl[0], bl[1]), pack2(bl[2], bl[3])};
                 }
-            } else {
-                const Frag<1> a = f16frag(&sm.bVT[0][0], LDT, mt * 16 + n16, 8 * g4);
-                const Frag<1> b = f16frag(&sm.u.p.Lpb[0][0], LDT, nt * 16 + n16, 8 * g4);
-                acc = mma<1>(a, b, acc);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sm.u.p.Z1T[mt * 16 + 4 * g4 + e][nt * 16 + n16] = f16_bits((_Float16)acc[e]);
+                for (int e = 0; e < 4; ++e)
+                    sm.u.p.Z1T[mt * 16 + 4 * g4 + e][nt * 16 + n16] = f16_bits((_Float16)zacc[c][e]);
             }
         }
         lds_barrier();
