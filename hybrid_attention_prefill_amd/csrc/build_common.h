@@ -6,6 +6,13 @@ namespace hypic {
 namespace bld {
 
 // fp32 16x16 block product on MFMA: returns A(16x16) B(16x16), D layout.
+// An empty asm that "modifies" x: values derived from it inside a loop body are
+// recomputed each iteration instead of being hoisted (and then spilled) by the compiler.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 __device__ __forceinline__ f32x4 mm16_f32(const float* A, int lda, const float* B, int ldb, int lane) {
     const int g4 = lane >> 4, n16 = lane & 15;
     f32x4 acc = zero4();

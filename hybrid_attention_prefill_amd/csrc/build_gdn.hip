@@ -146,13 +146,6 @@ __device__ __forceinline__ void to16(float x, uint16_t& hi, uint16_t& lo) {
     }
 }
 
-// An empty asm that "modifies" x: values derived from it inside a loop body are
-// recomputed each iteration instead of being hoisted (and then spilled) by the compiler.
-__device__ __forceinline__ int opaque(int x) {
-    asm volatile("" : "+v"(x));
-    return x;
-}
-
 // a lane's value moved by a DPP control (lanes without a source, or outside row_mask, get 0)
 template <int CTRL, int ROWS>
 __device__ __forceinline__ float dpp_move(float v) {

@@ -65,7 +65,7 @@ struct alignas(16) KdaSmem {
     uint16_t Kb[CK][D];            // K (bf16 bits), token-major, loaded global -> LDS directly
     float Ag[CK + 1][D + 4];       // exclusive cumulative log2-gate per channel; row t+1 inclusive, row CK = b_C
     float beta[CK];
-    float eBC[D];                  // e^{b_C} per channel (the chunk's decay of the state rows)
+    float eBC[2][D];               // e^{b_C} per channel (the chunk's decay of the state rows), by chunk parity
     float F1[CK][LDF];             // Lp (strictly lower, beta folded)
     float F1p[CK][LDF];            // L'
     union {
@@ -133,14 +133,20 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
     beg = beg < 0 ? 0 : (beg > n_tokens ? n_tokens : beg);
     end = end < beg ? beg : (end > n_tokens ? n_tokens : end);
 
+    // Column tiles of X = [T | S]: waves 0-3 own CTW S tiles each, waves 4-7 CTW T tiles each,
+    // so every A fragment of the update feeds CTW products, and each SIMD (waves w and w + 4)
+    // holds one wave of each kind.
+    static_assert(NCT == 8 * CTW, "the column tiles split evenly over the eight waves");
+    const bool s_wave = wave < 4;
+    const int tile0 = (s_wave ? RT : 0) + (wave & 3) * CTW;   // first owned column tile
     f32x4 X[RT][CTW];
 #pragma unroll
     for (int c = 0; c < CTW; ++c) {
-        const int ct = wave + 8 * c;
+        const int ct = tile0 + c;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             X[rt][c] = zero4();
-            if (ct < RT) {
+            if (!s_wave) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     X[rt][c][e] = (rt * 16 + 4 * g4 + e == ct * 16 + n16) ? 1.f : 0.f;
@@ -170,8 +176,9 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
         const size_t base = (size_t)c0n * tok_stride + (size_t)h * D;
         const unsigned ts = (unsigned)tok_stride;
         if (wave < NPC) {
-            const int e = wave * 512 + lane * 8;   // K: element e of the token-major plane
-            const int i = wave * 64 + lane;        // v, log-gates: staging item i
+            const int ln = opaque(lane);           // (recomputed here rather than kept live)
+            const int e = wave * 512 + ln * 8;     // K: element e of the token-major plane
+            const int i = wave * 64 + ln;          // v, log-gates: staging item i
             const unsigned ok = (unsigned)min(e / D, last) * ts + (unsigned)(e % D);
             const unsigned oi = (unsigned)min(i % CK, last) * ts + (unsigned)((i / CK) * 8);
             // (the addresses are locals: as calls inside the builtin's arguments they stop the
@@ -188,7 +195,11 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
     if (beg < end) fetch(beg);
     for (int64_t c0 = beg; c0 < end; c0 += CK) {
         const int n = (int)((end - c0) < CK ? (end - c0) : CK);
-        const int par = (int)(((c0 - beg) / CK) & 1);   // chunk parity (renormalisation records)
+        const int par = (int)(((c0 - beg) / CK) & 1);   // chunk parity (eBC, renormalisation records)
+        // The staging writes, before the chunk's first barrier, only what the previous chunk
+        // last read before its own final barrier (Ag, betas) or keeps apart by parity (eBC):
+        // other waves may still be in the previous chunk's state update, which reads eBC and
+        // (diag(b) V)^T, so the latter is written after the barrier.
         // ---- 1. staging: thread = item (channel group vcg, token vt): v, log-gates and beta to
         // registers; the inclusive cumulative log2-gate of its 8 channels over the chunk by a
         // 32-lane scan (the item's token is its lane within the half-wave), written to Ag with
@@ -238,15 +249,15 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
             }
             if (vt == CK - 1) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) sm.eBC[vcg * 8 + e] = exp2_raw(x[e]);
+                for (int e = 0; e < 8; ++e) sm.eBC[par][vcg * 8 + e] = exp2_raw(x[e]);
             }
             if (vcg == 0) sm.beta[vt] = bt;
         }
-        if (vt >= 0) {   // (diag(b) V)^T, fp16
+        lds_barrier();
+        if (vt >= 0) {   // (diag(b) V)^T, fp16 (first read after the Gram phase's barrier)
 #pragma unroll
             for (int e = 0; e < 8; ++e) sm.bVT[vcg * 8 + e][vt] = f16_bits((_Float16)vx[e]);
         }
-        lds_barrier();
 
         // ---- 2a. renormalise the T columns by a power of two when they have become small: the
         // largest |T| each wave posted after the previous chunk's update (read here, past this
@@ -260,20 +271,18 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
             if (mm > 0.f) frexpf(mm, &em);
             if (t_live && (mm == 0.f || log2s + em < -120)) {  // T is below the floor for good
                 t_live = false;
+                if (!s_wave)
 #pragma unroll
-                for (int c = 0; c < CTW; ++c)
-                    if (wave + 8 * c < RT)
+                    for (int c = 0; c < CTW; ++c)
 #pragma unroll
                         for (int rt = 0; rt < RT; ++rt) X[rt][c] = zero4();
             } else if (mm < 0x1p-16f) {
                 const float sc = ldexpf(1.f, -em);
+                if (!s_wave)
 #pragma unroll
-                for (int c = 0; c < CTW; ++c) {
-                    if (wave + 8 * c < RT) {
+                    for (int c = 0; c < CTW; ++c)
 #pragma unroll
                         for (int rt = 0; rt < RT; ++rt) X[rt][c] *= sc;
-                    }
-                }
                 log2s += em;
             }
         }
@@ -469,112 +478,112 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
         lds_barrier();
 
         if (c0 + CK < end) fetch(c0 + CK);   // Kb and RmT are not read again in this chunk
-        // ---- 5. per owned column tile: Y = W X, R = -(Y [+ U]), X <- e^{b_C} X + Kh^T R [+ Kh'^T bV]
+        // ---- 5. update of the owned column tiles: Y = W X, R = -(Y [+ U]),
+        // X <- e^{b_C} X + Kh^T R [+ Kh'^T bV].  The k-blocks of X are converted to B fragments
+        // as they are used; each A fragment is read once for all CTW tiles.
+        if (s_wave) {   // S columns: fp16 operands
+            const int vt0 = (wave & 3) * CTW;   // first owned value tile
+            f32x4 Y[CTW][2];
+            {   // U = Ap Z1 as the products' initial value
+                const Frag<1> a0 = f16frag(&sm.u.p.Ap[0][0], LDT, n16, 8 * g4);
+                const Frag<1> a1 = f16frag(&sm.u.p.Ap[0][0], LDT, 16 + n16, 8 * g4);
 #pragma unroll
-        for (int c = 0; c < CTW; ++c) {
-            const int ct = wave + 8 * c;
-            if (ct >= NCT) continue;
-            const bool is_s = ct >= RT;
-            const int vt16 = ct - RT;
-            if (!is_s) {  // T columns: bf16 hi + lo products
-                if (!t_live) continue;
-                FragB xb[KSD];
-#pragma unroll
-                for (int kb = 0; kb < KSD; ++kb) xb[kb] = dpair_to_fragb(X[2 * kb][c], X[2 * kb + 1][c]);
-                f32x4 R[2];
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt) {
-                    f32x4 y = zero4();
-#pragma unroll
-                    for (int kb = 0; kb < KSD; ++kb)
-                        y = mma3(fragb_at(&sm.u.p.WpB[0][0][0], &sm.u.p.WpB[1][0][0], D + 8, tt * 16 + n16, kb * 32 + 8 * g4),
-                                 xb[kb], y);
-                    R[tt] = -y;
+                for (int c = 0; c < CTW; ++c) {
+                    const Frag<1> b = f16frag(&sm.u.p.Z1T[0][0], LDT, (vt0 + c) * 16 + n16, 8 * g4);
+                    Y[c][0] = mma<1>(a0, b, zero4());
+                    Y[c][1] = mma<1>(a1, b, zero4());
                 }
-                const FragB rb = dpair_to_fragb(R[0], R[1]);
+            }
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    const f32x4 eb = *reinterpret_cast<const f32x4*>(&sm.eBC[rt * 16 + 4 * g4]);
+            for (int kb = 0; kb < KSD; ++kb) {
+                const Frag<1> a0 = f16frag(&sm.u.p.Wp[0][0], D + 8, n16, kb * 32 + 8 * g4);
+                const Frag<1> a1 = f16frag(&sm.u.p.Wp[0][0], D + 8, 16 + n16, kb * 32 + 8 * g4);
+#pragma unroll
+                for (int c = 0; c < CTW; ++c) {
+                    const Frag<1> xb = dpair_to_frag<1>(X[2 * kb][c], X[2 * kb + 1][c]);
+                    Y[c][0] = mma<1>(a0, xb, Y[c][0]);
+                    Y[c][1] = mma<1>(a1, xb, Y[c][1]);
+                }
+            }
+            Frag<1> rb[CTW], vb[CTW];
+#pragma unroll
+            for (int c = 0; c < CTW; ++c) {
+                rb[c] = dpair_to_frag<1>(-Y[c][0], -Y[c][1]);
+                vb[c] = f16frag(&sm.bVT[0][0], LDT, (vt0 + c) * 16 + n16, 8 * g4);
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const f32x4 eb = *reinterpret_cast<const f32x4*>(&sm.eBC[par][rt * 16 + 4 * g4]);
+                const Frag<1> a = f16frag(&sm.KhT[0][0], LDT, rt * 16 + n16, 8 * g4);
+                const Frag<1> a2 = f16frag(&sm.KhpT[0][0], LDT, rt * 16 + n16, 8 * g4);
+#pragma unroll
+                for (int c = 0; c < CTW; ++c) {
                     f32x4 acc;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) acc[e] = X[rt][c][e] * eb[e];
-                    X[rt][c] = mma3(fragb_at(&sm.KhTb[0][0][0], &sm.KhTb[1][0][0], LDT, rt * 16 + n16, 8 * g4), rb, acc);
-                }
-                continue;
-            }
-            f32x4 U[2] = {zero4(), zero4()};
-            if (is_s) {  // U = Ap Z1 for this value tile
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt) {
-                    const Frag<1> a = f16frag(&sm.u.p.Ap[0][0], LDT, tt * 16 + n16, 8 * g4);
-                    const Frag<1> b = f16frag(&sm.u.p.Z1T[0][0], LDT, vt16 * 16 + n16, 8 * g4);
-                    U[tt] = mma<1>(a, b, U[tt]);
+                    acc = mma<1>(a, rb[c], acc);
+                    X[rt][c] = mma<1>(a2, vb[c], acc);
                 }
             }
-            Frag<1> xb[KSD];
+        } else if (t_live) {   // T columns: bf16 hi + lo products
+            f32x4 Y[CTW][2];
 #pragma unroll
-            for (int kb = 0; kb < KSD; ++kb) xb[kb] = dpair_to_frag<1>(X[2 * kb][c], X[2 * kb + 1][c]);
-            f32x4 R[2];
+            for (int c = 0; c < CTW; ++c) Y[c][0] = Y[c][1] = zero4();
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                f32x4 y = zero4();
+            for (int kb = 0; kb < KSD; ++kb) {
+                const FragB a0 = fragb_at(&sm.u.p.WpB[0][0][0], &sm.u.p.WpB[1][0][0], D + 8, n16, kb * 32 + 8 * g4);
+                const FragB a1 = fragb_at(&sm.u.p.WpB[0][0][0], &sm.u.p.WpB[1][0][0], D + 8, 16 + n16, kb * 32 + 8 * g4);
 #pragma unroll
-                for (int kb = 0; kb < KSD; ++kb) {
-                    const Frag<1> a = f16frag(&sm.u.p.Wp[0][0], D + 8, tt * 16 + n16, kb * 32 + 8 * g4);
-                    y = mma<1>(a, xb[kb], y);
+                for (int c = 0; c < CTW; ++c) {
+                    const FragB xb = dpair_to_fragb(X[2 * kb][c], X[2 * kb + 1][c]);
+                    Y[c][0] = mma3(a0, xb, Y[c][0]);
+                    Y[c][1] = mma3(a1, xb, Y[c][1]);
                 }
-                R[tt] = -(y + U[tt]);
             }
-            const Frag<1> rb = dpair_to_frag<1>(R[0], R[1]);
-            Frag<1> vb;
-            if (is_s) vb = f16frag(&sm.bVT[0][0], LDT, vt16 * 16 + n16, 8 * g4);
+            FragB rb[CTW];
+#pragma unroll
+            for (int c = 0; c < CTW; ++c) rb[c] = dpair_to_fragb(-Y[c][0], -Y[c][1]);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
-                const f32x4 eb = *reinterpret_cast<const f32x4*>(&sm.eBC[rt * 16 + 4 * g4]);
-                f32x4 acc;
+                const f32x4 eb = *reinterpret_cast<const f32x4*>(&sm.eBC[par][rt * 16 + 4 * g4]);
+                const FragB a = fragb_at(&sm.KhTb[0][0][0], &sm.KhTb[1][0][0], LDT, rt * 16 + n16, 8 * g4);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] = X[rt][c][e] * eb[e];
-                const Frag<1> a = f16frag(&sm.KhT[0][0], LDT, rt * 16 + n16, 8 * g4);
-                acc = mma<1>(a, rb, acc);
-                if (is_s) {
-                    const Frag<1> a2 = f16frag(&sm.KhpT[0][0], LDT, rt * 16 + n16, 8 * g4);
-                    acc = mma<1>(a2, vb, acc);
+                for (int c = 0; c < CTW; ++c) {
+                    f32x4 acc;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[e] = X[rt][c][e] * eb[e];
+                    X[rt][c] = mma3(a, rb[c], acc);
                 }
-                X[rt][c] = acc;
             }
         }
         // ---- 6. post this wave's largest |T| for the next chunk's renormalisation (no barrier:
         // the next chunk's staging writes nothing this update reads, and its barriers come
-        // before the read)
+        // before the read); the S waves post 0
         float m = 0.f;
+        if (!s_wave) {
 #pragma unroll
-        for (int c = 0; c < CTW; ++c) {
-            const int ct = wave + 8 * c;
-            if (ct < RT) {
+            for (int c = 0; c < CTW; ++c)
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(X[rt][c][e]));
-            }
-        }
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+            for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+        }
         if (lane == 0) sm.red2[par][wave] = m;
     }
 
     const size_t pair = (size_t)seg * H + h;
+    if (!s_wave && T_out == nullptr) return;
 #pragma unroll
     for (int c = 0; c < CTW; ++c) {
-        const int ct = wave + 8 * c;
-        if (ct >= NCT) continue;
-        const bool is_s = ct >= RT;
-        if (!is_s && T_out == nullptr) continue;
+        const int ct = tile0 + c;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int row = rt * 16 + 4 * g4 + e;
-                if (is_s) S_out[pair * D * D + (size_t)row * D + (ct - RT) * 16 + n16] = X[rt][c][e];
+                if (s_wave) S_out[pair * D * D + (size_t)row * D + (ct - RT) * 16 + n16] = X[rt][c][e];
                 else put_t(T_out, t_split, pair, D, row, ct * 16 + n16, ldexpf(X[rt][c][e], log2s));
             }
     }
