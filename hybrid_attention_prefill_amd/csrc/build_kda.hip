@@ -259,34 +259,26 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
             for (int e = 0; e < 8; ++e) sm.bVT[vcg * 8 + e][vt] = f16_bits((_Float16)vx[e]);
         }
 
-        // ---- 2a. renormalise the T columns by a power of two when they have become small: the
-        // largest |T| each wave posted after the previous chunk's update (read here, past this
-        // chunk's first two barriers); once every T entry is below 2^-120 the T columns are dropped.  One
-        // chunk of delay is safe: a chunk decays T by at most e^{-32 max|g|}, far inside fp32.
-        if (c0 != beg) {
+        // ---- 2a. renormalisation of the T columns by a power of two when they have become
+        // small, from the largest |T| each wave posted after the previous chunk's update (read
+        // past this chunk's first barrier); the factor tsc is applied with e^{b_C} in the update,
+        // so no branch rewrites the state registers.  Once every T entry is below 2^-120 the T
+        // columns are dropped (no longer updated; written as zeros).  One chunk of delay is
+        // safe: a chunk decays T by at most e^{-32 max|g|}, far inside fp32.
+        float tsc = 1.f;
+        if (c0 != beg && t_live) {
             float mm = 0.f;
 #pragma unroll
             for (int w = 0; w < 8; ++w) mm = fmaxf(mm, sm.red2[par ^ 1][w]);
             int em = 0;
             if (mm > 0.f) frexpf(mm, &em);
-            if (t_live && (mm == 0.f || log2s + em < -120)) {  // T is below the floor for good
+            if (mm == 0.f || log2s + em < -120) {   // T is below the floor for good
                 t_live = false;
-                if (!s_wave)
-#pragma unroll
-                    for (int c = 0; c < CTW; ++c)
-#pragma unroll
-                        for (int rt = 0; rt < RT; ++rt) X[rt][c] = zero4();
             } else if (mm < 0x1p-16f) {
-                const float sc = ldexpf(1.f, -em);
-                if (!s_wave)
-#pragma unroll
-                    for (int c = 0; c < CTW; ++c)
-#pragma unroll
-                        for (int rt = 0; rt < RT; ++rt) X[rt][c] *= sc;
+                tsc = ldexpf(1.f, -em);
                 log2s += em;
             }
         }
-
 
         // ---- 2. decay-weighted Gram matrices Lp (waves 0-2) and L' (waves 3-5), bf16 hi+lo.
         // Their operands are formed once per chunk by all waves (one token, 8 channels per item):
@@ -542,10 +534,10 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
             }
             FragB rb[CTW];
 #pragma unroll
-            for (int c = 0; c < CTW; ++c) rb[c] = dpair_to_fragb(-Y[c][0], -Y[c][1]);
+            for (int c = 0; c < CTW; ++c) rb[c] = dpair_to_fragb(Y[c][0] * -tsc, Y[c][1] * -tsc);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
-                const f32x4 eb = *reinterpret_cast<const f32x4*>(&sm.eBC[par][rt * 16 + 4 * g4]);
+                const f32x4 eb = *reinterpret_cast<const f32x4*>(&sm.eBC[par][rt * 16 + 4 * g4]) * tsc;
                 const FragB a = fragb_at(&sm.KhTb[0][0][0], &sm.KhTb[1][0][0], LDT, rt * 16 + n16, 8 * g4);
 #pragma unroll
                 for (int c = 0; c < CTW; ++c) {
@@ -560,7 +552,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
         // the next chunk's staging writes nothing this update reads, and its barriers come
         // before the read); the S waves post 0
         float m = 0.f;
-        if (!s_wave) {
+        if (!s_wave && t_live) {
 #pragma unroll
             for (int c = 0; c < CTW; ++c)
 #pragma unroll
@@ -584,7 +576,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
             for (int e = 0; e < 4; ++e) {
                 const int row = rt * 16 + 4 * g4 + e;
                 if (s_wave) S_out[pair * D * D + (size_t)row * D + (ct - RT) * 16 + n16] = X[rt][c][e];
-                else put_t(T_out, t_split, pair, D, row, ct * 16 + n16, ldexpf(X[rt][c][e], log2s));
+                else put_t(T_out, t_split, pair, D, row, ct * 16 + n16, t_live ? ldexpf(X[rt][c][e], log2s) : 0.f);
             }
     }
 }
