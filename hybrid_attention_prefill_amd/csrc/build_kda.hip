@@ -280,46 +280,103 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
             }
         }
 
-        // ---- 2. decay-weighted Gram matrices Lp (waves 0-2) and L' (waves 3-5), bf16 hi+lo.
-        // Their operands are formed once per chunk by all waves (one token, 8 channels per item):
-        // with one reference rho = c_16 per channel (the second 16-token block's first gate)
-        // every factor is <= 1 except on a diagonal block, where it is bounded by one block's
-        // decay, and the products are exactly the decay-weighted ones (rho cancels).
-        for (int it = tid; it < CK * (D / 8); it += 512) {   // item: token t, channels c .. c+7
-            {
-                const int t = it / (D / 8), c = (it % (D / 8)) * 8;
-                const u32x4 kw = *reinterpret_cast<const u32x4*>(&sm.Kb[t][c]);
-                float kx[8], gl[8], gr[8], gr1[8];
+        // ---- 2. operands of the decay-weighted Gram matrices and the decay-scaled keys, in one
+        // pass (all waves; item = 4 tokens x 2 channels, channel pair fastest across lanes).
+        // With one reference rho = c_16 per channel (the second 16-token block's first gate),
+        // the Gram operands are k e^{c - rho}, k e^{rho - c} and k e^{rho - i} (i the inclusive
+        // gate): every factor is <= 1 except on a diagonal block, where it is bounded by one
+        // block's decay, and rho cancels in the products.  The key operands follow from the same
+        // factors and two per-channel constants: e^{a} o k = (k e^{c - rho}) e^{rho},
+        // Kh = (k e^{rho - c}) e^{b_C - rho}, Kh' = (k e^{rho - i}) e^{b_C - rho}; and e^{rho - i_t}
+        // = e^{rho - c_{t+1}} is the next token's e^{rho - c}, so a 4-token item takes 11
+        // exponentials per channel instead of 24.  Gram operands go token-major (4-byte stores of
+        // the channel pair), key operands channel-major (8-byte stores of the 4 tokens).
+        {
+            constexpr int NCP = D / 2;                 // channel pairs
+            static_assert((CK / 4) * NCP <= 512, "one item per thread");
+            if (tid < (CK / 4) * NCP) {
+                const int c = 2 * (tid % NCP), t0 = 4 * (tid / NCP);
+                float kx[4][2], A[5][2], eg[4][2], er[5][2];
+                float P[2], Q[2];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    kx[2 * e] = __uint_as_float(kw[e] << 16);
-                    kx[2 * e + 1] = __uint_as_float(kw[e] & 0xFFFF0000u);
+                for (int i = 0; i < 4; ++i) {
+                    const unsigned kw = *reinterpret_cast<const unsigned*>(&sm.Kb[t0 + i][c]);
+                    kx[i][0] = __uint_as_float(kw << 16);
+                    kx[i][1] = __uint_as_float(kw & 0xFFFF0000u);
                 }
+                // A[r] = the erase vectors' cumulative gate of token t0 + r (c_t; i_t = c_{t+1}
+                // when the gate comes first); A[4] is the next token's
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float rho = sm.Ag[16 + E1][c + e];
-                    const float ct = sm.Ag[t + E1][c + e];
-                    gl[e] = kx[e] * exp2_raw(ct - rho);
-                    gr[e] = kx[e] * exp2_raw(rho - ct);
-                    gr1[e] = E1 ? gr[e] : kx[e] * exp2_raw(rho - sm.Ag[t + 1][c + e]);
+                for (int r = 0; r < 5; ++r) {
+                    const f32x2 a2 = *reinterpret_cast<const f32x2*>(&sm.Ag[t0 + r + E1 < CK ? t0 + r + E1 : CK][c]);
+                    A[r][0] = a2.x;
+                    A[r][1] = a2.y;
                 }
-                auto put = [&](uint16_t (*P)[CK][D + 8], const float* v) {
-                    unsigned h[4], l[4];
+                const f32x2 rho2 = *reinterpret_cast<const f32x2*>(&sm.Ag[16 + E1][c]);
+                const f32x2 bc2 = *reinterpret_cast<const f32x2*>(&sm.Ag[CK][c]);
+                const float rho[2] = {rho2.x, rho2.y}, bc[2] = {bc2.x, bc2.y};
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        h[e] = cvt2_bf16(v[2 * e], v[2 * e + 1]);
-                        const f32x2 hv = bf16x2_to_f32(h[e]);
-                        l[e] = cvt2_bf16(v[2 * e] - hv.x, v[2 * e + 1] - hv.y);
-                    }
-                    *reinterpret_cast<u32x4*>(&P[0][t][c]) = u32x4{h[0], h[1], h[2], h[3]};
-                    *reinterpret_cast<u32x4*>(&P[1][t][c]) = u32x4{l[0], l[1], l[2], l[3]};
+                for (int j = 0; j < 2; ++j) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) eg[i][j] = exp2_raw(A[i][j] - rho[j]);
+#pragma unroll
+                    for (int i = 0; i < 5; ++i) er[i][j] = (E1 && i == 4) ? 0.f : exp2_raw(rho[j] - A[i][j]);
+                    P[j] = exp2_raw(rho[j]);
+                    Q[j] = exp2_raw(bc[j] - rho[j]);
+                }
+                // e^{rho - i_t}: the next token's e^{rho - c} (gate after the erase); e^{rho - c_t}
+                // itself when the gate comes first (i = c for the erase vectors then)
+                auto er1 = [&](int i, int j) { return E1 ? er[i][j] : er[i + 1][j]; };
+                // Gram operands, token-major
+                auto put_tok = [&](uint16_t (*Pl)[CK][D + 8], int t, float x0, float x1) {
+                    const unsigned hw = cvt2_bf16(x0, x1);
+                    const f32x2 hv = bf16x2_to_f32(hw);
+                    *reinterpret_cast<unsigned*>(&Pl[0][t][c]) = hw;
+                    *reinterpret_cast<unsigned*>(&Pl[1][t][c]) = cvt2_bf16(x0 - hv.x, x1 - hv.y);
                 };
-                put(sm.u.g.GL, gl);
-                put(sm.u.g.GR, gr);
-                if (!E1) put(sm.u.g.GR1, gr1);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    put_tok(sm.u.g.GL, t0 + i, kx[i][0] * eg[i][0], kx[i][1] * eg[i][1]);
+                    put_tok(sm.u.g.GR, t0 + i, kx[i][0] * er[i][0], kx[i][1] * er[i][1]);
+                    if (!E1) put_tok(sm.u.g.GR1, t0 + i, kx[i][0] * er1(i, 0), kx[i][1] * er1(i, 1));
+                }
+                // key operands, channel-major: 4 consecutive tokens of one channel per store
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    float rm[4], kh[4], kp[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        rm[i] = kx[i][j] * eg[i][j] * P[j];
+                        kh[i] = kx[i][j] * er[i][j] * Q[j];
+                        kp[i] = kx[i][j] * er1(i, j) * Q[j];
+                    }
+                    unsigned rh[2], rl[2];
+#pragma unroll
+                    for (int p2 = 0; p2 < 2; ++p2) {
+                        rh[p2] = cvt2_bf16(rm[2 * p2], rm[2 * p2 + 1]);
+                        const f32x2 hv = bf16x2_to_f32(rh[p2]);
+                        rl[p2] = cvt2_bf16(rm[2 * p2] - hv.x, rm[2 * p2 + 1] - hv.y);
+                    }
+                    *reinterpret_cast<u32x2*>(&sm.rv.RmT[0][c + j][t0]) = u32x2{rh[0], rh[1]};
+                    *reinterpret_cast<u32x2*>(&sm.rv.RmT[1][c + j][t0]) = u32x2{rl[0], rl[1]};
+                    *reinterpret_cast<u32x2*>(&sm.KhT[c + j][t0]) = u32x2{cvt2_f16(kh[0], kh[1]), cvt2_f16(kh[2], kh[3])};
+                    *reinterpret_cast<u32x2*>(&sm.KhpT[c + j][t0]) = u32x2{cvt2_f16(kp[0], kp[1]), cvt2_f16(kp[2], kp[3])};
+                    if (t_live) {
+                        unsigned khh[2], khl[2];
+#pragma unroll
+                        for (int p2 = 0; p2 < 2; ++p2) {
+                            khh[p2] = cvt2_bf16(kh[2 * p2], kh[2 * p2 + 1]);
+                            const f32x2 hv = bf16x2_to_f32(khh[p2]);
+                            khl[p2] = cvt2_bf16(kh[2 * p2] - hv.x, kh[2 * p2 + 1] - hv.y);
+                        }
+                        *reinterpret_cast<u32x2*>(&sm.KhTb[0][c + j][t0]) = u32x2{khh[0], khh[1]};
+                        *reinterpret_cast<u32x2*>(&sm.KhTb[1][c + j][t0]) = u32x2{khl[0], khl[1]};
+                    }
+                }
             }
         }
         lds_barrier();
+        // the six Gram tiles Lp (waves 0-2) and L' (waves 3-5), bf16 hi + lo
         if (wave < 6) {
             const bool lp = wave < 3;
             const int tile = lp ? wave : wave - 3;
@@ -344,44 +401,6 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                 if (lp) sm.F1[tt][ss] = ss < tt ? sm.beta[tt] * acc[e] : 0.f;
                 else sm.F1p[tt][ss] = ss < tt ? acc[e] : 0.f;
             }
-        }
-        // decay-scaled key operands (channel-major, token-contiguous), spread over all waves
-        // (waves 6 and 7 start at once, the others after their Gram tile): item = (4-token
-        // group, channel), channel fastest, so a wave reads consecutive channels of a token row
-        // and writes 4 consecutive tokens of a channel row per store
-        for (int it = tid; it < D * (CK / 4); it += 512) {
-            const int c = it % D, t0 = 4 * (it / D);
-            const float bc = sm.Ag[CK][c];
-            unsigned rh[2], rl[2], kh16[2], khh[2], khl[2], kp16[2];
-#pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                float rm[2], kh[2], kp[2];
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int t = t0 + 2 * p + i;
-                    const float kx = bf(sm.Kb[t][c]);
-                    const float at = sm.Ag[t + E1][c], at1 = sm.Ag[t + 1][c];
-                    rm[i] = kx * exp2_raw(at);
-                    kh[i] = kx * exp2_raw(bc - at);
-                    kp[i] = kx * exp2_raw(bc - at1);
-                }
-                rh[p] = cvt2_bf16(rm[0], rm[1]);
-                rl[p] = cvt2_bf16(rm[0] - bf16x2_to_f32(rh[p]).x, rm[1] - bf16x2_to_f32(rh[p]).y);
-                if (t_live) {
-                    khh[p] = cvt2_bf16(kh[0], kh[1]);
-                    khl[p] = cvt2_bf16(kh[0] - bf16x2_to_f32(khh[p]).x, kh[1] - bf16x2_to_f32(khh[p]).y);
-                }
-                kh16[p] = cvt2_f16(kh[0], kh[1]);
-                kp16[p] = cvt2_f16(kp[0], kp[1]);
-            }
-            *reinterpret_cast<u32x2*>(&sm.rv.RmT[0][c][t0]) = u32x2{rh[0], rh[1]};
-            *reinterpret_cast<u32x2*>(&sm.rv.RmT[1][c][t0]) = u32x2{rl[0], rl[1]};
-            if (t_live) {
-                *reinterpret_cast<u32x2*>(&sm.KhTb[0][c][t0]) = u32x2{khh[0], khh[1]};
-                *reinterpret_cast<u32x2*>(&sm.KhTb[1][c][t0]) = u32x2{khl[0], khl[1]};
-            }
-            *reinterpret_cast<u32x2*>(&sm.KhT[c][t0]) = u32x2{kh16[0], kh16[1]};
-            *reinterpret_cast<u32x2*>(&sm.KhpT[c][t0]) = u32x2{kp16[0], kp16[1]};
         }
         lds_barrier();
 
