@@ -78,11 +78,13 @@ const char* hypic_last_error(void) { return g_last_error.c_str(); }
 
 size_t hypic_build_workspace_bytes(const hypic_dims* dims, int32_t n_seg, int64_t n_tokens)
 {
-    if (!dims || dims->n_heads < 1 || dims->d_k != dims->d_v || n_seg < 1 || n_tokens < 0) return 0;
-    if (!valid_d(dims->d_k) || dims->gate < HYPIC_GATE_HEAD || dims->gate > HYPIC_GATE_DIAG) return 0;
+    if (!dims || dims->n_heads < 1 || n_seg < 1 || n_tokens < 0) return 0;
+    if (!valid_d(dims->d_k) || !valid_d(dims->d_v) || dims->gate < HYPIC_GATE_HEAD || dims->gate > HYPIC_GATE_DIAG)
+        return 0;
     if (!dims->delta)
-        return hypic::decay_workspace_bytes(dims->d_k, dims->n_heads, n_seg, n_tokens, dims->gate == HYPIC_GATE_DIAG);
-    if (dims->gate != HYPIC_GATE_TOKEN || dims->in_dtype != HYPIC_BF16) return 0;
+        return hypic::decay_workspace_bytes(dims->d_k, dims->d_v, dims->n_heads, n_seg, n_tokens,
+                                            dims->gate == HYPIC_GATE_DIAG);
+    if (dims->d_k != dims->d_v || dims->gate != HYPIC_GATE_TOKEN || dims->in_dtype != HYPIC_BF16) return 0;
     return hypic::split_workspace_bytes(dims->d_k, dims->n_heads, n_seg, n_tokens);
 }
 
@@ -100,9 +102,10 @@ hypic_status hypic_segment_build(const hypic_dims* dims, int32_t n_seg, const in
     if (n_tokens > 0 && (!k || !v || !g)) return fail(HYPIC_E_INVALID, "k, v or g is NULL");
     if (dims->delta && n_tokens > 0 && !beta) return fail(HYPIC_E_INVALID, "beta is NULL with the delta rule");
     if ((long long)n_seg * dims->n_heads > kMaxGrid) return fail(HYPIC_E_INVALID, "n_seg * n_heads too large");
-    if (dims->d_k != dims->d_v) return fail(HYPIC_E_UNSUPPORTED, "d_k != d_v is not implemented");
     const bool bf16 = dims->in_dtype == HYPIC_BF16;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (dims->delta && dims->d_k != dims->d_v)
+        return fail(HYPIC_E_UNSUPPORTED, "the delta-rule builds need d_k == d_v");
     if (!dims->delta) {
         const size_t need = workspace ? hypic_build_workspace_bytes(dims, n_seg, n_tokens) : 0;
         if (need > 0) {
@@ -111,7 +114,7 @@ hypic_status hypic_segment_build(const hypic_dims* dims, int32_t n_seg, const in
             if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
                 return fail(HYPIC_E_INVALID, "workspace must be 256-byte aligned");
         }
-        return from_hip(hypic::build_decay(dims->d_k, bf16, dims->gate, n_seg, dims->n_heads, seg_begin, seg_end,
+        return from_hip(hypic::build_decay(dims->d_k, dims->d_v, bf16, dims->gate, n_seg, dims->n_heads, seg_begin, seg_end,
                                            n_tokens, k, v, g, T_out, dims->t_layout, S_out,
                                            need > 0 ? workspace : nullptr, st),
                         "hypic_segment_build");
@@ -191,8 +194,7 @@ hypic_status hypic_compose(const hypic_dims* dims, int32_t n_chain, int32_t n_st
                                               dims->n_heads, n_step, pair_id, n_pair,
                                               static_cast<const float*>(T_cache), S_cache, S_run, st),
                         "hypic_compose");
-    if (dims->d_k != dims->d_v) return fail(HYPIC_E_UNSUPPORTED, "d_k != d_v is not implemented");
-    return from_hip(hypic::compose_dense(dims->d_k, n_chain, dims->n_heads, n_step, pair_id, n_pair, T_cache,
+    return from_hip(hypic::compose_dense(dims->d_k, dims->d_v, n_chain, dims->n_heads, n_step, pair_id, n_pair, T_cache,
                                          dims->t_layout == HYPIC_T_SPLIT, S_cache, S_run, nullptr, st),
                     "hypic_compose");
 }
@@ -267,7 +269,7 @@ hypic_status hypic::seam_advance_with(const hypic_dims* dims, int32_t n_chain, i
     // blocked scan: block aggregates composed in order (the state entering every block
     // kept), then the windows of blocks >= 1 read out from those states
     float* trail = reinterpret_cast<float*>(ws + pl.trail_off);
-    e = hypic::compose_dense(d, n_chain, H, pl.nblk - 1, nullptr, n_chain * (pl.nblk - 1), sa.agg_T, true, sa.agg_S,
+    e = hypic::compose_dense(d, d, n_chain, H, pl.nblk - 1, nullptr, n_chain * (pl.nblk - 1), sa.agg_T, true, sa.agg_S,
                              S_run, trail, st);
     if (e != hipSuccess) return from_hip(e, "hypic_seam_advance (composition of the block aggregates)");
     return from_hip(hypic::seam_readout(d, n_chain, H, n_step, pl.nblk, pl.blk, w, seam_start, n_tokens, sa.ox, trail,

@@ -47,9 +47,10 @@ __host__ __device__ inline PieceRange piece_range(int64_t beg, int64_t end, int 
     }
     return r;
 }
-// workspace: piece states [n_seg][H][8][D][D] fp32, then piece log-decays [n_seg][H][8][D]
-__host__ __device__ inline size_t piece_log_offset(int n_seg, int H, int D) {
-    return (size_t)n_seg * H * kMaxPieces * D * D;
+// workspace: piece states [n_seg][H][8][DK][DV] fp32, then piece log-decays [n_seg][H][8][DK]
+// (one value per piece for scalar gates)
+__host__ __device__ inline size_t piece_log_offset(int n_seg, int H, int DK, int DV) {
+    return (size_t)n_seg * H * kMaxPieces * DK * DV;
 }
 
 // 8 consecutive values at element e (zeros when !on; the address is not formed then)
@@ -82,7 +83,7 @@ __device__ __forceinline__ float ld1(const void* base, size_t e) {
 }
 }  // namespace
 
-template <int D, bool BF16, int GATE, bool PIECES>
+template <int DK, int DV, bool BF16, int GATE, bool PIECES>
 __global__ __launch_bounds__(256) void build_decay_kernel(
     int n_seg, int H, const int64_t* __restrict__ seg_begin, const int64_t* __restrict__ seg_end,
     int64_t n_tokens, const void* __restrict__ k, const void* __restrict__ v,
@@ -90,18 +91,19 @@ __global__ __launch_bounds__(256) void build_decay_kernel(
     float* __restrict__ piece_ws)
 {
     constexpr bool DIAG = GATE == 2;       // per-channel gate: the weights move from V to K
-    constexpr int RT = D / 16;
-    constexpr int NT = RT * RT;            // output tiles
+    constexpr int RTK = DK / 16, RTV = DV / 16;
+    constexpr int NT = RTK * RTV;          // output tiles
     constexpr int TW = (NT + 3) / 4;       // tiles per wave
-    constexpr int CG = D / 8;              // 8-channel groups per token
-    constexpr int NIT = (CH * CG + 255) / 256;   // staging items per thread
+    constexpr int CGK = DK / 8, CGV = DV / 8;   // 8-channel groups per token
+    constexpr int CG = CGK > CGV ? CGK : CGV;
+    constexpr int NIT = (CH * CGK + 255) / 256;   // gate staging items per thread
     constexpr bool KSPLIT = !BF16 || DIAG; // keys need a lo plane (fp32, or weighted per channel)
     constexpr bool VSPLIT = !BF16 || !DIAG;
-    __shared__ __attribute__((aligned(16))) uint16_t Kt[2][D][LDT];   // K^T (hi, lo); DIAG: weighted
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D][LDT];   // V^T (hi, lo); scalar: weighted
+    __shared__ __attribute__((aligned(16))) uint16_t Kt[2][DK][LDT];  // K^T (hi, lo); DIAG: weighted
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[2][DV][LDT];  // V^T (hi, lo); scalar: weighted
     __shared__ float gsh[CH], wsh[CH];
-    __shared__ float gd[DIAG ? CH : 1][DIAG ? D + 1 : 1];   // DIAG: gates, then in-chunk cumulative sums
-    __shared__ float bcd[DIAG ? D : 1], logd[DIAG ? D : 1];  // DIAG: chunk total and segment total per channel
+    __shared__ float gd[DIAG ? CH : 1][DIAG ? DK + 1 : 1];   // DIAG: gates, then in-chunk cumulative sums
+    __shared__ float bcd[DIAG ? DK : 1], logd[DIAG ? DK : 1];  // DIAG: chunk total and segment total per key channel
     __shared__ float bCs;
 
     // PIECES: one workgroup per (segment, head, piece); the piece's pair goes to the
@@ -125,9 +127,9 @@ __global__ __launch_bounds__(256) void build_decay_kernel(
     for (int i = 0; i < TW; ++i) acc[i] = zero4();
     float log_t = 0.f;
     const float ghead = GATE == 0 ? reinterpret_cast<const float*>(gl)[h] : 0.f;
-    const size_t stride = (size_t)H * D;
+    const size_t stride_k = (size_t)H * DK, stride_v = (size_t)H * DV;
     if constexpr (DIAG) {
-        for (int ch = tid; ch < D; ch += 256) logd[ch] = 0.f;
+        for (int ch = tid; ch < DK; ch += 256) logd[ch] = 0.f;
     }
 
     for (int64_t c0 = beg; c0 < end; c0 += CH) {
@@ -139,19 +141,19 @@ __global__ __launch_bounds__(256) void build_decay_kernel(
                 float gx[NIT][8];
 #pragma unroll
                 for (int r = 0; r < NIT; ++r) {
-                    const int it = tid + 256 * r, t = it / CG, c8 = (it % CG) * 8;
-                    load8<BF16>(gl, (size_t)(c0 + t) * stride + (size_t)h * D + c8, it < CH * CG && t < n, gx[r]);
+                    const int it = tid + 256 * r, t = it / CGK, c8 = (it % CGK) * 8;
+                    load8<BF16>(gl, (size_t)(c0 + t) * stride_k + (size_t)h * DK + c8, it < CH * CGK && t < n, gx[r]);
                 }
 #pragma unroll
                 for (int r = 0; r < NIT; ++r) {
-                    const int it = tid + 256 * r, t = it / CG, c8 = (it % CG) * 8;
-                    if (it < CH * CG)
+                    const int it = tid + 256 * r, t = it / CGK, c8 = (it % CGK) * 8;
+                    if (it < CH * CGK)
 #pragma unroll
                         for (int e = 0; e < 8; ++e) gd[t][c8 + e] = gx[r][e];
                 }
             }
             __syncthreads();
-            for (int ch = tid; ch < D; ch += 256) {
+            for (int ch = tid; ch < DK; ch += 256) {
                 float x = 0.f;
                 for (int t = 0; t < CH; ++t) {
                     x += gd[t][ch];
@@ -180,19 +182,20 @@ __global__ __launch_bounds__(256) void build_decay_kernel(
             }
         }
         __syncthreads();
-        {   // item: 4 tokens x 8 channels (4 loads of 8 channels), written as 4-token runs of 8
-            // channel rows of K^T and V^T; the token block is fastest across lanes, so the runs of
-            // one row from 16 lanes are contiguous
+        {   // item: 4 tokens x 8 channels (4 loads of 8 key and 8 value channels), written as
+            // 4-token runs of 8 channel rows of K^T and V^T; the token block is fastest across lanes,
+            // so the runs of one row from 16 lanes are contiguous.  With d_k != d_v the items past
+            // the smaller dimension load and write only the other.
             constexpr int NTB = CH / 4, NI = NTB * CG;
             for (int it = tid; it < NI; it += 256) {
                 const int tb = it % NTB, c8 = (it / NTB) * 8;
+                const bool hk = c8 < DK, hv = c8 < DV;
                 float kx[4][8], vx[4][8];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int t = 4 * tb + r;
-                    const size_t e = (size_t)(c0 + t) * stride + (size_t)h * D + c8;
-                    load8<BF16>(k, e, t < n, kx[r]);
-                    load8<BF16>(v, e, t < n, vx[r]);
+                    load8<BF16>(k, (size_t)(c0 + t) * stride_k + (size_t)h * DK + c8, hk && t < n, kx[r]);
+                    load8<BF16>(v, (size_t)(c0 + t) * stride_v + (size_t)h * DV + c8, hv && t < n, vx[r]);
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -200,8 +203,11 @@ __global__ __launch_bounds__(256) void build_decay_kernel(
                     if (t < n) {
 #pragma unroll
                         for (int x = 0; x < 8; ++x) {
-                            if constexpr (DIAG) kx[r][x] *= expf(bcd[c8 + x] - gd[t][c8 + x]);   // channel decays by e^{b_C - b_t}
-                            else vx[r][x] *= wsh[t];
+                            if constexpr (DIAG) {   // channel decays by e^{b_C - b_t}
+                                if (hk) kx[r][x] *= expf(bcd[c8 + x] - gd[t][c8 + x]);
+                            } else {
+                                vx[r][x] *= wsh[t];
+                            }
                         }
                     }
                 }
@@ -217,10 +223,14 @@ __global__ __launch_bounds__(256) void build_decay_kernel(
                         const f32x2 vf = bf16x2_to_f32(vh[r]);
                         vl[r] = cvt2_bf16(vx[2 * r][x] - vf.x, vx[2 * r + 1][x] - vf.y);
                     }
-                    *reinterpret_cast<u32x2*>(&Kt[0][c8 + x][4 * tb]) = u32x2{kh[0], kh[1]};
-                    *reinterpret_cast<u32x2*>(&Kt[1][c8 + x][4 * tb]) = u32x2{kl[0], kl[1]};
-                    *reinterpret_cast<u32x2*>(&Vt[0][c8 + x][4 * tb]) = u32x2{vh[0], vh[1]};
-                    *reinterpret_cast<u32x2*>(&Vt[1][c8 + x][4 * tb]) = u32x2{vl[0], vl[1]};
+                    if (hk) {
+                        *reinterpret_cast<u32x2*>(&Kt[0][c8 + x][4 * tb]) = u32x2{kh[0], kh[1]};
+                        *reinterpret_cast<u32x2*>(&Kt[1][c8 + x][4 * tb]) = u32x2{kl[0], kl[1]};
+                    }
+                    if (hv) {
+                        *reinterpret_cast<u32x2*>(&Vt[0][c8 + x][4 * tb]) = u32x2{vh[0], vh[1]};
+                        *reinterpret_cast<u32x2*>(&Vt[1][c8 + x][4 * tb]) = u32x2{vl[0], vl[1]};
+                    }
                 }
             }
         }
@@ -230,7 +240,7 @@ __global__ __launch_bounds__(256) void build_decay_kernel(
         for (int i = 0; i < TW; ++i) {
             const int tile = wave + 4 * i;
             if (tile >= NT) continue;
-            const int mt = tile / RT, nt = tile % RT;  // key-channel tile, value-channel tile
+            const int mt = tile / RTV, nt = tile % RTV;  // key-channel tile, value-channel tile
             f32x4 a;
             if constexpr (DIAG) {   // row (key channel) m decays by e^{b_C[m]}
 #pragma unroll
@@ -260,19 +270,19 @@ __global__ __launch_bounds__(256) void build_decay_kernel(
 
     const size_t pair = (size_t)seg * H + h;
     const size_t slot = PIECES ? pair * kMaxPieces + piece : pair;
-    float* S = (PIECES ? piece_ws : S_out) + slot * D * D;
+    float* S = (PIECES ? piece_ws : S_out) + slot * DK * DV;
 #pragma unroll
     for (int i = 0; i < TW; ++i) {
         const int tile = wave + 4 * i;
         if (tile >= NT) continue;
-        const int mt = tile / RT, nt = tile % RT;
+        const int mt = tile / RTV, nt = tile % RTV;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) S[(size_t)(mt * 16 + 4 * g4 + e) * D + nt * 16 + n16] = acc[i][e];
+        for (int e = 0; e < 4; ++e) S[(size_t)(mt * 16 + 4 * g4 + e) * DV + nt * 16 + n16] = acc[i][e];
     }
     if constexpr (PIECES) {   // the piece's log-decay (per key channel for the diagonal gate)
-        float* L = piece_ws + piece_log_offset(n_seg, H, D) + slot * (DIAG ? D : 1);
+        float* L = piece_ws + piece_log_offset(n_seg, H, DK, DV) + slot * (DIAG ? DK : 1);
         if constexpr (DIAG) {
-            for (int ch = tid; ch < D; ch += 256) L[ch] = logd[ch];
+            for (int ch = tid; ch < DK; ch += 256) L[ch] = logd[ch];
         } else {
             if (tid == 0) L[0] = log_t;
         }
@@ -281,18 +291,18 @@ __global__ __launch_bounds__(256) void build_decay_kernel(
     if (T_out) {
         if constexpr (DIAG) {
             if (t_layout == 3) {   // diagonal
-                for (int ch = tid; ch < D; ch += 256) reinterpret_cast<float*>(T_out)[pair * D + ch] = expf(logd[ch]);
+                for (int ch = tid; ch < DK; ch += 256) reinterpret_cast<float*>(T_out)[pair * DK + ch] = expf(logd[ch]);
             } else {               // dense diag(t), fp32 or bf16 hi/lo planes
-                for (int it = tid; it < D * D; it += 256)
-                    put_t(T_out, t_layout == 2, pair, D, it / D, it % D, (it / D == it % D) ? expf(logd[it / D]) : 0.f);
+                for (int it = tid; it < DK * DK; it += 256)
+                    put_t(T_out, t_layout == 2, pair, DK, it / DK, it % DK, (it / DK == it % DK) ? expf(logd[it / DK]) : 0.f);
             }
         } else {
             const float tval = expf(log_t);
             if (t_layout == 1) {   // scalar
                 if (tid == 0) reinterpret_cast<float*>(T_out)[pair] = tval;
             } else {               // dense t I, fp32 or bf16 hi/lo planes
-                for (int it = tid; it < D * D; it += 256)
-                    put_t(T_out, t_layout == 2, pair, D, it / D, it % D, (it / D == it % D) ? tval : 0.f);
+                for (int it = tid; it < DK * DK; it += 256)
+                    put_t(T_out, t_layout == 2, pair, DK, it / DK, it % DK, (it / DK == it % DK) ? tval : 0.f);
             }
         }
     }
@@ -302,7 +312,7 @@ __global__ __launch_bounds__(256) void build_decay_kernel(
 // T = prod_p t_p, with t_p = e^{(log-decay of piece p)} a scalar, or per key channel (row of S)
 // for the diagonal gate.  One workgroup per (segment, head); 4 consecutive entries of one row per
 // thread and step.  A segment without tokens gets the identity pair.
-template <int D, bool DIAG>
+template <int DK, int DV, bool DIAG>
 __global__ __launch_bounds__(256) void decay_fold_kernel(int n_seg, int H, const int64_t* __restrict__ seg_begin,
                                                          const int64_t* __restrict__ seg_end, int64_t n_tokens,
                                                          const float* __restrict__ piece_ws, void* __restrict__ T_out,
@@ -315,16 +325,16 @@ __global__ __launch_bounds__(256) void decay_fold_kernel(int n_seg, int H, const
     end = end < beg ? beg : (end > n_tokens ? n_tokens : end);
     const int np = piece_range(beg, end, 0).n_pieces;
     const size_t pair = (size_t)seg * H + h;
-    const float* Lg = piece_ws + piece_log_offset(n_seg, H, D) + pair * kMaxPieces * (DIAG ? D : 1);
-    const f32x4* Sp = reinterpret_cast<const f32x4*>(piece_ws + pair * kMaxPieces * D * D);
-    f32x4* S = reinterpret_cast<f32x4*>(S_out + pair * D * D);
-    constexpr int NQ = D * D / 4;
+    const float* Lg = piece_ws + piece_log_offset(n_seg, H, DK, DV) + pair * kMaxPieces * (DIAG ? DK : 1);
+    const f32x4* Sp = reinterpret_cast<const f32x4*>(piece_ws + pair * kMaxPieces * DK * DV);
+    f32x4* S = reinterpret_cast<f32x4*>(S_out + pair * DK * DV);
+    constexpr int NQ = DK * DV / 4;
     // weight of piece p for row r: e^{log-decay of the pieces after p} (one row for scalar T)
-    __shared__ float wt[kMaxPieces][DIAG ? D : 1];
-    for (int r = tid; r < (DIAG ? D : 1); r += 256) {
+    __shared__ float wt[kMaxPieces][DIAG ? DK : 1];
+    for (int r = tid; r < (DIAG ? DK : 1); r += 256) {
         float l[kMaxPieces];
 #pragma unroll
-        for (int p = 0; p < kMaxPieces; ++p) l[p] = p < np ? Lg[p * (DIAG ? D : 1) + r] : 0.f;
+        for (int p = 0; p < kMaxPieces; ++p) l[p] = p < np ? Lg[p * (DIAG ? DK : 1) + r] : 0.f;
         float lsum = 0.f;
 #pragma unroll
         for (int p = kMaxPieces - 1; p >= 0; --p) {
@@ -334,7 +344,7 @@ __global__ __launch_bounds__(256) void decay_fold_kernel(int n_seg, int H, const
     }
     __syncthreads();
     for (int q = tid; q < NQ; q += 256) {
-        const int row = DIAG ? 4 * q / D : 0;
+        const int row = DIAG ? 4 * q / DV : 0;   // key channel of the 4 entries
         f32x4 sp[kMaxPieces];
 #pragma unroll
         for (int p = 0; p < kMaxPieces; ++p) sp[p] = p < np ? Sp[(size_t)p * NQ + q] : zero4();
@@ -346,18 +356,18 @@ __global__ __launch_bounds__(256) void decay_fold_kernel(int n_seg, int H, const
     }
     if (T_out) {
         if constexpr (DIAG) {
-            for (int ch = tid; ch < D; ch += 256) {
+            for (int ch = tid; ch < DK; ch += 256) {
                 float l = 0.f;
-                for (int p = 0; p < np; ++p) l += Lg[p * D + ch];
-                if (t_layout == 3) reinterpret_cast<float*>(T_out)[pair * D + ch] = __expf(l);
+                for (int p = 0; p < np; ++p) l += Lg[p * DK + ch];
+                if (t_layout == 3) reinterpret_cast<float*>(T_out)[pair * DK + ch] = __expf(l);
             }
             if (t_layout != 3) {   // dense diag(t), fp32 or bf16 hi/lo planes
-                for (int it = tid; it < D * D; it += 256) {
-                    const int r = it / D, c = it % D;
+                for (int it = tid; it < DK * DK; it += 256) {
+                    const int r = it / DK, c = it % DK;
                     float l = 0.f;
                     if (r == c)
-                        for (int p = 0; p < np; ++p) l += Lg[p * D + r];
-                    put_t(T_out, t_layout == 2, pair, D, r, c, r == c ? __expf(l) : 0.f);
+                        for (int p = 0; p < np; ++p) l += Lg[p * DK + r];
+                    put_t(T_out, t_layout == 2, pair, DK, r, c, r == c ? __expf(l) : 0.f);
                 }
             }
         } else {
@@ -367,54 +377,56 @@ __global__ __launch_bounds__(256) void decay_fold_kernel(int n_seg, int H, const
             if (t_layout == 1) {   // scalar
                 if (tid == 0) reinterpret_cast<float*>(T_out)[pair] = tval;
             } else {               // dense t I, fp32 or bf16 hi/lo planes
-                for (int it = tid; it < D * D; it += 256)
-                    put_t(T_out, t_layout == 2, pair, D, it / D, it % D, (it / D == it % D) ? tval : 0.f);
+                for (int it = tid; it < DK * DK; it += 256)
+                    put_t(T_out, t_layout == 2, pair, DK, it / DK, it % DK, (it / DK == it % DK) ? tval : 0.f);
             }
         }
     }
 }
 
-template <int D, bool BF16, int GATE>
+template <int DK, int DV, bool BF16, int GATE>
 static hipError_t launch_decay(int n_seg, int H, const int64_t* sb, const int64_t* se, int64_t n_tok,
                                const void* k, const void* v, const void* g, void* T_out, int t_layout,
                                float* S_out, float* ws, hipStream_t st)
 {
     if (ws == nullptr) {
-        hipLaunchKernelGGL((build_decay_kernel<D, BF16, GATE, false>), dim3(n_seg * H), dim3(256), 0, st, n_seg, H,
-                           sb, se, n_tok, k, v, g, T_out, t_layout, S_out, nullptr);
+        hipLaunchKernelGGL((build_decay_kernel<DK, DV, BF16, GATE, false>), dim3(n_seg * H), dim3(256), 0, st, n_seg,
+                           H, sb, se, n_tok, k, v, g, T_out, t_layout, S_out, nullptr);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((build_decay_kernel<D, BF16, GATE, true>), dim3(n_seg * H * kMaxPieces), dim3(256), 0, st,
-                       n_seg, H, sb, se, n_tok, k, v, g, T_out, t_layout, S_out, ws);
+    hipLaunchKernelGGL((build_decay_kernel<DK, DV, BF16, GATE, true>), dim3(n_seg * H * kMaxPieces), dim3(256), 0,
+                       st, n_seg, H, sb, se, n_tok, k, v, g, T_out, t_layout, S_out, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decay_fold_kernel<D, GATE == 2>), dim3(n_seg * H), dim3(256), 0, st, n_seg, H, sb, se, n_tok,
-                       ws, T_out, t_layout, S_out);
+    hipLaunchKernelGGL((decay_fold_kernel<DK, DV, GATE == 2>), dim3(n_seg * H), dim3(256), 0, st, n_seg, H, sb, se,
+                       n_tok, ws, T_out, t_layout, S_out);
     return hipGetLastError();
 }
 
-size_t decay_workspace_bytes(int d, int H, int n_seg, int64_t n_tokens, bool diag)
+size_t decay_workspace_bytes(int dk, int dv, int H, int n_seg, int64_t n_tokens, bool diag)
 {
     // pieces pay where segments average at least 4 chunks (256 tokens)
     if (n_seg < 1 || H < 1 || n_tokens < (int64_t)n_seg * 4 * CH) return 0;
-    return ((size_t)n_seg * H * kMaxPieces * ((size_t)d * d + (diag ? d : 1)) * sizeof(float) + 255) / 256 * 256;
+    return ((size_t)n_seg * H * kMaxPieces * ((size_t)dk * dv + (diag ? dk : 1)) * sizeof(float) + 255) / 256 * 256;
 }
 
-hipError_t build_decay(int d, bool in_bf16, int gate, int n_seg, int H, const int64_t* sb,
+hipError_t build_decay(int dk, int dv, bool in_bf16, int gate, int n_seg, int H, const int64_t* sb,
                        const int64_t* se, int64_t n_tok, const void* k, const void* v, const void* g,
                        void* T_out, int t_layout, float* S_out, void* ws, hipStream_t st)
 {
     float* w = static_cast<float*>(ws);
-#define HYPIC_GATES(D_, B_)                                                                                     \
-    if (gate == 0) return launch_decay<D_, B_, 0>(n_seg, H, sb, se, n_tok, k, v, g, T_out, t_layout, S_out, w, st); \
-    if (gate == 1) return launch_decay<D_, B_, 1>(n_seg, H, sb, se, n_tok, k, v, g, T_out, t_layout, S_out, w, st); \
-    return launch_decay<D_, B_, 2>(n_seg, H, sb, se, n_tok, k, v, g, T_out, t_layout, S_out, w, st);
-#define HYPIC_CASE(D_)                    \
-    if (d == D_) {                        \
-        if (in_bf16) { HYPIC_GATES(D_, true) } \
-        HYPIC_GATES(D_, false)            \
+#define HYPIC_GATES(DK_, DV_, B_)                                                                             \
+    if (gate == 0) return launch_decay<DK_, DV_, B_, 0>(n_seg, H, sb, se, n_tok, k, v, g, T_out, t_layout, S_out, w, st); \
+    if (gate == 1) return launch_decay<DK_, DV_, B_, 1>(n_seg, H, sb, se, n_tok, k, v, g, T_out, t_layout, S_out, w, st); \
+    return launch_decay<DK_, DV_, B_, 2>(n_seg, H, sb, se, n_tok, k, v, g, T_out, t_layout, S_out, w, st);
+#define HYPIC_CASE(DK_, DV_)                        \
+    if (dk == DK_ && dv == DV_) {                   \
+        if (in_bf16) { HYPIC_GATES(DK_, DV_, true) } \
+        HYPIC_GATES(DK_, DV_, false)                \
     }
-    HYPIC_CASE(16) HYPIC_CASE(32) HYPIC_CASE(64) HYPIC_CASE(128)
+#define HYPIC_ROW(DK_) HYPIC_CASE(DK_, 16) HYPIC_CASE(DK_, 32) HYPIC_CASE(DK_, 64) HYPIC_CASE(DK_, 128)
+    HYPIC_ROW(16) HYPIC_ROW(32) HYPIC_ROW(64) HYPIC_ROW(128)
+#undef HYPIC_ROW
 #undef HYPIC_CASE
 #undef HYPIC_GATES
     return hipErrorNotSupported;

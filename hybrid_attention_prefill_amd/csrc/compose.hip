@@ -584,10 +584,23 @@ static int pick_nb(long long n_units, int dv)
     return nb;
 }
 
-hipError_t compose_dense(int d, int n_chain, int H, int n_step, const int32_t* pair_id, int n_pair,
+hipError_t compose_dense(int dk, int dv, int n_chain, int H, int n_step, const int32_t* pair_id, int n_pair,
                          const void* Tc, bool t_split, const float* Sc, float* Srun, float* trail,
                          hipStream_t st)
 {
+    if (dk != dv) {   // rectangular states: 16-column blocks
+#define HYPIC_RECT(DK_, DV_)                                                                                   \
+    if (dk == DK_ && dv == DV_)                                                                                \
+        return t_split ? launch_dense<DK_, DV_, 16, true>(n_chain, H, n_step, pair_id, n_pair, Tc, Sc, Srun, trail, st) \
+                       : launch_dense<DK_, DV_, 16, false>(n_chain, H, n_step, pair_id, n_pair, Tc, Sc, Srun, trail, st);
+        HYPIC_RECT(16, 32) HYPIC_RECT(16, 64) HYPIC_RECT(16, 128)
+        HYPIC_RECT(32, 16) HYPIC_RECT(32, 64) HYPIC_RECT(32, 128)
+        HYPIC_RECT(64, 16) HYPIC_RECT(64, 32) HYPIC_RECT(64, 128)
+        HYPIC_RECT(128, 16) HYPIC_RECT(128, 32) HYPIC_RECT(128, 64)
+#undef HYPIC_RECT
+        return hipErrorInvalidValue;
+    }
+    const int d = dk;
     const int nb = pick_nb((long long)n_chain * H, d);
     if (d == 128 && nb == 128 && trail == nullptr) {
         const int n_units = n_chain * H;

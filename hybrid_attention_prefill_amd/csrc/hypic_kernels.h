@@ -35,10 +35,10 @@ struct SeamPlan {
 };
 
 // compose.hip
-// t_split: T as bf16 hi/lo planes [n_pair][H][2][d][d]; else fp32 [n_pair][H][d][d]
-// pair_id NULL: step j of chain c applies pair c * n_step + j.  trail (may be NULL): the
-// state before each step, fp32 [n_chain][n_step][H][d][d].
-hipError_t compose_dense(int d, int n_chain, int H, int n_step, const int32_t* pair_id, int n_pair,
+// t_split: T as bf16 hi/lo planes [n_pair][H][2][dk][dk]; else fp32 [n_pair][H][dk][dk];
+// S fp32 [n_pair][H][dk][dv].  pair_id NULL: step j of chain c applies pair c * n_step + j.
+// trail (may be NULL): the state before each step, fp32 [n_chain][n_step][H][dk][dv].
+hipError_t compose_dense(int dk, int dv, int n_chain, int H, int n_step, const int32_t* pair_id, int n_pair,
                          const void* Tc, bool t_split, const float* Sc, float* Srun, float* trail,
                          hipStream_t st);
 // diag: T cached as fp32 [n_pair][H][dk] (T = diag(t)); else fp32 [n_pair][H] (T = t I)
@@ -85,8 +85,8 @@ hipError_t build_kda(int d, bool in_bf16, bool gate_first, int n_seg, int H, con
 // t_layout: 0 dense f32, 1 scalar, 2 dense bf16 hi/lo planes, 3 diagonal.  ws (may be NULL):
 // decay_workspace_bytes(...) bytes; segments are then built as up to 8 pieces in parallel
 // and the pieces composed.  The bytes are 0 where pieces would not pay.
-size_t decay_workspace_bytes(int d, int H, int n_seg, int64_t n_tokens, bool diag);
-hipError_t build_decay(int d, bool in_bf16, int gate, int n_seg, int H, const int64_t* sb,
+size_t decay_workspace_bytes(int dk, int dv, int H, int n_seg, int64_t n_tokens, bool diag);
+hipError_t build_decay(int dk, int dv, bool in_bf16, int gate, int n_seg, int H, const int64_t* sb,
                        const int64_t* se, int64_t n_tok, const void* k, const void* v, const void* g,
                        void* T_out, int t_layout, float* S_out, void* ws, hipStream_t st);
 

@@ -129,10 +129,11 @@ typedef struct {
  *                        length only, so its pair does not depend on the other segments
  *                        of the call.  Without it (or where the query returns 0) every
  *                        segment is one serial chain.
- * Implemented (d_k == d_v = d):
- *   gate HEAD, TOKEN or DIAG, delta 0 : d in {16, 32, 64, 128}, fp32 or bf16 inputs;
- *   gate TOKEN, delta 1 or 2    : d = 16 (fp32 or bf16), 64 or 128 (bf16);
- *   gate DIAG,  delta 1 or 2    : d = 64 or 128, bf16 inputs.
+ * Implemented:
+ *   gate HEAD, TOKEN or DIAG, delta 0 : any d_k and d_v in {16, 32, 64, 128}, fp32 or
+ *                                 bf16 inputs;
+ *   gate TOKEN, delta 1 or 2    : d_k == d_v = 16 (fp32 or bf16), 64 or 128 (bf16);
+ *   gate DIAG,  delta 1 or 2    : d_k == d_v = 64 or 128, bf16 inputs.
  * Other combinations return HYPIC_E_UNSUPPORTED.  For the delta-rule kernels
  * the state and values must stay within fp16 range (|entries| < 6e4): they are
  * fp16 operands of the matrix products (v itself with the scalar gate, beta * v
@@ -190,8 +191,7 @@ hypic_status hypic_segment_prefill(const hypic_dims* dims, int32_t n_seg,
  * linear layer; several layers go in one call as separate chains whose ids
  * index that layer's part of the caches.
  *   pair_id : int32 [n_chain][n_step]
- *   T_cache : in the dims' t_layout (any of the four; DENSE and SPLIT need
- *             d_k == d_v)
+ *   T_cache : in the dims' t_layout (any of the four, any d_k and d_v)
  *   S_run   : fp32 [n_chain][H][d_k][d_v], read and written in place
  */
 hypic_status hypic_compose(const hypic_dims* dims, int32_t n_chain, int32_t n_step,

@@ -47,6 +47,28 @@ def test_compose_matches_oracle(d, H, n_chain, n_step, layout):
 
 
 @pytest.mark.parametrize("layout", [hb.T_DENSE, hb.T_SPLIT])
+@pytest.mark.parametrize("dk,dv", [(16, 128), (32, 64), (64, 16), (128, 32), (128, 64), (64, 128)])
+def test_compose_rectangular_state(dk, dv, layout):
+    """d_k != d_v: T is d_k x d_k, S and the running state d_k x d_v."""
+    print(f"compose dk={dk} dv={dv} layout={layout}", flush=True)
+    H, n_chain, n_step, n_pair = 3, 2, 12, 7
+    rng = np.random.default_rng(dk * 131 + dv)
+    T = rng.standard_normal((n_pair, H, dk, dk)) / np.sqrt(dk)
+    T *= 0.9 / np.linalg.norm(T, ord=2, axis=(-2, -1))[..., None, None]
+    T = T.astype(np.float32)
+    S = rng.standard_normal((n_pair, H, dk, dv)).astype(np.float32)
+    Tc, Tv = _t_cache(T, layout)
+    ids = rng.integers(-1, n_pair, size=(n_chain, n_step)).astype(np.int32)
+    R0 = rng.standard_normal((n_chain, H, dk, dv)).astype(np.float32)
+    ref = oracle.compose(Tv, S, ids, R0)
+    Rg = dev(R0, torch.float32)
+    hb.compose(Tc, dev(S, torch.float32), dev(ids, torch.int32), Rg)
+    torch.cuda.synchronize()
+    err = rel_f(Rg.cpu().numpy(), ref)
+    assert err.max() < 1e-4, err.max()
+
+
+@pytest.mark.parametrize("layout", [hb.T_DENSE, hb.T_SPLIT])
 def test_compose_many_chains_full_width(layout):
     """Enough (chain, head) units for the full-width column block (the batched path)."""
     d, H, n_chain, n_step, n_pair = 128, 16, 64, 3, 5

@@ -215,3 +215,49 @@ def test_decay_build_in_pieces(name, in_dtype, t_layout):
     Ta, Sa = build(begin[3:4], end[3:4], ws)
     assert np.array_equal(Sa[0], Sb[3])
     assert torch.equal(Ta[0], Tb[3])
+
+
+@pytest.mark.parametrize("ws", ["auto", None])
+@pytest.mark.parametrize("dk,dv", [(16, 64), (128, 32), (64, 128)])
+@pytest.mark.parametrize("gate", [hb.GATE_HEAD, hb.GATE_TOKEN, hb.GATE_DIAG])
+def test_decay_build_rectangular_state(gate, dk, dv, ws):
+    """d_k != d_v without the erase (RetNet-, Mamba2- and GLA-style gates), bf16 inputs:
+    every pair against the oracle, with and without the pieces workspace, then the pairs
+    composed in order (scalar or diagonal T) against the full recurrence over the segments."""
+    print(f"rectangular gate={gate} dk={dk} dv={dv} ws={ws}", flush=True)
+    rng = np.random.default_rng(1000 * gate + dk + dv)
+    H = 2
+    lens = np.array([600, 333, 1, 0, 366])
+    N = int(lens.sum())
+    begin = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    end = begin + lens
+    kx = rng.standard_normal((N, H, dk))
+    k = wl.round_bf16(kx / np.linalg.norm(kx, axis=-1, keepdims=True))
+    v = wl.round_bf16(rng.standard_normal((N, H, dv)))
+    beta = None
+    if gate == hb.GATE_HEAD:
+        g = np.log1p(-np.exp2(-5.0 - np.arange(H))).astype(np.float32)
+        gt = torch.float32
+        t_layout = hb.T_SCALAR
+    elif gate == hb.GATE_TOKEN:
+        g = wl.round_bf16(-0.1 * np.logaddexp(0.0, rng.standard_normal((N, H))))
+        gt = torch.bfloat16
+        t_layout = hb.T_SCALAR
+    else:
+        g = wl.round_bf16(-np.logaddexp(0.0, rng.standard_normal((N, H, dk))) / 16.0)
+        gt = torch.bfloat16
+        t_layout = hb.T_DIAG
+    kd, vd, gd = dev(k, torch.bfloat16), dev(v, torch.bfloat16), dev(g, gt)
+    sb, se = dev(begin, torch.int64), dev(end, torch.int64)
+    T, S = hb.segment_build(kd, vd, gd, None, sb, se, gate=gate, delta=0, t_layout=t_layout, workspace=ws)
+    torch.cuda.synchronize()
+    T0, S0 = oracle.segment_build(k, v, g, None, begin, end, gate=gate, delta=0)
+    Sg = S.cpu().numpy()
+    assert np.all(np.isfinite(Sg))
+    assert rel_f(Sg, S0).max() <= TOL["bf16"]
+    assert rel_f(_dense(T, t_layout, dk), T0).max() <= TOL["bf16"]
+    R = torch.zeros((1, H, dk, dv), device="cuda")
+    hb.compose(T, S, dev(np.arange(len(lens), dtype=np.int32)[None, :], torch.int32), R)
+    torch.cuda.synchronize()
+    full, _ = oracle.run(k, v, g, None, gate=gate, delta=0)
+    assert rel_f(R.cpu().numpy()[0], full).max() <= TOL["bf16"]
