@@ -1106,6 +1106,9 @@ hipError_t build_gdn(int d, bool in_bf16, int n_seg, int H, const int64_t* sb, c
     HYPIC_GDN(64, 1, true, true)
     HYPIC_GDN(16, 2, false, false)
     HYPIC_GDN(16, 1, true, false)
+    HYPIC_GDN(32, 1, true, false)
+    HYPIC_GDN(32, 2, false, false)
+    HYPIC_GDN(64, 2, false, false)
 #undef HYPIC_GDN
     return hipErrorNotSupported;
 }

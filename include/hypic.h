@@ -132,7 +132,8 @@ typedef struct {
  * Implemented:
  *   gate HEAD, TOKEN or DIAG, delta 0 : any d_k and d_v in {16, 32, 64, 128}, fp32 or
  *                                 bf16 inputs;
- *   gate TOKEN, delta 1 or 2    : d_k == d_v = 16 (fp32 or bf16), 64 or 128 (bf16);
+ *   gate TOKEN, delta 1 or 2    : d_k == d_v = 16, 32 or 64 (fp32 or bf16), 128 (bf16;
+ *                                 fp32 at 128 would need 250 KiB of LDS);
  *   gate DIAG,  delta 1 or 2    : d_k == d_v = 64 or 128, bf16 inputs.
  * Other combinations return HYPIC_E_UNSUPPORTED.  For the delta-rule kernels
  * the state and values must stay within fp16 range (|entries| < 6e4): they are

@@ -378,3 +378,23 @@ def test_values_beyond_fp16_range_give_non_finite_S(name, kw, bad, mag):
         _, Sr = oracle.segment_build(W.k[b:e, 0:1], vb, W.g[b:e, 0:1], W.beta[b:e, 0:1], [0], [e - b],
                                      gate=W.gate, delta=True)
         assert rel_f(S1[0:1, 0:1].cpu().numpy(), Sr).max() <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("stress", [False, True])
+@pytest.mark.parametrize("name,d,tol", [("gdn-16h-d128-32k", 32, "bf16"), ("gdn-tiny-f32", 32, "f32"),
+                                        ("gdn-tiny-f32", 64, "f32")])
+def test_gdn_d32_and_fp32_d64(name, d, tol, stress):
+    """The gated delta rule at d = 32 (bf16 and fp32 inputs) and d = 64 with fp32 inputs
+    (fp16 hi + lo operands): ragged, one-token and empty segments, every pair against the
+    oracle and the pairs composed in order against the full recurrence."""
+    W = wl.make(name, stress=stress, n_heads=2, d=d, lengths=[300, 65, 1, 0, 700])
+    print(W.name, d, W.in_dtype, flush=True)
+    T, S = _gpu_build(W)
+    T0, S0 = _oracle_build(W)
+    eS, eT = assert_pairs_close(T, S, T0, S0, TOL[tol], W.name)
+    print(f"d={d} {W.in_dtype}: S {eS:.2e} T {eT}")
+    Rg = torch.zeros((1, 2, d, d), device="cuda")
+    hb.compose(dev(T, torch.float32), dev(S, torch.float32), dev(np.arange(5, dtype=np.int32)[None, :], torch.int32), Rg)
+    torch.cuda.synchronize()
+    full, _ = oracle.run(W.k, W.v, W.g, W.beta, gate=W.gate, delta=W.delta)
+    assert rel_f(Rg.cpu().numpy()[0], full).max() <= TOL[tol]
