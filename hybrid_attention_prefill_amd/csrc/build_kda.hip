@@ -168,31 +168,43 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
     constexpr int NPC = CK * D * 2 / 1024;   // 1-KiB pieces of a chunk's [CK][D] bf16 plane
     static_assert(NPC <= 8 && CK * (D / 8) <= 512, "one piece per wave, one staging item per thread");
     static_assert(sizeof(sm.rv.nx) <= sizeof(sm.rv.RmT), "v and log-gates fit over RmT");
+    // Who stages the next chunk.  While T is live the S waves do (52 products per chunk in the
+    // update against the T waves' 96): each of their threads takes IPT staging items and each
+    // of their waves loads IPT 1-KiB pieces of every plane, those of its own items.  Once T is
+    // dropped every wave stages one item and loads its own piece (the T waves, idle in the
+    // update, would otherwise wait for loads issued at its start).
+    constexpr int IPT = NPC / 4;
+    static_assert(NPC % 4 == 0, "four waves share the pieces evenly");
     uint16_t braw = 0;   // beta of token (tid mod CK) of the chunk being fetched
-    auto fetch = [&](int64_t c0n) {
+    auto fetch = [&](int64_t c0n, bool grp_s) {
         // chunk base (uniform, 64-bit) + row offset below 32 tokens (32-bit); rows past the
         // segment clamped to its last token
         const int last = (end - 1 - c0n) < CK - 1 ? (int)(end - 1 - c0n) : CK - 1;
         const size_t base = (size_t)c0n * tok_stride + (size_t)h * D;
         const unsigned ts = (unsigned)tok_stride;
-        if (wave < NPC) {
+        if (grp_s ? wave < 4 : wave < NPC) {
             const int ln = opaque(lane);           // (recomputed here rather than kept live)
-            const int e = wave * 512 + ln * 8;     // K: element e of the token-major plane
-            const int i = wave * 64 + ln;          // v, log-gates: staging item i
-            const unsigned ok = (unsigned)min(e / D, last) * ts + (unsigned)(e % D);
-            const unsigned oi = (unsigned)min(i % CK, last) * ts + (unsigned)((i / CK) * 8);
-            // (the addresses are locals: as calls inside the builtin's arguments they stop the
-            // host pass from emitting the kernel's launch stub)
-            const uint16_t* pk = k + base + ok;
-            const uint16_t* pv = v + base + oi;
-            const uint16_t* pg = gl + base + oi;
-            __builtin_amdgcn_global_load_lds(pk, (__attribute__((address_space(3))) void*)(&sm.Kb[0][0] + wave * 512), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(pv, (__attribute__((address_space(3))) void*)(sm.rv.nx.Vr + wave * 512), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(pg, (__attribute__((address_space(3))) void*)(sm.rv.nx.Gr + wave * 512), 16, 0, 0);
+#pragma unroll
+            for (int r = 0; r < (grp_s ? IPT : 1); ++r) {
+                const int pc = grp_s ? (wave & 3) + 4 * r : wave;   // piece
+                const int e = pc * 512 + ln * 8;       // K: element e of the token-major plane
+                const int i = pc * 64 + ln;            // v, log-gates: staging item i
+                const unsigned ok = (unsigned)min(e / D, last) * ts + (unsigned)(e % D);
+                const unsigned oi = (unsigned)min(i % CK, last) * ts + (unsigned)((i / CK) * 8);
+                // (the addresses are locals: as calls inside the builtin's arguments they stop
+                // the host pass from emitting the kernel's launch stub)
+                const uint16_t* pk = k + base + ok;
+                const uint16_t* pv = v + base + oi;
+                const uint16_t* pg = gl + base + oi;
+                __builtin_amdgcn_global_load_lds(pk, (__attribute__((address_space(3))) void*)(&sm.Kb[0][0] + pc * 512), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(pv, (__attribute__((address_space(3))) void*)(sm.rv.nx.Vr + pc * 512), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(pg, (__attribute__((address_space(3))) void*)(sm.rv.nx.Gr + pc * 512), 16, 0, 0);
+            }
         }
         braw = beta[(size_t)(c0n + min(tid & (CK - 1), last)) * H + h];
     };
-    if (beg < end) fetch(beg);
+    bool stg_s = true;   // the chunk being fetched is staged by waves 0-3 (else by all)
+    if (beg < end) fetch(beg, true);
     for (int64_t c0 = beg; c0 < end; c0 += CK) {
         const int n = (int)((end - c0) < CK ? (end - c0) : CK);
         const int par = (int)(((c0 - beg) / CK) & 1);   // chunk parity (eBC, renormalisation records)
@@ -200,30 +212,21 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
         // last read before its own final barrier (Ag, betas) or keeps apart by parity (eBC):
         // other waves may still be in the previous chunk's state update, which reads eBC and
         // (diag(b) V)^T, so the latter is written after the barrier.
-        // ---- 1. staging: thread = item (channel group vcg, token vt): v, log-gates and beta to
-        // registers; the inclusive cumulative log2-gate of its 8 channels over the chunk by a
-        // 32-lane scan (the item's token is its lane within the half-wave), written to Ag with
-        // (diag(b) V)^T and the betas
+        // ---- 1. staging (staging group): item (channel group vcg, token vt): v, log-gates and
+        // beta to registers; the inclusive cumulative log2-gate of its 8 channels over the
+        // chunk by a 32-lane scan (the item's token is its lane within the half-wave), written
+        // to Ag with (diag(b) V)^T and the betas
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0): this wave's direct loads have landed
         asm volatile("" ::: "memory");
-        float vx[8];
-        int vt = -1, vcg = 0;
-        if (tid < CK * (D / 8)) {
-            vt = tid % CK;
-            vcg = tid / CK;
+        const bool in_grp = stg_s ? wave < 4 : tid < CK * (D / 8);
+        const int st = stg_s ? (wave & 3) * 64 + lane : tid;   // items st + 256 r
+        const int ni = stg_s ? IPT : 1;                          // items of this thread
+        const int vt = st % CK;
+        float vx[IPT][8];
+        if (in_grp) {
             const bool live = vt < n;
-            const u32x4 vw = *reinterpret_cast<const u32x4*>(&sm.rv.nx.Vr[tid * 8]);
-            const u32x4 gw = *reinterpret_cast<const u32x4*>(&sm.rv.nx.Gr[tid * 8]);
             const float bt = live ? bf(braw) : 0.f;
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                vx[2 * e] = bt * __uint_as_float(vw[e] << 16);
-                vx[2 * e + 1] = bt * __uint_as_float(vw[e] & 0xFFFF0000u);
-                x[2 * e] = live ? __uint_as_float(gw[e] << 16) * kLog2e : 0.f;
-                x[2 * e + 1] = live ? __uint_as_float(gw[e] & 0xFFFF0000u) * kLog2e : 0.f;
-            }
             // inclusive scan over the 32 lanes of each half-wave: within rows of 16 lanes by
             // row shifts (lanes shifted in from outside the row read 0), then row 1 (3) adds the
             // total of row 0 (2) by row_bcast:15
@@ -232,31 +235,51 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                                                        decltype(ctrl)::value, decltype(rmask)::value, 0xf, true));
             };
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float r = x[e];
-                r = dpp_add(r, IntConst<0x111>{}, IntConst<0xf>{});   // row_shr:1
-                r = dpp_add(r, IntConst<0x112>{}, IntConst<0xf>{});   // row_shr:2
-                r = dpp_add(r, IntConst<0x114>{}, IntConst<0xf>{});   // row_shr:4
-                r = dpp_add(r, IntConst<0x118>{}, IntConst<0xf>{});   // row_shr:8
-                r = dpp_add(r, IntConst<0x142>{}, IntConst<0xa>{});   // row_bcast:15 into rows 1, 3
-                x[e] = r;
-            }
-            *reinterpret_cast<f32x4*>(&sm.Ag[vt + 1][vcg * 8]) = f32x4{x[0], x[1], x[2], x[3]};
-            *reinterpret_cast<f32x4*>(&sm.Ag[vt + 1][vcg * 8 + 4]) = f32x4{x[4], x[5], x[6], x[7]};
-            if (vt == 0) {
-                *reinterpret_cast<f32x4*>(&sm.Ag[0][vcg * 8]) = zero4();
-                *reinterpret_cast<f32x4*>(&sm.Ag[0][vcg * 8 + 4]) = zero4();
-            }
-            if (vt == CK - 1) {
+            for (int r = 0; r < IPT; ++r) {
+                if (r >= ni) break;
+                const int i = st + 256 * r, vcg = i / CK;
+                const u32x4 vw = *reinterpret_cast<const u32x4*>(&sm.rv.nx.Vr[i * 8]);
+                const u32x4 gw = *reinterpret_cast<const u32x4*>(&sm.rv.nx.Gr[i * 8]);
+                float x[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) sm.eBC[par][vcg * 8 + e] = exp2_raw(x[e]);
+                for (int e = 0; e < 4; ++e) {
+                    vx[r][2 * e] = bt * __uint_as_float(vw[e] << 16);
+                    vx[r][2 * e + 1] = bt * __uint_as_float(vw[e] & 0xFFFF0000u);
+                    x[2 * e] = live ? __uint_as_float(gw[e] << 16) * kLog2e : 0.f;
+                    x[2 * e + 1] = live ? __uint_as_float(gw[e] & 0xFFFF0000u) * kLog2e : 0.f;
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float a = x[e];
+                    a = dpp_add(a, IntConst<0x111>{}, IntConst<0xf>{});   // row_shr:1
+                    a = dpp_add(a, IntConst<0x112>{}, IntConst<0xf>{});   // row_shr:2
+                    a = dpp_add(a, IntConst<0x114>{}, IntConst<0xf>{});   // row_shr:4
+                    a = dpp_add(a, IntConst<0x118>{}, IntConst<0xf>{});   // row_shr:8
+                    a = dpp_add(a, IntConst<0x142>{}, IntConst<0xa>{});   // row_bcast:15 into rows 1, 3
+                    x[e] = a;
+                }
+                *reinterpret_cast<f32x4*>(&sm.Ag[vt + 1][vcg * 8]) = f32x4{x[0], x[1], x[2], x[3]};
+                *reinterpret_cast<f32x4*>(&sm.Ag[vt + 1][vcg * 8 + 4]) = f32x4{x[4], x[5], x[6], x[7]};
+                if (vt == 0) {
+                    *reinterpret_cast<f32x4*>(&sm.Ag[0][vcg * 8]) = zero4();
+                    *reinterpret_cast<f32x4*>(&sm.Ag[0][vcg * 8 + 4]) = zero4();
+                }
+                if (vt == CK - 1) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) sm.eBC[par][vcg * 8 + e] = exp2_raw(x[e]);
+                }
+                if (vcg == 0) sm.beta[vt] = bt;
             }
-            if (vcg == 0) sm.beta[vt] = bt;
         }
         lds_barrier();
-        if (vt >= 0) {   // (diag(b) V)^T, fp16 (first read after the Gram phase's barrier)
+        if (in_grp) {   // (diag(b) V)^T, fp16 (first read after the Gram phase's barrier)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sm.bVT[vcg * 8 + e][vt] = f16_bits((_Float16)vx[e]);
+            for (int r = 0; r < IPT; ++r) {
+                if (r >= ni) break;
+                const int vcg = (st + 256 * r) / CK;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sm.bVT[vcg * 8 + e][vt] = f16_bits((_Float16)vx[r][e]);
+            }
         }
 
         // ---- 2a. renormalisation of the T columns by a power of two when they have become
@@ -488,7 +511,10 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
         }
         lds_barrier();
 
-        if (c0 + CK < end) fetch(c0 + CK);   // Kb and RmT are not read again in this chunk
+        if (c0 + CK < end) {   // Kb and RmT are not read again in this chunk
+            fetch(c0 + CK, t_live);
+            stg_s = t_live;
+        }
         // ---- 5. update of the owned column tiles: Y = W X, R = -(Y [+ U]),
         // X <- e^{b_C} X + Kh^T R [+ Kh'^T bV].  The k-blocks of X are converted to B fragments
         // as they are used; each A fragment is read once for all CTW tiles.
