@@ -13,6 +13,49 @@ __device__ __forceinline__ int opaque(int x) {
     return x;
 }
 
+// A 16 x 16 block in the accumulator layout of v_mfma_f32_16x16x16_f16 (lane (g4, n16): rows
+// 4 g4 .. 4 g4 + 3 of column n16) as fp16 hi / lo operand bits: the B operand of that product,
+// or the A operand of the transposed block.
+struct Hl16 {
+    u32x2 h, l;
+};
+__device__ __forceinline__ Hl16 hl16(const f32x4& x) {
+    unsigned a, b, c, d;
+    pack_f16_split(x, a, b, c, d);
+    return Hl16{u32x2{a, b}, u32x2{c, d}};
+}
+// 16 x 16 x 16 product with fp16 hi / lo operands (three products; lo x lo dropped)
+__device__ __forceinline__ f32x4 mma16(const u32x2& ah, const u32x2& al, const u32x2& bh, const u32x2& bl, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, ah), __builtin_bit_cast(f16x4, bh), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, ah), __builtin_bit_cast(f16x4, bl), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, al), __builtin_bit_cast(f16x4, bh), c, 0, 0, 0);
+    return c;
+}
+__device__ __forceinline__ f32x4 mm16(const Hl16& a, const Hl16& b) { return mma16(a.h, a.l, b.h, b.l, zero4()); }
+
+// (I - N)^-1 for a strictly lower 16 x 16 block N (N^16 = 0), given N and N^T in the
+// accumulator layout; returns the inverse transposed, in the accumulator layout:
+//   (I - N)^-1 = P1 (I + N^4)(I + N^8),   P1 = (I + N)(I + N^2) = I + N + N^2 + N^3,
+// formed transposed, Y^T = (I + N^8)^T (I + N^4)^T P1^T, as 16 x 16 products on MFMA (fp16
+// hi / lo operands) with each identity term as a product's fp32 accumulator input.  A
+// product's A operand is the accumulator layout of the transposed factor, so N and N^T are
+// carried along.
+__device__ __forceinline__ f32x4 inv16_t(const f32x4& nd, const f32x4& nt, int g4, int n16) {
+    const Hl16 n1 = hl16(nd), n1t = hl16(nt);
+    const f32x4 n2 = mm16(n1t, n1), n2t = mm16(n1, n1t);                    // N^2, (N^2)^T
+    const Hl16 q2 = hl16(n2), q2t = hl16(n2t);
+    f32x4 c1;   // I + N^T + (N^2)^T
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c1[e] = nt[e] + n2t[e] + ((4 * g4 + e == n16) ? 1.f : 0.f);
+    const f32x4 n4 = mm16(q2t, q2), n4t = mm16(q2, q2t);                    // N^4, (N^4)^T
+    const f32x4 p1t = mma16(q2.h, q2.l, n1t.h, n1t.l, c1);                  // P1^T = c1 + (N^2)^T N^T
+    const Hl16 q4 = hl16(n4), q4t = hl16(n4t), r1t = hl16(p1t);
+    const f32x4 n8 = mm16(q4t, q4);                                         // N^8
+    const f32x4 p2t = mma16(q4.h, q4.l, r1t.h, r1t.l, p1t);                 // (P1 (I + N^4))^T
+    const Hl16 q8 = hl16(n8), r2t = hl16(p2t);
+    return mma16(q8.h, q8.l, r2t.h, r2t.l, p2t);
+}
+
 __device__ __forceinline__ f32x4 mm16_f32(const float* A, int lda, const float* B, int ldb, int lane) {
     const int g4 = lane >> 4, n16 = lane & 15;
     f32x4 acc = zero4();

@@ -66,7 +66,7 @@ struct alignas(16) KdaSmem {
     float Ag[CK + 1][D + 4];       // exclusive cumulative log2-gate per channel; row t+1 inclusive, row CK = b_C
     float beta[CK];
     float eBC[2][D];               // e^{b_C} per channel (the chunk's decay of the state rows), by chunk parity
-    float F1[CK][LDF];             // Lp (strictly lower, beta folded)
+    float F1[CK][LDF];             // Lp (strictly lower, beta folded), then A = (I + Lp)^-1 in place
     float F1p[CK][LDF];            // L'
     union {
         uint16_t RmT[2][D][LDT];   // (e^{a} o K)^T, bf16 hi / lo
@@ -81,7 +81,6 @@ struct alignas(16) KdaSmem {
     uint16_t bVT[D][LDT];          // (diag(b) V)^T
     union {
         struct {                       // phases 3-5
-            float F2[CK][LDF];             // A = (I + Lp)^-1 (diagonal blocks)
             uint16_t ApB[2][CK][LDT];      // A diag(b), bf16 hi / lo
             uint16_t WpB[2][CK][D + 8];    // W, token-major, bf16 hi / lo (T columns)
             uint16_t Ap[CK][LDT];          // A diag(b)
@@ -418,51 +417,53 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                 acc = mma_bf16(ah, bl, acc);
                 acc = mma_bf16(al, bh, acc);
             }
+            f32x4 nd;   // -Lp in the accumulator layout (waves 0 and 2: a diagonal block)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int tt = 16 * I + 4 * g4 + e, ss = 16 * J + n16;
-                if (lp) sm.F1[tt][ss] = ss < tt ? sm.beta[tt] * acc[e] : 0.f;
-                else sm.F1p[tt][ss] = ss < tt ? acc[e] : 0.f;
+                const float x = ss < tt ? (lp ? sm.beta[tt] : 1.f) * acc[e] : 0.f;
+                nd[e] = -x;
+                if (lp) sm.F1[tt][ss] = x;
+                else sm.F1p[tt][ss] = x;
+            }
+            if (lp && I == J) {
+                // D_I = (I + Lp_II)^-1 on MFMA in this wave (no barrier): N^T read back from the
+                // block just written (one wave's LDS accesses complete in order), the inverse
+                // written over the block (row n16: Y[n16][4 g4 .. 4 g4 + 3] = the transposed
+                // result's accumulator entries)
+                const int o = 16 * I;
+                asm volatile("" ::: "memory");
+                const f32x4 lt = *reinterpret_cast<const f32x4*>(&sm.F1[o + n16][o + 4 * g4]);
+                const f32x4 yt = inv16_t(nd, -lt, g4, n16);
+                asm volatile("" ::: "memory");
+                *reinterpret_cast<f32x4*>(&sm.F1[o + n16][o + 4 * g4]) = yt;
             }
         }
         lds_barrier();
 
-        // ---- 3. A = (I + Lp)^-1: diagonal 16x16 blocks D0, D1 by forward substitution (one
-        // lane per column), then A10 = -D1 (L10 D0) by one wave, then A diag(b) to its operand
-        // planes (fp16, and bf16 hi + lo)
-        if (wave < 2 && lane < 16) {
-            const int o = wave * 16, j = lane;
-            float x[16];
+        // ---- 3. A = (I + Lp)^-1: the diagonal blocks D0, D1 are in F1 (inverted above); now
+        // A10 = -D1 (L10 D0) by one wave, written over L10, while the others convert L' to
+        // fp16; then A diag(b) to its operand planes (fp16, and bf16 hi + lo)
+        if (wave == 0) {
+            // F = L10 D0 in MFMA accumulators (lane (g4, n16) holds rows 4 g4 .. 4 g4 + 3 of
+            // column n16), then -D1 F with the contraction index of k-step kb taken as
+            // 4 g4 + kb, so that F's accumulators are the B operand as they stand
+            const f32x4 f = mm16_f32(&sm.F1[16][0], LDF, &sm.F1[0][0], LDF, lane);
+            f32x4 acc = zero4();
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {   // row r of L0 (or L1) is read as four 16-byte pieces
-                float s_ = (r == j) ? 1.f : 0.f;
-#pragma unroll
-                for (int q = 0; q < r; ++q) s_ -= sm.F1[o + r][o + q] * x[q];
-                x[r] = s_;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sm.u.p.F2[o + r][o + j] = x[r];
+            for (int kb = 0; kb < 4; ++kb)
+                acc = mma_f32(sm.F1[16 + n16][16 + 4 * g4 + kb], f[kb], acc);
+            asm volatile("" ::: "memory");
+            st16_f32(&sm.F1[16][0], LDF, acc, lane, -1.f);
         }
         for (int it = tid; it < CK * CK; it += 512) {  // L' to fp16 (row-major); the block above
             const int t = it / CK, s = it % CK;          // the diagonal is never computed
             sm.u.p.Lpb[t][s] = f16_bits((_Float16)(s < t ? sm.F1p[t][s] : 0.f));
         }
         lds_barrier();
-        if (wave == 0) {
-            // F = L10 D0 in MFMA accumulators (lane (g4, n16) holds rows 4 g4 .. 4 g4 + 3 of
-            // column n16), then -D1 F with the contraction index of k-step kb taken as
-            // 4 g4 + kb, so that F's accumulators are the B operand as they stand
-            const f32x4 f = mm16_f32(&sm.F1[16][0], LDF, &sm.u.p.F2[0][0], LDF, lane);
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-                acc = mma_f32(sm.u.p.F2[16 + n16][16 + 4 * g4 + kb], f[kb], acc);
-            st16_f32(&sm.u.p.F2[16][0], LDF, acc, lane, -1.f);
-        }
-        lds_barrier();
         for (int it = tid; it < CK * CK; it += 512) {
             const int t = it / CK, s = it % CK;
-            const float ap = s <= t ? sm.u.p.F2[t][s] * sm.beta[s] : 0.f;
+            const float ap = s <= t ? sm.F1[t][s] * sm.beta[s] : 0.f;
             sm.u.p.Ap[t][s] = f16_bits((_Float16)ap);
             put_bf16_split(&sm.u.p.ApB[0][t][s], &sm.u.p.ApB[1][t][s], ap);
         }
