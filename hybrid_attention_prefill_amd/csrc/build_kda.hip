@@ -66,7 +66,7 @@ struct alignas(16) KdaSmem {
     float Ag[CK + 1][D + 4];       // exclusive cumulative log2-gate per channel; row t+1 inclusive, row CK = b_C
     float beta[CK];
     float eBC[2][D];               // e^{b_C} per channel (the chunk's decay of the state rows), by chunk parity
-    float F1[CK][LDF];             // Lp (strictly lower, beta folded), then A = (I + Lp)^-1 in place
+    float F1[CK][LDF];             // Lp (strictly lower, beta folded); its diagonal blocks then inverted in place
     float F1p[CK][LDF];            // L'
     union {
         uint16_t RmT[2][D][LDT];   // (e^{a} o K)^T, bf16 hi / lo
@@ -441,9 +441,14 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
         }
         lds_barrier();
 
-        // ---- 3. A = (I + Lp)^-1: the diagonal blocks D0, D1 are in F1 (inverted above); now
-        // A10 = -D1 (L10 D0) by one wave, written over L10, while the others convert L' to
-        // fp16; then A diag(b) to its operand planes (fp16, and bf16 hi + lo)
+        // ---- 3. A = (I + Lp)^-1 to the operand planes of A diag(b) (fp16, and bf16 hi + lo):
+        // the diagonal blocks D0, D1 are in F1 (inverted above) and are converted by all
+        // threads, beside L' to fp16, while one wave forms A10 = -D1 (L10 D0) and converts it
+        // from its accumulators
+        auto put_ap = [&](int t, int s_, float a) {   // a = A[t][s] b_s
+            sm.u.p.Ap[t][s_] = f16_bits((_Float16)a);
+            put_bf16_split(&sm.u.p.ApB[0][t][s_], &sm.u.p.ApB[1][t][s_], a);
+        };
         if (wave == 0) {
             // F = L10 D0 in MFMA accumulators (lane (g4, n16) holds rows 4 g4 .. 4 g4 + 3 of
             // column n16), then -D1 F with the contraction index of k-step kb taken as
@@ -453,19 +458,16 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
                 acc = mma_f32(sm.F1[16 + n16][16 + 4 * g4 + kb], f[kb], acc);
-            asm volatile("" ::: "memory");
-            st16_f32(&sm.F1[16][0], LDF, acc, lane, -1.f);
+            const float bn = sm.beta[n16];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) put_ap(16 + 4 * g4 + i, n16, -acc[i] * bn);
         }
-        for (int it = tid; it < CK * CK; it += 512) {  // L' to fp16 (row-major); the block above
-            const int t = it / CK, s = it % CK;          // the diagonal is never computed
-            sm.u.p.Lpb[t][s] = f16_bits((_Float16)(s < t ? sm.F1p[t][s] : 0.f));
-        }
-        lds_barrier();
         for (int it = tid; it < CK * CK; it += 512) {
             const int t = it / CK, s = it % CK;
-            const float ap = s <= t ? sm.F1[t][s] * sm.beta[s] : 0.f;
-            sm.u.p.Ap[t][s] = f16_bits((_Float16)ap);
-            put_bf16_split(&sm.u.p.ApB[0][t][s], &sm.u.p.ApB[1][t][s], ap);
+            // L' to fp16 (row-major); the block above the diagonal is never computed
+            sm.u.p.Lpb[t][s] = f16_bits((_Float16)(s < t ? sm.F1p[t][s] : 0.f));
+            if (t >= 16 && s < 16) continue;   // A10: wave 0
+            put_ap(t, s, s <= t ? sm.F1[t][s] * sm.beta[s] : 0.f);
         }
         lds_barrier();
 
