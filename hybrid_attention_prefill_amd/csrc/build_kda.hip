@@ -65,7 +65,7 @@ struct alignas(16) KdaSmem {
     uint16_t Kb[CK][D];            // K (bf16 bits), token-major, loaded global -> LDS directly
     float Ag[CK + 1][D + 4];       // exclusive cumulative log2-gate per channel; row t+1 inclusive, row CK = b_C
     float beta[CK];
-    float eBC[2][D];               // e^{b_C} per channel (the chunk's decay of the state rows), by chunk parity
+    float eBC[D];                  // e^{b_C} per channel (the chunk's decay of the state rows)
     float F1[CK][LDF];             // Lp (strictly lower, beta folded); its diagonal blocks then inverted in place
     float F1p[CK][LDF];            // L'
     union {
@@ -206,11 +206,11 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
     if (beg < end) fetch(beg, true);
     for (int64_t c0 = beg; c0 < end; c0 += CK) {
         const int n = (int)((end - c0) < CK ? (end - c0) : CK);
-        const int par = (int)(((c0 - beg) / CK) & 1);   // chunk parity (eBC, renormalisation records)
+        const int par = (int)(((c0 - beg) / CK) & 1);   // chunk parity (renormalisation records)
         // The staging writes, before the chunk's first barrier, only what the previous chunk
-        // last read before its own final barrier (Ag, betas) or keeps apart by parity (eBC):
-        // other waves may still be in the previous chunk's state update, which reads eBC and
-        // (diag(b) V)^T, so the latter is written after the barrier.
+        // last read before its own final barrier (Ag, betas): other waves may still be in the
+        // previous chunk's state update, which reads (diag(b) V)^T and e^{b_C}, so those are
+        // written after the barrier.
         // ---- 1. staging (staging group): item (channel group vcg, token vt): v, log-gates and
         // beta to registers; the inclusive cumulative log2-gate of its 8 channels over the
         // chunk by a 32-lane scan (the item's token is its lane within the half-wave), written
@@ -224,8 +224,10 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
         const int vt = st % CK;
         float vx[IPT][8];
         if (in_grp) {
-            const bool live = vt < n;
-            const float bt = live ? bf(braw) : 0.f;
+            // rows past the segment are masked by bits (a select on the loaded values compiles
+            // to branches around each conversion)
+            const unsigned lm = vt < n ? 0xFFFFFFFFu : 0u;
+            const float bt = __uint_as_float(((unsigned)braw << 16) & lm);
             // inclusive scan over the 32 lanes of each half-wave: within rows of 16 lanes by
             // row shifts (lanes shifted in from outside the row read 0), then row 1 (3) adds the
             // total of row 0 (2) by row_bcast:15
@@ -244,8 +246,8 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                 for (int e = 0; e < 4; ++e) {
                     vx[r][2 * e] = bt * __uint_as_float(vw[e] << 16);
                     vx[r][2 * e + 1] = bt * __uint_as_float(vw[e] & 0xFFFF0000u);
-                    x[2 * e] = live ? __uint_as_float(gw[e] << 16) * kLog2e : 0.f;
-                    x[2 * e + 1] = live ? __uint_as_float(gw[e] & 0xFFFF0000u) * kLog2e : 0.f;
+                    x[2 * e] = __uint_as_float((gw[e] << 16) & lm) * kLog2e;
+                    x[2 * e + 1] = __uint_as_float(gw[e] & 0xFFFF0000u & lm) * kLog2e;
                 }
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -262,10 +264,6 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                 if (vt == 0) {
                     *reinterpret_cast<f32x4*>(&sm.Ag[0][vcg * 8]) = zero4();
                     *reinterpret_cast<f32x4*>(&sm.Ag[0][vcg * 8 + 4]) = zero4();
-                }
-                if (vt == CK - 1) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) sm.eBC[par][vcg * 8 + e] = exp2_raw(x[e]);
                 }
                 if (vcg == 0) sm.beta[vt] = bt;
             }
@@ -345,6 +343,10 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                     for (int i = 0; i < 5; ++i) er[i][j] = (E1 && i == 4) ? 0.f : exp2_raw(rho[j] - A[i][j]);
                     P[j] = exp2_raw(rho[j]);
                     Q[j] = exp2_raw(bc[j] - rho[j]);
+                }
+                if (t0 == 0) {   // e^{b_C} (wave 0)
+                    sm.eBC[c] = exp2_raw(bc[0]);
+                    sm.eBC[c + 1] = exp2_raw(bc[1]);
                 }
                 // e^{rho - i_t}: the next token's e^{rho - c} (gate after the erase); e^{rho - c_t}
                 // itself when the gate comes first (i = c for the erase vectors then)
@@ -553,7 +555,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
             }
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
-                const f32x4 eb = *reinterpret_cast<const f32x4*>(&sm.eBC[par][rt * 16 + 4 * g4]);
+                const f32x4 eb = *reinterpret_cast<const f32x4*>(&sm.eBC[rt * 16 + 4 * g4]);
                 const Frag<1> a = f16frag(&sm.KhT[0][0], LDT, rt * 16 + n16, 8 * g4);
                 const Frag<1> a2 = f16frag(&sm.KhpT[0][0], LDT, rt * 16 + n16, 8 * g4);
 #pragma unroll
@@ -585,7 +587,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
             for (int c = 0; c < CTW; ++c) rb[c] = dpair_to_fragb(Y[c][0] * -tsc, Y[c][1] * -tsc);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
-                const f32x4 eb = *reinterpret_cast<const f32x4*>(&sm.eBC[par][rt * 16 + 4 * g4]) * tsc;
+                const f32x4 eb = *reinterpret_cast<const f32x4*>(&sm.eBC[rt * 16 + 4 * g4]) * tsc;
                 const FragB a = fragb_at(&sm.KhTb[0][0][0], &sm.KhTb[1][0][0], LDT, rt * 16 + n16, 8 * g4);
 #pragma unroll
                 for (int c = 0; c < CTW; ++c) {
