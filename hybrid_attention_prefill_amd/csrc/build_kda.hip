@@ -64,7 +64,7 @@ template <int D>
 struct alignas(16) KdaSmem {
     uint16_t Kb[CK][D];            // K (bf16 bits), token-major, loaded global -> LDS directly
     float Ag[CK + 1][D + 4];       // exclusive cumulative log2-gate per channel; row t+1 inclusive, row CK = b_C
-    float beta[CK];
+    float beta[2][CK];             // beta per token, by chunk parity
     float eBC[D];                  // e^{b_C} per channel (the chunk's decay of the state rows)
     float F1[CK][LDF];             // Lp (strictly lower, beta folded); its diagonal blocks then inverted in place
     float F1p[CK][LDF];            // L'
@@ -75,7 +75,13 @@ struct alignas(16) KdaSmem {
             uint16_t Gr[CK * D];
         } nx;
     } rv;
-    uint16_t KhTb[2][D][LDT];      // Kh^T, bf16 hi / lo (T columns)
+    union {
+        uint16_t KhTb[2][D][LDT];  // Kh^T, bf16 hi / lo (T columns)
+        struct {                   // once T is dropped: the next chunk's v and log-gates, loaded
+            uint16_t Vr[CK * D];   // during the Gram phase (item-major, as below)
+            uint16_t Gr[CK * D];
+        } nx;
+    } kt;
     uint16_t KhT[D][LDT];          // Kh^T
     uint16_t KhpT[D][LDT];         // Kh'^T
     uint16_t bVT[D][LDT];          // (diag(b) V)^T
@@ -156,126 +162,152 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
     bool t_live = true;  // false once every T entry is below 2^-120
 
     const size_t tok_stride = (size_t)H * D;
-    // A chunk's k, log-gates and v are loaded global -> LDS directly, one chunk ahead (16 bytes
-    // per lane, so one wave's load fills 1 KiB), while the previous chunk's state is updated:
-    // K into Kb, v and the log-gates over RmT (both read last before the update).  v and the
-    // log-gates go item-major: staging item i (channel group i / CK, token i % CK) is thread i,
-    // whose own wave loaded it, so no barrier is needed before it reads them.  Rows past the
-    // segment are read clamped to its last token (finite values) and masked where they are
-    // consumed: their log-gates count as zero and their betas are zero, which takes them out
-    // of every product.
+    // A chunk's k, log-gates and v are loaded global -> LDS directly, one chunk ahead, in 1-KiB
+    // pieces (16 bytes per lane): K token-major into Kb; v and the log-gates item-major, staging
+    // item i (channel group i / CK, token i % CK) in piece i / 64, so a thread that stages an
+    // item its own wave loaded needs no barrier first.  Rows past the segment are read clamped
+    // to its last token (finite values) and masked where they are consumed: their log-gates
+    // count as zero and their betas are zero, which takes them out of every product.
+    //   - While T is live the S waves (52 products per chunk in the update against the T
+    //     waves' 96) stage: wave w loads pieces w, w + 4, ... of every plane at the start of the
+    //     update (v and the log-gates over RmT, read last before it) and stages its items at
+    //     the top of the next chunk: a 32-lane scan of each item's 8 gates, v times beta to
+    //     registers.
+    //   - Once T is dropped the T waves, idle in the update, stage during it, so the next chunk
+    //     starts staged: they load the same pieces in the Gram phase, after their Gram tile
+    //     (into the T-only Kh^T planes; K into Kb, read last by the operand pass), stage them
+    //     the same way after the update but put v times beta back over v as fp16, and copy
+    //     that to (diag(b) V)^T at the top of the next chunk.
     constexpr int NPC = CK * D * 2 / 1024;   // 1-KiB pieces of a chunk's [CK][D] bf16 plane
-    static_assert(NPC <= 8 && CK * (D / 8) <= 512, "one piece per wave, one staging item per thread");
-    static_assert(sizeof(sm.rv.nx) <= sizeof(sm.rv.RmT), "v and log-gates fit over RmT");
-    // Who stages the next chunk.  While T is live the S waves do (52 products per chunk in the
-    // update against the T waves' 96): each of their threads takes IPT staging items and each
-    // of their waves loads IPT 1-KiB pieces of every plane, those of its own items.  Once T is
-    // dropped every wave stages one item and loads its own piece (the T waves, idle in the
-    // update, would otherwise wait for loads issued at its start).
-    constexpr int IPT = NPC / 4;
-    static_assert(NPC % 4 == 0, "four waves share the pieces evenly");
-    uint16_t braw = 0;   // beta of token (tid mod CK) of the chunk being fetched
-    auto fetch = [&](int64_t c0n, bool grp_s) {
+    static_assert(NPC % 4 == 0 && NPC <= 8 && CK * (D / 8) <= 512, "pieces and items spread evenly");
+    static_assert(sizeof(sm.rv.nx) <= sizeof(sm.rv.RmT) && sizeof(sm.kt.nx) <= sizeof(sm.kt.KhTb),
+                  "v and log-gates fit over RmT and over the Kh^T planes");
+    constexpr int IPT = NPC / 4;             // items per S-wave thread
+    const int vt = lane % CK;                // token of this thread's staging items
+    uint16_t braw = 0;   // beta of token vt of the chunk being fetched
+    // piece pc of chunk c0n: token-major (K) or item-major (v, log-gates)
+    auto dma = [&](int64_t c0n, const uint16_t* src, uint16_t* dst, int pc, bool item_major) {
         // chunk base (uniform, 64-bit) + row offset below 32 tokens (32-bit); rows past the
         // segment clamped to its last token
         const int last = (end - 1 - c0n) < CK - 1 ? (int)(end - 1 - c0n) : CK - 1;
-        const size_t base = (size_t)c0n * tok_stride + (size_t)h * D;
-        const unsigned ts = (unsigned)tok_stride;
-        if (grp_s ? wave < 4 : wave < NPC) {
-            const int ln = opaque(lane);           // (recomputed here rather than kept live)
-#pragma unroll
-            for (int r = 0; r < (grp_s ? IPT : 1); ++r) {
-                const int pc = grp_s ? (wave & 3) + 4 * r : wave;   // piece
-                const int e = pc * 512 + ln * 8;       // K: element e of the token-major plane
-                const int i = pc * 64 + ln;            // v, log-gates: staging item i
-                const unsigned ok = (unsigned)min(e / D, last) * ts + (unsigned)(e % D);
-                const unsigned oi = (unsigned)min(i % CK, last) * ts + (unsigned)((i / CK) * 8);
-                // (the addresses are locals: as calls inside the builtin's arguments they stop
-                // the host pass from emitting the kernel's launch stub)
-                const uint16_t* pk = k + base + ok;
-                const uint16_t* pv = v + base + oi;
-                const uint16_t* pg = gl + base + oi;
-                __builtin_amdgcn_global_load_lds(pk, (__attribute__((address_space(3))) void*)(&sm.Kb[0][0] + pc * 512), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(pv, (__attribute__((address_space(3))) void*)(sm.rv.nx.Vr + pc * 512), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(pg, (__attribute__((address_space(3))) void*)(sm.rv.nx.Gr + pc * 512), 16, 0, 0);
-            }
-        }
-        braw = beta[(size_t)(c0n + min(tid & (CK - 1), last)) * H + h];
+        const int ln = opaque(lane);           // (recomputed here rather than kept live)
+        const int e = pc * 512 + ln * 8;       // token-major: element e of the plane
+        const int i = pc * 64 + ln;            // item-major: item i
+        const unsigned off = item_major ? (unsigned)min(i % CK, last) * (unsigned)tok_stride + (unsigned)((i / CK) * 8)
+                                        : (unsigned)min(e / D, last) * (unsigned)tok_stride + (unsigned)(e % D);
+        // (the address is a local: as a call inside the builtin's arguments it stops the host
+        // pass from emitting the kernel's launch stub)
+        const uint16_t* ps = src + (size_t)c0n * tok_stride + (size_t)h * D + off;
+        __builtin_amdgcn_global_load_lds(ps, (__attribute__((address_space(3))) void*)(dst + pc * 512), 16, 0, 0);
     };
-    bool stg_s = true;   // the chunk being fetched is staged by waves 0-3 (else by all)
-    if (beg < end) fetch(beg, true);
+    auto load_beta = [&](int64_t c0n) {
+        const int last = (end - 1 - c0n) < CK - 1 ? (int)(end - 1 - c0n) : CK - 1;
+        braw = beta[(size_t)(c0n + min(vt, last)) * H + h];
+    };
+    auto fetch = [&](int64_t c0n, uint16_t* vr, uint16_t* gr) {   // pieces (wave & 3) + 4 r of every plane
+#pragma unroll 1   // (unrolled, the addresses of every piece are formed at once: spills)
+        for (int r = 0; r < IPT; ++r) {
+            const int pc = (wave & 3) + 4 * r;
+            dma(c0n, k, &sm.Kb[0][0], pc, false);
+            dma(c0n, v, vr, pc, true);
+            dma(c0n, gl, gr, pc, true);
+        }
+        load_beta(c0n);
+    };
+    auto wait_vm0 = []() {   // s_waitcnt vmcnt(0): this wave's loads have landed
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0x0070);
+        asm volatile("" ::: "memory");
+    };
+    // Staging (this wave's loads landed): for each of the thread's items (wave & 3) * 64 + lane
+    // + 256 r, v times beta to registers (vx, written to (diag(b) V)^T past the chunk's first
+    // barrier) or back over v as fp16 (to_lds), and the inclusive cumulative log2-gate of its 8
+    // channels over the chunk by a 32-lane scan (the item's token is its lane within the
+    // half-wave) to Ag; beta to LDS (by chunk parity: a chunk reads its own until its
+    // off-diagonal phase).  Rows past the segment are masked by bits (a select on the loaded
+    // values compiles to branches around each conversion).
+    auto stage = [&](uint16_t* vr, const uint16_t* gr, int nn, float (&vx)[IPT][8], bool to_lds, int bpar) {
+        const unsigned lm = vt < nn ? 0xFFFFFFFFu : 0u;
+        const float bt = __uint_as_float(((unsigned)braw << 16) & lm);
+        // inclusive scan over the 32 lanes of each half-wave: within rows of 16 lanes by row
+        // shifts (lanes shifted in from outside the row read 0), then row 1 (3) adds the total
+        // of row 0 (2) by row_bcast:15
+        auto dpp_add = [](float a, auto ctrl, auto rmask) {
+            return a + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a),
+                                                   decltype(ctrl)::value, decltype(rmask)::value, 0xf, true));
+        };
+#pragma unroll
+        for (int r = 0; r < IPT; ++r) {
+            const int i = (wave & 3) * 64 + lane + 256 * r, vcg = i / CK;
+            const u32x4 vw = *reinterpret_cast<const u32x4*>(&vr[i * 8]);
+            const u32x4 gw = *reinterpret_cast<const u32x4*>(&gr[i * 8]);
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                vx[r][2 * e] = bt * __uint_as_float(vw[e] << 16);
+                vx[r][2 * e + 1] = bt * __uint_as_float(vw[e] & 0xFFFF0000u);
+                x[2 * e] = __uint_as_float((gw[e] << 16) & lm) * kLog2e;
+                x[2 * e + 1] = __uint_as_float(gw[e] & 0xFFFF0000u & lm) * kLog2e;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float a = x[e];
+                a = dpp_add(a, IntConst<0x111>{}, IntConst<0xf>{});   // row_shr:1
+                a = dpp_add(a, IntConst<0x112>{}, IntConst<0xf>{});   // row_shr:2
+                a = dpp_add(a, IntConst<0x114>{}, IntConst<0xf>{});   // row_shr:4
+                a = dpp_add(a, IntConst<0x118>{}, IntConst<0xf>{});   // row_shr:8
+                a = dpp_add(a, IntConst<0x142>{}, IntConst<0xa>{});   // row_bcast:15 into rows 1, 3
+                x[e] = a;
+            }
+            *reinterpret_cast<f32x4*>(&sm.Ag[vt + 1][vcg * 8]) = f32x4{x[0], x[1], x[2], x[3]};
+            *reinterpret_cast<f32x4*>(&sm.Ag[vt + 1][vcg * 8 + 4]) = f32x4{x[4], x[5], x[6], x[7]};
+            if (vt == 0) {
+                *reinterpret_cast<f32x4*>(&sm.Ag[0][vcg * 8]) = zero4();
+                *reinterpret_cast<f32x4*>(&sm.Ag[0][vcg * 8 + 4]) = zero4();
+            }
+            if (vcg == 0) sm.beta[bpar][vt] = bt;
+            if (to_lds)
+                *reinterpret_cast<u32x4*>(&vr[i * 8]) =
+                    u32x4{cvt2_f16(vx[r][0], vx[r][1]), cvt2_f16(vx[r][2], vx[r][3]),
+                          cvt2_f16(vx[r][4], vx[r][5]), cvt2_f16(vx[r][6], vx[r][7])};
+        }
+    };
+    bool staged = false;   // the chunk at hand was staged by the T waves during the previous chunk
+    if (beg < end && wave < 4) fetch(beg, sm.rv.nx.Vr, sm.rv.nx.Gr);
     for (int64_t c0 = beg; c0 < end; c0 += CK) {
         const int n = (int)((end - c0) < CK ? (end - c0) : CK);
-        const int par = (int)(((c0 - beg) / CK) & 1);   // chunk parity (renormalisation records)
-        // The staging writes, before the chunk's first barrier, only what the previous chunk
-        // last read before its own final barrier (Ag, betas): other waves may still be in the
-        // previous chunk's state update, which reads (diag(b) V)^T and e^{b_C}, so those are
-        // written after the barrier.
-        // ---- 1. staging (staging group): item (channel group vcg, token vt): v, log-gates and
-        // beta to registers; the inclusive cumulative log2-gate of its 8 channels over the
-        // chunk by a 32-lane scan (the item's token is its lane within the half-wave), written
-        // to Ag with (diag(b) V)^T and the betas
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0): this wave's direct loads have landed
-        asm volatile("" ::: "memory");
-        const bool in_grp = stg_s ? wave < 4 : tid < CK * (D / 8);
-        const int st = stg_s ? (wave & 3) * 64 + lane : tid;   // items st + 256 r
-        const int ni = stg_s ? IPT : 1;                          // items of this thread
-        const int vt = st % CK;
+        const int par = (int)(((c0 - beg) / CK) & 1);   // chunk parity (betas, renormalisation records)
+        // ---- 1. staging.  Before the chunk's first barrier it writes only what the previous
+        // chunk last read before its own final barrier (Ag, betas of this parity): other waves
+        // may still be in the previous chunk's state update, which reads (diag(b) V)^T and
+        // e^{b_C}, so those are written after the barrier.
         float vx[IPT][8];
-        if (in_grp) {
-            // rows past the segment are masked by bits (a select on the loaded values compiles
-            // to branches around each conversion)
-            const unsigned lm = vt < n ? 0xFFFFFFFFu : 0u;
-            const float bt = __uint_as_float(((unsigned)braw << 16) & lm);
-            // inclusive scan over the 32 lanes of each half-wave: within rows of 16 lanes by
-            // row shifts (lanes shifted in from outside the row read 0), then row 1 (3) adds the
-            // total of row 0 (2) by row_bcast:15
-            auto dpp_add = [](float a, auto ctrl, auto rmask) {
-                return a + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a),
-                                                       decltype(ctrl)::value, decltype(rmask)::value, 0xf, true));
-            };
-#pragma unroll
-            for (int r = 0; r < IPT; ++r) {
-                if (r >= ni) break;
-                const int i = st + 256 * r, vcg = i / CK;
-                const u32x4 vw = *reinterpret_cast<const u32x4*>(&sm.rv.nx.Vr[i * 8]);
-                const u32x4 gw = *reinterpret_cast<const u32x4*>(&sm.rv.nx.Gr[i * 8]);
-                float x[8];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    vx[r][2 * e] = bt * __uint_as_float(vw[e] << 16);
-                    vx[r][2 * e + 1] = bt * __uint_as_float(vw[e] & 0xFFFF0000u);
-                    x[2 * e] = __uint_as_float((gw[e] << 16) & lm) * kLog2e;
-                    x[2 * e + 1] = __uint_as_float(gw[e] & 0xFFFF0000u & lm) * kLog2e;
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float a = x[e];
-                    a = dpp_add(a, IntConst<0x111>{}, IntConst<0xf>{});   // row_shr:1
-                    a = dpp_add(a, IntConst<0x112>{}, IntConst<0xf>{});   // row_shr:2
-                    a = dpp_add(a, IntConst<0x114>{}, IntConst<0xf>{});   // row_shr:4
-                    a = dpp_add(a, IntConst<0x118>{}, IntConst<0xf>{});   // row_shr:8
-                    a = dpp_add(a, IntConst<0x142>{}, IntConst<0xa>{});   // row_bcast:15 into rows 1, 3
-                    x[e] = a;
-                }
-                *reinterpret_cast<f32x4*>(&sm.Ag[vt + 1][vcg * 8]) = f32x4{x[0], x[1], x[2], x[3]};
-                *reinterpret_cast<f32x4*>(&sm.Ag[vt + 1][vcg * 8 + 4]) = f32x4{x[4], x[5], x[6], x[7]};
-                if (vt == 0) {
-                    *reinterpret_cast<f32x4*>(&sm.Ag[0][vcg * 8]) = zero4();
-                    *reinterpret_cast<f32x4*>(&sm.Ag[0][vcg * 8 + 4]) = zero4();
-                }
-                if (vcg == 0) sm.beta[vt] = bt;
-            }
+        if (!staged && wave < 4) {
+            wait_vm0();
+            stage(sm.rv.nx.Vr, sm.rv.nx.Gr, n, vx, false, par);
         }
         lds_barrier();
-        if (in_grp) {   // (diag(b) V)^T, fp16 (first read after the Gram phase's barrier)
+        // (diag(b) V)^T, fp16 (first read in the W and Z1 phase), by the staging waves for
+        // their items: from registers, or, when staged during the previous chunk, from the fp16
+        // values over v
+        if (staged ? wave >= 4 : wave < 4) {
 #pragma unroll
             for (int r = 0; r < IPT; ++r) {
-                if (r >= ni) break;
-                const int vcg = (st + 256 * r) / CK;
+                const int i = (wave & 3) * 64 + lane + 256 * r, vcg = i / CK;
+                uint16_t hv[8];
+                if (staged) {
+                    const u32x4 w4 = *reinterpret_cast<const u32x4*>(&sm.kt.nx.Vr[i * 8]);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) sm.bVT[vcg * 8 + e][vt] = f16_bits((_Float16)vx[r][e]);
+                    for (int e = 0; e < 4; ++e) {
+                        hv[2 * e] = (uint16_t)(w4[e] & 0xFFFFu);
+                        hv[2 * e + 1] = (uint16_t)(w4[e] >> 16);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) hv[e] = f16_bits((_Float16)vx[r][e]);
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sm.bVT[vcg * 8 + e][vt] = hv[e];
             }
         }
 
@@ -299,6 +331,8 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                 log2s += em;
             }
         }
+
+        const bool stage_next = !t_live && c0 + CK < end;   // the T waves stage the next chunk
 
         // ---- 2. operands of the decay-weighted Gram matrices and the decay-scaled keys, in one
         // pass (all waves; item = 4 tokens x 2 channels, channel pair fastest across lanes).
@@ -393,8 +427,8 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                             const f32x2 hv = bf16x2_to_f32(khh[p2]);
                             khl[p2] = cvt2_bf16(kh[2 * p2] - hv.x, kh[2 * p2 + 1] - hv.y);
                         }
-                        *reinterpret_cast<u32x2*>(&sm.KhTb[0][c + j][t0]) = u32x2{khh[0], khh[1]};
-                        *reinterpret_cast<u32x2*>(&sm.KhTb[1][c + j][t0]) = u32x2{khl[0], khl[1]};
+                        *reinterpret_cast<u32x2*>(&sm.kt.KhTb[0][c + j][t0]) = u32x2{khh[0], khh[1]};
+                        *reinterpret_cast<u32x2*>(&sm.kt.KhTb[1][c + j][t0]) = u32x2{khl[0], khl[1]};
                     }
                 }
             }
@@ -423,7 +457,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int tt = 16 * I + 4 * g4 + e, ss = 16 * J + n16;
-                const float x = ss < tt ? (lp ? sm.beta[tt] : 1.f) * acc[e] : 0.f;
+                const float x = ss < tt ? (lp ? sm.beta[par][tt] : 1.f) * acc[e] : 0.f;
                 nd[e] = -x;
                 if (lp) sm.F1[tt][ss] = x;
                 else sm.F1p[tt][ss] = x;
@@ -441,6 +475,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                 *reinterpret_cast<f32x4*>(&sm.F1[o + n16][o + 4 * g4]) = yt;
             }
         }
+        if (stage_next && wave >= 4) fetch(c0 + CK, sm.kt.nx.Vr, sm.kt.nx.Gr);   // (waves 4, 5 after their Gram tile)
         lds_barrier();
 
         // ---- 3. A = (I + Lp)^-1 to the operand planes of A diag(b) (fp16, and bf16 hi + lo):
@@ -460,7 +495,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
                 acc = mma_f32(sm.F1[16 + n16][16 + 4 * g4 + kb], f[kb], acc);
-            const float bn = sm.beta[n16];
+            const float bn = sm.beta[par][n16];
 #pragma unroll
             for (int i = 0; i < 4; ++i) put_ap(16 + 4 * g4 + i, n16, -acc[i] * bn);
         }
@@ -469,7 +504,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
             // L' to fp16 (row-major); the block above the diagonal is never computed
             sm.u.p.Lpb[t][s] = f16_bits((_Float16)(s < t ? sm.F1p[t][s] : 0.f));
             if (t >= 16 && s < 16) continue;   // A10: wave 0
-            put_ap(t, s, s <= t ? sm.F1[t][s] * sm.beta[s] : 0.f);
+            put_ap(t, s, s <= t ? sm.F1[t][s] * sm.beta[par][s] : 0.f);
         }
         lds_barrier();
 
@@ -516,10 +551,8 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
         }
         lds_barrier();
 
-        if (c0 + CK < end) {   // Kb and RmT are not read again in this chunk
-            fetch(c0 + CK, t_live);
-            stg_s = t_live;
-        }
+        if (t_live && c0 + CK < end && wave < 4)   // Kb and RmT are not read again in this chunk
+            fetch(c0 + CK, sm.rv.nx.Vr, sm.rv.nx.Gr);
         // ---- 5. update of the owned column tiles: Y = W X, R = -(Y [+ U]),
         // X <- e^{b_C} X + Kh^T R [+ Kh'^T bV].  The k-blocks of X are converted to B fragments
         // as they are used; each A fragment is read once for all CTW tiles.
@@ -588,7 +621,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
                 const f32x4 eb = *reinterpret_cast<const f32x4*>(&sm.eBC[rt * 16 + 4 * g4]) * tsc;
-                const FragB a = fragb_at(&sm.KhTb[0][0][0], &sm.KhTb[1][0][0], LDT, rt * 16 + n16, 8 * g4);
+                const FragB a = fragb_at(&sm.kt.KhTb[0][0][0], &sm.kt.KhTb[1][0][0], LDT, rt * 16 + n16, 8 * g4);
 #pragma unroll
                 for (int c = 0; c < CTW; ++c) {
                     f32x4 acc;
@@ -613,6 +646,13 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
             for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
         }
         if (lane == 0) sm.red2[par][wave] = m;
+        if (stage_next && !s_wave) {   // T waves, idle in the update: stage the next chunk
+            const int64_t c1 = c0 + CK;
+            float vx1[IPT][8];
+            wait_vm0();
+            stage(sm.kt.nx.Vr, sm.kt.nx.Gr, (int)((end - c1) < CK ? (end - c1) : CK), vx1, true, par ^ 1);
+        }
+        staged = stage_next;
     }
 
     const size_t pair = (size_t)seg * H + h;
