@@ -479,9 +479,8 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
         lds_barrier();
 
         // ---- 3. A = (I + Lp)^-1 to the operand planes of A diag(b) (fp16, and bf16 hi + lo):
-        // the diagonal blocks D0, D1 are in F1 (inverted above) and are converted by all
-        // threads, beside L' to fp16, while one wave forms A10 = -D1 (L10 D0) and converts it
-        // from its accumulators
+        // wave 0 forms A10 = -D1 (L10 D0) and converts it from its accumulators, while the other
+        // threads convert the diagonal blocks D0, D1 (in F1, inverted above) and L' to fp16
         auto put_ap = [&](int t, int s_, float a) {   // a = A[t][s] b_s
             sm.u.p.Ap[t][s_] = f16_bits((_Float16)a);
             put_bf16_split(&sm.u.p.ApB[0][t][s_], &sm.u.p.ApB[1][t][s_], a);
@@ -499,12 +498,28 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) put_ap(16 + 4 * g4 + i, n16, -acc[i] * bn);
         }
-        for (int it = tid; it < CK * CK; it += 512) {
-            const int t = it / CK, s = it % CK;
+        // the other blocks in row pieces of 4: threads 64 .. 64 + CK * CK / 4 - 1, one piece each
+        static_assert(64 + CK * CK / 4 <= 512 && LDF % 4 == 0 && LDT % 4 == 0, "one row piece per thread");
+        if (tid >= 64 && tid < 64 + CK * CK / 4) {
+            const int q = tid - 64, t = q / (CK / 4), s0 = 4 * (q % (CK / 4));
             // L' to fp16 (row-major); the block above the diagonal is never computed
-            sm.u.p.Lpb[t][s] = f16_bits((_Float16)(s < t ? sm.F1p[t][s] : 0.f));
-            if (t >= 16 && s < 16) continue;   // A10: wave 0
-            put_ap(t, s, s <= t ? sm.F1[t][s] * sm.beta[par][s] : 0.f);
+            const f32x4 l = *reinterpret_cast<const f32x4*>(&sm.F1p[t][s0]);
+            *reinterpret_cast<u32x2*>(&sm.u.p.Lpb[t][s0]) =
+                u32x2{cvt2_f16(s0 < t ? l[0] : 0.f, s0 + 1 < t ? l[1] : 0.f),
+                      cvt2_f16(s0 + 2 < t ? l[2] : 0.f, s0 + 3 < t ? l[3] : 0.f)};
+            if (!(t >= 16 && s0 < 16)) {   // (A10: wave 0)
+                const f32x4 f = *reinterpret_cast<const f32x4*>(&sm.F1[t][s0]);
+                const f32x4 b = *reinterpret_cast<const f32x4*>(&sm.beta[par][s0]);
+                float a[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[e] = s0 + e <= t ? f[e] * b[e] : 0.f;
+                *reinterpret_cast<u32x2*>(&sm.u.p.Ap[t][s0]) = u32x2{cvt2_f16(a[0], a[1]), cvt2_f16(a[2], a[3])};
+                uint16_t hi[4], lo[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) put_bf16_split(&hi[e], &lo[e], a[e]);
+                *reinterpret_cast<u32x2*>(&sm.u.p.ApB[0][t][s0]) = u32x2{pack2(hi[0], hi[1]), pack2(hi[2], hi[3])};
+                *reinterpret_cast<u32x2*>(&sm.u.p.ApB[1][t][s0]) = u32x2{pack2(lo[0], lo[1]), pack2(lo[2], lo[3])};
+            }
         }
         lds_barrier();
 
