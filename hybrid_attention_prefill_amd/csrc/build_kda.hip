@@ -249,16 +249,18 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                 x[2 * e] = __uint_as_float((gw[e] << 16) & lm) * kLog2e;
                 x[2 * e + 1] = __uint_as_float(gw[e] & 0xFFFF0000u & lm) * kLog2e;
             }
+            // step-major over the 8 channels, so that consecutive DPP operations are independent
+            // (channel-major, each step waits on the previous one's result)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float a = x[e];
-                a = dpp_add(a, IntConst<0x111>{}, IntConst<0xf>{});   // row_shr:1
-                a = dpp_add(a, IntConst<0x112>{}, IntConst<0xf>{});   // row_shr:2
-                a = dpp_add(a, IntConst<0x114>{}, IntConst<0xf>{});   // row_shr:4
-                a = dpp_add(a, IntConst<0x118>{}, IntConst<0xf>{});   // row_shr:8
-                a = dpp_add(a, IntConst<0x142>{}, IntConst<0xa>{});   // row_bcast:15 into rows 1, 3
-                x[e] = a;
-            }
+            for (int e = 0; e < 8; ++e) x[e] = dpp_add(x[e], IntConst<0x111>{}, IntConst<0xf>{});   // row_shr:1
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = dpp_add(x[e], IntConst<0x112>{}, IntConst<0xf>{});   // row_shr:2
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = dpp_add(x[e], IntConst<0x114>{}, IntConst<0xf>{});   // row_shr:4
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = dpp_add(x[e], IntConst<0x118>{}, IntConst<0xf>{});   // row_shr:8
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = dpp_add(x[e], IntConst<0x142>{}, IntConst<0xa>{});   // row_bcast:15 into rows 1, 3
             *reinterpret_cast<f32x4*>(&sm.Ag[vt + 1][vcg * 8]) = f32x4{x[0], x[1], x[2], x[3]};
             *reinterpret_cast<f32x4*>(&sm.Ag[vt + 1][vcg * 8 + 4]) = f32x4{x[4], x[5], x[6], x[7]};
             if (vt == 0) {
