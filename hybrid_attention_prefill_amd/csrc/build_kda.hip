@@ -24,9 +24,9 @@
 // Gram matrices, which are factored per 16-token row block I around
 // rho_I = c_{16 I}: left e^{c_t - rho_I} <= 1 and right e^{rho_I - c_s}, which is
 // <= 1 off the diagonal block and bounded by one 16-token block's decay on it.
-// Those two Gram matrices, W and every product of the T columns use bf16 hi + lo
-// operands (three products on v_mfma_f32_16x16x32_bf16, fp32 range): with strong
-// per-channel decay the decayed rows of W and Kh leave fp16's range while T is
+// Those two Gram matrices, W (while T is live) and every product of the T columns use
+// bf16 hi + lo operands (three products on v_mfma_f32_16x16x32_bf16, fp32 range): with
+// strong per-channel decay the decayed rows of W and Kh leave fp16's range while T is
 // still far above the floor.  The S columns use fp16 operands with fp32
 // accumulation on v_mfma_f32_16x16x32_f16 (their small entries are negligible
 // next to the fresh writes).  The T columns are renormalised by a power of two
@@ -410,15 +410,20 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                         kh[i] = kx[i][j] * er[i][j] * Q[j];
                         kp[i] = kx[i][j] * er1(i, j) * Q[j];
                     }
-                    unsigned rh[2], rl[2];
+                    if (t_live) {   // (e^{a} o K)^T as bf16 hi / lo (W feeds the T columns)
+                        unsigned rh[2], rl[2];
 #pragma unroll
-                    for (int p2 = 0; p2 < 2; ++p2) {
-                        rh[p2] = cvt2_bf16(rm[2 * p2], rm[2 * p2 + 1]);
-                        const f32x2 hv = bf16x2_to_f32(rh[p2]);
-                        rl[p2] = cvt2_bf16(rm[2 * p2] - hv.x, rm[2 * p2 + 1] - hv.y);
+                        for (int p2 = 0; p2 < 2; ++p2) {
+                            rh[p2] = cvt2_bf16(rm[2 * p2], rm[2 * p2 + 1]);
+                            const f32x2 hv = bf16x2_to_f32(rh[p2]);
+                            rl[p2] = cvt2_bf16(rm[2 * p2] - hv.x, rm[2 * p2 + 1] - hv.y);
+                        }
+                        *reinterpret_cast<u32x2*>(&sm.rv.RmT[0][c + j][t0]) = u32x2{rh[0], rh[1]};
+                        *reinterpret_cast<u32x2*>(&sm.rv.RmT[1][c + j][t0]) = u32x2{rl[0], rl[1]};
+                    } else {        // fp16, in plane 0 (W feeds only the fp16 S products)
+                        *reinterpret_cast<u32x2*>(&sm.rv.RmT[0][c + j][t0]) =
+                            u32x2{cvt2_f16(rm[0], rm[1]), cvt2_f16(rm[2], rm[3])};
                     }
-                    *reinterpret_cast<u32x2*>(&sm.rv.RmT[0][c + j][t0]) = u32x2{rh[0], rh[1]};
-                    *reinterpret_cast<u32x2*>(&sm.rv.RmT[1][c + j][t0]) = u32x2{rl[0], rl[1]};
                     *reinterpret_cast<u32x2*>(&sm.KhT[c + j][t0]) = u32x2{cvt2_f16(kh[0], kh[1]), cvt2_f16(kh[2], kh[3])};
                     *reinterpret_cast<u32x2*>(&sm.KhpT[c + j][t0]) = u32x2{cvt2_f16(kp[0], kp[1]), cvt2_f16(kp[2], kp[3])};
                     if (t_live) {
@@ -483,9 +488,10 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
         // ---- 3. A = (I + Lp)^-1 to the operand planes of A diag(b) (fp16, and bf16 hi + lo):
         // wave 0 forms A10 = -D1 (L10 D0) and converts it from its accumulators, while the other
         // threads convert the diagonal blocks D0, D1 (in F1, inverted above) and L' to fp16
+        // (the bf16 hi / lo planes only while T is live: then W is formed in bf16 hi / lo)
         auto put_ap = [&](int t, int s_, float a) {   // a = A[t][s] b_s
             sm.u.p.Ap[t][s_] = f16_bits((_Float16)a);
-            put_bf16_split(&sm.u.p.ApB[0][t][s_], &sm.u.p.ApB[1][t][s_], a);
+            if (t_live) put_bf16_split(&sm.u.p.ApB[0][t][s_], &sm.u.p.ApB[1][t][s_], a);
         };
         if (wave == 0) {
             // F = L10 D0 in MFMA accumulators (lane (g4, n16) holds rows 4 g4 .. 4 g4 + 3 of
@@ -516,38 +522,50 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) a[e] = s0 + e <= t ? f[e] * b[e] : 0.f;
                 *reinterpret_cast<u32x2*>(&sm.u.p.Ap[t][s0]) = u32x2{cvt2_f16(a[0], a[1]), cvt2_f16(a[2], a[3])};
-                uint16_t hi[4], lo[4];
+                if (t_live) {
+                    uint16_t hi[4], lo[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) put_bf16_split(&hi[e], &lo[e], a[e]);
-                *reinterpret_cast<u32x2*>(&sm.u.p.ApB[0][t][s0]) = u32x2{pack2(hi[0], hi[1]), pack2(hi[2], hi[3])};
-                *reinterpret_cast<u32x2*>(&sm.u.p.ApB[1][t][s0]) = u32x2{pack2(lo[0], lo[1]), pack2(lo[2], lo[3])};
+                    for (int e = 0; e < 4; ++e) put_bf16_split(&hi[e], &lo[e], a[e]);
+                    *reinterpret_cast<u32x2*>(&sm.u.p.ApB[0][t][s0]) = u32x2{pack2(hi[0], hi[1]), pack2(hi[2], hi[3])};
+                    *reinterpret_cast<u32x2*>(&sm.u.p.ApB[1][t][s0]) = u32x2{pack2(lo[0], lo[1]), pack2(lo[2], lo[3])};
+                }
             }
         }
         lds_barrier();
 
         // ---- 4. W^T = Rm^T Ap^T (-> W token-major) and Z1^T = (bV)^T L'^T: wave w takes tiles
         // w, w + 8, ... of each (channel tile t / 2, token tile t % 2, so one token tile per
-        // wave and one shared B fragment); every fragment is read before the first product
+        // wave and one shared B fragment); every fragment is read before the first product.
+        // W takes bf16 hi / lo operands while T is live, fp16 ones once only S is updated (it is
+        // then rounded to fp16 for the S products either way; rows that decay below fp16's range
+        // enter only erase terms of the carried state that are as small).
         {
             constexpr int TPW = RT * 2 / 8;   // W (and Z1) tiles per wave
             static_assert((RT * 2) % 8 == 0, "tiles spread evenly over the waves");
             const int nt = wave % 2;
-            const FragB wb = fragb_at(&sm.u.p.ApB[0][0][0], &sm.u.p.ApB[1][0][0], LDT, nt * 16 + n16, 8 * g4);
             const Frag<1> zb = f16frag(&sm.u.p.Lpb[0][0], LDT, nt * 16 + n16, 8 * g4);
-            FragB wa[TPW];
             Frag<1> za[TPW];
 #pragma unroll
-            for (int c = 0; c < TPW; ++c) {
-                const int mt = (wave + 8 * c) / 2;
-                wa[c] = fragb_at(&sm.rv.RmT[0][0][0], &sm.rv.RmT[1][0][0], LDT, mt * 16 + n16, 8 * g4);
-                za[c] = f16frag(&sm.bVT[0][0], LDT, mt * 16 + n16, 8 * g4);
-            }
+            for (int c = 0; c < TPW; ++c) za[c] = f16frag(&sm.bVT[0][0], LDT, ((wave + 8 * c) / 2) * 16 + n16, 8 * g4);
             f32x4 wacc[TPW], zacc[TPW];
+            if (t_live) {
+                const FragB wb = fragb_at(&sm.u.p.ApB[0][0][0], &sm.u.p.ApB[1][0][0], LDT, nt * 16 + n16, 8 * g4);
+                FragB wa[TPW];
 #pragma unroll
-            for (int c = 0; c < TPW; ++c) {
-                wacc[c] = mma3(wa[c], wb, zero4());
-                zacc[c] = mma<1>(za[c], zb, zero4());
+                for (int c = 0; c < TPW; ++c)
+                    wa[c] = fragb_at(&sm.rv.RmT[0][0][0], &sm.rv.RmT[1][0][0], LDT, ((wave + 8 * c) / 2) * 16 + n16, 8 * g4);
+#pragma unroll
+                for (int c = 0; c < TPW; ++c) wacc[c] = mma3(wa[c], wb, zero4());
+            } else {
+                const Frag<1> wb = f16frag(&sm.u.p.Ap[0][0], LDT, nt * 16 + n16, 8 * g4);
+                Frag<1> wa[TPW];
+#pragma unroll
+                for (int c = 0; c < TPW; ++c) wa[c] = f16frag(&sm.rv.RmT[0][0][0], LDT, ((wave + 8 * c) / 2) * 16 + n16, 8 * g4);
+#pragma unroll
+                for (int c = 0; c < TPW; ++c) wacc[c] = mma<1>(wa[c], wb, zero4());
             }
+#pragma unroll
+            for (int c = 0; c < TPW; ++c) zacc[c] = mma<1>(za[c], zb, zero4());
 #pragma unroll
             for (int c = 0; c < TPW; ++c) {
                 const int mt = (wave + 8 * c) / 2;
