@@ -101,6 +101,7 @@ struct alignas(16) KdaSmem {
         } g;
     } u;
     float red2[2][8];              // per wave: max |T| after a chunk's update (by chunk parity)
+    float bmx[2][4];               // per staging wave: the largest chunk log2-decay b_C it staged (by chunk parity)
 };
 
 __device__ __forceinline__ float bf(uint16_t b) { return bf16_bits_to_f32(b); }
@@ -228,6 +229,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
     // values compiles to branches around each conversion).
     auto stage = [&](uint16_t* vr, const uint16_t* gr, int nn, float (&vx)[IPT][8], bool to_lds, int bpar) {
         const unsigned lm = vt < nn ? 0xFFFFFFFFu : 0u;
+        float bm = -3.0e38f;   // largest b_C over this thread's channels (lanes of token CK - 1)
         const float bt = __uint_as_float(((unsigned)braw << 16) & lm);
         // inclusive scan over the 32 lanes of each half-wave: within rows of 16 lanes by row
         // shifts (lanes shifted in from outside the row read 0), then row 1 (3) adds the total
@@ -268,11 +270,17 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                 *reinterpret_cast<f32x4*>(&sm.Ag[0][vcg * 8 + 4]) = zero4();
             }
             if (vcg == 0) sm.beta[bpar][vt] = bt;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bm = fmaxf(bm, x[e]);
             if (to_lds)
                 *reinterpret_cast<u32x4*>(&vr[i * 8]) =
                     u32x4{cvt2_f16(vx[r][0], vx[r][1]), cvt2_f16(vx[r][2], vx[r][3]),
                           cvt2_f16(vx[r][4], vx[r][5]), cvt2_f16(vx[r][6], vx[r][7])};
         }
+        // lanes 31 and 63 hold token CK - 1: their cumulative values are the chunk totals
+        const float b31 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bm), 31));
+        const float b63 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bm), 63));
+        if (lane == 0) sm.bmx[bpar][wave & 3] = fmaxf(b31, b63);
     };
     bool staged = false;   // the chunk at hand was staged by the T waves during the previous chunk
     if (beg < end && wave < 4) fetch(beg, sm.rv.nx.Vr, sm.rv.nx.Gr);
@@ -334,6 +342,15 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
             }
         }
 
+        // Once T is dropped, a chunk whose decay factors e^{b_C} are all below 2^-8 carries
+        // the state into its update only through terms of that relative size (the decayed
+        // state and its erase); the Gram matrices then matter only through the chunk's own
+        // erase of its fresh writes (a few per cent of them), and their operands are single
+        // bf16 values instead of hi / lo pairs (errors ~2^-9 of those few per cent).
+        bool strong = false;
+        if (!t_live) {
+            strong = fmaxf(fmaxf(sm.bmx[par][0], sm.bmx[par][1]), fmaxf(sm.bmx[par][2], sm.bmx[par][3])) < -8.f;
+        }
         const bool stage_next = !t_live && c0 + CK < end;   // the T waves stage the next chunk
 
         // ---- 2. operands of the decay-weighted Gram matrices and the decay-scaled keys, in one
@@ -390,9 +407,11 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                 // Gram operands, token-major
                 auto put_tok = [&](uint16_t (*Pl)[CK][D + 8], int t, float x0, float x1) {
                     const unsigned hw = cvt2_bf16(x0, x1);
-                    const f32x2 hv = bf16x2_to_f32(hw);
                     *reinterpret_cast<unsigned*>(&Pl[0][t][c]) = hw;
-                    *reinterpret_cast<unsigned*>(&Pl[1][t][c]) = cvt2_bf16(x0 - hv.x, x1 - hv.y);
+                    if (!strong) {
+                        const f32x2 hv = bf16x2_to_f32(hw);
+                        *reinterpret_cast<unsigned*>(&Pl[1][t][c]) = cvt2_bf16(x0 - hv.x, x1 - hv.y);
+                    }
                 };
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -449,16 +468,25 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
             const int t = 16 * I + n16, s = 16 * J + n16;
             const uint16_t(*R)[CK][D + 8] = (lp || E1) ? sm.u.g.GR : sm.u.g.GR1;
             f32x4 acc = zero4();
+            if (strong) {   // single bf16 operands
 #pragma unroll
-            for (int ks = 0; ks < KSD; ++ks) {
-                const int c = ks * 32 + 8 * g4;
-                const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&sm.u.g.GL[0][t][c]);
-                const bf16x8 al = *reinterpret_cast<const bf16x8*>(&sm.u.g.GL[1][t][c]);
-                const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&R[0][s][c]);
-                const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&R[1][s][c]);
-                acc = mma_bf16(ah, bh, acc);
-                acc = mma_bf16(ah, bl, acc);
-                acc = mma_bf16(al, bh, acc);
+                for (int ks = 0; ks < KSD; ++ks) {
+                    const int c = ks * 32 + 8 * g4;
+                    acc = mma_bf16(*reinterpret_cast<const bf16x8*>(&sm.u.g.GL[0][t][c]),
+                                   *reinterpret_cast<const bf16x8*>(&R[0][s][c]), acc);
+                }
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks) {
+                    const int c = ks * 32 + 8 * g4;
+                    const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&sm.u.g.GL[0][t][c]);
+                    const bf16x8 al = *reinterpret_cast<const bf16x8*>(&sm.u.g.GL[1][t][c]);
+                    const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&R[0][s][c]);
+                    const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&R[1][s][c]);
+                    acc = mma_bf16(ah, bh, acc);
+                    acc = mma_bf16(ah, bl, acc);
+                    acc = mma_bf16(al, bh, acc);
+                }
             }
             f32x4 nd;   // -Lp in the accumulator layout (waves 0 and 2: a diagonal block)
 #pragma unroll
