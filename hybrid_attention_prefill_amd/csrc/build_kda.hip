@@ -106,6 +106,25 @@ struct alignas(16) KdaSmem {
 
 __device__ __forceinline__ float bf(uint16_t b) { return bf16_bits_to_f32(b); }
 
+// inv16_t (the transposed (I - N)^-1 by the four-factor product) with single fp16 operands:
+// one product per factor instead of three
+__device__ __forceinline__ f32x4 inv16_t1(const f32x4& nd, const f32x4& nt, int g4, int n16) {
+    auto h = [](const f32x4& x) { return __builtin_bit_cast(f16x4, u32x2{cvt2_f16(x[0], x[1]), cvt2_f16(x[2], x[3])}); };
+    auto mm = [](f16x4 a, f16x4 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0); };
+    const f16x4 n1 = h(nd), n1t = h(nt);
+    const f32x4 n2 = mm(n1t, n1, zero4()), n2t = mm(n1, n1t, zero4());     // N^2, (N^2)^T
+    const f16x4 q2 = h(n2), q2t = h(n2t);
+    f32x4 c1;   // I + N^T + (N^2)^T
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c1[e] = nt[e] + n2t[e] + ((4 * g4 + e == n16) ? 1.f : 0.f);
+    const f32x4 n4 = mm(q2t, q2, zero4()), n4t = mm(q2, q2t, zero4());     // N^4, (N^4)^T
+    const f32x4 p1t = mm(q2, n1t, c1);                                      // P1^T = c1 + (N^2)^T N^T
+    const f16x4 q4 = h(n4), q4t = h(n4t), r1t = h(p1t);
+    const f32x4 n8 = mm(q4t, q4, zero4());                                  // N^8
+    const f32x4 p2t = mm(q4, r1t, p1t);                                     // (P1 (I + N^4))^T
+    return mm(h(n8), h(p2t), p2t);
+}
+
 // fp16 operand fragment: 8 consecutive values at (row, col) of a row-major LDS matrix.
 __device__ __forceinline__ Frag<1> f16frag(const uint16_t* base, int ld, int row, int col) {
     Frag<1> f;
@@ -498,14 +517,15 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                 else sm.F1p[tt][ss] = x;
             }
             if (lp && I == J) {
-                // D_I = (I + Lp_II)^-1 on MFMA in this wave (no barrier): N^T read back from the
+                // D_I = (I + Lp_II)^-1 on MFMA in this wave (no barrier; single fp16 products in
+                // the chunks whose Gram operands are single bf16 values): N^T read back from the
                 // block just written (one wave's LDS accesses complete in order), the inverse
                 // written over the block (row n16: Y[n16][4 g4 .. 4 g4 + 3] = the transposed
                 // result's accumulator entries)
                 const int o = 16 * I;
                 asm volatile("" ::: "memory");
                 const f32x4 lt = *reinterpret_cast<const f32x4*>(&sm.F1[o + n16][o + 4 * g4]);
-                const f32x4 yt = inv16_t(nd, -lt, g4, n16);
+                const f32x4 yt = strong ? inv16_t1(nd, -lt, g4, n16) : inv16_t(nd, -lt, g4, n16);
                 asm volatile("" ::: "memory");
                 *reinterpret_cast<f32x4*>(&sm.F1[o + n16][o + 4 * g4]) = yt;
             }
