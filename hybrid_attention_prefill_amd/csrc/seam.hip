@@ -172,8 +172,10 @@ __global__ __launch_bounds__(256) void seam_prep_kernel(
         const float mo = s <= t ? scale * expf(dts) * gq : 0.f;
         __bf16 x, y;
         split_bf16(mo, x, y);
-        reinterpret_cast<uint16_t*>(rp + R::kM)[frag_off(t, s, W)] = bf16_bits(x);
-        reinterpret_cast<uint16_t*>(rp + R::kM + R::kPlaneM)[frag_off(t, s, W)] = bf16_bits(y);
+        if (t < w) {   // (rows past the window are never read: the chain zeroes them itself)
+            reinterpret_cast<uint16_t*>(rp + R::kM)[frag_off(t, s, W)] = bf16_bits(x);
+            reinterpret_cast<uint16_t*>(rp + R::kM + R::kPlaneM)[frag_off(t, s, W)] = bf16_bits(y);
+        }
         {   // lane-ordered copies: thread (l, e) -> lane l, row t = 4 (l / 16) + e
             const int l = tid >> 2, e = tid & 3, tl = 4 * (l >> 4) + e;
             reinterpret_cast<float*>(rp + R::kEbL)[tid] = expf(bs[tl]);
@@ -234,10 +236,11 @@ __global__ __launch_bounds__(256) void seam_prep_kernel(
         acc = mma_bf16(al, bh, acc);
         if (!in_bf16) acc = mma_bf16(ah, bl, acc);
         if (isu) {   // block cb, lane (g, n): rows 4g .. 4g+3 of column 16 cb + n
-            reinterpret_cast<f32x4*>(rp + R::kU)[cb * 64 + lane] = acc;
+            if (4 * g4 < w) reinterpret_cast<f32x4*>(rp + R::kU)[cb * 64 + lane] = acc;
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
+                if (4 * g4 + e >= w) continue;
                 const int off = frag_off(4 * g4 + e, cb * 16 + n16, D);
                 __bf16 h, l;
                 split_bf16(acc[e], h, l);
@@ -250,7 +253,7 @@ __global__ __launch_bounds__(256) void seam_prep_kernel(
     // plane, their lo planes are neither written nor read)
     {
         constexpr int CG = D / 8;
-        for (int it = tid; it < W * CG; it += 256) {
+        for (int it = tid; it < w * CG; it += 256) {   // (rows past the window are never read)
             const int t = it / CG, c0 = (it % CG) * 8;
             const int off = frag_off(t, c0, D) * 2;
             put_split8(reinterpret_cast<uint16_t*>(rp + R::kQ + off),

@@ -265,24 +265,27 @@ __global__ __launch_bounds__(64 * (DK / 16 + NB / 16)) void seam_chain_kernel(
                     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)slot, 4, 0, 0);
             }
         };
+        // rows past the window (tokens w .. 15) are neither written by the preparation nor
+        // fetched: their lanes' slots were zeroed once, at the start
+        const bool row_on = n16 < sa.w;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int k0 = (ks * 32 + 8 * g4) < DK ? ks * 32 + 8 * g4 : 0;   // past DK: B rows are zero
             const int off = frag_off(n16, k0, DK) * 2;
 #pragma unroll
             for (int p = 0; p < 2; ++p) {   // bf16 inputs have no lo part of k and q
-                item(rec + kRecW + p * kPlaneWD + off, &sw[s][ks][p][0], true);
-                item(rec + kRecK + p * kPlaneWD + off, &sk[s][ks][p][0], p == 0 || f32in);
-                item(rec + kRecQ + p * kPlaneWD + off, &sq[s][ks][p][0], p == 0 || f32in);
+                item(rec + kRecW + p * kPlaneWD + off, &sw[s][ks][p][0], row_on);
+                item(rec + kRecK + p * kPlaneWD + off, &sk[s][ks][p][0], (p == 0 || f32in) && row_on);
+                item(rec + kRecQ + p * kPlaneWD + off, &sq[s][ks][p][0], (p == 0 || f32in) && row_on);
             }
         }
 #pragma unroll
         for (int p = 0; p < 2; ++p)   // lanes g4 >= 2 fetch a duplicate (zeroed at use)
-            item(rec + kRecM + p * kPlaneM + frag_off(n16, 8 * (g4 & 1), 16) * 2, &sm[s][p][0], true);
-        if (!tcol) {   // the transition columns take no U
+            item(rec + kRecM + p * kPlaneM + frag_off(n16, 8 * (g4 & 1), 16) * 2, &sm[s][p][0], row_on);
+        if (!tcol) {   // the transition columns take no U (lane (g4, n16): rows 4 g4 .. 4 g4 + 3)
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct)
-                item(rec + kRecU + ((cb * CT + ct) * 64 + lane) * 16, &su[s][ct][0], true);
+                item(rec + kRecU + ((cb * CT + ct) * 64 + lane) * 16, &su[s][ct][0], 4 * g4 < sa.w);
         }
         item(rec + kRecEbwL + lane * 16, &su[s][CT][0], true);
         item(rec + kRecEbL + lane * 16, &su[s][CT + 1][0], true);
@@ -293,6 +296,23 @@ __global__ __launch_bounds__(64 * (DK / 16 + NB / 16)) void seam_chain_kernel(
     Step st;
     if (win) {
         if (wct == 0) {
+            // the slots of rows past the window, which no fetch writes, hold zeros
+#pragma unroll
+            for (int s = 0; s < kStages; ++s) {
+                if (n16 >= sa.w) {
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                        for (int p = 0; p < 2; ++p)
+                            sw[s][ks][p][lane] = sk[s][ks][p][lane] = sq[s][ks][p][lane] = u32x4{0, 0, 0, 0};
+#pragma unroll
+                    for (int p = 0; p < 2; ++p) sm[s][p][lane] = u32x4{0, 0, 0, 0};
+                }
+                if (4 * g4 >= sa.w) {
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) su[s][ct][lane] = zero4();
+                }
+            }
             fetch_window(j0);
             fetch_window(j0 + 1);
             __builtin_amdgcn_s_waitcnt(kWaitAll);

@@ -8,7 +8,9 @@
 
 namespace hypic {
 
-constexpr int kSeamMaxW = 16;  // windows are padded to 16 tokens
+constexpr int kSeamMaxW = 16;  // windows are padded to 16 tokens; the rows of tokens w .. 15 of
+                                // the W, q, k, Mo and U parts are neither written nor read (the
+                                // chain kernel keeps zeros in their place)
 
 template <int D>
 struct SeamRec {
