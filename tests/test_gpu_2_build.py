@@ -147,6 +147,27 @@ def test_kda_ragged(stress):
     print(f"{W.name}: S {eS:.2e} T {eT}")
 
 
+@pytest.mark.parametrize("switch", [1024, 1040])
+def test_kda_decay_weakens_after_T_is_dropped(switch):
+    """KDA segments of 2048 tokens whose gates decay strongly up to token `switch` (T falls
+    below the floor and is dropped within the first chunks) and weakly after it (chunk decay
+    factors near 1).  The chunks after the switch take the S-only path without the
+    strong-decay operand precision (single bf16 Gram operands, single fp16 inverses), which
+    holds only while every chunk decay factor is below 2^-8; S is checked against the oracle
+    for every (segment, head)."""
+    W = wl.make("kda-32h-d128-131k", n_heads=2, n_seg=2, n_req=1, n_step=1, n_layers=1)
+    g = np.array(W.g, dtype=np.float64)
+    for b, e in zip(W.cache_begin, W.cache_end):
+        g[b + switch:e] *= 1e-3
+    W.g = wl._finish(g, "bf16")
+    print(W.name, "weak after", switch, flush=True)
+    T, S = _gpu_build(W)
+    T0, S0 = _oracle_build(W)
+    assert np.all(np.sqrt(np.sum(T0.astype(np.float64) ** 2, axis=(-2, -1))) < 1e-30)   # T dropped
+    eS, _ = assert_pairs_close(T, S, T0, S0, TOL["bf16"], f"{W.name} weak after {switch}")
+    print(f"S rel_F max {eS:.2e}")
+
+
 def test_kda_stress_compose_matches_full():
     W = wl.make("kda-32h-d128-131k", stress=True, n_heads=2, n_seg=4, seg_len=300, n_req=1, n_step=1, n_layers=1)
     T, S = _gpu_build(W)
