@@ -46,7 +46,7 @@ __device__ __forceinline__ f32x4 inv16_t(const f32x4& nd, const f32x4& nt, int g
     const Hl16 q2 = hl16(n2), q2t = hl16(n2t);
     f32x4 c1;   // I + N^T + (N^2)^T
 #pragma unroll
-    for (int e = 0; e < 4; ++e) c1[e] = nt[e] + n2t[e] + ((4 * g4 + e == n16) ? 1.f : 0.f);
+    for (int e = 0; e < 4; ++e) c1[e] = nt[e] + n2t[e] + ((4 * g4 + e == opaque(n16)) ? 1.f : 0.f);   // (formed here, not kept)
     const f32x4 n4 = mm16(q2t, q2), n4t = mm16(q2, q2t);                    // N^4, (N^4)^T
     const f32x4 p1t = mma16(q2.h, q2.l, n1t.h, n1t.l, c1);                  // P1^T = c1 + (N^2)^T N^T
     const Hl16 q4 = hl16(n4), q4t = hl16(n4t), r1t = hl16(p1t);

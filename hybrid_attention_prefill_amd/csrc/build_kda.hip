@@ -116,7 +116,7 @@ __device__ __forceinline__ f32x4 inv16_t1(const f32x4& nd, const f32x4& nt, int 
     const f16x4 q2 = h(n2), q2t = h(n2t);
     f32x4 c1;   // I + N^T + (N^2)^T
 #pragma unroll
-    for (int e = 0; e < 4; ++e) c1[e] = nt[e] + n2t[e] + ((4 * g4 + e == n16) ? 1.f : 0.f);
+    for (int e = 0; e < 4; ++e) c1[e] = nt[e] + n2t[e] + ((4 * g4 + e == opaque(n16)) ? 1.f : 0.f);   // (formed here, not kept)
     const f32x4 n4 = mm(q2t, q2, zero4()), n4t = mm(q2, q2t, zero4());     // N^4, (N^4)^T
     const f32x4 p1t = mm(q2, n1t, c1);                                      // P1^T = c1 + (N^2)^T N^T
     const f16x4 q4 = h(n4), q4t = h(n4t), r1t = h(p1t);
@@ -124,6 +124,13 @@ __device__ __forceinline__ f32x4 inv16_t1(const f32x4& nd, const f32x4& nt, int 
     const f32x4 p2t = mm(q4, r1t, p1t);                                     // (P1 (I + N^4))^T
     return mm(h(n8), h(p2t), p2t);
 }
+
+// The channel-major key planes ((e^{a} o K)^T, Kh^T, Kh'^T; [D][LDT] 16-bit) hold row r's
+// 16-byte token chunk q at chunk q ^ ((r >> 3) & 3): the operand pass stores 4 tokens of a
+// channel pair per lane with rows two apart across the lanes, which without the swizzle fall on
+// 8 of the 32 banks (4-way conflicts; 2-way with it, by a bank model), while the 16-byte
+// fragment reads of 16 consecutive rows stay conflict-free.
+__device__ __forceinline__ int kswz(int row, int t) { return (((t >> 3) ^ ((row >> 3) & 3)) << 3) | (t & 7); }
 
 // fp16 operand fragment: 8 consecutive values at (row, col) of a row-major LDS matrix.
 __device__ __forceinline__ Frag<1> f16frag(const uint16_t* base, int ld, int row, int col) {
@@ -438,7 +445,9 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                     put_tok(sm.u.g.GR, t0 + i, kx[i][0] * er[i][0], kx[i][1] * er[i][1]);
                     if (!E1) put_tok(sm.u.g.GR1, t0 + i, kx[i][0] * er1(i, 0), kx[i][1] * er1(i, 1));
                 }
-                // key operands, channel-major: 4 consecutive tokens of one channel per store
+                // key operands, channel-major: 4 consecutive tokens of one channel per store, at
+                // the swizzled column of rows c and c + 1 (the same for both)
+                const int tsw = kswz(opaque(c), t0);
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     float rm[4], kh[4], kp[4];
@@ -456,14 +465,14 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                             const f32x2 hv = bf16x2_to_f32(rh[p2]);
                             rl[p2] = cvt2_bf16(rm[2 * p2] - hv.x, rm[2 * p2 + 1] - hv.y);
                         }
-                        *reinterpret_cast<u32x2*>(&sm.rv.RmT[0][c + j][t0]) = u32x2{rh[0], rh[1]};
-                        *reinterpret_cast<u32x2*>(&sm.rv.RmT[1][c + j][t0]) = u32x2{rl[0], rl[1]};
+                        *reinterpret_cast<u32x2*>(&sm.rv.RmT[0][c + j][tsw]) = u32x2{rh[0], rh[1]};
+                        *reinterpret_cast<u32x2*>(&sm.rv.RmT[1][c + j][tsw]) = u32x2{rl[0], rl[1]};
                     } else {        // fp16, in plane 0 (W feeds only the fp16 S products)
-                        *reinterpret_cast<u32x2*>(&sm.rv.RmT[0][c + j][t0]) =
+                        *reinterpret_cast<u32x2*>(&sm.rv.RmT[0][c + j][tsw]) =
                             u32x2{cvt2_f16(rm[0], rm[1]), cvt2_f16(rm[2], rm[3])};
                     }
-                    *reinterpret_cast<u32x2*>(&sm.KhT[c + j][t0]) = u32x2{cvt2_f16(kh[0], kh[1]), cvt2_f16(kh[2], kh[3])};
-                    *reinterpret_cast<u32x2*>(&sm.KhpT[c + j][t0]) = u32x2{cvt2_f16(kp[0], kp[1]), cvt2_f16(kp[2], kp[3])};
+                    *reinterpret_cast<u32x2*>(&sm.KhT[c + j][tsw]) = u32x2{cvt2_f16(kh[0], kh[1]), cvt2_f16(kh[2], kh[3])};
+                    *reinterpret_cast<u32x2*>(&sm.KhpT[c + j][tsw]) = u32x2{cvt2_f16(kp[0], kp[1]), cvt2_f16(kp[2], kp[3])};
                     if (t_live) {
                         unsigned khh[2], khl[2];
 #pragma unroll
@@ -472,8 +481,8 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                             const f32x2 hv = bf16x2_to_f32(khh[p2]);
                             khl[p2] = cvt2_bf16(kh[2 * p2] - hv.x, kh[2 * p2 + 1] - hv.y);
                         }
-                        *reinterpret_cast<u32x2*>(&sm.kt.KhTb[0][c + j][t0]) = u32x2{khh[0], khh[1]};
-                        *reinterpret_cast<u32x2*>(&sm.kt.KhTb[1][c + j][t0]) = u32x2{khl[0], khl[1]};
+                        *reinterpret_cast<u32x2*>(&sm.kt.KhTb[0][c + j][tsw]) = u32x2{khh[0], khh[1]};
+                        *reinterpret_cast<u32x2*>(&sm.kt.KhTb[1][c + j][tsw]) = u32x2{khl[0], khl[1]};
                     }
                 }
             }
@@ -557,7 +566,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
         // the other blocks in row pieces of 4: threads 64 .. 64 + CK * CK / 4 - 1, one piece each
         static_assert(64 + CK * CK / 4 <= 512 && LDF % 4 == 0 && LDT % 4 == 0, "one row piece per thread");
         if (tid >= 64 && tid < 64 + CK * CK / 4) {
-            const int q = tid - 64, t = q / (CK / 4), s0 = 4 * (q % (CK / 4));
+            const int q = opaque(tid) - 64, t = q / (CK / 4), s0 = 4 * (q % (CK / 4));   // (addresses formed here)
             // L' to fp16 (row-major); the block above the diagonal is never computed
             const f32x4 l = *reinterpret_cast<const f32x4*>(&sm.F1p[t][s0]);
             *reinterpret_cast<u32x2*>(&sm.u.p.Lpb[t][s0]) =
@@ -596,19 +605,21 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
 #pragma unroll
             for (int c = 0; c < TPW; ++c) za[c] = f16frag(&sm.bVT[0][0], LDT, ((wave + 8 * c) / 2) * 16 + n16, 8 * g4);
             f32x4 wacc[TPW], zacc[TPW];
+            // swizzled fragment column of rows 16 mt + n16, mt = wave / 2 + 4 c (the same for every c)
+            const int rcol = kswz((wave / 2) * 16 + opaque(n16), 8 * g4);
             if (t_live) {
                 const FragB wb = fragb_at(&sm.u.p.ApB[0][0][0], &sm.u.p.ApB[1][0][0], LDT, nt * 16 + n16, 8 * g4);
                 FragB wa[TPW];
 #pragma unroll
                 for (int c = 0; c < TPW; ++c)
-                    wa[c] = fragb_at(&sm.rv.RmT[0][0][0], &sm.rv.RmT[1][0][0], LDT, ((wave + 8 * c) / 2) * 16 + n16, 8 * g4);
+                    wa[c] = fragb_at(&sm.rv.RmT[0][0][0], &sm.rv.RmT[1][0][0], LDT, ((wave + 8 * c) / 2) * 16 + n16, rcol);
 #pragma unroll
                 for (int c = 0; c < TPW; ++c) wacc[c] = mma3(wa[c], wb, zero4());
             } else {
                 const Frag<1> wb = f16frag(&sm.u.p.Ap[0][0], LDT, nt * 16 + n16, 8 * g4);
                 Frag<1> wa[TPW];
 #pragma unroll
-                for (int c = 0; c < TPW; ++c) wa[c] = f16frag(&sm.rv.RmT[0][0][0], LDT, ((wave + 8 * c) / 2) * 16 + n16, 8 * g4);
+                for (int c = 0; c < TPW; ++c) wa[c] = f16frag(&sm.rv.RmT[0][0][0], LDT, ((wave + 8 * c) / 2) * 16 + n16, rcol);
 #pragma unroll
                 for (int c = 0; c < TPW; ++c) wacc[c] = mma<1>(wa[c], wb, zero4());
             }
@@ -636,6 +647,9 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
 
         if (t_live && c0 + CK < end && wave < 4)   // Kb and RmT are not read again in this chunk
             fetch(c0 + CK, sm.rv.nx.Vr, sm.rv.nx.Gr);
+        // fragment column of the swizzled key planes for rows 16 rt + n16: kswz gives chunk
+        // g4 ^ ((2 rt + n16 / 8) & 3), one of two values by the parity of rt
+        const int kcol0 = 8 * (g4 ^ (n16 >> 3)), kcol1 = kcol0 ^ 16;
         // ---- 5. update of the owned column tiles: Y = W X, R = -(Y [+ U]),
         // X <- e^{b_C} X + Kh^T R [+ Kh'^T bV].  The k-blocks of X are converted to B fragments
         // as they are used; each A fragment is read once for all CTW tiles.
@@ -672,8 +686,8 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
                 const f32x4 eb = *reinterpret_cast<const f32x4*>(&sm.eBC[rt * 16 + 4 * g4]);
-                const Frag<1> a = f16frag(&sm.KhT[0][0], LDT, rt * 16 + n16, 8 * g4);
-                const Frag<1> a2 = f16frag(&sm.KhpT[0][0], LDT, rt * 16 + n16, 8 * g4);
+                const Frag<1> a = f16frag(&sm.KhT[0][0], LDT, rt * 16 + n16, (rt & 1) ? kcol1 : kcol0);
+                const Frag<1> a2 = f16frag(&sm.KhpT[0][0], LDT, rt * 16 + n16, (rt & 1) ? kcol1 : kcol0);
 #pragma unroll
                 for (int c = 0; c < CTW; ++c) {
                     f32x4 acc;
@@ -704,7 +718,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
                 const f32x4 eb = *reinterpret_cast<const f32x4*>(&sm.eBC[rt * 16 + 4 * g4]) * tsc;
-                const FragB a = fragb_at(&sm.kt.KhTb[0][0][0], &sm.kt.KhTb[1][0][0], LDT, rt * 16 + n16, 8 * g4);
+                const FragB a = fragb_at(&sm.kt.KhTb[0][0][0], &sm.kt.KhTb[1][0][0], LDT, rt * 16 + n16, (rt & 1) ? kcol1 : kcol0);
 #pragma unroll
                 for (int c = 0; c < CTW; ++c) {
                     f32x4 acc;
