@@ -168,6 +168,37 @@ def test_seam_scan_without_pairs():
     assert rel_f(R, S).max() <= TOL["bf16"]
 
 
+def test_long_chain_composition_through_the_scan():
+    """One long chain of compositions without windows (every seam_start -1) through
+    hypic_seam_advance, which runs it as a blocked scan: the 32 x 1024 stress pairs at 16 heads
+    composed along 128 steps (each pair four times, out of order) equal the serial
+    hypic_compose and the fp64 composition of the same pairs."""
+    W = wl.make("gdn-16h-d128-32k", stress=True)
+    x = workload_tensors(W)
+    T, S = hb.segment_build(x["k"], x["v"], x["g"], x["beta"], dev(W.cache_begin, torch.int64),
+                            dev(W.cache_end, torch.int64), gate=W.gate, delta=W.delta, t_layout=hb.T_SPLIT)
+    rng = np.random.default_rng(17)
+    ids = np.concatenate([rng.permutation(32) for _ in range(4)]).astype(np.int32)[None, :]
+    pid = dev(ids, torch.int32)
+    H, d, n_step = W.n_heads, 128, ids.shape[1]
+    R_ser = torch.zeros((1, H, d, d), device="cuda")
+    hb.compose(T, S, pid, R_ser)
+    R_scan = torch.zeros_like(R_ser)
+    out = torch.zeros((1, n_step, 8, H, d), device="cuda")
+    ws = torch.empty(hb.seam_workspace_bytes(H, d, d, 1, n_step, 8), dtype=torch.uint8, device="cuda")
+    hb.seam_advance(x["k"], x["k"], x["v"], x["g"], x["beta"], dev(np.full((1, n_step), -1, np.int64), torch.int64),
+                    R_scan, out, gate=W.gate, delta=W.delta, w=8, scale=1.0, pair_id=pid, T_cache=T, S_cache=S,
+                    workspace=ws)
+    torch.cuda.synchronize()
+    T0, S0 = oracle.segment_build(W.k, W.v, W.g, W.beta, W.cache_begin, W.cache_end, gate=W.gate, delta=W.delta)
+    ref = oracle.compose(T0, S0, ids)[0]
+    e_scan = rel_f(R_scan.cpu().numpy()[0], ref).max()
+    e_ser = rel_f(R_ser.cpu().numpy()[0], ref).max()
+    print(f"128-step chain: scan {e_scan:.2e}, serial {e_ser:.2e}")
+    assert e_scan <= TOL["bf16"] and e_ser <= TOL["bf16"]
+    assert np.all(out.cpu().numpy() == 0)   # no window: no output row is written
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_seam_scan_two_chains_mixed_plan(d):
     """Two chains from nonzero states; chain 1 skips some windows and some pairs and
