@@ -147,6 +147,21 @@ def test_kda_ragged(stress):
     print(f"{W.name}: S {eS:.2e} T {eT}")
 
 
+@pytest.mark.parametrize("gate_first", [False, True])
+def test_kda_ragged_tails_after_T_is_dropped(gate_first):
+    """KDA segments long enough for T to be dropped (after a few chunks on the default gates)
+    that end in a partial chunk, so the chunks after the drop -- staged during the previous
+    chunk by the waves that held T -- include ragged tails: 300, 1000 and 2050 tokens, and a
+    segment of exactly 7 chunks.  Every (segment, head) against the oracle."""
+    W = wl.make("kda-32h-d128-131k", gate_first=gate_first, n_heads=2, lengths=[300, 1000, 2050, 224],
+                n_req=1, n_step=1, n_layers=1)
+    print(W.name, "ragged tails after the drop", flush=True)
+    T, S = _gpu_build(W)
+    T0, S0 = _oracle_build(W)
+    eS, _ = assert_pairs_close(T, S, T0, S0, TOL["bf16"], W.name)
+    print(f"S rel_F max {eS:.2e}")
+
+
 @pytest.mark.parametrize("switch", [1024, 1040])
 def test_kda_decay_weakens_after_T_is_dropped(switch):
     """KDA segments of 2048 tokens whose gates decay strongly up to token `switch` (T falls
