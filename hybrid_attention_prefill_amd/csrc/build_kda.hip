@@ -390,7 +390,11 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
         // = e^{rho - c_{t+1}} is the next token's e^{rho - c}, so a 4-token item takes 11
         // exponentials per channel instead of 24.  Gram operands go token-major (4-byte stores of
         // the channel pair), key operands channel-major (8-byte stores of the 4 tokens).
-        {
+        // The pass is instantiated once per precision mode (LIVE: T is live; LO: Gram operands
+        // as hi / lo pairs), so that each form is straight-line code: a uniform branch per
+        // store kept every exponential next to its store, one dependent chain at a time.
+        auto operand_pass = [&](auto live_c, auto lo_c) {
+            constexpr bool LIVE = decltype(live_c)::value != 0, LO = decltype(lo_c)::value != 0;
             constexpr int NCP = D / 2;                 // channel pairs
             static_assert((CK / 4) * NCP <= 512, "one item per thread");
             if (tid < (CK / 4) * NCP) {
@@ -423,10 +427,6 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                     P[j] = exp2_raw(rho[j]);
                     Q[j] = exp2_raw(bc[j] - rho[j]);
                 }
-                if (t0 == 0) {   // e^{b_C} (wave 0)
-                    sm.eBC[c] = exp2_raw(bc[0]);
-                    sm.eBC[c + 1] = exp2_raw(bc[1]);
-                }
                 // e^{rho - i_t}: the next token's e^{rho - c} (gate after the erase); e^{rho - c_t}
                 // itself when the gate comes first (i = c for the erase vectors then)
                 auto er1 = [&](int i, int j) { return E1 ? er[i][j] : er[i + 1][j]; };
@@ -434,7 +434,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                 auto put_tok = [&](uint16_t (*Pl)[CK][D + 8], int t, float x0, float x1) {
                     const unsigned hw = cvt2_bf16(x0, x1);
                     *reinterpret_cast<unsigned*>(&Pl[0][t][c]) = hw;
-                    if (!strong) {
+                    if constexpr (LO) {
                         const f32x2 hv = bf16x2_to_f32(hw);
                         *reinterpret_cast<unsigned*>(&Pl[1][t][c]) = cvt2_bf16(x0 - hv.x, x1 - hv.y);
                     }
@@ -457,7 +457,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                         kh[i] = kx[i][j] * er[i][j] * Q[j];
                         kp[i] = kx[i][j] * er1(i, j) * Q[j];
                     }
-                    if (t_live) {   // (e^{a} o K)^T as bf16 hi / lo (W feeds the T columns)
+                    if constexpr (LIVE) {   // (e^{a} o K)^T as bf16 hi / lo (W feeds the T columns)
                         unsigned rh[2], rl[2];
 #pragma unroll
                         for (int p2 = 0; p2 < 2; ++p2) {
@@ -473,7 +473,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                     }
                     *reinterpret_cast<u32x2*>(&sm.KhT[c + j][tsw]) = u32x2{cvt2_f16(kh[0], kh[1]), cvt2_f16(kh[2], kh[3])};
                     *reinterpret_cast<u32x2*>(&sm.KhpT[c + j][tsw]) = u32x2{cvt2_f16(kp[0], kp[1]), cvt2_f16(kp[2], kp[3])};
-                    if (t_live) {
+                    if constexpr (LIVE) {
                         unsigned khh[2], khl[2];
 #pragma unroll
                         for (int p2 = 0; p2 < 2; ++p2) {
@@ -485,8 +485,15 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                         *reinterpret_cast<u32x2*>(&sm.kt.KhTb[1][c + j][tsw]) = u32x2{khl[0], khl[1]};
                     }
                 }
+                if (t0 == 0) {   // e^{b_C} (wave 0)
+                    sm.eBC[c] = exp2_raw(bc[0]);
+                    sm.eBC[c + 1] = exp2_raw(bc[1]);
+                }
             }
-        }
+        };
+        if (t_live) operand_pass(IntConst<1>{}, IntConst<1>{});
+        else if (!strong) operand_pass(IntConst<0>{}, IntConst<1>{});
+        else operand_pass(IntConst<0>{}, IntConst<0>{});
         lds_barrier();
         // the six Gram tiles Lp (waves 0-2) and L' (waves 3-5), bf16 hi + lo
         if (wave < 6) {
