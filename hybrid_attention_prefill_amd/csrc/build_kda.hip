@@ -524,13 +524,15 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                 }
             }
             f32x4 nd;   // -Lp in the accumulator layout (waves 0 and 2: a diagonal block)
+            // (the destination and the beta factor selected per wave, so the stores need no branch)
+            float(*F)[LDF] = lp ? sm.F1 : sm.F1p;
+            const f32x4 b4 = *reinterpret_cast<const f32x4*>(&sm.beta[par][16 * I + 4 * g4]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int tt = 16 * I + 4 * g4 + e, ss = 16 * J + n16;
-                const float x = ss < tt ? (lp ? sm.beta[par][tt] : 1.f) * acc[e] : 0.f;
+                const float x = ss < tt ? (lp ? b4[e] : 1.f) * acc[e] : 0.f;
                 nd[e] = -x;
-                if (lp) sm.F1[tt][ss] = x;
-                else sm.F1p[tt][ss] = x;
+                F[tt][ss] = x;
             }
             if (lp && I == J) {
                 // D_I = (I + Lp_II)^-1 on MFMA in this wave (no barrier; single fp16 products in
@@ -553,9 +555,9 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
         // wave 0 forms A10 = -D1 (L10 D0) and converts it from its accumulators, while the other
         // threads convert the diagonal blocks D0, D1 (in F1, inverted above) and L' to fp16
         // (the bf16 hi / lo planes only while T is live: then W is formed in bf16 hi / lo)
-        auto put_ap = [&](int t, int s_, float a) {   // a = A[t][s] b_s
+        auto put_ap = [&](int t, int s_, float a, auto live_c) {   // a = A[t][s] b_s
             sm.u.p.Ap[t][s_] = f16_bits((_Float16)a);
-            if (t_live) put_bf16_split(&sm.u.p.ApB[0][t][s_], &sm.u.p.ApB[1][t][s_], a);
+            if constexpr (decltype(live_c)::value != 0) put_bf16_split(&sm.u.p.ApB[0][t][s_], &sm.u.p.ApB[1][t][s_], a);
         };
         if (wave == 0) {
             // F = L10 D0 in MFMA accumulators (lane (g4, n16) holds rows 4 g4 .. 4 g4 + 3 of
@@ -567,12 +569,19 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
             for (int kb = 0; kb < 4; ++kb)
                 acc = mma_f32(sm.F1[16 + n16][16 + 4 * g4 + kb], f[kb], acc);
             const float bn = sm.beta[par][n16];
+            if (t_live) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) put_ap(16 + 4 * g4 + i, n16, -acc[i] * bn);
+                for (int i = 0; i < 4; ++i) put_ap(16 + 4 * g4 + i, n16, -acc[i] * bn, IntConst<1>{});
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) put_ap(16 + 4 * g4 + i, n16, -acc[i] * bn, IntConst<0>{});
+            }
         }
         // the other blocks in row pieces of 4: threads 64 .. 64 + CK * CK / 4 - 1, one piece each
+        // (instantiated with and without the bf16 hi / lo planes, so each form is straight-line)
         static_assert(64 + CK * CK / 4 <= 512 && LDF % 4 == 0 && LDT % 4 == 0, "one row piece per thread");
-        if (tid >= 64 && tid < 64 + CK * CK / 4) {
+        auto convert = [&](auto live_c) {
+            constexpr bool LIVE = decltype(live_c)::value != 0;
             const int q = opaque(tid) - 64, t = q / (CK / 4), s0 = 4 * (q % (CK / 4));   // (addresses formed here)
             // L' to fp16 (row-major); the block above the diagonal is never computed
             const f32x4 l = *reinterpret_cast<const f32x4*>(&sm.F1p[t][s0]);
@@ -586,7 +595,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) a[e] = s0 + e <= t ? f[e] * b[e] : 0.f;
                 *reinterpret_cast<u32x2*>(&sm.u.p.Ap[t][s0]) = u32x2{cvt2_f16(a[0], a[1]), cvt2_f16(a[2], a[3])};
-                if (t_live) {
+                if constexpr (LIVE) {
                     uint16_t hi[4], lo[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) put_bf16_split(&hi[e], &lo[e], a[e]);
@@ -594,6 +603,10 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                     *reinterpret_cast<u32x2*>(&sm.u.p.ApB[1][t][s0]) = u32x2{pack2(lo[0], lo[1]), pack2(lo[2], lo[3])};
                 }
             }
+        };
+        if (tid >= 64 && tid < 64 + CK * CK / 4) {
+            if (t_live) convert(IntConst<1>{});
+            else convert(IntConst<0>{});
         }
         lds_barrier();
 
@@ -622,6 +635,15 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                     wa[c] = fragb_at(&sm.rv.RmT[0][0][0], &sm.rv.RmT[1][0][0], LDT, ((wave + 8 * c) / 2) * 16 + n16, rcol);
 #pragma unroll
                 for (int c = 0; c < TPW; ++c) wacc[c] = mma3(wa[c], wb, zero4());
+#pragma unroll
+                for (int c = 0; c < TPW; ++c) {   // W as bf16 hi / lo (T columns)
+                    const int row = nt * 16 + n16, col = ((wave + 8 * c) / 2) * 16 + 4 * g4;
+                    uint16_t bh[4], bl[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) put_bf16_split(&bh[e], &bl[e], wacc[c][e]);
+                    *reinterpret_cast<u32x2*>(&sm.u.p.WpB[0][row][col]) = u32x2{pack2(bh[0], bh[1]), pack2(bh[2], bh[3])};
+                    *reinterpret_cast<u32x2*>(&sm.u.p.WpB[1][row][col]) = u32x2{pack2(bl[0], bl[1]), pack2(bl[2], bl[3])};
+                }
             } else {
                 const Frag<1> wb = f16frag(&sm.u.p.Ap[0][0], LDT, nt * 16 + n16, 8 * g4);
                 Frag<1> wa[TPW];
@@ -638,13 +660,6 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
                 const f32x4 acc = wacc[c];
                 const int row = nt * 16 + n16, col = mt * 16 + 4 * g4;
                 *reinterpret_cast<u32x2*>(&sm.u.p.Wp[row][col]) = u32x2{cvt2_f16(acc[0], acc[1]), cvt2_f16(acc[2], acc[3])};
-                if (t_live) {
-                    uint16_t bh[4], bl[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) put_bf16_split(&bh[e], &bl[e], acc[e]);
-                    *reinterpret_cast<u32x2*>(&sm.u.p.WpB[0][row][col]) = u32x2{pack2(bh[0], bh[1]), pack2(bh[2], bh[3])};
-                    *reinterpret_cast<u32x2*>(&sm.u.p.WpB[1][row][col]) = u32x2{pack2(bl[0], bl[1]), pack2(bl[2], bl[3])};
-                }
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     sm.u.p.Z1T[mt * 16 + 4 * g4 + e][nt * 16 + n16] = f16_bits((_Float16)zacc[c][e]);
