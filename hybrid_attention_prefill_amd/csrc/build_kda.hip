@@ -291,10 +291,6 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
             for (int e = 0; e < 8; ++e) x[e] = dpp_add(x[e], IntConst<0x142>{}, IntConst<0xa>{});   // row_bcast:15 into rows 1, 3
             *reinterpret_cast<f32x4*>(&sm.Ag[vt + 1][vcg * 8]) = f32x4{x[0], x[1], x[2], x[3]};
             *reinterpret_cast<f32x4*>(&sm.Ag[vt + 1][vcg * 8 + 4]) = f32x4{x[4], x[5], x[6], x[7]};
-            if (vt == 0) {
-                *reinterpret_cast<f32x4*>(&sm.Ag[0][vcg * 8]) = zero4();
-                *reinterpret_cast<f32x4*>(&sm.Ag[0][vcg * 8 + 4]) = zero4();
-            }
             if (vcg == 0) sm.beta[bpar][vt] = bt;
 #pragma unroll
             for (int e = 0; e < 8; ++e) bm = fmaxf(bm, x[e]);
@@ -310,6 +306,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
     };
     bool staged = false;   // the chunk at hand was staged by the T waves during the previous chunk
     if (beg < end && wave < 4) fetch(beg, sm.rv.nx.Vr, sm.rv.nx.Gr);
+    for (int c = tid; c < D; c += 512) sm.Ag[0][c] = 0.f;   // row 0 (exclusive gate of token 0) stays zero
     for (int64_t c0 = beg; c0 < end; c0 += CK) {
         const int n = (int)((end - c0) < CK ? (end - c0) : CK);
         const int par = (int)(((c0 - beg) / CK) & 1);   // chunk parity (betas, renormalisation records)
@@ -326,24 +323,33 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
         // (diag(b) V)^T, fp16 (first read in the W and Z1 phase), by the staging waves for
         // their items: from registers, or, when staged during the previous chunk, from the fp16
         // values over v
-        if (staged ? wave >= 4 : wave < 4) {
+        auto put_bvt = [&](int r, const uint16_t (&hv)[8]) {
+            const int vcg = ((wave & 3) * 64 + lane + 256 * r) / CK;
 #pragma unroll
-            for (int r = 0; r < IPT; ++r) {
-                const int i = (wave & 3) * 64 + lane + 256 * r, vcg = i / CK;
-                uint16_t hv[8];
-                if (staged) {
+            for (int e = 0; e < 8; ++e) sm.bVT[vcg * 8 + e][vt] = hv[e];
+        };
+        if (staged) {
+            if (wave >= 4) {
+#pragma unroll
+                for (int r = 0; r < IPT; ++r) {
+                    const int i = (wave & 3) * 64 + lane + 256 * r;
                     const u32x4 w4 = *reinterpret_cast<const u32x4*>(&sm.kt.nx.Vr[i * 8]);
+                    uint16_t hv[8];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         hv[2 * e] = (uint16_t)(w4[e] & 0xFFFFu);
                         hv[2 * e + 1] = (uint16_t)(w4[e] >> 16);
                     }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) hv[e] = f16_bits((_Float16)vx[r][e]);
+                    put_bvt(r, hv);
                 }
+            }
+        } else if (wave < 4) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) sm.bVT[vcg * 8 + e][vt] = hv[e];
+            for (int r = 0; r < IPT; ++r) {
+                uint16_t hv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) hv[e] = f16_bits((_Float16)vx[r][e]);
+                put_bvt(r, hv);
             }
         }
 
