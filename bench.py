@@ -432,7 +432,9 @@ def main():
 
 
 # Sources of the kernels each library call launches (a stored counter measurement is
-# reported only while these files are unchanged).
+# reported only while these files are unchanged); a segment build launches the kernels of
+# its workload's transition family only.
+BUILD_SOURCES = {"kda": ["build_kda.hip"], "gdn": ["build_gdn.hip", "build_split.hip"]}
 CALL_SOURCES = {
     "seam_advance": ["seam.hip", "seam_chain.hip", "seam_layout.h", "compose.hip", "hypic_device.h", "hypic_kernels.h"],
     "compose": ["compose.hip", "hypic_device.h", "hypic_kernels.h"],
@@ -443,10 +445,17 @@ CALL_SOURCES = {
 }
 
 
-def sources_digest(call):
+def call_sources(call, workload):
+    fam = workload.split("-")[0]
+    if call == "segment_build" and fam in BUILD_SOURCES:
+        return BUILD_SOURCES[fam] + ["build_common.h", "hypic_device.h", "hypic_kernels.h"]
+    return CALL_SOURCES[call]
+
+
+def sources_digest(call, workload):
     import hashlib
     h = hashlib.sha256()
-    for f in CALL_SOURCES[call]:
+    for f in call_sources(call, workload):
         with open(os.path.join(ROOT, "hybrid_attention_prefill_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -463,7 +472,7 @@ def measured_traffic(workload, call):
         for ln in fh:
             if ln.startswith("traffic-json: "):
                 rec = json.loads(ln[len("traffic-json: "):])
-                if rec.get("call") == call and rec.get("sources") == sources_digest(call):
+                if rec.get("call") == call and rec.get("sources") == sources_digest(call, workload):
                     return int(rec["bytes_per_call"])
     return None
 
