@@ -104,8 +104,30 @@ hypic_status hypic_segment_build(const hypic_dims* dims, int32_t n_seg, const in
     if ((long long)n_seg * dims->n_heads > kMaxGrid) return fail(HYPIC_E_INVALID, "n_seg * n_heads too large");
     const bool bf16 = dims->in_dtype == HYPIC_BF16;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    if (dims->delta && dims->d_k != dims->d_v)
-        return fail(HYPIC_E_UNSUPPORTED, "the delta-rule builds need d_k == d_v");
+    if (dims->delta && dims->d_k != dims->d_v) {
+        // The columns of S evolve independently under the delta rule (the erase and the gate
+        // act on its rows): a d_k x d_v state with d_v = m d_k is built as m blocks of d_k
+        // columns with the square kernels, T with the first block; no segment is cut.
+        if (dims->d_v % dims->d_k != 0 || (dims->gate != HYPIC_GATE_TOKEN && dims->gate != HYPIC_GATE_DIAG))
+            return fail(HYPIC_E_UNSUPPORTED, "the delta-rule builds need d_v a multiple of d_k and gate TOKEN or DIAG");
+        const int m = dims->d_v / dims->d_k;
+        const size_t esz = bf16 ? 2 : 4;
+        for (int j = 0; j < m; ++j) {
+            const void* vj = v ? static_cast<const char*>(v) + (size_t)j * dims->d_k * esz : nullptr;
+            float* Sj = S_out + (size_t)j * dims->d_k;
+            void* Tj = j == 0 ? T_out : nullptr;
+            const hipError_t e =
+                dims->gate == HYPIC_GATE_TOKEN
+                    ? hypic::build_gdn(dims->d_k, bf16, n_seg, dims->n_heads, seg_begin, seg_end, n_tokens, k, vj, g,
+                                       beta, Tj, dims->t_layout == HYPIC_T_SPLIT, Sj, hypic::BuildItems{},
+                                       hypic::BuildOut{}, st, dims->d_v)
+                    : hypic::build_kda(dims->d_k, bf16, dims->delta == 2, n_seg, dims->n_heads, seg_begin, seg_end,
+                                       n_tokens, k, vj, g, beta, Tj, dims->t_layout == HYPIC_T_SPLIT, Sj, st,
+                                       dims->d_v);
+            if (e != hipSuccess) return from_hip(e, "hypic_segment_build");
+        }
+        return ok();
+    }
     if (!dims->delta) {
         const size_t need = workspace ? hypic_build_workspace_bytes(dims, n_seg, n_tokens) : 0;
         if (need > 0) {

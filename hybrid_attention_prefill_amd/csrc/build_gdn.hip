@@ -174,8 +174,11 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
     int n_seg, int H, const int64_t* __restrict__ seg_begin, const int64_t* __restrict__ seg_end,
     int64_t n_tokens, const void* __restrict__ k, const void* __restrict__ v,
     const void* __restrict__ gl, const void* __restrict__ beta, void* __restrict__ T_out, int t_split,
-    float* __restrict__ S_out, BuildItems items, BuildOut ob)
+    float* __restrict__ S_out, int v_ld, BuildItems items, BuildOut ob)
 {
+    // v_ld: the row length of v ([n_tokens][H][v_ld]) and of S_out ([pair][D][v_ld]); v and
+    // S_out point at this call's D columns (D columns of a wider state, built one block at a
+    // time: the columns of S evolve independently)
     // Without outputs the chunks are pipelined (two steps per chunk, see the loop below);
     // with outputs they run one after the other, in four steps.
     constexpr bool PIPE = !OUT;
@@ -201,6 +204,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
     // the caller's slot out >= 0 or to workspace slot -1 - out (T as bf16 hi/lo planes)
     int64_t beg = seg_begin[seg], end = seg_end[seg];
     int out = seg;
+    int s_ld = v_ld;   // row length of the S destination (workspace slots are D x D)
     if (items.out) {
         // the item's fields are read before the live-item check (the arrays hold n_seg
         // entries), so the loads go out together
@@ -211,6 +215,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
             T_out = items.T_ws;
             t_split = 1;
             S_out = items.S_ws;
+            s_ld = D;
             out = -1 - out;
         }
     }
@@ -269,7 +274,9 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
     const bool blk_v = blk >= NBLK;
     const int tb0 = (blk % NBLK) / CB, cb0 = (blk % NBLK) % CB;
     const void* blk_src = blk_v ? v : k;
-    const size_t tok_stride = (size_t)H * D;
+    // row length of this thread's matrix: K blocks d, V blocks v_ld (uniform per wave where the
+    // V blocks fill whole waves, so it is kept in a scalar register there)
+    const int blk_ld = (NBLK % 64 == 0) ? __builtin_amdgcn_readfirstlane(blk_v ? v_ld : D) : (blk_v ? v_ld : D);
     u32x4 raw[4][WPR];            // 4 token rows x 8 channels, raw input bits
     uint32_t graw = 0, braw = 0;  // gate and beta of token `lane` (wave 0), raw bits
     auto prefetch = [&](int64_t c0) {
@@ -280,7 +287,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
         for (int r = 0; r < 4; ++r) {
             int64_t t = c0 + tb * 4 + r;
             t = t < end ? t : end - 1;
-            const size_t e = (size_t)t * tok_stride + (size_t)h * D + cb * 8;
+            const size_t e = ((size_t)t * H + h) * blk_ld + cb * 8;
             if constexpr (BF16) {
                 raw[r][0] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(blk_src) + e);
             } else {
@@ -1067,7 +1074,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int row = rt * 16 + 4 * g4 + e;
-                if (is_s) S_out[pair * D * D + (size_t)row * D + (ct - RT) * 16 + n16] = X[rt][c][e];
+                if (is_s) S_out[pair * D * s_ld + (size_t)row * s_ld + (ct - RT) * 16 + n16] = X[rt][c][e];
                 else put_t(T_out, t_split, pair, D, row, ct * 16 + n16, tscale * X[rt][c][e]);
             }
     }
@@ -1077,29 +1084,30 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
 template <int D, int NSPLIT, bool BF16, bool OUT>
 static hipError_t launch_gdn(int n_seg, int H, const int64_t* sb, const int64_t* se, int64_t n_tok,
                              const void* k, const void* v, const void* g, const void* beta,
-                             void* T_out, bool t_split, float* S_out, const BuildItems& items,
+                             void* T_out, bool t_split, float* S_out, int v_ld, const BuildItems& items,
                              const BuildOut& ob, hipStream_t st)
 {
     // pieces of cut segments always produce T (the fold needs it)
     if (T_out != nullptr || items.out != nullptr)
         hipLaunchKernelGGL((build_gdn_kernel<D, NSPLIT, BF16, true, OUT>), dim3(n_seg * H), dim3(512), 0, st, n_seg,
-                           H, sb, se, n_tok, k, v, g, beta, T_out, (int)t_split, S_out, items, ob);
+                           H, sb, se, n_tok, k, v, g, beta, T_out, (int)t_split, S_out, v_ld, items, ob);
     else
         hipLaunchKernelGGL((build_gdn_kernel<D, NSPLIT, BF16, false, OUT>), dim3(n_seg * H), dim3(512), 0, st, n_seg,
-                           H, sb, se, n_tok, k, v, g, beta, T_out, (int)t_split, S_out, items, ob);
+                           H, sb, se, n_tok, k, v, g, beta, T_out, (int)t_split, S_out, v_ld, items, ob);
     return hipGetLastError();
 }
 
 hipError_t build_gdn(int d, bool in_bf16, int n_seg, int H, const int64_t* sb, const int64_t* se,
                      int64_t n_tok, const void* k, const void* v, const void* g, const void* beta,
                      void* T_out, bool t_split, float* S_out, const BuildItems& items, const BuildOut& ob,
-                     hipStream_t st)
+                     hipStream_t st, int v_ld)
 {
     const bool out = ob.out != nullptr;
+    if (v_ld == 0) v_ld = d;
 #define HYPIC_GDN(D_, NS_, BF_, OUT_)                                                                     \
     if (d == D_ && in_bf16 == BF_ && out == OUT_)                                                         \
         return launch_gdn<D_, NS_, BF_, OUT_>(n_seg, H, sb, se, n_tok, k, v, g, beta, T_out, t_split, S_out, \
-                                              items, ob, st);
+                                              v_ld, items, ob, st);
     HYPIC_GDN(128, 1, true, false)
     HYPIC_GDN(128, 1, true, true)
     HYPIC_GDN(64, 1, true, false)

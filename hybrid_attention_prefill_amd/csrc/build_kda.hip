@@ -146,8 +146,11 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
     int n_seg, int H, const int64_t* __restrict__ seg_begin, const int64_t* __restrict__ seg_end,
     int64_t n_tokens, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ gl, const uint16_t* __restrict__ beta, void* __restrict__ T_out,
-    int t_split, float* __restrict__ S_out)
+    int t_split, float* __restrict__ S_out, int v_ld)
 {
+    // v_ld: the row length of v ([n_tokens][H][v_ld]) and of S_out ([pair][D][v_ld]); v and
+    // S_out point at this call's D columns (D columns of a wider state, built one block at a
+    // time: the columns of S evolve independently)
     using SM = KdaSmem<D>;
     constexpr int RT = D / 16;
     constexpr int NCT = 2 * RT;
@@ -212,19 +215,20 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
     constexpr int IPT = NPC / 4;             // items per S-wave thread
     const int vt = lane % CK;                // token of this thread's staging items
     uint16_t braw = 0;   // beta of token vt of the chunk being fetched
-    // piece pc of chunk c0n: token-major (K) or item-major (v, log-gates)
-    auto dma = [&](int64_t c0n, const uint16_t* src, uint16_t* dst, int pc, bool item_major) {
+    // piece pc of chunk c0n: token-major (K) or item-major (v, log-gates); ts and ho are the
+    // source's token stride and head offset
+    auto dma = [&](int64_t c0n, const uint16_t* src, uint16_t* dst, int pc, bool item_major, size_t ts, int ho) {
         // chunk base (uniform, 64-bit) + row offset below 32 tokens (32-bit); rows past the
         // segment clamped to its last token
         const int last = (end - 1 - c0n) < CK - 1 ? (int)(end - 1 - c0n) : CK - 1;
         const int ln = opaque(lane);           // (recomputed here rather than kept live)
         const int e = pc * 512 + ln * 8;       // token-major: element e of the plane
         const int i = pc * 64 + ln;            // item-major: item i
-        const unsigned off = item_major ? (unsigned)min(i % CK, last) * (unsigned)tok_stride + (unsigned)((i / CK) * 8)
-                                        : (unsigned)min(e / D, last) * (unsigned)tok_stride + (unsigned)(e % D);
+        const unsigned off = item_major ? (unsigned)min(i % CK, last) * (unsigned)ts + (unsigned)((i / CK) * 8)
+                                        : (unsigned)min(e / D, last) * (unsigned)ts + (unsigned)(e % D);
         // (the address is a local: as a call inside the builtin's arguments it stops the host
         // pass from emitting the kernel's launch stub)
-        const uint16_t* ps = src + (size_t)c0n * tok_stride + (size_t)h * D + off;
+        const uint16_t* ps = src + (size_t)c0n * ts + (size_t)ho + off;
         __builtin_amdgcn_global_load_lds(ps, (__attribute__((address_space(3))) void*)(dst + pc * 512), 16, 0, 0);
     };
     auto load_beta = [&](int64_t c0n) {
@@ -235,9 +239,9 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
 #pragma unroll 1   // (unrolled, the addresses of every piece are formed at once: spills)
         for (int r = 0; r < IPT; ++r) {
             const int pc = (wave & 3) + 4 * r;
-            dma(c0n, k, &sm.Kb[0][0], pc, false);
-            dma(c0n, v, vr, pc, true);
-            dma(c0n, gl, gr, pc, true);
+            dma(c0n, k, &sm.Kb[0][0], pc, false, tok_stride, h * D);
+            dma(c0n, v, vr, pc, true, (size_t)H * v_ld, h * v_ld);
+            dma(c0n, gl, gr, pc, true, tok_stride, h * D);
         }
         load_beta(c0n);
     };
@@ -790,7 +794,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int row = rt * 16 + 4 * g4 + e;
-                if (s_wave) S_out[pair * D * D + (size_t)row * D + (ct - RT) * 16 + n16] = X[rt][c][e];
+                if (s_wave) S_out[pair * D * v_ld + (size_t)row * v_ld + (ct - RT) * 16 + n16] = X[rt][c][e];
                 else put_t(T_out, t_split, pair, D, row, ct * 16 + n16, t_live ? ldexpf(X[rt][c][e], log2s) : 0.f);
             }
     }
@@ -798,15 +802,16 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
 
 hipError_t build_kda(int d, bool in_bf16, bool gate_first, int n_seg, int H, const int64_t* sb, const int64_t* se, int64_t n_tok,
                      const void* k, const void* v, const void* g, const void* beta, void* T_out, bool t_split,
-                     float* S_out, hipStream_t st)
+                     float* S_out, hipStream_t st, int v_ld)
 {
+    if (v_ld == 0) v_ld = d;
     if (!in_bf16) return hipErrorNotSupported;
     const uint16_t *k16 = static_cast<const uint16_t*>(k), *v16 = static_cast<const uint16_t*>(v),
                    *g16 = static_cast<const uint16_t*>(g), *b16 = static_cast<const uint16_t*>(beta);
 #define HYPIC_KDA(DD, GFV)                                                                                      \
     if (d == DD && gate_first == GFV) {                                                                          \
         hipLaunchKernelGGL((build_kda_kernel<DD, GFV>), dim3(n_seg * H), dim3(512), 0, st, n_seg, H, sb, se,      \
-                           n_tok, k16, v16, g16, b16, T_out, (int)t_split, S_out);                              \
+                           n_tok, k16, v16, g16, b16, T_out, (int)t_split, S_out, v_ld);                              \
         return hipGetLastError();                                                                                \
     }
     HYPIC_KDA(128, false)

@@ -64,10 +64,11 @@ struct BuildOut {
     float* out = nullptr;
 };
 // build_gdn.hip (scalar gate, delta rule)
+// v_ld: row length of v and S_out when they are d-column blocks of a wider state (0 = d).
 hipError_t build_gdn(int d, bool in_bf16, int n_seg, int H, const int64_t* sb, const int64_t* se,
                      int64_t n_tok, const void* k, const void* v, const void* g, const void* beta,
                      void* T_out, bool t_split, float* S_out, const BuildItems& items, const BuildOut& ob,
-                     hipStream_t st);
+                     hipStream_t st, int v_ld = 0);
 
 // build_split.hip: long segments built as pieces in parallel and folded by composition
 // (GDN, d in {64, 128}).  Workspace bytes for (d, H, n_seg, n_tokens); 0 = never cut.
@@ -79,7 +80,7 @@ hipError_t build_gdn_split(int d, bool in_bf16, int n_seg, int H, const int64_t*
 // build_kda.hip (per-channel gate, delta rule; bf16 inputs)
 hipError_t build_kda(int d, bool in_bf16, bool gate_first, int n_seg, int H, const int64_t* sb, const int64_t* se, int64_t n_tok,
                      const void* k, const void* v, const void* g, const void* beta, void* T_out, bool t_split,
-                     float* S_out, hipStream_t st);
+                     float* S_out, hipStream_t st, int v_ld = 0);
 
 // build_decay.hip (gate: 0 head-constant, 1 per-token scalar, 2 per-channel; no erase);
 // t_layout: 0 dense f32, 1 scalar, 2 dense bf16 hi/lo planes, 3 diagonal.  ws (may be NULL):

@@ -132,9 +132,15 @@ typedef struct {
  * Implemented:
  *   gate HEAD, TOKEN or DIAG, delta 0 : any d_k and d_v in {16, 32, 64, 128}, fp32 or
  *                                 bf16 inputs;
- *   gate TOKEN, delta 1 or 2    : d_k == d_v = 16, 32 or 64 (fp32 or bf16), 128 (bf16;
+ *   gate TOKEN, delta 1 or 2    : d_k = 16, 32 or 64 (fp32 or bf16), 128 (bf16;
  *                                 fp32 at 128 would need 250 KiB of LDS);
- *   gate DIAG,  delta 1 or 2    : d_k == d_v = 64 or 128, bf16 inputs.
+ *   gate DIAG,  delta 1 or 2    : d_k = 64 or 128, bf16 inputs;
+ *   with the delta rule d_v is d_k or a multiple of it: the columns of S evolve
+ *                                 independently (the erase and the gate act on its
+ *                                 rows), so a wider state is built as d_v / d_k blocks
+ *                                 of d_k columns, one launch each, T with the first;
+ *                                 such calls do not cut segments (the workspace is not
+ *                                 used).
  * Other combinations return HYPIC_E_UNSUPPORTED.  For the delta-rule kernels
  * the state and values must stay within fp16 range (|entries| < 6e4): they are
  * fp16 operands of the matrix products (v itself with the scalar gate, beta * v

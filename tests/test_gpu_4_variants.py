@@ -261,3 +261,52 @@ def test_decay_build_rectangular_state(gate, dk, dv, ws):
     torch.cuda.synchronize()
     full, _ = oracle.run(k, v, g, None, gate=gate, delta=0)
     assert rel_f(R.cpu().numpy()[0], full).max() <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("family,dk,dv,in_dtype,delta", [
+    ("gdn", 64, 128, "bf16", 1), ("gdn", 32, 128, "bf16", 1), ("gdn", 16, 32, "f32", 1),
+    ("kda", 64, 128, "bf16", 1), ("kda", 64, 128, "bf16", 2)])
+def test_delta_build_rectangular_state(family, dk, dv, in_dtype, delta):
+    """d_v a multiple of d_k with the delta rule: the state is built as d_v / d_k blocks of
+    d_k columns (its columns evolve independently).  Every pair against the oracle; each
+    column block bit-identical to a square build of the same value columns; the pairs
+    composed in order against the full recurrence."""
+    print(f"rectangular delta family={family} dk={dk} dv={dv} in={in_dtype} delta={delta}", flush=True)
+    rng = np.random.default_rng(7000 + 100 * dk + dv + delta)
+    H = 2
+    lens = np.array([600, 333, 1, 0, 366])
+    N = int(lens.sum())
+    begin = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    end = begin + lens
+    rnd = wl.round_bf16 if in_dtype == "bf16" else (lambda a: a.astype(np.float32))
+    tt = torch.bfloat16 if in_dtype == "bf16" else torch.float32
+    kx = rng.standard_normal((N, H, dk))
+    k = rnd(kx / np.linalg.norm(kx, axis=-1, keepdims=True))
+    v = rnd(rng.standard_normal((N, H, dv)))
+    beta = rnd(1.0 / (1.0 + np.exp(-rng.standard_normal((N, H)))))
+    if family == "gdn":
+        gate = hb.GATE_TOKEN
+        g = rnd(-0.1 * np.logaddexp(0.0, rng.standard_normal((N, H))))
+    else:
+        gate = hb.GATE_DIAG
+        g = rnd(-np.logaddexp(0.0, rng.standard_normal((N, H, dk))) / 16.0)
+    kd, gd, bd = dev(k, tt), dev(g, tt), dev(beta, tt)
+    sb, se = dev(begin, torch.int64), dev(end, torch.int64)
+    T, S = hb.segment_build(kd, dev(v, tt), gd, bd, sb, se, gate=gate, delta=delta, t_layout=hb.T_SPLIT)
+    torch.cuda.synchronize()
+    T0, S0 = oracle.segment_build(k, v, g, beta, begin, end, gate=gate, delta=delta)
+    Sg = S.cpu().numpy()
+    eS, eT = assert_pairs_close(t_value(T, dk), Sg, T0, S0, TOL[in_dtype], f"{family} {dk}x{dv}")
+    print(f"  S rel_F max {eS:.2e}, T rel_F max {eT}", flush=True)
+    for j in range(dv // dk):   # each column block as a square build of the same columns
+        Tj, Sj = hb.segment_build(kd, dev(np.ascontiguousarray(v[:, :, j * dk:(j + 1) * dk]), tt), gd, bd, sb, se,
+                                  gate=gate, delta=delta, t_layout=hb.T_SPLIT)
+        torch.cuda.synchronize()
+        assert np.array_equal(Sj.cpu().numpy(), Sg[..., j * dk:(j + 1) * dk]), f"column block {j}"
+        assert torch.equal(Tj, T)
+    R = torch.zeros((1, H, dk, dv), device="cuda")
+    hb.compose(T, S, dev(np.arange(len(lens), dtype=np.int32)[None, :], torch.int32), R)
+    torch.cuda.synchronize()
+    full, _ = oracle.run(k, v, g, beta, gate=gate, delta=delta)
+    eR = rel_f(R.cpu().numpy()[0], full).max()
+    assert eR <= TOL[in_dtype], f"composed state rel_F {eR:.3e}"
