@@ -181,20 +181,29 @@ hypic_status hypic_segment_prefill(const hypic_dims* dims, int32_t n_seg, const 
     if (!S_out || !out) return fail(HYPIC_E_INVALID, "S_out or out is NULL");
     if (n_tokens > 0 && (!q || !k || !v || !g || !beta)) return fail(HYPIC_E_INVALID, "q, k, v, g or beta is NULL");
     if ((long long)n_seg * dims->n_heads > kMaxGrid) return fail(HYPIC_E_INVALID, "n_seg * n_heads too large");
-    if (dims->gate != HYPIC_GATE_TOKEN || !dims->delta || dims->in_dtype != HYPIC_BF16 || dims->d_k != dims->d_v ||
-        (dims->d_k != 64 && dims->d_k != 128))
+    if (dims->gate != HYPIC_GATE_TOKEN || !dims->delta || dims->in_dtype != HYPIC_BF16 ||
+        dims->d_v % dims->d_k != 0 || (dims->d_k != 64 && dims->d_k != 128))
         return fail(HYPIC_E_UNSUPPORTED,
-                    "hypic_segment_prefill: implemented for gate TOKEN with the delta rule, bf16, d_k = d_v in {64, 128}");
+                    "hypic_segment_prefill: implemented for gate TOKEN with the delta rule, bf16, d_k in {64, 128} "
+                    "and d_v a multiple of d_k");
     if (dims->t_layout != HYPIC_T_DENSE && dims->t_layout != HYPIC_T_SPLIT)
         return fail(HYPIC_E_INVALID, "hypic_segment_prefill: T layout DENSE or SPLIT");
-    hypic::BuildOut ob;
-    ob.q = q;
-    ob.scale = scale;
-    ob.out = out;
-    return from_hip(hypic::build_gdn(dims->d_k, true, n_seg, dims->n_heads, seg_begin, seg_end, n_tokens, k, v, g,
-                                     beta, T_out, dims->t_layout == HYPIC_T_SPLIT, S_out, hypic::BuildItems{}, ob,
-                                     reinterpret_cast<hipStream_t>(stream)),
-                    "hypic_segment_prefill");
+    // A wider state in blocks of d_k value columns (as in hypic_segment_build): output column
+    // n depends on state column n only.
+    for (int j = 0; j < dims->d_v / dims->d_k; ++j) {
+        const size_t c = (size_t)j * dims->d_k;
+        hypic::BuildOut ob;
+        ob.q = q;
+        ob.scale = scale;
+        ob.out = out + c;
+        const hipError_t e =
+            hypic::build_gdn(dims->d_k, true, n_seg, dims->n_heads, seg_begin, seg_end, n_tokens, k,
+                             v ? static_cast<const char*>(v) + c * 2 : nullptr, g, beta, j == 0 ? T_out : nullptr,
+                             dims->t_layout == HYPIC_T_SPLIT, S_out + c, hypic::BuildItems{}, ob,
+                             reinterpret_cast<hipStream_t>(stream), dims->d_v);
+        if (e != hipSuccess) return from_hip(e, "hypic_segment_prefill");
+    }
+    return ok();
 }
 
 hypic_status hypic_compose(const hypic_dims* dims, int32_t n_chain, int32_t n_step, const int32_t* pair_id,

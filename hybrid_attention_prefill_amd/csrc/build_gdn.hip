@@ -808,7 +808,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
                                 const int t = tt * 16 + 4 * g4 + e;
-                                if (t < n) ob.out[((size_t)(c0 + t) * H + h) * D + vq * 16 + n16] = o[e];
+                                if (t < n) ob.out[((size_t)(c0 + t) * H + h) * v_ld + vq * 16 + n16] = o[e];
                             }
                         }
                     }

@@ -180,8 +180,10 @@ size_t hypic_build_workspace_bytes(const hypic_dims* dims, int32_t n_seg, int64_
  * every token's prefix state).
  *   q     : [n_tokens][H][d_k], dtype in_dtype
  *   out   : fp32 [n_tokens][H][d_v]
- * Implemented: gate TOKEN, delta 1 or 2, bf16 inputs, d_k == d_v in {64, 128}; T layout
- * DENSE or SPLIT.  Other combinations return HYPIC_E_UNSUPPORTED.
+ * Implemented: gate TOKEN, delta 1 or 2, bf16 inputs, d_k in {64, 128} and d_v = d_k or a
+ * multiple of it (column blocks of d_k, as in hypic_segment_build: output column n depends
+ * on state column n only); T layout DENSE or SPLIT.  Other combinations return
+ * HYPIC_E_UNSUPPORTED.
  */
 hypic_status hypic_segment_prefill(const hypic_dims* dims, int32_t n_seg,
                                    const int64_t* seg_begin, const int64_t* seg_end,

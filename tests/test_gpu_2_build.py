@@ -345,6 +345,44 @@ def test_prefill_outputs(d, stress, want_T):
     assert np.all(o[300:307] == 7.0)
 
 
+@pytest.mark.parametrize("want_T", [True, False])
+def test_prefill_rectangular_state(want_T):
+    """Cold prefill with d_v = 2 d_k (64 x 128): built in two column blocks of 64 value
+    columns; every token's output per 16-token block and the pairs against the oracle's
+    recurrence per segment; tokens outside the segments untouched."""
+    rng = np.random.default_rng(4242 + want_T)
+    H, dk, dv = 2, 64, 128
+    begin = np.array([0, 307, 436, 437, 436], dtype=np.int64)
+    end = np.array([300, 436, 437, 600, 436], dtype=np.int64)
+    N = 600
+    unit = lambda a: a / np.linalg.norm(a, axis=-1, keepdims=True)
+    q = wl.round_bf16(rng.standard_normal((N, H, dk)))
+    k = wl.round_bf16(unit(rng.standard_normal((N, H, dk))))
+    v = wl.round_bf16(rng.standard_normal((N, H, dv)))
+    g = wl.round_bf16(-0.1 * np.logaddexp(0.0, rng.standard_normal((N, H))))
+    beta = wl.round_bf16(1.0 / (1.0 + np.exp(-rng.standard_normal((N, H)))))
+    bf = torch.bfloat16
+    out0 = torch.full((N, H, dv), 7.0, device="cuda")
+    print("prefill rectangular", dk, dv, want_T, flush=True)
+    scale = 1.0 / np.sqrt(dk)
+    T, S, out = hb.segment_prefill(dev(q, bf), dev(k, bf), dev(v, bf), dev(g, bf), dev(beta, bf),
+                                   dev(begin, torch.int64), dev(end, torch.int64), scale=scale,
+                                   want_T=want_T, out=out0)
+    torch.cuda.synchronize()
+    T0, S0 = oracle.segment_build(k, v, g, beta, begin, end, gate=hb.GATE_TOKEN, delta=1)
+    assert_pairs_close(t_value(T, dk) if want_T else None, S.cpu().numpy(), T0, S0, TOL["bf16"], "64x128")
+    o = out.cpu().numpy().astype(np.float64)
+    for b, e in zip(begin, end):
+        if e == b:
+            continue
+        _, ref = oracle.run(k, v, g, beta, gate=hb.GATE_TOKEN, delta=1, t0=b, t1=e, q=q, scale=scale)
+        for t0 in range(0, e - b, 16):
+            blk = slice(t0, min(t0 + 16, e - b))
+            err = np.linalg.norm(o[b:e][blk] - ref[blk], axis=(0, 2)) / np.linalg.norm(ref[blk], axis=(0, 2))
+            assert err.max() <= TOL["bf16"], f"segment [{b}, {e}) tokens {t0}..: output rel_F {err.max():.2e}"
+    assert np.all(o[300:307] == 7.0)
+
+
 @pytest.mark.parametrize("path", ["build", "prefill"])
 def test_deltanet_long_segment_T(path):
     """DeltaNet (no gate) over one 6144-token segment at d = 128, built as one chain (no
