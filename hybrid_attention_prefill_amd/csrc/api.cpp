@@ -232,7 +232,8 @@ hypic_status hypic_compose(const hypic_dims* dims, int32_t n_chain, int32_t n_st
 
 size_t hypic_seam_workspace_bytes(const hypic_dims* dims, int32_t n_chain, int32_t n_step, int32_t w)
 {
-    if (!dims || dims->n_heads < 1 || !valid_d(dims->d_k) || dims->d_k != dims->d_v) return 0;
+    if (!dims || dims->n_heads < 1 || !valid_d(dims->d_k) || !valid_d(dims->d_v) || dims->d_v % dims->d_k != 0)
+        return 0;
     if (n_chain < 0 || n_step < 0 || w < 1 || w > 16) return 0;
     return hypic::seam_plan(dims->d_k, n_chain, dims->n_heads, n_step, w).bytes;
 }
@@ -250,6 +251,14 @@ hypic_status hypic_seam_advance(const hypic_dims* dims, int32_t n_chain, int32_t
 }
 
 }  // extern "C"
+
+namespace hypic {
+static hypic_status seam_block(int d, int dv, int n_chain, int n_step, int H, int w, const int64_t* seam_start,
+                               int64_t n_tokens, const void* q, const void* k, const void* v, const void* g,
+                               const void* beta, bool bf16, float scale, const int32_t* pair_id, int n_pair,
+                               const void* T_cache, bool t_split, const float* S_cache, float* S_run, float* out,
+                               void* workspace, hipStream_t st);
+}
 
 hypic_status hypic::seam_advance_with(const hypic_dims* dims, int32_t n_chain, int32_t n_step, int32_t w,
                                       const int64_t* seam_start, int64_t n_tokens, const void* q, const void* k,
@@ -270,7 +279,9 @@ hypic_status hypic::seam_advance_with(const hypic_dims* dims, int32_t n_chain, i
         return fail(HYPIC_E_UNSUPPORTED, "hypic_seam_advance: only the scalar-gated delta rule is implemented");
     if (dims->t_layout == HYPIC_T_SCALAR || dims->t_layout == HYPIC_T_DIAG)
         return fail(HYPIC_E_UNSUPPORTED, "hypic_seam_advance needs a dense T (layout DENSE or SPLIT)");
-    if (dims->d_k != dims->d_v) return fail(HYPIC_E_UNSUPPORTED, "d_k != d_v is not implemented");
+    if (dims->d_v % dims->d_k != 0)
+        return fail(HYPIC_E_UNSUPPORTED, "hypic_seam_advance: d_v must be d_k or a multiple of it (got %d, %d)",
+                    dims->d_k, dims->d_v);
     if ((long long)n_chain * n_step * dims->n_heads > kMaxGrid || (long long)n_chain * dims->n_heads * 8 > kMaxGrid)
         return fail(HYPIC_E_INVALID, "too many chains or steps");
     const size_t need = hypic_seam_workspace_bytes(dims, n_chain, n_step, w);
@@ -279,13 +290,36 @@ hypic_status hypic::seam_advance_with(const hypic_dims* dims, int32_t n_chain, i
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(HYPIC_E_INVALID, "workspace must be 256-byte aligned");
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const bool bf16 = dims->in_dtype == HYPIC_BF16;
-    const int d = dims->d_k, H = dims->n_heads;
+    const int d = dims->d_k, H = dims->n_heads, dv = dims->d_v;
+    // A state wider than d_k (d_v = m d_k) advances in m blocks of d_k columns, one after the
+    // other through the same workspace: the columns of R, of the pairs' S, of the windows' U
+    // and of the outputs evolve independently (T, the erase and the gates act on rows).
+    for (int j = 0; j < dv / d; ++j) {
+        const size_t c = (size_t)j * d;
+        const void* vj = v ? static_cast<const char*>(v) + c * (bf16 ? 2 : 4) : nullptr;
+        const hypic_status s = seam_block(d, dv, n_chain, n_step, H, w, seam_start, n_tokens, q, k, vj, g, beta,
+                                          bf16, scale, pair_id, n_pair, T_cache, dims->t_layout == HYPIC_T_SPLIT,
+                                          S_cache ? S_cache + c : nullptr, S_run + c, out + c, workspace, st);
+        if (s != HYPIC_OK) return s;
+    }
+    return ok();
+}
+
+// One block of d state columns of hypic_seam_advance (S_cache, S_run and out point at the
+// block's first column; their rows hold dv values).
+hypic_status hypic::seam_block(int d, int dv, int n_chain, int n_step, int H, int w, const int64_t* seam_start,
+                               int64_t n_tokens, const void* q, const void* k, const void* v, const void* g,
+                               const void* beta, bool bf16, float scale, const int32_t* pair_id, int n_pair,
+                               const void* T_cache, bool t_split, const float* S_cache, float* S_run, float* out,
+                               void* workspace, hipStream_t st)
+{
     const hypic::SeamPlan pl = hypic::seam_plan(d, n_chain, H, n_step, w);
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     hipError_t e = hypic::seam_prep(d, n_chain, n_step, H, seam_start, n_tokens, w, q, k, v, g, beta, bf16, scale,
-                                    ws, st);
+                                    ws, st, dv);
     if (e != hipSuccess) return from_hip(e, "hypic_seam_advance (window preparation)");
     hypic::SeamArgs sa{seam_start, n_tokens, w, (int)bf16, scale, q, k, ws, out};
+    sa.ld = dv;
     sa.nblk = pl.nblk;
     sa.blk = pl.blk;
     if (pl.nblk > 1) {
@@ -294,17 +328,16 @@ hypic_status hypic::seam_advance_with(const hypic_dims* dims, int32_t n_chain, i
         sa.agg_S = reinterpret_cast<float*>(ws + pl.agg_s_off);
     }
     const int np = pair_id ? n_pair : 0;
-    e = hypic::seam_chain(d, pl.nb, n_chain, H, n_step, pair_id, np, T_cache, dims->t_layout == HYPIC_T_SPLIT,
-                          S_cache, S_run, sa, st);
+    e = hypic::seam_chain(d, pl.nb, n_chain, H, n_step, pair_id, np, T_cache, t_split, S_cache, S_run, sa, st);
     if (e != hipSuccess || pl.nblk == 1) return from_hip(e, "hypic_seam_advance");
     // blocked scan: block aggregates composed in order (the state entering every block
     // kept), then the windows of blocks >= 1 read out from those states
     float* trail = reinterpret_cast<float*>(ws + pl.trail_off);
     e = hypic::compose_dense(d, d, n_chain, H, pl.nblk - 1, nullptr, n_chain * (pl.nblk - 1), sa.agg_T, true, sa.agg_S,
-                             S_run, trail, st);
+                             S_run, trail, st, dv);
     if (e != hipSuccess) return from_hip(e, "hypic_seam_advance (composition of the block aggregates)");
     return from_hip(hypic::seam_readout(d, n_chain, H, n_step, pl.nblk, pl.blk, w, seam_start, n_tokens, sa.ox, trail,
-                                        out, st),
+                                        out, st, dv),
                     "hypic_seam_advance (window outputs)");
 }
 

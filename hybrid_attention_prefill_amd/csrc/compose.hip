@@ -38,8 +38,11 @@ constexpr int chain_waves(int dk) { return dk >= 128 ? 8 : 4; }
 template <int DK, int DV, int NB, bool TS>
 __global__ __launch_bounds__(64 * chain_waves(DK)) void compose_dense_kernel(
     int n_units, int H, int n_step, const int32_t* __restrict__ pair_id, int n_pair,
-    const void* __restrict__ Tc, const float* __restrict__ Sc, float* __restrict__ Srun, float* __restrict__ trail)
+    const void* __restrict__ Tc, const float* __restrict__ Sc, float* __restrict__ Srun, float* __restrict__ trail,
+    int r_ld)
 {
+    // r_ld: row length of the running states ([chain][H][DK][r_ld]; DV unless Srun points at DV
+    // columns of a wider state)
     constexpr int NCB = DV / NB;
     constexpr int KP = DK < 32 ? 32 : DK;   // contraction length padded to the MFMA K
     constexpr int KS = KP / 32;
@@ -66,7 +69,7 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void compose_dense_kernel(
     }
     __syncthreads();
 
-    float* Rg = Srun + ((size_t)c * H + h) * DK * DV + cb * NB;
+    float* Rg = Srun + ((size_t)c * H + h) * DK * r_ld + cb * NB;
     f32x4 acc[RTW][CT];
 #pragma unroll
     for (int i = 0; i < RTW; ++i) {
@@ -77,7 +80,7 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void compose_dense_kernel(
             if (rt < RT) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    acc[i][ct][e] = Rg[(size_t)(rt * 16 + 4 * g4 + e) * DV + ct * 16 + n16];
+                    acc[i][ct][e] = Rg[(size_t)(rt * 16 + 4 * g4 + e) * r_ld + ct * 16 + n16];
             }
         }
     }
@@ -292,7 +295,7 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void compose_dense_kernel(
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                Rg[(size_t)(rt * 16 + 4 * g4 + e) * DV + ct * 16 + n16] = acc[i][ct][e];
+                Rg[(size_t)(rt * 16 + 4 * g4 + e) * r_ld + ct * 16 + n16] = acc[i][ct][e];
     }
 }
 
@@ -566,12 +569,12 @@ __global__ __launch_bounds__(256) void compose_scalar_kernel(
 // ---------------------------------------------------------------- launchers
 template <int DK, int DV, int NB, bool TS>
 static hipError_t launch_dense(int n_chain, int H, int n_step, const int32_t* pair_id, int n_pair,
-                               const void* Tc, const float* Sc, float* Srun, float* trail, hipStream_t st)
+                               const void* Tc, const float* Sc, float* Srun, float* trail, hipStream_t st, int r_ld)
 {
     const int n_units = n_chain * H;
     const int grid = xcd_grid_size(n_units, DV / NB);
     hipLaunchKernelGGL((compose_dense_kernel<DK, DV, NB, TS>), dim3(grid), dim3(64 * chain_waves(DK)), 0, st,
-                       n_units, H, n_step, pair_id, n_pair, Tc, Sc, Srun, trail);
+                       n_units, H, n_step, pair_id, n_pair, Tc, Sc, Srun, trail, r_ld ? r_ld : DV);
     return hipGetLastError();
 }
 
@@ -586,13 +589,13 @@ static int pick_nb(long long n_units, int dv)
 
 hipError_t compose_dense(int dk, int dv, int n_chain, int H, int n_step, const int32_t* pair_id, int n_pair,
                          const void* Tc, bool t_split, const float* Sc, float* Srun, float* trail,
-                         hipStream_t st)
+                         hipStream_t st, int r_ld)
 {
     if (dk != dv) {   // rectangular states: 16-column blocks
 #define HYPIC_RECT(DK_, DV_)                                                                                   \
     if (dk == DK_ && dv == DV_)                                                                                \
-        return t_split ? launch_dense<DK_, DV_, 16, true>(n_chain, H, n_step, pair_id, n_pair, Tc, Sc, Srun, trail, st) \
-                       : launch_dense<DK_, DV_, 16, false>(n_chain, H, n_step, pair_id, n_pair, Tc, Sc, Srun, trail, st);
+        return t_split ? launch_dense<DK_, DV_, 16, true>(n_chain, H, n_step, pair_id, n_pair, Tc, Sc, Srun, trail, st, r_ld) \
+                       : launch_dense<DK_, DV_, 16, false>(n_chain, H, n_step, pair_id, n_pair, Tc, Sc, Srun, trail, st, r_ld);
         HYPIC_RECT(16, 32) HYPIC_RECT(16, 64) HYPIC_RECT(16, 128)
         HYPIC_RECT(32, 16) HYPIC_RECT(32, 64) HYPIC_RECT(32, 128)
         HYPIC_RECT(64, 16) HYPIC_RECT(64, 32) HYPIC_RECT(64, 128)
@@ -602,7 +605,7 @@ hipError_t compose_dense(int dk, int dv, int n_chain, int H, int n_step, const i
     }
     const int d = dk;
     const int nb = pick_nb((long long)n_chain * H, d);
-    if (d == 128 && nb == 128 && trail == nullptr) {
+    if (d == 128 && nb == 128 && trail == nullptr && (r_ld == 0 || r_ld == dv)) {
         const int n_units = n_chain * H;
         const int grid = (n_units + 7) / 8 * 8;
         if (t_split)
@@ -616,8 +619,8 @@ hipError_t compose_dense(int dk, int dv, int n_chain, int H, int n_step, const i
 #define HYPIC_CASE(D_, NB_)                                                                                   \
     if (d == D_ && nb == NB_)                                                                                 \
         return t_split                                                                                        \
-                   ? launch_dense<D_, D_, NB_, true>(n_chain, H, n_step, pair_id, n_pair, Tc, Sc, Srun, trail, st) \
-                   : launch_dense<D_, D_, NB_, false>(n_chain, H, n_step, pair_id, n_pair, Tc, Sc, Srun, trail, st);
+                   ? launch_dense<D_, D_, NB_, true>(n_chain, H, n_step, pair_id, n_pair, Tc, Sc, Srun, trail, st, r_ld) \
+                   : launch_dense<D_, D_, NB_, false>(n_chain, H, n_step, pair_id, n_pair, Tc, Sc, Srun, trail, st, r_ld);
     HYPIC_CASE(16, 16)
     HYPIC_CASE(32, 32) HYPIC_CASE(32, 16)
     HYPIC_CASE(64, 64) HYPIC_CASE(64, 32) HYPIC_CASE(64, 16)

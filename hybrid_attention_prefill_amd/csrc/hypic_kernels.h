@@ -15,7 +15,9 @@ struct SeamArgs {
     const void* q;
     const void* k;
     const void* ws;             // records of seam_prep (seam_layout.h)
-    float* out;                 // [n_chain][n_step][w][H][d_v]
+    float* out;                 // [n_chain][n_step][w][H][ld]
+    int ld = 0;                 // row length of S_cache, S_run and out: d_v of the caller's tensors,
+                                // when they point at d columns of a wider state (0 = d)
     // blocked scan (nblk > 1): blocks of blk steps run at once (seam_chain.hip)
     int nblk = 1;
     int blk = 0;
@@ -38,9 +40,10 @@ struct SeamPlan {
 // t_split: T as bf16 hi/lo planes [n_pair][H][2][dk][dk]; else fp32 [n_pair][H][dk][dk];
 // S fp32 [n_pair][H][dk][dv].  pair_id NULL: step j of chain c applies pair c * n_step + j.
 // trail (may be NULL): the state before each step, fp32 [n_chain][n_step][H][dk][dv].
+// r_ld: row length of Srun when it holds dv columns of a wider state (0 = dv)
 hipError_t compose_dense(int dk, int dv, int n_chain, int H, int n_step, const int32_t* pair_id, int n_pair,
                          const void* Tc, bool t_split, const float* Sc, float* Srun, float* trail,
-                         hipStream_t st);
+                         hipStream_t st, int r_ld = 0);
 // diag: T cached as fp32 [n_pair][H][dk] (T = diag(t)); else fp32 [n_pair][H] (T = t I)
 hipError_t compose_scalar(int dk, int dv, bool diag, int n_chain, int H, int n_step, const int32_t* pair_id,
                           int n_pair, const float* Tc, const float* Sc, float* Srun, hipStream_t st);
@@ -92,9 +95,10 @@ hipError_t build_decay(int dk, int dv, bool in_bf16, int gate, int n_seg, int H,
                        void* T_out, int t_layout, float* S_out, void* ws, hipStream_t st);
 
 // seam.hip
+// v_ld: row length of v when it points at d columns of wider values (0 = d)
 hipError_t seam_prep(int d, int n_chain, int n_step, int H, const int64_t* seam_start, int64_t n_tokens,
                      int w, const void* q, const void* k, const void* v, const void* g, const void* beta,
-                     bool in_bf16, float scale, void* ws, hipStream_t st);
+                     bool in_bf16, float scale, void* ws, hipStream_t st, int v_ld = 0);
 size_t seam_record_bytes(int d);
 
 // seam_chain.hip (pair_id may be NULL: windows only)
@@ -104,7 +108,7 @@ hipError_t seam_chain(int d, int nb, int n_chain, int H, int n_step, const int32
                       hipStream_t st);
 hipError_t seam_readout(int d, int n_chain, int H, int n_step, int nblk, int blk, int w,
                         const int64_t* seam_start, int64_t n_tokens, const float* ox, const float* trail,
-                        float* out, hipStream_t st);
+                        float* out, hipStream_t st, int ld = 0);
 
 // selftest.hip
 hipError_t selftest_layouts(const float* in, float* out, hipStream_t st);

@@ -55,8 +55,9 @@ __global__ __launch_bounds__(256) void seam_prep_kernel(
     int n_cj, int H, const int64_t* __restrict__ seam_start, int64_t n_tokens, int w,
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const void* __restrict__ gl, const void* __restrict__ beta, int in_bf16, float scale,
-    unsigned char* __restrict__ ws)
+    unsigned char* __restrict__ ws, int v_ld)
 {
+    // v_ld: row length of v ([n_tokens][H][v_ld]); v points at this call's D value columns
     constexpr int W = kSeamMaxW;
     constexpr int LD = D + 4;                 // padded rows (float4 aligned)
     constexpr int KP = D < 32 ? 32 : D;       // contraction length padded to the MFMA K
@@ -81,9 +82,10 @@ __global__ __launch_bounds__(256) void seam_prep_kernel(
             float kx[8], vx[8], qx[8];
             if (t < w) {
                 const size_t e = (size_t)(s0 + t) * H * D + (size_t)h * D + c0;
+                const size_t ev = ((size_t)(s0 + t) * H + h) * v_ld + c0;
                 if (in_bf16) {
                     const u32x4 a = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(k) + e);
-                    const u32x4 b = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(v) + e);
+                    const u32x4 b = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(v) + ev);
                     const u32x4 c = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(q) + e);
 #pragma unroll
                     for (int x = 0; x < 4; ++x) {
@@ -93,7 +95,7 @@ __global__ __launch_bounds__(256) void seam_prep_kernel(
                     }
                 } else {
                     const f32x4* a = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(k) + e);
-                    const f32x4* b = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(v) + e);
+                    const f32x4* b = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(v) + ev);
                     const f32x4* c = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(q) + e);
 #pragma unroll
                     for (int x = 0; x < 4; ++x) {
@@ -266,15 +268,16 @@ __global__ __launch_bounds__(256) void seam_prep_kernel(
 
 hipError_t seam_prep(int d, int n_chain, int n_step, int H, const int64_t* seam_start, int64_t n_tokens,
                      int w, const void* q, const void* k, const void* v, const void* g, const void* beta,
-                     bool in_bf16, float scale, void* ws, hipStream_t st)
+                     bool in_bf16, float scale, void* ws, hipStream_t st, int v_ld)
 {
+    if (v_ld == 0) v_ld = d;
     const long long n_rec = (long long)n_chain * n_step * H;
     if (n_rec == 0) return hipSuccess;
 #define HYPIC_CASE(D_)                                                                                       \
     if (d == D_) {                                                                                           \
         hipLaunchKernelGGL(seam_prep_kernel<D_>, dim3((unsigned)n_rec), dim3(256), 0, st, n_chain * n_step, \
                            H, seam_start, n_tokens, w, q, k, v, g, beta, (int)in_bf16, scale,                \
-                           static_cast<unsigned char*>(ws));                                                 \
+                           static_cast<unsigned char*>(ws), v_ld);                                           \
         return hipGetLastError();                                                                            \
     }
     HYPIC_CASE(16) HYPIC_CASE(32) HYPIC_CASE(64) HYPIC_CASE(128)

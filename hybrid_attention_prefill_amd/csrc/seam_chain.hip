@@ -142,7 +142,10 @@ __global__ __launch_bounds__(64 * (DK / 16 + NB / 16)) void seam_chain_kernel(
     const int g4 = lane >> 4, n16 = lane & 15;
     const bool f32in = !sa.in_bf16;
 
-    float* Rg = Srun + ((size_t)c * H + h) * DK * DV + cb * NB;
+    // S_run, the pairs' S and the outputs have rows of sa.ld values (DV unless they hold DV
+    // columns of a wider state); the workspace parts (readouts, aggregates) have rows of DV
+    const int ld = sa.ld;
+    float* Rg = Srun + ((size_t)c * H + h) * DK * ld + cb * NB;
     f32x4 acc[CT];   // row waves: rows rt*16 + 4 g4 + e, column ct*16 + n16 of the block
     auto store_split = [&]() {
 #pragma unroll
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(64 * (DK / 16 + NB / 16)) void seam_chain_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int row = rt * 16 + 4 * g4 + e, col = cb * NB + ct * 16 + n16;
-                acc[ct][e] = b == 0 ? Rg[(size_t)row * DV + ct * 16 + n16] : (tcol && row == col ? 1.f : 0.f);
+                acc[ct][e] = b == 0 ? Rg[(size_t)row * ld + ct * 16 + n16] : (tcol && row == col ? 1.f : 0.f);
             }
         store_split();
     }
@@ -217,11 +220,11 @@ __global__ __launch_bounds__(64 * (DK / 16 + NB / 16)) void seam_chain_kernel(
     };
     auto load_s = [&](int id, Step& st) {
         if (!tcol) {   // uniform; the transition columns add no S
-            const float* S = Sc + ((size_t)id * H + h) * DK * DV + cb * NB;
+            const float* S = Sc + ((size_t)id * H + h) * DK * ld + cb * NB;
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) st.sv[ct][e] = S[(size_t)(rt * 16 + 4 * g4 + e) * DV + ct * 16 + n16];
+                for (int e = 0; e < 4; ++e) st.sv[ct][e] = S[(size_t)(rt * 16 + 4 * g4 + e) * ld + ct * 16 + n16];
         }
     };
     auto load_rows = [&](int id, Step& st) {
@@ -410,7 +413,7 @@ __global__ __launch_bounds__(64 * (DK / 16 + NB / 16)) void seam_chain_kernel(
                     const int t = 4 * g4 + e;
                     if (t < sa.w) {
                         if (b == 0)
-                            sa.out[((cj * sa.w + t) * H + h) * DV + col] = o[e];
+                            sa.out[((cj * sa.w + t) * H + h) * ld + col] = o[e];
                         else
                             sa.ox[((cj * sa.w + t) * H + h) * 2 * DV + (tcol ? 0 : DV) + col] = o[e];
                     }
@@ -538,7 +541,7 @@ __global__ __launch_bounds__(64 * (DK / 16 + NB / 16)) void seam_chain_kernel(
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Rg[(size_t)(rt * 16 + 4 * g4 + e) * DV + ct * 16 + n16] = acc[ct][e];
+            for (int e = 0; e < 4; ++e) Rg[(size_t)(rt * 16 + 4 * g4 + e) * ld + ct * 16 + n16] = acc[ct][e];
     } else if (tcol) {   // the block's aggregate transition, bf16 hi/lo planes
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
@@ -562,8 +565,10 @@ __global__ __launch_bounds__(64 * (DK / 16 + NB / 16)) void seam_chain_kernel(
 template <int DK>
 __global__ __launch_bounds__(512) void seam_readout_kernel(
     int n_chain, int H, int n_step, int nblk, int blk, int w, const int64_t* __restrict__ seam_start,
-    int64_t n_tokens, const float* __restrict__ ox, const float* __restrict__ trail, float* __restrict__ out)
+    int64_t n_tokens, const float* __restrict__ ox, const float* __restrict__ trail, float* __restrict__ out,
+    int ld)
 {
+    // ld: row length of the outputs (DV unless they hold DV columns of wider ones)
     constexpr int DV = DK;
     constexpr int KP = DK < 32 ? 32 : DK;
     constexpr int KS = KP / 32;
@@ -661,7 +666,7 @@ __global__ __launch_bounds__(512) void seam_readout_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 4 * g4 + e;
-                if (t < w) out[((cj * w + t) * H + h) * DV + col] = o[e];
+                if (t < w) out[((cj * w + t) * H + h) * ld + col] = o[e];
             }
         }
     }
@@ -722,9 +727,11 @@ static hipError_t launch_seam_chain(int n_chain, int H, int n_step, const int32_
 }
 
 hipError_t seam_chain(int d, int nb, int n_chain, int H, int n_step, const int32_t* pair_id, int n_pair,
-                      const void* Tc, bool t_split, const float* Sc, float* Srun, const SeamArgs& sa,
+                      const void* Tc, bool t_split, const float* Sc, float* Srun, const SeamArgs& sa_in,
                       hipStream_t st)
 {
+    SeamArgs sa = sa_in;
+    if (sa.ld == 0) sa.ld = d;
 #define HYPIC_CASE(D_, NB_)                                                                                     \
     if (d == D_ && nb == NB_)                                                                                   \
         return t_split ? launch_seam_chain<D_, true, NB_>(n_chain, H, n_step, pair_id, n_pair, Tc, Sc, Srun, sa, st) \
@@ -737,14 +744,15 @@ hipError_t seam_chain(int d, int nb, int n_chain, int H, int n_step, const int32
 
 hipError_t seam_readout(int d, int n_chain, int H, int n_step, int nblk, int blk, int w,
                         const int64_t* seam_start, int64_t n_tokens, const float* ox, const float* trail,
-                        float* out, hipStream_t st)
+                        float* out, hipStream_t st, int ld)
 {
+    if (ld == 0) ld = d;
     const long long grid = (long long)n_chain * (nblk - 1) * H * ((blk + 7) / 8);
     if (nblk < 2 || grid <= 0) return hipSuccess;
 #define HYPIC_CASE(D_)                                                                                   \
     if (d == D_) {                                                                                       \
         hipLaunchKernelGGL(seam_readout_kernel<D_>, dim3((unsigned)grid), dim3(512), 0, st, n_chain, H, \
-                           n_step, nblk, blk, w, seam_start, n_tokens, ox, trail, out);                  \
+                           n_step, nblk, blk, w, seam_start, n_tokens, ox, trail, out, ld);              \
         return hipGetLastError();                                                                        \
     }
     HYPIC_CASE(16) HYPIC_CASE(32) HYPIC_CASE(64) HYPIC_CASE(128)

@@ -102,6 +102,22 @@ def test_seam_gdn_fp32_d16(stress, t_layout):
     _check(W, R, out, S_ref, outs_ref, TOL["f32"])
 
 
+@pytest.mark.parametrize("lens", [[150, 97, 72, 300, 40], [40 + (7 * i) % 23 for i in range(48)]])
+def test_seam_rectangular_state(lens):
+    """d_v = 2 d_k (64 x 128): the state advances in two blocks of 64 columns through one
+    workspace; a short prompt (plain chain) and a 48-segment one (blocked scan), against the
+    full recurrence: final state and every window's outputs."""
+    W = _seam_workload("gdn-16h-d128-32k", lens, 8, H=2, d=64)
+    rng = np.random.default_rng(64128 + len(lens))
+    W.v = wl.round_bf16(rng.standard_normal((W.n_tokens, 2, 128)))
+    W.d_v = 128
+    print(W.name, "rectangular seam", len(lens), "segments", flush=True)
+    R, out = _gpu(W)
+    S_ref, outs_ref = _reference(W)
+    worst = _check(W, R, out, S_ref, outs_ref, TOL["bf16"])
+    print(f"  outputs rel_F max {worst:.2e}", flush=True)
+
+
 def test_seam_only_without_pairs():
     """pair_id NULL: only the seam windows advance the state."""
     W = _seam_workload("gdn-16h-d128-32k", [40, 30, 50], 8, H=2)
