@@ -107,10 +107,12 @@ hypic_status hypic_segment_build(const hypic_dims* dims, int32_t n_seg, const in
     if (dims->delta && dims->d_k != dims->d_v) {
         // The columns of S evolve independently under the delta rule (the erase and the gate
         // act on its rows): a d_k x d_v state with d_v = m d_k is built as m blocks of d_k
-        // columns with the square kernels, T with the first block; no segment is cut.
-        if (dims->d_v % dims->d_k != 0 || (dims->gate != HYPIC_GATE_TOKEN && dims->gate != HYPIC_GATE_DIAG))
-            return fail(HYPIC_E_UNSUPPORTED, "the delta-rule builds need d_v a multiple of d_k and gate TOKEN or DIAG");
-        const int m = dims->d_v / dims->d_k;
+        // columns with the square kernels, T with the first block; with d_v < d_k in one
+        // launch whose missing value columns read as zeros and are not written.  No segment is cut.
+        if ((dims->d_v > dims->d_k && dims->d_v % dims->d_k != 0) ||
+            (dims->gate != HYPIC_GATE_TOKEN && dims->gate != HYPIC_GATE_DIAG))
+            return fail(HYPIC_E_UNSUPPORTED, "the delta-rule builds need d_v < d_k or a multiple of it, and gate TOKEN or DIAG");
+        const int m = dims->d_v > dims->d_k ? dims->d_v / dims->d_k : 1;
         const size_t esz = bf16 ? 2 : 4;
         for (int j = 0; j < m; ++j) {
             const void* vj = v ? static_cast<const char*>(v) + (size_t)j * dims->d_k * esz : nullptr;
@@ -182,15 +184,15 @@ hypic_status hypic_segment_prefill(const hypic_dims* dims, int32_t n_seg, const 
     if (n_tokens > 0 && (!q || !k || !v || !g || !beta)) return fail(HYPIC_E_INVALID, "q, k, v, g or beta is NULL");
     if ((long long)n_seg * dims->n_heads > kMaxGrid) return fail(HYPIC_E_INVALID, "n_seg * n_heads too large");
     if (dims->gate != HYPIC_GATE_TOKEN || !dims->delta || dims->in_dtype != HYPIC_BF16 ||
-        dims->d_v % dims->d_k != 0 || (dims->d_k != 64 && dims->d_k != 128))
+        (dims->d_v > dims->d_k && dims->d_v % dims->d_k != 0) || (dims->d_k != 64 && dims->d_k != 128))
         return fail(HYPIC_E_UNSUPPORTED,
                     "hypic_segment_prefill: implemented for gate TOKEN with the delta rule, bf16, d_k in {64, 128} "
-                    "and d_v a multiple of d_k");
+                    "and d_v below d_k or a multiple of it");
     if (dims->t_layout != HYPIC_T_DENSE && dims->t_layout != HYPIC_T_SPLIT)
         return fail(HYPIC_E_INVALID, "hypic_segment_prefill: T layout DENSE or SPLIT");
     // A wider state in blocks of d_k value columns (as in hypic_segment_build): output column
     // n depends on state column n only.
-    for (int j = 0; j < dims->d_v / dims->d_k; ++j) {
+    for (int j = 0; j < (dims->d_v > dims->d_k ? dims->d_v / dims->d_k : 1); ++j) {
         const size_t c = (size_t)j * dims->d_k;
         hypic::BuildOut ob;
         ob.q = q;

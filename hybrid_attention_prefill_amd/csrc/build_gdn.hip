@@ -169,7 +169,7 @@ __device__ __forceinline__ u32x4 pack8(const uint16_t* x) {
 
 }  // namespace
 
-template <int D, int NSPLIT, bool BF16, bool WANT_T, bool OUT>
+template <int D, int NSPLIT, bool BF16, bool WANT_T, bool OUT, bool NW>
 __global__ __launch_bounds__(512) void build_gdn_kernel(
     int n_seg, int H, const int64_t* __restrict__ seg_begin, const int64_t* __restrict__ seg_end,
     int64_t n_tokens, const void* __restrict__ k, const void* __restrict__ v,
@@ -178,7 +178,10 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
 {
     // v_ld: the row length of v ([n_tokens][H][v_ld]) and of S_out ([pair][D][v_ld]); v and
     // S_out point at this call's D columns (D columns of a wider state, built one block at a
-    // time: the columns of S evolve independently)
+    // time: the columns of S evolve independently).  With v_ld < D (NW, narrow values) the
+    // values have only v_ld columns: the rest are read as zeros and those columns of S are not
+    // written.
+    const int v_cols = NW ? v_ld : D;
     // Without outputs the chunks are pipelined (two steps per chunk, see the loop below);
     // with outputs they run one after the other, in four steps.
     constexpr bool PIPE = !OUT;
@@ -205,6 +208,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
     int64_t beg = seg_begin[seg], end = seg_end[seg];
     int out = seg;
     int s_ld = v_ld;   // row length of the S destination (workspace slots are D x D)
+    int s_cols = v_cols;
     if (items.out) {
         // the item's fields are read before the live-item check (the arrays hold n_seg
         // entries), so the loads go out together
@@ -216,6 +220,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
             t_split = 1;
             S_out = items.S_ws;
             s_ld = D;
+            s_cols = D;
             out = -1 - out;
         }
     }
@@ -277,12 +282,15 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
     // row length of this thread's matrix: K blocks d, V blocks v_ld (uniform per wave where the
     // V blocks fill whole waves, so it is kept in a scalar register there)
     const int blk_ld = (NBLK % 64 == 0) ? __builtin_amdgcn_readfirstlane(blk_v ? v_ld : D) : (blk_v ? v_ld : D);
+    // V blocks past the value columns (v_ld < D) load column block 0 and are not staged: their
+    // rows of the V^T planes keep the zeros written at the start
+    const bool blk_zero = NW && blk_v && cb0 * 8 >= v_cols;
     u32x4 raw[4][WPR];            // 4 token rows x 8 channels, raw input bits
     uint32_t graw = 0, braw = 0;  // gate and beta of token `lane` (wave 0), raw bits
     auto prefetch = [&](int64_t c0) {
         // rows past the segment are clamped into it (masked when staged); the loads are
         // unconditional so that nothing waits for them before the next chunk's staging
-        const int tb = opaque(tb0), cb = opaque(cb0);
+        const int tb = opaque(tb0), cb = blk_zero ? 0 : opaque(cb0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             int64_t t = c0 + tb * 4 + r;
@@ -413,7 +421,7 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
     };
     auto stage_b = [&](int n_s, int kbuf) {
         const int tb = opaque(tb0), cb = opaque(cb0);
-        if (has_blk) {   // transposed: one channel row, 4 consecutive tokens = 8 contiguous bytes
+        if (has_blk && !blk_zero) {   // transposed: one channel row, 4 consecutive tokens = 8 contiguous bytes
             uint16_t(*dst)[D * CH] = blk_v ? sm.Vt[kbuf] : sm.Kt[kbuf];
             float f[4][8];
             if constexpr (!(NSPLIT == 1 && BF16)) stage_rows(f);
@@ -438,6 +446,10 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
         fetch_q(beg, 0);
         if (beg + CH < end) fetch_q(beg + CH, 1);
         prefetch(beg);
+    }
+    if (NW) {   // value channels past v_ld: zero rows of the V^T planes, never staged
+        uint32_t* z = reinterpret_cast<uint32_t*>(&sm.Vt[0][0][0]);
+        for (int i = tid; i < (int)(sizeof(sm.Vt) / 4); i += 512) z[i] = 0u;
     }
     if constexpr (OUT) {
         // the output products read M in 32-column blocks: of the tiles above the diagonal,
@@ -808,7 +820,8 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
                                 const int t = tt * 16 + 4 * g4 + e;
-                                if (t < n) ob.out[((size_t)(c0 + t) * H + h) * v_ld + vq * 16 + n16] = o[e];
+                                if (t < n && (!NW || vq * 16 + n16 < v_cols))
+                                    ob.out[((size_t)(c0 + t) * H + h) * v_ld + vq * 16 + n16] = o[e];
                             }
                         }
                     }
@@ -1074,11 +1087,30 @@ __global__ __launch_bounds__(512) void build_gdn_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int row = rt * 16 + 4 * g4 + e;
-                if (is_s) S_out[pair * D * s_ld + (size_t)row * s_ld + (ct - RT) * 16 + n16] = X[rt][c][e];
+                if (is_s) {
+                    if (!NW || (ct - RT) * 16 + n16 < s_cols)
+                        S_out[pair * D * s_ld + (size_t)row * s_ld + (ct - RT) * 16 + n16] = X[rt][c][e];
+                }
                 else put_t(T_out, t_split, pair, D, row, ct * 16 + n16, tscale * X[rt][c][e]);
             }
     }
 
+}
+
+template <int D, int NSPLIT, bool BF16, bool OUT, bool NW>
+static hipError_t launch_gdn_nw(int n_seg, int H, const int64_t* sb, const int64_t* se, int64_t n_tok,
+                                const void* k, const void* v, const void* g, const void* beta,
+                                void* T_out, bool t_split, float* S_out, int v_ld, const BuildItems& items,
+                                const BuildOut& ob, hipStream_t st)
+{
+    // pieces of cut segments always produce T (the fold needs it)
+    if (T_out != nullptr || items.out != nullptr)
+        hipLaunchKernelGGL((build_gdn_kernel<D, NSPLIT, BF16, true, OUT, NW>), dim3(n_seg * H), dim3(512), 0, st,
+                           n_seg, H, sb, se, n_tok, k, v, g, beta, T_out, (int)t_split, S_out, v_ld, items, ob);
+    else
+        hipLaunchKernelGGL((build_gdn_kernel<D, NSPLIT, BF16, false, OUT, NW>), dim3(n_seg * H), dim3(512), 0, st,
+                           n_seg, H, sb, se, n_tok, k, v, g, beta, T_out, (int)t_split, S_out, v_ld, items, ob);
+    return hipGetLastError();
 }
 
 template <int D, int NSPLIT, bool BF16, bool OUT>
@@ -1087,14 +1119,10 @@ static hipError_t launch_gdn(int n_seg, int H, const int64_t* sb, const int64_t*
                              void* T_out, bool t_split, float* S_out, int v_ld, const BuildItems& items,
                              const BuildOut& ob, hipStream_t st)
 {
-    // pieces of cut segments always produce T (the fold needs it)
-    if (T_out != nullptr || items.out != nullptr)
-        hipLaunchKernelGGL((build_gdn_kernel<D, NSPLIT, BF16, true, OUT>), dim3(n_seg * H), dim3(512), 0, st, n_seg,
-                           H, sb, se, n_tok, k, v, g, beta, T_out, (int)t_split, S_out, v_ld, items, ob);
-    else
-        hipLaunchKernelGGL((build_gdn_kernel<D, NSPLIT, BF16, false, OUT>), dim3(n_seg * H), dim3(512), 0, st, n_seg,
-                           H, sb, se, n_tok, k, v, g, beta, T_out, (int)t_split, S_out, v_ld, items, ob);
-    return hipGetLastError();
+    return v_ld < D ? launch_gdn_nw<D, NSPLIT, BF16, OUT, true>(n_seg, H, sb, se, n_tok, k, v, g, beta, T_out,
+                                                              t_split, S_out, v_ld, items, ob, st)
+                    : launch_gdn_nw<D, NSPLIT, BF16, OUT, false>(n_seg, H, sb, se, n_tok, k, v, g, beta, T_out,
+                                                               t_split, S_out, v_ld, items, ob, st);
 }
 
 hipError_t build_gdn(int d, bool in_bf16, int n_seg, int H, const int64_t* sb, const int64_t* se,

@@ -141,7 +141,7 @@ __device__ __forceinline__ Frag<1> f16frag(const uint16_t* base, int ld, int row
 
 }  // namespace
 
-template <int D, bool GF>
+template <int D, bool GF, bool NW>
 __global__ __launch_bounds__(512) void build_kda_kernel(
     int n_seg, int H, const int64_t* __restrict__ seg_begin, const int64_t* __restrict__ seg_end,
     int64_t n_tokens, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -150,7 +150,10 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
 {
     // v_ld: the row length of v ([n_tokens][H][v_ld]) and of S_out ([pair][D][v_ld]); v and
     // S_out point at this call's D columns (D columns of a wider state, built one block at a
-    // time: the columns of S evolve independently)
+    // time: the columns of S evolve independently).  With v_ld < D (NW, narrow values) the
+    // values have only v_ld columns: the rest are read as zeros and those columns of S are not
+    // written.
+    const int v_cols = NW ? v_ld : D;
     using SM = KdaSmem<D>;
     constexpr int RT = D / 16;
     constexpr int NCT = 2 * RT;
@@ -216,15 +219,18 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
     const int vt = lane % CK;                // token of this thread's staging items
     uint16_t braw = 0;   // beta of token vt of the chunk being fetched
     // piece pc of chunk c0n: token-major (K) or item-major (v, log-gates); ts and ho are the
-    // source's token stride and head offset
-    auto dma = [&](int64_t c0n, const uint16_t* src, uint16_t* dst, int pc, bool item_major, size_t ts, int ho) {
+    // source's token stride and head offset, cols its channels (an item past them loads
+    // channel group 0, and is zeroed where staged)
+    auto dma = [&](int64_t c0n, const uint16_t* src, uint16_t* dst, int pc, bool item_major, size_t ts, int ho,
+                   int cols) {
         // chunk base (uniform, 64-bit) + row offset below 32 tokens (32-bit); rows past the
         // segment clamped to its last token
         const int last = (end - 1 - c0n) < CK - 1 ? (int)(end - 1 - c0n) : CK - 1;
         const int ln = opaque(lane);           // (recomputed here rather than kept live)
         const int e = pc * 512 + ln * 8;       // token-major: element e of the plane
         const int i = pc * 64 + ln;            // item-major: item i
-        const unsigned off = item_major ? (unsigned)min(i % CK, last) * (unsigned)ts + (unsigned)((i / CK) * 8)
+        const int cg = (NW && (i / CK) * 8 >= cols) ? 0 : (i / CK) * 8;
+        const unsigned off = item_major ? (unsigned)min(i % CK, last) * (unsigned)ts + (unsigned)cg
                                         : (unsigned)min(e / D, last) * (unsigned)ts + (unsigned)(e % D);
         // (the address is a local: as a call inside the builtin's arguments it stops the host
         // pass from emitting the kernel's launch stub)
@@ -239,9 +245,9 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
 #pragma unroll 1   // (unrolled, the addresses of every piece are formed at once: spills)
         for (int r = 0; r < IPT; ++r) {
             const int pc = (wave & 3) + 4 * r;
-            dma(c0n, k, &sm.Kb[0][0], pc, false, tok_stride, h * D);
-            dma(c0n, v, vr, pc, true, (size_t)H * v_ld, h * v_ld);
-            dma(c0n, gl, gr, pc, true, tok_stride, h * D);
+            dma(c0n, k, &sm.Kb[0][0], pc, false, tok_stride, h * D, D);
+            dma(c0n, v, vr, pc, true, (size_t)H * v_ld, h * v_ld, v_cols);
+            dma(c0n, gl, gr, pc, true, tok_stride, h * D, D);
         }
         load_beta(c0n);
     };
@@ -311,6 +317,10 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
     bool staged = false;   // the chunk at hand was staged by the T waves during the previous chunk
     if (beg < end && wave < 4) fetch(beg, sm.rv.nx.Vr, sm.rv.nx.Gr);
     for (int c = tid; c < D; c += 512) sm.Ag[0][c] = 0.f;   // row 0 (exclusive gate of token 0) stays zero
+    if (NW) {   // value channels past v_ld: zero rows of (diag(b) V)^T (token columns)
+        for (int i = v_cols * LDT + tid; i < D * LDT; i += 512) (&sm.bVT[0][0])[i] = 0;
+    }
+    static_assert(LDT >= CK + 8, "padding columns of the token-indexed rows");
     for (int64_t c0 = beg; c0 < end; c0 += CK) {
         const int n = (int)((end - c0) < CK ? (end - c0) : CK);
         const int par = (int)(((c0 - beg) / CK) & 1);   // chunk parity (betas, renormalisation records)
@@ -327,10 +337,14 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
         // (diag(b) V)^T, fp16 (first read in the W and Z1 phase), by the staging waves for
         // their items: from registers, or, when staged during the previous chunk, from the fp16
         // values over v
+        // Value channels past v_ld keep the zero rows written at the start: their items write
+        // to the rows' padding columns instead (CK .. LDT-1, which no fragment reads), so the
+        // stores need no branch.
         auto put_bvt = [&](int r, const uint16_t (&hv)[8]) {
             const int vcg = ((wave & 3) * 64 + lane + 256 * r) / CK;
+            const int col = (NW && vcg * 8 >= v_cols) ? CK + (vt & 7) : vt;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sm.bVT[vcg * 8 + e][vt] = hv[e];
+            for (int e = 0; e < 8; ++e) sm.bVT[vcg * 8 + e][col] = hv[e];
         };
         if (staged) {
             if (wave >= 4) {
@@ -794,7 +808,10 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int row = rt * 16 + 4 * g4 + e;
-                if (s_wave) S_out[pair * D * v_ld + (size_t)row * v_ld + (ct - RT) * 16 + n16] = X[rt][c][e];
+                if (s_wave) {
+                    if (!NW || (ct - RT) * 16 + n16 < v_cols)
+                        S_out[pair * D * v_ld + (size_t)row * v_ld + (ct - RT) * 16 + n16] = X[rt][c][e];
+                }
                 else put_t(T_out, t_split, pair, D, row, ct * 16 + n16, t_live ? ldexpf(X[rt][c][e], log2s) : 0.f);
             }
     }
@@ -810,8 +827,12 @@ hipError_t build_kda(int d, bool in_bf16, bool gate_first, int n_seg, int H, con
                    *g16 = static_cast<const uint16_t*>(g), *b16 = static_cast<const uint16_t*>(beta);
 #define HYPIC_KDA(DD, GFV)                                                                                      \
     if (d == DD && gate_first == GFV) {                                                                          \
-        hipLaunchKernelGGL((build_kda_kernel<DD, GFV>), dim3(n_seg * H), dim3(512), 0, st, n_seg, H, sb, se,      \
-                           n_tok, k16, v16, g16, b16, T_out, (int)t_split, S_out, v_ld);                              \
+        if (v_ld < DD)                                                                                           \
+            hipLaunchKernelGGL((build_kda_kernel<DD, GFV, true>), dim3(n_seg * H), dim3(512), 0, st, n_seg, H,    \
+                               sb, se, n_tok, k16, v16, g16, b16, T_out, (int)t_split, S_out, v_ld);             \
+        else                                                                                                     \
+            hipLaunchKernelGGL((build_kda_kernel<DD, GFV, false>), dim3(n_seg * H), dim3(512), 0, st, n_seg, H,   \
+                               sb, se, n_tok, k16, v16, g16, b16, T_out, (int)t_split, S_out, v_ld);             \
         return hipGetLastError();                                                                                \
     }
     HYPIC_KDA(128, false)

@@ -135,12 +135,14 @@ typedef struct {
  *   gate TOKEN, delta 1 or 2    : d_k = 16, 32 or 64 (fp32 or bf16), 128 (bf16;
  *                                 fp32 at 128 would need 250 KiB of LDS);
  *   gate DIAG,  delta 1 or 2    : d_k = 64 or 128, bf16 inputs;
- *   with the delta rule d_v is d_k or a multiple of it: the columns of S evolve
- *                                 independently (the erase and the gate act on its
- *                                 rows), so a wider state is built as d_v / d_k blocks
- *                                 of d_k columns, one launch each, T with the first;
- *                                 such calls do not cut segments (the workspace is not
- *                                 used).
+ *   with the delta rule any d_v: the columns of S evolve independently (the
+ *                                 erase and the gate act on its rows), so a state
+ *                                 wider than d_k (d_v a multiple of d_k) is built as
+ *                                 d_v / d_k blocks of d_k columns, one launch each, T
+ *                                 with the first, and a narrower one in one launch
+ *                                 whose missing value columns read as zeros and are not
+ *                                 written; calls with d_v != d_k do not cut segments
+ *                                 (the workspace is not used).
  * Other combinations return HYPIC_E_UNSUPPORTED.  For the delta-rule kernels
  * the state and values must stay within fp16 range (|entries| < 6e4): they are
  * fp16 operands of the matrix products (v itself with the scalar gate, beta * v
@@ -180,9 +182,9 @@ size_t hypic_build_workspace_bytes(const hypic_dims* dims, int32_t n_seg, int64_
  * every token's prefix state).
  *   q     : [n_tokens][H][d_k], dtype in_dtype
  *   out   : fp32 [n_tokens][H][d_v]
- * Implemented: gate TOKEN, delta 1 or 2, bf16 inputs, d_k in {64, 128} and d_v = d_k or a
- * multiple of it (column blocks of d_k, as in hypic_segment_build: output column n depends
- * on state column n only); T layout DENSE or SPLIT.  Other combinations return
+ * Implemented: gate TOKEN, delta 1 or 2, bf16 inputs, d_k in {64, 128} and any d_v (as in
+ * hypic_segment_build: column blocks of d_k, or one launch with zero-padded values below
+ * d_k; output column n depends on state column n only); T layout DENSE or SPLIT.  Other combinations return
  * HYPIC_E_UNSUPPORTED.
  */
 hypic_status hypic_segment_prefill(const hypic_dims* dims, int32_t n_seg,

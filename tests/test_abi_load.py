@@ -87,8 +87,8 @@ def test_empty_work_is_ok(lib):
 
 
 def test_unsupported_reported(lib):
-    # the delta rule with d_v not a multiple of d_k (a multiple is built in column blocks)
-    d = _dims(dk=32, dv=16)
+    # the delta rule with a per-head scalar gate (the delta-rule builds take token or channel gates)
+    d = _dims(gate=hb.GATE_HEAD)
     p = ctypes.c_void_p(16)  # never dereferenced: the shape is rejected first
     st = lib.hypic_segment_build(ctypes.byref(d), 1, p, p, 4, p, p, p, p, p, p, None, 0, None)
     assert st == hb.HYPIC_E_UNSUPPORTED

@@ -345,13 +345,14 @@ def test_prefill_outputs(d, stress, want_T):
     assert np.all(o[300:307] == 7.0)
 
 
-@pytest.mark.parametrize("want_T", [True, False])
-def test_prefill_rectangular_state(want_T):
-    """Cold prefill with d_v = 2 d_k (64 x 128): built in two column blocks of 64 value
-    columns; every token's output per 16-token block and the pairs against the oracle's
-    recurrence per segment; tokens outside the segments untouched."""
-    rng = np.random.default_rng(4242 + want_T)
-    H, dk, dv = 2, 64, 128
+@pytest.mark.parametrize("dk,dv,want_T", [(64, 128, True), (64, 128, False), (128, 64, True)])
+def test_prefill_rectangular_state(dk, dv, want_T):
+    """Cold prefill with d_k != d_v: 64 x 128 in two column blocks of 64 value columns,
+    128 x 64 in one launch with the missing value columns read as zeros; every token's
+    output per 16-token block and the pairs against the oracle's recurrence per segment;
+    tokens outside the segments untouched."""
+    rng = np.random.default_rng(4242 + want_T + dk)
+    H = 2
     begin = np.array([0, 307, 436, 437, 436], dtype=np.int64)
     end = np.array([300, 436, 437, 600, 436], dtype=np.int64)
     N = 600
@@ -370,7 +371,7 @@ def test_prefill_rectangular_state(want_T):
                                    want_T=want_T, out=out0)
     torch.cuda.synchronize()
     T0, S0 = oracle.segment_build(k, v, g, beta, begin, end, gate=hb.GATE_TOKEN, delta=1)
-    assert_pairs_close(t_value(T, dk) if want_T else None, S.cpu().numpy(), T0, S0, TOL["bf16"], "64x128")
+    assert_pairs_close(t_value(T, dk) if want_T else None, S.cpu().numpy(), T0, S0, TOL["bf16"], f"{dk}x{dv}")
     o = out.cpu().numpy().astype(np.float64)
     for b, e in zip(begin, end):
         if e == b:

@@ -265,12 +265,14 @@ def test_decay_build_rectangular_state(gate, dk, dv, ws):
 
 @pytest.mark.parametrize("family,dk,dv,in_dtype,delta", [
     ("gdn", 64, 128, "bf16", 1), ("gdn", 32, 128, "bf16", 1), ("gdn", 16, 32, "f32", 1),
-    ("kda", 64, 128, "bf16", 1), ("kda", 64, 128, "bf16", 2)])
+    ("kda", 64, 128, "bf16", 1), ("kda", 64, 128, "bf16", 2),
+    ("gdn", 128, 64, "bf16", 1), ("gdn", 32, 16, "f32", 1), ("kda", 128, 32, "bf16", 1), ("kda", 128, 64, "bf16", 2)])
 def test_delta_build_rectangular_state(family, dk, dv, in_dtype, delta):
-    """d_v a multiple of d_k with the delta rule: the state is built as d_v / d_k blocks of
-    d_k columns (its columns evolve independently).  Every pair against the oracle; each
-    column block bit-identical to a square build of the same value columns; the pairs
-    composed in order against the full recurrence."""
+    """d_k != d_v with the delta rule (its columns evolve independently): a multiple of d_k
+    is built as d_v / d_k blocks of d_k columns, a narrower state in one launch with the
+    missing value columns read as zeros.  Every pair against the oracle; each column block
+    bit-identical to a square build of the same value columns; the pairs composed in order
+    against the full recurrence."""
     print(f"rectangular delta family={family} dk={dk} dv={dv} in={in_dtype} delta={delta}", flush=True)
     rng = np.random.default_rng(7000 + 100 * dk + dv + delta)
     H = 2
