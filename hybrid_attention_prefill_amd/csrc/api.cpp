@@ -234,7 +234,8 @@ hypic_status hypic_compose(const hypic_dims* dims, int32_t n_chain, int32_t n_st
 
 size_t hypic_seam_workspace_bytes(const hypic_dims* dims, int32_t n_chain, int32_t n_step, int32_t w)
 {
-    if (!dims || dims->n_heads < 1 || !valid_d(dims->d_k) || !valid_d(dims->d_v) || dims->d_v % dims->d_k != 0)
+    if (!dims || dims->n_heads < 1 || !valid_d(dims->d_k) || !valid_d(dims->d_v) ||
+        (dims->d_v > dims->d_k && dims->d_v % dims->d_k != 0))
         return 0;
     if (n_chain < 0 || n_step < 0 || w < 1 || w > 16) return 0;
     return hypic::seam_plan(dims->d_k, n_chain, dims->n_heads, n_step, w).bytes;
@@ -281,8 +282,8 @@ hypic_status hypic::seam_advance_with(const hypic_dims* dims, int32_t n_chain, i
         return fail(HYPIC_E_UNSUPPORTED, "hypic_seam_advance: only the scalar-gated delta rule is implemented");
     if (dims->t_layout == HYPIC_T_SCALAR || dims->t_layout == HYPIC_T_DIAG)
         return fail(HYPIC_E_UNSUPPORTED, "hypic_seam_advance needs a dense T (layout DENSE or SPLIT)");
-    if (dims->d_v % dims->d_k != 0)
-        return fail(HYPIC_E_UNSUPPORTED, "hypic_seam_advance: d_v must be d_k or a multiple of it (got %d, %d)",
+    if (dims->d_v > dims->d_k && dims->d_v % dims->d_k != 0)
+        return fail(HYPIC_E_UNSUPPORTED, "hypic_seam_advance: d_v must be below d_k or a multiple of it (got %d, %d)",
                     dims->d_k, dims->d_v);
     if ((long long)n_chain * n_step * dims->n_heads > kMaxGrid || (long long)n_chain * dims->n_heads * 8 > kMaxGrid)
         return fail(HYPIC_E_INVALID, "too many chains or steps");
@@ -295,8 +296,9 @@ hypic_status hypic::seam_advance_with(const hypic_dims* dims, int32_t n_chain, i
     const int d = dims->d_k, H = dims->n_heads, dv = dims->d_v;
     // A state wider than d_k (d_v = m d_k) advances in m blocks of d_k columns, one after the
     // other through the same workspace: the columns of R, of the pairs' S, of the windows' U
-    // and of the outputs evolve independently (T, the erase and the gates act on rows).
-    for (int j = 0; j < dv / d; ++j) {
+    // and of the outputs evolve independently (T, the erase and the gates act on rows).  A
+    // narrower one (d_v < d_k) in one pass whose column blocks end at its last column.
+    for (int j = 0; j < (dv > d ? dv / d : 1); ++j) {
         const size_t c = (size_t)j * d;
         const void* vj = v ? static_cast<const char*>(v) + c * (bf16 ? 2 : 4) : nullptr;
         const hypic_status s = seam_block(d, dv, n_chain, n_step, H, w, seam_start, n_tokens, q, k, vj, g, beta,
@@ -315,7 +317,7 @@ hypic_status hypic::seam_block(int d, int dv, int n_chain, int n_step, int H, in
                                const void* T_cache, bool t_split, const float* S_cache, float* S_run, float* out,
                                void* workspace, hipStream_t st)
 {
-    const hypic::SeamPlan pl = hypic::seam_plan(d, n_chain, H, n_step, w);
+    const hypic::SeamPlan pl = hypic::seam_plan(d, n_chain, H, n_step, w, dv < d ? dv : 0);
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     hipError_t e = hypic::seam_prep(d, n_chain, n_step, H, seam_start, n_tokens, w, q, k, v, g, beta, bf16, scale,
                                     ws, st, dv);

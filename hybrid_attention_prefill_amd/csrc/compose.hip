@@ -58,6 +58,7 @@ __global__ __launch_bounds__(64 * chain_waves(DK)) void compose_dense_kernel(
     const UnitSlot us = xcd_unit_slot(blockIdx.x, NCB);
     if (us.unit >= n_units) return;
     const int c = us.unit / H, h = us.unit % H, cb = us.sub;
+    if (r_ld < DV && cb * NB >= r_ld) return;   // past the columns of a narrower running state (a multiple of NB)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g4 = lane >> 4, n16 = lane & 15;
 
@@ -604,7 +605,8 @@ hipError_t compose_dense(int dk, int dv, int n_chain, int H, int n_step, const i
         return hipErrorInvalidValue;
     }
     const int d = dk;
-    const int nb = pick_nb((long long)n_chain * H, d);
+    int nb = pick_nb((long long)n_chain * H, d);
+    while (r_ld > 0 && r_ld < dv && r_ld % nb != 0) nb /= 2;   // blocks that end at a narrower state's last column
     if (d == 128 && nb == 128 && trail == nullptr && (r_ld == 0 || r_ld == dv)) {
         const int n_units = n_chain * H;
         const int grid = (n_units + 7) / 8 * 8;

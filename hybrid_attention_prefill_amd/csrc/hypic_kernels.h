@@ -17,7 +17,8 @@ struct SeamArgs {
     const void* ws;             // records of seam_prep (seam_layout.h)
     float* out;                 // [n_chain][n_step][w][H][ld]
     int ld = 0;                 // row length of S_cache, S_run and out: d_v of the caller's tensors,
-                                // when they point at d columns of a wider state (0 = d)
+                                // when they point at d columns of a wider state, or a narrower
+                                // state's d_v < d (its missing columns are not computed) (0 = d)
     // blocked scan (nblk > 1): blocks of blk steps run at once (seam_chain.hip)
     int nblk = 1;
     int blk = 0;
@@ -102,7 +103,8 @@ hipError_t seam_prep(int d, int n_chain, int n_step, int H, const int64_t* seam_
 size_t seam_record_bytes(int d);
 
 // seam_chain.hip (pair_id may be NULL: windows only)
-SeamPlan seam_plan(int d, int n_chain, int H, int n_step, int w);
+// dv: the state's columns when fewer than d (0: d); the column blocks then end at its last column
+SeamPlan seam_plan(int d, int n_chain, int H, int n_step, int w, int dv = 0);
 hipError_t seam_chain(int d, int nb, int n_chain, int H, int n_step, const int32_t* pair_id, int n_pair,
                       const void* Tc, bool t_split, const float* Sc, float* Srun, const SeamArgs& sa,
                       hipStream_t st);

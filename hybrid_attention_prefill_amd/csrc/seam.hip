@@ -58,6 +58,8 @@ __global__ __launch_bounds__(256) void seam_prep_kernel(
     unsigned char* __restrict__ ws, int v_ld)
 {
     // v_ld: row length of v ([n_tokens][H][v_ld]); v points at this call's D value columns
+    // (with v_ld < D, the channels past v_ld read as zeros: U has zero columns there)
+    const int v_cols = v_ld < D ? v_ld : D;
     constexpr int W = kSeamMaxW;
     constexpr int LD = D + 4;                 // padded rows (float4 aligned)
     constexpr int KP = D < 32 ? 32 : D;       // contraction length padded to the MFMA K
@@ -82,7 +84,8 @@ __global__ __launch_bounds__(256) void seam_prep_kernel(
             float kx[8], vx[8], qx[8];
             if (t < w) {
                 const size_t e = (size_t)(s0 + t) * H * D + (size_t)h * D + c0;
-                const size_t ev = ((size_t)(s0 + t) * H + h) * v_ld + c0;
+                const bool vok = c0 < v_cols;
+                const size_t ev = ((size_t)(s0 + t) * H + h) * v_ld + (vok ? c0 : 0);
                 if (in_bf16) {
                     const u32x4 a = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(k) + e);
                     const u32x4 b = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(v) + ev);
@@ -107,6 +110,10 @@ __global__ __launch_bounds__(256) void seam_prep_kernel(
             } else {
 #pragma unroll
                 for (int x = 0; x < 8; ++x) kx[x] = vx[x] = qx[x] = 0.f;
+            }
+            if (c0 >= v_cols) {
+#pragma unroll
+                for (int x = 0; x < 8; ++x) vx[x] = 0.f;
             }
 #pragma unroll
             for (int x = 0; x < 8; x += 4) {

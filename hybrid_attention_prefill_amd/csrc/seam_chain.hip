@@ -131,6 +131,9 @@ __global__ __launch_bounds__(64 * (DK / 16 + NB / 16)) void seam_chain_kernel(
     if (b == 0 && sub < NCB && nblk > 1) return;   // block 0 has state columns only (uniform)
     const bool tcol = b > 0 && sub < NCB;          // transition columns of X
     const int cb = sub % NCB;
+    // a state narrower than DV (sa.ld < DV, a multiple of NB): its missing column blocks have
+    // no work (the transition columns are all needed)
+    if (!tcol && sa.ld < DV && cb * NB >= sa.ld) return;
     const int j0 = b * sa.blk, j1 = min(n_step, j0 + sa.blk);
     const size_t agg = (size_t)c * (nblk - 1) + (b - 1);   // aggregate slot of block b >= 1
 
@@ -666,7 +669,7 @@ __global__ __launch_bounds__(512) void seam_readout_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 4 * g4 + e;
-                if (t < w) out[((cj * w + t) * H + h) * ld + col] = o[e];
+                if (t < w && col < ld) out[((cj * w + t) * H + h) * ld + col] = o[e];
             }
         }
     }
@@ -676,7 +679,7 @@ __global__ __launch_bounds__(512) void seam_readout_kernel(
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-SeamPlan seam_plan(int d, int n_chain, int H, int n_step, int w)
+SeamPlan seam_plan(int d, int n_chain, int H, int n_step, int w, int dv)
 {
     SeamPlan p;
     const long long units16 = (long long)n_chain * H * (d / 16);
@@ -693,6 +696,7 @@ SeamPlan seam_plan(int d, int n_chain, int H, int n_step, int w)
         nblk = nblk < n_step / 4 ? nblk : n_step / 4;        // at least 4 steps per block
         p.nblk = nblk < 2 ? 1 : (int)nblk;
     }
+    if (dv > 0 && dv < d && dv % p.nb != 0) p.nb = 16;   // column blocks that end at a narrower state's last column
     p.blk = p.nblk > 1 ? (n_step + p.nblk - 1) / p.nblk : n_step;
     if (p.nblk > 1) p.nblk = (n_step + p.blk - 1) / p.blk;
     const size_t n_rec = (size_t)n_chain * n_step * H;

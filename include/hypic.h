@@ -232,10 +232,11 @@ hypic_status hypic_compose(const hypic_dims* dims, int32_t n_chain, int32_t n_st
  *                owned by the caller, 256-byte aligned; contents are
  *                overwritten; concurrent calls need distinct workspaces.
  *   T_cache    : t_layout DENSE or SPLIT
- * Implemented: gate TOKEN, delta 1 or 2, d_k in {16, 32, 64, 128} and d_v = d_k or a
- * multiple of it.  A wider state advances in d_v / d_k blocks of d_k columns, one after the
- * other through the same workspace (sized for one block): the columns of the state, of the
- * pairs' S, of the windows' values and of the outputs evolve independently.
+ * Implemented: gate TOKEN, delta 1 or 2, d_k and d_v in {16, 32, 64, 128}.  The columns of
+ * the state, of the pairs' S, of the windows' values and of the outputs evolve
+ * independently: a state wider than d_k advances in d_v / d_k blocks of d_k columns, one
+ * after the other through the same workspace (sized for one block), a narrower one in one
+ * pass whose column blocks end at its last column.
  */
 hypic_status hypic_seam_advance(const hypic_dims* dims, int32_t n_chain, int32_t n_step,
                                 int32_t w, const int64_t* seam_start, int64_t n_tokens,

@@ -126,4 +126,7 @@ def test_seam_workspace_size(lib):
     assert one > 0 and one % 256 == 0 and one % 2 == 0
     assert hb.seam_workspace_bytes(2, 128, 128, 3, 5, 8) == 15 * one
     assert hb.seam_workspace_bytes(2, 128, 128, 1, 1, 17) == 0
-    assert hb.seam_workspace_bytes(2, 128, 64, 1, 1, 8) == 0
+    # d_k != d_v: the state advances in column blocks of at most d_k through one workspace
+    assert hb.seam_workspace_bytes(2, 128, 64, 1, 1, 8) == one
+    assert hb.seam_workspace_bytes(2, 64, 128, 1, 1, 8) == hb.seam_workspace_bytes(2, 64, 64, 1, 1, 8)
+    assert hb.seam_workspace_bytes(2, 24, 24, 1, 1, 8) == 0

@@ -102,15 +102,17 @@ def test_seam_gdn_fp32_d16(stress, t_layout):
     _check(W, R, out, S_ref, outs_ref, TOL["f32"])
 
 
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64), (64, 16)])
 @pytest.mark.parametrize("lens", [[150, 97, 72, 300, 40], [40 + (7 * i) % 23 for i in range(48)]])
-def test_seam_rectangular_state(lens):
-    """d_v = 2 d_k (64 x 128): the state advances in two blocks of 64 columns through one
-    workspace; a short prompt (plain chain) and a 48-segment one (blocked scan), against the
+def test_seam_rectangular_state(lens, dk, dv):
+    """d_k != d_v: a wider state (64 x 128) advances in two blocks of 64 columns through one
+    workspace, a narrower one (128 x 64, 64 x 16) in one pass whose column blocks end at its
+    last column; a short prompt (plain chain) and a 48-segment one (blocked scan), against the
     full recurrence: final state and every window's outputs."""
-    W = _seam_workload("gdn-16h-d128-32k", lens, 8, H=2, d=64)
-    rng = np.random.default_rng(64128 + len(lens))
-    W.v = wl.round_bf16(rng.standard_normal((W.n_tokens, 2, 128)))
-    W.d_v = 128
+    W = _seam_workload("gdn-16h-d128-32k", lens, 8, H=2, d=dk)
+    rng = np.random.default_rng(64128 + len(lens) + dk + dv)
+    W.v = wl.round_bf16(rng.standard_normal((W.n_tokens, 2, dv)))
+    W.d_v = dv
     print(W.name, "rectangular seam", len(lens), "segments", flush=True)
     R, out = _gpu(W)
     S_ref, outs_ref = _reference(W)
