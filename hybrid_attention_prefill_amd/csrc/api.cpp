@@ -109,14 +109,16 @@ hypic_status hypic_segment_build(const hypic_dims* dims, int32_t n_seg, const in
         // act on its rows): a d_k x d_v state with d_v = m d_k is built as m blocks of d_k
         // columns with the square kernels, T with the first block; with d_v < d_k in one
         // launch whose missing value columns read as zeros and are not written.  No segment is cut.
-        if ((dims->d_v > dims->d_k && dims->d_v % dims->d_k != 0) ||
+        // (the KDA build runs d_k = 16, 32 on its d = 64 kernel: blocks of 64 value columns)
+        const int bw = dims->gate == HYPIC_GATE_DIAG && dims->d_k < 64 ? 64 : dims->d_k;
+        if ((dims->d_v > bw && dims->d_v % bw != 0) ||
             (dims->gate != HYPIC_GATE_TOKEN && dims->gate != HYPIC_GATE_DIAG))
             return fail(HYPIC_E_UNSUPPORTED, "the delta-rule builds need d_v < d_k or a multiple of it, and gate TOKEN or DIAG");
-        const int m = dims->d_v > dims->d_k ? dims->d_v / dims->d_k : 1;
+        const int m = dims->d_v > bw ? dims->d_v / bw : 1;
         const size_t esz = bf16 ? 2 : 4;
         for (int j = 0; j < m; ++j) {
-            const void* vj = v ? static_cast<const char*>(v) + (size_t)j * dims->d_k * esz : nullptr;
-            float* Sj = S_out + (size_t)j * dims->d_k;
+            const void* vj = v ? static_cast<const char*>(v) + (size_t)j * bw * esz : nullptr;
+            float* Sj = S_out + (size_t)j * bw;
             void* Tj = j == 0 ? T_out : nullptr;
             const hipError_t e =
                 dims->gate == HYPIC_GATE_TOKEN

@@ -141,12 +141,12 @@ __device__ __forceinline__ Frag<1> f16frag(const uint16_t* base, int ld, int row
 
 }  // namespace
 
-template <int D, bool GF, bool NW>
+template <int D, bool GF, bool NW, bool NK>
 __global__ __launch_bounds__(512) void build_kda_kernel(
     int n_seg, int H, const int64_t* __restrict__ seg_begin, const int64_t* __restrict__ seg_end,
     int64_t n_tokens, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ gl, const uint16_t* __restrict__ beta, void* __restrict__ T_out,
-    int t_split, float* __restrict__ S_out, int v_ld)
+    int t_split, float* __restrict__ S_out, int v_ld, int k_d)
 {
     // v_ld: the row length of v ([n_tokens][H][v_ld]) and of S_out ([pair][D][v_ld]); v and
     // S_out point at this call's D columns (D columns of a wider state, built one block at a
@@ -154,6 +154,11 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
     // values have only v_ld columns: the rest are read as zeros and those columns of S are not
     // written.
     const int v_cols = NW ? v_ld : D;
+    // k_d: with NK (narrow keys, d_k = k_d < D) the keys and log-gates have k_d channels; the
+    // kernel runs at D with the other channels read as zeros (key 0, log-gate 0: they take no
+    // part, and the rows and columns of T past k_d stay those of the identity), and T and S
+    // are written for their first k_d rows (T also for its first k_d columns) only
+    const int k_ld = NK ? k_d : D;
     using SM = KdaSmem<D>;
     constexpr int RT = D / 16;
     constexpr int NCT = 2 * RT;
@@ -194,7 +199,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
     int log2s = 0;       // T = 2^log2s * X_T
     bool t_live = true;  // false once every T entry is below 2^-120
 
-    const size_t tok_stride = (size_t)H * D;
+    const size_t tok_stride = (size_t)H * k_ld;
     // A chunk's k, log-gates and v are loaded global -> LDS directly, one chunk ahead, in 1-KiB
     // pieces (16 bytes per lane): K token-major into Kb; v and the log-gates item-major, staging
     // item i (channel group i / CK, token i % CK) in piece i / 64, so a thread that stages an
@@ -229,9 +234,10 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
         const int ln = opaque(lane);           // (recomputed here rather than kept live)
         const int e = pc * 512 + ln * 8;       // token-major: element e of the plane
         const int i = pc * 64 + ln;            // item-major: item i
-        const int cg = (NW && (i / CK) * 8 >= cols) ? 0 : (i / CK) * 8;
+        const int cg = ((NW || NK) && (i / CK) * 8 >= cols) ? 0 : (i / CK) * 8;
+        const int ch = (NK && e % D >= cols) ? 0 : e % D;
         const unsigned off = item_major ? (unsigned)min(i % CK, last) * (unsigned)ts + (unsigned)cg
-                                        : (unsigned)min(e / D, last) * (unsigned)ts + (unsigned)(e % D);
+                                        : (unsigned)min(e / D, last) * (unsigned)ts + (unsigned)ch;
         // (the address is a local: as a call inside the builtin's arguments it stops the host
         // pass from emitting the kernel's launch stub)
         const uint16_t* ps = src + (size_t)c0n * ts + (size_t)ho + off;
@@ -245,9 +251,9 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
 #pragma unroll 1   // (unrolled, the addresses of every piece are formed at once: spills)
         for (int r = 0; r < IPT; ++r) {
             const int pc = (wave & 3) + 4 * r;
-            dma(c0n, k, &sm.Kb[0][0], pc, false, tok_stride, h * D, D);
+            dma(c0n, k, &sm.Kb[0][0], pc, false, tok_stride, h * k_ld, k_ld);
             dma(c0n, v, vr, pc, true, (size_t)H * v_ld, h * v_ld, v_cols);
-            dma(c0n, gl, gr, pc, true, tok_stride, h * D, D);
+            dma(c0n, gl, gr, pc, true, tok_stride, h * k_ld, k_ld);
         }
         load_beta(c0n);
     };
@@ -278,7 +284,12 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
         for (int r = 0; r < IPT; ++r) {
             const int i = (wave & 3) * 64 + lane + 256 * r, vcg = i / CK;
             const u32x4 vw = *reinterpret_cast<const u32x4*>(&vr[i * 8]);
-            const u32x4 gw = *reinterpret_cast<const u32x4*>(&gr[i * 8]);
+            u32x4 gw = *reinterpret_cast<const u32x4*>(&gr[i * 8]);
+            if constexpr (NK) {   // log-gates of the channels past k_d: 0 (bit masks, no branch)
+                const unsigned gm = vcg * 8 < k_ld ? ~0u : 0u;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) gw[e] &= gm;
+            }
             float x[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -303,7 +314,7 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
             *reinterpret_cast<f32x4*>(&sm.Ag[vt + 1][vcg * 8 + 4]) = f32x4{x[4], x[5], x[6], x[7]};
             if (vcg == 0) sm.beta[bpar][vt] = bt;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) bm = fmaxf(bm, x[e]);
+            for (int e = 0; e < 8; ++e) bm = fmaxf(bm, (NK && vcg * 8 >= k_ld) ? -3.0e38f : x[e]);   // (real channels only)
             if (to_lds)
                 *reinterpret_cast<u32x4*>(&vr[i * 8]) =
                     u32x4{cvt2_f16(vx[r][0], vx[r][1]), cvt2_f16(vx[r][2], vx[r][3]),
@@ -423,13 +434,14 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
             static_assert((CK / 4) * NCP <= 512, "one item per thread");
             if (tid < (CK / 4) * NCP) {
                 const int c = 2 * (tid % NCP), t0 = 4 * (tid / NCP);
+                const unsigned km = (!NK || c < k_ld) ? ~0u : 0u;   // keys of the channels past k_d: 0
                 float kx[4][2], A[5][2], eg[4][2], er[5][2];
                 float P[2], Q[2];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const unsigned kw = *reinterpret_cast<const unsigned*>(&sm.Kb[t0 + i][c]);
-                    kx[i][0] = __uint_as_float(kw << 16);
-                    kx[i][1] = __uint_as_float(kw & 0xFFFF0000u);
+                    kx[i][0] = __uint_as_float((kw << 16) & km);
+                    kx[i][1] = __uint_as_float(kw & 0xFFFF0000u & km);
                 }
                 // A[r] = the erase vectors' cumulative gate of token t0 + r (c_t; i_t = c_{t+1}
                 // when the gate comes first); A[4] is the next token's
@@ -784,7 +796,10 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(X[rt][c][e]));
+                    for (int e = 0; e < 4; ++e) {   // (NK: the real block of T only; the rest is the identity's)
+                        if (!NK || (rt * 16 + 4 * g4 + e < k_ld && (tile0 + c) * 16 + n16 < k_ld))
+                            m = fmaxf(m, fabsf(X[rt][c][e]));
+                    }
 #pragma unroll
             for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
         }
@@ -809,10 +824,11 @@ __global__ __launch_bounds__(512) void build_kda_kernel(
             for (int e = 0; e < 4; ++e) {
                 const int row = rt * 16 + 4 * g4 + e;
                 if (s_wave) {
-                    if (!NW || (ct - RT) * 16 + n16 < v_cols)
-                        S_out[pair * D * v_ld + (size_t)row * v_ld + (ct - RT) * 16 + n16] = X[rt][c][e];
+                    if ((!NW || (ct - RT) * 16 + n16 < v_cols) && (!NK || row < k_ld))
+                        S_out[pair * k_ld * v_ld + (size_t)row * v_ld + (ct - RT) * 16 + n16] = X[rt][c][e];
                 }
-                else put_t(T_out, t_split, pair, D, row, ct * 16 + n16, t_live ? ldexpf(X[rt][c][e], log2s) : 0.f);
+                else if (!NK || (row < k_ld && ct * 16 + n16 < k_ld))
+                    put_t(T_out, t_split, pair, k_ld, row, ct * 16 + n16, t_live ? ldexpf(X[rt][c][e], log2s) : 0.f);
             }
     }
 }
@@ -822,17 +838,27 @@ hipError_t build_kda(int d, bool in_bf16, bool gate_first, int n_seg, int H, con
                      float* S_out, hipStream_t st, int v_ld)
 {
     if (v_ld == 0) v_ld = d;
+    // d_k = 16 or 32: the D = 64 kernel with the key channels past d_k read as zeros
+    const int k_d = d;
+    const bool nk = d < 64;
+    if (nk) d = 64;
     if (!in_bf16) return hipErrorNotSupported;
     const uint16_t *k16 = static_cast<const uint16_t*>(k), *v16 = static_cast<const uint16_t*>(v),
                    *g16 = static_cast<const uint16_t*>(g), *b16 = static_cast<const uint16_t*>(beta);
+#define HYPIC_KDA_NW(DD, GFV, NKV)                                                                              \
+    if (v_ld < DD)                                                                                               \
+        hipLaunchKernelGGL((build_kda_kernel<DD, GFV, true, NKV>), dim3(n_seg * H), dim3(512), 0, st, n_seg, H,    \
+                           sb, se, n_tok, k16, v16, g16, b16, T_out, (int)t_split, S_out, v_ld, k_d);            \
+    else                                                                                                         \
+        hipLaunchKernelGGL((build_kda_kernel<DD, GFV, false, NKV>), dim3(n_seg * H), dim3(512), 0, st, n_seg, H,   \
+                           sb, se, n_tok, k16, v16, g16, b16, T_out, (int)t_split, S_out, v_ld, k_d);
 #define HYPIC_KDA(DD, GFV)                                                                                      \
     if (d == DD && gate_first == GFV) {                                                                          \
-        if (v_ld < DD)                                                                                           \
-            hipLaunchKernelGGL((build_kda_kernel<DD, GFV, true>), dim3(n_seg * H), dim3(512), 0, st, n_seg, H,    \
-                               sb, se, n_tok, k16, v16, g16, b16, T_out, (int)t_split, S_out, v_ld);             \
-        else                                                                                                     \
-            hipLaunchKernelGGL((build_kda_kernel<DD, GFV, false>), dim3(n_seg * H), dim3(512), 0, st, n_seg, H,   \
-                               sb, se, n_tok, k16, v16, g16, b16, T_out, (int)t_split, S_out, v_ld);             \
+        if (DD == 64 && nk) {                                                                                    \
+            HYPIC_KDA_NW(64, GFV, true)                                                                          \
+        } else {                                                                                                 \
+            HYPIC_KDA_NW(DD, GFV, false)                                                                         \
+        }                                                                                                        \
         return hipGetLastError();                                                                                \
     }
     HYPIC_KDA(128, false)
@@ -840,6 +866,7 @@ hipError_t build_kda(int d, bool in_bf16, bool gate_first, int n_seg, int H, con
     HYPIC_KDA(64, false)
     HYPIC_KDA(64, true)
 #undef HYPIC_KDA
+#undef HYPIC_KDA_NW
     return hipErrorNotSupported;
 }
 

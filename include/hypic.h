@@ -134,7 +134,9 @@ typedef struct {
  *                                 bf16 inputs;
  *   gate TOKEN, delta 1 or 2    : d_k = 16, 32 or 64 (fp32 or bf16), 128 (bf16;
  *                                 fp32 at 128 would need 250 KiB of LDS);
- *   gate DIAG,  delta 1 or 2    : d_k = 64 or 128, bf16 inputs;
+ *   gate DIAG,  delta 1 or 2    : any d_k, bf16 inputs (d_k = 16 and 32 run on the
+ *                                 d_k = 64 kernel with the key channels past d_k read
+ *                                 as zeros);
  *   with the delta rule any d_v: the columns of S evolve independently (the
  *                                 erase and the gate act on its rows), so a state
  *                                 wider than d_k (d_v a multiple of d_k) is built as

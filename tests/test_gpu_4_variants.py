@@ -266,7 +266,8 @@ def test_decay_build_rectangular_state(gate, dk, dv, ws):
 @pytest.mark.parametrize("family,dk,dv,in_dtype,delta", [
     ("gdn", 64, 128, "bf16", 1), ("gdn", 32, 128, "bf16", 1), ("gdn", 16, 32, "f32", 1),
     ("kda", 64, 128, "bf16", 1), ("kda", 64, 128, "bf16", 2),
-    ("gdn", 128, 64, "bf16", 1), ("gdn", 32, 16, "f32", 1), ("kda", 128, 32, "bf16", 1), ("kda", 128, 64, "bf16", 2)])
+    ("gdn", 128, 64, "bf16", 1), ("gdn", 32, 16, "f32", 1), ("kda", 128, 32, "bf16", 1), ("kda", 128, 64, "bf16", 2),
+    ("kda", 32, 32, "bf16", 1), ("kda", 16, 16, "bf16", 2), ("kda", 32, 128, "bf16", 1), ("kda", 16, 64, "bf16", 2)])
 def test_delta_build_rectangular_state(family, dk, dv, in_dtype, delta):
     """d_k != d_v with the delta rule (its columns evolve independently): a multiple of d_k
     is built as d_v / d_k blocks of d_k columns, a narrower state in one launch with the
